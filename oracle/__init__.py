@@ -1,0 +1,11 @@
+"""Float64 CPU oracle for Spatial Sparse Attention (SSA).  Test infrastructure only.
+
+Only the test suite, the smoke check and the benchmark's CPU-baseline leg may
+import this package.  The HIP library never calls it, and it shares no code
+with the HIP library.
+"""
+from .ssa_oracle import (  # noqa: F401
+    Partition, partition, pool, compressed_block, select_topk, selected_block,
+    window_partition, window_attention, combine, forward, forward_items, backward,
+    sdpa_dense,
+)

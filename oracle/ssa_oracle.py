@@ -1,0 +1,351 @@
+"""Spatial Sparse Attention (SSA), forward and backward, as a plain float64 CPU oracle.
+
+TEST INFRASTRUCTURE ONLY: imported by tests/, the smoke check and the
+benchmark's cpu_baseline leg, never by the HIP product path.
+
+What SSA computes, as the pages state it (Direct3D-S2 pages: the pixal-3d.com
+landing page, "What is Direct3D-S2?" and the FAQ entry "What is SSA?"; the
+nav.superapi.store page, "Technical principles of Direct3D-S2", first bullet):
+tokens carrying 3D coordinates are partitioned into blocks by coordinate; a
+compression module reduces each block to one token by pooling and attends to
+those block tokens (global context); the attention scores of the compression
+module pick the important blocks, whose tokens are attended at full
+resolution (selection); a local window module attends to nearby tokens; and the
+three outputs are aggregated with predicted gating scores.
+
+The pages give no equations.  The readings taken where they are silent:
+  * blocks are axis-aligned B^3 cubes anchored at the origin, ids ordered by the
+    x-major linear block key; only occupied blocks exist;
+  * compression = arithmetic mean of the block's token keys/values followed by a
+    linear map (k~ = kbar @ W_k, row-vector convention, shared by all heads);
+  * softmax scale tau = 1/sqrt(d) in every branch unless given; no masks, no
+    position terms; a token attends to every compressed block, its own included;
+  * block importance sigma_h(Bq, b) = sum over the query block's tokens of their
+    compressed softmax probabilities for block b;
+  * selection = the min(k, M) blocks with the largest sigma, ties to the lower
+    block id, reported in ascending id order and padded with -1;
+  * the selected branch is one softmax over the union of the selected blocks'
+    tokens; the window branch is one softmax over all tokens in the query's
+    window cell (non-overlapping w^3 cells anchored at the origin);
+  * gates are used as given, layout [N,H,3] in the order (compressed, selected,
+    window).
+Everything is float64; inputs are the dtype-rounded values, upcast exactly.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+
+import numpy as np
+
+
+# --------------------------------------------------------------------------- partition
+@dataclasses.dataclass
+class Partition:
+    """Blocks of a coordinate set.
+
+    perm[r]    token index at sorted position r (tokens ordered by block key, then index)
+    blk_off    [M+1] first sorted position of each block, blk_off[M] = N
+    blk_key    [M] linear block key kappa of each block (ascending)
+    tok2blk    [N] block id of each token (caller order)
+    """
+    perm: np.ndarray
+    blk_off: np.ndarray
+    blk_key: np.ndarray
+    tok2blk: np.ndarray
+    edge: int
+    dims: tuple
+
+    @property
+    def M(self) -> int:
+        return len(self.blk_key)
+
+    def tokens(self, b: int) -> np.ndarray:
+        return self.perm[self.blk_off[b]:self.blk_off[b + 1]]
+
+
+def partition(coords: np.ndarray, edge: int, grid) -> Partition:
+    """Partition tokens into edge^3 blocks by their 3D coordinates.
+
+    Follows the pages' "partitions input tokens by 3D coordinates" (nav.superapi.store,
+    "Technical principles of Direct3D-S2"): beta = floor(c / edge) per axis, block key
+    kappa = (beta_x * n_y + beta_y) * n_z + beta_z with n_a = ceil(G_a / edge); blocks
+    are the distinct keys in ascending order; tokens within a block keep index order.
+    """
+    c = np.asarray(coords, dtype=np.int64)
+    g = np.broadcast_to(np.asarray(grid, dtype=np.int64), (3,))
+    if c.size and (c.min() < 0 or np.any(c >= g[None, :])):
+        raise ValueError("coordinate outside the grid")
+    dims = tuple(int(-(-int(x) // edge)) for x in g)
+    beta = c // edge
+    key = (beta[:, 0] * dims[1] + beta[:, 1]) * dims[2] + beta[:, 2]
+    order = np.argsort(key, kind="stable")
+    ks = key[order]
+    if len(ks):
+        uniq, starts, counts = np.unique(ks, return_index=True, return_counts=True)
+    else:
+        uniq = starts = counts = np.zeros(0, dtype=np.int64)
+    blk_off = np.append(starts, len(ks)).astype(np.int64)
+    tok2blk = np.empty(len(ks), dtype=np.int64)
+    tok2blk[order] = np.repeat(np.arange(len(uniq)), counts)
+    return Partition(order.astype(np.int64), blk_off, uniq.astype(np.int64), tok2blk, edge, dims)
+
+
+# --------------------------------------------------------------------------- compression
+def pool(k: np.ndarray, v: np.ndarray, wk: np.ndarray, wv: np.ndarray, part: Partition):
+    """Compressed keys/values per block and head: mean over the block's tokens, then W.
+
+    The pages' compression extracts block-level information by convolution and pooling
+    (nav.superapi.store, "Technical principles of Direct3D-S2"); the reading here is
+    a mean-pool followed by one linear map.  Returns (ktil, vtil), each [H, M, d].
+    """
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    H, d = k.shape[1], k.shape[2]
+    kbar = np.empty((part.M, H, d))
+    vbar = np.empty((part.M, H, d))
+    for b in range(part.M):
+        t = part.tokens(b)
+        kbar[b] = k[t].mean(axis=0)
+        vbar[b] = v[t].mean(axis=0)
+    ktil = np.einsum("bhi,ij->hbj", kbar, np.asarray(wk, dtype=np.float64))
+    vtil = np.einsum("bhi,ij->hbj", vbar, np.asarray(wv, dtype=np.float64))
+    return ktil, vtil
+
+
+def _softmax_rows(s: np.ndarray) -> np.ndarray:
+    s = s - s.max(axis=1, keepdims=True)
+    e = np.exp(s)
+    return e / e.sum(axis=1, keepdims=True)
+
+
+def compressed_block(qb: np.ndarray, ktil_h: np.ndarray, vtil_h: np.ndarray, scale: float):
+    """Compressed branch for the queries of one block and one head.
+
+    Each query attends to every compressed block token (global context; pixal-3d.com
+    "What is Direct3D-S2?").  The block importance vector is the column sum of the
+    probabilities over the query block ("based on the attention scores of the
+    compression module", nav.superapi.store).  Returns (o_c [n,d], sigma [M]).
+    """
+    s = scale * (np.asarray(qb, dtype=np.float64) @ ktil_h.T)
+    p = _softmax_rows(s)
+    return p @ vtil_h, p.sum(axis=0)
+
+
+def select_topk(sigma: np.ndarray, k: int) -> np.ndarray:
+    """The min(k, M) most important blocks (ties to the lower id), ascending, -1 padded."""
+    M = len(sigma)
+    order = np.lexsort((np.arange(M), -np.asarray(sigma, dtype=np.float64)))
+    chosen = np.sort(order[:min(k, M)])
+    out = np.full(k, -1, dtype=np.int64)
+    out[:len(chosen)] = chosen
+    return out
+
+
+def _attend(qb, kj, vj, scale):
+    s = scale * (qb @ kj.T)
+    return _softmax_rows(s) @ vj
+
+
+def selected_block(qb, k_h, v_h, part: Partition, sel_row: np.ndarray, scale: float):
+    """Fine branch: one softmax over all tokens of the selected blocks (nav.superapi.store,
+    "selects important blocks for fine-grained feature extraction")."""
+    blocks = [int(b) for b in sel_row if b >= 0]
+    j = np.concatenate([part.tokens(b) for b in blocks]) if blocks else np.zeros(0, np.int64)
+    return _attend(np.asarray(qb, np.float64), k_h[j], v_h[j], scale)
+
+
+def window_partition(coords, w: int, grid) -> Partition:
+    """Window cells: non-overlapping w^3 cells anchored at the origin (same construction
+    as the block partition, with edge w)."""
+    return partition(coords, w, grid)
+
+
+def window_attention(q, k, v, wpart: Partition, scale: float) -> np.ndarray:
+    """Local window branch: every token attends to all tokens of its own window cell
+    ("injects local features based on local window operations", nav.superapi.store)."""
+    q = np.asarray(q, np.float64)
+    k = np.asarray(k, np.float64)
+    v = np.asarray(v, np.float64)
+    N, H, d = q.shape
+    out = np.empty((N, H, d))
+    for c in range(wpart.M):
+        t = wpart.tokens(c)
+        for h in range(H):
+            out[t, h] = _attend(q[t, h], k[t, h], v[t, h], scale)
+    return out
+
+
+def combine(gates, oc, os_, ow):
+    """Gated aggregation of the three branch outputs (nav.superapi.store: "aggregates the
+    outputs of the three modules based on predicted gating scores")."""
+    g = np.asarray(gates, np.float64)
+    return g[..., 0:1] * oc + g[..., 1:2] * os_ + g[..., 2:3] * ow
+
+
+# --------------------------------------------------------------------------- driver
+def _scale(scale, d):
+    return 1.0 / math.sqrt(d) if (scale is None or scale == 0) else float(scale)
+
+
+def forward_items(inp: dict, items, sel_override=None, scale=None, ktv=None):
+    """Forward outputs for chosen (head, query block) items only.
+
+    Returns a dict keyed by (h, Bq) with the block's sorted rows' outputs:
+      'rows'  the token indices (caller order) of the block, in sorted order
+      'out'   [n, d] combined output      'oc','os','ow' the branch outputs
+      'sigma' [M] importance vector      'sel' [k] selected ids (or the override)
+    plus 'part', 'ktil', 'vtil'.  sel_override maps (h, Bq) -> forced selection.
+    """
+    q = np.asarray(inp["q"], np.float64)
+    k = np.asarray(inp["k"], np.float64)
+    v = np.asarray(inp["v"], np.float64)
+    N, H, d = q.shape
+    sc = _scale(scale, d)
+    part = partition(inp["coords"], inp["block"], inp["grid"])
+    wpart = window_partition(inp["coords"], inp["window"], inp["grid"])
+    if ktv is None:
+        ktil, vtil = pool(k, v, inp["wk"], inp["wv"], part)
+    else:
+        ktil, vtil = ktv
+    g = np.asarray(inp["gates"], np.float64)
+    res = {"part": part, "ktil": ktil, "vtil": vtil}
+    for (h, bq) in items:
+        rows = part.tokens(bq)
+        qb = q[rows, h]
+        oc, sigma = compressed_block(qb, ktil[h], vtil[h], sc)
+        if sel_override is not None and (h, bq) in sel_override:
+            sel = np.asarray(sel_override[(h, bq)], np.int64)
+        else:
+            sel = select_topk(sigma, inp["topk"])
+        os_ = selected_block(qb, k[:, h], v[:, h], part, sel, sc)
+        ow = np.empty_like(oc)
+        cells = wpart.tok2blk[rows]
+        for c in np.unique(cells):
+            m = cells == c
+            t = wpart.tokens(int(c))
+            ow[m] = _attend(qb[m], k[t, h], v[t, h], sc)
+        out = combine(g[rows, h], oc, os_, ow)
+        res[(h, bq)] = {"rows": rows, "out": out, "oc": oc, "os": os_, "ow": ow,
+                        "sigma": sigma, "sel": sel}
+    return res
+
+
+def forward(inp: dict, sel_override=None, scale=None, keep_sigma=True):
+    """Full SSA forward.  Returns dict with 'out' [N,H,d], 'sel' [H,M,k], branch outputs
+    'oc','os','ow' [N,H,d], 'sigma' [H,M,M] (if keep_sigma) and the partition."""
+    q = np.asarray(inp["q"])
+    N, H, d = q.shape
+    part = partition(inp["coords"], inp["block"], inp["grid"])
+    items = [(h, b) for h in range(H) for b in range(part.M)]
+    r = forward_items(inp, items, sel_override=sel_override, scale=scale)
+    out = np.zeros((N, H, d))
+    oc = np.zeros((N, H, d))
+    os_ = np.zeros((N, H, d))
+    ow = np.zeros((N, H, d))
+    sel = np.full((H, part.M, inp["topk"]), -1, np.int64)
+    sigma = np.zeros((H, part.M, part.M)) if keep_sigma else None
+    for (h, b) in items:
+        it = r[(h, b)]
+        rows = it["rows"]
+        out[rows, h] = it["out"]
+        oc[rows, h] = it["oc"]
+        os_[rows, h] = it["os"]
+        ow[rows, h] = it["ow"]
+        sel[h, b] = it["sel"]
+        if keep_sigma:
+            sigma[h, b] = it["sigma"]
+    return {"out": out, "oc": oc, "os": os_, "ow": ow, "sel": sel, "sigma": sigma,
+            "part": part, "ktil": r["ktil"], "vtil": r["vtil"]}
+
+
+# --------------------------------------------------------------------------- backward
+def _attend_bwd(qb, kj, vj, do_x, scale):
+    """Backward of o = softmax(scale q k^T) v for one query set.  Returns dq, dk, dv."""
+    s = scale * (qb @ kj.T)
+    p = _softmax_rows(s)
+    o = p @ vj
+    dv = p.T @ do_x
+    dp = do_x @ vj.T
+    dd = (do_x * o).sum(axis=1, keepdims=True)
+    ds = p * (dp - dd)
+    dq = scale * (ds @ kj)
+    dk = scale * (ds.T @ qb)
+    return dq, dk, dv
+
+
+def backward(inp: dict, sel: np.ndarray, dout: np.ndarray, scale=None):
+    """Analytic float64 backward of the forward above with the selection held fixed.
+
+    Gradients flow into Q, K, V (through all three branches; the compressed branch
+    reaches K and V through the mean pool and W) and into the gates.  sigma and
+    the top-k carry no gradient; W gets none.  Returns dq, dk, dv, dgates.
+    """
+    q = np.asarray(inp["q"], np.float64)
+    k = np.asarray(inp["k"], np.float64)
+    v = np.asarray(inp["v"], np.float64)
+    wk = np.asarray(inp["wk"], np.float64)
+    wv = np.asarray(inp["wv"], np.float64)
+    g = np.asarray(inp["gates"], np.float64)
+    do = np.asarray(dout, np.float64)
+    N, H, d = q.shape
+    sc = _scale(scale, d)
+    part = partition(inp["coords"], inp["block"], inp["grid"])
+    wpart = window_partition(inp["coords"], inp["window"], inp["grid"])
+    ktil, vtil = pool(k, v, wk, wv, part)
+    dq = np.zeros((N, H, d))
+    dk = np.zeros((N, H, d))
+    dv = np.zeros((N, H, d))
+    dg = np.zeros((N, H, 3))
+    dktil = np.zeros_like(ktil)
+    dvtil = np.zeros_like(vtil)
+    for h in range(H):
+        for b in range(part.M):
+            rows = part.tokens(b)
+            qb = q[rows, h]
+            # compressed branch
+            s = sc * (qb @ ktil[h].T)
+            p = _softmax_rows(s)
+            oc = p @ vtil[h]
+            dg[rows, h, 0] = (do[rows, h] * oc).sum(1)
+            dqc, dkc, dvc = _attend_bwd(qb, ktil[h], vtil[h], g[rows, h, 0:1] * do[rows, h], sc)
+            dq[rows, h] += dqc
+            dktil[h] += dkc
+            dvtil[h] += dvc
+            # selected branch
+            blocks = [int(x) for x in sel[h, b] if x >= 0]
+            j = np.concatenate([part.tokens(x) for x in blocks])
+            os_ = _attend(qb, k[j, h], v[j, h], sc)
+            dg[rows, h, 1] = (do[rows, h] * os_).sum(1)
+            dqs, dks, dvs = _attend_bwd(qb, k[j, h], v[j, h], g[rows, h, 1:2] * do[rows, h], sc)
+            dq[rows, h] += dqs
+            np.add.at(dk[:, h], j, dks)
+            np.add.at(dv[:, h], j, dvs)
+        # window branch
+        for c in range(wpart.M):
+            t = wpart.tokens(c)
+            ow = _attend(q[t, h], k[t, h], v[t, h], sc)
+            dg[t, h, 2] = (do[t, h] * ow).sum(1)
+            dqw, dkw, dvw = _attend_bwd(q[t, h], k[t, h], v[t, h], g[t, h, 2:3] * do[t, h], sc)
+            dq[t, h] += dqw
+            dk[t, h] += dkw
+            dv[t, h] += dvw
+    # through the projection and the mean pool
+    for b in range(part.M):
+        t = part.tokens(b)
+        n = len(t)
+        dk[t] += (dktil[:, b] @ wk.T)[None] / n
+        dv[t] += (dvtil[:, b] @ wv.T)[None] / n
+    return dq, dk, dv, dg
+
+
+# --------------------------------------------------------------------------- textbook
+def sdpa_dense(q, k, v, scale):
+    """Textbook dense softmax attention per head via torch's float64 CPU SDPA (a library
+    routine used only by pins that reduce a branch to full attention)."""
+    import torch
+    qt = torch.from_numpy(np.ascontiguousarray(np.asarray(q, np.float64).transpose(1, 0, 2)))
+    kt = torch.from_numpy(np.ascontiguousarray(np.asarray(k, np.float64).transpose(1, 0, 2)))
+    vt = torch.from_numpy(np.ascontiguousarray(np.asarray(v, np.float64).transpose(1, 0, 2)))
+    o = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, scale=scale)
+    return o.numpy().transpose(1, 0, 2)
