@@ -1,0 +1,406 @@
+// Block partition of a voxel coordinate set on the GPU.
+//
+// The pages state that SSA partitions its input tokens by their 3D coordinates
+// (nav.superapi.store "Direct3D-S2", section "Technical principles of
+// Direct3D-S2").  Here a block is the B^3 cube floor(c / B); tokens are sorted by
+// the x-major block key with a stable LSD radix sort (8-bit digits, one tile of
+// 256 keys per workgroup, in-tile ranks from wave ballots), then run boundaries
+// give the segment offsets.  The same kernels group blocks into window cells and
+// order blocks longest-first for load balance.
+#include <hip/hip_runtime.h>
+#include <string.h>
+#include <algorithm>
+#include "ssa_internal.h"
+
+namespace {
+
+constexpr int RTILE = 256;   // radix tile: one key per thread
+constexpr int STILE = 1024;  // segment-scan tile: 4 elements per thread
+
+__global__ void k_block_keys(const int32_t* __restrict__ coords, int64_t n, int3 grid, int B,
+                             int3 dims, uint32_t* __restrict__ keys, int32_t* __restrict__ vals,
+                             int32_t* __restrict__ err) {
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  int x = coords[3 * i], y = coords[3 * i + 1], z = coords[3 * i + 2];
+  bool ok = x >= 0 && y >= 0 && z >= 0 && x < grid.x && y < grid.y && z < grid.z;
+  if (!ok) {
+    atomicOr(err, 1);
+    x = y = z = 0;
+  }
+  uint32_t bx = x / B, by = y / B, bz = z / B;
+  keys[i] = (bx * (uint32_t)dims.y + by) * (uint32_t)dims.z + bz;
+  vals[i] = (int32_t)i;
+}
+
+// Per tile: stable rank of every key among equal digits, and the tile's digit histogram
+// stored digit-major (hist[digit * tiles + tile]).
+__global__ __launch_bounds__(RTILE) void k_radix_hist(const uint32_t* __restrict__ keys, int n,
+                                                      int shift, int32_t* __restrict__ rank,
+                                                      int32_t* __restrict__ hist, int tiles) {
+  __shared__ int32_t wcount[RTILE / 64][256];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int j = tid; j < (RTILE / 64) * 256; j += RTILE) (&wcount[0][0])[j] = 0;
+  __syncthreads();
+  const int i = blockIdx.x * RTILE + tid;
+  const bool valid = i < n;
+  const uint32_t digit = valid ? ((keys[i] >> shift) & 255u) : 0u;
+  // lanes holding the same digit: AND of per-bit agreement masks
+  uint64_t same = __ballot(valid);
+  for (int b = 0; b < 8; ++b) {
+    uint64_t m = __ballot(valid && ((digit >> b) & 1u));
+    same &= ((digit >> b) & 1u) ? m : ~m;
+  }
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  const int rw = __popcll(same & below);
+  if (valid && rw == 0) wcount[wave][digit] = __popcll(same);
+  __syncthreads();
+  if (valid) {
+    int r = rw;
+    for (int w = 0; w < wave; ++w) r += wcount[w][digit];
+    rank[i] = r;
+  }
+  {
+    const int d = tid;  // RTILE == 256 digits
+    int tot = 0;
+    for (int w = 0; w < RTILE / 64; ++w) tot += wcount[w][d];
+    hist[(int64_t)d * tiles + blockIdx.x] = tot;
+  }
+}
+
+// Exclusive scan of `len` ints in place, one workgroup of 1024 threads.
+__global__ __launch_bounds__(1024) void k_scan_single(int32_t* __restrict__ a, int len,
+                                                      int32_t* __restrict__ total) {
+  __shared__ int32_t part[1024];
+  const int tid = threadIdx.x;
+  const int per = (len + 1023) / 1024;
+  const int lo = min(len, tid * per), hi = min(len, lo + per);
+  int s = 0;
+  for (int j = lo; j < hi; ++j) s += a[j];
+  part[tid] = s;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    int t = (tid >= off) ? part[tid - off] : 0;
+    __syncthreads();
+    part[tid] += t;
+    __syncthreads();
+  }
+  int run = part[tid] - s;
+  for (int j = lo; j < hi; ++j) {
+    int x = a[j];
+    a[j] = run;
+    run += x;
+  }
+  if (tid == 1023 && total) *total = part[1023];
+}
+
+__global__ __launch_bounds__(RTILE) void k_radix_scatter(
+    const uint32_t* __restrict__ kin, const int32_t* __restrict__ vin, int n, int shift,
+    const int32_t* __restrict__ rank, const int32_t* __restrict__ hist, int tiles,
+    uint32_t* __restrict__ kout, int32_t* __restrict__ vout) {
+  const int i = blockIdx.x * RTILE + threadIdx.x;
+  if (i >= n) return;
+  const uint32_t key = kin[i];
+  const uint32_t digit = (key >> shift) & 255u;
+  const int dst = hist[(int64_t)digit * tiles + blockIdx.x] + rank[i];
+  kout[dst] = key;
+  vout[dst] = vin[i];
+}
+
+// Segment boundaries of a sorted key array: count run starts per tile.
+__global__ __launch_bounds__(256) void k_seg_count(const uint32_t* __restrict__ keys, int n,
+                                                   int32_t* __restrict__ tile_cnt) {
+  __shared__ int32_t red[256];
+  const int base = blockIdx.x * STILE + threadIdx.x * 4;
+  int c = 0;
+  for (int j = 0; j < 4; ++j) {
+    int r = base + j;
+    if (r < n) c += (r == 0 || keys[r] != keys[r - 1]);
+  }
+  red[threadIdx.x] = c;
+  __syncthreads();
+  for (int off = 128; off > 0; off >>= 1) {
+    if (threadIdx.x < off) red[threadIdx.x] += red[threadIdx.x + off];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) tile_cnt[blockIdx.x] = red[0];
+}
+
+// Emit segment ids: seg_off[id] = start, seg_key[id] = key, elem_seg[vals[r]] = id.
+__global__ __launch_bounds__(256) void k_seg_emit(const uint32_t* __restrict__ keys,
+                                                  const int32_t* __restrict__ vals, int n,
+                                                  const int32_t* __restrict__ tile_base,
+                                                  int32_t* __restrict__ seg_off,
+                                                  int32_t* __restrict__ seg_key,
+                                                  int32_t* __restrict__ elem_seg) {
+  __shared__ int32_t part[256];
+  const int tid = threadIdx.x;
+  const int base = blockIdx.x * STILE + tid * 4;
+  int f[4], c = 0;
+  for (int j = 0; j < 4; ++j) {
+    int r = base + j;
+    f[j] = (r < n) && (r == 0 || keys[r] != keys[r - 1]);
+    c += f[j];
+  }
+  part[tid] = c;
+  __syncthreads();
+  for (int off = 1; off < 256; off <<= 1) {
+    int t = (tid >= off) ? part[tid - off] : 0;
+    __syncthreads();
+    part[tid] += t;
+    __syncthreads();
+  }
+  int id = tile_base[blockIdx.x] + part[tid] - c - 1;  // id of the run before this thread's first
+  for (int j = 0; j < 4; ++j) {
+    int r = base + j;
+    if (r >= n) break;
+    id += f[j];
+    if (f[j]) {
+      seg_off[id] = r;
+      if (seg_key) seg_key[id] = (int32_t)keys[r];
+    }
+    if (elem_seg) elem_seg[vals[r]] = id;
+    if (r == n - 1) seg_off[id + 1] = n;
+  }
+}
+
+__global__ void k_block_stats(const int32_t* __restrict__ blk_off, int M, int n,
+                              uint32_t* __restrict__ lpt_key, int32_t* __restrict__ ids,
+                              int32_t* __restrict__ max_rows) {
+  int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= M) return;
+  int rows = blk_off[b + 1] - blk_off[b];
+  atomicMax(max_rows, rows);
+  lpt_key[b] = (uint32_t)(n - rows);
+  ids[b] = b;
+}
+
+__global__ void k_cell_keys(const int32_t* __restrict__ blk_key, int M, int3 dims, int ratio,
+                            bool single, int3 cdims, uint32_t* __restrict__ ckey,
+                            int32_t* __restrict__ ids) {
+  int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= M) return;
+  uint32_t key = (uint32_t)blk_key[b];
+  uint32_t bz = key % dims.z, t = key / dims.z;
+  uint32_t by = t % dims.y, bx = t / dims.y;
+  uint32_t c = 0;
+  if (!single) {
+    uint32_t cx = bx / ratio, cy = by / ratio, cz = bz / ratio;
+    c = (cx * cdims.y + cy) * cdims.z + cz;
+  }
+  ckey[b] = c;
+  ids[b] = b;
+}
+
+__global__ void k_identity_cells(int M, int32_t* blk_cell, int32_t* cell_off, int32_t* cell_blk) {
+  int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b > M) return;
+  cell_off[b] = b;
+  if (b < M) {
+    blk_cell[b] = b;
+    cell_blk[b] = b;
+  }
+}
+
+inline int bits_for(uint64_t maxval) {
+  int b = 0;
+  while (b < 32 && (maxval >> b) != 0) ++b;
+  return b;
+}
+
+// Stable LSD radix sort of (key, val) pairs; returns which buffers hold the result.
+hipError_t radix_sort(uint32_t*& ka, int32_t*& va, uint32_t*& kb, int32_t*& vb, int n, int nbits,
+                      int32_t* rank, int32_t* hist, hipStream_t s) {
+  const int tiles = (n + RTILE - 1) / RTILE;
+  for (int shift = 0; shift < nbits; shift += 8) {
+    hipLaunchKernelGGL(k_radix_hist, dim3(tiles), dim3(RTILE), 0, s, ka, n, shift, rank, hist, tiles);
+    hipLaunchKernelGGL(k_scan_single, dim3(1), dim3(1024), 0, s, hist, tiles * 256, (int32_t*)nullptr);
+    hipLaunchKernelGGL(k_radix_scatter, dim3(tiles), dim3(RTILE), 0, s, ka, va, n, shift, rank, hist,
+                       tiles, kb, vb);
+    std::swap(ka, kb);
+    std::swap(va, vb);
+  }
+  return hipGetLastError();
+}
+
+hipError_t segments(const uint32_t* keys, const int32_t* vals, int n, int32_t* tile_cnt,
+                    int32_t* total, int32_t* seg_off, int32_t* seg_key, int32_t* elem_seg,
+                    hipStream_t s) {
+  const int tiles = (n + STILE - 1) / STILE;
+  hipLaunchKernelGGL(k_seg_count, dim3(tiles), dim3(256), 0, s, keys, n, tile_cnt);
+  hipLaunchKernelGGL(k_scan_single, dim3(1), dim3(1024), 0, s, tile_cnt, tiles, total);
+  hipLaunchKernelGGL(k_seg_emit, dim3(tiles), dim3(256), 0, s, keys, vals, n, tile_cnt, seg_off,
+                     seg_key, elem_seg);
+  return hipGetLastError();
+}
+
+bool window_supported(const int32_t grid[3], int B, int w, bool* single) {
+  *single = w >= grid[0] && w >= grid[1] && w >= grid[2];
+  return *single || (w % B == 0);
+}
+
+}  // namespace
+
+size_t plan_carve(Carver& c, int64_t n, PlanWs* w) {
+  const int64_t n1 = n > 0 ? n : 1;
+  const int64_t tiles = (n1 + RTILE - 1) / RTILE;
+  PlanWs t;
+  t.perm = c.take<int32_t>(n1);
+  t.blk_off = c.take<int32_t>(n1 + 1);
+  t.blk_key = c.take<int32_t>(n1);
+  t.tok2blk = c.take<int32_t>(n1);
+  t.blk_cell = c.take<int32_t>(n1);
+  t.cell_off = c.take<int32_t>(n1 + 1);
+  t.cell_blk = c.take<int32_t>(n1);
+  t.lpt = c.take<int32_t>(n1);
+  t.key_a = c.take<uint32_t>(n1);
+  t.key_b = c.take<uint32_t>(n1);
+  t.val_a = c.take<int32_t>(n1);
+  t.val_b = c.take<int32_t>(n1);
+  t.rank = c.take<int32_t>(n1);
+  t.hist = c.take<int32_t>(tiles * 256);
+  t.tile_cnt = c.take<int32_t>((n1 + STILE - 1) / STILE + 1);
+  t.counters = c.take<int32_t>(8);
+  t.cell_key = c.take<int32_t>(n1);
+  if (w) *w = t;
+  return c.off;
+}
+
+extern "C" size_t ssa_plan_workspace_size(int64_t n, const int32_t grid[3], int32_t block,
+                                          int32_t window) {
+  (void)grid; (void)block; (void)window;
+  if (n < 0) return 0;
+  Carver c(nullptr);
+  return plan_carve(c, n, nullptr) + 256;
+}
+
+extern "C" ssa_status ssa_plan_create(const int32_t* coords, int64_t n, const int32_t grid[3],
+                                      int32_t block, int32_t window, void* ws, size_t ws_bytes,
+                                      hipStream_t stream, ssa_plan* out) {
+  if (!out || !grid) return SSA_ERR_INVALID_ARG;
+  *out = nullptr;
+  if (n < 0 || block < 1 || window < 1) return SSA_ERR_INVALID_ARG;
+  if (grid[0] < 1 || grid[1] < 1 || grid[2] < 1) return SSA_ERR_INVALID_ARG;
+  if (n > 0 && !coords) return SSA_ERR_INVALID_ARG;
+  if (n >= (int64_t)1 << 31) return SSA_ERR_UNSUPPORTED;
+  int32_t dims[3];
+  uint64_t nblocks = 1;
+  for (int a = 0; a < 3; ++a) {
+    dims[a] = (grid[a] + block - 1) / block;
+    nblocks *= (uint64_t)dims[a];
+  }
+  if (nblocks > (1ull << 31)) return SSA_ERR_UNSUPPORTED;
+  bool single = false;
+  if (!window_supported(grid, block, window, &single)) return SSA_ERR_UNSUPPORTED;
+  if (!ws) return SSA_ERR_WORKSPACE;
+  if (ws_bytes < ssa_plan_workspace_size(n, grid, block, window)) return SSA_ERR_WORKSPACE;
+
+  Carver c(ws);
+  c.off = (256 - (reinterpret_cast<uintptr_t>(ws) & 255)) & 255;
+  PlanWs w;
+  plan_carve(c, n, &w);
+
+  ssa_plan_s* p = new ssa_plan_s();
+  p->magic = SSA_PLAN_MAGIC;
+  p->n = n;
+  memcpy(p->grid, grid, sizeof(p->grid));
+  memcpy(p->dims, dims, sizeof(p->dims));
+  p->block = block;
+  p->window = window;
+  p->window_is_block = (window == block) || (single && nblocks == 1);
+  p->perm = w.perm; p->blk_off = w.blk_off; p->blk_key = w.blk_key; p->tok2blk = w.tok2blk;
+  p->blk_cell = w.blk_cell; p->cell_off = w.cell_off; p->cell_blk = w.cell_blk; p->lpt = w.lpt;
+  p->M = 0; p->ncells = 0; p->max_rows = 0;
+  if (n == 0) {
+    *out = p;
+    return SSA_OK;
+  }
+  const int ni = (int)n;
+  int32_t host_cnt[8];
+  auto fail = [&](ssa_status st) { delete p; return st; };
+  if (hipMemsetAsync(w.counters, 0, 8 * sizeof(int32_t), stream) != hipSuccess) return fail(SSA_ERR_HIP);
+  hipLaunchKernelGGL(k_block_keys, dim3((ni + 255) / 256), dim3(256), 0, stream, coords, n,
+                     make_int3(grid[0], grid[1], grid[2]), block, make_int3(dims[0], dims[1], dims[2]),
+                     w.key_a, w.val_a, w.counters + 7);
+  uint32_t *ka = w.key_a, *kb = w.key_b;
+  int32_t *va = w.val_a, *vb = w.val_b;
+  if (radix_sort(ka, va, kb, vb, ni, bits_for(nblocks - 1), w.rank, w.hist, stream) != hipSuccess)
+    return fail(SSA_ERR_HIP);
+  if (hipMemcpyAsync(w.perm, va, n * sizeof(int32_t), hipMemcpyDeviceToDevice, stream) != hipSuccess)
+    return fail(SSA_ERR_HIP);
+  if (segments(ka, va, ni, w.tile_cnt, w.counters + 0, w.blk_off, w.blk_key, w.tok2blk, stream) !=
+      hipSuccess)
+    return fail(SSA_ERR_HIP);
+  if (hipMemcpyAsync(host_cnt, w.counters, sizeof(host_cnt), hipMemcpyDeviceToHost, stream) != hipSuccess ||
+      hipStreamSynchronize(stream) != hipSuccess)
+    return fail(SSA_ERR_HIP);
+  if (host_cnt[7]) return fail(SSA_ERR_COORD_RANGE);
+  const int M = host_cnt[0];
+  p->M = M;
+
+  // longest-first block order (stable: ties keep ascending block id)
+  hipLaunchKernelGGL(k_block_stats, dim3((M + 255) / 256), dim3(256), 0, stream, w.blk_off, M, ni,
+                     w.key_a, w.val_a, w.counters + 1);
+  ka = w.key_a; kb = w.key_b; va = w.val_a; vb = w.val_b;
+  if (radix_sort(ka, va, kb, vb, M, bits_for((uint64_t)n), w.rank, w.hist, stream) != hipSuccess)
+    return fail(SSA_ERR_HIP);
+  if (hipMemcpyAsync(w.lpt, va, M * sizeof(int32_t), hipMemcpyDeviceToDevice, stream) != hipSuccess)
+    return fail(SSA_ERR_HIP);
+
+  // window cells as groups of blocks
+  if (p->window_is_block) {
+    hipLaunchKernelGGL(k_identity_cells, dim3((M + 256) / 256), dim3(256), 0, stream, M, w.blk_cell,
+                       w.cell_off, w.cell_blk);
+  } else {
+    const int ratio = single ? 1 : window / block;
+    int3 cd = make_int3(1, 1, 1);
+    if (!single)
+      cd = make_int3((dims[0] + ratio - 1) / ratio, (dims[1] + ratio - 1) / ratio,
+                     (dims[2] + ratio - 1) / ratio);
+    uint64_t ncmax = (uint64_t)cd.x * cd.y * cd.z;
+    hipLaunchKernelGGL(k_cell_keys, dim3((M + 255) / 256), dim3(256), 0, stream, w.blk_key, M,
+                       make_int3(dims[0], dims[1], dims[2]), ratio, single, cd, w.key_a, w.val_a);
+    ka = w.key_a; kb = w.key_b; va = w.val_a; vb = w.val_b;
+    if (radix_sort(ka, va, kb, vb, M, bits_for(ncmax - 1), w.rank, w.hist, stream) != hipSuccess)
+      return fail(SSA_ERR_HIP);
+    if (hipMemcpyAsync(w.cell_blk, va, M * sizeof(int32_t), hipMemcpyDeviceToDevice, stream) != hipSuccess)
+      return fail(SSA_ERR_HIP);
+    if (segments(ka, va, M, w.tile_cnt, w.counters + 2, w.cell_off, nullptr, w.blk_cell, stream) !=
+        hipSuccess)
+      return fail(SSA_ERR_HIP);
+  }
+  if (hipMemcpyAsync(host_cnt, w.counters, sizeof(host_cnt), hipMemcpyDeviceToHost, stream) != hipSuccess ||
+      hipStreamSynchronize(stream) != hipSuccess)
+    return fail(SSA_ERR_HIP);
+  p->max_rows = host_cnt[1];
+  p->ncells = p->window_is_block ? M : host_cnt[2];
+  *out = p;
+  return SSA_OK;
+}
+
+extern "C" ssa_status ssa_plan_get_info(ssa_plan p, ssa_plan_info_t* info) {
+  if (!p || p->magic != SSA_PLAN_MAGIC) return SSA_ERR_BAD_PLAN;
+  if (!info) return SSA_ERR_INVALID_ARG;
+  info->n = p->n;
+  info->num_blocks = p->M;
+  info->num_cells = p->ncells;
+  info->block = p->block;
+  info->window = p->window;
+  info->max_block_rows = p->max_rows;
+  info->perm = p->perm;
+  info->blk_off = p->blk_off;
+  info->blk_key = p->blk_key;
+  info->tok2blk = p->tok2blk;
+  info->blk_cell = p->blk_cell;
+  info->cell_off = p->cell_off;
+  info->cell_blk = p->cell_blk;
+  info->lpt = p->lpt;
+  return SSA_OK;
+}
+
+extern "C" void ssa_plan_destroy(ssa_plan p) {
+  if (p && p->magic == SSA_PLAN_MAGIC) {
+    p->magic = 0;
+    delete p;
+  }
+}

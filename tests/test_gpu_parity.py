@@ -1,0 +1,172 @@
+"""GPU parity: the HIP library through its C ABI against the float64 oracle."""
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+from brute import tiny_case
+from parity import check_items, check_selection, compare, gpu_forward, to_dev
+
+pytestmark = pytest.mark.gpu
+
+FULL = ["sphere2k", "torus20k", "shells80k", "shells110k"]
+_cache = {}
+
+
+def _workload(name):
+    if name not in _cache:
+        _cache[name] = W.make_inputs(name)
+    return _cache[name]
+
+
+def _plan_arrays(plan):
+    return {k: v.cpu().numpy().astype(np.int64) for k, v in plan.arrays().items()}
+
+
+# ------------------------------------------------------------------ plan
+def _check_plan(inp, plan):
+    ref = oracle.partition(inp["coords"], inp["block"], inp["grid"])
+    a = _plan_arrays(plan)
+    assert plan.num_blocks == ref.M
+    np.testing.assert_array_equal(a["perm"], ref.perm)
+    np.testing.assert_array_equal(a["blk_off"], ref.blk_off)
+    np.testing.assert_array_equal(a["blk_key"], ref.blk_key)
+    np.testing.assert_array_equal(a["tok2blk"], ref.tok2blk)
+    sizes = np.diff(ref.blk_off)
+    assert plan.max_block_rows == sizes.max()
+    np.testing.assert_array_equal(a["lpt"], np.lexsort((np.arange(ref.M), -sizes)))
+    # window cells: blocks grouped by cell, ascending inside a cell
+    wp = oracle.window_partition(inp["coords"], inp["window"], inp["grid"])
+    cell_of_block = wp.tok2blk[ref.perm[ref.blk_off[:-1]]]
+    assert plan.num_cells == wp.M
+    np.testing.assert_array_equal(a["blk_cell"], cell_of_block)
+    for cidx in range(wp.M):
+        blocks = a["cell_blk"][a["cell_off"][cidx]:a["cell_off"][cidx + 1]]
+        np.testing.assert_array_equal(blocks, np.nonzero(cell_of_block == cidx)[0])
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_plan_full_workloads(name):
+    import spatial_sparse_attention_amd as ssa
+    wl, inp = _workload(name)
+    dev = to_dev(inp)
+    plan = ssa.Plan(dev["coords"], inp["grid"], inp["block"], inp["window"])
+    _check_plan(inp, plan)
+
+
+@pytest.mark.parametrize("N,G,B,w", [(500, 16, 1, 1), (3000, 40, 3, 6), (4000, 64, 5, 64),
+                                     (700, 12, 2, 8), (1, 4, 2, 2), (900, 10, 16, 16),
+                                     (2500, 30, 4, 100)])
+def test_plan_random(N, G, B, w):
+    import spatial_sparse_attention_amd as ssa
+    rng = np.random.default_rng(N + G)
+    coords = rng.integers(0, G, (N, 3)).astype(np.int32)   # duplicates allowed
+    inp = {"coords": coords, "grid": G, "block": B, "window": w}
+    import torch
+    plan = ssa.Plan(torch.from_numpy(coords).cuda(), G, B, w)
+    _check_plan(inp, plan)
+
+
+def test_plan_rejects_out_of_grid():
+    import torch
+    import spatial_sparse_attention_amd as ssa
+    coords = torch.tensor([[0, 0, 0], [3, 8, 1]], dtype=torch.int32, device="cuda")
+    with pytest.raises(ssa.SSAError) as e:
+        ssa.Plan(coords, 8, 2, 2)
+    assert e.value.status == 4
+
+
+# ------------------------------------------------------------------ forward, small and exhaustive
+SMALL = [  # (N, G, H, d, B, w, k, dtype)
+    (300, 12, 2, 32, 2, 2, 3, "f32"),
+    (1500, 20, 2, 64, 4, 4, 4, "f16"),
+    (1500, 20, 2, 96, 4, 4, 4, "f16"),
+    (1200, 16, 2, 128, 4, 8, 2, "bf16"),
+    (2000, 24, 1, 96, 3, 6, 5, "f16"),
+    (800, 10, 2, 64, 2, 100, 100, "bf16"),   # every block selected; one window cell
+    (700, 9, 1, 32, 1, 1, 6, "f32"),         # single-token blocks
+    (400, 8, 2, 96, 8, 8, 3, "f16"),         # one block holds every token
+    (512, 8, 1, 64, 8, 8, 2, "f16"),         # one full 8^3 block (512 rows)
+    (1, 4, 1, 32, 2, 2, 4, "f32"),           # one token
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[f"{c[7]}_d{c[3]}_B{c[4]}_w{c[5]}_k{c[6]}_N{c[0]}" for c in SMALL])
+def test_forward_small(case):
+    N, G, H, d, B, w, k, dt = case
+    rng = np.random.default_rng(N * 7 + d)
+    if N == 512 and G == 8:
+        flat = np.arange(512)
+        coords = np.stack(np.unravel_index(rng.permutation(flat), (8, 8, 8)), -1).astype(np.int32)
+        c = tiny_case(rng, N, G, H, d)
+        c["coords"] = coords
+    else:
+        c = tiny_case(rng, N, G, H, d)
+    inp = W.random_inputs(c["coords"], H, d, dt, seed=N + d, grid=G)
+    inp.update(block=B, window=w, topk=k)
+    out, sel, plan = gpu_forward(inp)
+    ref = oracle.forward(inp)
+    M = ref["part"].M
+    items = [(h, b) for h in range(H) for b in range(M)]
+    near = {}
+    for (h, b) in items:
+        if check_selection(ref["sigma"][h, b], k, sel[h, b]) == "near":
+            near[(h, b)] = sel[h, b]
+    if near:
+        ref = oracle.forward(inp, sel_override=near)
+    compare(out, ref["out"], dt, "all outputs")
+
+
+def test_forward_sphere2k_all_items():
+    wl, inp = _workload("sphere2k")
+    out, sel, plan = gpu_forward(inp)
+    items = [(h, b) for h in range(wl.heads) for b in range(plan.num_blocks)]
+    counts = check_items(inp, out, sel, items)
+    assert counts["exact"] + counts["near"] == len(items)
+
+
+@pytest.mark.parametrize("name", ["torus20k", "shells80k", "shells110k"])
+def test_forward_full_sampled(name):
+    wl, inp = _workload(name)
+    out, sel, plan = gpu_forward(inp)
+    a = _plan_arrays(plan)
+    sizes = np.diff(a["blk_off"])
+    rng = np.random.default_rng(0)
+    M = plan.num_blocks
+    big = list(np.argsort(-sizes, kind="stable")[:3])
+    small = list(np.argsort(sizes, kind="stable")[:3])
+    rand = list(rng.choice(M, 10, replace=False))
+    items = sorted({(int(rng.integers(0, wl.heads)), int(b)) for b in big + small + rand})
+    check_items(inp, out, sel, items)
+    # properties over every output: finite, every selection row valid
+    assert np.isfinite(out).all()
+    kk = min(wl.topk, M)
+    assert (sel[:, :, :kk] >= 0).all() and (sel[:, :, kk:] == -1).all()
+    assert (np.diff(sel[:, :, :kk], axis=2) > 0).all()
+
+
+def test_forward_deterministic():
+    wl, inp = _workload("torus20k")
+    o1, s1, plan = gpu_forward(inp)
+    o2, s2, _ = gpu_forward(inp, plan=plan)
+    np.testing.assert_array_equal(s1, s2)
+    np.testing.assert_array_equal(o1, o2)
+
+
+def test_forward_within_block_permutation():
+    rng = np.random.default_rng(3)
+    c = tiny_case(rng, 1500, 20, 2, 64)
+    inp = W.random_inputs(c["coords"], 2, 64, "f16", seed=9, grid=20)
+    inp.update(block=4, window=4, topk=4)
+    o1, s1, _ = gpu_forward(inp)
+    part = oracle.partition(inp["coords"], 4, 20)
+    pi = np.arange(1500)
+    for b in range(part.M):
+        t = part.tokens(b)
+        pi[t] = rng.permutation(t)
+    inp2 = dict(inp)
+    for key in ("coords", "q", "k", "v", "gates"):
+        inp2[key] = inp[key][pi]
+    o2, s2, _ = gpu_forward(inp2)
+    np.testing.assert_array_equal(s1, s2)
+    np.testing.assert_allclose(o2, o1[pi], atol=2e-3)
