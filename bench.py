@@ -1,0 +1,177 @@
+"""Benchmark: SSA forward on one MI355X at the 80k-voxel sparse-transformer shape.
+
+Workload "shells80k": 80,000 voxels from a seeded union of six ellipsoid shells in a
+64^3 grid (about 30% occupancy, 1..512 tokens per 8^3 block), 22 heads x 96, fp16,
+block 8^3, top-k 8, window 8^3 -- the shape of the first refinement pass on the
+Sparc3D/Hi3D pipeline page ("How the pipeline works", "Stage 3").
+
+A step is one pass of the whole path over resident inputs: the block partition
+(ssa_plan_create) and the forward's three stages (pooled keys, compressed branch
++ selection, selected/window branches + gated combine).  HIP events on the launch
+stream time every stage of every step.  The CPU baseline is the float64 oracle
+timed on a bounded sample of the same workload on the host.
+Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu]
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+WORKLOAD = "shells80k"
+PEAK_F16_TFLOPS = 2500.0      # MI355X dense fp16/bf16 MFMA
+PEAK_F32_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0
+
+
+def attended_pairs(plan_arrays, sel, window_is_block):
+    """Per-head sum over queries of (M + |selected keys| + |window keys|)."""
+    blk_off = plan_arrays["blk_off"].astype(np.int64)
+    sizes = np.diff(blk_off)
+    M = len(sizes)
+    H = sel.shape[0]
+    sel_keys = np.where(sel >= 0, sizes[np.clip(sel, 0, M - 1)], 0).sum(axis=2)  # [H, M]
+    cell_off = plan_arrays["cell_off"].astype(np.int64)
+    cell_blk = plan_arrays["cell_blk"].astype(np.int64)
+    cell_sizes = np.add.reduceat(sizes[cell_blk], cell_off[:-1]) if M else np.zeros(0)
+    win_keys = cell_sizes[plan_arrays["blk_cell"].astype(np.int64)]           # [M]
+    per_head = (sizes[None, :] * (M + sel_keys + win_keys[None, :])).sum(axis=1)
+    return per_head, sizes
+
+
+def cpu_baseline(inp, heads_sample):
+    """The float64 oracle, as it stands, on `heads_sample` heads of the workload."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    t0 = time.perf_counter()
+    part = oracle.partition(inp["coords"], inp["block"], inp["grid"])
+    ktv = oracle.pool(inp["k"], inp["v"], inp["wk"], inp["wv"], part)
+    items = [(h, b) for h in range(heads_sample) for b in range(part.M)]
+    oracle.forward_items(inp, items, ktv=ktv)
+    dt = time.perf_counter() - t0
+    H = inp["q"].shape[1]
+    N = inp["q"].shape[0]
+    return {"value": N * (heads_sample / H) / dt, "unit": "tokens/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"partition + pooling of all {H} heads, then all {part.M} blocks of "
+                      f"{heads_sample} of {H} heads ({dt:.1f} s); tokens/s scaled by the head fraction"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-heads", type=int, default=4)
+    ap.add_argument("--workload", default=WORKLOAD)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: SSA shards by head with no exchange, and this "
+              "build runs and reports the single-GPU path (use --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import workloads as W
+    import spatial_sparse_attention_amd as ssa
+
+    wl, inp = W.make_inputs(args.workload)
+    tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[wl.dtype]
+    dev = {k: torch.from_numpy(np.ascontiguousarray(inp[k])).cuda().to(tdt)
+           for k in ("q", "k", "v", "wk", "wv", "gates")}
+    coords = torch.from_numpy(inp["coords"]).cuda()
+    N, H, d = dev["q"].shape
+    stream = torch.cuda.current_stream()
+
+    plan = ssa.Plan(coords, wl.grid, wl.block, wl.window)
+    out = torch.empty_like(dev["q"])
+    sel = torch.empty((H, plan.num_blocks, wl.topk), dtype=torch.int32, device="cuda")
+    ws = torch.empty(ssa.forward_workspace_size(plan, tdt, H, d, wl.topk), dtype=torch.uint8,
+                     device="cuda")
+
+    def step(evs=None):
+        rec = (lambda i: evs[i].record(stream)) if evs else (lambda i: None)
+        rec(0)
+        p = ssa.Plan(coords, wl.grid, wl.block, wl.window)
+        rec(1)
+        for si, stage in enumerate((ssa.STAGE_POOL, ssa.STAGE_SELECT, ssa.STAGE_ATTEND)):
+            ssa.forward(p, dev["q"], dev["k"], dev["v"], dev["wk"], dev["wv"], dev["gates"],
+                        wl.topk, 0.0, out=out, sel_out=sel, ws=ws, stages=stage)
+            rec(2 + si)
+        return p
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(evs[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    names = ["plan", "pool", "select", "attend"]
+    stage_ms = {nm: float(np.mean([evs[s][i].elapsed_time(evs[s][i + 1]) for s in range(args.steps)]))
+                for i, nm in enumerate(names)}
+    ms_step = wall * 1e3 / args.steps
+    fwd_ms = stage_ms["pool"] + stage_ms["select"] + stage_ms["attend"]
+
+    # credited work: 4 d FLOPs per attended (query, key, head) pair over the three branches
+    arrays = {k: v.cpu().numpy() for k, v in plan.arrays().items()}
+    per_head, sizes = attended_pairs(arrays, sel.cpu().numpy(), plan.num_cells == plan.num_blocks)
+    flops = 4.0 * d * float(per_head.sum())
+    M = plan.num_blocks
+    cmp_flops = 4.0 * d * H * N * M               # the compressed branch alone
+    es = 4 if wl.dtype == "f32" else 2
+    alg_bytes = N * H * es * (4 * d + 3) + 12 * N + 2 * d * d * es
+    peak = PEAK_F32_TFLOPS if wl.dtype == "f32" else PEAK_F16_TFLOPS
+    sel_tflops = cmp_flops / (stage_ms["select"] * 1e-3) / 1e12
+    res = {
+        "metric": "SSA fwd tokens/s and TFLOP/s (% MFMA peak) at 80k voxels, 22h×96d fp16",
+        "value": N / (ms_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic",
+        "config": {"workload": f"{wl.name}: {N} voxels, union of ellipsoid shells in a {wl.grid}^3 grid, "
+                               f"block {wl.block}^3, top-k {wl.topk}, window {wl.window}^3, "
+                               f"{H} heads x {d}, {wl.dtype}",
+                   "N": N, "heads": H, "dim": d, "block": wl.block, "topk": wl.topk,
+                   "window": wl.window, "blocks": M, "max_block_rows": int(sizes.max()),
+                   "parallelism": "single GPU"},
+        "tflops": flops / (ms_step * 1e-3) / 1e12,
+        "mfma_peak_frac": flops / (ms_step * 1e-3) / 1e12 / peak,
+        "forward_only": {"ms": fwd_ms, "tokens_per_s": N / (fwd_ms * 1e-3),
+                         "tflops": flops / (fwd_ms * 1e-3) / 1e12,
+                         "mfma_peak_frac": flops / (fwd_ms * 1e-3) / 1e12 / peak},
+        "stage_ms": stage_ms,
+        "credited_flops": flops,
+        "algorithmic_bytes": alg_bytes,
+        "roofline": {"kernel": "k_select (compressed branch + top-k)", "bound": "mfma",
+                     "achieved": sel_tflops, "peak": peak, "unit": "TFLOP/s",
+                     "frac": sel_tflops / peak, "traffic": None,
+                     "work_per_launch_flops": cmp_flops},
+    }
+    if not args.no_cpu:
+        res["cpu_baseline"] = cpu_baseline(inp, min(args.cpu_heads, H))
+    print(json.dumps(res))
+
+
+if __name__ == "__main__":
+    main()

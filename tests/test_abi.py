@@ -1,0 +1,111 @@
+"""The C ABI on the CPU: the library loads, exports every function ssa.h declares, and
+its host-side argument checks return the documented status codes (no GPU needed)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ssa.h")
+
+
+@pytest.fixture(scope="module")
+def ssa():
+    import spatial_sparse_attention_amd as m
+    return m
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ssa_[a-z_]+)\s*\(", text)))
+
+
+def test_header_symbols_exported(ssa):
+    names = _declared()
+    assert "ssa_forward" in names and "ssa_plan_create" in names
+    out = subprocess.run(["nm", "-D", "--defined-only", ssa.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r" T (ssa_\w+)", out))
+    missing = [n for n in names if n not in exported]
+    assert not missing, missing
+    for n in names:
+        assert hasattr(ssa.lib, n)
+
+
+def test_status_strings(ssa):
+    for code in range(7):
+        assert ssa.lib.ssa_status_string(code)
+    assert ssa.lib.ssa_status_string(99) == b"unknown status"
+
+
+def _grid(g=(8, 8, 8)):
+    return (ctypes.c_int32 * 3)(*g)
+
+
+FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: checks fail before any access
+
+
+def test_plan_argument_errors(ssa):
+    L = ssa.lib
+    h = ctypes.c_void_p()
+    ws = ctypes.create_string_buffer(1 << 16)
+    size = L.ssa_plan_workspace_size(10, _grid(), 2, 2)
+    assert size > 0
+    assert L.ssa_plan_create(FAKE, 10, _grid(), 2, 2, ws, size, None, None) == 1
+    assert L.ssa_plan_create(FAKE, -1, _grid(), 2, 2, ws, size, None, ctypes.byref(h)) == 1
+    assert L.ssa_plan_create(FAKE, 10, _grid(), 0, 2, ws, size, None, ctypes.byref(h)) == 1
+    assert L.ssa_plan_create(FAKE, 10, _grid(), 2, 0, ws, size, None, ctypes.byref(h)) == 1
+    assert L.ssa_plan_create(FAKE, 10, _grid((8, 0, 8)), 2, 2, ws, size, None, ctypes.byref(h)) == 1
+    assert L.ssa_plan_create(None, 10, _grid(), 2, 2, ws, size, None, ctypes.byref(h)) == 1
+    # window cells that are not unions of blocks
+    assert L.ssa_plan_create(FAKE, 10, _grid(), 2, 3, ws, size, None, ctypes.byref(h)) == 2
+    assert L.ssa_plan_create(FAKE, 10, _grid(), 4, 2, ws, size, None, ctypes.byref(h)) == 2
+    # workspace missing / too small
+    assert L.ssa_plan_create(FAKE, 10, _grid(), 2, 2, None, size, None, ctypes.byref(h)) == 3
+    assert L.ssa_plan_create(FAKE, 10, _grid(), 2, 2, ws, size - 1, None, ctypes.byref(h)) == 3
+    assert h.value is None
+
+
+def test_empty_plan_and_forward_checks(ssa):
+    L = ssa.lib
+    h = ctypes.c_void_p()
+    size = L.ssa_plan_workspace_size(0, _grid(), 2, 4)
+    ws = ctypes.create_string_buffer(size)
+    assert L.ssa_plan_create(None, 0, _grid(), 2, 4, ws, size, None, ctypes.byref(h)) == 0
+    info = ssa.PlanInfo()
+    assert L.ssa_plan_get_info(h, ctypes.byref(info)) == 0
+    assert info.n == 0 and info.num_blocks == 0
+    wsz = L.ssa_forward_workspace_size(h, 1, 2, 64, 4)
+    assert wsz > 0
+    fws = ctypes.create_string_buffer(wsz)
+    args = lambda dt=1, H=2, d=64, k=4, sc=0.0: (h, dt, H, d, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, k,
+                                                 ctypes.c_float(sc), FAKE, None, fws, wsz, None)
+    assert L.ssa_forward(*args()) == 0                 # N = 0: nothing to do
+    assert L.ssa_forward(*args(dt=3)) == 1
+    assert L.ssa_forward(*args(dt=-1)) == 1
+    assert L.ssa_forward(*args(H=0)) == 1
+    assert L.ssa_forward(*args(d=48)) == 2
+    assert L.ssa_forward(*args(k=0)) == 1
+    assert L.ssa_forward(*args(k=300)) == 2
+    assert L.ssa_forward(*args(sc=-1.0)) == 1
+    assert L.ssa_forward(*args(sc=float("nan"))) == 1
+    assert L.ssa_forward(*args(sc=float("inf"))) == 1
+    assert L.ssa_forward_stages(*(args() + (0,))) == 1
+    assert L.ssa_forward_stages(*(args() + (8,))) == 1
+    assert L.ssa_plan_get_info(h, None) == 1
+    assert L.ssa_plan_get_info(None, ctypes.byref(info)) == 6
+    assert L.ssa_forward(None, 1, 2, 64, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, ctypes.c_float(0),
+                         FAKE, None, fws, wsz, None) == 6
+    L.ssa_plan_destroy(h)
+    L.ssa_plan_destroy(None)
+
+
+def test_workspace_sizes_monotone(ssa):
+    L = ssa.lib
+    a = L.ssa_plan_workspace_size(1000, _grid(), 2, 2)
+    b = L.ssa_plan_workspace_size(100000, _grid(), 2, 2)
+    assert 0 < a < b
+    assert L.ssa_plan_workspace_size(-5, _grid(), 2, 2) == 0
