@@ -26,8 +26,7 @@ size_t fwd_carve(Carver& c, const ssa_plan_s* p, ssa_dtype dt, int H, int d, int
   const int64_t n1 = p->n > 0 ? p->n : 1;
   const size_t es = esize_of(dt);
   FwdWs t;
-  t.ksplit = c.take<char>((size_t)nsplit_of(dt) * H * Mp * d * es);
-  t.vtil_t = c.take<char>((size_t)H * d * Mp * es);
+  t.pooled = c.take<char>((size_t)H * (Mp / KT) * stage_elems(dt, d) * es);
   t.oc = c.take<char>((size_t)H * n1 * d * es);
   t.sel = c.take<int32_t>((size_t)H * (p->M > 0 ? p->M : 1) * topk);
   if (w) *w = t;

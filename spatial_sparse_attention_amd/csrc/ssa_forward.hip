@@ -7,140 +7,188 @@
 // the important blocks for fine attention; a local window module attends to the
 // query's neighbourhood; predicted gates aggregate the three outputs.
 //
-// Work item of the attention kernels: one (query block, head), taken in
-// longest-block-first order.  Four waves each own 32 query rows per sweep.
-// Scores come from 32x32 MFMA tiles.  The compressed branch runs twice over the
-// pooled keys:
+// Scores come from 32x32 MFMA tiles; each wave owns 32 query rows.  Key and value
+// tiles (32 keys) are copied straight from HBM into LDS (global_load_lds), double
+// buffered: the next tile's copy is issued before the current tile's math.  The PV
+// product is O^T += V^T P^T: P^T comes straight from the score registers and V^T from
+// LDS transpose reads of the row-major value tile.
+//
+// The compressed branch runs twice over the pooled keys:
 //   pass 1 computes S^T = Ktil Q^T (a lane holds one query, 16 keys), keeps an
-//          online softmax and accumulates O^T += Vtil^T P^T with P^T straight
-//          from registers; it yields o_c and the exact log-sum-exp;
+//          online softmax, accumulates O^T, and yields o_c and the exact
+//          log-sum-exp;
 //   pass 2 computes S = Q Ktil^T (a lane holds one key, 16 queries), so the
 //          importance column sums over the block's queries are register sums.
-// The pooled keys are fp32; they enter the MFMA as two (f16) or three (bf16)
-// dtype planes whose sum reproduces the fp32 value, so the scores that decide the
-// top-k carry fp32-level error.
+// The pooled keys are fp32; they enter the MFMA as two (f16) or three (bf16) dtype
+// planes whose sum reproduces the fp32 value, so the scores that decide the top-k
+// carry fp32-level error.
 #include <hip/hip_runtime.h>
 #include "ssa_internal.h"
 #include "ssa_mfma.h"
 
 namespace {
 
-constexpr int NWAVE = 4;
-constexpr int NT = 64 * NWAVE;
-constexpr int ROWS_PER_SWEEP = 32 * NWAVE;
-constexpr int KT = 32;  // keys per tile
+constexpr int KT = 32;            // keys per tile
+constexpr int SEL_WAVES = 8;      // compressed/select workgroup: 8 waves, 256 rows per sweep
+constexpr int ATT_WAVES = 4;      // attend workgroup: 4 waves, 128 rows per chunk
+constexpr int ATT_ROWS = 32 * ATT_WAVES;
+constexpr float RESCALE_SLACK = 8.f;  // log2 units the running max may lag the true max
 
-template <class T> struct Pad { static constexpr int v = 16 / sizeof(T); };
+// ------------------------------------------------------------------ tile geometry
+template <int DT, int D>
+struct Cfg {
+  using T = typename Tr<DT>::T;
+  using F = typename Tr<DT>::frag;
+  static constexpr int NS = Tr<DT>::NSPLIT;
+  static constexpr int KS = Tr<DT>::KS, KPL = Tr<DT>::KPL;
+  static constexpr int NKS = D / KS;                    // K steps over the head dim
+  static constexpr int NDV = D / 32;                    // 32-wide output column tiles
+  static constexpr int EPC = 16 / sizeof(T);            // elements per 16-byte chunk
+  static constexpr int CPR = D / EPC;                   // data chunks per row
+  static constexpr int KROW = D + 16 / sizeof(T);       // K tile row (b128 fragment reads)
+  static constexpr int VROW = D + 32 / sizeof(T);       // V tile row (transpose reads)
+  static constexpr int KTILE = KT * KROW, VTILE = KT * VROW;
+  static constexpr int KCH = KTILE * sizeof(T) / 16;    // 16-byte chunks of a K tile
+  static constexpr int VCH = VTILE * sizeof(T) / 16;
+  static constexpr int STAGE = NS * KTILE + VTILE;      // pooled stage (elements)
+  static constexpr int PK = KT / KS;                    // K steps over a 32-key tile (PV)
+};
 
 // ------------------------------------------------------------------ pooling
 // grid (Mp, H).  ktil[h,b] = mean_{i in b} K[i,h] @ Wk ; same for V.  Writes the fp32
-// value split into NSPLIT dtype planes ksplit[s][h][b][:], and vtil_t[h][:][b].
-template <int DT>
+// pooled key split into NSPLIT dtype planes and the pooled value, in the per-(head, tile)
+// stage layout; row padding and padding blocks (b >= M) are zero.
+template <int DT, int D>
 __global__ __launch_bounds__(256) void k_pool(
     const typename Tr<DT>::T* __restrict__ kin, const typename Tr<DT>::T* __restrict__ vin,
     const typename Tr<DT>::T* __restrict__ wk, const typename Tr<DT>::T* __restrict__ wv,
     const int32_t* __restrict__ perm, const int32_t* __restrict__ blk_off, int M, int Mp, int H,
-    int d, typename Tr<DT>::T* __restrict__ ksplit, typename Tr<DT>::T* __restrict__ vtil_t) {
+    typename Tr<DT>::T* __restrict__ pooled) {
+  using C = Cfg<DT, D>;
   using T = typename Tr<DT>::T;
-  constexpr int NS = Tr<DT>::NSPLIT;
-  constexpr int VEC = 16 / sizeof(T);
-  extern __shared__ float smem[];
+  constexpr int NS = C::NS, VEC = C::EPC, CH = C::CPR, RSUB = 256 / CH;
+  constexpr int U = 4;  // rows in flight per thread
+  __shared__ float redk[RSUB * D], redv[RSUB * D], kbar[D], vbar[D];
   const int b = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
-  if (b >= M) {  // padding keys: zeros
-    for (int j = tid; j < d; j += 256) {
-      for (int s = 0; s < NS; ++s) ksplit[(((int64_t)s * H + h) * Mp + b) * d + j] = (T)0.f;
-      vtil_t[((int64_t)h * d + j) * Mp + b] = (T)0.f;
-    }
-    return;
-  }
-  const int CH = d / VEC, RSUB = 256 / CH;
-  float* redk = smem;               // [RSUB][d]
-  float* redv = smem + RSUB * d;    // [RSUB][d]
-  float* kbar = redv + RSUB * d;    // [d]
-  float* vbar = kbar + d;           // [d]
+  T* stg = pooled + ((int64_t)h * (Mp / KT) + b / KT) * C::STAGE;
+  T* krow = stg + (b % KT) * C::KROW;                    // plane s at + s * KTILE
+  T* vrow = stg + NS * C::KTILE + (b % KT) * C::VROW;
+  for (int j = (b >= M ? 0 : D) + tid; j < C::KROW; j += 256)
+    for (int s = 0; s < NS; ++s) krow[s * C::KTILE + j] = (T)0.f;
+  for (int j = (b >= M ? 0 : D) + tid; j < C::VROW; j += 256) vrow[j] = (T)0.f;
+  if (b >= M) return;
   const int r0 = blk_off[b], r1 = blk_off[b + 1];
   const int sub = tid / CH, ch = tid % CH;
   if (sub < RSUB) {
     float ak[VEC], av[VEC];
     for (int e = 0; e < VEC; ++e) ak[e] = av[e] = 0.f;
-    for (int r = r0 + sub; r < r1; r += RSUB) {
-      const int64_t base = ((int64_t)perm[r] * H + h) * d + ch * VEC;
-      const T* kp = kin + base;
-      const T* vp = vin + base;
-      for (int e = 0; e < VEC; ++e) {
-        ak[e] += Tr<DT>::up(kp[e]);
-        av[e] += Tr<DT>::up(vp[e]);
+    for (int r = r0 + sub; r < r1; r += U * RSUB) {
+      uint4 kb[U], vb[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int rr = r + u * RSUB;
+        if (rr < r1) {
+          const int64_t base = ((int64_t)perm[rr] * H + h) * D + ch * VEC;
+          kb[u] = *reinterpret_cast<const uint4*>(kin + base);
+          vb[u] = *reinterpret_cast<const uint4*>(vin + base);
+        } else {
+          kb[u] = vb[u] = make_uint4(0, 0, 0, 0);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const T* kp = reinterpret_cast<const T*>(&kb[u]);
+        const T* vp = reinterpret_cast<const T*>(&vb[u]);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) {
+          ak[e] += Tr<DT>::up(kp[e]);
+          av[e] += Tr<DT>::up(vp[e]);
+        }
       }
     }
     for (int e = 0; e < VEC; ++e) {
-      redk[sub * d + ch * VEC + e] = ak[e];
-      redv[sub * d + ch * VEC + e] = av[e];
+      redk[sub * D + ch * VEC + e] = ak[e];
+      redv[sub * D + ch * VEC + e] = av[e];
     }
   }
   __syncthreads();
   const float inv = 1.f / (float)(r1 - r0);
-  for (int j = tid; j < 2 * d; j += 256) {
-    const float* red = j < d ? redk : redv;
-    const int c = j < d ? j : j - d;
+  for (int j = tid; j < 2 * D; j += 256) {
+    const float* red = j < D ? redk : redv;
+    const int c = j < D ? j : j - D;
     float s = 0.f;
-    for (int u = 0; u < RSUB; ++u) s += red[u * d + c];
-    (j < d ? kbar : vbar)[c] = s * inv;
+    for (int u = 0; u < RSUB; ++u) s += red[u * D + c];
+    (j < D ? kbar : vbar)[c] = s * inv;
   }
   __syncthreads();
-  for (int j = tid; j < 2 * d; j += 256) {
-    const bool isk = j < d;
-    const int c = isk ? j : j - d;
+  for (int j = tid; j < 2 * D; j += 256) {
+    const bool isk = j < D;
+    const int c = isk ? j : j - D;
     const T* W = isk ? wk : wv;
     const float* xb = isk ? kbar : vbar;
     float acc = 0.f;
-    for (int i = 0; i < d; ++i) acc += xb[i] * Tr<DT>::up(W[(int64_t)i * d + c]);
+    for (int i = 0; i < D; ++i) acc += xb[i] * Tr<DT>::up(W[(int64_t)i * D + c]);
     if (isk) {
       float rem = acc;
       for (int s = 0; s < NS; ++s) {
-        T part = Tr<DT>::cvt(rem);
-        ksplit[(((int64_t)s * H + h) * Mp + b) * d + c] = part;
+        const T part = Tr<DT>::cvt(rem);
+        krow[s * C::KTILE + c] = part;
         rem -= Tr<DT>::up(part);
       }
     } else {
-      vtil_t[((int64_t)h * d + c) * Mp + b] = Tr<DT>::cvt(acc);
+      vrow[c] = Tr<DT>::cvt(acc);
     }
   }
 }
 
-// ------------------------------------------------------------------ shared pieces
-template <int DT, int D>
-struct Frags {
-  using T = typename Tr<DT>::T;
-  using F = typename Tr<DT>::frag;
-  static constexpr int KS = Tr<DT>::KS, KPL = Tr<DT>::KPL;
-  static constexpr int NKS = D / KS;   // K steps over the head dim
-  static constexpr int NDV = D / 32;   // 32-wide output column tiles
-  static constexpr int KROW = D + Pad<T>::v;
-  static constexpr int VROW = KT + Pad<T>::v;
-  static constexpr int PK = KT / KS;   // K steps over a 32-key tile (PV product)
-};
-
-// A operand of O^T += V^T P^T for K step `ks` of a 32-key tile: lane (dv = row, g)
-// supplies V^T[dv][key] for the keys held by P^T registers ks*KPL .. ks*KPL+KPL-1.
-template <int DT, int D>
-__device__ inline typename Tr<DT>::frag vt_frag(const typename Tr<DT>::T* vrow, int ks, int g) {
-  using Fr = Frags<DT, D>;
-  typename Tr<DT>::frag f;
-  if constexpr (Fr::KPL == 1) {
-    f = vrow[res_row(ks, g)];
-  } else {
-    // registers ks*8 .. ks*8+7 hold keys 16ks + {4g..4g+3, 8+4g..8+4g+3}
-    typedef typename Tr<DT>::T T;
-    typedef T T4 __attribute__((ext_vector_type(4)));
-    const T4 lo = *reinterpret_cast<const T4*>(vrow + 16 * ks + 4 * g);
-    const T4 hi = *reinterpret_cast<const T4*>(vrow + 16 * ks + 8 + 4 * g);
-    f[0] = lo[0]; f[1] = lo[1]; f[2] = lo[2]; f[3] = lo[3];
-    f[4] = hi[0]; f[5] = hi[1]; f[6] = hi[2]; f[7] = hi[3];
-  }
-  return f;
+// ------------------------------------------------------------------ MFMA building blocks
+// Reduction with the other half of the wave (lanes l and l^32 hold the same query row):
+// v_permlane32_swap returns the pair {x[l], x[l^32]} in its two results.
+__device__ inline float xor32_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float xor32_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// B operand (P^T) for K step ks from the 16 fp32 probabilities of a lane.
+// A operand (V^T) of O^T += V^T P^T, K step ks of a 32-key tile stored row-major in LDS
+// (vt[key][dv], row stride VROW), output columns 32*j .. 32*j+31.  Lane l covers
+// dv = 32j + l%32 and the keys held by P^T registers ks*KPL .. ks*KPL + KPL - 1, i.e.
+// keys 16ks + 4g + {0..3} and 16ks + 8 + 4g + {0..3} (g = l/32) for 16-bit types.
+template <int DT, int D>
+__device__ inline typename Tr<DT>::frag vt_frag(const typename Tr<DT>::T* vt, int ks, int j, int lane) {
+  using C = Cfg<DT, D>;
+  if constexpr (C::KPL == 1) {
+    return vt[res_row(ks, lane >> 5) * C::VROW + 32 * j + (lane & 31)];
+  } else {
+    const int i = lane & 15, G = lane >> 4;
+    const typename Tr<DT>::T* p =
+        vt + (16 * ks + 4 * (G >> 1) + (i >> 2)) * C::VROW + 32 * j + 16 * (G & 1) + 4 * (i & 3);
+    typedef unsigned u2 __attribute__((ext_vector_type(2)));
+    typedef unsigned u4 __attribute__((ext_vector_type(4)));
+    const u2 a = __builtin_bit_cast(u2, lds_read_tr16(p));
+    const u2 b = __builtin_bit_cast(u2, lds_read_tr16(p + 8 * C::VROW));
+    const u4 u = {a.x, a.y, b.x, b.y};
+    return __builtin_bit_cast(typename Tr<DT>::frag, u);
+  }
+}
+
+// The V^T fragments of one 32-key tile, read before the next tile's copy is issued: the
+// transpose reads carry no alias information, so reading them after the copy is issued
+// would make the compiler wait for that copy.
+template <int DT, int D>
+struct VFrags {
+  typename Tr<DT>::frag f[Cfg<DT, D>::PK][Cfg<DT, D>::NDV];
+  __device__ inline void read(const typename Tr<DT>::T* vt, int lane) {
+#pragma unroll
+    for (int ks = 0; ks < Cfg<DT, D>::PK; ++ks)
+#pragma unroll
+      for (int j = 0; j < Cfg<DT, D>::NDV; ++j) f[ks][j] = vt_frag<DT, D>(vt, ks, j, lane);
+  }
+};
+
 template <int DT>
 __device__ inline typename Tr<DT>::frag p_frag(const ssa_f16v& p, int ks) {
   typename Tr<DT>::frag f;
@@ -156,16 +204,27 @@ __device__ inline typename Tr<DT>::frag p_frag(const ssa_f16v& p, int ks) {
 template <int DT>
 __device__ inline typename Tr<DT>::frag zero_frag() {
   typename Tr<DT>::frag f;
-  if constexpr (Tr<DT>::KPL == 1) f = 0.f;
-  else {
+  if constexpr (Tr<DT>::KPL == 1) {
+    f = 0.f;
+  } else {
 #pragma unroll
     for (int t = 0; t < 8; ++t) f[t] = (typename Tr<DT>::T)0.f;
   }
   return f;
 }
 
-// Online-softmax state of one query row (duplicated in lanes c and c+32, which hold
-// different keys of the same row).  Scores are in log2 units.
+__device__ inline ssa_f16v zero16() {
+  ssa_f16v z;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) z[r] = 0.f;
+  return z;
+}
+
+// Online softmax of one query row (duplicated in lanes c and c+32, which hold different
+// keys of the row), in log2 units.  The running max m may lag the true max by up to
+// RESCALE_SLACK, so the accumulator is rescaled only when a tile raises the max by more
+// than that (probabilities stay below 2^RESCALE_SLACK); the normalisation by l and
+// lse = m + log2(l) are exact either way.
 template <int NDV>
 struct Online {
   float m, l;
@@ -174,65 +233,109 @@ struct Online {
     m = -INFINITY;
     l = 0.f;
 #pragma unroll
-    for (int j = 0; j < NDV; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[j][r] = 0.f;
+    for (int j = 0; j < NDV; ++j) o[j] = zero16();
   }
-  // x: the lane's 16 scores (log2 units, -inf for masked keys); returns p in place.
-  __device__ inline void update(ssa_f16v& x) {
-    float mt = x[0];
+  // s: raw scores (-inf for masked keys); sl2 = scale * log2(e) > 0.  Returns p in s.
+  __device__ inline void update(ssa_f16v& s, float sl2) {
+    float mt = fmaxf(s[0], s[1]);
 #pragma unroll
-    for (int r = 1; r < 16; ++r) mt = fmaxf(mt, x[r]);
-    mt = fmaxf(mt, __shfl_xor(mt, 32));
-    const float mn = fmaxf(m, mt);
-    const float alpha = fast_exp2(m - mn);
-    float s = 0.f;
+    for (int r = 2; r < 16; r += 2) mt = fmaxf(mt, fmaxf(s[r], s[r + 1]));
+    mt = xor32_max(mt) * sl2;
+    if (__builtin_amdgcn_ballot_w64(mt > m + RESCALE_SLACK)) {
+      const float mn = fmaxf(m, mt);
+      const float alpha = fast_exp2(m - mn);
+      l *= alpha;
+#pragma unroll
+      for (int j = 0; j < NDV; ++j) o[j] *= alpha;
+      m = mn;
+    }
+    float sum = 0.f;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      x[r] = fast_exp2(x[r] - mn);
-      s += x[r];
+      s[r] = fast_exp2(__builtin_fmaf(s[r], sl2, -m));
+      sum += s[r];
     }
-    l = l * alpha + s;
-#pragma unroll
-    for (int j = 0; j < NDV; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[j][r] *= alpha;
-    m = mn;
+    l += sum;
   }
 };
 
-// O^T += V^T P^T for one 32-key tile.
+// S^T tile (keys x queries) from a K tile in LDS ([32][KROW]).
 template <int DT, int D>
-__device__ inline void pv_tile(Online<D / 32>& st, const ssa_f16v& p,
-                               const typename Tr<DT>::T* v_lds, int c, int g) {
-  using Fr = Frags<DT, D>;
+__device__ inline ssa_f16v st_tile(const typename Tr<DT>::T* kt, const typename Tr<DT>::frag* qf,
+                                   ssa_f16v acc, int lane) {
+  using C = Cfg<DT, D>;
+  const typename Tr<DT>::T* row = kt + (lane & 31) * C::KROW + (lane >> 5) * C::KPL;
 #pragma unroll
-  for (int ks = 0; ks < Fr::PK; ++ks) {
+  for (int ks = 0; ks < C::NKS; ++ks) acc = Tr<DT>::mma(load_frag<DT>(row + ks * C::KS), qf[ks], acc);
+  return acc;
+}
+
+// S tile (queries x keys) from a K tile in LDS.
+template <int DT, int D>
+__device__ inline ssa_f16v s_tile(const typename Tr<DT>::T* kt, const typename Tr<DT>::frag* qf,
+                                  ssa_f16v acc, int lane) {
+  using C = Cfg<DT, D>;
+  const typename Tr<DT>::T* row = kt + (lane & 31) * C::KROW + (lane >> 5) * C::KPL;
+#pragma unroll
+  for (int ks = 0; ks < C::NKS; ++ks) acc = Tr<DT>::mma(qf[ks], load_frag<DT>(row + ks * C::KS), acc);
+  return acc;
+}
+
+template <int DT, int D>
+__device__ inline void pv_tile(Online<D / 32>& st, const ssa_f16v& p, const VFrags<DT, D>& vf) {
+  using C = Cfg<DT, D>;
+#pragma unroll
+  for (int ks = 0; ks < C::PK; ++ks) {
     const typename Tr<DT>::frag pf = p_frag<DT>(p, ks);
 #pragma unroll
-    for (int j = 0; j < Fr::NDV; ++j) {
-      const typename Tr<DT>::frag vf = vt_frag<DT, D>(v_lds + (32 * j + c) * Fr::VROW, ks, g);
-      st.o[j] = Tr<DT>::mma(vf, pf, st.o[j]);
-    }
+    for (int j = 0; j < C::NDV; ++j) st.o[j] = Tr<DT>::mma(vf.f[ks][j], pf, st.o[j]);
+  }
+}
+
+template <int DT, int D>
+__device__ inline void load_q(typename Tr<DT>::frag* qf, const typename Tr<DT>::T* qrow, bool valid,
+                              int lane) {
+  using C = Cfg<DT, D>;
+#pragma unroll
+  for (int s = 0; s < C::NKS; ++s)
+    qf[s] = valid ? load_frag<DT>(qrow + s * C::KS + (lane >> 5) * C::KPL) : zero_frag<DT>();
+}
+
+// ------------------------------------------------------------------ direct global->LDS copies
+// global_load_lds_dwordx4: lane l of a wave writes its 16 bytes at the (wave-uniform) LDS
+// base + 16*l.  A tile is a sequence of 16-byte positions; instruction i covers positions
+// 64i .. 64i+63, and the workgroup's waves take instructions round-robin.
+typedef __attribute__((address_space(3))) void lds_void_t;
+__device__ inline void dma16(const void* g, void* lds_instr_base) {
+  __builtin_amdgcn_global_load_lds(g, (lds_void_t*)lds_instr_base, 16, 0, 0);
+}
+__device__ inline void dma_wait() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+template <int NW>
+__device__ inline void dma_contiguous(void* lds, const void* g, int nchunks, int wave, int lane) {
+  for (int i = wave; i * 64 < nchunks; i += NW) {
+    const int p = i * 64 + lane;
+    if (p < nchunks) dma16((const char*)g + (int64_t)p * 16, (char*)lds + i * 1024);
   }
 }
 
 // ------------------------------------------------------------------ compressed + select
+// One workgroup per (query block, head), longest blocks first.
 template <int DT, int D>
-__global__ __launch_bounds__(NT) void k_select(
-    const typename Tr<DT>::T* __restrict__ q, const typename Tr<DT>::T* __restrict__ ksplit,
-    const typename Tr<DT>::T* __restrict__ vtil_t, const int32_t* __restrict__ perm,
-    const int32_t* __restrict__ blk_off, const int32_t* __restrict__ lpt, int M, int Mp, int H,
-    int64_t N, float sl2, int topk, typename Tr<DT>::T* __restrict__ oc,
-    int32_t* __restrict__ sel) {
-  using Fr = Frags<DT, D>;
+__global__ __launch_bounds__(64 * SEL_WAVES) void k_select(
+    const typename Tr<DT>::T* __restrict__ q, const typename Tr<DT>::T* __restrict__ pooled,
+    const int32_t* __restrict__ perm, const int32_t* __restrict__ blk_off,
+    const int32_t* __restrict__ lpt, int M, int Mp, int H, int64_t N, float sl2, int topk,
+    typename Tr<DT>::T* __restrict__ oc, int32_t* __restrict__ sel) {
+  using C = Cfg<DT, D>;
   using T = typename Tr<DT>::T;
   using F = typename Tr<DT>::frag;
-  constexpr int NS = Tr<DT>::NSPLIT;
-  __shared__ __attribute__((aligned(16))) T k_lds[NS][KT][Fr::KROW];
-  __shared__ __attribute__((aligned(16))) T v_lds[D][Fr::VROW];
-  __shared__ float stage[NWAVE][32];
-  __shared__ float lse_lds[ROWS_PER_SWEEP];
+  constexpr int NS = C::NS;
+  constexpr int ROWS = 32 * SEL_WAVES;
+  __shared__ __attribute__((aligned(1024))) T stage0[C::STAGE];
+  __shared__ __attribute__((aligned(1024))) T stage1[C::STAGE];
+  __shared__ float stage_sum[2][SEL_WAVES][32];
+  __shared__ float lse_lds[ROWS];
   __shared__ int32_t pick[256];
   extern __shared__ float sig[];  // [Mp]
 
@@ -240,112 +343,103 @@ __global__ __launch_bounds__(NT) void k_select(
   const int h = blockIdx.x % H;
   const int b = lpt[blockIdx.x / H];
   const int r0 = blk_off[b], rows = blk_off[b + 1] - r0;
-  for (int j = tid; j < Mp; j += NT) sig[j] = 0.f;
+  for (int j = tid; j < Mp; j += 64 * SEL_WAVES) sig[j] = 0.f;
   const int ntile = Mp / KT;
-  constexpr int KCH = D * sizeof(T) / 16;  // 16-byte chunks per key row
-  constexpr int VCH = KT * sizeof(T) / 16;  // 16-byte chunks per V^T row
-  constexpr int EPC = 16 / sizeof(T);
+  const T* pstage = pooled + (int64_t)h * ntile * C::STAGE;
+  constexpr int NCH1 = C::STAGE * sizeof(T) / 16, NCH2 = NS * C::KCH;
 
-  for (int sw = 0; sw * ROWS_PER_SWEEP < rows; ++sw) {
-    const int row_base = sw * ROWS_PER_SWEEP + wave * 32;
+  for (int sw = 0; sw * ROWS < rows; ++sw) {
+    const int row_base = sw * ROWS + wave * 32;
     const bool wave_active = row_base < rows;
     const int my_row = row_base + c;
     const bool valid = my_row < rows;
-    F qf[Fr::NKS];
-    {
-      const int64_t tok = valid ? perm[r0 + my_row] : 0;
-      const T* qrow = q + (tok * H + h) * D;
-#pragma unroll
-      for (int s = 0; s < Fr::NKS; ++s)
-        qf[s] = valid ? load_frag<DT>(qrow + s * Fr::KS + g * Fr::KPL) : zero_frag<DT>();
-    }
-    // ---------------- pass 1: online softmax, o_c, lse
-    Online<Fr::NDV> st;
+    F qf[C::NKS];
+    load_q<DT, D>(qf, q + ((int64_t)(valid ? perm[r0 + my_row] : 0) * H + h) * D, valid, lane);
+
+    // ---------------- pass 1: online softmax over all pooled keys -> o_c, lse
+    Online<C::NDV> st;
     st.init();
-    for (int kt = 0; kt < ntile; ++kt) {
-      __syncthreads();
-      for (int idx = tid; idx < NS * KT * KCH; idx += NT) {
-        const int s = idx / (KT * KCH), rem = idx % (KT * KCH), key = rem / KCH, ch = rem % KCH;
-        *reinterpret_cast<uint4*>(&k_lds[s][key][ch * EPC]) = *reinterpret_cast<const uint4*>(
-            ksplit + (((int64_t)s * H + h) * Mp + kt * KT + key) * D + ch * EPC);
+    {
+      auto p1 = [&](int t, T* cur, T* nxt) {
+        dma_wait();
+        __syncthreads();
+        VFrags<DT, D> vf;
+        if (wave_active) vf.read(cur + NS * C::KTILE, lane);
+        if (t + 1 < ntile) dma_contiguous<SEL_WAVES>(nxt, pstage + (int64_t)(t + 1) * C::STAGE, NCH1, wave, lane);
+        if (wave_active) {
+          ssa_f16v acc = zero16();
+#pragma unroll
+          for (int s = 0; s < NS; ++s) acc = st_tile<DT, D>(cur + s * C::KTILE, qf, acc, lane);
+          if (t == ntile - 1) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+              if (t * KT + res_row(r, g) >= M) acc[r] = -INFINITY;
+          }
+          st.update(acc, sl2);
+          pv_tile<DT, D>(st, acc, vf);
+        }
+      };
+      __syncthreads();  // the previous sweep is done with both stage buffers
+      dma_contiguous<SEL_WAVES>(stage0, pstage, NCH1, wave, lane);
+      for (int t = 0; t < ntile; t += 2) {
+        p1(t, stage0, stage1);
+        if (t + 1 < ntile) p1(t + 1, stage1, stage0);
       }
-      for (int idx = tid; idx < D * VCH; idx += NT) {
-        const int dv = idx / VCH, ch = idx % VCH;
-        *reinterpret_cast<uint4*>(&v_lds[dv][ch * EPC]) = *reinterpret_cast<const uint4*>(
-            vtil_t + ((int64_t)h * D + dv) * Mp + kt * KT + ch * EPC);
-      }
-      __syncthreads();
-      if (!wave_active) continue;
-      ssa_f16v acc;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[r] = 0.f;
-#pragma unroll
-      for (int s = 0; s < NS; ++s)
-#pragma unroll
-        for (int ks = 0; ks < Fr::NKS; ++ks)
-          acc = Tr<DT>::mma(load_frag<DT>(&k_lds[s][c][ks * Fr::KS + g * Fr::KPL]), qf[ks], acc);
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = kt * KT + res_row(r, g);
-        acc[r] = key < M ? acc[r] * sl2 : -INFINITY;
-      }
-      st.update(acc);
-      pv_tile<DT, D>(st, acc, &v_lds[0][0], c, g);
     }
-    const float ltot = st.l + __shfl_xor(st.l, 32);
-    const float inv = 1.f / ltot;
+    const float ltot = xor32_sum(st.l);
     if (wave_active && valid) {
+      const float inv = 1.f / ltot;
       T* orow = oc + ((int64_t)h * N + r0 + my_row) * D;
 #pragma unroll
-      for (int j = 0; j < Fr::NDV; ++j)
+      for (int j = 0; j < C::NDV; ++j)
 #pragma unroll
         for (int r = 0; r < 16; ++r) orow[32 * j + res_row(r, g)] = Tr<DT>::cvt(st.o[j][r] * inv);
     }
-    if (g == 0) lse_lds[wave * 32 + c] = st.m + fast_log2(ltot);
+    // rows past the block get +inf, so their probabilities in pass 2 are exactly zero
+    if (g == 0) lse_lds[wave * 32 + c] = valid ? st.m + fast_log2(ltot) : INFINITY;
     __syncthreads();
-    // ---------------- pass 2: importance column sums
+
+    // ---------------- pass 2: importance column sums (S layout)
     float lrow[16];
-    bool vrow[16];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int rr = res_row(r, g);
-      vrow[r] = row_base + rr < rows;
-      lrow[r] = lse_lds[wave * 32 + rr];
-    }
-    for (int kt = 0; kt < ntile; ++kt) {
-      __syncthreads();
-      for (int idx = tid; idx < NS * KT * KCH; idx += NT) {
-        const int s = idx / (KT * KCH), rem = idx % (KT * KCH), key = rem / KCH, ch = rem % KCH;
-        *reinterpret_cast<uint4*>(&k_lds[s][key][ch * EPC]) = *reinterpret_cast<const uint4*>(
-            ksplit + (((int64_t)s * H + h) * Mp + kt * KT + key) * D + ch * EPC);
+    for (int r = 0; r < 16; ++r) lrow[r] = lse_lds[wave * 32 + res_row(r, g)];
+    {
+      auto fold = [&](int t) {  // sum the per-wave column sums of tile t into sigma (fixed order)
+        if (tid < 32) {
+          const int key = t * KT + tid;
+          float s = stage_sum[t & 1][0][tid];
+#pragma unroll
+          for (int w = 1; w < SEL_WAVES; ++w) s += stage_sum[t & 1][w][tid];
+          if (key < M) sig[key] += s;
+        }
+      };
+      auto p2 = [&](int t, T* cur, T* nxt) {
+        dma_wait();
+        __syncthreads();
+        if (t + 1 < ntile) dma_contiguous<SEL_WAVES>(nxt, pstage + (int64_t)(t + 1) * C::STAGE, NCH2, wave, lane);
+        if (t > 0) fold(t - 1);
+        float colsum = 0.f;
+        if (wave_active) {
+          ssa_f16v acc = zero16();
+#pragma unroll
+          for (int s = 0; s < NS; ++s) acc = s_tile<DT, D>(cur + s * C::KTILE, qf, acc, lane);
+#pragma unroll
+          for (int r = 0; r < 16; ++r) colsum += fast_exp2(__builtin_fmaf(acc[r], sl2, -lrow[r]));
+          colsum = xor32_sum(colsum);
+        }
+        if (g == 0) stage_sum[t & 1][wave][c] = colsum;
+      };
+      dma_contiguous<SEL_WAVES>(stage0, pstage, NCH2, wave, lane);
+      for (int t = 0; t < ntile; t += 2) {
+        p2(t, stage0, stage1);
+        if (t + 1 < ntile) p2(t + 1, stage1, stage0);
       }
       __syncthreads();
-      float colsum = 0.f;
-      if (wave_active) {
-        ssa_f16v acc;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[r] = 0.f;
-#pragma unroll
-        for (int s = 0; s < NS; ++s)
-#pragma unroll
-          for (int ks = 0; ks < Fr::NKS; ++ks)
-            acc = Tr<DT>::mma(qf[ks], load_frag<DT>(&k_lds[s][c][ks * Fr::KS + g * Fr::KPL]), acc);
-#pragma unroll
-        for (int r = 0; r < 16; ++r) colsum += vrow[r] ? fast_exp2(acc[r] * sl2 - lrow[r]) : 0.f;
-        colsum += __shfl_xor(colsum, 32);
-      }
-      if (g == 0) stage[wave][c] = colsum;
+      fold(ntile - 1);
       __syncthreads();
-      if (tid < 32) {
-        const int key = kt * KT + tid;
-        float s = stage[0][tid];
-#pragma unroll
-        for (int w = 1; w < NWAVE; ++w) s += stage[w][tid];
-        if (key < M) sig[key] += s;
-      }
     }
   }
-  __syncthreads();
+
   // ---------------- top-k (wave 0): repeated arg-max of (sigma bits, ~id) below the last pick
   if (wave == 0) {
     const int keff = min(topk, M);
@@ -366,7 +460,7 @@ __global__ __launch_bounds__(NT) void k_select(
       if (lane == 0) pick[it] = (int32_t)(0xFFFFFFFFu - (uint32_t)best);
     }
     if (lane == 0) {
-      for (int i = 1; i < keff; ++i) {  // ascending ids
+      for (int i = 1; i < keff; ++i) {
         int x = pick[i], j = i - 1;
         while (j >= 0 && pick[j] > x) { pick[j + 1] = pick[j]; --j; }
         pick[j + 1] = x;
@@ -377,174 +471,207 @@ __global__ __launch_bounds__(NT) void k_select(
 }
 
 // ------------------------------------------------------------------ selected + window + combine
-// Key sets are lists of blocks (the selected blocks; the blocks of the query's window
-// cell), concatenated in sorted token order and cut into 32-key tiles.
+// A key set is a list of blocks (the selected blocks, or the blocks of the query's window
+// cell), concatenated in sorted token order and cut into 32-key tiles.  A stage holds the
+// tile's K rows ([32][KROW]) followed by its V rows ([32][VROW]), copied straight from the
+// caller's K and V through the token permutation.  Keys past the end of the set reuse the
+// set's first key (finite values; their scores are masked).
+template <int DT, int D>
+struct Gather {
+  using C = Cfg<DT, D>;
+  static constexpr int KRC = C::KCH / KT, VRC = C::VCH / KT;  // chunks per padded row
+  static constexpr int NPOS = C::KCH + C::VCH;
+  static constexpr int NINSTR = (NPOS + 63) / 64;
+  static constexpr int NI = (NINSTR + ATT_WAVES - 1) / ATT_WAVES;  // copies per lane per tile
+  int32_t row[NI];    // tile row of each copy (-1: none)
+  int32_t goff[NI];   // element offset inside the token's head row, with bit 30 set for V
+  int32_t tok[NI];
+  __device__ inline void init(int wave, int lane) {
+#pragma unroll
+    for (int m = 0; m < NI; ++m) {
+      const int i = wave + m * ATT_WAVES, p = i * 64 + lane;
+      const bool isk = p < C::KCH;
+      const int q = isk ? p : p - C::KCH;
+      const int rr = isk ? q / KRC : q / VRC, ch = isk ? q % KRC : q % VRC;
+      const bool ok = i < NINSTR && p < NPOS && ch < C::CPR;
+      row[m] = ok ? rr : -1;
+      goff[m] = ch * C::EPC + (isk ? 0 : (1 << 30));
+    }
+  }
+  // tokens of this lane's copies for the tile starting at key k0
+  __device__ inline void lookup(int k0, int total, int L, const int32_t* pre, const int32_t* lst_off,
+                                const int32_t* __restrict__ perm) {
+#pragma unroll
+    for (int m = 0; m < NI; ++m) {
+      int j = k0 + (row[m] < 0 ? 0 : row[m]);
+      if (j >= total) j = 0;
+      int lo = 0, hi = L - 1;  // last list entry starting at or before key j
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (pre[mid] <= j) lo = mid; else hi = mid - 1;
+      }
+      tok[m] = perm[lst_off[lo] + (j - pre[lo])];
+    }
+  }
+  __device__ inline void issue(typename Tr<DT>::T* stage, const typename Tr<DT>::T* kin,
+                               const typename Tr<DT>::T* vin, int H, int h, int wave) const {
+#pragma unroll
+    for (int m = 0; m < NI; ++m) {
+      if (row[m] >= 0) {
+        const bool isv = goff[m] & (1 << 30);
+        const typename Tr<DT>::T* src = (isv ? vin : kin) + ((int64_t)tok[m] * H + h) * D + (goff[m] & ((1 << 30) - 1));
+        dma16(src, stage + (wave + m * ATT_WAVES) * 64 * C::EPC);
+      }
+    }
+  }
+};
+
 template <int DT, int D>
 __device__ inline void gathered_branch(
-    Online<D / 32>& st, const int32_t* blist, int nlist, const typename Tr<DT>::frag* qf,
-    const typename Tr<DT>::T* __restrict__ kin, const typename Tr<DT>::T* __restrict__ vin,
-    const int32_t* __restrict__ perm, const int32_t* __restrict__ blk_off, int H, int h,
-    float sl2, bool wave_active, typename Tr<DT>::T (*k_lds)[Frags<DT, D>::KROW],
-    typename Tr<DT>::T (*v_lds)[Frags<DT, D>::VROW], int32_t* pre, int32_t* lst, int32_t* tok) {
-  using Fr = Frags<DT, D>;
+    Online<D / 32>& st, const Gather<DT, D>& ga0, const int32_t* blist, int nlist,
+    const typename Tr<DT>::frag* qf, const typename Tr<DT>::T* __restrict__ kin,
+    const typename Tr<DT>::T* __restrict__ vin, const int32_t* __restrict__ perm,
+    const int32_t* __restrict__ blk_off, int H, int h, float sl2, bool wave_active,
+    typename Tr<DT>::T* stage0, typename Tr<DT>::T* stage1, int32_t* pre, int32_t* lst_off) {
+  using C = Cfg<DT, D>;
   using T = typename Tr<DT>::T;
-  constexpr int KCH = D * sizeof(T) / 16;
-  constexpr int EPC = 16 / sizeof(T);
-  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, c = lane & 31;
+  constexpr int NTH = 64 * ATT_WAVES;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 5;
   st.init();
-  for (int l0 = 0; l0 < nlist; l0 += NT) {
-    const int L = min(NT, nlist - l0);
+  Gather<DT, D> ga = ga0;
+  for (int l0 = 0; l0 < nlist; l0 += NTH) {
+    const int L = min(NTH, nlist - l0);
     __syncthreads();
-    // exclusive prefix of the chunk's block sizes
     int sz = 0;
     if (tid < L) {
       const int bb = blist[l0 + tid];
-      lst[tid] = bb;
+      lst_off[tid] = blk_off[bb];
       sz = blk_off[bb + 1] - blk_off[bb];
     }
     pre[tid + 1] = sz;
     if (tid == 0) pre[0] = 0;
     __syncthreads();
-    for (int off = 1; off < NT; off <<= 1) {
+    for (int off = 1; off < NTH; off <<= 1) {
       const int t = (tid + 1 > off) ? pre[tid + 1 - off] : 0;
       __syncthreads();
       pre[tid + 1] += t;
       __syncthreads();
     }
     const int total = pre[L];
-    for (int k0 = 0; k0 < total; k0 += KT) {
+    const int ntile = (total + KT - 1) / KT;
+    auto step = [&](int t, T* cur, T* nxt) {
+      dma_wait();
       __syncthreads();
-      if (tid < KT) {
-        const int j = k0 + tid;
-        int t = -1;
-        if (j < total) {
-          int lo = 0, hi = L - 1;  // last block with pre[idx] <= j
-          while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (pre[mid] <= j) lo = mid; else hi = mid - 1;
-          }
-          t = perm[blk_off[lst[lo]] + (j - pre[lo])];
+      VFrags<DT, D> vf;
+      if (wave_active) vf.read(cur + C::KTILE, lane);
+      if (t + 1 < ntile) ga.issue(nxt, kin, vin, H, h, wave);
+      if (t + 2 < ntile) ga.lookup((t + 2) * KT, total, L, pre, lst_off, perm);
+      if (wave_active) {
+        ssa_f16v acc = st_tile<DT, D>(cur, qf, zero16(), lane);
+        if (t == ntile - 1) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (t * KT + res_row(r, g) >= total) acc[r] = -INFINITY;
         }
-        tok[tid] = t;
+        st.update(acc, sl2);
+        pv_tile<DT, D>(st, acc, vf);
       }
-      __syncthreads();
-      for (int idx = tid; idx < KT * KCH; idx += NT) {
-        const int key = idx / KCH, ch = idx % KCH;
-        const int t = tok[key];
-        uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
-        if (t >= 0) {
-          const int64_t base = ((int64_t)t * H + h) * D + ch * EPC;
-          kv = *reinterpret_cast<const uint4*>(kin + base);
-          vv = *reinterpret_cast<const uint4*>(vin + base);
-        }
-        *reinterpret_cast<uint4*>(&k_lds[key][ch * EPC]) = kv;
-        const T* ve = reinterpret_cast<const T*>(&vv);
-#pragma unroll
-        for (int e = 0; e < EPC; ++e) v_lds[ch * EPC + e][key] = ve[e];
-      }
-      __syncthreads();
-      if (!wave_active) continue;
-      ssa_f16v acc;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[r] = 0.f;
-#pragma unroll
-      for (int ks = 0; ks < Fr::NKS; ++ks)
-        acc = Tr<DT>::mma(load_frag<DT>(&k_lds[c][ks * Fr::KS + g * Fr::KPL]), qf[ks], acc);
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int j = k0 + res_row(r, g);
-        acc[r] = j < total ? acc[r] * sl2 : -INFINITY;
-      }
-      st.update(acc);
-      pv_tile<DT, D>(st, acc, &v_lds[0][0], c, g);
+    };
+    ga.lookup(0, total, L, pre, lst_off, perm);
+    ga.issue(stage0, kin, vin, H, h, wave);
+    if (ntile > 1) ga.lookup(KT, total, L, pre, lst_off, perm);
+    for (int t = 0; t < ntile; t += 2) {
+      step(t, stage0, stage1);
+      if (t + 1 < ntile) step(t + 1, stage1, stage0);
     }
+    dma_wait();
   }
 }
 
+// One workgroup per (128-row chunk of a query block, head); grid = lpt rank x chunk x head.
 template <int DT, int D>
-__global__ __launch_bounds__(NT) void k_attend(
+__global__ __launch_bounds__(64 * ATT_WAVES) __attribute__((amdgpu_waves_per_eu(2))) void k_attend(
     const typename Tr<DT>::T* __restrict__ q, const typename Tr<DT>::T* __restrict__ kin,
     const typename Tr<DT>::T* __restrict__ vin, const typename Tr<DT>::T* __restrict__ gates,
     const int32_t* __restrict__ perm, const int32_t* __restrict__ blk_off,
     const int32_t* __restrict__ blk_cell, const int32_t* __restrict__ cell_off,
     const int32_t* __restrict__ cell_blk, const int32_t* __restrict__ lpt,
     const int32_t* __restrict__ sel, const typename Tr<DT>::T* __restrict__ oc, int M, int H,
-    int64_t N, int topk, float sl2, typename Tr<DT>::T* __restrict__ out) {
-  using Fr = Frags<DT, D>;
+    int nchunk, int64_t N, int topk, float sl2, typename Tr<DT>::T* __restrict__ out) {
+  using C = Cfg<DT, D>;
   using T = typename Tr<DT>::T;
   using F = typename Tr<DT>::frag;
-  __shared__ __attribute__((aligned(16))) T k_lds[KT][Fr::KROW];
-  __shared__ __attribute__((aligned(16))) T v_lds[D][Fr::VROW];
-  __shared__ int32_t pre[NT + 1];
-  __shared__ int32_t lst[NT];
-  __shared__ int32_t tok[KT];
+  constexpr int NTH = 64 * ATT_WAVES;
+  __shared__ __attribute__((aligned(1024))) T stage0[C::KTILE + C::VTILE];
+  __shared__ __attribute__((aligned(1024))) T stage1[C::KTILE + C::VTILE];
+  __shared__ int32_t pre[NTH + 1];
+  __shared__ int32_t lst_off[NTH];
   __shared__ int32_t sel_lds[256];
+  // the selected branch's weighted output, parked while the window branch runs
+  __shared__ float res_lds[ATT_WAVES][C::NDV * 16][64];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 5, c = lane & 31;
   const int h = blockIdx.x % H;
-  const int b = lpt[blockIdx.x / H];
+  const int chunk = (blockIdx.x / H) % nchunk;
+  const int b = lpt[blockIdx.x / (H * nchunk)];
   const int r0 = blk_off[b], rows = blk_off[b + 1] - r0;
-  // selected block list (valid ids)
+  if (chunk * ATT_ROWS >= rows) return;  // uniform across the workgroup
   int nsel = 0;
-  for (int t = 0; t < topk; ++t) nsel += sel[((int64_t)h * M + b) * topk + t] >= 0;
-  for (int t = tid; t < nsel; t += NT) sel_lds[t] = sel[((int64_t)h * M + b) * topk + t];
+  const int32_t* srow = sel + ((int64_t)h * M + b) * topk;
+  for (int t = 0; t < topk; ++t) nsel += srow[t] >= 0;
+  for (int t = tid; t < nsel; t += NTH) sel_lds[t] = srow[t];
   const int cell = blk_cell[b];
   const int c0 = cell_off[cell], c1 = cell_off[cell + 1];
 
-  for (int sw = 0; sw * ROWS_PER_SWEEP < rows; ++sw) {
-    const int row_base = sw * ROWS_PER_SWEEP + wave * 32;
-    const bool wave_active = row_base < rows;
-    const int my_row = row_base + c;
-    const bool valid = my_row < rows;
-    const int64_t tok_q = valid ? perm[r0 + my_row] : 0;
-    F qf[Fr::NKS];
-    {
-      const T* qrow = q + (tok_q * H + h) * D;
+  const int row_base = chunk * ATT_ROWS + wave * 32;
+  const bool wave_active = row_base < rows;
+  const int my_row = row_base + c;
+  const bool valid = my_row < rows;
+  const int64_t tok_q = valid ? perm[r0 + my_row] : 0;
+  F qf[C::NKS];
+  load_q<DT, D>(qf, q + (tok_q * H + h) * D, valid, lane);
+  Gather<DT, D> ga;
+  ga.init(wave, lane);
+
+  Online<C::NDV> st;
+  gathered_branch<DT, D>(st, ga, sel_lds, nsel, qf, kin, vin, perm, blk_off, H, h, sl2, wave_active,
+                         stage0, stage1, pre, lst_off);
+  {
+    const float g1 = valid ? Tr<DT>::up(gates[(tok_q * H + h) * 3 + 1]) : 0.f;
+    const float f = g1 / xor32_sum(st.l);
 #pragma unroll
-      for (int s = 0; s < Fr::NKS; ++s)
-        qf[s] = valid ? load_frag<DT>(qrow + s * Fr::KS + g * Fr::KPL) : zero_frag<DT>();
-    }
-    float gate[3] = {0.f, 0.f, 0.f};
-    if (valid)
-      for (int x = 0; x < 3; ++x) gate[x] = Tr<DT>::up(gates[(tok_q * H + h) * 3 + x]);
-    // result = g0 * o_c
-    ssa_f16v res[Fr::NDV];
-    {
-      const T* orow = oc + ((int64_t)h * N + r0 + (valid ? my_row : 0)) * D;
+    for (int j = 0; j < C::NDV; ++j)
 #pragma unroll
-      for (int j = 0; j < Fr::NDV; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) res[j][r] = valid ? gate[0] * Tr<DT>::up(orow[32 * j + res_row(r, g)]) : 0.f;
-    }
-    Online<Fr::NDV> st;
-    gathered_branch<DT, D>(st, sel_lds, nsel, qf, kin, vin, perm, blk_off, H, h, sl2, wave_active,
-                           k_lds, v_lds, pre, lst, tok);
-    {
-      const float ltot = st.l + __shfl_xor(st.l, 32);
-      const float f = gate[1] / ltot;
-#pragma unroll
-      for (int j = 0; j < Fr::NDV; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) res[j][r] += f * st.o[j][r];
-    }
-    gathered_branch<DT, D>(st, cell_blk + c0, c1 - c0, qf, kin, vin, perm, blk_off, H, h, sl2,
-                           wave_active, k_lds, v_lds, pre, lst, tok);
-    {
-      const float ltot = st.l + __shfl_xor(st.l, 32);
-      const float f = gate[2] / ltot;
-#pragma unroll
-      for (int j = 0; j < Fr::NDV; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) res[j][r] += f * st.o[j][r];
-    }
-    if (wave_active && valid) {
-      T* orow = out + (tok_q * H + h) * D;
-#pragma unroll
-      for (int j = 0; j < Fr::NDV; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) orow[32 * j + res_row(r, g)] = Tr<DT>::cvt(res[j][r]);
-    }
+      for (int r = 0; r < 16; ++r) res_lds[wave][j * 16 + r][lane] = st.o[j][r] * f;
   }
+  gathered_branch<DT, D>(st, ga, cell_blk + c0, c1 - c0, qf, kin, vin, perm, blk_off, H, h, sl2,
+                         wave_active, stage0, stage1, pre, lst_off);
+  const float ltot = xor32_sum(st.l);
+  if (wave_active && valid) {
+    const float g0 = Tr<DT>::up(gates[(tok_q * H + h) * 3 + 0]);
+    const float g2 = Tr<DT>::up(gates[(tok_q * H + h) * 3 + 2]);
+    const float f = g2 / ltot;
+    const T* orow = oc + ((int64_t)h * N + r0 + my_row) * D;
+    T* dst = out + (tok_q * H + h) * D;
+#pragma unroll
+    for (int j = 0; j < C::NDV; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int dv = 32 * j + res_row(r, g);
+        dst[dv] = Tr<DT>::cvt(res_lds[wave][j * 16 + r][lane] + f * st.o[j][r] + g0 * Tr<DT>::up(orow[dv]));
+      }
+  }
+}
+
+// ------------------------------------------------------------------ launchers
+template <int DT, int D>
+hipError_t run_pool(const ssa_plan_s* p, int H, const void* k, const void* v, const void* wk,
+                    const void* wv, const FwdWs& w, hipStream_t s) {
+  using T = typename Tr<DT>::T;
+  const int Mp = (int)round_up(p->M, KT);
+  hipLaunchKernelGGL((k_pool<DT, D>), dim3(Mp, H), dim3(256), 0, s, (const T*)k, (const T*)v,
+                     (const T*)wk, (const T*)wv, p->perm, p->blk_off, (int)p->M, Mp, H, (T*)w.pooled);
+  return hipGetLastError();
 }
 
 template <int DT, int D>
@@ -553,9 +680,9 @@ hipError_t run_select(const ssa_plan_s* p, int H, int topk, float sl2, const voi
   using T = typename Tr<DT>::T;
   const int Mp = (int)round_up(p->M, KT);
   const size_t shm = (size_t)Mp * sizeof(float);
-  hipLaunchKernelGGL((k_select<DT, D>), dim3((unsigned)(p->M * H)), dim3(NT), shm, s,
-                     (const T*)q, (const T*)w.ksplit, (const T*)w.vtil_t, p->perm, p->blk_off,
-                     p->lpt, (int)p->M, Mp, H, p->n, sl2, topk, (T*)w.oc, sel);
+  hipLaunchKernelGGL((k_select<DT, D>), dim3((unsigned)(p->M * H)), dim3(64 * SEL_WAVES), shm, s,
+                     (const T*)q, (const T*)w.pooled, p->perm, p->blk_off, p->lpt, (int)p->M, Mp, H,
+                     p->n, sl2, topk, (T*)w.oc, sel);
   return hipGetLastError();
 }
 
@@ -564,24 +691,24 @@ hipError_t run_attend(const ssa_plan_s* p, int H, int topk, float sl2, const voi
                       const void* k, const void* v, const void* gates, const FwdWs& w,
                       const int32_t* sel, void* out, hipStream_t s) {
   using T = typename Tr<DT>::T;
-  hipLaunchKernelGGL((k_attend<DT, D>), dim3((unsigned)(p->M * H)), dim3(NT), 0, s, (const T*)q,
-                     (const T*)k, (const T*)v, (const T*)gates, p->perm, p->blk_off, p->blk_cell,
-                     p->cell_off, p->cell_blk, p->lpt, sel, (const T*)w.oc, (int)p->M, H, p->n,
-                     topk, sl2, (T*)out);
+  const int nchunk = (p->max_rows + ATT_ROWS - 1) / ATT_ROWS;
+  hipLaunchKernelGGL((k_attend<DT, D>), dim3((unsigned)(p->M * H * nchunk)), dim3(64 * ATT_WAVES), 0,
+                     s, (const T*)q, (const T*)k, (const T*)v, (const T*)gates, p->perm, p->blk_off,
+                     p->blk_cell, p->cell_off, p->cell_blk, p->lpt, sel, (const T*)w.oc, (int)p->M,
+                     H, nchunk, p->n, topk, sl2, (T*)out);
   return hipGetLastError();
 }
 
 template <int DT>
-hipError_t run_pool(const ssa_plan_s* p, int H, int d, const void* k, const void* v,
-                    const void* wk, const void* wv, const FwdWs& w, hipStream_t s) {
-  using T = typename Tr<DT>::T;
-  const int Mp = (int)round_up(p->M, KT);
-  const int VEC = 16 / sizeof(T), CH = d / VEC, RSUB = 256 / CH;
-  const size_t shm = (size_t)(2 * RSUB * d + 2 * d) * sizeof(float);
-  hipLaunchKernelGGL((k_pool<DT>), dim3(Mp, H), dim3(256), shm, s, (const T*)k, (const T*)v,
-                     (const T*)wk, (const T*)wv, p->perm, p->blk_off, (int)p->M, Mp, H, d,
-                     (T*)w.ksplit, (T*)w.vtil_t);
-  return hipGetLastError();
+hipError_t pool_d(int d, const ssa_plan_s* p, int H, const void* k, const void* v, const void* wk,
+                  const void* wv, const FwdWs& w, hipStream_t s) {
+  switch (d) {
+    case 32: return run_pool<DT, 32>(p, H, k, v, wk, wv, w, s);
+    case 64: return run_pool<DT, 64>(p, H, k, v, wk, wv, w, s);
+    case 96: return run_pool<DT, 96>(p, H, k, v, wk, wv, w, s);
+    case 128: return run_pool<DT, 128>(p, H, k, v, wk, wv, w, s);
+  }
+  return hipErrorInvalidValue;
 }
 
 template <int DT>
@@ -615,9 +742,9 @@ hipError_t launch_pool(ssa_dtype dt, const ssa_plan_s* p, int H, int d, const vo
                        const void* v, const void* wk, const void* wv, const FwdWs& w,
                        hipStream_t s) {
   switch (dt) {
-    case SSA_F32: return run_pool<DT_F32>(p, H, d, k, v, wk, wv, w, s);
-    case SSA_F16: return run_pool<DT_F16>(p, H, d, k, v, wk, wv, w, s);
-    case SSA_BF16: return run_pool<DT_BF16>(p, H, d, k, v, wk, wv, w, s);
+    case SSA_F32: return pool_d<DT_F32>(d, p, H, k, v, wk, wv, w, s);
+    case SSA_F16: return pool_d<DT_F16>(d, p, H, k, v, wk, wv, w, s);
+    case SSA_BF16: return pool_d<DT_BF16>(d, p, H, k, v, wk, wv, w, s);
   }
   return hipErrorInvalidValue;
 }

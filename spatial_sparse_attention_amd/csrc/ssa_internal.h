@@ -42,18 +42,28 @@ struct PlanWs {
 };
 size_t plan_carve(Carver& c, int64_t n, PlanWs* w);
 
+static inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+static inline int nsplit_of(ssa_dtype dt) { return dt == SSA_F32 ? 1 : (dt == SSA_F16 ? 2 : 3); }
+static inline size_t esize_of(ssa_dtype dt) { return dt == SSA_F32 ? 4 : 2; }
+
+// Row strides (elements) of the padded 32-row tiles staged in LDS.  The pooled keys and
+// values are stored in HBM as one "stage" per (head, 32-block tile): the NSPLIT key planes
+// ([32][krow] each) followed by the value tile ([32][vrow]), exactly the LDS layout, so a
+// tile is one contiguous copy.
+static inline int krow_of(ssa_dtype dt, int d) { return d + (dt == SSA_F32 ? 4 : 8); }
+static inline int vrow_of(ssa_dtype dt, int d) { return d + (dt == SSA_F32 ? 8 : 16); }
+static inline int64_t stage_elems(ssa_dtype dt, int d) {
+  return (int64_t)32 * (nsplit_of(dt) * krow_of(dt, d) + vrow_of(dt, d));
+}
+
 // Forward workspace layout.
 struct FwdWs {
-  void* ksplit;      // [nsplit][H][Mp][d] dtype (f32: one fp32 plane)
-  void* vtil_t;      // [H][d][Mp] dtype (f32 for F32)
+  void* pooled;      // [H][Mp/32][stage] dtype: pooled key planes + pooled values, padding zero
   void* oc;          // [H][N][d] compressed-branch output, block-sorted rows (dtype)
   int32_t* sel;      // [H][M][topk]
 };
 size_t fwd_carve(Carver& c, const ssa_plan_s* p, ssa_dtype dt, int H, int d, int topk, FwdWs* w);
 
-static inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
-static inline int nsplit_of(ssa_dtype dt) { return dt == SSA_F32 ? 1 : (dt == SSA_F16 ? 2 : 3); }
-static inline size_t esize_of(ssa_dtype dt) { return dt == SSA_F32 ? 4 : 2; }
 
 #define SSA_HIP_CHECK(expr)                          \
   do {                                               \

@@ -60,4 +60,15 @@ __device__ inline typename Tr<DT>::frag load_frag(const typename Tr<DT>::T* p) {
 __device__ inline int res_row(int r, int g) { return 8 * (r >> 2) + 4 * g + (r & 3); }
 
 __device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// gfx950 LDS transpose read (ds_read_b64_tr_b16).  Within each group of 16 lanes,
+// source lane i = 4t + a points at 4 consecutive 16-bit values S[i][0..3];
+// destination lane j receives S[4t + j/4][j%4] for t = 0..3.  Pointing source lane
+// 4t + a at row (r0 + t), column (c0 + 4a) of a row-major matrix gives lane j the
+// column c0 + j of rows r0..r0+3.
+typedef short ssa_s4 __attribute__((ext_vector_type(4)));
+__device__ inline ssa_s4 lds_read_tr16(const void* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) ssa_s4*)(p));
+}
 __device__ inline float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
