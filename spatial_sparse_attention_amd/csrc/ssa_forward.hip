@@ -23,15 +23,18 @@
 // planes whose sum reproduces the fp32 value, so the scores that decide the top-k
 // carry fp32-level error.
 #include <hip/hip_runtime.h>
+#include <type_traits>
 #include "ssa_internal.h"
 #include "ssa_mfma.h"
 
 namespace {
 
 constexpr int KT = 32;            // keys per tile
-constexpr int SEL_WAVES = 8;      // compressed/select workgroup: 8 waves, 256 rows per sweep
-constexpr int ATT_WAVES = 4;      // attend workgroup: 4 waves, 128 rows per chunk
-constexpr int ATT_ROWS = 32 * ATT_WAVES;
+constexpr int SEL_RT = 1;         // compressed/select: 32-row query tiles per wave
+constexpr int SEL_WAVES = 8;      //   and waves per workgroup (256 rows per sweep)
+constexpr int ATT_RT = 2;         // selected/window: 32-row query tiles per wave
+constexpr int ATT_WAVES = 4;      //   and waves per workgroup (256 rows per chunk)
+constexpr int ATT_ROWS = 32 * ATT_RT * ATT_WAVES;
 constexpr float RESCALE_SLACK = 8.f;  // log2 units the running max may lag the true max
 
 // ------------------------------------------------------------------ tile geometry
@@ -320,7 +323,8 @@ __device__ inline void dma_contiguous(void* lds, const void* g, int nchunks, int
 }
 
 // ------------------------------------------------------------------ compressed + select
-// One workgroup per (query block, head), longest blocks first.
+// One workgroup per (query block, head), longest blocks first.  Each wave owns RT row
+// tiles of 32 queries, so every K or V fragment read from LDS feeds RT MFMAs.
 template <int DT, int D>
 __global__ __launch_bounds__(64 * SEL_WAVES) void k_select(
     const typename Tr<DT>::T* __restrict__ q, const typename Tr<DT>::T* __restrict__ pooled,
@@ -331,7 +335,8 @@ __global__ __launch_bounds__(64 * SEL_WAVES) void k_select(
   using T = typename Tr<DT>::T;
   using F = typename Tr<DT>::frag;
   constexpr int NS = C::NS;
-  constexpr int ROWS = 32 * SEL_WAVES;
+  constexpr int RT = SEL_RT;
+  constexpr int ROWS = 32 * RT * SEL_WAVES;
   __shared__ __attribute__((aligned(1024))) T stage0[C::STAGE];
   __shared__ __attribute__((aligned(1024))) T stage1[C::STAGE];
   __shared__ float stage_sum[2][SEL_WAVES][32];
@@ -349,16 +354,21 @@ __global__ __launch_bounds__(64 * SEL_WAVES) void k_select(
   constexpr int NCH1 = C::STAGE * sizeof(T) / 16, NCH2 = NS * C::KCH;
 
   for (int sw = 0; sw * ROWS < rows; ++sw) {
-    const int row_base = sw * ROWS + wave * 32;
-    const bool wave_active = row_base < rows;
-    const int my_row = row_base + c;
-    const bool valid = my_row < rows;
-    F qf[C::NKS];
-    load_q<DT, D>(qf, q + ((int64_t)(valid ? perm[r0 + my_row] : 0) * H + h) * D, valid, lane);
+    const int wbase = sw * ROWS + wave * 32 * RT;   // first row of this wave
+    const bool wave_active = wbase < rows;
+    F qf[RT][C::NKS];
+    bool valid[RT];
+#pragma unroll
+    for (int u = 0; u < RT; ++u) {
+      const int my_row = wbase + 32 * u + c;
+      valid[u] = my_row < rows;
+      load_q<DT, D>(qf[u], q + ((int64_t)(valid[u] ? perm[r0 + my_row] : 0) * H + h) * D, valid[u], lane);
+    }
 
     // ---------------- pass 1: online softmax over all pooled keys -> o_c, lse
-    Online<C::NDV> st;
-    st.init();
+    Online<C::NDV> st[RT];
+#pragma unroll
+    for (int u = 0; u < RT; ++u) st[u].init();
     {
       auto p1 = [&](int t, T* cur, T* nxt) {
         dma_wait();
@@ -367,16 +377,35 @@ __global__ __launch_bounds__(64 * SEL_WAVES) void k_select(
         if (wave_active) vf.read(cur + NS * C::KTILE, lane);
         if (t + 1 < ntile) dma_contiguous<SEL_WAVES>(nxt, pstage + (int64_t)(t + 1) * C::STAGE, NCH1, wave, lane);
         if (wave_active) {
-          ssa_f16v acc = zero16();
+          ssa_f16v acc[RT];
 #pragma unroll
-          for (int s = 0; s < NS; ++s) acc = st_tile<DT, D>(cur + s * C::KTILE, qf, acc, lane);
-          if (t == ntile - 1) {
+          for (int u = 0; u < RT; ++u) acc[u] = zero16();
+          const T* krow = cur + (lane & 31) * C::KROW + (lane >> 5) * C::KPL;
 #pragma unroll
-            for (int r = 0; r < 16; ++r)
-              if (t * KT + res_row(r, g) >= M) acc[r] = -INFINITY;
+          for (int s = 0; s < NS; ++s)
+#pragma unroll
+            for (int ks = 0; ks < C::NKS; ++ks) {
+              const F kf = load_frag<DT>(krow + s * C::KTILE + ks * C::KS);
+#pragma unroll
+              for (int u = 0; u < RT; ++u) acc[u] = Tr<DT>::mma(kf, qf[u][ks], acc[u]);
+            }
+#pragma unroll
+          for (int u = 0; u < RT; ++u) {
+            if (t == ntile - 1) {
+#pragma unroll
+              for (int r = 0; r < 16; ++r)
+                if (t * KT + res_row(r, g) >= M) acc[u][r] = -INFINITY;
+            }
+            st[u].update(acc[u], sl2);
           }
-          st.update(acc, sl2);
-          pv_tile<DT, D>(st, acc, vf);
+#pragma unroll
+          for (int ks = 0; ks < C::PK; ++ks)
+#pragma unroll
+            for (int u = 0; u < RT; ++u) {
+              const F pf = p_frag<DT>(acc[u], ks);
+#pragma unroll
+              for (int j = 0; j < C::NDV; ++j) st[u].o[j] = Tr<DT>::mma(vf.f[ks][j], pf, st[u].o[j]);
+            }
         }
       };
       __syncthreads();  // the previous sweep is done with both stage buffers
@@ -386,23 +415,29 @@ __global__ __launch_bounds__(64 * SEL_WAVES) void k_select(
         if (t + 1 < ntile) p1(t + 1, stage1, stage0);
       }
     }
-    const float ltot = xor32_sum(st.l);
-    if (wave_active && valid) {
-      const float inv = 1.f / ltot;
-      T* orow = oc + ((int64_t)h * N + r0 + my_row) * D;
 #pragma unroll
-      for (int j = 0; j < C::NDV; ++j)
+    for (int u = 0; u < RT; ++u) {
+      const float ltot = xor32_sum(st[u].l);
+      const int my_row = wbase + 32 * u + c;
+      if (wave_active && valid[u]) {
+        const float inv = 1.f / ltot;
+        T* orow = oc + ((int64_t)h * N + r0 + my_row) * D;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) orow[32 * j + res_row(r, g)] = Tr<DT>::cvt(st.o[j][r] * inv);
+        for (int j = 0; j < C::NDV; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) orow[32 * j + res_row(r, g)] = Tr<DT>::cvt(st[u].o[j][r] * inv);
+      }
+      // rows past the block get +inf, so their probabilities in pass 2 are exactly zero
+      if (g == 0) lse_lds[wave * 32 * RT + 32 * u + c] = valid[u] ? st[u].m + fast_log2(ltot) : INFINITY;
     }
-    // rows past the block get +inf, so their probabilities in pass 2 are exactly zero
-    if (g == 0) lse_lds[wave * 32 + c] = valid ? st.m + fast_log2(ltot) : INFINITY;
     __syncthreads();
 
     // ---------------- pass 2: importance column sums (S layout)
-    float lrow[16];
+    float lrow[RT][16];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) lrow[r] = lse_lds[wave * 32 + res_row(r, g)];
+    for (int u = 0; u < RT; ++u)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) lrow[u][r] = lse_lds[wave * 32 * RT + 32 * u + res_row(r, g)];
     {
       auto fold = [&](int t) {  // sum the per-wave column sums of tile t into sigma (fixed order)
         if (tid < 32) {
@@ -420,11 +455,22 @@ __global__ __launch_bounds__(64 * SEL_WAVES) void k_select(
         if (t > 0) fold(t - 1);
         float colsum = 0.f;
         if (wave_active) {
-          ssa_f16v acc = zero16();
+          ssa_f16v acc[RT];
 #pragma unroll
-          for (int s = 0; s < NS; ++s) acc = s_tile<DT, D>(cur + s * C::KTILE, qf, acc, lane);
+          for (int u = 0; u < RT; ++u) acc[u] = zero16();
+          const T* krow = cur + (lane & 31) * C::KROW + (lane >> 5) * C::KPL;
 #pragma unroll
-          for (int r = 0; r < 16; ++r) colsum += fast_exp2(__builtin_fmaf(acc[r], sl2, -lrow[r]));
+          for (int s = 0; s < NS; ++s)
+#pragma unroll
+            for (int ks = 0; ks < C::NKS; ++ks) {
+              const F kf = load_frag<DT>(krow + s * C::KTILE + ks * C::KS);
+#pragma unroll
+              for (int u = 0; u < RT; ++u) acc[u] = Tr<DT>::mma(qf[u][ks], kf, acc[u]);
+            }
+#pragma unroll
+          for (int u = 0; u < RT; ++u)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) colsum += fast_exp2(__builtin_fmaf(acc[u][r], sl2, -lrow[u][r]));
           colsum = xor32_sum(colsum);
         }
         if (g == 0) stage_sum[t & 1][wave][c] = colsum;
@@ -505,8 +551,8 @@ struct Gather {
     for (int m = 0; m < NI; ++m) {
       int j = k0 + (row[m] < 0 ? 0 : row[m]);
       if (j >= total) j = 0;
-      int lo = 0, hi = L - 1;  // last list entry starting at or before key j
-      while (lo < hi) {
+      int lo = 0, hi = L - 1;  // last list entry starting at or before key j (none to search
+      while (lo < hi) {        // when the list is one block)
         const int mid = (lo + hi + 1) >> 1;
         if (pre[mid] <= j) lo = mid; else hi = mid - 1;
       }
@@ -528,16 +574,18 @@ struct Gather {
 
 template <int DT, int D>
 __device__ inline void gathered_branch(
-    Online<D / 32>& st, const Gather<DT, D>& ga0, const int32_t* blist, int nlist,
-    const typename Tr<DT>::frag* qf, const typename Tr<DT>::T* __restrict__ kin,
+    Online<D / 32>* st, const Gather<DT, D>& ga0, const int32_t* blist, int nlist,
+    const typename Tr<DT>::frag (*qf)[Cfg<DT, D>::NKS], const typename Tr<DT>::T* __restrict__ kin,
     const typename Tr<DT>::T* __restrict__ vin, const int32_t* __restrict__ perm,
     const int32_t* __restrict__ blk_off, int H, int h, float sl2, bool wave_active,
     typename Tr<DT>::T* stage0, typename Tr<DT>::T* stage1, int32_t* pre, int32_t* lst_off) {
   using C = Cfg<DT, D>;
   using T = typename Tr<DT>::T;
+  using F = typename Tr<DT>::frag;
   constexpr int NTH = 64 * ATT_WAVES;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 5;
-  st.init();
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, wave = tid >> 6;
+#pragma unroll
+  for (int u = 0; u < ATT_RT; ++u) st[u].init();
   Gather<DT, D> ga = ga0;
   for (int l0 = 0; l0 < nlist; l0 += NTH) {
     const int L = min(NTH, nlist - l0);
@@ -551,11 +599,13 @@ __device__ inline void gathered_branch(
     pre[tid + 1] = sz;
     if (tid == 0) pre[0] = 0;
     __syncthreads();
-    for (int off = 1; off < NTH; off <<= 1) {
-      const int t = (tid + 1 > off) ? pre[tid + 1 - off] : 0;
-      __syncthreads();
-      pre[tid + 1] += t;
-      __syncthreads();
+    if (L > 1) {
+      for (int off = 1; off < NTH; off <<= 1) {
+        const int t = (tid + 1 > off) ? pre[tid + 1 - off] : 0;
+        __syncthreads();
+        pre[tid + 1] += t;
+        __syncthreads();
+      }
     }
     const int total = pre[L];
     const int ntile = (total + KT - 1) / KT;
@@ -567,14 +617,33 @@ __device__ inline void gathered_branch(
       if (t + 1 < ntile) ga.issue(nxt, kin, vin, H, h, wave);
       if (t + 2 < ntile) ga.lookup((t + 2) * KT, total, L, pre, lst_off, perm);
       if (wave_active) {
-        ssa_f16v acc = st_tile<DT, D>(cur, qf, zero16(), lane);
-        if (t == ntile - 1) {
+        ssa_f16v acc[ATT_RT];
 #pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if (t * KT + res_row(r, g) >= total) acc[r] = -INFINITY;
+        for (int u = 0; u < ATT_RT; ++u) acc[u] = zero16();
+        const T* krow = cur + (lane & 31) * C::KROW + (lane >> 5) * C::KPL;
+#pragma unroll
+        for (int ks = 0; ks < C::NKS; ++ks) {
+          const F kf = load_frag<DT>(krow + ks * C::KS);
+#pragma unroll
+          for (int u = 0; u < ATT_RT; ++u) acc[u] = Tr<DT>::mma(kf, qf[u][ks], acc[u]);
         }
-        st.update(acc, sl2);
-        pv_tile<DT, D>(st, acc, vf);
+#pragma unroll
+        for (int u = 0; u < ATT_RT; ++u) {
+          if (t == ntile - 1) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+              if (t * KT + res_row(r, g) >= total) acc[u][r] = -INFINITY;
+          }
+          st[u].update(acc[u], sl2);
+        }
+#pragma unroll
+        for (int ks = 0; ks < C::PK; ++ks)
+#pragma unroll
+          for (int u = 0; u < ATT_RT; ++u) {
+            const F pf = p_frag<DT>(acc[u], ks);
+#pragma unroll
+            for (int j = 0; j < C::NDV; ++j) st[u].o[j] = Tr<DT>::mma(vf.f[ks][j], pf, st[u].o[j]);
+          }
       }
     };
     ga.lookup(0, total, L, pre, lst_off, perm);
@@ -588,7 +657,7 @@ __device__ inline void gathered_branch(
   }
 }
 
-// One workgroup per (128-row chunk of a query block, head); grid = lpt rank x chunk x head.
+// One workgroup per (ATT_ROWS-row chunk of a query block, head); grid = lpt rank x chunk x head.
 template <int DT, int D>
 __global__ __launch_bounds__(64 * ATT_WAVES) __attribute__((amdgpu_waves_per_eu(2))) void k_attend(
     const typename Tr<DT>::T* __restrict__ q, const typename Tr<DT>::T* __restrict__ kin,
@@ -607,8 +676,12 @@ __global__ __launch_bounds__(64 * ATT_WAVES) __attribute__((amdgpu_waves_per_eu(
   __shared__ int32_t pre[NTH + 1];
   __shared__ int32_t lst_off[NTH];
   __shared__ int32_t sel_lds[256];
-  // the selected branch's weighted output, parked while the window branch runs
-  __shared__ float res_lds[ATT_WAVES][C::NDV * 16][64];
+  // the selected branch's weighted output, parked in LDS as fp16 while the window branch
+  // runs (16-bit dtypes: the rounding is far below the output dtype's); fp32 keeps it in
+  // registers
+  constexpr bool PARK = DT != DT_F32;
+  __shared__ _Float16 res_lds[PARK ? ATT_WAVES : 1][PARK ? ATT_RT * C::NDV * 16 : 1][64];
+  ssa_f16v res[PARK ? 1 : ATT_RT][PARK ? 1 : C::NDV];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 5, c = lane & 31;
   const int h = blockIdx.x % H;
@@ -623,43 +696,61 @@ __global__ __launch_bounds__(64 * ATT_WAVES) __attribute__((amdgpu_waves_per_eu(
   const int cell = blk_cell[b];
   const int c0 = cell_off[cell], c1 = cell_off[cell + 1];
 
-  const int row_base = chunk * ATT_ROWS + wave * 32;
-  const bool wave_active = row_base < rows;
-  const int my_row = row_base + c;
-  const bool valid = my_row < rows;
-  const int64_t tok_q = valid ? perm[r0 + my_row] : 0;
-  F qf[C::NKS];
-  load_q<DT, D>(qf, q + (tok_q * H + h) * D, valid, lane);
+  const int wbase = chunk * ATT_ROWS + wave * 32 * ATT_RT;
+  const bool wave_active = wbase < rows;
+  F qf[ATT_RT][C::NKS];
+  int64_t tok_q[ATT_RT];
+  bool valid[ATT_RT];
+#pragma unroll
+  for (int u = 0; u < ATT_RT; ++u) {
+    const int my_row = wbase + 32 * u + c;
+    valid[u] = my_row < rows;
+    tok_q[u] = valid[u] ? perm[r0 + my_row] : 0;
+    load_q<DT, D>(qf[u], q + (tok_q[u] * H + h) * D, valid[u], lane);
+  }
   Gather<DT, D> ga;
   ga.init(wave, lane);
 
-  Online<C::NDV> st;
+  Online<C::NDV> st[ATT_RT];
   gathered_branch<DT, D>(st, ga, sel_lds, nsel, qf, kin, vin, perm, blk_off, H, h, sl2, wave_active,
                          stage0, stage1, pre, lst_off);
-  {
-    const float g1 = valid ? Tr<DT>::up(gates[(tok_q * H + h) * 3 + 1]) : 0.f;
-    const float f = g1 / xor32_sum(st.l);
 #pragma unroll
-    for (int j = 0; j < C::NDV; ++j)
+  for (int u = 0; u < ATT_RT; ++u) {
+    const float g1 = valid[u] ? Tr<DT>::up(gates[(tok_q[u] * H + h) * 3 + 1]) : 0.f;
+    const float f = g1 / xor32_sum(st[u].l);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) res_lds[wave][j * 16 + r][lane] = st.o[j][r] * f;
+    for (int j = 0; j < C::NDV; ++j) {
+      if constexpr (PARK) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) res_lds[wave][(u * C::NDV + j) * 16 + r][lane] = (_Float16)(st[u].o[j][r] * f);
+      } else {
+        res[u][j] = st[u].o[j] * f;
+      }
+    }
   }
   gathered_branch<DT, D>(st, ga, cell_blk + c0, c1 - c0, qf, kin, vin, perm, blk_off, H, h, sl2,
                          wave_active, stage0, stage1, pre, lst_off);
-  const float ltot = xor32_sum(st.l);
-  if (wave_active && valid) {
-    const float g0 = Tr<DT>::up(gates[(tok_q * H + h) * 3 + 0]);
-    const float g2 = Tr<DT>::up(gates[(tok_q * H + h) * 3 + 2]);
-    const float f = g2 / ltot;
-    const T* orow = oc + ((int64_t)h * N + r0 + my_row) * D;
-    T* dst = out + (tok_q * H + h) * D;
 #pragma unroll
-    for (int j = 0; j < C::NDV; ++j)
+  for (int u = 0; u < ATT_RT; ++u) {
+    const float ltot = xor32_sum(st[u].l);
+    const int my_row = wbase + 32 * u + c;
+    if (wave_active && valid[u]) {
+      const float g0 = Tr<DT>::up(gates[(tok_q[u] * H + h) * 3 + 0]);
+      const float g2 = Tr<DT>::up(gates[(tok_q[u] * H + h) * 3 + 2]);
+      const float f = g2 / ltot;
+      const T* orow = oc + ((int64_t)h * N + r0 + my_row) * D;
+      T* dst = out + (tok_q[u] * H + h) * D;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int dv = 32 * j + res_row(r, g);
-        dst[dv] = Tr<DT>::cvt(res_lds[wave][j * 16 + r][lane] + f * st.o[j][r] + g0 * Tr<DT>::up(orow[dv]));
-      }
+      for (int j = 0; j < C::NDV; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int dv = 32 * j + res_row(r, g);
+          float rs;
+          if constexpr (PARK) rs = (float)res_lds[wave][(u * C::NDV + j) * 16 + r][lane];
+          else rs = res[u][j][r];
+          dst[dv] = Tr<DT>::cvt(rs + f * st[u].o[j][r] + g0 * Tr<DT>::up(orow[dv]));
+        }
+    }
   }
 }
 

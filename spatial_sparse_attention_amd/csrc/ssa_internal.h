@@ -37,7 +37,7 @@ struct Carver {
 struct PlanWs {
   int32_t *perm, *blk_off, *blk_key, *tok2blk, *blk_cell, *cell_off, *cell_blk, *lpt;
   uint32_t *key_a, *key_b;
-  int32_t *val_a, *val_b, *rank, *hist, *tile_cnt, *counters;
+  int32_t *val_a, *val_b, *rank, *hist, *tile_cnt, *counters, *scan_part;
   int32_t* cell_key;
 };
 size_t plan_carve(Carver& c, int64_t n, PlanWs* w);

@@ -94,6 +94,50 @@ __global__ __launch_bounds__(1024) void k_scan_single(int32_t* __restrict__ a, i
   if (tid == 1023 && total) *total = part[1023];
 }
 
+// Multi-workgroup exclusive scan for long arrays: per-chunk sums, a scan of the chunk
+// sums, then a scan of each chunk plus its offset.
+constexpr int SCHUNK = 4096;  // 256 threads x 16 elements
+
+__global__ __launch_bounds__(256) void k_scan_reduce(const int32_t* __restrict__ a, int len,
+                                                     int32_t* __restrict__ part) {
+  __shared__ int32_t red[256];
+  const int base = blockIdx.x * SCHUNK + threadIdx.x * 16;
+  int s = 0;
+  for (int j = 0; j < 16; ++j) s += base + j < len ? a[base + j] : 0;
+  red[threadIdx.x] = s;
+  __syncthreads();
+  for (int off = 128; off > 0; off >>= 1) {
+    if (threadIdx.x < off) red[threadIdx.x] += red[threadIdx.x + off];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) part[blockIdx.x] = red[0];
+}
+
+__global__ __launch_bounds__(256) void k_scan_apply(int32_t* __restrict__ a, int len,
+                                                    const int32_t* __restrict__ part) {
+  __shared__ int32_t pre[256];
+  const int tid = threadIdx.x;
+  const int base = blockIdx.x * SCHUNK + tid * 16;
+  int v[16], s = 0;
+  for (int j = 0; j < 16; ++j) {
+    v[j] = base + j < len ? a[base + j] : 0;
+    s += v[j];
+  }
+  pre[tid] = s;
+  __syncthreads();
+  for (int off = 1; off < 256; off <<= 1) {
+    const int t = tid >= off ? pre[tid - off] : 0;
+    __syncthreads();
+    pre[tid] += t;
+    __syncthreads();
+  }
+  int run = part[blockIdx.x] + pre[tid] - s;
+  for (int j = 0; j < 16; ++j) {
+    if (base + j < len) a[base + j] = run;
+    run += v[j];
+  }
+}
+
 __global__ __launch_bounds__(RTILE) void k_radix_scatter(
     const uint32_t* __restrict__ kin, const int32_t* __restrict__ vin, int n, int shift,
     const int32_t* __restrict__ rank, const int32_t* __restrict__ hist, int tiles,
@@ -208,13 +252,26 @@ inline int bits_for(uint64_t maxval) {
   return b;
 }
 
+// Exclusive scan of a[0..len) in place; `total` (device, may be null) receives the sum.
+// `part` needs len / SCHUNK + 2 ints.
+void device_scan(int32_t* a, int len, int32_t* total, int32_t* part, hipStream_t s) {
+  if (len <= SCHUNK) {
+    hipLaunchKernelGGL(k_scan_single, dim3(1), dim3(1024), 0, s, a, len, total);
+    return;
+  }
+  const int chunks = (len + SCHUNK - 1) / SCHUNK;
+  hipLaunchKernelGGL(k_scan_reduce, dim3(chunks), dim3(256), 0, s, a, len, part);
+  hipLaunchKernelGGL(k_scan_single, dim3(1), dim3(1024), 0, s, part, chunks, total);
+  hipLaunchKernelGGL(k_scan_apply, dim3(chunks), dim3(256), 0, s, a, len, part);
+}
+
 // Stable LSD radix sort of (key, val) pairs; returns which buffers hold the result.
 hipError_t radix_sort(uint32_t*& ka, int32_t*& va, uint32_t*& kb, int32_t*& vb, int n, int nbits,
-                      int32_t* rank, int32_t* hist, hipStream_t s) {
+                      int32_t* rank, int32_t* hist, int32_t* part, hipStream_t s) {
   const int tiles = (n + RTILE - 1) / RTILE;
   for (int shift = 0; shift < nbits; shift += 8) {
     hipLaunchKernelGGL(k_radix_hist, dim3(tiles), dim3(RTILE), 0, s, ka, n, shift, rank, hist, tiles);
-    hipLaunchKernelGGL(k_scan_single, dim3(1), dim3(1024), 0, s, hist, tiles * 256, (int32_t*)nullptr);
+    device_scan(hist, tiles * 256, nullptr, part, s);
     hipLaunchKernelGGL(k_radix_scatter, dim3(tiles), dim3(RTILE), 0, s, ka, va, n, shift, rank, hist,
                        tiles, kb, vb);
     std::swap(ka, kb);
@@ -225,10 +282,10 @@ hipError_t radix_sort(uint32_t*& ka, int32_t*& va, uint32_t*& kb, int32_t*& vb, 
 
 hipError_t segments(const uint32_t* keys, const int32_t* vals, int n, int32_t* tile_cnt,
                     int32_t* total, int32_t* seg_off, int32_t* seg_key, int32_t* elem_seg,
-                    hipStream_t s) {
+                    int32_t* part, hipStream_t s) {
   const int tiles = (n + STILE - 1) / STILE;
   hipLaunchKernelGGL(k_seg_count, dim3(tiles), dim3(256), 0, s, keys, n, tile_cnt);
-  hipLaunchKernelGGL(k_scan_single, dim3(1), dim3(1024), 0, s, tile_cnt, tiles, total);
+  device_scan(tile_cnt, tiles, total, part, s);
   hipLaunchKernelGGL(k_seg_emit, dim3(tiles), dim3(256), 0, s, keys, vals, n, tile_cnt, seg_off,
                      seg_key, elem_seg);
   return hipGetLastError();
@@ -261,6 +318,7 @@ size_t plan_carve(Carver& c, int64_t n, PlanWs* w) {
   t.hist = c.take<int32_t>(tiles * 256);
   t.tile_cnt = c.take<int32_t>((n1 + STILE - 1) / STILE + 1);
   t.counters = c.take<int32_t>(8);
+  t.scan_part = c.take<int32_t>(tiles * 256 / 4096 + 2);
   t.cell_key = c.take<int32_t>(n1);
   if (w) *w = t;
   return c.off;
@@ -324,11 +382,11 @@ extern "C" ssa_status ssa_plan_create(const int32_t* coords, int64_t n, const in
                      w.key_a, w.val_a, w.counters + 7);
   uint32_t *ka = w.key_a, *kb = w.key_b;
   int32_t *va = w.val_a, *vb = w.val_b;
-  if (radix_sort(ka, va, kb, vb, ni, bits_for(nblocks - 1), w.rank, w.hist, stream) != hipSuccess)
+  if (radix_sort(ka, va, kb, vb, ni, bits_for(nblocks - 1), w.rank, w.hist, w.scan_part, stream) != hipSuccess)
     return fail(SSA_ERR_HIP);
   if (hipMemcpyAsync(w.perm, va, n * sizeof(int32_t), hipMemcpyDeviceToDevice, stream) != hipSuccess)
     return fail(SSA_ERR_HIP);
-  if (segments(ka, va, ni, w.tile_cnt, w.counters + 0, w.blk_off, w.blk_key, w.tok2blk, stream) !=
+  if (segments(ka, va, ni, w.tile_cnt, w.counters + 0, w.blk_off, w.blk_key, w.tok2blk, w.scan_part, stream) !=
       hipSuccess)
     return fail(SSA_ERR_HIP);
   if (hipMemcpyAsync(host_cnt, w.counters, sizeof(host_cnt), hipMemcpyDeviceToHost, stream) != hipSuccess ||
@@ -342,7 +400,7 @@ extern "C" ssa_status ssa_plan_create(const int32_t* coords, int64_t n, const in
   hipLaunchKernelGGL(k_block_stats, dim3((M + 255) / 256), dim3(256), 0, stream, w.blk_off, M, ni,
                      w.key_a, w.val_a, w.counters + 1);
   ka = w.key_a; kb = w.key_b; va = w.val_a; vb = w.val_b;
-  if (radix_sort(ka, va, kb, vb, M, bits_for((uint64_t)n), w.rank, w.hist, stream) != hipSuccess)
+  if (radix_sort(ka, va, kb, vb, M, bits_for((uint64_t)n), w.rank, w.hist, w.scan_part, stream) != hipSuccess)
     return fail(SSA_ERR_HIP);
   if (hipMemcpyAsync(w.lpt, va, M * sizeof(int32_t), hipMemcpyDeviceToDevice, stream) != hipSuccess)
     return fail(SSA_ERR_HIP);
@@ -361,11 +419,11 @@ extern "C" ssa_status ssa_plan_create(const int32_t* coords, int64_t n, const in
     hipLaunchKernelGGL(k_cell_keys, dim3((M + 255) / 256), dim3(256), 0, stream, w.blk_key, M,
                        make_int3(dims[0], dims[1], dims[2]), ratio, single, cd, w.key_a, w.val_a);
     ka = w.key_a; kb = w.key_b; va = w.val_a; vb = w.val_b;
-    if (radix_sort(ka, va, kb, vb, M, bits_for(ncmax - 1), w.rank, w.hist, stream) != hipSuccess)
+    if (radix_sort(ka, va, kb, vb, M, bits_for(ncmax - 1), w.rank, w.hist, w.scan_part, stream) != hipSuccess)
       return fail(SSA_ERR_HIP);
     if (hipMemcpyAsync(w.cell_blk, va, M * sizeof(int32_t), hipMemcpyDeviceToDevice, stream) != hipSuccess)
       return fail(SSA_ERR_HIP);
-    if (segments(ka, va, M, w.tile_cnt, w.counters + 2, w.cell_off, nullptr, w.blk_cell, stream) !=
+    if (segments(ka, va, M, w.tile_cnt, w.counters + 2, w.cell_off, nullptr, w.blk_cell, w.scan_part, stream) !=
         hipSuccess)
       return fail(SSA_ERR_HIP);
   }
