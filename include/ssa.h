@@ -106,19 +106,21 @@ void ssa_plan_destroy(ssa_plan plan);
  * scale = 0 means 1/sqrt(d).  wk and wv may alias.  out [N,H,d] (dtype) is
  * written completely.  sel_out, if not NULL, receives the selection int32
  * [H,M,topk] (ascending block ids, -1 padded).  ws: device workspace of at
- * least ssa_forward_workspace_size(...) bytes; distinct concurrent calls need
- * distinct workspaces.  Asynchronous on `stream`; returns SSA_ERR_HIP if a
- * launch fails.  Accumulation is fp32 (the compressed scores that decide the
+ * least ssa_forward_workspace_size(...) bytes, queried with the same
+ * save_for_bwd; distinct concurrent calls need distinct workspaces.  With
+ * save_for_bwd != 0 the workspace also keeps what ssa_backward needs (per-branch
+ * log-sum-exp and branch outputs).  Asynchronous on `stream`; returns SSA_ERR_HIP
+ * if a launch fails.  Accumulation is fp32 (the compressed scores that decide the
  * selection are computed from a split of the fp32 pooled keys into two (f16) or
  * three (bf16) dtype terms, so they carry fp32-level accuracy).
  */
 size_t ssa_forward_workspace_size(ssa_plan plan, ssa_dtype dtype, int32_t heads, int32_t dim,
-                                  int32_t topk);
+                                  int32_t topk, int save_for_bwd);
 ssa_status ssa_forward(ssa_plan plan, ssa_dtype dtype, int32_t heads, int32_t dim,
                        const void* q, const void* k, const void* v, const void* wk,
                        const void* wv, const void* gates, int32_t topk, float scale,
                        void* out, int32_t* sel_out, void* ws, size_t ws_bytes,
-                       hipStream_t stream);
+                       int save_for_bwd, hipStream_t stream);
 
 /*
  * The forward's three stages, for per-stage timing: bit 0 = pooled keys and
@@ -132,7 +134,27 @@ ssa_status ssa_forward_stages(ssa_plan plan, ssa_dtype dtype, int32_t heads, int
                               const void* q, const void* k, const void* v, const void* wk,
                               const void* wv, const void* gates, int32_t topk, float scale,
                               void* out, int32_t* sel_out, void* ws, size_t ws_bytes,
-                              hipStream_t stream, uint32_t stages);
+                              int save_for_bwd, hipStream_t stream, uint32_t stages);
+
+/*
+ * SSA backward (the gradients that a training step at the 80k-voxel shape needs):
+ * given dout = dL/dout [N,H,d] (dtype) and the selection sel [H,M,topk] that the
+ * forward used (held fixed: no gradient flows through the importance scores or the
+ * top-k, and none into W_k, W_v), writes fp32 dq, dk, dv [N,H,d] and dgates
+ * [N,H,3] (order: compressed, selected, window).  fwd_ws is the workspace of an
+ * ssa_forward call with save_for_bwd != 0 on the same plan and inputs (read only).
+ * ws: device workspace of at least ssa_backward_workspace_size(...) bytes.  Every
+ * sum runs in a fixed order (no atomics), so results are bitwise reproducible.
+ * Asynchronous on `stream`.
+ */
+size_t ssa_backward_workspace_size(ssa_plan plan, ssa_dtype dtype, int32_t heads, int32_t dim,
+                                   int32_t topk);
+ssa_status ssa_backward(ssa_plan plan, ssa_dtype dtype, int32_t heads, int32_t dim,
+                        const void* q, const void* k, const void* v, const void* wk,
+                        const void* wv, const void* gates, int32_t topk, float scale,
+                        const int32_t* sel, const void* dout, float* dq, float* dk, float* dv,
+                        float* dgates, const void* fwd_ws, size_t fwd_ws_bytes, void* ws,
+                        size_t ws_bytes, hipStream_t stream);
 
 const char* ssa_status_string(ssa_status status);
 

@@ -2,7 +2,7 @@
 
 Argument marshalling only: every step of the computation runs in the library's
 HIP kernels.  PyTorch supplies device memory (tensors) and the stream.  The
-library must have been built (``python -m spatial_sparse_attention_amd.build``);
+library must have been built (``python spatial_sparse_attention_amd/build.py``);
 importing the binding without it raises immediately.
 """
 from __future__ import annotations
@@ -12,8 +12,8 @@ import os
 
 import torch
 
-__all__ = ["Plan", "forward", "forward_workspace_size", "SSAError", "lib", "LIB_PATH",
-           "STAGE_POOL", "STAGE_SELECT", "STAGE_ATTEND", "STAGE_ALL"]
+__all__ = ["Plan", "forward", "forward_workspace_size", "backward", "backward_workspace_size",
+           "SSAError", "lib", "LIB_PATH", "STAGE_POOL", "STAGE_SELECT", "STAGE_ATTEND", "STAGE_ALL"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libssa.so")
 STAGE_POOL, STAGE_SELECT, STAGE_ATTEND, STAGE_ALL = 1, 2, 4, 7
@@ -37,7 +37,7 @@ class PlanInfo(ctypes.Structure):
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build it with "
-                          "`python -m spatial_sparse_attention_amd.build`")
+                          "`python spatial_sparse_attention_amd/build.py`")
     L = ctypes.CDLL(LIB_PATH)
     grid_t = ctypes.POINTER(_i32)
     L.ssa_plan_workspace_size.argtypes = [_i64, grid_t, _i32, _i32]
@@ -48,14 +48,19 @@ def _load():
     L.ssa_plan_get_info.restype = ctypes.c_int
     L.ssa_plan_destroy.argtypes = [_vp]
     L.ssa_plan_destroy.restype = None
-    L.ssa_forward_workspace_size.argtypes = [_vp, ctypes.c_int, _i32, _i32, _i32]
+    L.ssa_forward_workspace_size.argtypes = [_vp, ctypes.c_int, _i32, _i32, _i32, ctypes.c_int]
     L.ssa_forward_workspace_size.restype = _sz
     fwd = [_vp, ctypes.c_int, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _i32, ctypes.c_float,
-           _vp, _vp, _vp, _sz, _vp]
+           _vp, _vp, _vp, _sz, ctypes.c_int, _vp]
     L.ssa_forward.argtypes = fwd
     L.ssa_forward.restype = ctypes.c_int
     L.ssa_forward_stages.argtypes = fwd + [ctypes.c_uint32]
     L.ssa_forward_stages.restype = ctypes.c_int
+    L.ssa_backward_workspace_size.argtypes = [_vp, ctypes.c_int, _i32, _i32, _i32]
+    L.ssa_backward_workspace_size.restype = _sz
+    L.ssa_backward.argtypes = [_vp, ctypes.c_int, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _i32,
+                               ctypes.c_float, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp, _sz, _vp]
+    L.ssa_backward.restype = ctypes.c_int
     L.ssa_status_string.argtypes = [ctypes.c_int]
     L.ssa_status_string.restype = ctypes.c_char_p
     return L
@@ -137,14 +142,13 @@ class Plan:
             self.handle = None
 
 
-def forward_workspace_size(plan: Plan, dtype, heads: int, dim: int, topk: int) -> int:
-    return int(lib.ssa_forward_workspace_size(plan.handle, _DTYPES[dtype], heads, dim, topk))
+def forward_workspace_size(plan: Plan, dtype, heads: int, dim: int, topk: int,
+                           save_for_bwd: bool = False) -> int:
+    return int(lib.ssa_forward_workspace_size(plan.handle, _DTYPES[dtype], heads, dim, topk,
+                                              int(save_for_bwd)))
 
 
-def forward(plan: Plan, q, k, v, wk, wv, gates, topk: int, scale: float = 0.0, out=None,
-            sel_out=None, ws=None, stream=None, stages: int = STAGE_ALL, want_sel: bool = True):
-    """SSA forward (ssa_forward_stages).  q,k,v [N,H,d], gates [N,H,3], wk,wv [d,d], one dtype.
-    Returns (out [N,H,d], sel [H,M,topk] int32 or None)."""
+def _check_qkv(plan, q, k, v, wk, wv, gates):
     if q.dtype not in _DTYPES:
         raise ValueError(f"unsupported dtype {q.dtype}")
     for t in (q, k, v, wk, wv, gates):
@@ -154,18 +158,60 @@ def forward(plan: Plan, q, k, v, wk, wv, gates, topk: int, scale: float = 0.0, o
     if N != plan.n or k.shape != q.shape or v.shape != q.shape or gates.shape != (N, H, 3) \
             or wk.shape != (d, d) or wv.shape != (d, d):
         raise ValueError("shape mismatch")
+    return N, H, d
+
+
+def forward(plan: Plan, q, k, v, wk, wv, gates, topk: int, scale: float = 0.0, out=None,
+            sel_out=None, ws=None, stream=None, stages: int = STAGE_ALL, want_sel: bool = True,
+            save_for_bwd: bool = False):
+    """SSA forward (ssa_forward_stages).  q,k,v [N,H,d], gates [N,H,3], wk,wv [d,d], one dtype.
+    Returns (out [N,H,d], sel [H,M,topk] int32 or None).  With save_for_bwd, `ws` must be
+    kept and passed to backward()."""
+    N, H, d = _check_qkv(plan, q, k, v, wk, wv, gates)
     dt = _DTYPES[q.dtype]
     if out is None:
         out = torch.empty_like(q)
     if sel_out is None and want_sel:
         sel_out = torch.empty((H, max(plan.num_blocks, 1), topk), dtype=torch.int32, device=q.device)
-    size = lib.ssa_forward_workspace_size(plan.handle, dt, H, d, topk)
+    size = lib.ssa_forward_workspace_size(plan.handle, dt, H, d, topk, int(save_for_bwd))
     if size == 0:
         raise SSAError(2, "ssa_forward_workspace_size")
     if ws is None or ws.numel() < size:
         ws = torch.empty(size, dtype=torch.uint8, device=q.device)
     st = lib.ssa_forward_stages(plan.handle, dt, H, d, _ptr(q), _ptr(k), _ptr(v), _ptr(wk),
                                 _ptr(wv), _ptr(gates), int(topk), float(scale), _ptr(out),
-                                _ptr(sel_out), _ptr(ws), ws.numel(), _stream(stream), int(stages))
+                                _ptr(sel_out), _ptr(ws), ws.numel(), int(save_for_bwd),
+                                _stream(stream), int(stages))
     _check(st, "ssa_forward")
     return out, sel_out
+
+
+def backward_workspace_size(plan: Plan, dtype, heads: int, dim: int, topk: int) -> int:
+    return int(lib.ssa_backward_workspace_size(plan.handle, _DTYPES[dtype], heads, dim, topk))
+
+
+def backward(plan: Plan, q, k, v, wk, wv, gates, topk: int, sel, dout, fwd_ws, scale: float = 0.0,
+             ws=None, stream=None):
+    """SSA backward (ssa_backward) with the selection `sel` held fixed.  fwd_ws: the workspace
+    of a forward run with save_for_bwd=True on the same inputs.  Returns fp32
+    (dq, dk, dv, dgates)."""
+    N, H, d = _check_qkv(plan, q, k, v, wk, wv, gates)
+    if dout.shape != q.shape or dout.dtype != q.dtype or not dout.is_contiguous():
+        raise ValueError("dout must match q")
+    if sel.dtype != torch.int32 or not sel.is_contiguous():
+        raise ValueError("sel must be a contiguous int32 tensor [H, M, topk]")
+    dt = _DTYPES[q.dtype]
+    f32 = dict(dtype=torch.float32, device=q.device)
+    dq, dk, dv = torch.empty(q.shape, **f32), torch.empty(q.shape, **f32), torch.empty(q.shape, **f32)
+    dg = torch.empty((N, H, 3), **f32)
+    size = lib.ssa_backward_workspace_size(plan.handle, dt, H, d, topk)
+    if size == 0:
+        raise SSAError(2, "ssa_backward_workspace_size")
+    if ws is None or ws.numel() < size:
+        ws = torch.empty(size, dtype=torch.uint8, device=q.device)
+    st = lib.ssa_backward(plan.handle, dt, H, d, _ptr(q), _ptr(k), _ptr(v), _ptr(wk), _ptr(wv),
+                          _ptr(gates), int(topk), float(scale), _ptr(sel), _ptr(dout), _ptr(dq),
+                          _ptr(dk), _ptr(dv), _ptr(dg), _ptr(fwd_ws), fwd_ws.numel(), _ptr(ws),
+                          ws.numel(), _stream(stream))
+    _check(st, "ssa_backward")
+    return dq, dk, dv, dg

@@ -1,4 +1,4 @@
-"""Build libssa.so (HIP, gfx950) in-tree with hipcc.  Usage: python -m spatial_sparse_attention_amd.build"""
+"""Build libssa.so (HIP, gfx950) in-tree with hipcc.  Usage: python spatial_sparse_attention_amd/build.py"""
 import concurrent.futures
 import os
 import subprocess
@@ -8,7 +8,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libssa.so")
-SOURCES = ["ssa_plan.hip", "ssa_forward.hip", "ssa_api.hip"]
+SOURCES = ["ssa_plan.hip", "ssa_forward.hip", "ssa_backward.hip", "ssa_api.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

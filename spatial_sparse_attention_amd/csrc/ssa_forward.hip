@@ -26,36 +26,16 @@
 #include <type_traits>
 #include "ssa_internal.h"
 #include "ssa_mfma.h"
+#include "ssa_tiles.h"
 
 namespace {
 
-constexpr int KT = 32;            // keys per tile
+using namespace ssa_dev;
 constexpr int SEL_RT = 1;         // compressed/select: 32-row query tiles per wave
 constexpr int SEL_WAVES = 8;      //   and waves per workgroup (256 rows per sweep)
 constexpr int ATT_RT = 2;         // selected/window: 32-row query tiles per wave
 constexpr int ATT_WAVES = 4;      //   and waves per workgroup (256 rows per chunk)
 constexpr int ATT_ROWS = 32 * ATT_RT * ATT_WAVES;
-constexpr float RESCALE_SLACK = 8.f;  // log2 units the running max may lag the true max
-
-// ------------------------------------------------------------------ tile geometry
-template <int DT, int D>
-struct Cfg {
-  using T = typename Tr<DT>::T;
-  using F = typename Tr<DT>::frag;
-  static constexpr int NS = Tr<DT>::NSPLIT;
-  static constexpr int KS = Tr<DT>::KS, KPL = Tr<DT>::KPL;
-  static constexpr int NKS = D / KS;                    // K steps over the head dim
-  static constexpr int NDV = D / 32;                    // 32-wide output column tiles
-  static constexpr int EPC = 16 / sizeof(T);            // elements per 16-byte chunk
-  static constexpr int CPR = D / EPC;                   // data chunks per row
-  static constexpr int KROW = D + 16 / sizeof(T);       // K tile row (b128 fragment reads)
-  static constexpr int VROW = D + 32 / sizeof(T);       // V tile row (transpose reads)
-  static constexpr int KTILE = KT * KROW, VTILE = KT * VROW;
-  static constexpr int KCH = KTILE * sizeof(T) / 16;    // 16-byte chunks of a K tile
-  static constexpr int VCH = VTILE * sizeof(T) / 16;
-  static constexpr int STAGE = NS * KTILE + VTILE;      // pooled stage (elements)
-  static constexpr int PK = KT / KS;                    // K steps over a 32-key tile (PV)
-};
 
 // ------------------------------------------------------------------ pooling
 // grid (Mp, H).  ktil[h,b] = mean_{i in b} K[i,h] @ Wk ; same for V.  Writes the fp32
@@ -144,184 +124,6 @@ __global__ __launch_bounds__(256) void k_pool(
   }
 }
 
-// ------------------------------------------------------------------ MFMA building blocks
-// Reduction with the other half of the wave (lanes l and l^32 hold the same query row):
-// v_permlane32_swap returns the pair {x[l], x[l^32]} in its two results.
-__device__ inline float xor32_max(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ inline float xor32_sum(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-// A operand (V^T) of O^T += V^T P^T, K step ks of a 32-key tile stored row-major in LDS
-// (vt[key][dv], row stride VROW), output columns 32*j .. 32*j+31.  Lane l covers
-// dv = 32j + l%32 and the keys held by P^T registers ks*KPL .. ks*KPL + KPL - 1, i.e.
-// keys 16ks + 4g + {0..3} and 16ks + 8 + 4g + {0..3} (g = l/32) for 16-bit types.
-template <int DT, int D>
-__device__ inline typename Tr<DT>::frag vt_frag(const typename Tr<DT>::T* vt, int ks, int j, int lane) {
-  using C = Cfg<DT, D>;
-  if constexpr (C::KPL == 1) {
-    return vt[res_row(ks, lane >> 5) * C::VROW + 32 * j + (lane & 31)];
-  } else {
-    const int i = lane & 15, G = lane >> 4;
-    const typename Tr<DT>::T* p =
-        vt + (16 * ks + 4 * (G >> 1) + (i >> 2)) * C::VROW + 32 * j + 16 * (G & 1) + 4 * (i & 3);
-    typedef unsigned u2 __attribute__((ext_vector_type(2)));
-    typedef unsigned u4 __attribute__((ext_vector_type(4)));
-    const u2 a = __builtin_bit_cast(u2, lds_read_tr16(p));
-    const u2 b = __builtin_bit_cast(u2, lds_read_tr16(p + 8 * C::VROW));
-    const u4 u = {a.x, a.y, b.x, b.y};
-    return __builtin_bit_cast(typename Tr<DT>::frag, u);
-  }
-}
-
-// The V^T fragments of one 32-key tile, read before the next tile's copy is issued: the
-// transpose reads carry no alias information, so reading them after the copy is issued
-// would make the compiler wait for that copy.
-template <int DT, int D>
-struct VFrags {
-  typename Tr<DT>::frag f[Cfg<DT, D>::PK][Cfg<DT, D>::NDV];
-  __device__ inline void read(const typename Tr<DT>::T* vt, int lane) {
-#pragma unroll
-    for (int ks = 0; ks < Cfg<DT, D>::PK; ++ks)
-#pragma unroll
-      for (int j = 0; j < Cfg<DT, D>::NDV; ++j) f[ks][j] = vt_frag<DT, D>(vt, ks, j, lane);
-  }
-};
-
-template <int DT>
-__device__ inline typename Tr<DT>::frag p_frag(const ssa_f16v& p, int ks) {
-  typename Tr<DT>::frag f;
-  if constexpr (Tr<DT>::KPL == 1) {
-    f = p[ks];
-  } else {
-#pragma unroll
-    for (int t = 0; t < 8; ++t) f[t] = Tr<DT>::cvt(p[ks * 8 + t]);
-  }
-  return f;
-}
-
-template <int DT>
-__device__ inline typename Tr<DT>::frag zero_frag() {
-  typename Tr<DT>::frag f;
-  if constexpr (Tr<DT>::KPL == 1) {
-    f = 0.f;
-  } else {
-#pragma unroll
-    for (int t = 0; t < 8; ++t) f[t] = (typename Tr<DT>::T)0.f;
-  }
-  return f;
-}
-
-__device__ inline ssa_f16v zero16() {
-  ssa_f16v z;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) z[r] = 0.f;
-  return z;
-}
-
-// Online softmax of one query row (duplicated in lanes c and c+32, which hold different
-// keys of the row), in log2 units.  The running max m may lag the true max by up to
-// RESCALE_SLACK, so the accumulator is rescaled only when a tile raises the max by more
-// than that (probabilities stay below 2^RESCALE_SLACK); the normalisation by l and
-// lse = m + log2(l) are exact either way.
-template <int NDV>
-struct Online {
-  float m, l;
-  ssa_f16v o[NDV];
-  __device__ inline void init() {
-    m = -INFINITY;
-    l = 0.f;
-#pragma unroll
-    for (int j = 0; j < NDV; ++j) o[j] = zero16();
-  }
-  // s: raw scores (-inf for masked keys); sl2 = scale * log2(e) > 0.  Returns p in s.
-  __device__ inline void update(ssa_f16v& s, float sl2) {
-    float mt = fmaxf(s[0], s[1]);
-#pragma unroll
-    for (int r = 2; r < 16; r += 2) mt = fmaxf(mt, fmaxf(s[r], s[r + 1]));
-    mt = xor32_max(mt) * sl2;
-    if (__builtin_amdgcn_ballot_w64(mt > m + RESCALE_SLACK)) {
-      const float mn = fmaxf(m, mt);
-      const float alpha = fast_exp2(m - mn);
-      l *= alpha;
-#pragma unroll
-      for (int j = 0; j < NDV; ++j) o[j] *= alpha;
-      m = mn;
-    }
-    float sum = 0.f;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      s[r] = fast_exp2(__builtin_fmaf(s[r], sl2, -m));
-      sum += s[r];
-    }
-    l += sum;
-  }
-};
-
-// S^T tile (keys x queries) from a K tile in LDS ([32][KROW]).
-template <int DT, int D>
-__device__ inline ssa_f16v st_tile(const typename Tr<DT>::T* kt, const typename Tr<DT>::frag* qf,
-                                   ssa_f16v acc, int lane) {
-  using C = Cfg<DT, D>;
-  const typename Tr<DT>::T* row = kt + (lane & 31) * C::KROW + (lane >> 5) * C::KPL;
-#pragma unroll
-  for (int ks = 0; ks < C::NKS; ++ks) acc = Tr<DT>::mma(load_frag<DT>(row + ks * C::KS), qf[ks], acc);
-  return acc;
-}
-
-// S tile (queries x keys) from a K tile in LDS.
-template <int DT, int D>
-__device__ inline ssa_f16v s_tile(const typename Tr<DT>::T* kt, const typename Tr<DT>::frag* qf,
-                                  ssa_f16v acc, int lane) {
-  using C = Cfg<DT, D>;
-  const typename Tr<DT>::T* row = kt + (lane & 31) * C::KROW + (lane >> 5) * C::KPL;
-#pragma unroll
-  for (int ks = 0; ks < C::NKS; ++ks) acc = Tr<DT>::mma(qf[ks], load_frag<DT>(row + ks * C::KS), acc);
-  return acc;
-}
-
-template <int DT, int D>
-__device__ inline void pv_tile(Online<D / 32>& st, const ssa_f16v& p, const VFrags<DT, D>& vf) {
-  using C = Cfg<DT, D>;
-#pragma unroll
-  for (int ks = 0; ks < C::PK; ++ks) {
-    const typename Tr<DT>::frag pf = p_frag<DT>(p, ks);
-#pragma unroll
-    for (int j = 0; j < C::NDV; ++j) st.o[j] = Tr<DT>::mma(vf.f[ks][j], pf, st.o[j]);
-  }
-}
-
-template <int DT, int D>
-__device__ inline void load_q(typename Tr<DT>::frag* qf, const typename Tr<DT>::T* qrow, bool valid,
-                              int lane) {
-  using C = Cfg<DT, D>;
-#pragma unroll
-  for (int s = 0; s < C::NKS; ++s)
-    qf[s] = valid ? load_frag<DT>(qrow + s * C::KS + (lane >> 5) * C::KPL) : zero_frag<DT>();
-}
-
-// ------------------------------------------------------------------ direct global->LDS copies
-// global_load_lds_dwordx4: lane l of a wave writes its 16 bytes at the (wave-uniform) LDS
-// base + 16*l.  A tile is a sequence of 16-byte positions; instruction i covers positions
-// 64i .. 64i+63, and the workgroup's waves take instructions round-robin.
-typedef __attribute__((address_space(3))) void lds_void_t;
-__device__ inline void dma16(const void* g, void* lds_instr_base) {
-  __builtin_amdgcn_global_load_lds(g, (lds_void_t*)lds_instr_base, 16, 0, 0);
-}
-__device__ inline void dma_wait() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-
-template <int NW>
-__device__ inline void dma_contiguous(void* lds, const void* g, int nchunks, int wave, int lane) {
-  for (int i = wave; i * 64 < nchunks; i += NW) {
-    const int p = i * 64 + lane;
-    if (p < nchunks) dma16((const char*)g + (int64_t)p * 16, (char*)lds + i * 1024);
-  }
-}
-
 // ------------------------------------------------------------------ compressed + select
 // One workgroup per (query block, head), longest blocks first.  Each wave owns RT row
 // tiles of 32 queries, so every K or V fragment read from LDS feeds RT MFMAs.
@@ -330,7 +132,8 @@ __global__ __launch_bounds__(64 * SEL_WAVES) void k_select(
     const typename Tr<DT>::T* __restrict__ q, const typename Tr<DT>::T* __restrict__ pooled,
     const int32_t* __restrict__ perm, const int32_t* __restrict__ blk_off,
     const int32_t* __restrict__ lpt, int M, int Mp, int H, int64_t N, float sl2, int topk,
-    typename Tr<DT>::T* __restrict__ oc, int32_t* __restrict__ sel) {
+    typename Tr<DT>::T* __restrict__ oc, int32_t* __restrict__ sel, float* __restrict__ lse_save,
+    float* __restrict__ oc_save) {
   using C = Cfg<DT, D>;
   using T = typename Tr<DT>::T;
   using F = typename Tr<DT>::frag;
@@ -421,11 +224,16 @@ __global__ __launch_bounds__(64 * SEL_WAVES) void k_select(
       const int my_row = wbase + 32 * u + c;
       if (wave_active && valid[u]) {
         const float inv = 1.f / ltot;
-        T* orow = oc + ((int64_t)h * N + r0 + my_row) * D;
+        T* orow = oc + ((int64_t)(r0 + my_row) * H + h) * D;
+        if (lse_save && g == 0) lse_save[(int64_t)h * N + r0 + my_row] = st[u].m + fast_log2(ltot);
+        float* srow = oc_save ? oc_save + ((int64_t)(r0 + my_row) * H + h) * D : nullptr;
 #pragma unroll
         for (int j = 0; j < C::NDV; ++j)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) orow[32 * j + res_row(r, g)] = Tr<DT>::cvt(st[u].o[j][r] * inv);
+          for (int r = 0; r < 16; ++r) {
+            orow[32 * j + res_row(r, g)] = Tr<DT>::cvt(st[u].o[j][r] * inv);
+            if (srow) srow[32 * j + res_row(r, g)] = st[u].o[j][r] * inv;
+          }
       }
       // rows past the block get +inf, so their probabilities in pass 2 are exactly zero
       if (g == 0) lse_lds[wave * 32 * RT + 32 * u + c] = valid[u] ? st[u].m + fast_log2(ltot) : INFINITY;
@@ -523,58 +331,8 @@ __global__ __launch_bounds__(64 * SEL_WAVES) void k_select(
 // caller's K and V through the token permutation.  Keys past the end of the set reuse the
 // set's first key (finite values; their scores are masked).
 template <int DT, int D>
-struct Gather {
-  using C = Cfg<DT, D>;
-  static constexpr int KRC = C::KCH / KT, VRC = C::VCH / KT;  // chunks per padded row
-  static constexpr int NPOS = C::KCH + C::VCH;
-  static constexpr int NINSTR = (NPOS + 63) / 64;
-  static constexpr int NI = (NINSTR + ATT_WAVES - 1) / ATT_WAVES;  // copies per lane per tile
-  int32_t row[NI];    // tile row of each copy (-1: none)
-  int32_t goff[NI];   // element offset inside the token's head row, with bit 30 set for V
-  int32_t tok[NI];
-  __device__ inline void init(int wave, int lane) {
-#pragma unroll
-    for (int m = 0; m < NI; ++m) {
-      const int i = wave + m * ATT_WAVES, p = i * 64 + lane;
-      const bool isk = p < C::KCH;
-      const int q = isk ? p : p - C::KCH;
-      const int rr = isk ? q / KRC : q / VRC, ch = isk ? q % KRC : q % VRC;
-      const bool ok = i < NINSTR && p < NPOS && ch < C::CPR;
-      row[m] = ok ? rr : -1;
-      goff[m] = ch * C::EPC + (isk ? 0 : (1 << 30));
-    }
-  }
-  // tokens of this lane's copies for the tile starting at key k0
-  __device__ inline void lookup(int k0, int total, int L, const int32_t* pre, const int32_t* lst_off,
-                                const int32_t* __restrict__ perm) {
-#pragma unroll
-    for (int m = 0; m < NI; ++m) {
-      int j = k0 + (row[m] < 0 ? 0 : row[m]);
-      if (j >= total) j = 0;
-      int lo = 0, hi = L - 1;  // last list entry starting at or before key j (none to search
-      while (lo < hi) {        // when the list is one block)
-        const int mid = (lo + hi + 1) >> 1;
-        if (pre[mid] <= j) lo = mid; else hi = mid - 1;
-      }
-      tok[m] = perm[lst_off[lo] + (j - pre[lo])];
-    }
-  }
-  __device__ inline void issue(typename Tr<DT>::T* stage, const typename Tr<DT>::T* kin,
-                               const typename Tr<DT>::T* vin, int H, int h, int wave) const {
-#pragma unroll
-    for (int m = 0; m < NI; ++m) {
-      if (row[m] >= 0) {
-        const bool isv = goff[m] & (1 << 30);
-        const typename Tr<DT>::T* src = (isv ? vin : kin) + ((int64_t)tok[m] * H + h) * D + (goff[m] & ((1 << 30) - 1));
-        dma16(src, stage + (wave + m * ATT_WAVES) * 64 * C::EPC);
-      }
-    }
-  }
-};
-
-template <int DT, int D>
 __device__ inline void gathered_branch(
-    Online<D / 32>* st, const Gather<DT, D>& ga0, const int32_t* blist, int nlist,
+    Online<D / 32>* st, const Gather<DT, D, ATT_WAVES>& ga0, const int32_t* blist, int nlist,
     const typename Tr<DT>::frag (*qf)[Cfg<DT, D>::NKS], const typename Tr<DT>::T* __restrict__ kin,
     const typename Tr<DT>::T* __restrict__ vin, const int32_t* __restrict__ perm,
     const int32_t* __restrict__ blk_off, int H, int h, float sl2, bool wave_active,
@@ -586,7 +344,7 @@ __device__ inline void gathered_branch(
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, wave = tid >> 6;
 #pragma unroll
   for (int u = 0; u < ATT_RT; ++u) st[u].init();
-  Gather<DT, D> ga = ga0;
+  Gather<DT, D, ATT_WAVES> ga = ga0;
   for (int l0 = 0; l0 < nlist; l0 += NTH) {
     const int L = min(NTH, nlist - l0);
     __syncthreads();
@@ -666,7 +424,8 @@ __global__ __launch_bounds__(64 * ATT_WAVES) __attribute__((amdgpu_waves_per_eu(
     const int32_t* __restrict__ blk_cell, const int32_t* __restrict__ cell_off,
     const int32_t* __restrict__ cell_blk, const int32_t* __restrict__ lpt,
     const int32_t* __restrict__ sel, const typename Tr<DT>::T* __restrict__ oc, int M, int H,
-    int nchunk, int64_t N, int topk, float sl2, typename Tr<DT>::T* __restrict__ out) {
+    int nchunk, int64_t N, int topk, float sl2, typename Tr<DT>::T* __restrict__ out,
+    float* __restrict__ lse_save, float* __restrict__ os_save, float* __restrict__ ow_save) {
   using C = Cfg<DT, D>;
   using T = typename Tr<DT>::T;
   using F = typename Tr<DT>::frag;
@@ -708,7 +467,7 @@ __global__ __launch_bounds__(64 * ATT_WAVES) __attribute__((amdgpu_waves_per_eu(
     tok_q[u] = valid[u] ? perm[r0 + my_row] : 0;
     load_q<DT, D>(qf[u], q + (tok_q[u] * H + h) * D, valid[u], lane);
   }
-  Gather<DT, D> ga;
+  Gather<DT, D, ATT_WAVES> ga;
   ga.init(wave, lane);
 
   Online<C::NDV> st[ATT_RT];
@@ -717,7 +476,17 @@ __global__ __launch_bounds__(64 * ATT_WAVES) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
   for (int u = 0; u < ATT_RT; ++u) {
     const float g1 = valid[u] ? Tr<DT>::up(gates[(tok_q[u] * H + h) * 3 + 1]) : 0.f;
-    const float f = g1 / xor32_sum(st[u].l);
+    const float ls = xor32_sum(st[u].l);
+    const float f = g1 / ls;
+    if (lse_save && wave_active && valid[u]) {
+      const int64_t row = r0 + wbase + 32 * u + c;
+      if (g == 0) lse_save[(int64_t)(H + h) * N + row] = st[u].m + fast_log2(ls);
+      float* srow = os_save + (row * H + h) * D;
+#pragma unroll
+      for (int j = 0; j < C::NDV; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) srow[32 * j + res_row(r, g)] = st[u].o[j][r] / ls;
+    }
 #pragma unroll
     for (int j = 0; j < C::NDV; ++j) {
       if constexpr (PARK) {
@@ -738,8 +507,16 @@ __global__ __launch_bounds__(64 * ATT_WAVES) __attribute__((amdgpu_waves_per_eu(
       const float g0 = Tr<DT>::up(gates[(tok_q[u] * H + h) * 3 + 0]);
       const float g2 = Tr<DT>::up(gates[(tok_q[u] * H + h) * 3 + 2]);
       const float f = g2 / ltot;
-      const T* orow = oc + ((int64_t)h * N + r0 + my_row) * D;
+      const T* orow = oc + ((int64_t)(r0 + my_row) * H + h) * D;
       T* dst = out + (tok_q[u] * H + h) * D;
+      if (lse_save) {
+        if (g == 0) lse_save[(int64_t)(2 * H + h) * N + r0 + my_row] = st[u].m + fast_log2(ltot);
+        float* wrow = ow_save + ((int64_t)(r0 + my_row) * H + h) * D;
+#pragma unroll
+        for (int j = 0; j < C::NDV; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) wrow[32 * j + res_row(r, g)] = st[u].o[j][r] / ltot;
+      }
 #pragma unroll
       for (int j = 0; j < C::NDV; ++j)
 #pragma unroll
@@ -773,7 +550,7 @@ hipError_t run_select(const ssa_plan_s* p, int H, int topk, float sl2, const voi
   const size_t shm = (size_t)Mp * sizeof(float);
   hipLaunchKernelGGL((k_select<DT, D>), dim3((unsigned)(p->M * H)), dim3(64 * SEL_WAVES), shm, s,
                      (const T*)q, (const T*)w.pooled, p->perm, p->blk_off, p->lpt, (int)p->M, Mp, H,
-                     p->n, sl2, topk, (T*)w.oc, sel);
+                     p->n, sl2, topk, (T*)w.oc, sel, w.lse, w.obr);
   return hipGetLastError();
 }
 
@@ -786,7 +563,8 @@ hipError_t run_attend(const ssa_plan_s* p, int H, int topk, float sl2, const voi
   hipLaunchKernelGGL((k_attend<DT, D>), dim3((unsigned)(p->M * H * nchunk)), dim3(64 * ATT_WAVES), 0,
                      s, (const T*)q, (const T*)k, (const T*)v, (const T*)gates, p->perm, p->blk_off,
                      p->blk_cell, p->cell_off, p->cell_blk, p->lpt, sel, (const T*)w.oc, (int)p->M,
-                     H, nchunk, p->n, topk, sl2, (T*)out);
+                     H, nchunk, p->n, topk, sl2, (T*)out, w.lse,
+                     w.obr ? w.obr + p->n * H * D : nullptr, w.obr ? w.obr + 2 * p->n * H * D : nullptr);
   return hipGetLastError();
 }
 

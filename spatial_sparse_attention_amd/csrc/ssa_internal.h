@@ -56,13 +56,17 @@ static inline int64_t stage_elems(ssa_dtype dt, int d) {
   return (int64_t)32 * (nsplit_of(dt) * krow_of(dt, d) + vrow_of(dt, d));
 }
 
-// Forward workspace layout.
+// Forward workspace layout.  Rows r are block-sorted token positions.
 struct FwdWs {
   void* pooled;      // [H][Mp/32][stage] dtype: pooled key planes + pooled values, padding zero
-  void* oc;          // [H][N][d] compressed-branch output, block-sorted rows (dtype)
+  void* oc;          // [N][H][d] compressed-branch output (dtype)
   int32_t* sel;      // [H][M][topk]
+  // saved for the backward (save_for_bwd only; else null)
+  float* lse;        // [3][H][N] per-branch log2-sum-exp2 of the scaled scores
+  float* obr;        // [3][N][H][d] the three branch outputs in fp32 (compressed, selected, window)
 };
-size_t fwd_carve(Carver& c, const ssa_plan_s* p, ssa_dtype dt, int H, int d, int topk, FwdWs* w);
+size_t fwd_carve(Carver& c, const ssa_plan_s* p, ssa_dtype dt, int H, int d, int topk, int save,
+                 FwdWs* w);
 
 
 #define SSA_HIP_CHECK(expr)                          \
@@ -70,12 +74,29 @@ size_t fwd_carve(Carver& c, const ssa_plan_s* p, ssa_dtype dt, int H, int d, int
     if ((expr) != hipSuccess) return SSA_ERR_HIP;    \
   } while (0)
 
+// Device sorting helpers of the plan (stable LSD radix sort on 8-bit digits).
+namespace ssa_sort {
+int bits_for(uint64_t maxval);
+void device_scan(int32_t* a, int len, int32_t* total, int32_t* part, hipStream_t s);
+hipError_t radix_sort(uint32_t*& ka, int32_t*& va, uint32_t*& kb, int32_t*& vb, int n, int nbits,
+                      int32_t* rank, int32_t* hist, int32_t* part, hipStream_t s);
+}  // namespace ssa_sort
+// Scratch sizes of radix_sort over n elements.
+static inline int64_t radix_hist_len(int64_t n) { return (n + 255) / 256 * 256; }
+static inline int64_t scan_part_len(int64_t len) { return len / 4096 + 2; }
+
 // Kernel-launch entry points implemented in the .hip files.
 hipError_t launch_pool(ssa_dtype dt, const ssa_plan_s* p, int H, int d, const void* k,
                        const void* v, const void* wk, const void* wv, const FwdWs& w,
                        hipStream_t s);
 hipError_t launch_select(ssa_dtype dt, const ssa_plan_s* p, int H, int d, int topk, float scale,
                          const void* q, const FwdWs& w, int32_t* sel, hipStream_t s);
+hipError_t launch_backward(ssa_dtype dt, const ssa_plan_s* p, int H, int d, int topk, float scale,
+                           const void* q, const void* k, const void* v, const void* wk,
+                           const void* wv, const void* gates, const int32_t* sel, const void* dout,
+                           float* dq, float* dk, float* dv, float* dgates, const FwdWs& fw,
+                           void* ws, hipStream_t s);
+size_t bwd_carve(Carver& c, const ssa_plan_s* p, int H, int d, int topk, void* w);
 hipError_t launch_attend(ssa_dtype dt, const ssa_plan_s* p, int H, int d, int topk, float scale,
                          const void* q, const void* k, const void* v, const void* gates,
                          const FwdWs& w, const int32_t* sel, void* out, hipStream_t s);

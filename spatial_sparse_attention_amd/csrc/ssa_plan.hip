@@ -246,7 +246,11 @@ __global__ void k_identity_cells(int M, int32_t* blk_cell, int32_t* cell_off, in
   }
 }
 
-inline int bits_for(uint64_t maxval) {
+}  // namespace
+
+namespace ssa_sort {
+
+int bits_for(uint64_t maxval) {
   int b = 0;
   while (b < 32 && (maxval >> b) != 0) ++b;
   return b;
@@ -290,6 +294,11 @@ hipError_t segments(const uint32_t* keys, const int32_t* vals, int n, int32_t* t
                      seg_key, elem_seg);
   return hipGetLastError();
 }
+
+}  // namespace ssa_sort
+
+namespace {
+using namespace ssa_sort;
 
 bool window_supported(const int32_t grid[3], int B, int w, bool* single) {
   *single = w >= grid[0] && w >= grid[1] && w >= grid[2];

@@ -1,0 +1,274 @@
+// Tile geometry and MFMA building blocks shared by the forward and backward kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include "ssa_mfma.h"
+
+namespace ssa_dev {
+
+constexpr int KT = 32;                // keys (or queries) per tile
+constexpr float RESCALE_SLACK = 8.f;  // log2 units the running max may lag the true max
+
+template <int DT, int D>
+struct Cfg {
+  using T = typename Tr<DT>::T;
+  using F = typename Tr<DT>::frag;
+  static constexpr int NS = Tr<DT>::NSPLIT;
+  static constexpr int KS = Tr<DT>::KS, KPL = Tr<DT>::KPL;
+  static constexpr int NKS = D / KS;                    // K steps over the head dim
+  static constexpr int NDV = D / 32;                    // 32-wide output column tiles
+  static constexpr int EPC = 16 / sizeof(T);            // elements per 16-byte chunk
+  static constexpr int CPR = D / EPC;                   // data chunks per row
+  static constexpr int KROW = D + 16 / sizeof(T);       // K tile row (b128 fragment reads)
+  static constexpr int VROW = D + 32 / sizeof(T);       // V tile row (transpose reads)
+  static constexpr int KTILE = KT * KROW, VTILE = KT * VROW;
+  static constexpr int KCH = KTILE * sizeof(T) / 16;    // 16-byte chunks of a K tile
+  static constexpr int VCH = VTILE * sizeof(T) / 16;
+  static constexpr int STAGE = NS * KTILE + VTILE;      // pooled stage (elements)
+  static constexpr int PK = KT / KS;                    // K steps over a 32-key tile (PV)
+};
+
+// ------------------------------------------------------------------ MFMA building blocks
+// Reduction with the other half of the wave (lanes l and l^32 hold the same query row):
+// v_permlane32_swap returns the pair {x[l], x[l^32]} in its two results.
+__device__ inline float xor32_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ inline float xor32_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// A operand (V^T) of O^T += V^T P^T, K step ks of a 32-key tile stored row-major in LDS
+// (vt[key][dv], row stride VROW), output columns 32*j .. 32*j+31.  Lane l covers
+// dv = 32j + l%32 and the keys held by P^T registers ks*KPL .. ks*KPL + KPL - 1, i.e.
+// keys 16ks + 4g + {0..3} and 16ks + 8 + 4g + {0..3} (g = l/32) for 16-bit types.
+// MFMA operand fragment from a row-major 32-row tile in LDS (tile[row][col], row stride ROW
+// elements), K step ks over the rows, output columns 32*j .. 32*j+31: lane l supplies
+// column 32j + l%32 at the rows held by result registers ks*KPL .. ks*KPL + KPL - 1 of a
+// score tile, i.e. rows 16ks + 4g + {0..3} and 16ks + 8 + 4g + {0..3} (g = l/32) for
+// 16-bit types.  It is the A operand V^T of O^T += V^T P^T and equally the B operand X of
+// Y += P^T X when the rows are the contraction index.
+template <int DT, int ROW>
+__device__ inline typename Tr<DT>::frag tr_frag(const typename Tr<DT>::T* tile, int ks, int j, int lane) {
+  if constexpr (Tr<DT>::KPL == 1) {
+    return tile[res_row(ks, lane >> 5) * ROW + 32 * j + (lane & 31)];
+  } else {
+    const int i = lane & 15, G = lane >> 4;
+    const typename Tr<DT>::T* p =
+        tile + (16 * ks + 4 * (G >> 1) + (i >> 2)) * ROW + 32 * j + 16 * (G & 1) + 4 * (i & 3);
+    typedef unsigned u2 __attribute__((ext_vector_type(2)));
+    typedef unsigned u4 __attribute__((ext_vector_type(4)));
+    const u2 a = __builtin_bit_cast(u2, lds_read_tr16(p));
+    const u2 b = __builtin_bit_cast(u2, lds_read_tr16(p + 8 * ROW));
+    const u4 u = {a.x, a.y, b.x, b.y};
+    return __builtin_bit_cast(typename Tr<DT>::frag, u);
+  }
+}
+
+template <int DT, int D>
+__device__ inline typename Tr<DT>::frag vt_frag(const typename Tr<DT>::T* vt, int ks, int j, int lane) {
+  return tr_frag<DT, Cfg<DT, D>::VROW>(vt, ks, j, lane);
+}
+
+// The V^T fragments of one 32-key tile, read before the next tile's copy is issued: the
+// transpose reads carry no alias information, so reading them after the copy is issued
+// would make the compiler wait for that copy.
+template <int DT, int D>
+struct VFrags {
+  typename Tr<DT>::frag f[Cfg<DT, D>::PK][Cfg<DT, D>::NDV];
+  __device__ inline void read(const typename Tr<DT>::T* vt, int lane) {
+#pragma unroll
+    for (int ks = 0; ks < Cfg<DT, D>::PK; ++ks)
+#pragma unroll
+      for (int j = 0; j < Cfg<DT, D>::NDV; ++j) f[ks][j] = vt_frag<DT, D>(vt, ks, j, lane);
+  }
+};
+
+template <int DT>
+__device__ inline typename Tr<DT>::frag p_frag(const ssa_f16v& p, int ks) {
+  typename Tr<DT>::frag f;
+  if constexpr (Tr<DT>::KPL == 1) {
+    f = p[ks];
+  } else {
+#pragma unroll
+    for (int t = 0; t < 8; ++t) f[t] = Tr<DT>::cvt(p[ks * 8 + t]);
+  }
+  return f;
+}
+
+template <int DT>
+__device__ inline typename Tr<DT>::frag zero_frag() {
+  typename Tr<DT>::frag f;
+  if constexpr (Tr<DT>::KPL == 1) {
+    f = 0.f;
+  } else {
+#pragma unroll
+    for (int t = 0; t < 8; ++t) f[t] = (typename Tr<DT>::T)0.f;
+  }
+  return f;
+}
+
+__device__ inline ssa_f16v zero16() {
+  ssa_f16v z;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) z[r] = 0.f;
+  return z;
+}
+
+// Online softmax of one query row (duplicated in lanes c and c+32, which hold different
+// keys of the row), in log2 units.  The running max m may lag the true max by up to
+// RESCALE_SLACK, so the accumulator is rescaled only when a tile raises the max by more
+// than that (probabilities stay below 2^RESCALE_SLACK); the normalisation by l and
+// lse = m + log2(l) are exact either way.
+template <int NDV>
+struct Online {
+  float m, l;
+  ssa_f16v o[NDV];
+  __device__ inline void init() {
+    m = -INFINITY;
+    l = 0.f;
+#pragma unroll
+    for (int j = 0; j < NDV; ++j) o[j] = zero16();
+  }
+  // s: raw scores (-inf for masked keys); sl2 = scale * log2(e) > 0.  Returns p in s.
+  __device__ inline void update(ssa_f16v& s, float sl2) {
+    float mt = fmaxf(s[0], s[1]);
+#pragma unroll
+    for (int r = 2; r < 16; r += 2) mt = fmaxf(mt, fmaxf(s[r], s[r + 1]));
+    mt = xor32_max(mt) * sl2;
+    if (__builtin_amdgcn_ballot_w64(mt > m + RESCALE_SLACK)) {
+      const float mn = fmaxf(m, mt);
+      const float alpha = fast_exp2(m - mn);
+      l *= alpha;
+#pragma unroll
+      for (int j = 0; j < NDV; ++j) o[j] *= alpha;
+      m = mn;
+    }
+    float sum = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      s[r] = fast_exp2(__builtin_fmaf(s[r], sl2, -m));
+      sum += s[r];
+    }
+    l += sum;
+  }
+};
+
+// S^T tile (keys x queries) from a K tile in LDS ([32][KROW]).
+template <int DT, int D>
+__device__ inline ssa_f16v st_tile(const typename Tr<DT>::T* kt, const typename Tr<DT>::frag* qf,
+                                   ssa_f16v acc, int lane) {
+  using C = Cfg<DT, D>;
+  const typename Tr<DT>::T* row = kt + (lane & 31) * C::KROW + (lane >> 5) * C::KPL;
+#pragma unroll
+  for (int ks = 0; ks < C::NKS; ++ks) acc = Tr<DT>::mma(load_frag<DT>(row + ks * C::KS), qf[ks], acc);
+  return acc;
+}
+
+// S tile (queries x keys) from a K tile in LDS.
+template <int DT, int D>
+__device__ inline ssa_f16v s_tile(const typename Tr<DT>::T* kt, const typename Tr<DT>::frag* qf,
+                                  ssa_f16v acc, int lane) {
+  using C = Cfg<DT, D>;
+  const typename Tr<DT>::T* row = kt + (lane & 31) * C::KROW + (lane >> 5) * C::KPL;
+#pragma unroll
+  for (int ks = 0; ks < C::NKS; ++ks) acc = Tr<DT>::mma(qf[ks], load_frag<DT>(row + ks * C::KS), acc);
+  return acc;
+}
+
+template <int DT, int D>
+__device__ inline void pv_tile(Online<D / 32>& st, const ssa_f16v& p, const VFrags<DT, D>& vf) {
+  using C = Cfg<DT, D>;
+#pragma unroll
+  for (int ks = 0; ks < C::PK; ++ks) {
+    const typename Tr<DT>::frag pf = p_frag<DT>(p, ks);
+#pragma unroll
+    for (int j = 0; j < C::NDV; ++j) st.o[j] = Tr<DT>::mma(vf.f[ks][j], pf, st.o[j]);
+  }
+}
+
+template <int DT, int D>
+__device__ inline void load_q(typename Tr<DT>::frag* qf, const typename Tr<DT>::T* qrow, bool valid,
+                              int lane) {
+  using C = Cfg<DT, D>;
+#pragma unroll
+  for (int s = 0; s < C::NKS; ++s)
+    qf[s] = valid ? load_frag<DT>(qrow + s * C::KS + (lane >> 5) * C::KPL) : zero_frag<DT>();
+}
+
+// ------------------------------------------------------------------ direct global->LDS copies
+// global_load_lds_dwordx4: lane l of a wave writes its 16 bytes at the (wave-uniform) LDS
+// base + 16*l.  A tile is a sequence of 16-byte positions; instruction i covers positions
+// 64i .. 64i+63, and the workgroup's waves take instructions round-robin.
+typedef __attribute__((address_space(3))) void lds_void_t;
+__device__ inline void dma16(const void* g, void* lds_instr_base) {
+  __builtin_amdgcn_global_load_lds(g, (lds_void_t*)lds_instr_base, 16, 0, 0);
+}
+__device__ inline void dma_wait() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+template <int NW>
+__device__ inline void dma_contiguous(void* lds, const void* g, int nchunks, int wave, int lane) {
+  for (int i = wave; i * 64 < nchunks; i += NW) {
+    const int p = i * 64 + lane;
+    if (p < nchunks) dma16((const char*)g + (int64_t)p * 16, (char*)lds + i * 1024);
+  }
+}
+
+// ------------------------------------------------------------------ gathered token tiles
+// A key (or query) set is a list of blocks, concatenated in sorted token order and cut into
+// 32-row tiles.  A stage holds the tile's first-operand rows ([32][KROW]) followed by its
+// second-operand rows ([32][VROW]), copied straight from two caller tensors [N,H,d] through
+// the token permutation.  Rows past the end of the set reuse the set's first row (finite
+// values; callers mask them).
+template <int DT, int D, int NW>
+struct Gather {
+  using C = Cfg<DT, D>;
+  static constexpr int KRC = C::KCH / KT, VRC = C::VCH / KT;  // chunks per padded row
+  static constexpr int NPOS = C::KCH + C::VCH;
+  static constexpr int NINSTR = (NPOS + 63) / 64;
+  static constexpr int NI = (NINSTR + NW - 1) / NW;  // copies per lane per tile
+  int32_t row[NI];    // tile row of each copy (-1: none)
+  int32_t goff[NI];   // element offset inside the token's head row, with bit 30 set for V
+  int32_t tok[NI];
+  __device__ inline void init(int wave, int lane) {
+#pragma unroll
+    for (int m = 0; m < NI; ++m) {
+      const int i = wave + m * NW, p = i * 64 + lane;
+      const bool isk = p < C::KCH;
+      const int q = isk ? p : p - C::KCH;
+      const int rr = isk ? q / KRC : q / VRC, ch = isk ? q % KRC : q % VRC;
+      const bool ok = i < NINSTR && p < NPOS && ch < C::CPR;
+      row[m] = ok ? rr : -1;
+      goff[m] = ch * C::EPC + (isk ? 0 : (1 << 30));
+    }
+  }
+  // tokens of this lane's copies for the tile starting at key k0
+  __device__ inline void lookup(int k0, int total, int L, const int32_t* pre, const int32_t* lst_off,
+                                const int32_t* __restrict__ perm) {
+#pragma unroll
+    for (int m = 0; m < NI; ++m) {
+      int j = k0 + (row[m] < 0 ? 0 : row[m]);
+      if (j >= total) j = 0;
+      int lo = 0, hi = L - 1;  // last list entry starting at or before key j (none to search
+      while (lo < hi) {        // when the list is one block)
+        const int mid = (lo + hi + 1) >> 1;
+        if (pre[mid] <= j) lo = mid; else hi = mid - 1;
+      }
+      tok[m] = perm[lst_off[lo] + (j - pre[lo])];
+    }
+  }
+  __device__ inline void issue(typename Tr<DT>::T* stage, const typename Tr<DT>::T* kin,
+                               const typename Tr<DT>::T* vin, int H, int h, int wave) const {
+#pragma unroll
+    for (int m = 0; m < NI; ++m) {
+      if (row[m] >= 0) {
+        const bool isv = goff[m] & (1 << 30);
+        const typename Tr<DT>::T* src = (isv ? vin : kin) + ((int64_t)tok[m] * H + h) * D + (goff[m] & ((1 << 30) - 1));
+        dma16(src, stage + (wave + m * NW) * 64 * C::EPC);
+      }
+    }
+  }
+};
+
+}  // namespace ssa_dev

@@ -95,3 +95,37 @@ def check_items(inp, out_gpu, sel_gpu, items, dt=None):
     ref = np.concatenate([res[it]["out"] for it in items])
     compare(got, ref, dt, f"{len(items)} items")
     return counts
+
+
+def gpu_backward(inp, dout, dt=None, plan=None):
+    """GPU forward (saving state) + backward.  Returns numpy float64 (out, sel, dq, dk, dv, dg)."""
+    import torch
+    import spatial_sparse_attention_amd as ssa
+    dev = to_dev(inp, dt)
+    do = torch.from_numpy(np.ascontiguousarray(dout)).to("cuda").to(dev["q"].dtype)
+    if plan is None:
+        plan = ssa.Plan(dev["coords"], inp["grid"], inp["block"], inp["window"])
+    N, H, d = dev["q"].shape
+    fws = torch.empty(ssa.forward_workspace_size(plan, dev["q"].dtype, H, d, inp["topk"], True),
+                      dtype=torch.uint8, device="cuda")
+    out, sel = ssa.forward(plan, dev["q"], dev["k"], dev["v"], dev["wk"], dev["wv"], dev["gates"],
+                           inp["topk"], 0.0, ws=fws, save_for_bwd=True)
+    dq, dk, dv, dg = ssa.backward(plan, dev["q"], dev["k"], dev["v"], dev["wk"], dev["wv"],
+                                  dev["gates"], inp["topk"], sel, do, fws)
+    torch.cuda.synchronize()
+    f = lambda t: t.double().cpu().numpy()
+    return f(out), sel.cpu().numpy().astype(np.int64), f(dq), f(dk), f(dv), f(dg)
+
+
+GRAD_TOL = {"f32": {"abs": 1e-3, "rel_l2": 1e-5}, "f16": {"abs": 2e-2, "rel_l2": 5e-3},
+            "bf16": {"abs": 2e-2, "rel_l2": 5e-3}}
+
+
+def compare_grad(got, ref, dt, what=""):
+    tol = GRAD_TOL[dt]
+    assert np.isfinite(got).all(), f"{what}: non-finite"
+    err = np.abs(got - ref).max()
+    rel = np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-30)
+    assert err <= tol["abs"], f"{what}: max-abs {err:.3g} > {tol['abs']} (rel-L2 {rel:.3g})"
+    assert rel <= tol["rel_l2"], f"{what}: rel-L2 {rel:.3g} > {tol['rel_l2']}"
+    return float(err), float(rel)

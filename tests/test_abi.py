@@ -78,11 +78,12 @@ def test_empty_plan_and_forward_checks(ssa):
     info = ssa.PlanInfo()
     assert L.ssa_plan_get_info(h, ctypes.byref(info)) == 0
     assert info.n == 0 and info.num_blocks == 0
-    wsz = L.ssa_forward_workspace_size(h, 1, 2, 64, 4)
+    wsz = L.ssa_forward_workspace_size(h, 1, 2, 64, 4, 0)
     assert wsz > 0
+    assert L.ssa_forward_workspace_size(h, 1, 2, 64, 4, 1) > wsz   # saved state for backward
     fws = ctypes.create_string_buffer(wsz)
     args = lambda dt=1, H=2, d=64, k=4, sc=0.0: (h, dt, H, d, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, k,
-                                                 ctypes.c_float(sc), FAKE, None, fws, wsz, None)
+                                                 ctypes.c_float(sc), FAKE, None, fws, wsz, 0, None)
     assert L.ssa_forward(*args()) == 0                 # N = 0: nothing to do
     assert L.ssa_forward(*args(dt=3)) == 1
     assert L.ssa_forward(*args(dt=-1)) == 1
@@ -98,7 +99,20 @@ def test_empty_plan_and_forward_checks(ssa):
     assert L.ssa_plan_get_info(h, None) == 1
     assert L.ssa_plan_get_info(None, ctypes.byref(info)) == 6
     assert L.ssa_forward(None, 1, 2, 64, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4, ctypes.c_float(0),
-                         FAKE, None, fws, wsz, None) == 6
+                         FAKE, None, fws, wsz, 0, None) == 6
+    # backward
+    bsz = L.ssa_backward_workspace_size(h, 1, 2, 64, 4)
+    assert bsz > 0
+    bws = ctypes.create_string_buffer(bsz)
+    bargs = lambda dt=1, d=64, k=4, sc=0.0: (h, dt, 2, d, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, k,
+                                             ctypes.c_float(sc), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                             fws, wsz, bws, bsz, None)
+    assert L.ssa_backward(*bargs()) == 0              # N = 0
+    assert L.ssa_backward(*bargs(dt=5)) == 1
+    assert L.ssa_backward(*bargs(d=80)) == 2
+    assert L.ssa_backward(*bargs(k=0)) == 1
+    assert L.ssa_backward(*bargs(sc=-2.0)) == 1
+    assert L.ssa_backward(*((None,) + bargs()[1:])) == 6
     L.ssa_plan_destroy(h)
     L.ssa_plan_destroy(None)
 
