@@ -112,7 +112,10 @@ void ssa_plan_destroy(ssa_plan plan);
  * log-sum-exp and branch outputs).  Asynchronous on `stream`; returns SSA_ERR_HIP
  * if a launch fails.  Accumulation is fp32 (the compressed scores that decide the
  * selection are computed from a split of the fp32 pooled keys into two (f16) or
- * three (bf16) dtype terms, so they carry fp32-level accuracy).
+ * three (bf16) dtype terms, so they carry fp32-level accuracy).  The selection
+ * keeps each work item's importance vector in on-chip memory, which bounds the
+ * number of occupied blocks M: at most 6144, and at most 5760 (f32) or 4608
+ * (bf16) for d = 128; a larger plan returns SSA_ERR_UNSUPPORTED.
  */
 size_t ssa_forward_workspace_size(ssa_plan plan, ssa_dtype dtype, int32_t heads, int32_t dim,
                                   int32_t topk, int save_for_bwd);

@@ -23,11 +23,12 @@ ssa_status check_common(ssa_plan p, ssa_dtype dt, int32_t H, int32_t d, int32_t 
 
 size_t fwd_carve(Carver& c, const ssa_plan_s* p, ssa_dtype dt, int H, int d, int topk, int save,
                  FwdWs* w) {
-  const int64_t Mp = round_up(p->M > 0 ? p->M : 1, KT);
+  const int64_t Mp = round_up(p->M > 0 ? p->M : 1, POOL_TILE);
   const int64_t n1 = p->n > 0 ? p->n : 1;
   const size_t es = esize_of(dt);
   FwdWs t;
-  t.pooled = c.take<char>((size_t)H * (Mp / KT) * stage_elems(dt, d) * es);
+  t.pooled = c.take<char>((size_t)H * (Mp / POOL_TILE) * stage_elems(dt, d) * es);
+  t.pooled_v = c.take<char>((size_t)H * Mp * vrow_of(dt, d) * es);
   t.oc = c.take<char>((size_t)H * n1 * d * es);
   t.sel = c.take<int32_t>((size_t)H * (p->M > 0 ? p->M : 1) * topk);
   t.lse = nullptr;
@@ -70,8 +71,10 @@ extern "C" ssa_status ssa_forward_stages(ssa_plan p, ssa_dtype dt, int32_t H, in
   int32_t* sel = sel_out ? sel_out : w.sel;
   if (stages & SSA_STAGE_POOL)
     if (launch_pool(dt, p, H, d, k, v, wk, wv, w, stream) != hipSuccess) return SSA_ERR_HIP;
-  if (stages & SSA_STAGE_SELECT)
+  if (stages & SSA_STAGE_SELECT) {
+    if (p->M > select_block_limit(dt, d)) return SSA_ERR_UNSUPPORTED;
     if (launch_select(dt, p, H, d, topk, scale, q, w, sel, stream) != hipSuccess) return SSA_ERR_HIP;
+  }
   if (stages & SSA_STAGE_ATTEND)
     if (launch_attend(dt, p, H, d, topk, scale, q, k, v, gates, w, sel, out, stream) != hipSuccess)
       return SSA_ERR_HIP;

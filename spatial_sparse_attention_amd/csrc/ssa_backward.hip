@@ -43,7 +43,7 @@ int cmp_chunks(int64_t Mp, int H) {
 
 size_t carve(Carver& c, const ssa_plan_s* p, int H, int d, int topk, BwdWs* w) {
   const int64_t M = p->M > 0 ? p->M : 1, n1 = p->n > 0 ? p->n : 1;
-  const int64_t Mp = round_up(M, KT);
+  const int64_t Mp = round_up(M, POOL_TILE);
   const int64_t E = (int64_t)H * M * topk;
   BwdWs t;
   t.qch = cmp_chunks(Mp, H);
@@ -172,7 +172,8 @@ __global__ __launch_bounds__(64 * BW) void k_bwd_dq(
     const typename Tr<DT>::T* __restrict__ q, const typename Tr<DT>::T* __restrict__ kin,
     const typename Tr<DT>::T* __restrict__ vin, const typename Tr<DT>::T* __restrict__ gates,
     const typename Tr<DT>::T* __restrict__ dout, const typename Tr<DT>::T* __restrict__ pooled,
-    const float* __restrict__ lse3, const float* __restrict__ D3, const int32_t* __restrict__ perm,
+    const typename Tr<DT>::T* __restrict__ pooled_v, const float* __restrict__ lse3,
+    const float* __restrict__ D3, const int32_t* __restrict__ perm,
     const int32_t* __restrict__ blk_off, const int32_t* __restrict__ blk_cell,
     const int32_t* __restrict__ cell_off, const int32_t* __restrict__ cell_blk,
     const int32_t* __restrict__ lpt, const int32_t* __restrict__ sel, int M, int Mp, int H,
@@ -214,15 +215,18 @@ __global__ __launch_bounds__(64 * BW) void k_bwd_dq(
     Dx[x] = valid ? D3[((int64_t)x * H + h) * N + row] : 0.f;
   }
 
-  // compressed branch: K = first (hi) pooled key plane, V = pooled values
-  const T* pst = pooled + (int64_t)h * (Mp / KT) * C::STAGE;
-  for (int t = 0; t < Mp / KT; ++t) {
+  // compressed branch, 32 pooled keys per tile: K = first (hi) pooled key plane of the
+  // 64-key stage, V = the row-major pooled values
+  const T* pst = pooled + (int64_t)h * (Mp / C::PT) * C::STAGE;
+  const T* pvh = pooled_v + (int64_t)h * Mp * C::VROW;
+  for (int t = 0; t * KT < M; ++t) {
     __syncthreads();
+    const T* ksrc = pst + (int64_t)(t / 2) * C::STAGE + (t % 2) * KT * C::KROW;
+    const T* vsrc = pvh + (int64_t)t * KT * C::VROW;
     for (int i = wave; i * 64 < C::KCH + C::VCH; i += BW) {
       const int p = i * 64 + lane;
       if (p < C::KCH + C::VCH) {
-        const T* src = p < C::KCH ? pst + (int64_t)t * C::STAGE + p * C::EPC
-                                  : pst + (int64_t)t * C::STAGE + C::NS * C::KTILE + (p - C::KCH) * C::EPC;
+        const T* src = p < C::KCH ? ksrc + p * C::EPC : vsrc + (p - C::KCH) * C::EPC;
         dma16(src, stage + i * 64 * C::EPC);
       }
     }
@@ -426,8 +430,8 @@ template <int DT, int D>
 __global__ __launch_bounds__(64 * BW) void k_bwd_cmp(
     const typename Tr<DT>::T* __restrict__ q, const typename Tr<DT>::T* __restrict__ gates,
     const typename Tr<DT>::T* __restrict__ dout, const typename Tr<DT>::T* __restrict__ pooled,
-    const float* __restrict__ lse3, const float* __restrict__ D3, const int32_t* __restrict__ perm,
-    int Mp, int H, int qch, int64_t N, float scale, float sl2, float* __restrict__ part_k,
+    const typename Tr<DT>::T* __restrict__ pooled_v, const float* __restrict__ lse3,
+    const float* __restrict__ D3, const int32_t* __restrict__ perm, int Mp, int H, int qch, int64_t N, float scale, float sl2, float* __restrict__ part_k,
     float* __restrict__ part_v) {
   using C = Cfg<DT, D>;
   using T = typename Tr<DT>::T;
@@ -442,10 +446,12 @@ __global__ __launch_bounds__(64 * BW) void k_bwd_cmp(
   const int h = (blockIdx.x / qch) % H;
   const int kt = (blockIdx.x / (qch * H)) * BW + wave;
   const bool ktv = kt < ntile;
-  const T* pst = pooled + ((int64_t)h * ntile + (ktv ? kt : 0)) * C::STAGE;
+  const int ktc = ktv ? kt : 0;
+  const T* krow = pooled + ((int64_t)h * (Mp / C::PT) + ktc / 2) * C::STAGE + ((ktc % 2) * KT + c) * C::KROW;
+  const T* vrow = pooled_v + ((int64_t)h * Mp + ktc * KT + c) * C::VROW;
   KvState<DT, D> S;
-  load_q<DT, D>(S.kf, pst + c * C::KROW, ktv, lane);
-  load_q<DT, D>(S.vf, pst + C::NS * C::KTILE + c * C::VROW, ktv, lane);
+  load_q<DT, D>(S.kf, krow, ktv, lane);
+  load_q<DT, D>(S.vf, vrow, ktv, lane);
 #pragma unroll
   for (int j = 0; j < C::NDV; ++j) S.dk[j] = S.dv[j] = zero16();
   const int64_t qlen = (N + qch - 1) / qch;
@@ -532,7 +538,7 @@ hipError_t run_backward(const ssa_plan_s* p, int H, int topk, float scale, const
                         hipStream_t s) {
   using T = typename Tr<DT>::T;
   const int M = (int)p->M;
-  const int Mp = (int)round_up(M, KT);
+  const int Mp = (int)round_up(M, POOL_TILE);
   const int64_t N = p->n;
   const float sl2 = scale * 1.4426950408889634f;
   const int nchunk = (p->max_rows + BROWS - 1) / BROWS;
@@ -540,7 +546,7 @@ hipError_t run_backward(const ssa_plan_s* p, int H, int topk, float scale, const
                      (const T*)dout, (const T*)gates, fw.obr, p->perm, N, H, dgates, w.D);
   hipLaunchKernelGGL((k_bwd_dq<DT, D>), dim3((unsigned)(M * H * nchunk)), dim3(64 * BW), 0, s,
                      (const T*)q, (const T*)k, (const T*)v, (const T*)gates, (const T*)dout,
-                     (const T*)fw.pooled, fw.lse, w.D, p->perm, p->blk_off, p->blk_cell,
+                     (const T*)fw.pooled, (const T*)fw.pooled_v, fw.lse, w.D, p->perm, p->blk_off, p->blk_cell,
                      p->cell_off, p->cell_blk, p->lpt, sel, M, Mp, H, nchunk, N, topk, scale, sl2, dq);
   // inverse selection
   const int64_t E = (int64_t)H * M * topk;
@@ -559,7 +565,8 @@ hipError_t run_backward(const ssa_plan_s* p, int H, int topk, float scale, const
                      w.inv_off, va, M, H, nchunk, N, scale, sl2, dk, dv);
   const int groups = (Mp / KT + BW - 1) / BW;
   hipLaunchKernelGGL((k_bwd_cmp<DT, D>), dim3((unsigned)(groups * H * w.qch)), dim3(64 * BW), 0, s,
-                     (const T*)q, (const T*)gates, (const T*)dout, (const T*)fw.pooled, fw.lse, w.D,
+                     (const T*)q, (const T*)gates, (const T*)dout, (const T*)fw.pooled,
+                     (const T*)fw.pooled_v, fw.lse, w.D,
                      p->perm, Mp, H, w.qch, N, scale, sl2, w.part_k, w.part_v);
   hipLaunchKernelGGL((k_bwd_pool<DT, D>), dim3(M, H), dim3(256), 0, s, (const T*)wk, (const T*)wv,
                      w.part_k, w.part_v, p->perm, p->blk_off, Mp, H, w.qch, dk, dv);

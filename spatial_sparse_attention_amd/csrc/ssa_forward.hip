@@ -39,27 +39,34 @@ constexpr int ATT_ROWS = 32 * ATT_RT * ATT_WAVES;
 
 // ------------------------------------------------------------------ pooling
 // grid (Mp, H).  ktil[h,b] = mean_{i in b} K[i,h] @ Wk ; same for V.  Writes the fp32
-// pooled key split into NSPLIT dtype planes and the pooled value, in the per-(head, tile)
-// stage layout; row padding and padding blocks (b >= M) are zero.
+// pooled key split into NSPLIT dtype planes and the pooled value (transposed) in the
+// per-(head, 64-block tile) stage layout, plus the row-major pooled value; padding
+// blocks (b >= M) and key-row padding are zero.
 template <int DT, int D>
 __global__ __launch_bounds__(256) void k_pool(
     const typename Tr<DT>::T* __restrict__ kin, const typename Tr<DT>::T* __restrict__ vin,
     const typename Tr<DT>::T* __restrict__ wk, const typename Tr<DT>::T* __restrict__ wv,
     const int32_t* __restrict__ perm, const int32_t* __restrict__ blk_off, int M, int Mp, int H,
-    typename Tr<DT>::T* __restrict__ pooled) {
+    typename Tr<DT>::T* __restrict__ pooled, typename Tr<DT>::T* __restrict__ pooled_v) {
   using C = Cfg<DT, D>;
   using T = typename Tr<DT>::T;
   constexpr int NS = C::NS, VEC = C::EPC, CH = C::CPR, RSUB = 256 / CH;
   constexpr int U = 4;  // rows in flight per thread
   __shared__ float redk[RSUB * D], redv[RSUB * D], kbar[D], vbar[D];
   const int b = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
-  T* stg = pooled + ((int64_t)h * (Mp / KT) + b / KT) * C::STAGE;
-  T* krow = stg + (b % KT) * C::KROW;                    // plane s at + s * KTILE
-  T* vrow = stg + NS * C::KTILE + (b % KT) * C::VROW;
+  T* stg = pooled + ((int64_t)h * (Mp / C::PT) + b / C::PT) * C::STAGE;
+  T* krow = stg + (b % C::PT) * C::KROW;          // plane s at + s * KPLANE
+  T* vtcol = stg + NS * C::KPLANE + (b % C::PT);  // column dv at + dv * VTROW
+  T* vrow = pooled_v + ((int64_t)h * Mp + b) * C::VROW;
   for (int j = (b >= M ? 0 : D) + tid; j < C::KROW; j += 256)
-    for (int s = 0; s < NS; ++s) krow[s * C::KTILE + j] = (T)0.f;
-  for (int j = (b >= M ? 0 : D) + tid; j < C::VROW; j += 256) vrow[j] = (T)0.f;
-  if (b >= M) return;
+    for (int s = 0; s < NS; ++s) krow[s * C::KPLANE + j] = (T)0.f;
+  if (b >= M) {
+    for (int j = tid; j < D; j += 256) {
+      vtcol[j * C::VTROW] = (T)0.f;
+      vrow[j] = (T)0.f;
+    }
+    return;
+  }
   const int r0 = blk_off[b], r1 = blk_off[b + 1];
   const int sub = tid / CH, ch = tid % CH;
   if (sub < RSUB) {
@@ -115,11 +122,13 @@ __global__ __launch_bounds__(256) void k_pool(
       float rem = acc;
       for (int s = 0; s < NS; ++s) {
         const T part = Tr<DT>::cvt(rem);
-        krow[s * C::KTILE + c] = part;
+        krow[s * C::KPLANE + c] = part;
         rem -= Tr<DT>::up(part);
       }
     } else {
-      vrow[c] = Tr<DT>::cvt(acc);
+      const T val = Tr<DT>::cvt(acc);
+      vtcol[c * C::VTROW] = val;
+      vrow[c] = val;
     }
   }
 }
@@ -142,7 +151,7 @@ __global__ __launch_bounds__(64 * SEL_WAVES) void k_select(
   constexpr int ROWS = 32 * RT * SEL_WAVES;
   __shared__ __attribute__((aligned(1024))) T stage0[C::STAGE];
   __shared__ __attribute__((aligned(1024))) T stage1[C::STAGE];
-  __shared__ float stage_sum[2][SEL_WAVES][32];
+  __shared__ float stage_sum[2][SEL_WAVES][64];
   __shared__ float lse_lds[ROWS];
   __shared__ int32_t pick[256];
   extern __shared__ float sig[];  // [Mp]
@@ -152,9 +161,9 @@ __global__ __launch_bounds__(64 * SEL_WAVES) void k_select(
   const int b = lpt[blockIdx.x / H];
   const int r0 = blk_off[b], rows = blk_off[b + 1] - r0;
   for (int j = tid; j < Mp; j += 64 * SEL_WAVES) sig[j] = 0.f;
-  const int ntile = Mp / KT;
+  const int ntile = Mp / C::PT;
   const T* pstage = pooled + (int64_t)h * ntile * C::STAGE;
-  constexpr int NCH1 = C::STAGE * sizeof(T) / 16, NCH2 = NS * C::KCH;
+  constexpr int NCH1 = C::STAGE * sizeof(T) / 16, NCH2 = NS * C::KPLANE * sizeof(T) / 16;
 
   for (int sw = 0; sw * ROWS < rows; ++sw) {
     const int wbase = sw * ROWS + wave * 32 * RT;   // first row of this wave
@@ -169,6 +178,7 @@ __global__ __launch_bounds__(64 * SEL_WAVES) void k_select(
     }
 
     // ---------------- pass 1: online softmax over all pooled keys -> o_c, lse
+    // 64 pooled keys per stage: two independent 32-key score tiles per wave.
     Online<C::NDV> st[RT];
 #pragma unroll
     for (int u = 0; u < RT; ++u) st[u].init();
@@ -176,39 +186,38 @@ __global__ __launch_bounds__(64 * SEL_WAVES) void k_select(
       auto p1 = [&](int t, T* cur, T* nxt) {
         dma_wait();
         __syncthreads();
-        VFrags<DT, D> vf;
-        if (wave_active) vf.read(cur + NS * C::KTILE, lane);
         if (t + 1 < ntile) dma_contiguous<SEL_WAVES>(nxt, pstage + (int64_t)(t + 1) * C::STAGE, NCH1, wave, lane);
         if (wave_active) {
-          ssa_f16v acc[RT];
-#pragma unroll
-          for (int u = 0; u < RT; ++u) acc[u] = zero16();
           const T* krow = cur + (lane & 31) * C::KROW + (lane >> 5) * C::KPL;
-#pragma unroll
-          for (int s = 0; s < NS; ++s)
-#pragma unroll
-            for (int ks = 0; ks < C::NKS; ++ks) {
-              const F kf = load_frag<DT>(krow + s * C::KTILE + ks * C::KS);
-#pragma unroll
-              for (int u = 0; u < RT; ++u) acc[u] = Tr<DT>::mma(kf, qf[u][ks], acc[u]);
-            }
+          const T* vtt = cur + NS * C::KPLANE;
 #pragma unroll
           for (int u = 0; u < RT; ++u) {
+            ssa_f16v a0 = zero16(), a1 = zero16();
+#pragma unroll
+            for (int s = 0; s < NS; ++s)
+#pragma unroll
+              for (int ks = 0; ks < C::NKS; ++ks) {
+                a0 = Tr<DT>::mma(load_frag<DT>(krow + s * C::KPLANE + ks * C::KS), qf[u][ks], a0);
+                a1 = Tr<DT>::mma(load_frag<DT>(krow + s * C::KPLANE + 32 * C::KROW + ks * C::KS), qf[u][ks], a1);
+              }
             if (t == ntile - 1) {
 #pragma unroll
-              for (int r = 0; r < 16; ++r)
-                if (t * KT + res_row(r, g) >= M) acc[u][r] = -INFINITY;
+              for (int r = 0; r < 16; ++r) {
+                if (t * C::PT + res_row(r, g) >= M) a0[r] = -INFINITY;
+                if (t * C::PT + 32 + res_row(r, g) >= M) a1[r] = -INFINITY;
+              }
             }
-            st[u].update(acc[u], sl2);
+            st[u].update2(a0, a1, sl2);
+#pragma unroll
+            for (int ks = 0; ks < C::PK; ++ks) {
+              const F p0 = p_frag<DT>(a0, ks), p1f = p_frag<DT>(a1, ks);
+#pragma unroll
+              for (int j = 0; j < C::NDV; ++j) {
+                st[u].o[j] = Tr<DT>::mma(vtt_frag<DT, D>(vtt, 0, ks, j, lane), p0, st[u].o[j]);
+                st[u].o[j] = Tr<DT>::mma(vtt_frag<DT, D>(vtt, 32, ks, j, lane), p1f, st[u].o[j]);
+              }
+            }
           }
-#pragma unroll
-          for (int ks = 0; ks < C::PK; ++ks)
-#pragma unroll
-            for (int u = 0; u < RT; ++u) {
-              const F pf = p_frag<DT>(acc[u], ks);
-#pragma unroll
-              for (int j = 0; j < C::NDV; ++j) st[u].o[j] = Tr<DT>::mma(vf.f[ks][j], pf, st[u].o[j]);
-            }
         }
       };
       __syncthreads();  // the previous sweep is done with both stage buffers
@@ -248,8 +257,8 @@ __global__ __launch_bounds__(64 * SEL_WAVES) void k_select(
       for (int r = 0; r < 16; ++r) lrow[u][r] = lse_lds[wave * 32 * RT + 32 * u + res_row(r, g)];
     {
       auto fold = [&](int t) {  // sum the per-wave column sums of tile t into sigma (fixed order)
-        if (tid < 32) {
-          const int key = t * KT + tid;
+        if (tid < C::PT) {
+          const int key = t * C::PT + tid;
           float s = stage_sum[t & 1][0][tid];
 #pragma unroll
           for (int w = 1; w < SEL_WAVES; ++w) s += stage_sum[t & 1][w][tid];
@@ -261,27 +270,32 @@ __global__ __launch_bounds__(64 * SEL_WAVES) void k_select(
         __syncthreads();
         if (t + 1 < ntile) dma_contiguous<SEL_WAVES>(nxt, pstage + (int64_t)(t + 1) * C::STAGE, NCH2, wave, lane);
         if (t > 0) fold(t - 1);
-        float colsum = 0.f;
+        float cs0 = 0.f, cs1 = 0.f;
         if (wave_active) {
-          ssa_f16v acc[RT];
-#pragma unroll
-          for (int u = 0; u < RT; ++u) acc[u] = zero16();
           const T* krow = cur + (lane & 31) * C::KROW + (lane >> 5) * C::KPL;
 #pragma unroll
-          for (int s = 0; s < NS; ++s)
+          for (int u = 0; u < RT; ++u) {
+            ssa_f16v a0 = zero16(), a1 = zero16();
 #pragma unroll
-            for (int ks = 0; ks < C::NKS; ++ks) {
-              const F kf = load_frag<DT>(krow + s * C::KTILE + ks * C::KS);
+            for (int s = 0; s < NS; ++s)
 #pragma unroll
-              for (int u = 0; u < RT; ++u) acc[u] = Tr<DT>::mma(qf[u][ks], kf, acc[u]);
+              for (int ks = 0; ks < C::NKS; ++ks) {
+                a0 = Tr<DT>::mma(qf[u][ks], load_frag<DT>(krow + s * C::KPLANE + ks * C::KS), a0);
+                a1 = Tr<DT>::mma(qf[u][ks], load_frag<DT>(krow + s * C::KPLANE + 32 * C::KROW + ks * C::KS), a1);
+              }
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              cs0 += fast_exp2(__builtin_fmaf(a0[r], sl2, -lrow[u][r]));
+              cs1 += fast_exp2(__builtin_fmaf(a1[r], sl2, -lrow[u][r]));
             }
-#pragma unroll
-          for (int u = 0; u < RT; ++u)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) colsum += fast_exp2(__builtin_fmaf(acc[u][r], sl2, -lrow[u][r]));
-          colsum = xor32_sum(colsum);
+          }
+          cs0 = xor32_sum(cs0);
+          cs1 = xor32_sum(cs1);
         }
-        if (g == 0) stage_sum[t & 1][wave][c] = colsum;
+        if (g == 0) {
+          stage_sum[t & 1][wave][c] = cs0;
+          stage_sum[t & 1][wave][32 + c] = cs1;
+        }
       };
       dma_contiguous<SEL_WAVES>(stage0, pstage, NCH2, wave, lane);
       for (int t = 0; t < ntile; t += 2) {
@@ -536,9 +550,10 @@ template <int DT, int D>
 hipError_t run_pool(const ssa_plan_s* p, int H, const void* k, const void* v, const void* wk,
                     const void* wv, const FwdWs& w, hipStream_t s) {
   using T = typename Tr<DT>::T;
-  const int Mp = (int)round_up(p->M, KT);
+  const int Mp = (int)round_up(p->M, POOL_TILE);
   hipLaunchKernelGGL((k_pool<DT, D>), dim3(Mp, H), dim3(256), 0, s, (const T*)k, (const T*)v,
-                     (const T*)wk, (const T*)wv, p->perm, p->blk_off, (int)p->M, Mp, H, (T*)w.pooled);
+                     (const T*)wk, (const T*)wv, p->perm, p->blk_off, (int)p->M, Mp, H, (T*)w.pooled,
+                     (T*)w.pooled_v);
   return hipGetLastError();
 }
 
@@ -546,7 +561,7 @@ template <int DT, int D>
 hipError_t run_select(const ssa_plan_s* p, int H, int topk, float sl2, const void* q,
                       const FwdWs& w, int32_t* sel, hipStream_t s) {
   using T = typename Tr<DT>::T;
-  const int Mp = (int)round_up(p->M, KT);
+  const int Mp = (int)round_up(p->M, POOL_TILE);
   const size_t shm = (size_t)Mp * sizeof(float);
   hipLaunchKernelGGL((k_select<DT, D>), dim3((unsigned)(p->M * H)), dim3(64 * SEL_WAVES), shm, s,
                      (const T*)q, (const T*)w.pooled, p->perm, p->blk_off, p->lpt, (int)p->M, Mp, H,
@@ -578,6 +593,31 @@ hipError_t pool_d(int d, const ssa_plan_s* p, int H, const void* k, const void* 
     case 128: return run_pool<DT, 128>(p, H, k, v, wk, wv, w, s);
   }
   return hipErrorInvalidValue;
+}
+
+// Most pooled blocks the selection kernel takes: its importance vector [round_up(M, 64)]
+// fp32 lives in LDS beside the kernel's static arrays, within the 160 KB of a workgroup.
+template <int DT, int D>
+int64_t select_limit() {
+  static int64_t lim = -1;
+  if (lim < 0) {
+    hipFuncAttributes a;
+    if (hipFuncGetAttributes(&a, reinterpret_cast<const void*>(&k_select<DT, D>)) != hipSuccess) return 0;
+    const int64_t room = (int64_t)LDS_BYTES - (int64_t)a.sharedSizeBytes;
+    lim = room <= 0 ? 0 : room / (int64_t)sizeof(float) / POOL_TILE * POOL_TILE;
+  }
+  return lim;
+}
+
+template <int DT>
+int64_t select_limit_d(int d) {
+  switch (d) {
+    case 32: return select_limit<DT, 32>();
+    case 64: return select_limit<DT, 64>();
+    case 96: return select_limit<DT, 96>();
+    case 128: return select_limit<DT, 128>();
+  }
+  return 0;
 }
 
 template <int DT>
@@ -616,6 +656,15 @@ hipError_t launch_pool(ssa_dtype dt, const ssa_plan_s* p, int H, int d, const vo
     case SSA_BF16: return pool_d<DT_BF16>(d, p, H, k, v, wk, wv, w, s);
   }
   return hipErrorInvalidValue;
+}
+
+int64_t select_block_limit(ssa_dtype dt, int d) {
+  switch (dt) {
+    case SSA_F32: return select_limit_d<DT_F32>(d);
+    case SSA_F16: return select_limit_d<DT_F16>(d);
+    case SSA_BF16: return select_limit_d<DT_BF16>(d);
+  }
+  return 0;
 }
 
 hipError_t launch_select(ssa_dtype dt, const ssa_plan_s* p, int H, int d, int topk, float scale,

@@ -46,19 +46,23 @@ static inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * 
 static inline int nsplit_of(ssa_dtype dt) { return dt == SSA_F32 ? 1 : (dt == SSA_F16 ? 2 : 3); }
 static inline size_t esize_of(ssa_dtype dt) { return dt == SSA_F32 ? 4 : 2; }
 
-// Row strides (elements) of the padded 32-row tiles staged in LDS.  The pooled keys and
-// values are stored in HBM as one "stage" per (head, 32-block tile): the NSPLIT key planes
-// ([32][krow] each) followed by the value tile ([32][vrow]), exactly the LDS layout, so a
-// tile is one contiguous copy.
+// Row strides (elements) of the padded tiles staged in LDS.  The pooled keys and values
+// are stored in HBM as one "stage" per (head, 64-block tile): the NSPLIT key planes
+// ([64][krow] each) followed by the values transposed ([d][vtrow]), exactly the LDS
+// layout, so a tile is one contiguous copy.  A row-major copy of the pooled values
+// ([H][Mp][vrow]) serves the backward.
+constexpr int POOL_TILE = 64;
 static inline int krow_of(ssa_dtype dt, int d) { return d + (dt == SSA_F32 ? 4 : 8); }
 static inline int vrow_of(ssa_dtype dt, int d) { return d + (dt == SSA_F32 ? 8 : 16); }
+static inline int vtrow_of(ssa_dtype dt) { return dt == SSA_F32 ? POOL_TILE + 1 : POOL_TILE + 4; }
 static inline int64_t stage_elems(ssa_dtype dt, int d) {
-  return (int64_t)32 * (nsplit_of(dt) * krow_of(dt, d) + vrow_of(dt, d));
+  return (int64_t)POOL_TILE * nsplit_of(dt) * krow_of(dt, d) + (int64_t)d * vtrow_of(dt);
 }
 
 // Forward workspace layout.  Rows r are block-sorted token positions.
 struct FwdWs {
-  void* pooled;      // [H][Mp/32][stage] dtype: pooled key planes + pooled values, padding zero
+  void* pooled;      // [H][Mp/64][stage] dtype: pooled key planes + pooled values^T, padding zero
+  void* pooled_v;    // [H][Mp][vrow] dtype: pooled values, row-major
   void* oc;          // [N][H][d] compressed-branch output (dtype)
   int32_t* sel;      // [H][M][topk]
   // saved for the backward (save_for_bwd only; else null)
@@ -89,6 +93,8 @@ static inline int64_t scan_part_len(int64_t len) { return len / 4096 + 2; }
 hipError_t launch_pool(ssa_dtype dt, const ssa_plan_s* p, int H, int d, const void* k,
                        const void* v, const void* wk, const void* wv, const FwdWs& w,
                        hipStream_t s);
+constexpr int LDS_BYTES = 160 * 1024;  // LDS of one workgroup on gfx950
+int64_t select_block_limit(ssa_dtype dt, int d);
 hipError_t launch_select(ssa_dtype dt, const ssa_plan_s* p, int H, int d, int topk, float scale,
                          const void* q, const FwdWs& w, int32_t* sel, hipStream_t s);
 hipError_t launch_backward(ssa_dtype dt, const ssa_plan_s* p, int H, int d, int topk, float scale,

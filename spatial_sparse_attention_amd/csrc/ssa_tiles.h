@@ -23,8 +23,12 @@ struct Cfg {
   static constexpr int KTILE = KT * KROW, VTILE = KT * VROW;
   static constexpr int KCH = KTILE * sizeof(T) / 16;    // 16-byte chunks of a K tile
   static constexpr int VCH = VTILE * sizeof(T) / 16;
-  static constexpr int STAGE = NS * KTILE + VTILE;      // pooled stage (elements)
   static constexpr int PK = KT / KS;                    // K steps over a 32-key tile (PV)
+  // pooled stage: NS key planes [64][KROW], then the values transposed [D][VTROW]
+  static constexpr int PT = 64;
+  static constexpr int VTROW = sizeof(T) == 4 ? PT + 1 : PT + 4;
+  static constexpr int KPLANE = PT * KROW;
+  static constexpr int STAGE = NS * KPLANE + D * VTROW;
 };
 
 // ------------------------------------------------------------------ MFMA building blocks
@@ -69,6 +73,27 @@ __device__ inline typename Tr<DT>::frag tr_frag(const typename Tr<DT>::T* tile, 
 template <int DT, int D>
 __device__ inline typename Tr<DT>::frag vt_frag(const typename Tr<DT>::T* vt, int ks, int j, int lane) {
   return tr_frag<DT, Cfg<DT, D>::VROW>(vt, ks, j, lane);
+}
+
+// The same A operand (V^T, output columns 32j..32j+31, K step ks) from a transposed value
+// tile vtt[dv][key] (row stride VTROW) whose 32-key sub-tile starts at key kb: ordinary
+// 8-byte LDS reads of keys kb + 16ks + 4g + {0..3} and kb + 16ks + 8 + 4g + {0..3}.
+template <int DT, int D>
+__device__ inline typename Tr<DT>::frag vtt_frag(const typename Tr<DT>::T* vtt, int kb, int ks, int j,
+                                                 int lane) {
+  using C = Cfg<DT, D>;
+  const int g = lane >> 5;
+  const typename Tr<DT>::T* row = vtt + (32 * j + (lane & 31)) * C::VTROW + kb;
+  if constexpr (C::KPL == 1) {
+    return row[res_row(ks, g)];
+  } else {
+    typedef unsigned u2 __attribute__((ext_vector_type(2)));
+    typedef unsigned u4 __attribute__((ext_vector_type(4)));
+    const u2 a = *reinterpret_cast<const u2*>(row + 16 * ks + 4 * g);
+    const u2 b = *reinterpret_cast<const u2*>(row + 16 * ks + 8 + 4 * g);
+    const u4 u = {a.x, a.y, b.x, b.y};
+    return __builtin_bit_cast(typename Tr<DT>::frag, u);
+  }
 }
 
 // The V^T fragments of one 32-key tile, read before the next tile's copy is issued: the
@@ -130,6 +155,33 @@ struct Online {
     l = 0.f;
 #pragma unroll
     for (int j = 0; j < NDV; ++j) o[j] = zero16();
+  }
+  // Two 16-score sets of the same row (a 64-key tile).  Returns p in s0, s1.
+  __device__ inline void update2(ssa_f16v& s0, ssa_f16v& s1, float sl2) {
+    float mt0 = fmaxf(s0[0], s0[1]), mt1 = fmaxf(s1[0], s1[1]);
+#pragma unroll
+    for (int r = 2; r < 16; r += 2) {
+      mt0 = fmaxf(mt0, fmaxf(s0[r], s0[r + 1]));
+      mt1 = fmaxf(mt1, fmaxf(s1[r], s1[r + 1]));
+    }
+    const float mt = xor32_max(fmaxf(mt0, mt1)) * sl2;
+    if (__builtin_amdgcn_ballot_w64(mt > m + RESCALE_SLACK)) {
+      const float mn = fmaxf(m, mt);
+      const float alpha = fast_exp2(m - mn);
+      l *= alpha;
+#pragma unroll
+      for (int j = 0; j < NDV; ++j) o[j] *= alpha;
+      m = mn;
+    }
+    float sum0 = 0.f, sum1 = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      s0[r] = fast_exp2(__builtin_fmaf(s0[r], sl2, -m));
+      s1[r] = fast_exp2(__builtin_fmaf(s1[r], sl2, -m));
+      sum0 += s0[r];
+      sum1 += s1[r];
+    }
+    l += sum0 + sum1;
   }
   // s: raw scores (-inf for masked keys); sl2 = scale * log2(e) > 0.  Returns p in s.
   __device__ inline void update(ssa_f16v& s, float sl2) {
