@@ -12,6 +12,8 @@ SOURCES = ["ssa_plan.hip", "ssa_forward.hip", "ssa_backward.hip", "ssa_api.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         # kernels never rely on NaN semantics: lets max/min skip NaN quieting
+         "-Xarch_device", "-fno-honor-nans",
          "-I" + os.path.join(ROOT, "include"), "-I" + CSRC]
 
 

@@ -23,7 +23,6 @@
 // planes whose sum reproduces the fp32 value, so the scores that decide the top-k
 // carry fp32-level error.
 #include <hip/hip_runtime.h>
-#include <type_traits>
 #include "ssa_internal.h"
 #include "ssa_mfma.h"
 #include "ssa_tiles.h"
@@ -31,8 +30,7 @@
 namespace {
 
 using namespace ssa_dev;
-constexpr int SEL_RT = 1;         // compressed/select: 32-row query tiles per wave
-constexpr int SEL_WAVES = 8;      //   and waves per workgroup (256 rows per sweep)
+constexpr int SEL_WAVES = 8;      // compressed/select: waves per workgroup (256 rows per sweep)
 constexpr int ATT_RT = 2;         // selected/window: 32-row query tiles per wave
 constexpr int ATT_WAVES = 4;      //   and waves per workgroup (256 rows per chunk)
 constexpr int ATT_ROWS = 32 * ATT_RT * ATT_WAVES;
@@ -134,8 +132,63 @@ __global__ __launch_bounds__(256) void k_pool(
 }
 
 // ------------------------------------------------------------------ compressed + select
-// One workgroup per (query block, head), longest blocks first.  Each wave owns RT row
-// tiles of 32 queries, so every K or V fragment read from LDS feeds RT MFMAs.
+// Scores of one wave's 32 query rows against the 64 pooled keys of a stage, as two 32-key
+// halves a0 (keys 0..31) and a1 (keys 32..63), summed over the NSPLIT key planes.
+// KQ: S^T layout (lane = query; pooled keys are the A operand), else S layout (lane = key).
+// krow: this lane's row of key plane 0 (row lane%32, column offset (lane/32)*KPL).
+// The fragment reads run PF steps ahead of the MFMAs that use them.  With vtt != nullptr the
+// transposed value fragments of both halves (for O^T += V^T P^T) are read into vt behind the
+// key fragments, so that they arrive while the softmax runs.
+template <int DT, int D, bool KQ, bool VPRE>
+__device__ inline void stage_scores(const typename Tr<DT>::T* krow, const typename Tr<DT>::frag* qf,
+                                    ssa_f16v& a0, ssa_f16v& a1, const typename Tr<DT>::T* vtt,
+                                    typename Tr<DT>::frag (*vt)[Cfg<DT, D>::PK][Cfg<DT, D>::NDV],
+                                    int lane) {
+  using C = Cfg<DT, D>;
+  using F = typename Tr<DT>::frag;
+  constexpr int NST = C::NS * C::NKS, PF = 3;
+  F f0[NST], f1[NST];
+#pragma unroll
+  for (int i = 0; i < NST; ++i) {
+    const int s = i / C::NKS, ks = i % C::NKS;
+    f0[i] = load_frag<DT>(krow + s * C::KPLANE + ks * C::KS);
+    f1[i] = load_frag<DT>(krow + s * C::KPLANE + 32 * C::KROW + ks * C::KS);
+  }
+  a0 = zero16();
+  a1 = zero16();
+#pragma unroll
+  for (int i = 0; i < NST; ++i) {
+    const int ks = i % C::NKS;
+    if constexpr (KQ) {
+      a0 = Tr<DT>::mma(f0[i], qf[ks], a0);
+      a1 = Tr<DT>::mma(f1[i], qf[ks], a1);
+    } else {
+      a0 = Tr<DT>::mma(qf[ks], f0[i], a0);
+      a1 = Tr<DT>::mma(qf[ks], f1[i], a1);
+    }
+  }
+  if constexpr (VPRE) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int ks = 0; ks < C::PK; ++ks)
+#pragma unroll
+        for (int j = 0; j < C::NDV; ++j) vt[h][ks][j] = vtt_frag<DT, D>(vtt, 32 * h, ks, j, lane);
+  }
+  // schedule (16-bit types): PF steps of key reads, then per step two MFMAs and the reads PF
+  // steps ahead.  fp32 (one register per fragment, 2x the steps) is left to the compiler.
+  if constexpr (sizeof(typename Tr<DT>::T) == 2) {
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * PF, 0);
+#pragma unroll
+    for (int i = 0; i < NST; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      if (i + PF < NST) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+  }
+}
+
+// One workgroup per (query block, head), longest blocks first; each wave owns a tile of 32
+// query rows, and the workgroup sweeps the block 32 * SEL_WAVES rows at a time.
 template <int DT, int D>
 __global__ __launch_bounds__(64 * SEL_WAVES) void k_select(
     const typename Tr<DT>::T* __restrict__ q, const typename Tr<DT>::T* __restrict__ pooled,
@@ -147,8 +200,7 @@ __global__ __launch_bounds__(64 * SEL_WAVES) void k_select(
   using T = typename Tr<DT>::T;
   using F = typename Tr<DT>::frag;
   constexpr int NS = C::NS;
-  constexpr int RT = SEL_RT;
-  constexpr int ROWS = 32 * RT * SEL_WAVES;
+  constexpr int ROWS = 32 * SEL_WAVES;
   __shared__ __attribute__((aligned(1024))) T stage0[C::STAGE];
   __shared__ __attribute__((aligned(1024))) T stage1[C::STAGE];
   __shared__ float stage_sum[2][SEL_WAVES][64];
@@ -166,55 +218,48 @@ __global__ __launch_bounds__(64 * SEL_WAVES) void k_select(
   constexpr int NCH1 = C::STAGE * sizeof(T) / 16, NCH2 = NS * C::KPLANE * sizeof(T) / 16;
 
   for (int sw = 0; sw * ROWS < rows; ++sw) {
-    const int wbase = sw * ROWS + wave * 32 * RT;   // first row of this wave
-    const bool wave_active = wbase < rows;
-    F qf[RT][C::NKS];
-    bool valid[RT];
-#pragma unroll
-    for (int u = 0; u < RT; ++u) {
-      const int my_row = wbase + 32 * u + c;
-      valid[u] = my_row < rows;
-      load_q<DT, D>(qf[u], q + ((int64_t)(valid[u] ? perm[r0 + my_row] : 0) * H + h) * D, valid[u], lane);
-    }
+    const int my_row = sw * ROWS + wave * 32 + c;
+    const bool wave_active = sw * ROWS + wave * 32 < rows;
+    const bool valid = my_row < rows;
+    F qf[C::NKS];
+    load_q<DT, D>(qf, q + ((int64_t)(valid ? perm[r0 + my_row] : 0) * H + h) * D, valid, lane);
 
     // ---------------- pass 1: online softmax over all pooled keys -> o_c, lse
     // 64 pooled keys per stage: two independent 32-key score tiles per wave.
-    Online<C::NDV> st[RT];
-#pragma unroll
-    for (int u = 0; u < RT; ++u) st[u].init();
+    Online<C::NDV> st;
+    st.init();
     {
       auto p1 = [&](int t, T* cur, T* nxt) {
         dma_wait();
         __syncthreads();
         if (t + 1 < ntile) dma_contiguous<SEL_WAVES>(nxt, pstage + (int64_t)(t + 1) * C::STAGE, NCH1, wave, lane);
         if (wave_active) {
-          const T* krow = cur + (lane & 31) * C::KROW + (lane >> 5) * C::KPL;
+          ssa_f16v a0, a1;
+          // value fragments read ahead for 16-bit types (fp32 ones would take 2*D registers)
+          constexpr bool VPRE = sizeof(T) == 2;
           const T* vtt = cur + NS * C::KPLANE;
+          F vt[2][C::PK][C::NDV];
+          stage_scores<DT, D, true, VPRE>(cur + (lane & 31) * C::KROW + (lane >> 5) * C::KPL, qf, a0,
+                                          a1, vtt, vt, lane);
+          if (t == ntile - 1) {
 #pragma unroll
-          for (int u = 0; u < RT; ++u) {
-            ssa_f16v a0 = zero16(), a1 = zero16();
-#pragma unroll
-            for (int s = 0; s < NS; ++s)
-#pragma unroll
-              for (int ks = 0; ks < C::NKS; ++ks) {
-                a0 = Tr<DT>::mma(load_frag<DT>(krow + s * C::KPLANE + ks * C::KS), qf[u][ks], a0);
-                a1 = Tr<DT>::mma(load_frag<DT>(krow + s * C::KPLANE + 32 * C::KROW + ks * C::KS), qf[u][ks], a1);
-              }
-            if (t == ntile - 1) {
-#pragma unroll
-              for (int r = 0; r < 16; ++r) {
-                if (t * C::PT + res_row(r, g) >= M) a0[r] = -INFINITY;
-                if (t * C::PT + 32 + res_row(r, g) >= M) a1[r] = -INFINITY;
-              }
+            for (int r = 0; r < 16; ++r) {
+              if (t * C::PT + res_row(r, g) >= M) a0[r] = -INFINITY;
+              if (t * C::PT + 32 + res_row(r, g) >= M) a1[r] = -INFINITY;
             }
-            st[u].update2(a0, a1, sl2);
+          }
+          st.update2(a0, a1, sl2);
 #pragma unroll
-            for (int ks = 0; ks < C::PK; ++ks) {
-              const F p0 = p_frag<DT>(a0, ks), p1f = p_frag<DT>(a1, ks);
+          for (int ks = 0; ks < C::PK; ++ks) {
+            const F p0 = p_frag<DT>(a0, ks), p1f = p_frag<DT>(a1, ks);
 #pragma unroll
-              for (int j = 0; j < C::NDV; ++j) {
-                st[u].o[j] = Tr<DT>::mma(vtt_frag<DT, D>(vtt, 0, ks, j, lane), p0, st[u].o[j]);
-                st[u].o[j] = Tr<DT>::mma(vtt_frag<DT, D>(vtt, 32, ks, j, lane), p1f, st[u].o[j]);
+            for (int j = 0; j < C::NDV; ++j) {
+              if constexpr (VPRE) {
+                st.o[j] = Tr<DT>::mma(vt[0][ks][j], p0, st.o[j]);
+                st.o[j] = Tr<DT>::mma(vt[1][ks][j], p1f, st.o[j]);
+              } else {
+                st.o[j] = Tr<DT>::mma(vtt_frag<DT, D>(vtt, 0, ks, j, lane), p0, st.o[j]);
+                st.o[j] = Tr<DT>::mma(vtt_frag<DT, D>(vtt, 32, ks, j, lane), p1f, st.o[j]);
               }
             }
           }
@@ -227,34 +272,30 @@ __global__ __launch_bounds__(64 * SEL_WAVES) void k_select(
         if (t + 1 < ntile) p1(t + 1, stage1, stage0);
       }
     }
-#pragma unroll
-    for (int u = 0; u < RT; ++u) {
-      const float ltot = xor32_sum(st[u].l);
-      const int my_row = wbase + 32 * u + c;
-      if (wave_active && valid[u]) {
+    {
+      const float ltot = xor32_sum(st.l);
+      if (wave_active && valid) {
         const float inv = 1.f / ltot;
         T* orow = oc + ((int64_t)(r0 + my_row) * H + h) * D;
-        if (lse_save && g == 0) lse_save[(int64_t)h * N + r0 + my_row] = st[u].m + fast_log2(ltot);
+        if (lse_save && g == 0) lse_save[(int64_t)h * N + r0 + my_row] = st.m + fast_log2(ltot);
         float* srow = oc_save ? oc_save + ((int64_t)(r0 + my_row) * H + h) * D : nullptr;
 #pragma unroll
         for (int j = 0; j < C::NDV; ++j)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            orow[32 * j + res_row(r, g)] = Tr<DT>::cvt(st[u].o[j][r] * inv);
-            if (srow) srow[32 * j + res_row(r, g)] = st[u].o[j][r] * inv;
+            orow[32 * j + res_row(r, g)] = Tr<DT>::cvt(st.o[j][r] * inv);
+            if (srow) srow[32 * j + res_row(r, g)] = st.o[j][r] * inv;
           }
       }
       // rows past the block get +inf, so their probabilities in pass 2 are exactly zero
-      if (g == 0) lse_lds[wave * 32 * RT + 32 * u + c] = valid[u] ? st[u].m + fast_log2(ltot) : INFINITY;
+      if (g == 0) lse_lds[wave * 32 + c] = valid ? st.m + fast_log2(ltot) : INFINITY;
     }
     __syncthreads();
 
     // ---------------- pass 2: importance column sums (S layout)
-    float lrow[RT][16];
+    float lrow[16];
 #pragma unroll
-    for (int u = 0; u < RT; ++u)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) lrow[u][r] = lse_lds[wave * 32 * RT + 32 * u + res_row(r, g)];
+    for (int r = 0; r < 16; ++r) lrow[r] = lse_lds[wave * 32 + res_row(r, g)];
     {
       auto fold = [&](int t) {  // sum the per-wave column sums of tile t into sigma (fixed order)
         if (tid < C::PT) {
@@ -272,22 +313,13 @@ __global__ __launch_bounds__(64 * SEL_WAVES) void k_select(
         if (t > 0) fold(t - 1);
         float cs0 = 0.f, cs1 = 0.f;
         if (wave_active) {
-          const T* krow = cur + (lane & 31) * C::KROW + (lane >> 5) * C::KPL;
+          ssa_f16v a0, a1;
+          stage_scores<DT, D, false, false>(cur + (lane & 31) * C::KROW + (lane >> 5) * C::KPL, qf,
+                                            a0, a1, nullptr, nullptr, lane);
 #pragma unroll
-          for (int u = 0; u < RT; ++u) {
-            ssa_f16v a0 = zero16(), a1 = zero16();
-#pragma unroll
-            for (int s = 0; s < NS; ++s)
-#pragma unroll
-              for (int ks = 0; ks < C::NKS; ++ks) {
-                a0 = Tr<DT>::mma(qf[u][ks], load_frag<DT>(krow + s * C::KPLANE + ks * C::KS), a0);
-                a1 = Tr<DT>::mma(qf[u][ks], load_frag<DT>(krow + s * C::KPLANE + 32 * C::KROW + ks * C::KS), a1);
-              }
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              cs0 += fast_exp2(__builtin_fmaf(a0[r], sl2, -lrow[u][r]));
-              cs1 += fast_exp2(__builtin_fmaf(a1[r], sl2, -lrow[u][r]));
-            }
+          for (int r = 0; r < 16; ++r) {
+            cs0 += fast_exp2(__builtin_fmaf(a0[r], sl2, -lrow[r]));
+            cs1 += fast_exp2(__builtin_fmaf(a1[r], sl2, -lrow[r]));
           }
           cs0 = xor32_sum(cs0);
           cs1 = xor32_sum(cs1);
