@@ -114,7 +114,7 @@ void ssa_plan_destroy(ssa_plan plan);
  * selection are computed from a split of the fp32 pooled keys into two (f16) or
  * three (bf16) dtype terms, so they carry fp32-level accuracy).  The selection
  * keeps each work item's importance vector in on-chip memory, which bounds the
- * number of occupied blocks M: at most 6144, and at most 5760 (f32) or 4608
+ * number of occupied blocks M: at most 6144, and at most 5760 (f32) or 4480
  * (bf16) for d = 128; a larger plan returns SSA_ERR_UNSUPPORTED.
  */
 size_t ssa_forward_workspace_size(ssa_plan plan, ssa_dtype dtype, int32_t heads, int32_t dim,

@@ -23,7 +23,7 @@ ssa_status check_common(ssa_plan p, ssa_dtype dt, int32_t H, int32_t d, int32_t 
 
 size_t fwd_carve(Carver& c, const ssa_plan_s* p, ssa_dtype dt, int H, int d, int topk, int save,
                  FwdWs* w) {
-  const int64_t Mp = round_up(p->M > 0 ? p->M : 1, POOL_TILE);
+  const int64_t Mp = pooled_rows(p->M);
   const int64_t n1 = p->n > 0 ? p->n : 1;
   const size_t es = esize_of(dt);
   FwdWs t;

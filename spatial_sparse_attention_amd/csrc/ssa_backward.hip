@@ -43,7 +43,7 @@ int cmp_chunks(int64_t Mp, int H) {
 
 size_t carve(Carver& c, const ssa_plan_s* p, int H, int d, int topk, BwdWs* w) {
   const int64_t M = p->M > 0 ? p->M : 1, n1 = p->n > 0 ? p->n : 1;
-  const int64_t Mp = round_up(M, POOL_TILE);
+  const int64_t Mp = pooled_rows(M);
   const int64_t E = (int64_t)H * M * topk;
   BwdWs t;
   t.qch = cmp_chunks(Mp, H);
@@ -538,7 +538,7 @@ hipError_t run_backward(const ssa_plan_s* p, int H, int topk, float scale, const
                         hipStream_t s) {
   using T = typename Tr<DT>::T;
   const int M = (int)p->M;
-  const int Mp = (int)round_up(M, POOL_TILE);
+  const int Mp = (int)pooled_rows(M);
   const int64_t N = p->n;
   const float sl2 = scale * 1.4426950408889634f;
   const int nchunk = (p->max_rows + BROWS - 1) / BROWS;

@@ -187,8 +187,101 @@ __device__ inline void stage_scores(const typename Tr<DT>::T* krow, const typena
   }
 }
 
+// Stores 4 consecutive floats as the element type (one 8- or 16-byte store).
+template <typename T>
+__device__ inline void store4(T* p, float a, float b, float c, float d) {
+  if constexpr (sizeof(T) == 4) {
+    *reinterpret_cast<float4*>(p) = make_float4(a, b, c, d);
+  } else {
+    typedef unsigned u2 __attribute__((ext_vector_type(2)));
+    const T v[4] = {(T)a, (T)b, (T)c, (T)d};
+    *reinterpret_cast<u2*>(p) = __builtin_bit_cast(u2, v);
+  }
+}
+
+// Top keff = min(topk, M) entries of sig[0..M) (ties to the lower id), written in ascending
+// id order to out[0..keff), out[keff..topk) = -1.  sig >= 0, so the fp32 bit patterns order
+// like the values: a radix select over four 8-bit digits finds the keff-th largest pattern
+// T and how many entries equal to T to take; a scan in id order then places every entry
+// above T and the first such ties.  All NW waves take part.
+template <int NW>
+__device__ void topk_radix(const float* sig, int M, int topk, int32_t* __restrict__ out,
+                           uint32_t* hist, uint32_t* bc, uint32_t (*wc)[NW], int tid) {
+  constexpr int NTH = 64 * NW;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int keff = min(topk, M);
+  uint32_t prefix = 0, need = (uint32_t)keff;
+  const bool all = keff == M;
+  if (!all) {
+    for (int shift = 24; shift >= 0; shift -= 8) {
+      const uint32_t hmask = shift == 24 ? 0u : (0xFFFFFFFFu << (shift + 8));
+      for (int e = tid; e < 256; e += NTH) hist[e] = 0;
+      __syncthreads();
+      for (int j = tid; j < M; j += NTH) {
+        const uint32_t u = __float_as_uint(sig[j]);
+        if ((u & hmask) == prefix) atomicAdd(&hist[(u >> shift) & 255], 1u);
+      }
+      __syncthreads();
+      if (wave == 0) {
+        uint32_t hb[4], sum = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sum += (hb[i] = hist[4 * lane + i]);
+        uint32_t incl = sum;  // inclusive suffix sum over lanes >= lane
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+          const uint32_t o = __shfl_down(incl, off);
+          if (lane + off < 64) incl += o;
+        }
+        uint32_t acc = incl - sum;  // candidates whose digit lies in higher lanes' bins
+#pragma unroll
+        for (int i = 3; i >= 0; --i) {
+          if (acc < need && acc + hb[i] >= need) {
+            bc[0] = prefix | ((uint32_t)(4 * lane + i) << shift);
+            bc[1] = need - acc;
+          }
+          acc += hb[i];
+        }
+      }
+      __syncthreads();
+      prefix = bc[0];
+      need = bc[1];
+    }
+  }
+  uint32_t run_gt = 0, run_eq = 0;
+  for (int base = 0; base < M; base += NTH) {
+    const int j = base + tid;
+    const uint32_t u = j < M ? __float_as_uint(sig[j]) : 0u;
+    const bool gt = j < M && (all || u > prefix);
+    const bool eq = j < M && !all && u == prefix;
+    const uint64_t bg = __builtin_amdgcn_ballot_w64(gt), be = __builtin_amdgcn_ballot_w64(eq);
+    if (lane == 0) {
+      wc[0][wave] = (uint32_t)__builtin_popcountll(bg);
+      wc[1][wave] = (uint32_t)__builtin_popcountll(be);
+    }
+    __syncthreads();
+    uint32_t lg = run_gt, le = run_eq;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      if (w < wave) {
+        lg += wc[0][w];
+        le += wc[1][w];
+      }
+      run_gt += wc[0][w];
+      run_eq += wc[1][w];
+    }
+    lg += __builtin_amdgcn_mbcnt_hi((uint32_t)(bg >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bg, 0u));
+    le += __builtin_amdgcn_mbcnt_hi((uint32_t)(be >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)be, 0u));
+    if (gt || (eq && le < need)) out[lg + min(le, need)] = j;
+    __syncthreads();
+  }
+  for (int t = keff + tid; t < topk; t += NTH) out[t] = -1;
+}
+
 // One workgroup per (query block, head), longest blocks first; each wave owns a tile of 32
-// query rows, and the workgroup sweeps the block 32 * SEL_WAVES rows at a time.
+// query rows, and the workgroup sweeps the block 32 * SEL_WAVES rows at a time.  Per sweep,
+// pass 1 streams every pooled stage (online softmax: compressed output and lse) and pass 2
+// streams the key planes again (importance column sums).  The stages of all passes and
+// sweeps form one stream, double buffered: step k's copy is issued at step k - 1.
 template <int DT, int D>
 __global__ __launch_bounds__(64 * SEL_WAVES) void k_select(
     const typename Tr<DT>::T* __restrict__ q, const typename Tr<DT>::T* __restrict__ pooled,
@@ -205,90 +298,117 @@ __global__ __launch_bounds__(64 * SEL_WAVES) void k_select(
   __shared__ __attribute__((aligned(1024))) T stage1[C::STAGE];
   __shared__ float stage_sum[2][SEL_WAVES][64];
   __shared__ float lse_lds[ROWS];
-  __shared__ int32_t pick[256];
+  __shared__ uint32_t hist[256];
+  __shared__ uint32_t bcast[2];
+  __shared__ uint32_t wcnt[2][SEL_WAVES];
   extern __shared__ float sig[];  // [Mp]
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 5, c = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, c = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int h = blockIdx.x % H;
   const int b = lpt[blockIdx.x / H];
   const int r0 = blk_off[b], rows = blk_off[b + 1] - r0;
-  for (int j = tid; j < Mp; j += 64 * SEL_WAVES) sig[j] = 0.f;
   const int ntile = Mp / C::PT;
+  const int nsw = (rows + ROWS - 1) / ROWS;
+  const int nstep = nsw * 2 * ntile;
   const T* pstage = pooled + (int64_t)h * ntile * C::STAGE;
   constexpr int NCH1 = C::STAGE * sizeof(T) / 16, NCH2 = NS * C::KPLANE * sizeof(T) / 16;
+  auto issue = [&](int k, T* dst) {  // copy of step k's stage
+    const int pos = k % (2 * ntile);
+    const int t = pos < ntile ? pos : pos - ntile;
+    dma_contiguous<SEL_WAVES>(dst, pstage + (int64_t)t * C::STAGE, pos < ntile ? NCH1 : NCH2, wave, lane);
+  };
+  issue(0, stage0);
+  for (int j = tid; j < Mp; j += 64 * SEL_WAVES) sig[j] = 0.f;
 
-  for (int sw = 0; sw * ROWS < rows; ++sw) {
-    const int my_row = sw * ROWS + wave * 32 + c;
+  auto row_of = [&](int sw) { return sw * ROWS + wave * 32 + c; };
+  F qf[C::NKS];
+  {
+    const int my_row = row_of(0);
+    load_q<DT, D>(qf, q + ((int64_t)(my_row < rows ? perm[r0 + my_row] : 0) * H + h) * D, my_row < rows, lane);
+  }
+
+  auto fold = [&](int t) {  // sum the per-wave column sums of tile t into sigma (fixed order)
+    if (tid < C::PT) {
+      const int key = t * C::PT + tid;
+      float s = stage_sum[t & 1][0][tid];
+#pragma unroll
+      for (int w = 1; w < SEL_WAVES; ++w) s += stage_sum[t & 1][w][tid];
+      if (key < M) sig[key] += s;
+    }
+  };
+
+  int k = 0;  // step of the stage stream
+  for (int sw = 0; sw < nsw; ++sw) {
+    const int my_row = row_of(sw);
     const bool wave_active = sw * ROWS + wave * 32 < rows;
     const bool valid = my_row < rows;
-    F qf[C::NKS];
-    load_q<DT, D>(qf, q + ((int64_t)(valid ? perm[r0 + my_row] : 0) * H + h) * D, valid, lane);
 
     // ---------------- pass 1: online softmax over all pooled keys -> o_c, lse
-    // 64 pooled keys per stage: two independent 32-key score tiles per wave.
     Online<C::NDV> st;
     st.init();
-    {
-      auto p1 = [&](int t, T* cur, T* nxt) {
-        dma_wait();
-        __syncthreads();
-        if (t + 1 < ntile) dma_contiguous<SEL_WAVES>(nxt, pstage + (int64_t)(t + 1) * C::STAGE, NCH1, wave, lane);
-        if (wave_active) {
-          ssa_f16v a0, a1;
-          // value fragments read ahead for 16-bit types (fp32 ones would take 2*D registers)
-          constexpr bool VPRE = sizeof(T) == 2;
-          const T* vtt = cur + NS * C::KPLANE;
-          F vt[2][C::PK][C::NDV];
-          stage_scores<DT, D, true, VPRE>(cur + (lane & 31) * C::KROW + (lane >> 5) * C::KPL, qf, a0,
-                                          a1, vtt, vt, lane);
-          if (t == ntile - 1) {
+    auto p1 = [&](int t, T* cur, T* nxt) {
+      dma_wait();
+      __syncthreads();
+      if (k + (t & 1) + 1 < nstep) issue(k + (t & 1) + 1, nxt);
+      if (t == 0 && sw > 0) fold(ntile - 1);  // the previous sweep's last column sums
+      if (wave_active && t * C::PT < M) {
+        ssa_f16v a0, a1;
+        // value fragments read ahead for 16-bit types (fp32 ones would take 2*D registers)
+        constexpr bool VPRE = sizeof(T) == 2;
+        const T* vtt = cur + NS * C::KPLANE;
+        F vt[2][C::PK][C::NDV];
+        stage_scores<DT, D, true, VPRE>(cur + (lane & 31) * C::KROW + (lane >> 5) * C::KPL, qf, a0,
+                                        a1, vtt, vt, lane);
+        if ((t + 1) * C::PT > M) {  // padding blocks
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              if (t * C::PT + res_row(r, g) >= M) a0[r] = -INFINITY;
-              if (t * C::PT + 32 + res_row(r, g) >= M) a1[r] = -INFINITY;
-            }
+          for (int r = 0; r < 16; ++r) {
+            if (t * C::PT + res_row(r, g) >= M) a0[r] = -INFINITY;
+            if (t * C::PT + 32 + res_row(r, g) >= M) a1[r] = -INFINITY;
           }
-          st.update2(a0, a1, sl2);
+        }
+        st.update2(a0, a1, sl2);
 #pragma unroll
-          for (int ks = 0; ks < C::PK; ++ks) {
-            const F p0 = p_frag<DT>(a0, ks), p1f = p_frag<DT>(a1, ks);
+        for (int ks = 0; ks < C::PK; ++ks) {
+          const F p0 = p_frag<DT>(a0, ks), p1f = p_frag<DT>(a1, ks);
 #pragma unroll
-            for (int j = 0; j < C::NDV; ++j) {
-              if constexpr (VPRE) {
-                st.o[j] = Tr<DT>::mma(vt[0][ks][j], p0, st.o[j]);
-                st.o[j] = Tr<DT>::mma(vt[1][ks][j], p1f, st.o[j]);
-              } else {
-                st.o[j] = Tr<DT>::mma(vtt_frag<DT, D>(vtt, 0, ks, j, lane), p0, st.o[j]);
-                st.o[j] = Tr<DT>::mma(vtt_frag<DT, D>(vtt, 32, ks, j, lane), p1f, st.o[j]);
-              }
+          for (int j = 0; j < C::NDV; ++j) {
+            if constexpr (VPRE) {
+              st.o[j] = Tr<DT>::mma(vt[0][ks][j], p0, st.o[j]);
+              st.o[j] = Tr<DT>::mma(vt[1][ks][j], p1f, st.o[j]);
+            } else {
+              st.o[j] = Tr<DT>::mma(vtt_frag<DT, D>(vtt, 0, ks, j, lane), p0, st.o[j]);
+              st.o[j] = Tr<DT>::mma(vtt_frag<DT, D>(vtt, 32, ks, j, lane), p1f, st.o[j]);
             }
           }
         }
-      };
-      __syncthreads();  // the previous sweep is done with both stage buffers
-      dma_contiguous<SEL_WAVES>(stage0, pstage, NCH1, wave, lane);
-      for (int t = 0; t < ntile; t += 2) {
-        p1(t, stage0, stage1);
-        if (t + 1 < ntile) p1(t + 1, stage1, stage0);
       }
+    };
+    for (int t = 0; t < ntile; t += 2, k += 2) {  // ntile is even: every pass starts on stage0
+      p1(t, stage0, stage1);
+      p1(t + 1, stage1, stage0);
     }
-    {
+    {  // this sweep's compressed output and lse
       const float ltot = xor32_sum(st.l);
+      const float lse = st.m + fast_log2(ltot);
       if (wave_active && valid) {
         const float inv = 1.f / ltot;
         T* orow = oc + ((int64_t)(r0 + my_row) * H + h) * D;
-        if (lse_save && g == 0) lse_save[(int64_t)h * N + r0 + my_row] = st.m + fast_log2(ltot);
         float* srow = oc_save ? oc_save + ((int64_t)(r0 + my_row) * H + h) * D : nullptr;
+        if (lse_save && g == 0) lse_save[(int64_t)h * N + r0 + my_row] = lse;
 #pragma unroll
         for (int j = 0; j < C::NDV; ++j)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            orow[32 * j + res_row(r, g)] = Tr<DT>::cvt(st.o[j][r] * inv);
-            if (srow) srow[32 * j + res_row(r, g)] = st.o[j][r] * inv;
+          for (int rq = 0; rq < 4; ++rq) {
+            const int col = 32 * j + 8 * rq + 4 * g;
+            const float v0 = st.o[j][4 * rq] * inv, v1 = st.o[j][4 * rq + 1] * inv;
+            const float v2 = st.o[j][4 * rq + 2] * inv, v3 = st.o[j][4 * rq + 3] * inv;
+            store4(orow + col, v0, v1, v2, v3);
+            if (srow) store4(srow + col, v0, v1, v2, v3);
           }
       }
       // rows past the block get +inf, so their probabilities in pass 2 are exactly zero
-      if (g == 0) lse_lds[wave * 32 + c] = valid ? st.m + fast_log2(ltot) : INFINITY;
+      if (g == 0) lse_lds[wave * 32 + c] = valid ? lse : INFINITY;
     }
     __syncthreads();
 
@@ -296,78 +416,54 @@ __global__ __launch_bounds__(64 * SEL_WAVES) void k_select(
     float lrow[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) lrow[r] = lse_lds[wave * 32 + res_row(r, g)];
-    {
-      auto fold = [&](int t) {  // sum the per-wave column sums of tile t into sigma (fixed order)
-        if (tid < C::PT) {
-          const int key = t * C::PT + tid;
-          float s = stage_sum[t & 1][0][tid];
+    // next sweep's queries, loaded under pass 2 where the registers allow
+    constexpr bool QPRE = D * sizeof(T) <= 192;
+    F qn[C::NKS];
+    if (QPRE && sw + 1 < nsw) {
+      const int nrow = row_of(sw + 1);
+      load_q<DT, D>(qn, q + ((int64_t)(nrow < rows ? perm[r0 + nrow] : 0) * H + h) * D, nrow < rows, lane);
+    }
+    auto p2 = [&](int t, T* cur, T* nxt) {
+      dma_wait();
+      __syncthreads();
+      if (k + (t & 1) + 1 < nstep) issue(k + (t & 1) + 1, nxt);
+      if (t > 0) fold(t - 1);
+      float cs0 = 0.f, cs1 = 0.f;
+      if (wave_active && t * C::PT < M) {
+        ssa_f16v a0, a1;
+        stage_scores<DT, D, false, false>(cur + (lane & 31) * C::KROW + (lane >> 5) * C::KPL, qf,
+                                          a0, a1, nullptr, nullptr, lane);
 #pragma unroll
-          for (int w = 1; w < SEL_WAVES; ++w) s += stage_sum[t & 1][w][tid];
-          if (key < M) sig[key] += s;
+        for (int r = 0; r < 16; ++r) {
+          cs0 += fast_exp2(__builtin_fmaf(a0[r], sl2, -lrow[r]));
+          cs1 += fast_exp2(__builtin_fmaf(a1[r], sl2, -lrow[r]));
         }
-      };
-      auto p2 = [&](int t, T* cur, T* nxt) {
-        dma_wait();
-        __syncthreads();
-        if (t + 1 < ntile) dma_contiguous<SEL_WAVES>(nxt, pstage + (int64_t)(t + 1) * C::STAGE, NCH2, wave, lane);
-        if (t > 0) fold(t - 1);
-        float cs0 = 0.f, cs1 = 0.f;
-        if (wave_active) {
-          ssa_f16v a0, a1;
-          stage_scores<DT, D, false, false>(cur + (lane & 31) * C::KROW + (lane >> 5) * C::KPL, qf,
-                                            a0, a1, nullptr, nullptr, lane);
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            cs0 += fast_exp2(__builtin_fmaf(a0[r], sl2, -lrow[r]));
-            cs1 += fast_exp2(__builtin_fmaf(a1[r], sl2, -lrow[r]));
-          }
-          cs0 = xor32_sum(cs0);
-          cs1 = xor32_sum(cs1);
-        }
-        if (g == 0) {
-          stage_sum[t & 1][wave][c] = cs0;
-          stage_sum[t & 1][wave][32 + c] = cs1;
-        }
-      };
-      dma_contiguous<SEL_WAVES>(stage0, pstage, NCH2, wave, lane);
-      for (int t = 0; t < ntile; t += 2) {
-        p2(t, stage0, stage1);
-        if (t + 1 < ntile) p2(t + 1, stage1, stage0);
+        cs0 = xor32_sum(cs0);
+        cs1 = xor32_sum(cs1);
       }
-      __syncthreads();
-      fold(ntile - 1);
-      __syncthreads();
+      if (g == 0) {
+        stage_sum[t & 1][wave][c] = cs0;
+        stage_sum[t & 1][wave][32 + c] = cs1;
+      }
+    };
+    for (int t = 0; t < ntile; t += 2, k += 2) {
+      p2(t, stage0, stage1);
+      p2(t + 1, stage1, stage0);
+    }
+    if (sw + 1 < nsw) {
+      if constexpr (QPRE) {
+#pragma unroll
+        for (int i = 0; i < C::NKS; ++i) qf[i] = qn[i];
+      } else {
+        const int nrow = row_of(sw + 1);
+        load_q<DT, D>(qf, q + ((int64_t)(nrow < rows ? perm[r0 + nrow] : 0) * H + h) * D, nrow < rows, lane);
+      }
     }
   }
-
-  // ---------------- top-k (wave 0): repeated arg-max of (sigma bits, ~id) below the last pick
-  if (wave == 0) {
-    const int keff = min(topk, M);
-    uint64_t prev = ~0ull;
-    for (int it = 0; it < keff; ++it) {
-      uint64_t best = 0;
-      for (int j = lane; j < M; j += 64) {
-        const uint64_t key = ((uint64_t)__float_as_uint(sig[j]) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)j);
-        if (key < prev && key > best) best = key;
-      }
-#pragma unroll
-      for (int off = 32; off > 0; off >>= 1) {
-        const uint32_t lo = __shfl_xor((uint32_t)best, off), hi = __shfl_xor((uint32_t)(best >> 32), off);
-        const uint64_t o = ((uint64_t)hi << 32) | lo;
-        best = o > best ? o : best;
-      }
-      prev = best;
-      if (lane == 0) pick[it] = (int32_t)(0xFFFFFFFFu - (uint32_t)best);
-    }
-    if (lane == 0) {
-      for (int i = 1; i < keff; ++i) {
-        int x = pick[i], j = i - 1;
-        while (j >= 0 && pick[j] > x) { pick[j + 1] = pick[j]; --j; }
-        pick[j + 1] = x;
-      }
-    }
-    for (int t = lane; t < topk; t += 64) sel[((int64_t)h * M + b) * topk + t] = t < keff ? pick[t] : -1;
-  }
+  __syncthreads();
+  fold(ntile - 1);
+  __syncthreads();
+  topk_radix<SEL_WAVES>(sig, M, topk, sel + ((int64_t)h * M + b) * topk, hist, bcast, wcnt, tid);
 }
 
 // ------------------------------------------------------------------ selected + window + combine
@@ -582,7 +678,7 @@ template <int DT, int D>
 hipError_t run_pool(const ssa_plan_s* p, int H, const void* k, const void* v, const void* wk,
                     const void* wv, const FwdWs& w, hipStream_t s) {
   using T = typename Tr<DT>::T;
-  const int Mp = (int)round_up(p->M, POOL_TILE);
+  const int Mp = (int)pooled_rows(p->M);
   hipLaunchKernelGGL((k_pool<DT, D>), dim3(Mp, H), dim3(256), 0, s, (const T*)k, (const T*)v,
                      (const T*)wk, (const T*)wv, p->perm, p->blk_off, (int)p->M, Mp, H, (T*)w.pooled,
                      (T*)w.pooled_v);
@@ -593,7 +689,7 @@ template <int DT, int D>
 hipError_t run_select(const ssa_plan_s* p, int H, int topk, float sl2, const void* q,
                       const FwdWs& w, int32_t* sel, hipStream_t s) {
   using T = typename Tr<DT>::T;
-  const int Mp = (int)round_up(p->M, POOL_TILE);
+  const int Mp = (int)pooled_rows(p->M);
   const size_t shm = (size_t)Mp * sizeof(float);
   hipLaunchKernelGGL((k_select<DT, D>), dim3((unsigned)(p->M * H)), dim3(64 * SEL_WAVES), shm, s,
                      (const T*)q, (const T*)w.pooled, p->perm, p->blk_off, p->lpt, (int)p->M, Mp, H,
@@ -627,7 +723,7 @@ hipError_t pool_d(int d, const ssa_plan_s* p, int H, const void* k, const void* 
   return hipErrorInvalidValue;
 }
 
-// Most pooled blocks the selection kernel takes: its importance vector [round_up(M, 64)]
+// Most pooled blocks the selection kernel takes: its importance vector [pooled_rows(M)]
 // fp32 lives in LDS beside the kernel's static arrays, within the 160 KB of a workgroup.
 template <int DT, int D>
 int64_t select_limit() {
@@ -636,7 +732,7 @@ int64_t select_limit() {
     hipFuncAttributes a;
     if (hipFuncGetAttributes(&a, reinterpret_cast<const void*>(&k_select<DT, D>)) != hipSuccess) return 0;
     const int64_t room = (int64_t)LDS_BYTES - (int64_t)a.sharedSizeBytes;
-    lim = room <= 0 ? 0 : room / (int64_t)sizeof(float) / POOL_TILE * POOL_TILE;
+    lim = room <= 0 ? 0 : room / (int64_t)sizeof(float) / 128 * 128;  // pooled_rows(M) fits
   }
   return lim;
 }

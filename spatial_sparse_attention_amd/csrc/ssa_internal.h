@@ -52,6 +52,9 @@ static inline size_t esize_of(ssa_dtype dt) { return dt == SSA_F32 ? 4 : 2; }
 // layout, so a tile is one contiguous copy.  A row-major copy of the pooled values
 // ([H][Mp][vrow]) serves the backward.
 constexpr int POOL_TILE = 64;
+// Pooled blocks per head as stored: a whole, even number of 64-block stages, so that every
+// pass of the selection starts on the same stage buffer.
+static inline int64_t pooled_rows(int64_t M) { return ((M > 0 ? M : 1) + 127) / 128 * 128; }
 static inline int krow_of(ssa_dtype dt, int d) { return d + (dt == SSA_F32 ? 4 : 8); }
 static inline int vrow_of(ssa_dtype dt, int d) { return d + (dt == SSA_F32 ? 8 : 16); }
 static inline int vtrow_of(ssa_dtype dt) { return dt == SSA_F32 ? POOL_TILE + 1 : POOL_TILE + 4; }
