@@ -167,7 +167,7 @@ struct DqState {
   }
 };
 
-template <int DT, int D>
+template <int DT, int D, bool BUF>
 __global__ __launch_bounds__(64 * BW) void k_bwd_dq(
     const typename Tr<DT>::T* __restrict__ q, const typename Tr<DT>::T* __restrict__ kin,
     const typename Tr<DT>::T* __restrict__ vin, const typename Tr<DT>::T* __restrict__ gates,
@@ -223,13 +223,8 @@ __global__ __launch_bounds__(64 * BW) void k_bwd_dq(
     __syncthreads();
     const T* ksrc = pst + (int64_t)(t / 2) * C::STAGE + (t % 2) * KT * C::KROW;
     const T* vsrc = pvh + (int64_t)t * KT * C::VROW;
-    for (int i = wave; i * 64 < C::KCH + C::VCH; i += BW) {
-      const int p = i * 64 + lane;
-      if (p < C::KCH + C::VCH) {
-        const T* src = p < C::KCH ? ksrc + p * C::EPC : vsrc + (p - C::KCH) * C::EPC;
-        dma16(src, stage + i * 64 * C::EPC);
-      }
-    }
+    dma_contiguous<BW>(stage, ksrc, C::KCH, wave, lane);
+    dma_contiguous<BW>(stage + C::KTILE, vsrc, C::VCH, wave, lane);
     dma_wait();
     __syncthreads();
     S.tile(stage, min(KT, M - t * KT), sl2, lse[0], gx[0], Dx[0], lane);
@@ -247,7 +242,7 @@ __global__ __launch_bounds__(64 * BW) void k_bwd_dq(
       for (int k0 = 0; k0 < total; k0 += KT) {
         __syncthreads();
         ga.lookup(k0, total, L, pre, lst_off, perm);
-        ga.issue(stage, kin, vin, H, h, wave);
+        ga.template issue<BUF>(stage, kin, vin, H, h, wave);
         dma_wait();
         __syncthreads();
         S.tile(stage, min(KT, total - k0), sl2, lse[x], gx[x], Dx[x], lane);
@@ -349,7 +344,7 @@ __device__ inline void fill_info(float4* info, int k0, int total, int L, const i
   info[j] = v;
 }
 
-template <int DT, int D>
+template <int DT, int D, bool BUF>
 __global__ __launch_bounds__(64 * BW) void k_bwd_dkdv(
     const typename Tr<DT>::T* __restrict__ q, const typename Tr<DT>::T* __restrict__ kin,
     const typename Tr<DT>::T* __restrict__ vin, const typename Tr<DT>::T* __restrict__ gates,
@@ -400,7 +395,7 @@ __global__ __launch_bounds__(64 * BW) void k_bwd_dkdv(
       for (int k0 = 0; k0 < total; k0 += KT) {
         __syncthreads();
         ga.lookup(k0, total, L, pre, lst_off, perm);
-        ga.issue(stage, q, dout, H, h, wave);
+        ga.template issue<BUF>(stage, q, dout, H, h, wave);
         fill_info(info, k0, total, L, pre, lst_off, lse, Dx, gates, dt16, perm, H, h, x);
         dma_wait();
         __syncthreads();
@@ -426,7 +421,7 @@ __global__ __launch_bounds__(64 * BW) void k_bwd_dkdv(
 // ------------------------------------------------------------------ compressed key side
 // Wave w of a workgroup owns pooled key tile blockIdx-group*BW + w; the workgroup walks the
 // sorted query rows of its chunk.  Partials per chunk: part[qc][h][key][d].
-template <int DT, int D>
+template <int DT, int D, bool BUF>
 __global__ __launch_bounds__(64 * BW) void k_bwd_cmp(
     const typename Tr<DT>::T* __restrict__ q, const typename Tr<DT>::T* __restrict__ gates,
     const typename Tr<DT>::T* __restrict__ dout, const typename Tr<DT>::T* __restrict__ pooled,
@@ -471,7 +466,7 @@ __global__ __launch_bounds__(64 * BW) void k_bwd_cmp(
   for (int k0 = 0; k0 < total; k0 += KT) {
     __syncthreads();
     ga.lookup(k0, total, 1, pre, lst_off, perm);
-    ga.issue(stage, q, dout, H, h, wave);
+    ga.template issue<BUF>(stage, q, dout, H, h, wave);
     fill_info(info, k0, total, 1, pre, lst_off, lse, Dx, gates, dt16, perm, H, h, 0);
     dma_wait();
     __syncthreads();
@@ -544,7 +539,14 @@ hipError_t run_backward(const ssa_plan_s* p, int H, int topk, float scale, const
   const int nchunk = (p->max_rows + BROWS - 1) / BROWS;
   hipLaunchKernelGGL((k_bwd_prep<DT, D>), dim3((unsigned)((N * H + 255) / 256)), dim3(256), 0, s,
                      (const T*)dout, (const T*)gates, fw.obr, p->perm, N, H, dgates, w.D);
-  hipLaunchKernelGGL((k_bwd_dq<DT, D>), dim3((unsigned)(M * H * nchunk)), dim3(64 * BW), 0, s,
+  const bool buf = buffer_addressable(N * H * D * (int64_t)sizeof(T));
+  if (buf)
+    hipLaunchKernelGGL((k_bwd_dq<DT, D, true>), dim3((unsigned)(M * H * nchunk)), dim3(64 * BW), 0, s,
+                     (const T*)q, (const T*)k, (const T*)v, (const T*)gates, (const T*)dout,
+                     (const T*)fw.pooled, (const T*)fw.pooled_v, fw.lse, w.D, p->perm, p->blk_off, p->blk_cell,
+                     p->cell_off, p->cell_blk, p->lpt, sel, M, Mp, H, nchunk, N, topk, scale, sl2, dq);
+  else
+    hipLaunchKernelGGL((k_bwd_dq<DT, D, false>), dim3((unsigned)(M * H * nchunk)), dim3(64 * BW), 0, s,
                      (const T*)q, (const T*)k, (const T*)v, (const T*)gates, (const T*)dout,
                      (const T*)fw.pooled, (const T*)fw.pooled_v, fw.lse, w.D, p->perm, p->blk_off, p->blk_cell,
                      p->cell_off, p->cell_blk, p->lpt, sel, M, Mp, H, nchunk, N, topk, scale, sl2, dq);
@@ -559,12 +561,24 @@ hipError_t run_backward(const ssa_plan_s* p, int H, int topk, float scale, const
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_inv_off, dim3((unsigned)((H * M + 1 + 255) / 256)), dim3(256), 0, s, ka, E,
                      H * M, w.inv_off);
-  hipLaunchKernelGGL((k_bwd_dkdv<DT, D>), dim3((unsigned)(M * H * nchunk)), dim3(64 * BW), 0, s,
+  if (buf)
+    hipLaunchKernelGGL((k_bwd_dkdv<DT, D, true>), dim3((unsigned)(M * H * nchunk)), dim3(64 * BW), 0, s,
+                     (const T*)q, (const T*)k, (const T*)v, (const T*)gates, (const T*)dout, fw.lse,
+                     w.D, p->perm, p->blk_off, p->blk_cell, p->cell_off, p->cell_blk, p->lpt,
+                     w.inv_off, va, M, H, nchunk, N, scale, sl2, dk, dv);
+  else
+    hipLaunchKernelGGL((k_bwd_dkdv<DT, D, false>), dim3((unsigned)(M * H * nchunk)), dim3(64 * BW), 0, s,
                      (const T*)q, (const T*)k, (const T*)v, (const T*)gates, (const T*)dout, fw.lse,
                      w.D, p->perm, p->blk_off, p->blk_cell, p->cell_off, p->cell_blk, p->lpt,
                      w.inv_off, va, M, H, nchunk, N, scale, sl2, dk, dv);
   const int groups = (Mp / KT + BW - 1) / BW;
-  hipLaunchKernelGGL((k_bwd_cmp<DT, D>), dim3((unsigned)(groups * H * w.qch)), dim3(64 * BW), 0, s,
+  if (buf)
+    hipLaunchKernelGGL((k_bwd_cmp<DT, D, true>), dim3((unsigned)(groups * H * w.qch)), dim3(64 * BW), 0, s,
+                     (const T*)q, (const T*)gates, (const T*)dout, (const T*)fw.pooled,
+                     (const T*)fw.pooled_v, fw.lse, w.D,
+                     p->perm, Mp, H, w.qch, N, scale, sl2, w.part_k, w.part_v);
+  else
+    hipLaunchKernelGGL((k_bwd_cmp<DT, D, false>), dim3((unsigned)(groups * H * w.qch)), dim3(64 * BW), 0, s,
                      (const T*)q, (const T*)gates, (const T*)dout, (const T*)fw.pooled,
                      (const T*)fw.pooled_v, fw.lse, w.D,
                      p->perm, Mp, H, w.qch, N, scale, sl2, w.part_k, w.part_v);

@@ -31,9 +31,8 @@ namespace {
 
 using namespace ssa_dev;
 constexpr int SEL_WAVES = 8;      // compressed/select: waves per workgroup (256 rows per sweep)
-constexpr int ATT_RT = 2;         // selected/window: 32-row query tiles per wave
-constexpr int ATT_WAVES = 4;      //   and waves per workgroup (256 rows per chunk)
-constexpr int ATT_ROWS = 32 * ATT_RT * ATT_WAVES;
+constexpr int ATT_WAVES = 4;      // selected/window: waves per workgroup, 32 query rows each
+constexpr int ATT_ROWS = 32 * ATT_WAVES;
 
 // ------------------------------------------------------------------ pooling
 // grid (Mp, H).  ktil[h,b] = mean_{i in b} K[i,h] @ Wk ; same for V.  Writes the fp32
@@ -196,6 +195,21 @@ __device__ inline void store4(T* p, float a, float b, float c, float d) {
     typedef unsigned u2 __attribute__((ext_vector_type(2)));
     const T v[4] = {(T)a, (T)b, (T)c, (T)d};
     *reinterpret_cast<u2*>(p) = __builtin_bit_cast(u2, v);
+  }
+}
+
+// Loads 4 consecutive elements as floats (one 8- or 16-byte load).
+template <typename T>
+__device__ inline void load4(const T* p, float* v) {
+  if constexpr (sizeof(T) == 4) {
+    const float4 x = *reinterpret_cast<const float4*>(p);
+    v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
+  } else {
+    typedef unsigned u2 __attribute__((ext_vector_type(2)));
+    struct V4 { T e[4]; };
+    const V4 x = __builtin_bit_cast(V4, *reinterpret_cast<const u2*>(p));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = (float)x.e[i];
   }
 }
 
@@ -467,26 +481,96 @@ __global__ __launch_bounds__(64 * SEL_WAVES) void k_select(
 }
 
 // ------------------------------------------------------------------ selected + window + combine
+// Copies of one gathered 32-key tile (K rows [32][KROW], then V rows [32][VROW]) from the
+// caller's K and V into LDS, 16 bytes per lane and instruction.  Every wave issues the same
+// NI instructions per tile, so a wave can wait for all but its newest tile's copies with one
+// count.  Lanes on a row's padding chunk, or past the tile, copy a valid chunk into a spot
+// nobody reads (the row padding, or the buffer's tail).
+template <int DT, int D, int NW>
+struct TileCopy {
+  using C = Cfg<DT, D>;
+  using T = typename Tr<DT>::T;
+  static constexpr int KRC = C::KCH / KT, VRC = C::VCH / KT;  // chunks per padded row
+  static constexpr int NPOS = C::KCH + C::VCH;
+  static constexpr int NI = ((NPOS + 63) / 64 + NW - 1) / NW;
+  static constexpr int ELEMS = NI * NW * 64 * C::EPC;  // stage buffer, tail included
+  int32_t row[NI];   // tile row (key) of each copy
+  int32_t goff[NI];  // element offset inside the token's head row, bit 30 set for V
+  int32_t tok[NI];
+  __device__ inline void init(int wave, int lane) {
+#pragma unroll
+    for (int m = 0; m < NI; ++m) {
+      const int p = (wave + m * NW) * 64 + lane;
+      const bool isk = p < C::KCH;
+      const int q = isk ? p : p - C::KCH;
+      const int rr = isk ? q / KRC : q / VRC, ch = isk ? q % KRC : q % VRC;
+      const bool ok = p < NPOS && ch < C::CPR;
+      row[m] = p < NPOS ? rr : 0;
+      goff[m] = (ok ? ch * C::EPC : 0) + (isk || p >= NPOS ? 0 : (1 << 30));
+    }
+  }
+  // tokens of the tile starting at key k0 of a staged segment of n keys (rows past n: key 0)
+  __device__ inline void fetch(const int32_t* keytok, int k0, int n) {
+#pragma unroll
+    for (int m = 0; m < NI; ++m) {
+      const int j = k0 + row[m];
+      tok[m] = keytok[j < n ? j : 0];
+    }
+  }
+  template <bool BUF>
+  __device__ inline void issue(T* stage, const T* kin, const T* vin, int H, int h, int wave) const {
+    if constexpr (BUF) {
+      const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(kin + h * D), 0, -1, 0x00020000);
+      const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(vin + h * D), 0, -1, 0x00020000);
+#pragma unroll
+      for (int m = 0; m < NI; ++m) {
+        const uint32_t off = ((uint32_t)tok[m] * (uint32_t)(H * D) + (uint32_t)(goff[m] & ((1 << 30) - 1))) * (uint32_t)sizeof(T);
+        lds_void_t* dst = (lds_void_t*)(stage + (wave + m * NW) * 64 * C::EPC);
+        // one instruction per copy: the V flag selects the descriptor, not the instruction
+        const __amdgpu_buffer_rsrc_t rs = (goff[m] & (1 << 30)) ? rv : rk;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 16, off, 0, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int m = 0; m < NI; ++m) {
+        const bool isv = goff[m] & (1 << 30);
+        const T* src = (isv ? vin : kin) + ((int64_t)tok[m] * H + h) * D + (goff[m] & ((1 << 30) - 1));
+        dma16(src, stage + (wave + m * NW) * 64 * C::EPC);
+      }
+    }
+  }
+};
+
+// Waits until at most N of this wave's vector memory operations are outstanding.
+template <int N>
+__device__ inline void vm_wait() {
+  static_assert(N >= 0 && N < 16, "vmcnt immediate");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+}
+
 // A key set is a list of blocks (the selected blocks, or the blocks of the query's window
-// cell), concatenated in sorted token order and cut into 32-key tiles.  A stage holds the
-// tile's K rows ([32][KROW]) followed by its V rows ([32][VROW]), copied straight from the
-// caller's K and V through the token permutation.  Keys past the end of the set reuse the
-// set's first key (finite values; their scores are masked).
-template <int DT, int D>
+// cell), concatenated in sorted token order and cut into 32-key tiles.  The set is staged in
+// segments of up to KSEG keys: first the token of every key of the segment goes to LDS
+// (keytok), then the segment's tiles stream through three stage buffers, the copy of tile
+// t + 2 being issued while tile t is in use.  Keys past the end of a segment reuse its first
+// key (finite values; their scores are masked).
+constexpr int KSEG = 2048;
+template <int DT, int D, bool BUF>
 __device__ inline void gathered_branch(
-    Online<D / 32>* st, const Gather<DT, D, ATT_WAVES>& ga0, const int32_t* blist, int nlist,
-    const typename Tr<DT>::frag (*qf)[Cfg<DT, D>::NKS], const typename Tr<DT>::T* __restrict__ kin,
+    Online<D / 32>& st, const TileCopy<DT, D, ATT_WAVES>& tc0, const int32_t* blist, int nlist,
+    const typename Tr<DT>::frag* qf, const typename Tr<DT>::T* __restrict__ kin,
     const typename Tr<DT>::T* __restrict__ vin, const int32_t* __restrict__ perm,
     const int32_t* __restrict__ blk_off, int H, int h, float sl2, bool wave_active,
-    typename Tr<DT>::T* stage0, typename Tr<DT>::T* stage1, int32_t* pre, int32_t* lst_off) {
+    typename Tr<DT>::T* buf0, typename Tr<DT>::T* buf1, typename Tr<DT>::T* buf2, int32_t* pre,
+    int32_t* lst_off, int32_t* keytok) {
   using C = Cfg<DT, D>;
   using T = typename Tr<DT>::T;
   using F = typename Tr<DT>::frag;
+  using TC = TileCopy<DT, D, ATT_WAVES>;
   constexpr int NTH = 64 * ATT_WAVES;
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, wave = tid >> 6;
-#pragma unroll
-  for (int u = 0; u < ATT_RT; ++u) st[u].init();
-  Gather<DT, D, ATT_WAVES> ga = ga0;
+  st.init();
+  TC tc = tc0;
   for (int l0 = 0; l0 < nlist; l0 += NTH) {
     const int L = min(NTH, nlist - l0);
     __syncthreads();
@@ -508,57 +592,69 @@ __device__ inline void gathered_branch(
       }
     }
     const int total = pre[L];
-    const int ntile = (total + KT - 1) / KT;
-    auto step = [&](int t, T* cur, T* nxt) {
-      dma_wait();
-      __syncthreads();
-      VFrags<DT, D> vf;
-      if (wave_active) vf.read(cur + C::KTILE, lane);
-      if (t + 1 < ntile) ga.issue(nxt, kin, vin, H, h, wave);
-      if (t + 2 < ntile) ga.lookup((t + 2) * KT, total, L, pre, lst_off, perm);
-      if (wave_active) {
-        ssa_f16v acc[ATT_RT];
-#pragma unroll
-        for (int u = 0; u < ATT_RT; ++u) acc[u] = zero16();
-        const T* krow = cur + (lane & 31) * C::KROW + (lane >> 5) * C::KPL;
-#pragma unroll
-        for (int ks = 0; ks < C::NKS; ++ks) {
-          const F kf = load_frag<DT>(krow + ks * C::KS);
-#pragma unroll
-          for (int u = 0; u < ATT_RT; ++u) acc[u] = Tr<DT>::mma(kf, qf[u][ks], acc[u]);
+    for (int ks0 = 0; ks0 < total; ks0 += KSEG) {
+      const int n = min(KSEG, total - ks0);
+      __syncthreads();  // the previous segment's tiles have been read
+      for (int j = tid; j < n; j += NTH) {
+        const int key = ks0 + j;
+        int lo = 0, hi = L - 1;  // last list entry starting at or before the key
+        while (lo < hi) {
+          const int mid = (lo + hi + 1) >> 1;
+          if (pre[mid] <= key) lo = mid; else hi = mid - 1;
         }
+        keytok[j] = perm[lst_off[lo] + (key - pre[lo])];
+      }
+      __syncthreads();
+      const int ntile = (n + KT - 1) / KT;
+      auto step = [&](int t, T* cur, T* nx2) {
+        if (t + 1 < ntile) vm_wait<TC::NI>();  // tile t landed; tile t + 1 may be in flight
+        else vm_wait<0>();
+        __syncthreads();
+        ssa_f16v acc = zero16();
+        if (wave_active) {
+          const T* krow = cur + (lane & 31) * C::KROW + (lane >> 5) * C::KPL;
 #pragma unroll
-        for (int u = 0; u < ATT_RT; ++u) {
+          for (int ks = 0; ks < C::NKS; ++ks) acc = Tr<DT>::mma(load_frag<DT>(krow + ks * C::KS), qf[ks], acc);
           if (t == ntile - 1) {
 #pragma unroll
             for (int r = 0; r < 16; ++r)
-              if (t * KT + res_row(r, g) >= total) acc[u][r] = -INFINITY;
+              if (t * KT + res_row(r, g) >= n) acc[r] = -INFINITY;
           }
-          st[u].update(acc[u], sl2);
+          st.update(acc, sl2);
         }
+        // the value fragments are read before tile t + 2's copy is issued: the transpose
+        // reads carry no alias information, so reading after it would wait for that copy
+        VFrags<DT, D> vf;
+        if (wave_active) vf.read(cur + C::KTILE, lane);
+        if (t + 2 < ntile) tc.template issue<BUF>(nx2, kin, vin, H, h, wave);
+        if (t + 3 < ntile) tc.fetch(keytok, (t + 3) * KT, n);
+        if (wave_active) {
 #pragma unroll
-        for (int ks = 0; ks < C::PK; ++ks)
+          for (int ks = 0; ks < C::PK; ++ks) {
+            const F pf = p_frag<DT>(acc, ks);
 #pragma unroll
-          for (int u = 0; u < ATT_RT; ++u) {
-            const F pf = p_frag<DT>(acc[u], ks);
-#pragma unroll
-            for (int j = 0; j < C::NDV; ++j) st[u].o[j] = Tr<DT>::mma(vf.f[ks][j], pf, st[u].o[j]);
+            for (int j = 0; j < C::NDV; ++j) st.o[j] = Tr<DT>::mma(vf.f[ks][j], pf, st.o[j]);
           }
+        }
+      };
+      tc.fetch(keytok, 0, n);
+      tc.template issue<BUF>(buf0, kin, vin, H, h, wave);
+      if (ntile > 1) {
+        tc.fetch(keytok, KT, n);
+        tc.template issue<BUF>(buf1, kin, vin, H, h, wave);
       }
-    };
-    ga.lookup(0, total, L, pre, lst_off, perm);
-    ga.issue(stage0, kin, vin, H, h, wave);
-    if (ntile > 1) ga.lookup(KT, total, L, pre, lst_off, perm);
-    for (int t = 0; t < ntile; t += 2) {
-      step(t, stage0, stage1);
-      if (t + 1 < ntile) step(t + 1, stage1, stage0);
+      if (ntile > 2) tc.fetch(keytok, 2 * KT, n);
+      for (int t = 0; t < ntile; t += 3) {
+        step(t, buf0, buf2);
+        if (t + 1 < ntile) step(t + 1, buf1, buf0);
+        if (t + 2 < ntile) step(t + 2, buf2, buf1);
+      }
     }
-    dma_wait();
   }
 }
 
 // One workgroup per (ATT_ROWS-row chunk of a query block, head); grid = lpt rank x chunk x head.
-template <int DT, int D>
+template <int DT, int D, bool BUF>
 __global__ __launch_bounds__(64 * ATT_WAVES) __attribute__((amdgpu_waves_per_eu(2))) void k_attend(
     const typename Tr<DT>::T* __restrict__ q, const typename Tr<DT>::T* __restrict__ kin,
     const typename Tr<DT>::T* __restrict__ vin, const typename Tr<DT>::T* __restrict__ gates,
@@ -571,18 +667,15 @@ __global__ __launch_bounds__(64 * ATT_WAVES) __attribute__((amdgpu_waves_per_eu(
   using C = Cfg<DT, D>;
   using T = typename Tr<DT>::T;
   using F = typename Tr<DT>::frag;
+  using TC = TileCopy<DT, D, ATT_WAVES>;
   constexpr int NTH = 64 * ATT_WAVES;
-  __shared__ __attribute__((aligned(1024))) T stage0[C::KTILE + C::VTILE];
-  __shared__ __attribute__((aligned(1024))) T stage1[C::KTILE + C::VTILE];
+  __shared__ __attribute__((aligned(1024))) T buf0[TC::ELEMS];
+  __shared__ __attribute__((aligned(1024))) T buf1[TC::ELEMS];
+  __shared__ __attribute__((aligned(1024))) T buf2[TC::ELEMS];
   __shared__ int32_t pre[NTH + 1];
   __shared__ int32_t lst_off[NTH];
   __shared__ int32_t sel_lds[256];
-  // the selected branch's weighted output, parked in LDS as fp16 while the window branch
-  // runs (16-bit dtypes: the rounding is far below the output dtype's); fp32 keeps it in
-  // registers
-  constexpr bool PARK = DT != DT_F32;
-  __shared__ _Float16 res_lds[PARK ? ATT_WAVES : 1][PARK ? ATT_RT * C::NDV * 16 : 1][64];
-  ssa_f16v res[PARK ? 1 : ATT_RT][PARK ? 1 : C::NDV];
+  __shared__ int32_t keytok[KSEG];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 5, c = lane & 31;
   const int h = blockIdx.x % H;
@@ -597,79 +690,70 @@ __global__ __launch_bounds__(64 * ATT_WAVES) __attribute__((amdgpu_waves_per_eu(
   const int cell = blk_cell[b];
   const int c0 = cell_off[cell], c1 = cell_off[cell + 1];
 
-  const int wbase = chunk * ATT_ROWS + wave * 32 * ATT_RT;
+  const int wbase = chunk * ATT_ROWS + wave * 32;
   const bool wave_active = wbase < rows;
-  F qf[ATT_RT][C::NKS];
-  int64_t tok_q[ATT_RT];
-  bool valid[ATT_RT];
-#pragma unroll
-  for (int u = 0; u < ATT_RT; ++u) {
-    const int my_row = wbase + 32 * u + c;
-    valid[u] = my_row < rows;
-    tok_q[u] = valid[u] ? perm[r0 + my_row] : 0;
-    load_q<DT, D>(qf[u], q + (tok_q[u] * H + h) * D, valid[u], lane);
-  }
-  Gather<DT, D, ATT_WAVES> ga;
-  ga.init(wave, lane);
+  const int my_row = wbase + c;
+  const bool valid = my_row < rows;
+  const int64_t tok_q = valid ? perm[r0 + my_row] : 0;
+  F qf[C::NKS];
+  load_q<DT, D>(qf, q + (tok_q * H + h) * D, valid, lane);
+  TC tc;
+  tc.init(wave, lane);
 
-  Online<C::NDV> st[ATT_RT];
-  gathered_branch<DT, D>(st, ga, sel_lds, nsel, qf, kin, vin, perm, blk_off, H, h, sl2, wave_active,
-                         stage0, stage1, pre, lst_off);
-#pragma unroll
-  for (int u = 0; u < ATT_RT; ++u) {
-    const float g1 = valid[u] ? Tr<DT>::up(gates[(tok_q[u] * H + h) * 3 + 1]) : 0.f;
-    const float ls = xor32_sum(st[u].l);
+  Online<C::NDV> st;
+  gathered_branch<DT, D, BUF>(st, tc, sel_lds, nsel, qf, kin, vin, perm, blk_off, H, h, sl2,
+                              wave_active, buf0, buf1, buf2, pre, lst_off, keytok);
+  ssa_f16v res[C::NDV];  // the selected branch's gated output
+  {
+    const float g1 = valid ? Tr<DT>::up(gates[(tok_q * H + h) * 3 + 1]) : 0.f;
+    const float ls = xor32_sum(st.l);
     const float f = g1 / ls;
-    if (lse_save && wave_active && valid[u]) {
-      const int64_t row = r0 + wbase + 32 * u + c;
-      if (g == 0) lse_save[(int64_t)(H + h) * N + row] = st[u].m + fast_log2(ls);
-      float* srow = os_save + (row * H + h) * D;
+    if (lse_save && wave_active && valid) {
+      const int64_t row = r0 + my_row;
+      if (g == 0) lse_save[(int64_t)(H + h) * N + row] = st.m + fast_log2(ls);
+      float* srow2 = os_save + (row * H + h) * D;
+      const float inv = 1.f / ls;
 #pragma unroll
       for (int j = 0; j < C::NDV; ++j)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) srow[32 * j + res_row(r, g)] = st[u].o[j][r] / ls;
+        for (int rq = 0; rq < 4; ++rq)
+          store4(srow2 + 32 * j + 8 * rq + 4 * g, st.o[j][4 * rq] * inv, st.o[j][4 * rq + 1] * inv,
+                 st.o[j][4 * rq + 2] * inv, st.o[j][4 * rq + 3] * inv);
     }
 #pragma unroll
-    for (int j = 0; j < C::NDV; ++j) {
-      if constexpr (PARK) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) res_lds[wave][(u * C::NDV + j) * 16 + r][lane] = (_Float16)(st[u].o[j][r] * f);
-      } else {
-        res[u][j] = st[u].o[j] * f;
-      }
-    }
+    for (int j = 0; j < C::NDV; ++j) res[j] = st.o[j] * f;
   }
-  gathered_branch<DT, D>(st, ga, cell_blk + c0, c1 - c0, qf, kin, vin, perm, blk_off, H, h, sl2,
-                         wave_active, stage0, stage1, pre, lst_off);
-#pragma unroll
-  for (int u = 0; u < ATT_RT; ++u) {
-    const float ltot = xor32_sum(st[u].l);
-    const int my_row = wbase + 32 * u + c;
-    if (wave_active && valid[u]) {
-      const float g0 = Tr<DT>::up(gates[(tok_q[u] * H + h) * 3 + 0]);
-      const float g2 = Tr<DT>::up(gates[(tok_q[u] * H + h) * 3 + 2]);
-      const float f = g2 / ltot;
-      const T* orow = oc + ((int64_t)(r0 + my_row) * H + h) * D;
-      T* dst = out + (tok_q[u] * H + h) * D;
-      if (lse_save) {
-        if (g == 0) lse_save[(int64_t)(2 * H + h) * N + r0 + my_row] = st[u].m + fast_log2(ltot);
-        float* wrow = ow_save + ((int64_t)(r0 + my_row) * H + h) * D;
-#pragma unroll
-        for (int j = 0; j < C::NDV; ++j)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) wrow[32 * j + res_row(r, g)] = st[u].o[j][r] / ltot;
-      }
+  gathered_branch<DT, D, BUF>(st, tc, cell_blk + c0, c1 - c0, qf, kin, vin, perm, blk_off, H, h, sl2,
+                              wave_active, buf0, buf1, buf2, pre, lst_off, keytok);
+  if (wave_active && valid) {
+    const float ltot = xor32_sum(st.l);
+    const float g0 = Tr<DT>::up(gates[(tok_q * H + h) * 3 + 0]);
+    const float g2 = Tr<DT>::up(gates[(tok_q * H + h) * 3 + 2]);
+    const float f = g2 / ltot;
+    const T* orow = oc + ((int64_t)(r0 + my_row) * H + h) * D;
+    T* dst = out + (tok_q * H + h) * D;
+    if (lse_save) {
+      if (g == 0) lse_save[(int64_t)(2 * H + h) * N + r0 + my_row] = st.m + fast_log2(ltot);
+      float* wrow = ow_save + ((int64_t)(r0 + my_row) * H + h) * D;
+      const float inv = 1.f / ltot;
 #pragma unroll
       for (int j = 0; j < C::NDV; ++j)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int dv = 32 * j + res_row(r, g);
-          float rs;
-          if constexpr (PARK) rs = (float)res_lds[wave][(u * C::NDV + j) * 16 + r][lane];
-          else rs = res[u][j][r];
-          dst[dv] = Tr<DT>::cvt(rs + f * st[u].o[j][r] + g0 * Tr<DT>::up(orow[dv]));
-        }
+        for (int rq = 0; rq < 4; ++rq)
+          store4(wrow + 32 * j + 8 * rq + 4 * g, st.o[j][4 * rq] * inv, st.o[j][4 * rq + 1] * inv,
+                 st.o[j][4 * rq + 2] * inv, st.o[j][4 * rq + 3] * inv);
     }
+#pragma unroll
+    for (int j = 0; j < C::NDV; ++j)
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq) {
+        const int col = 32 * j + 8 * rq + 4 * g;
+        float v[4];
+        load4(orow + col, v);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = res[j][4 * rq + e] + f * st.o[j][4 * rq + e] + g0 * v[e];
+        store4(dst + col, v[0], v[1], v[2], v[3]);
+      }
   }
 }
 
@@ -703,7 +787,14 @@ hipError_t run_attend(const ssa_plan_s* p, int H, int topk, float sl2, const voi
                       const int32_t* sel, void* out, hipStream_t s) {
   using T = typename Tr<DT>::T;
   const int nchunk = (p->max_rows + ATT_ROWS - 1) / ATT_ROWS;
-  hipLaunchKernelGGL((k_attend<DT, D>), dim3((unsigned)(p->M * H * nchunk)), dim3(64 * ATT_WAVES), 0,
+  if (buffer_addressable(p->n * H * D * (int64_t)sizeof(T)))
+    hipLaunchKernelGGL((k_attend<DT, D, true>), dim3((unsigned)(p->M * H * nchunk)), dim3(64 * ATT_WAVES), 0,
+                     s, (const T*)q, (const T*)k, (const T*)v, (const T*)gates, p->perm, p->blk_off,
+                     p->blk_cell, p->cell_off, p->cell_blk, p->lpt, sel, (const T*)w.oc, (int)p->M,
+                     H, nchunk, p->n, topk, sl2, (T*)out, w.lse,
+                     w.obr ? w.obr + p->n * H * D : nullptr, w.obr ? w.obr + 2 * p->n * H * D : nullptr);
+  else
+    hipLaunchKernelGGL((k_attend<DT, D, false>), dim3((unsigned)(p->M * H * nchunk)), dim3(64 * ATT_WAVES), 0,
                      s, (const T*)q, (const T*)k, (const T*)v, (const T*)gates, p->perm, p->blk_off,
                      p->blk_cell, p->cell_off, p->cell_blk, p->lpt, sel, (const T*)w.oc, (int)p->M,
                      H, nchunk, p->n, topk, sl2, (T*)out, w.lse,

@@ -52,6 +52,8 @@ static inline size_t esize_of(ssa_dtype dt) { return dt == SSA_F32 ? 4 : 2; }
 // layout, so a tile is one contiguous copy.  A row-major copy of the pooled values
 // ([H][Mp][vrow]) serves the backward.
 constexpr int POOL_TILE = 64;
+// Gathers from a token tensor use 32-bit byte offsets (buffer loads) when it is below 4 GiB.
+static inline bool buffer_addressable(int64_t bytes) { return bytes <= (int64_t)0xFFFFFFF0; }
 // Pooled blocks per head as stored: a whole, even number of 64-block stages, so that every
 // pass of the selection starts on the same stage buffer.
 static inline int64_t pooled_rows(int64_t M) { return ((M > 0 ? M : 1) + 127) / 128 * 128; }

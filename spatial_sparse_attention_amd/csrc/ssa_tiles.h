@@ -302,6 +302,15 @@ struct Gather {
       goff[m] = ch * C::EPC + (isk ? 0 : (1 << 30));
     }
   }
+  // tokens of this lane's copies for the tile starting at key k0 of a staged key segment
+  // (keytok: token of each of the segment's n keys, in LDS); rows past n take key 0
+  __device__ inline void fetch(const int32_t* keytok, int k0, int n) {
+#pragma unroll
+    for (int m = 0; m < NI; ++m) {
+      const int j = k0 + (row[m] < 0 ? 0 : row[m]);
+      tok[m] = keytok[j < n ? j : 0];
+    }
+  }
   // tokens of this lane's copies for the tile starting at key k0
   __device__ inline void lookup(int k0, int total, int L, const int32_t* pre, const int32_t* lst_off,
                                 const int32_t* __restrict__ perm) {
@@ -317,14 +326,34 @@ struct Gather {
       tok[m] = perm[lst_off[lo] + (j - pre[lo])];
     }
   }
+  // BUF: buffer loads to LDS with 32-bit offsets from each tensor's head-h row (tensors
+  // below 4 GiB); else global loads to LDS.  The buffer form keeps the compiler's LDS read
+  // counting exact (with the global form it waits for every LDS read at once).
+  template <bool BUF>
   __device__ inline void issue(typename Tr<DT>::T* stage, const typename Tr<DT>::T* kin,
                                const typename Tr<DT>::T* vin, int H, int h, int wave) const {
+    using T = typename Tr<DT>::T;
+    if constexpr (BUF) {
+      const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(kin + h * D), 0, -1, 0x00020000);
+      const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(vin + h * D), 0, -1, 0x00020000);
 #pragma unroll
-    for (int m = 0; m < NI; ++m) {
-      if (row[m] >= 0) {
-        const bool isv = goff[m] & (1 << 30);
-        const typename Tr<DT>::T* src = (isv ? vin : kin) + ((int64_t)tok[m] * H + h) * D + (goff[m] & ((1 << 30) - 1));
-        dma16(src, stage + (wave + m * NW) * 64 * C::EPC);
+      for (int m = 0; m < NI; ++m) {
+        if (row[m] >= 0) {
+          const bool isv = goff[m] & (1 << 30);
+          const uint32_t off = ((uint32_t)tok[m] * (uint32_t)(H * D) + (uint32_t)(goff[m] & ((1 << 30) - 1))) * (uint32_t)sizeof(T);
+          lds_void_t* dst = (lds_void_t*)(stage + (wave + m * NW) * 64 * C::EPC);
+          if (isv) __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, dst, 16, off, 0, 0, 0);
+          else __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, dst, 16, off, 0, 0, 0);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int m = 0; m < NI; ++m) {
+        if (row[m] >= 0) {
+          const bool isv = goff[m] & (1 << 30);
+          const T* src = (isv ? vin : kin) + ((int64_t)tok[m] * H + h) * D + (goff[m] & ((1 << 30) - 1));
+          dma16(src, stage + (wave + m * NW) * 64 * C::EPC);
+        }
       }
     }
   }
