@@ -10,7 +10,7 @@ A step is one pass of the whole path over resident inputs: the block partition
 + selection, selected/window branches + gated combine).  HIP events on the launch
 stream time every stage of every step.  The CPU baseline is the float64 oracle
 timed on a bounded sample of the same workload on the host.
-Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu]
+Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu] [--no-bwd] [--copy-probe]
 """
 import argparse
 import json
@@ -67,15 +67,56 @@ def cpu_baseline(inp, heads_sample):
                       f"{heads_sample} of {H} heads ({dt:.1f} s); tokens/s scaled by the head fraction"}
 
 
+def backward_timing(ssa, plan, dev, wl, torch, stream, reps=5):
+    """Forward with saved state, then the backward (fixed selection, seeded dout), timed
+    apart from the step: HIP events around `reps` backward calls."""
+    q = dev["q"]
+    N, H, d = q.shape
+    gen = torch.Generator(device="cuda").manual_seed(5)
+    dout = torch.randn(q.shape, generator=gen, device="cuda", dtype=torch.float32).to(q.dtype)
+    fws = torch.empty(ssa.forward_workspace_size(plan, q.dtype, H, d, wl.topk, save_for_bwd=True),
+                      dtype=torch.uint8, device="cuda")
+    sel = torch.empty((H, plan.num_blocks, wl.topk), dtype=torch.int32, device="cuda")
+    ssa.forward(plan, q, dev["k"], dev["v"], dev["wk"], dev["wv"], dev["gates"], wl.topk, 0.0,
+                sel_out=sel, ws=fws, save_for_bwd=True)
+    bws = torch.empty(ssa.backward_workspace_size(plan, q.dtype, H, d, wl.topk), dtype=torch.uint8,
+                      device="cuda")
+    run = lambda: ssa.backward(plan, q, dev["k"], dev["v"], dev["wk"], dev["wv"], dev["gates"],
+                               wl.topk, sel, dout, fws, ws=bws)
+    run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        run()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return {"ms": e0.elapsed_time(e1) / reps, "reps": reps,
+            "what": "dQ, dK, dV, dgates with the forward's selection held fixed (fp32 outputs)"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--cpu-heads", type=int, default=4)
+    ap.add_argument("--cpu-heads", type=int, default=22,
+                    help="heads of the workload the CPU oracle runs (all 22: about 15 s)")
+    ap.add_argument("--no-bwd", action="store_true", help="skip the backward timing")
     ap.add_argument("--workload", default=WORKLOAD)
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only run a plain 1 GiB device copy 3 times (HBM counter calibration)")
     args = ap.parse_args()
+    if args.copy_probe:
+        import torch
+        x = torch.ones(1 << 28, dtype=torch.float32, device="cuda")   # 1 GiB
+        y = torch.empty_like(x)
+        for _ in range(3):
+            y.copy_(x)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": x.numel() * 4, "launches": 3}))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: SSA shards by head with no exchange, and this "
               "build runs and reports the single-GPU path (use --gpus 1).", file=sys.stderr)
@@ -168,6 +209,8 @@ def main():
                      "frac": sel_tflops / peak, "traffic": None,
                      "work_per_launch_flops": cmp_flops},
     }
+    if not args.no_bwd:
+        res["backward"] = backward_timing(ssa, plan, dev, wl, torch, stream)
     if not args.no_cpu:
         res["cpu_baseline"] = cpu_baseline(inp, min(args.cpu_heads, H))
     print(json.dumps(res))
