@@ -186,9 +186,11 @@ __global__ __launch_bounds__(64 * BW) void k_bwd_dq(
   __shared__ int32_t lst_off[NTH];
   __shared__ int32_t sel_lds[256];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 5, c = lane & 31;
-  const int h = blockIdx.x % H;
-  const int chunk = (blockIdx.x / H) % nchunk;
-  const int b = lpt[blockIdx.x / (H * nchunk)];
+  int unit, member;
+  xcd_split(blockIdx.x, nchunk * H, unit, member);
+  if (unit >= M) return;
+  const int h = member % H, chunk = member / H;
+  const int b = lpt[unit];
   const int r0 = blk_off[b], rows = blk_off[b + 1] - r0;
   if (chunk * BROWS >= rows) return;
   int nsel = 0;
@@ -363,9 +365,11 @@ __global__ __launch_bounds__(64 * BW) void k_bwd_dkdv(
   __shared__ int32_t pre[NTH + 1];
   __shared__ int32_t lst_off[NTH];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 5, c = lane & 31;
-  const int h = blockIdx.x % H;
-  const int chunk = (blockIdx.x / H) % nchunk;
-  const int b = lpt[blockIdx.x / (H * nchunk)];
+  int unit, member;
+  xcd_split(blockIdx.x, nchunk * H, unit, member);
+  if (unit >= M) return;
+  const int h = member % H, chunk = member / H;
+  const int b = lpt[unit];
   const int r0 = blk_off[b], rows = blk_off[b + 1] - r0;
   if (chunk * BROWS >= rows) return;
   const int kbase = chunk * BROWS + wave * 32;
@@ -541,12 +545,12 @@ hipError_t run_backward(const ssa_plan_s* p, int H, int topk, float scale, const
                      (const T*)dout, (const T*)gates, fw.obr, p->perm, N, H, dgates, w.D);
   const bool buf = buffer_addressable(N * H * D * (int64_t)sizeof(T));
   if (buf)
-    hipLaunchKernelGGL((k_bwd_dq<DT, D, true>), dim3((unsigned)(M * H * nchunk)), dim3(64 * BW), 0, s,
+    hipLaunchKernelGGL((k_bwd_dq<DT, D, true>), dim3(xcd_grid(M, (int64_t)H * nchunk)), dim3(64 * BW), 0, s,
                      (const T*)q, (const T*)k, (const T*)v, (const T*)gates, (const T*)dout,
                      (const T*)fw.pooled, (const T*)fw.pooled_v, fw.lse, w.D, p->perm, p->blk_off, p->blk_cell,
                      p->cell_off, p->cell_blk, p->lpt, sel, M, Mp, H, nchunk, N, topk, scale, sl2, dq);
   else
-    hipLaunchKernelGGL((k_bwd_dq<DT, D, false>), dim3((unsigned)(M * H * nchunk)), dim3(64 * BW), 0, s,
+    hipLaunchKernelGGL((k_bwd_dq<DT, D, false>), dim3(xcd_grid(M, (int64_t)H * nchunk)), dim3(64 * BW), 0, s,
                      (const T*)q, (const T*)k, (const T*)v, (const T*)gates, (const T*)dout,
                      (const T*)fw.pooled, (const T*)fw.pooled_v, fw.lse, w.D, p->perm, p->blk_off, p->blk_cell,
                      p->cell_off, p->cell_blk, p->lpt, sel, M, Mp, H, nchunk, N, topk, scale, sl2, dq);
@@ -562,12 +566,12 @@ hipError_t run_backward(const ssa_plan_s* p, int H, int topk, float scale, const
   hipLaunchKernelGGL(k_inv_off, dim3((unsigned)((H * M + 1 + 255) / 256)), dim3(256), 0, s, ka, E,
                      H * M, w.inv_off);
   if (buf)
-    hipLaunchKernelGGL((k_bwd_dkdv<DT, D, true>), dim3((unsigned)(M * H * nchunk)), dim3(64 * BW), 0, s,
+    hipLaunchKernelGGL((k_bwd_dkdv<DT, D, true>), dim3(xcd_grid(M, (int64_t)H * nchunk)), dim3(64 * BW), 0, s,
                      (const T*)q, (const T*)k, (const T*)v, (const T*)gates, (const T*)dout, fw.lse,
                      w.D, p->perm, p->blk_off, p->blk_cell, p->cell_off, p->cell_blk, p->lpt,
                      w.inv_off, va, M, H, nchunk, N, scale, sl2, dk, dv);
   else
-    hipLaunchKernelGGL((k_bwd_dkdv<DT, D, false>), dim3((unsigned)(M * H * nchunk)), dim3(64 * BW), 0, s,
+    hipLaunchKernelGGL((k_bwd_dkdv<DT, D, false>), dim3(xcd_grid(M, (int64_t)H * nchunk)), dim3(64 * BW), 0, s,
                      (const T*)q, (const T*)k, (const T*)v, (const T*)gates, (const T*)dout, fw.lse,
                      w.D, p->perm, p->blk_off, p->blk_cell, p->cell_off, p->cell_blk, p->lpt,
                      w.inv_off, va, M, H, nchunk, N, scale, sl2, dk, dv);

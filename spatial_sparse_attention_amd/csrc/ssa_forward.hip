@@ -35,7 +35,7 @@ constexpr int ATT_WAVES = 4;      // selected/window: waves per workgroup, 32 qu
 constexpr int ATT_ROWS = 32 * ATT_WAVES;
 
 // ------------------------------------------------------------------ pooling
-// grid (Mp, H).  ktil[h,b] = mean_{i in b} K[i,h] @ Wk ; same for V.  Writes the fp32
+// One workgroup per (block, head).  ktil[h,b] = mean_{i in b} K[i,h] @ Wk ; same for V.  Writes the fp32
 // pooled key split into NSPLIT dtype planes and the pooled value (transposed) in the
 // per-(head, 64-block tile) stage layout, plus the row-major pooled value; padding
 // blocks (b >= M) and key-row padding are zero.
@@ -50,7 +50,10 @@ __global__ __launch_bounds__(256) void k_pool(
   constexpr int NS = C::NS, VEC = C::EPC, CH = C::CPR, RSUB = 256 / CH;
   constexpr int U = 4;  // rows in flight per thread
   __shared__ float redk[RSUB * D], redv[RSUB * D], kbar[D], vbar[D];
-  const int b = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+  int b, h;
+  xcd_split(blockIdx.x, H, b, h);  // a block's heads share the rows' cache lines
+  if (b >= Mp) return;
+  const int tid = threadIdx.x;
   T* stg = pooled + ((int64_t)h * (Mp / C::PT) + b / C::PT) * C::STAGE;
   T* krow = stg + (b % C::PT) * C::KROW;          // plane s at + s * KPLANE
   T* vtcol = stg + NS * C::KPLANE + (b % C::PT);  // column dv at + dv * VTROW
@@ -319,8 +322,10 @@ __global__ __launch_bounds__(64 * SEL_WAVES) void k_select(
 
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, c = lane & 31;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int h = blockIdx.x % H;
-  const int b = lpt[blockIdx.x / H];
+  int unit, h;
+  xcd_split(blockIdx.x, H, unit, h);
+  if (unit >= M) return;
+  const int b = lpt[unit];
   const int r0 = blk_off[b], rows = blk_off[b + 1] - r0;
   const int ntile = Mp / C::PT;
   const int nsw = (rows + ROWS - 1) / ROWS;
@@ -653,7 +658,8 @@ __device__ inline void gathered_branch(
   }
 }
 
-// One workgroup per (ATT_ROWS-row chunk of a query block, head); grid = lpt rank x chunk x head.
+// One workgroup per (ATT_ROWS-row chunk of a query block, head); a block's chunks and heads
+// form one XCD unit (they gather the same key rows), blocks in longest-first order.
 template <int DT, int D, bool BUF>
 __global__ __launch_bounds__(64 * ATT_WAVES) __attribute__((amdgpu_waves_per_eu(2))) void k_attend(
     const typename Tr<DT>::T* __restrict__ q, const typename Tr<DT>::T* __restrict__ kin,
@@ -678,9 +684,11 @@ __global__ __launch_bounds__(64 * ATT_WAVES) __attribute__((amdgpu_waves_per_eu(
   __shared__ int32_t keytok[KSEG];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 5, c = lane & 31;
-  const int h = blockIdx.x % H;
-  const int chunk = (blockIdx.x / H) % nchunk;
-  const int b = lpt[blockIdx.x / (H * nchunk)];
+  int unit, member;
+  xcd_split(blockIdx.x, nchunk * H, unit, member);
+  if (unit >= M) return;
+  const int h = member % H, chunk = member / H;
+  const int b = lpt[unit];
   const int r0 = blk_off[b], rows = blk_off[b + 1] - r0;
   if (chunk * ATT_ROWS >= rows) return;  // uniform across the workgroup
   int nsel = 0;
@@ -763,7 +771,7 @@ hipError_t run_pool(const ssa_plan_s* p, int H, const void* k, const void* v, co
                     const void* wv, const FwdWs& w, hipStream_t s) {
   using T = typename Tr<DT>::T;
   const int Mp = (int)pooled_rows(p->M);
-  hipLaunchKernelGGL((k_pool<DT, D>), dim3(Mp, H), dim3(256), 0, s, (const T*)k, (const T*)v,
+  hipLaunchKernelGGL((k_pool<DT, D>), dim3(xcd_grid(Mp, H)), dim3(256), 0, s, (const T*)k, (const T*)v,
                      (const T*)wk, (const T*)wv, p->perm, p->blk_off, (int)p->M, Mp, H, (T*)w.pooled,
                      (T*)w.pooled_v);
   return hipGetLastError();
@@ -775,7 +783,7 @@ hipError_t run_select(const ssa_plan_s* p, int H, int topk, float sl2, const voi
   using T = typename Tr<DT>::T;
   const int Mp = (int)pooled_rows(p->M);
   const size_t shm = (size_t)Mp * sizeof(float);
-  hipLaunchKernelGGL((k_select<DT, D>), dim3((unsigned)(p->M * H)), dim3(64 * SEL_WAVES), shm, s,
+  hipLaunchKernelGGL((k_select<DT, D>), dim3(xcd_grid(p->M, H)), dim3(64 * SEL_WAVES), shm, s,
                      (const T*)q, (const T*)w.pooled, p->perm, p->blk_off, p->lpt, (int)p->M, Mp, H,
                      p->n, sl2, topk, (T*)w.oc, sel, w.lse, w.obr);
   return hipGetLastError();
@@ -788,13 +796,13 @@ hipError_t run_attend(const ssa_plan_s* p, int H, int topk, float sl2, const voi
   using T = typename Tr<DT>::T;
   const int nchunk = (p->max_rows + ATT_ROWS - 1) / ATT_ROWS;
   if (buffer_addressable(p->n * H * D * (int64_t)sizeof(T)))
-    hipLaunchKernelGGL((k_attend<DT, D, true>), dim3((unsigned)(p->M * H * nchunk)), dim3(64 * ATT_WAVES), 0,
+    hipLaunchKernelGGL((k_attend<DT, D, true>), dim3(xcd_grid(p->M, (int64_t)H * nchunk)), dim3(64 * ATT_WAVES), 0,
                      s, (const T*)q, (const T*)k, (const T*)v, (const T*)gates, p->perm, p->blk_off,
                      p->blk_cell, p->cell_off, p->cell_blk, p->lpt, sel, (const T*)w.oc, (int)p->M,
                      H, nchunk, p->n, topk, sl2, (T*)out, w.lse,
                      w.obr ? w.obr + p->n * H * D : nullptr, w.obr ? w.obr + 2 * p->n * H * D : nullptr);
   else
-    hipLaunchKernelGGL((k_attend<DT, D, false>), dim3((unsigned)(p->M * H * nchunk)), dim3(64 * ATT_WAVES), 0,
+    hipLaunchKernelGGL((k_attend<DT, D, false>), dim3(xcd_grid(p->M, (int64_t)H * nchunk)), dim3(64 * ATT_WAVES), 0,
                      s, (const T*)q, (const T*)k, (const T*)v, (const T*)gates, p->perm, p->blk_off,
                      p->blk_cell, p->cell_off, p->cell_blk, p->lpt, sel, (const T*)w.oc, (int)p->M,
                      H, nchunk, p->n, topk, sl2, (T*)out, w.lse,

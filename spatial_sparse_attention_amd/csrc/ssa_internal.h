@@ -52,6 +52,8 @@ static inline size_t esize_of(ssa_dtype dt) { return dt == SSA_F32 ? 4 : 2; }
 // layout, so a tile is one contiguous copy.  A row-major copy of the pooled values
 // ([H][Mp][vrow]) serves the backward.
 constexpr int POOL_TILE = 64;
+// Workgroups for nunits units of `per` members each, dealt to the 8 XCDs round-robin.
+static inline unsigned xcd_grid(int64_t nunits, int64_t per) { return (unsigned)((nunits + 7) / 8 * 8 * per); }
 // Gathers from a token tensor use 32-bit byte offsets (buffer loads) when it is below 4 GiB.
 static inline bool buffer_addressable(int64_t bytes) { return bytes <= (int64_t)0xFFFFFFF0; }
 // Pooled blocks per head as stored: a whole, even number of 64-block stages, so that every

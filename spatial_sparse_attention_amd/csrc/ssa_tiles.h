@@ -274,6 +274,19 @@ __device__ inline void dma_contiguous(void* lds, const void* g, int nchunks, int
   }
 }
 
+// ------------------------------------------------------------------ XCD-aware work order
+// gfx950 dispatches workgroup i of a grid to XCD i % 8, and each XCD has its own L2.  Work
+// comes in units of `per` workgroups that read the same rows (the heads and chunks of one
+// query block); units are dealt to the XCDs round-robin and a unit's members run on one XCD,
+// consecutively, so they share that XCD's L2.  Grid: xcd_grid(nunits, per) workgroups;
+// unit >= nunits means no work.
+constexpr int NXCD = 8;
+__device__ inline void xcd_split(int id, int per, int& unit, int& member) {
+  const int x = id % NXCD, k = id / NXCD;
+  unit = (k / per) * NXCD + x;
+  member = k % per;
+}
+
 // ------------------------------------------------------------------ gathered token tiles
 // A key (or query) set is a list of blocks, concatenated in sorted token order and cut into
 // 32-row tiles.  A stage holds the tile's first-operand rows ([32][KROW]) followed by its
