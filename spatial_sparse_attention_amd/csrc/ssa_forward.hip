@@ -23,6 +23,7 @@
 // planes whose sum reproduces the fp32 value, so the scores that decide the top-k
 // carry fp32-level error.
 #include <hip/hip_runtime.h>
+#include <type_traits>
 #include "ssa_internal.h"
 #include "ssa_mfma.h"
 #include "ssa_tiles.h"
@@ -313,7 +314,7 @@ __global__ __launch_bounds__(64 * SEL_WAVES) void k_select(
   constexpr int ROWS = 32 * SEL_WAVES;
   __shared__ __attribute__((aligned(1024))) T stage0[C::STAGE];
   __shared__ __attribute__((aligned(1024))) T stage1[C::STAGE];
-  __shared__ float stage_sum[2][SEL_WAVES][64];
+  __shared__ float stage_sum[3][SEL_WAVES][64];
   __shared__ float lse_lds[ROWS];
   __shared__ uint32_t hist[256];
   __shared__ uint32_t bcast[2];
@@ -332,7 +333,7 @@ __global__ __launch_bounds__(64 * SEL_WAVES) void k_select(
   const int nstep = nsw * 2 * ntile;
   const T* pstage = pooled + (int64_t)h * ntile * C::STAGE;
   constexpr int NCH1 = C::STAGE * sizeof(T) / 16, NCH2 = NS * C::KPLANE * sizeof(T) / 16;
-  auto issue = [&](int k, T* dst) {  // copy of step k's stage
+  auto issue = [&](int k, T* dst) __attribute__((always_inline)) {  // copy of step k's stage
     const int pos = k % (2 * ntile);
     const int t = pos < ntile ? pos : pos - ntile;
     dma_contiguous<SEL_WAVES>(dst, pstage + (int64_t)t * C::STAGE, pos < ntile ? NCH1 : NCH2, wave, lane);
@@ -340,45 +341,48 @@ __global__ __launch_bounds__(64 * SEL_WAVES) void k_select(
   issue(0, stage0);
   for (int j = tid; j < Mp; j += 64 * SEL_WAVES) sig[j] = 0.f;
 
-  auto row_of = [&](int sw) { return sw * ROWS + wave * 32 + c; };
+  // Waves 0-3 (group A) and 4-7 (group B) share the four SIMDs pairwise.  Group B runs half
+  // a step behind: after a stage's barrier it first finishes the previous stage (softmax and
+  // PV, or column sums) from registers, then computes this stage's scores, so that on each
+  // SIMD one wave's VALU work overlaps the other's MFMAs.  Row tiles go to waves so that the
+  // tiles of a block pair up on the SIMDs: wave w takes tile 2 (w % 4) + w / 4.
+  const bool lag = wave >= SEL_WAVES / 2;
+  const int wt = 2 * (wave % (SEL_WAVES / 2)) + wave / (SEL_WAVES / 2);
+  auto row_of = [&](int sw) __attribute__((always_inline)) { return sw * ROWS + wt * 32 + c; };
   F qf[C::NKS];
   {
     const int my_row = row_of(0);
     load_q<DT, D>(qf, q + ((int64_t)(my_row < rows ? perm[r0 + my_row] : 0) * H + h) * D, my_row < rows, lane);
   }
 
-  auto fold = [&](int t) {  // sum the per-wave column sums of tile t into sigma (fixed order)
+  auto fold = [&](int t) __attribute__((always_inline)) {  // sum the per-wave column sums of tile t into sigma (fixed order)
     if (tid < C::PT) {
       const int key = t * C::PT + tid;
-      float s = stage_sum[t & 1][0][tid];
+      float s = stage_sum[t % 3][0][tid];
 #pragma unroll
-      for (int w = 1; w < SEL_WAVES; ++w) s += stage_sum[t & 1][w][tid];
+      for (int w = 1; w < SEL_WAVES; ++w) s += stage_sum[t % 3][w][tid];
       if (key < M) sig[key] += s;
     }
   };
 
+  constexpr bool VPRE = sizeof(T) == 2;  // value fragments read with the scores (16-bit types)
   int k = 0;  // step of the stage stream
   for (int sw = 0; sw < nsw; ++sw) {
     const int my_row = row_of(sw);
-    const bool wave_active = sw * ROWS + wave * 32 < rows;
+    const bool wave_active = sw * ROWS + wt * 32 < rows;
     const bool valid = my_row < rows;
-
     // ---------------- pass 1: online softmax over all pooled keys -> o_c, lse
     Online<C::NDV> st;
     st.init();
-    auto p1 = [&](int t, T* cur, T* nxt) {
-      dma_wait();
-      __syncthreads();
-      if (k + (t & 1) + 1 < nstep) issue(k + (t & 1) + 1, nxt);
-      if (t == 0 && sw > 0) fold(ntile - 1);  // the previous sweep's last column sums
-      if (wave_active && t * C::PT < M) {
-        ssa_f16v a0, a1;
-        // value fragments read ahead for 16-bit types (fp32 ones would take 2*D registers)
-        constexpr bool VPRE = sizeof(T) == 2;
-        const T* vtt = cur + NS * C::KPLANE;
-        F vt[2][C::PK][C::NDV];
+    // LAG: group B's order (finish the previous stage, then score this one).  fp32 reads its
+    // value fragments at use, from a stage that must still be resident, so it never lags.
+    auto pass1 = [&](auto lagc) __attribute__((always_inline)) {
+      constexpr bool LAG = decltype(lagc)::value && VPRE;
+      ssa_f16v a0, a1;  // scores of the stage in flight
+      F vt[2][C::PK][C::NDV];
+      auto scores = [&](int t, const T* cur) __attribute__((always_inline)) {
         stage_scores<DT, D, true, VPRE>(cur + (lane & 31) * C::KROW + (lane >> 5) * C::KPL, qf, a0,
-                                        a1, vtt, vt, lane);
+                                        a1, cur + NS * C::KPLANE, vt, lane);
         if ((t + 1) * C::PT > M) {  // padding blocks
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
@@ -386,6 +390,8 @@ __global__ __launch_bounds__(64 * SEL_WAVES) void k_select(
             if (t * C::PT + 32 + res_row(r, g) >= M) a1[r] = -INFINITY;
           }
         }
+      };
+      auto finish = [&](const T* cur) __attribute__((always_inline)) {
         st.update2(a0, a1, sl2);
 #pragma unroll
         for (int ks = 0; ks < C::PK; ++ks) {
@@ -396,17 +402,36 @@ __global__ __launch_bounds__(64 * SEL_WAVES) void k_select(
               st.o[j] = Tr<DT>::mma(vt[0][ks][j], p0, st.o[j]);
               st.o[j] = Tr<DT>::mma(vt[1][ks][j], p1f, st.o[j]);
             } else {
+              const T* vtt = cur + NS * C::KPLANE;
               st.o[j] = Tr<DT>::mma(vtt_frag<DT, D>(vtt, 0, ks, j, lane), p0, st.o[j]);
               st.o[j] = Tr<DT>::mma(vtt_frag<DT, D>(vtt, 32, ks, j, lane), p1f, st.o[j]);
             }
           }
         }
+      };
+      auto p1 = [&](int t, T* cur, T* nxt) __attribute__((always_inline)) {
+        dma_wait();
+        __syncthreads();
+        if (k + t + 1 < nstep) issue(k + t + 1, nxt);
+        if (wave_active) {
+          if constexpr (LAG) {
+            if (t > 0 && (t - 1) * C::PT < M) finish(nullptr);
+            if (t * C::PT < M) scores(t, cur);
+          } else if (t * C::PT < M) {
+            scores(t, cur);
+            finish(cur);
+          }
+        }
+      };
+      for (int t = 0; t < ntile; t += 2) {  // ntile is even: every pass starts on stage0
+        p1(t, stage0, stage1);
+        p1(t + 1, stage1, stage0);
       }
+      if (LAG && wave_active && (ntile - 1) * C::PT < M) finish(nullptr);
     };
-    for (int t = 0; t < ntile; t += 2, k += 2) {  // ntile is even: every pass starts on stage0
-      p1(t, stage0, stage1);
-      p1(t + 1, stage1, stage0);
-    }
+    if (lag) pass1(std::true_type());
+    else pass1(std::false_type());
+    k += ntile;
     {  // this sweep's compressed output and lse
       const float ltot = xor32_sum(st.l);
       const float lse = st.m + fast_log2(ltot);
@@ -427,14 +452,14 @@ __global__ __launch_bounds__(64 * SEL_WAVES) void k_select(
           }
       }
       // rows past the block get +inf, so their probabilities in pass 2 are exactly zero
-      if (g == 0) lse_lds[wave * 32 + c] = valid ? lse : INFINITY;
+      if (g == 0) lse_lds[wt * 32 + c] = valid ? lse : INFINITY;
     }
     __syncthreads();
 
     // ---------------- pass 2: importance column sums (S layout)
     float lrow[16];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) lrow[r] = lse_lds[wave * 32 + res_row(r, g)];
+    for (int r = 0; r < 16; ++r) lrow[r] = lse_lds[wt * 32 + res_row(r, g)];
     // next sweep's queries, loaded under pass 2 where the registers allow
     constexpr bool QPRE = D * sizeof(T) <= 192;
     F qn[C::NKS];
@@ -442,33 +467,56 @@ __global__ __launch_bounds__(64 * SEL_WAVES) void k_select(
       const int nrow = row_of(sw + 1);
       load_q<DT, D>(qn, q + ((int64_t)(nrow < rows ? perm[r0 + nrow] : 0) * H + h) * D, nrow < rows, lane);
     }
-    auto p2 = [&](int t, T* cur, T* nxt) {
-      dma_wait();
-      __syncthreads();
-      if (k + (t & 1) + 1 < nstep) issue(k + (t & 1) + 1, nxt);
-      if (t > 0) fold(t - 1);
-      float cs0 = 0.f, cs1 = 0.f;
-      if (wave_active && t * C::PT < M) {
-        ssa_f16v a0, a1;
-        stage_scores<DT, D, false, false>(cur + (lane & 31) * C::KROW + (lane >> 5) * C::KPL, qf,
-                                          a0, a1, nullptr, nullptr, lane);
+    auto pass2 = [&](auto lagc) __attribute__((always_inline)) {
+      constexpr bool LAG = decltype(lagc)::value;
+      ssa_f16v a0, a1;  // scores of the stage in flight
+      // column sums of tile t from the scores in a0, a1 (zero for inactive waves)
+      auto finish = [&](int t, bool have) __attribute__((always_inline)) {
+        float cs0 = 0.f, cs1 = 0.f;
+        if (have) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          cs0 += fast_exp2(__builtin_fmaf(a0[r], sl2, -lrow[r]));
-          cs1 += fast_exp2(__builtin_fmaf(a1[r], sl2, -lrow[r]));
+          for (int r = 0; r < 16; ++r) {
+            cs0 += fast_exp2(__builtin_fmaf(a0[r], sl2, -lrow[r]));
+            cs1 += fast_exp2(__builtin_fmaf(a1[r], sl2, -lrow[r]));
+          }
+          cs0 = xor32_sum(cs0);
+          cs1 = xor32_sum(cs1);
         }
-        cs0 = xor32_sum(cs0);
-        cs1 = xor32_sum(cs1);
+        if (g == 0) {
+          stage_sum[t % 3][wave][c] = cs0;
+          stage_sum[t % 3][wave][32 + c] = cs1;
+        }
+      };
+      auto scores = [&](const T* cur) __attribute__((always_inline)) {
+        stage_scores<DT, D, false, false>(cur + (lane & 31) * C::KROW + (lane >> 5) * C::KPL, qf, a0,
+                                          a1, nullptr, nullptr, lane);
+      };
+      auto p2 = [&](int t, T* cur, T* nxt) __attribute__((always_inline)) {
+        dma_wait();
+        __syncthreads();
+        if (k + t + 1 < nstep) issue(k + t + 1, nxt);
+        if (t >= 2) fold(t - 2);  // both groups' sums of tile t - 2 are in
+        const bool on = wave_active && t * C::PT < M;
+        if constexpr (LAG) {
+          if (t > 0) finish(t - 1, wave_active && (t - 1) * C::PT < M);
+          if (on) scores(cur);
+        } else {
+          if (on) scores(cur);
+          finish(t, on);
+        }
+      };
+      for (int t = 0; t < ntile; t += 2) {
+        p2(t, stage0, stage1);
+        p2(t + 1, stage1, stage0);
       }
-      if (g == 0) {
-        stage_sum[t & 1][wave][c] = cs0;
-        stage_sum[t & 1][wave][32 + c] = cs1;
-      }
+      if (LAG) finish(ntile - 1, wave_active && (ntile - 1) * C::PT < M);
     };
-    for (int t = 0; t < ntile; t += 2, k += 2) {
-      p2(t, stage0, stage1);
-      p2(t + 1, stage1, stage0);
-    }
+    if (lag) pass2(std::true_type());
+    else pass2(std::false_type());
+    k += ntile;
+    __syncthreads();
+    if (ntile >= 2) fold(ntile - 2);
+    fold(ntile - 1);
     if (sw + 1 < nsw) {
       if constexpr (QPRE) {
 #pragma unroll
@@ -480,38 +528,39 @@ __global__ __launch_bounds__(64 * SEL_WAVES) void k_select(
     }
   }
   __syncthreads();
-  fold(ntile - 1);
-  __syncthreads();
   topk_radix<SEL_WAVES>(sig, M, topk, sel + ((int64_t)h * M + b) * topk, hist, bcast, wcnt, tid);
 }
 
 // ------------------------------------------------------------------ selected + window + combine
-// Copies of one gathered 32-key tile (K rows [32][KROW], then V rows [32][VROW]) from the
-// caller's K and V into LDS, 16 bytes per lane and instruction.  Every wave issues the same
-// NI instructions per tile, so a wave can wait for all but its newest tile's copies with one
-// count.  Lanes on a row's padding chunk, or past the tile, copy a valid chunk into a spot
-// nobody reads (the row padding, or the buffer's tail).
+// Copies of one gathered 32-key tile from the caller's K and V into LDS, 16 bytes per lane
+// and instruction: the K rows ([32][KROW]) at the start of the stage, the V rows ([32][VROW])
+// at VOFF.  K and V copies never share an instruction, so each instruction reads through one
+// (wave-uniform) buffer descriptor, and every wave issues the same NI instructions per tile,
+// so a wave can wait for all but its newest tile's copies with one count.  Lanes on a row's
+// padding chunk, past a part's chunks or past the tile copy a valid chunk into a spot nobody
+// reads (the row padding, the gap before VOFF, or the buffer's tail).
 template <int DT, int D, int NW>
 struct TileCopy {
   using C = Cfg<DT, D>;
   using T = typename Tr<DT>::T;
   static constexpr int KRC = C::KCH / KT, VRC = C::VCH / KT;  // chunks per padded row
-  static constexpr int NPOS = C::KCH + C::VCH;
-  static constexpr int NI = ((NPOS + 63) / 64 + NW - 1) / NW;
+  static constexpr int KI = (C::KCH + 63) / 64, VI = (C::VCH + 63) / 64;  // instructions
+  static constexpr int NI = (KI + VI + NW - 1) / NW;
   static constexpr int ELEMS = NI * NW * 64 * C::EPC;  // stage buffer, tail included
+  static constexpr int VOFF = KI * 64 * C::EPC;         // V rows' offset in the stage
   int32_t row[NI];   // tile row (key) of each copy
-  int32_t goff[NI];  // element offset inside the token's head row, bit 30 set for V
+  int32_t goff[NI];  // element offset inside the token's head row
   int32_t tok[NI];
   __device__ inline void init(int wave, int lane) {
 #pragma unroll
     for (int m = 0; m < NI; ++m) {
-      const int p = (wave + m * NW) * 64 + lane;
-      const bool isk = p < C::KCH;
-      const int q = isk ? p : p - C::KCH;
-      const int rr = isk ? q / KRC : q / VRC, ch = isk ? q % KRC : q % VRC;
-      const bool ok = p < NPOS && ch < C::CPR;
-      row[m] = p < NPOS ? rr : 0;
-      goff[m] = (ok ? ch * C::EPC : 0) + (isk || p >= NPOS ? 0 : (1 << 30));
+      const int i = wave + m * NW;
+      const bool isk = i < KI;
+      const int p = (isk ? i : i - KI) * 64 + lane;
+      const int rr = isk ? p / KRC : p / VRC, ch = isk ? p % KRC : p % VRC;
+      const bool ok = (isk ? p < C::KCH : (i < KI + VI && p < C::VCH)) && ch < C::CPR;
+      row[m] = ok ? rr : 0;
+      goff[m] = ok ? ch * C::EPC : 0;
     }
   }
   // tokens of the tile starting at key k0 of a staged segment of n keys (rows past n: key 0)
@@ -529,17 +578,14 @@ struct TileCopy {
       const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(vin + h * D), 0, -1, 0x00020000);
 #pragma unroll
       for (int m = 0; m < NI; ++m) {
-        const uint32_t off = ((uint32_t)tok[m] * (uint32_t)(H * D) + (uint32_t)(goff[m] & ((1 << 30) - 1))) * (uint32_t)sizeof(T);
+        const uint32_t off = ((uint32_t)tok[m] * (uint32_t)(H * D) + (uint32_t)goff[m]) * (uint32_t)sizeof(T);
         lds_void_t* dst = (lds_void_t*)(stage + (wave + m * NW) * 64 * C::EPC);
-        // one instruction per copy: the V flag selects the descriptor, not the instruction
-        const __amdgpu_buffer_rsrc_t rs = (goff[m] & (1 << 30)) ? rv : rk;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 16, off, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(wave + m * NW < KI ? rk : rv, dst, 16, off, 0, 0, 0);
       }
     } else {
 #pragma unroll
       for (int m = 0; m < NI; ++m) {
-        const bool isv = goff[m] & (1 << 30);
-        const T* src = (isv ? vin : kin) + ((int64_t)tok[m] * H + h) * D + (goff[m] & ((1 << 30) - 1));
+        const T* src = (wave + m * NW < KI ? kin : vin) + ((int64_t)tok[m] * H + h) * D + goff[m];
         dma16(src, stage + (wave + m * NW) * 64 * C::EPC);
       }
     }
@@ -573,7 +619,8 @@ __device__ inline void gathered_branch(
   using F = typename Tr<DT>::frag;
   using TC = TileCopy<DT, D, ATT_WAVES>;
   constexpr int NTH = 64 * ATT_WAVES;
-  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   st.init();
   TC tc = tc0;
   for (int l0 = 0; l0 < nlist; l0 += NTH) {
@@ -630,7 +677,7 @@ __device__ inline void gathered_branch(
         // the value fragments are read before tile t + 2's copy is issued: the transpose
         // reads carry no alias information, so reading after it would wait for that copy
         VFrags<DT, D> vf;
-        if (wave_active) vf.read(cur + C::KTILE, lane);
+        if (wave_active) vf.read(cur + TC::VOFF, lane);
         if (t + 2 < ntile) tc.template issue<BUF>(nx2, kin, vin, H, h, wave);
         if (t + 3 < ntile) tc.fetch(keytok, (t + 3) * KT, n);
         if (wave_active) {
@@ -683,7 +730,8 @@ __global__ __launch_bounds__(64 * ATT_WAVES) __attribute__((amdgpu_waves_per_eu(
   __shared__ int32_t sel_lds[256];
   __shared__ int32_t keytok[KSEG];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 5, c = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, c = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   int unit, member;
   xcd_split(blockIdx.x, nchunk * H, unit, member);
   if (unit >= M) return;
