@@ -705,8 +705,25 @@ __device__ inline void gathered_branch(
   }
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ inline int wave_incl_scan(int x, int lane) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(x, off);
+    if (lane >= off) x += y;
+  }
+  return x;
+}
+
 // One workgroup per (ATT_ROWS-row chunk of a query block, head); a block's chunks and heads
 // form one XCD unit (they gather the same key rows), blocks in longest-first order.
+//
+// Usual case (at most 64 selected and 64 window blocks, at most KSEG keys in all): both key
+// sets form one stream -- the selected blocks' keys, padding to a whole tile, then the window
+// cell's keys -- whose token table is built once, and whose tiles flow through the stage
+// buffers without a break; at the boundary tile the selected branch is closed (its gated
+// output kept in registers) and the window branch starts.  Otherwise each set is streamed on
+// its own (gathered_branch).
 template <int DT, int D, bool BUF>
 __global__ __launch_bounds__(64 * ATT_WAVES) __attribute__((amdgpu_waves_per_eu(2))) void k_attend(
     const typename Tr<DT>::T* __restrict__ q, const typename Tr<DT>::T* __restrict__ kin,
@@ -715,13 +732,14 @@ __global__ __launch_bounds__(64 * ATT_WAVES) __attribute__((amdgpu_waves_per_eu(
     const int32_t* __restrict__ blk_cell, const int32_t* __restrict__ cell_off,
     const int32_t* __restrict__ cell_blk, const int32_t* __restrict__ lpt,
     const int32_t* __restrict__ sel, const typename Tr<DT>::T* __restrict__ oc, int M, int H,
-    int nchunk, int64_t N, int topk, float sl2, typename Tr<DT>::T* __restrict__ out,
+    int nchunk, int64_t N, int topk, float sl2, int window_is_block, typename Tr<DT>::T* __restrict__ out,
     float* __restrict__ lse_save, float* __restrict__ os_save, float* __restrict__ ow_save) {
   using C = Cfg<DT, D>;
   using T = typename Tr<DT>::T;
   using F = typename Tr<DT>::frag;
   using TC = TileCopy<DT, D, ATT_WAVES>;
   constexpr int NTH = 64 * ATT_WAVES;
+  static_assert(NTH >= 256, "one thread per top-k slot");
   __shared__ __attribute__((aligned(1024))) T buf0[TC::ELEMS];
   __shared__ __attribute__((aligned(1024))) T buf1[TC::ELEMS];
   __shared__ __attribute__((aligned(1024))) T buf2[TC::ELEMS];
@@ -729,6 +747,8 @@ __global__ __launch_bounds__(64 * ATT_WAVES) __attribute__((amdgpu_waves_per_eu(
   __shared__ int32_t lst_off[NTH];
   __shared__ int32_t sel_lds[256];
   __shared__ int32_t keytok[KSEG];
+  __shared__ int32_t e_pre[2][65];  // stream offsets of the usual case's entries (per set)
+  __shared__ int32_t e_off[2][64];  // their first sorted position
 
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, c = lane & 31;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -739,13 +759,16 @@ __global__ __launch_bounds__(64 * ATT_WAVES) __attribute__((amdgpu_waves_per_eu(
   const int b = lpt[unit];
   const int r0 = blk_off[b], rows = blk_off[b + 1] - r0;
   if (chunk * ATT_ROWS >= rows) return;  // uniform across the workgroup
-  int nsel = 0;
-  const int32_t* srow = sel + ((int64_t)h * M + b) * topk;
-  for (int t = 0; t < topk; ++t) nsel += srow[t] >= 0;
-  for (int t = tid; t < nsel; t += NTH) sel_lds[t] = srow[t];
-  const int cell = blk_cell[b];
-  const int c0 = cell_off[cell], c1 = cell_off[cell + 1];
 
+  // ---- metadata, loads issued side by side: selection row, window cell, queries, gates
+  const int32_t* srow = sel + ((int64_t)h * M + b) * topk;
+  const int sb = tid < topk ? srow[tid] : -1;  // selected ids ascend, -1 padded at the end
+  int c0 = b, c1 = b + 1;                       // window cell as a range of cell_blk
+  if (!window_is_block) {
+    const int cell = blk_cell[b];
+    c0 = cell_off[cell];
+    c1 = cell_off[cell + 1];
+  }
   const int wbase = chunk * ATT_ROWS + wave * 32;
   const bool wave_active = wbase < rows;
   const int my_row = wbase + c;
@@ -753,17 +776,22 @@ __global__ __launch_bounds__(64 * ATT_WAVES) __attribute__((amdgpu_waves_per_eu(
   const int64_t tok_q = valid ? perm[r0 + my_row] : 0;
   F qf[C::NKS];
   load_q<DT, D>(qf, q + (tok_q * H + h) * D, valid, lane);
+  float gt[3] = {0.f, 0.f, 0.f};
+  if (valid) {
+#pragma unroll
+    for (int x = 0; x < 3; ++x) gt[x] = Tr<DT>::up(gates[(tok_q * H + h) * 3 + x]);
+  }
+  if (sb >= 0) sel_lds[tid] = sb;
+  const int nsel = __syncthreads_count(sb >= 0);
+  const int nwin = c1 - c0;
   TC tc;
   tc.init(wave, lane);
-
   Online<C::NDV> st;
-  gathered_branch<DT, D, BUF>(st, tc, sel_lds, nsel, qf, kin, vin, perm, blk_off, H, h, sl2,
-                              wave_active, buf0, buf1, buf2, pre, lst_off, keytok);
   ssa_f16v res[C::NDV];  // the selected branch's gated output
-  {
-    const float g1 = valid ? Tr<DT>::up(gates[(tok_q * H + h) * 3 + 1]) : 0.f;
+
+  auto close_selected = [&]() __attribute__((always_inline)) {
     const float ls = xor32_sum(st.l);
-    const float f = g1 / ls;
+    const float f = gt[1] / ls;
     if (lse_save && wave_active && valid) {
       const int64_t row = r0 + my_row;
       if (g == 0) lse_save[(int64_t)(H + h) * N + row] = st.m + fast_log2(ls);
@@ -778,14 +806,106 @@ __global__ __launch_bounds__(64 * ATT_WAVES) __attribute__((amdgpu_waves_per_eu(
     }
 #pragma unroll
     for (int j = 0; j < C::NDV; ++j) res[j] = st.o[j] * f;
+  };
+
+  bool fast = nsel <= 64 && nwin <= 64;
+  if (fast) {
+    // entries: wave 0 the selected blocks, wave 1 the window cell's blocks
+    if (wave < 2) {
+      const int ne = wave == 0 ? nsel : nwin;
+      int off = 0, sz = 0;
+      if (lane < ne) {
+        const int blk = wave == 0 ? sel_lds[lane] : (window_is_block ? b : cell_blk[c0 + lane]);
+        off = blk_off[blk];
+        sz = blk_off[blk + 1] - off;
+      }
+      const int incl = wave_incl_scan(sz, lane);
+      if (lane < ne) {
+        e_off[wave][lane] = off;
+        e_pre[wave][lane + 1] = incl;
+      }
+      if (lane == 0) e_pre[wave][0] = 0;
+    }
+    __syncthreads();
+    const int S = e_pre[0][nsel], W = e_pre[1][nwin];
+    fast = (S + KT - 1) / KT * KT + W <= KSEG;
   }
-  gathered_branch<DT, D, BUF>(st, tc, cell_blk + c0, c1 - c0, qf, kin, vin, perm, blk_off, H, h, sl2,
-                              wave_active, buf0, buf1, buf2, pre, lst_off, keytok);
+  if (fast) {
+    const int S = e_pre[0][nsel], W = e_pre[1][nwin];
+    const int P1 = (S + KT - 1) / KT * KT;  // the window keys start on a tile
+    const int tot = P1 + W;
+    for (int j = tid; j < tot; j += NTH) {
+      const int part = j < P1 ? 0 : 1;
+      const int key = part ? j - P1 : (j < S ? j : 0);  // padding keys reuse key 0
+      const int ne = part ? nwin : nsel;
+      int lo = 0, hi = ne - 1;  // last entry starting at or before the key
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (e_pre[part][mid] <= key) lo = mid; else hi = mid - 1;
+      }
+      keytok[j] = perm[e_off[part][lo] + (key - e_pre[part][lo])];
+    }
+    __syncthreads();
+    const int ntile = (tot + KT - 1) / KT, tb = P1 / KT;
+    st.init();
+    auto step = [&](int t, T* cur, T* nx2) __attribute__((always_inline)) {
+      if (t + 1 < ntile) vm_wait<TC::NI>();  // tile t landed; tile t + 1 may be in flight
+      else vm_wait<0>();
+      __syncthreads();
+      if (t == tb) {  // first window tile: close the selected branch
+        close_selected();
+        st.init();
+      }
+      const int lim = t < tb ? S : tot;  // keys at or past lim are masked
+      ssa_f16v acc = zero16();
+      if (wave_active) {
+        const T* krow = cur + (lane & 31) * C::KROW + (lane >> 5) * C::KPL;
+#pragma unroll
+        for (int ks = 0; ks < C::NKS; ++ks) acc = Tr<DT>::mma(load_frag<DT>(krow + ks * C::KS), qf[ks], acc);
+        if ((t + 1) * KT > lim) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (t * KT + res_row(r, g) >= lim) acc[r] = -INFINITY;
+        }
+        st.update(acc, sl2);
+      }
+      // the value fragments are read before tile t + 2's copy is issued: the transpose
+      // reads carry no alias information, so reading after it would wait for that copy
+      VFrags<DT, D> vf;
+      if (wave_active) vf.read(cur + TC::VOFF, lane);
+      if (t + 2 < ntile) tc.template issue<BUF>(nx2, kin, vin, H, h, wave);
+      if (t + 3 < ntile) tc.fetch(keytok, (t + 3) * KT, tot);
+      if (wave_active) {
+#pragma unroll
+        for (int ks = 0; ks < C::PK; ++ks) {
+          const F pf = p_frag<DT>(acc, ks);
+#pragma unroll
+          for (int j = 0; j < C::NDV; ++j) st.o[j] = Tr<DT>::mma(vf.f[ks][j], pf, st.o[j]);
+        }
+      }
+    };
+    tc.fetch(keytok, 0, tot);
+    tc.template issue<BUF>(buf0, kin, vin, H, h, wave);
+    if (ntile > 1) {
+      tc.fetch(keytok, KT, tot);
+      tc.template issue<BUF>(buf1, kin, vin, H, h, wave);
+    }
+    if (ntile > 2) tc.fetch(keytok, 2 * KT, tot);
+    for (int t = 0; t < ntile; t += 3) {
+      step(t, buf0, buf2);
+      if (t + 1 < ntile) step(t + 1, buf1, buf0);
+      if (t + 2 < ntile) step(t + 2, buf2, buf1);
+    }
+  } else {
+    gathered_branch<DT, D, BUF>(st, tc, sel_lds, nsel, qf, kin, vin, perm, blk_off, H, h, sl2,
+                                wave_active, buf0, buf1, buf2, pre, lst_off, keytok);
+    close_selected();
+    gathered_branch<DT, D, BUF>(st, tc, cell_blk + c0, nwin, qf, kin, vin, perm, blk_off, H, h, sl2,
+                                wave_active, buf0, buf1, buf2, pre, lst_off, keytok);
+  }
   if (wave_active && valid) {
     const float ltot = xor32_sum(st.l);
-    const float g0 = Tr<DT>::up(gates[(tok_q * H + h) * 3 + 0]);
-    const float g2 = Tr<DT>::up(gates[(tok_q * H + h) * 3 + 2]);
-    const float f = g2 / ltot;
+    const float f = gt[2] / ltot;
     const T* orow = oc + ((int64_t)(r0 + my_row) * H + h) * D;
     T* dst = out + (tok_q * H + h) * D;
     if (lse_save) {
@@ -807,7 +927,7 @@ __global__ __launch_bounds__(64 * ATT_WAVES) __attribute__((amdgpu_waves_per_eu(
         float v[4];
         load4(orow + col, v);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = res[j][4 * rq + e] + f * st.o[j][4 * rq + e] + g0 * v[e];
+        for (int e = 0; e < 4; ++e) v[e] = res[j][4 * rq + e] + f * st.o[j][4 * rq + e] + gt[0] * v[e];
         store4(dst + col, v[0], v[1], v[2], v[3]);
       }
   }
@@ -847,13 +967,13 @@ hipError_t run_attend(const ssa_plan_s* p, int H, int topk, float sl2, const voi
     hipLaunchKernelGGL((k_attend<DT, D, true>), dim3(xcd_grid(p->M, (int64_t)H * nchunk)), dim3(64 * ATT_WAVES), 0,
                      s, (const T*)q, (const T*)k, (const T*)v, (const T*)gates, p->perm, p->blk_off,
                      p->blk_cell, p->cell_off, p->cell_blk, p->lpt, sel, (const T*)w.oc, (int)p->M,
-                     H, nchunk, p->n, topk, sl2, (T*)out, w.lse,
+                     H, nchunk, p->n, topk, sl2, (int)p->window_is_block, (T*)out, w.lse,
                      w.obr ? w.obr + p->n * H * D : nullptr, w.obr ? w.obr + 2 * p->n * H * D : nullptr);
   else
     hipLaunchKernelGGL((k_attend<DT, D, false>), dim3(xcd_grid(p->M, (int64_t)H * nchunk)), dim3(64 * ATT_WAVES), 0,
                      s, (const T*)q, (const T*)k, (const T*)v, (const T*)gates, p->perm, p->blk_off,
                      p->blk_cell, p->cell_off, p->cell_blk, p->lpt, sel, (const T*)w.oc, (int)p->M,
-                     H, nchunk, p->n, topk, sl2, (T*)out, w.lse,
+                     H, nchunk, p->n, topk, sl2, (int)p->window_is_block, (T*)out, w.lse,
                      w.obr ? w.obr + p->n * H * D : nullptr, w.obr ? w.obr + 2 * p->n * H * D : nullptr);
   return hipGetLastError();
 }
