@@ -314,7 +314,7 @@ __global__ __launch_bounds__(64 * SEL_WAVES) void k_select(
   constexpr int ROWS = 32 * SEL_WAVES;
   __shared__ __attribute__((aligned(1024))) T stage0[C::STAGE];
   __shared__ __attribute__((aligned(1024))) T stage1[C::STAGE];
-  __shared__ float stage_sum[3][SEL_WAVES][64];
+  __shared__ float stage_sum[2][SEL_WAVES][64];
   __shared__ float lse_lds[ROWS];
   __shared__ uint32_t hist[256];
   __shared__ uint32_t bcast[2];
@@ -323,17 +323,15 @@ __global__ __launch_bounds__(64 * SEL_WAVES) void k_select(
 
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, c = lane & 31;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  int unit, h;
-  xcd_split(blockIdx.x, H, unit, h);
-  if (unit >= M) return;
-  const int b = lpt[unit];
+  const int h = blockIdx.x % H;  // consecutive workgroups: the heads of one block
+  const int b = lpt[blockIdx.x / H];
   const int r0 = blk_off[b], rows = blk_off[b + 1] - r0;
   const int ntile = Mp / C::PT;
   const int nsw = (rows + ROWS - 1) / ROWS;
   const int nstep = nsw * 2 * ntile;
   const T* pstage = pooled + (int64_t)h * ntile * C::STAGE;
   constexpr int NCH1 = C::STAGE * sizeof(T) / 16, NCH2 = NS * C::KPLANE * sizeof(T) / 16;
-  auto issue = [&](int k, T* dst) __attribute__((always_inline)) {  // copy of step k's stage
+  auto issue = [&](int k, T* dst) {  // copy of step k's stage
     const int pos = k % (2 * ntile);
     const int t = pos < ntile ? pos : pos - ntile;
     dma_contiguous<SEL_WAVES>(dst, pstage + (int64_t)t * C::STAGE, pos < ntile ? NCH1 : NCH2, wave, lane);
@@ -341,48 +339,45 @@ __global__ __launch_bounds__(64 * SEL_WAVES) void k_select(
   issue(0, stage0);
   for (int j = tid; j < Mp; j += 64 * SEL_WAVES) sig[j] = 0.f;
 
-  // Waves 0-3 (group A) and 4-7 (group B) share the four SIMDs pairwise.  Group B runs half
-  // a step behind: after a stage's barrier it first finishes the previous stage (softmax and
-  // PV, or column sums) from registers, then computes this stage's scores, so that on each
-  // SIMD one wave's VALU work overlaps the other's MFMAs.  Row tiles go to waves so that the
-  // tiles of a block pair up on the SIMDs: wave w takes tile 2 (w % 4) + w / 4.
-  const bool lag = wave >= SEL_WAVES / 2;
-  const int wt = 2 * (wave % (SEL_WAVES / 2)) + wave / (SEL_WAVES / 2);
-  auto row_of = [&](int sw) __attribute__((always_inline)) { return sw * ROWS + wt * 32 + c; };
+  auto row_of = [&](int sw) { return sw * ROWS + wave * 32 + c; };
   F qf[C::NKS];
   {
     const int my_row = row_of(0);
     load_q<DT, D>(qf, q + ((int64_t)(my_row < rows ? perm[r0 + my_row] : 0) * H + h) * D, my_row < rows, lane);
   }
 
-  auto fold = [&](int t) __attribute__((always_inline)) {  // sum the per-wave column sums of tile t into sigma (fixed order)
+  auto fold = [&](int t) {  // sum the per-wave column sums of tile t into sigma (fixed order)
     if (tid < C::PT) {
       const int key = t * C::PT + tid;
-      float s = stage_sum[t % 3][0][tid];
+      float s = stage_sum[t & 1][0][tid];
 #pragma unroll
-      for (int w = 1; w < SEL_WAVES; ++w) s += stage_sum[t % 3][w][tid];
+      for (int w = 1; w < SEL_WAVES; ++w) s += stage_sum[t & 1][w][tid];
       if (key < M) sig[key] += s;
     }
   };
 
-  constexpr bool VPRE = sizeof(T) == 2;  // value fragments read with the scores (16-bit types)
   int k = 0;  // step of the stage stream
   for (int sw = 0; sw < nsw; ++sw) {
     const int my_row = row_of(sw);
-    const bool wave_active = sw * ROWS + wt * 32 < rows;
+    const bool wave_active = sw * ROWS + wave * 32 < rows;
     const bool valid = my_row < rows;
+
     // ---------------- pass 1: online softmax over all pooled keys -> o_c, lse
     Online<C::NDV> st;
     st.init();
-    // LAG: group B's order (finish the previous stage, then score this one).  fp32 reads its
-    // value fragments at use, from a stage that must still be resident, so it never lags.
-    auto pass1 = [&](auto lagc) __attribute__((always_inline)) {
-      constexpr bool LAG = decltype(lagc)::value && VPRE;
-      ssa_f16v a0, a1;  // scores of the stage in flight
-      F vt[2][C::PK][C::NDV];
-      auto scores = [&](int t, const T* cur) __attribute__((always_inline)) {
+    auto p1 = [&](int t, T* cur, T* nxt) {
+      dma_wait();
+      __syncthreads();
+      if (k + (t & 1) + 1 < nstep) issue(k + (t & 1) + 1, nxt);
+      if (t == 0 && sw > 0) fold(ntile - 1);  // the previous sweep's last column sums
+      if (wave_active && t * C::PT < M) {
+        ssa_f16v a0, a1;
+        // value fragments read ahead for 16-bit types (fp32 ones would take 2*D registers)
+        constexpr bool VPRE = sizeof(T) == 2;
+        const T* vtt = cur + NS * C::KPLANE;
+        F vt[2][C::PK][C::NDV];
         stage_scores<DT, D, true, VPRE>(cur + (lane & 31) * C::KROW + (lane >> 5) * C::KPL, qf, a0,
-                                        a1, cur + NS * C::KPLANE, vt, lane);
+                                        a1, vtt, vt, lane);
         if ((t + 1) * C::PT > M) {  // padding blocks
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
@@ -390,8 +385,6 @@ __global__ __launch_bounds__(64 * SEL_WAVES) void k_select(
             if (t * C::PT + 32 + res_row(r, g) >= M) a1[r] = -INFINITY;
           }
         }
-      };
-      auto finish = [&](const T* cur) __attribute__((always_inline)) {
         st.update2(a0, a1, sl2);
 #pragma unroll
         for (int ks = 0; ks < C::PK; ++ks) {
@@ -402,36 +395,17 @@ __global__ __launch_bounds__(64 * SEL_WAVES) void k_select(
               st.o[j] = Tr<DT>::mma(vt[0][ks][j], p0, st.o[j]);
               st.o[j] = Tr<DT>::mma(vt[1][ks][j], p1f, st.o[j]);
             } else {
-              const T* vtt = cur + NS * C::KPLANE;
               st.o[j] = Tr<DT>::mma(vtt_frag<DT, D>(vtt, 0, ks, j, lane), p0, st.o[j]);
               st.o[j] = Tr<DT>::mma(vtt_frag<DT, D>(vtt, 32, ks, j, lane), p1f, st.o[j]);
             }
           }
         }
-      };
-      auto p1 = [&](int t, T* cur, T* nxt) __attribute__((always_inline)) {
-        dma_wait();
-        __syncthreads();
-        if (k + t + 1 < nstep) issue(k + t + 1, nxt);
-        if (wave_active) {
-          if constexpr (LAG) {
-            if (t > 0 && (t - 1) * C::PT < M) finish(nullptr);
-            if (t * C::PT < M) scores(t, cur);
-          } else if (t * C::PT < M) {
-            scores(t, cur);
-            finish(cur);
-          }
-        }
-      };
-      for (int t = 0; t < ntile; t += 2) {  // ntile is even: every pass starts on stage0
-        p1(t, stage0, stage1);
-        p1(t + 1, stage1, stage0);
       }
-      if (LAG && wave_active && (ntile - 1) * C::PT < M) finish(nullptr);
     };
-    if (lag) pass1(std::true_type());
-    else pass1(std::false_type());
-    k += ntile;
+    for (int t = 0; t < ntile; t += 2, k += 2) {  // ntile is even: every pass starts on stage0
+      p1(t, stage0, stage1);
+      p1(t + 1, stage1, stage0);
+    }
     {  // this sweep's compressed output and lse
       const float ltot = xor32_sum(st.l);
       const float lse = st.m + fast_log2(ltot);
@@ -452,14 +426,14 @@ __global__ __launch_bounds__(64 * SEL_WAVES) void k_select(
           }
       }
       // rows past the block get +inf, so their probabilities in pass 2 are exactly zero
-      if (g == 0) lse_lds[wt * 32 + c] = valid ? lse : INFINITY;
+      if (g == 0) lse_lds[wave * 32 + c] = valid ? lse : INFINITY;
     }
     __syncthreads();
 
     // ---------------- pass 2: importance column sums (S layout)
     float lrow[16];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) lrow[r] = lse_lds[wt * 32 + res_row(r, g)];
+    for (int r = 0; r < 16; ++r) lrow[r] = lse_lds[wave * 32 + res_row(r, g)];
     // next sweep's queries, loaded under pass 2 where the registers allow
     constexpr bool QPRE = D * sizeof(T) <= 192;
     F qn[C::NKS];
@@ -467,56 +441,33 @@ __global__ __launch_bounds__(64 * SEL_WAVES) void k_select(
       const int nrow = row_of(sw + 1);
       load_q<DT, D>(qn, q + ((int64_t)(nrow < rows ? perm[r0 + nrow] : 0) * H + h) * D, nrow < rows, lane);
     }
-    auto pass2 = [&](auto lagc) __attribute__((always_inline)) {
-      constexpr bool LAG = decltype(lagc)::value;
-      ssa_f16v a0, a1;  // scores of the stage in flight
-      // column sums of tile t from the scores in a0, a1 (zero for inactive waves)
-      auto finish = [&](int t, bool have) __attribute__((always_inline)) {
-        float cs0 = 0.f, cs1 = 0.f;
-        if (have) {
+    auto p2 = [&](int t, T* cur, T* nxt) {
+      dma_wait();
+      __syncthreads();
+      if (k + (t & 1) + 1 < nstep) issue(k + (t & 1) + 1, nxt);
+      if (t > 0) fold(t - 1);
+      float cs0 = 0.f, cs1 = 0.f;
+      if (wave_active && t * C::PT < M) {
+        ssa_f16v a0, a1;
+        stage_scores<DT, D, false, false>(cur + (lane & 31) * C::KROW + (lane >> 5) * C::KPL, qf,
+                                          a0, a1, nullptr, nullptr, lane);
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            cs0 += fast_exp2(__builtin_fmaf(a0[r], sl2, -lrow[r]));
-            cs1 += fast_exp2(__builtin_fmaf(a1[r], sl2, -lrow[r]));
-          }
-          cs0 = xor32_sum(cs0);
-          cs1 = xor32_sum(cs1);
+        for (int r = 0; r < 16; ++r) {
+          cs0 += fast_exp2(__builtin_fmaf(a0[r], sl2, -lrow[r]));
+          cs1 += fast_exp2(__builtin_fmaf(a1[r], sl2, -lrow[r]));
         }
-        if (g == 0) {
-          stage_sum[t % 3][wave][c] = cs0;
-          stage_sum[t % 3][wave][32 + c] = cs1;
-        }
-      };
-      auto scores = [&](const T* cur) __attribute__((always_inline)) {
-        stage_scores<DT, D, false, false>(cur + (lane & 31) * C::KROW + (lane >> 5) * C::KPL, qf, a0,
-                                          a1, nullptr, nullptr, lane);
-      };
-      auto p2 = [&](int t, T* cur, T* nxt) __attribute__((always_inline)) {
-        dma_wait();
-        __syncthreads();
-        if (k + t + 1 < nstep) issue(k + t + 1, nxt);
-        if (t >= 2) fold(t - 2);  // both groups' sums of tile t - 2 are in
-        const bool on = wave_active && t * C::PT < M;
-        if constexpr (LAG) {
-          if (t > 0) finish(t - 1, wave_active && (t - 1) * C::PT < M);
-          if (on) scores(cur);
-        } else {
-          if (on) scores(cur);
-          finish(t, on);
-        }
-      };
-      for (int t = 0; t < ntile; t += 2) {
-        p2(t, stage0, stage1);
-        p2(t + 1, stage1, stage0);
+        cs0 = xor32_sum(cs0);
+        cs1 = xor32_sum(cs1);
       }
-      if (LAG) finish(ntile - 1, wave_active && (ntile - 1) * C::PT < M);
+      if (g == 0) {
+        stage_sum[t & 1][wave][c] = cs0;
+        stage_sum[t & 1][wave][32 + c] = cs1;
+      }
     };
-    if (lag) pass2(std::true_type());
-    else pass2(std::false_type());
-    k += ntile;
-    __syncthreads();
-    if (ntile >= 2) fold(ntile - 2);
-    fold(ntile - 1);
+    for (int t = 0; t < ntile; t += 2, k += 2) {
+      p2(t, stage0, stage1);
+      p2(t + 1, stage1, stage0);
+    }
     if (sw + 1 < nsw) {
       if constexpr (QPRE) {
 #pragma unroll
@@ -527,6 +478,8 @@ __global__ __launch_bounds__(64 * SEL_WAVES) void k_select(
       }
     }
   }
+  __syncthreads();
+  fold(ntile - 1);
   __syncthreads();
   topk_radix<SEL_WAVES>(sig, M, topk, sel + ((int64_t)h * M + b) * topk, hist, bcast, wcnt, tid);
 }
@@ -951,7 +904,7 @@ hipError_t run_select(const ssa_plan_s* p, int H, int topk, float sl2, const voi
   using T = typename Tr<DT>::T;
   const int Mp = (int)pooled_rows(p->M);
   const size_t shm = (size_t)Mp * sizeof(float);
-  hipLaunchKernelGGL((k_select<DT, D>), dim3(xcd_grid(p->M, H)), dim3(64 * SEL_WAVES), shm, s,
+  hipLaunchKernelGGL((k_select<DT, D>), dim3((unsigned)(p->M * H)), dim3(64 * SEL_WAVES), shm, s,
                      (const T*)q, (const T*)w.pooled, p->perm, p->blk_off, p->lpt, (int)p->M, Mp, H,
                      p->n, sl2, topk, (T*)w.oc, sel, w.lse, w.obr);
   return hipGetLastError();
