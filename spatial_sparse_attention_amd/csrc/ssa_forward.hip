@@ -23,6 +23,7 @@
 // planes whose sum reproduces the fp32 value, so the scores that decide the top-k
 // carry fp32-level error.
 #include <hip/hip_runtime.h>
+#include <algorithm>
 #include <type_traits>
 #include "ssa_internal.h"
 #include "ssa_mfma.h"
@@ -36,100 +37,119 @@ constexpr int ATT_WAVES = 4;      // selected/window: waves per workgroup, 32 qu
 constexpr int ATT_ROWS = 32 * ATT_WAVES;
 
 // ------------------------------------------------------------------ pooling
-// One workgroup per (block, head).  ktil[h,b] = mean_{i in b} K[i,h] @ Wk ; same for V.  Writes the fp32
-// pooled key split into NSPLIT dtype planes and the pooled value (transposed) in the
-// per-(head, 64-block tile) stage layout, plus the row-major pooled value; padding
-// blocks (b >= M) and key-row padding are zero.
+// One workgroup per (block, group of hg heads), blocks longest first: ktil[h,b] =
+// mean_{i in b} K[i,h] @ Wk, vtil likewise.  Each token row of the block is read whole for the
+// group's heads (hg * D contiguous elements of K and of V): thread t owns the 16-byte columns
+// t, t + POOL_NT, ... of the [K | V] row pair, so a column sum needs no exchange, and POOL_U
+// rows are in flight per thread.  The means go to LDS and are projected by Wk, Wv with fp32
+// dot products.  Writes the fp32 pooled key split into NSPLIT dtype planes and the pooled
+// value (transposed) in the per-(head, 64-block tile) stage layout, plus the row-major pooled
+// value; padding blocks (b >= M) and row padding are zero.
+constexpr int POOL_NT = 512, POOL_CPT = 2, POOL_U = 16;
+
 template <int DT, int D>
-__global__ __launch_bounds__(256) void k_pool(
+__global__ __launch_bounds__(POOL_NT) void k_pool(
     const typename Tr<DT>::T* __restrict__ kin, const typename Tr<DT>::T* __restrict__ vin,
     const typename Tr<DT>::T* __restrict__ wk, const typename Tr<DT>::T* __restrict__ wv,
-    const int32_t* __restrict__ perm, const int32_t* __restrict__ blk_off, int M, int Mp, int H,
+    const int32_t* __restrict__ perm, const int32_t* __restrict__ blk_off,
+    const int32_t* __restrict__ lpt, int M, int Mp, int H, int hg,
     typename Tr<DT>::T* __restrict__ pooled, typename Tr<DT>::T* __restrict__ pooled_v) {
   using C = Cfg<DT, D>;
   using T = typename Tr<DT>::T;
-  constexpr int NS = C::NS, VEC = C::EPC, CH = C::CPR, RSUB = 256 / CH;
-  constexpr int U = 4;  // rows in flight per thread
-  __shared__ float redk[RSUB * D], redv[RSUB * D], kbar[D], vbar[D];
-  int b, h;
-  xcd_split(blockIdx.x, H, b, h);  // a block's heads share the rows' cache lines
-  if (b >= Mp) return;
+  constexpr int NS = C::NS, EPC = C::EPC;
+  extern __shared__ float bar[];  // [2][hg * D]: K means, then V means
+  const int nhg = (H + hg - 1) / hg;
+  const int unit = blockIdx.x / nhg, h0 = (blockIdx.x % nhg) * hg;
+  const int hn = min(hg, H - h0);
   const int tid = threadIdx.x;
-  T* stg = pooled + ((int64_t)h * (Mp / C::PT) + b / C::PT) * C::STAGE;
-  T* krow = stg + (b % C::PT) * C::KROW;          // plane s at + s * KPLANE
-  T* vtcol = stg + NS * C::KPLANE + (b % C::PT);  // column dv at + dv * VTROW
-  T* vrow = pooled_v + ((int64_t)h * Mp + b) * C::VROW;
-  for (int j = (b >= M ? 0 : D) + tid; j < C::KROW; j += 256)
-    for (int s = 0; s < NS; ++s) krow[s * C::KPLANE + j] = (T)0.f;
-  if (b >= M) {
-    for (int j = tid; j < D; j += 256) {
-      vtcol[j * C::VTROW] = (T)0.f;
-      vrow[j] = (T)0.f;
+  const int b = unit < M ? lpt[unit] : unit;  // padding blocks M..Mp-1 follow the real ones
+  auto stage_of = [&](int h) { return pooled + ((int64_t)h * (Mp / C::PT) + b / C::PT) * C::STAGE; };
+  if (b >= M) {  // zero padding block
+    for (int j = tid; j < hn * D; j += POOL_NT) {
+      const int h = h0 + j / D, c = j % D;
+      T* stg = stage_of(h);
+      for (int s = 0; s < NS; ++s) stg[s * C::KPLANE + (b % C::PT) * C::KROW + c] = (T)0.f;
+      stg[NS * C::KPLANE + c * C::VTROW + (b % C::PT)] = (T)0.f;
+      pooled_v[((int64_t)h * Mp + b) * C::VROW + c] = (T)0.f;
+    }
+    for (int j = tid; j < hn * (C::KROW - D); j += POOL_NT) {
+      const int h = h0 + j / (C::KROW - D), c = D + j % (C::KROW - D);
+      for (int s = 0; s < NS; ++s) stage_of(h)[s * C::KPLANE + (b % C::PT) * C::KROW + c] = (T)0.f;
     }
     return;
   }
   const int r0 = blk_off[b], r1 = blk_off[b + 1];
-  const int sub = tid / CH, ch = tid % CH;
-  if (sub < RSUB) {
-    float ak[VEC], av[VEC];
-    for (int e = 0; e < VEC; ++e) ak[e] = av[e] = 0.f;
-    for (int r = r0 + sub; r < r1; r += U * RSUB) {
-      uint4 kb[U], vb[U];
+  const int cols = hn * D / EPC;  // 16-byte columns per tensor
+  float acc[POOL_CPT][EPC];
+  int col[POOL_CPT];
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int rr = r + u * RSUB;
-        if (rr < r1) {
-          const int64_t base = ((int64_t)perm[rr] * H + h) * D + ch * VEC;
-          kb[u] = *reinterpret_cast<const uint4*>(kin + base);
-          vb[u] = *reinterpret_cast<const uint4*>(vin + base);
-        } else {
-          kb[u] = vb[u] = make_uint4(0, 0, 0, 0);
-        }
-      }
+  for (int m = 0; m < POOL_CPT; ++m) {
+    col[m] = tid + m * POOL_NT;
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const T* kp = reinterpret_cast<const T*>(&kb[u]);
-        const T* vp = reinterpret_cast<const T*>(&vb[u]);
+    for (int e = 0; e < EPC; ++e) acc[m][e] = 0.f;
+  }
+  const int64_t rowlen = (int64_t)H * D;
+  for (int r = r0; r < r1; r += POOL_U) {
+    uint4 buf[POOL_U][POOL_CPT];
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) {
-          ak[e] += Tr<DT>::up(kp[e]);
-          av[e] += Tr<DT>::up(vp[e]);
-        }
+    for (int u = 0; u < POOL_U; ++u) {
+      const int rr = r + u < r1 ? r + u : r;  // past the block: reload row r, not summed
+      const int64_t base = (int64_t)perm[rr] * rowlen + (int64_t)h0 * D;
+#pragma unroll
+      for (int m = 0; m < POOL_CPT; ++m) {
+        const bool on = col[m] < 2 * cols;
+        const int cc = col[m] < cols ? col[m] : (on ? col[m] - cols : 0);  // K columns, then V
+        const T* src = (col[m] < cols ? kin : vin) + base + (int64_t)cc * EPC;
+        buf[u][m] = on ? *reinterpret_cast<const uint4*>(src) : make_uint4(0, 0, 0, 0);
       }
     }
-    for (int e = 0; e < VEC; ++e) {
-      redk[sub * D + ch * VEC + e] = ak[e];
-      redv[sub * D + ch * VEC + e] = av[e];
+#pragma unroll
+    for (int u = 0; u < POOL_U; ++u) {
+      if (r + u < r1) {
+#pragma unroll
+        for (int m = 0; m < POOL_CPT; ++m) {
+          const T* x = reinterpret_cast<const T*>(&buf[u][m]);
+#pragma unroll
+          for (int e = 0; e < EPC; ++e) acc[m][e] += Tr<DT>::up(x[e]);
+        }
+      }
     }
   }
-  __syncthreads();
   const float inv = 1.f / (float)(r1 - r0);
-  for (int j = tid; j < 2 * D; j += 256) {
-    const float* red = j < D ? redk : redv;
-    const int c = j < D ? j : j - D;
-    float s = 0.f;
-    for (int u = 0; u < RSUB; ++u) s += red[u * D + c];
-    (j < D ? kbar : vbar)[c] = s * inv;
-  }
+#pragma unroll
+  for (int m = 0; m < POOL_CPT; ++m)
+    if (col[m] < 2 * cols) {
+      const int kv = col[m] < cols ? 0 : 1, cc = kv ? col[m] - cols : col[m];
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) bar[kv * hn * D + cc * EPC + e] = acc[m][e] * inv;
+    }
   __syncthreads();
-  for (int j = tid; j < 2 * D; j += 256) {
-    const bool isk = j < D;
-    const int c = isk ? j : j - D;
-    const T* W = isk ? wk : wv;
-    const float* xb = isk ? kbar : vbar;
-    float acc = 0.f;
-    for (int i = 0; i < D; ++i) acc += xb[i] * Tr<DT>::up(W[(int64_t)i * D + c]);
-    if (isk) {
-      float rem = acc;
+  for (int j = tid; j < 2 * hn * D; j += POOL_NT) {
+    const int kv = j / (hn * D), hh = (j % (hn * D)) / D, c = j % D;
+    const T* W = kv ? wv : wk;
+    const float* xb = bar + kv * hn * D + hh * D;
+    float s0 = 0.f, s1 = 0.f;
+#pragma unroll 8
+    for (int i = 0; i < D; i += 2) {
+      s0 += xb[i] * Tr<DT>::up(W[i * D + c]);
+      s1 += xb[i + 1] * Tr<DT>::up(W[(i + 1) * D + c]);
+    }
+    const float val = s0 + s1;
+    const int h = h0 + hh;
+    T* stg = stage_of(h);
+    if (kv == 0) {
+      float rem = val;
       for (int s = 0; s < NS; ++s) {
         const T part = Tr<DT>::cvt(rem);
-        krow[s * C::KPLANE + c] = part;
+        stg[s * C::KPLANE + (b % C::PT) * C::KROW + c] = part;
         rem -= Tr<DT>::up(part);
       }
+      if (c < C::KROW - D)
+        for (int s = 0; s < NS; ++s) stg[s * C::KPLANE + (b % C::PT) * C::KROW + D + c] = (T)0.f;
     } else {
-      const T val = Tr<DT>::cvt(acc);
-      vtcol[c * C::VTROW] = val;
-      vrow[c] = val;
+      const T v = Tr<DT>::cvt(val);
+      stg[NS * C::KPLANE + c * C::VTROW + (b % C::PT)] = v;
+      pooled_v[((int64_t)h * Mp + b) * C::VROW + c] = v;
     }
   }
 }
@@ -892,9 +912,13 @@ hipError_t run_pool(const ssa_plan_s* p, int H, const void* k, const void* v, co
                     const void* wv, const FwdWs& w, hipStream_t s) {
   using T = typename Tr<DT>::T;
   const int Mp = (int)pooled_rows(p->M);
-  hipLaunchKernelGGL((k_pool<DT, D>), dim3(xcd_grid(Mp, H)), dim3(256), 0, s, (const T*)k, (const T*)v,
-                     (const T*)wk, (const T*)wv, p->perm, p->blk_off, (int)p->M, Mp, H, (T*)w.pooled,
-                     (T*)w.pooled_v);
+  // heads per workgroup: the group's columns fit POOL_CPT per thread, its means the LDS
+  const int hg = std::max(1, std::min(H, POOL_NT * POOL_CPT * Cfg<DT, D>::EPC / (2 * D)));
+  const int nhg = (H + hg - 1) / hg;
+  const size_t shm = (size_t)2 * hg * D * sizeof(float);
+  hipLaunchKernelGGL((k_pool<DT, D>), dim3((unsigned)(Mp * nhg)), dim3(POOL_NT), shm, s, (const T*)k,
+                     (const T*)v, (const T*)wk, (const T*)wv, p->perm, p->blk_off, p->lpt, (int)p->M,
+                     Mp, H, hg, (T*)w.pooled, (T*)w.pooled_v);
   return hipGetLastError();
 }
 
