@@ -31,6 +31,7 @@ size_t fwd_carve(Carver& c, const ssa_plan_s* p, ssa_dtype dt, int H, int d, int
   t.pooled_v = c.take<char>((size_t)H * Mp * vrow_of(dt, d) * es);
   t.oc = c.take<char>((size_t)H * n1 * d * es);
   t.sel = c.take<int32_t>((size_t)H * (p->M > 0 ? p->M : 1) * topk);
+  t.sigma = split_topk(p->M, H) ? c.take<float>((size_t)H * (p->M > 0 ? p->M : 1) * Mp) : nullptr;
   t.lse = nullptr;
   t.obr = nullptr;
   if (save) {

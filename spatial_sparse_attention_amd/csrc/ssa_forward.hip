@@ -315,27 +315,40 @@ __device__ void topk_radix(const float* sig, int M, int topk, int32_t* __restric
   for (int t = keff + tid; t < topk; t += NTH) out[t] = -1;
 }
 
-// One workgroup per (query block, head), longest blocks first; each wave owns a tile of 32
-// query rows, and the workgroup sweeps the block 32 * SEL_WAVES rows at a time.  Per sweep,
-// pass 1 streams every pooled stage (online softmax: compressed output and lse) and pass 2
-// streams the key planes again (importance column sums).  The stages of all passes and
-// sweeps form one stream, double buffered: step k's copy is issued at step k - 1.
+// One workgroup per (query block, head), longest blocks first; the workgroup sweeps the block
+// 32 * SEL_WAVES rows at a time.
+//  Pass 1 (query-stationary): each wave owns a tile of 32 query rows and streams every pooled
+//  stage through two LDS buffers (online softmax: compressed output and lse); stage t + 1's
+//  copy is issued at step t.
+//  Pass 2 (key-stationary): the sweep's queries and lse go to LDS (the stage buffers); the
+//  (32-key tile, 32-query tile) pairs, key-tile major, are split into equal contiguous ranges,
+//  one per wave, so a wave keeps a key tile's fragments in registers while it walks query
+//  tiles, and column-sums the probabilities.  A key tile whose pairs lie in one wave's range
+//  goes straight into sigma; the ends of ranges are folded in wave order, so every sum is in
+//  a fixed order.
 template <int DT, int D>
 __global__ __launch_bounds__(64 * SEL_WAVES) void k_select(
     const typename Tr<DT>::T* __restrict__ q, const typename Tr<DT>::T* __restrict__ pooled,
     const int32_t* __restrict__ perm, const int32_t* __restrict__ blk_off,
     const int32_t* __restrict__ lpt, int M, int Mp, int H, int64_t N, float sl2, int topk,
     typename Tr<DT>::T* __restrict__ oc, int32_t* __restrict__ sel, float* __restrict__ lse_save,
-    float* __restrict__ oc_save) {
+    float* __restrict__ oc_save, float* __restrict__ sigma_out) {
   using C = Cfg<DT, D>;
   using T = typename Tr<DT>::T;
   using F = typename Tr<DT>::frag;
   constexpr int NS = C::NS;
   constexpr int ROWS = 32 * SEL_WAVES;
+  // queries of a sweep in LDS for pass 2, half in each stage buffer: row stride QROW
+  constexpr int QROW = sizeof(T) == 2 ? D + 8 : D;
+  static_assert(ROWS / 2 * QROW <= C::STAGE, "half the sweep's queries fit a stage buffer");
   __shared__ __attribute__((aligned(1024))) T stage0[C::STAGE];
   __shared__ __attribute__((aligned(1024))) T stage1[C::STAGE];
-  __shared__ float stage_sum[2][SEL_WAVES][64];
+  auto qtile = [&](int u) __attribute__((always_inline)) {  // query tile u (32 rows) in LDS
+    return (u < SEL_WAVES / 2 ? stage0 : stage1) + (u % (SEL_WAVES / 2)) * 32 * QROW;
+  };
   __shared__ float lse_lds[ROWS];
+  __shared__ float bpart[SEL_WAVES][2][32];  // column sums of a range's first / last key tile
+  __shared__ int32_t bkt[SEL_WAVES][2];
   __shared__ uint32_t hist[256];
   __shared__ uint32_t bcast[2];
   __shared__ uint32_t wcnt[2][SEL_WAVES];
@@ -347,49 +360,39 @@ __global__ __launch_bounds__(64 * SEL_WAVES) void k_select(
   const int b = lpt[blockIdx.x / H];
   const int r0 = blk_off[b], rows = blk_off[b + 1] - r0;
   const int ntile = Mp / C::PT;
+  const int nkt = (M + KT - 1) / KT;  // 32-key tiles holding real blocks
   const int nsw = (rows + ROWS - 1) / ROWS;
-  const int nstep = nsw * 2 * ntile;
   const T* pstage = pooled + (int64_t)h * ntile * C::STAGE;
-  constexpr int NCH1 = C::STAGE * sizeof(T) / 16, NCH2 = NS * C::KPLANE * sizeof(T) / 16;
-  auto issue = [&](int k, T* dst) {  // copy of step k's stage
-    const int pos = k % (2 * ntile);
-    const int t = pos < ntile ? pos : pos - ntile;
-    dma_contiguous<SEL_WAVES>(dst, pstage + (int64_t)t * C::STAGE, pos < ntile ? NCH1 : NCH2, wave, lane);
+  constexpr int NCH1 = C::STAGE * sizeof(T) / 16;
+  auto issue = [&](int t, T* dst) __attribute__((always_inline)) {
+    dma_contiguous<SEL_WAVES>(dst, pstage + (int64_t)t * C::STAGE, NCH1, wave, lane);
   };
   issue(0, stage0);
   for (int j = tid; j < Mp; j += 64 * SEL_WAVES) sig[j] = 0.f;
 
-  auto row_of = [&](int sw) { return sw * ROWS + wave * 32 + c; };
+  auto row_of = [&](int sw) __attribute__((always_inline)) { return sw * ROWS + wave * 32 + c; };
   F qf[C::NKS];
   {
     const int my_row = row_of(0);
     load_q<DT, D>(qf, q + ((int64_t)(my_row < rows ? perm[r0 + my_row] : 0) * H + h) * D, my_row < rows, lane);
   }
 
-  auto fold = [&](int t) {  // sum the per-wave column sums of tile t into sigma (fixed order)
-    if (tid < C::PT) {
-      const int key = t * C::PT + tid;
-      float s = stage_sum[t & 1][0][tid];
-#pragma unroll
-      for (int w = 1; w < SEL_WAVES; ++w) s += stage_sum[t & 1][w][tid];
-      if (key < M) sig[key] += s;
-    }
-  };
-
-  int k = 0;  // step of the stage stream
   for (int sw = 0; sw < nsw; ++sw) {
     const int my_row = row_of(sw);
     const bool wave_active = sw * ROWS + wave * 32 < rows;
     const bool valid = my_row < rows;
+    if (sw > 0) {  // the previous sweep's pass 2 is done with the stage buffers
+      issue(0, stage0);
+      load_q<DT, D>(qf, q + ((int64_t)(valid ? perm[r0 + my_row] : 0) * H + h) * D, valid, lane);
+    }
 
     // ---------------- pass 1: online softmax over all pooled keys -> o_c, lse
     Online<C::NDV> st;
     st.init();
-    auto p1 = [&](int t, T* cur, T* nxt) {
+    auto p1 = [&](int t, T* cur, T* nxt) __attribute__((always_inline)) {
       dma_wait();
       __syncthreads();
-      if (k + (t & 1) + 1 < nstep) issue(k + (t & 1) + 1, nxt);
-      if (t == 0 && sw > 0) fold(ntile - 1);  // the previous sweep's last column sums
+      if (t + 1 < ntile) issue(t + 1, nxt);
       if (wave_active && t * C::PT < M) {
         ssa_f16v a0, a1;
         // value fragments read ahead for 16-bit types (fp32 ones would take 2*D registers)
@@ -422,7 +425,7 @@ __global__ __launch_bounds__(64 * SEL_WAVES) void k_select(
         }
       }
     };
-    for (int t = 0; t < ntile; t += 2, k += 2) {  // ntile is even: every pass starts on stage0
+    for (int t = 0; t < ntile; t += 2) {  // ntile is even
       p1(t, stage0, stage1);
       p1(t + 1, stage1, stage0);
     }
@@ -448,60 +451,129 @@ __global__ __launch_bounds__(64 * SEL_WAVES) void k_select(
       // rows past the block get +inf, so their probabilities in pass 2 are exactly zero
       if (g == 0) lse_lds[wave * 32 + c] = valid ? lse : INFINITY;
     }
+    __syncthreads();  // every wave is done with the stage buffers
+    {  // this wave's queries to LDS, in the layout the fragments were read in
+      T* qrow = qtile(wave) + c * QROW + g * C::KPL;
+#pragma unroll
+      for (int ks = 0; ks < C::NKS; ++ks) *reinterpret_cast<F*>(qrow + ks * C::KS) = qf[ks];
+    }
+    if (tid < SEL_WAVES * 2) bkt[tid / 2][tid % 2] = -1;
     __syncthreads();
 
-    // ---------------- pass 2: importance column sums (S layout)
-    float lrow[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) lrow[r] = lse_lds[wave * 32 + res_row(r, g)];
-    // next sweep's queries, loaded under pass 2 where the registers allow
-    constexpr bool QPRE = D * sizeof(T) <= 192;
-    F qn[C::NKS];
-    if (QPRE && sw + 1 < nsw) {
-      const int nrow = row_of(sw + 1);
-      load_q<DT, D>(qn, q + ((int64_t)(nrow < rows ? perm[r0 + nrow] : 0) * H + h) * D, nrow < rows, lane);
-    }
-    auto p2 = [&](int t, T* cur, T* nxt) {
-      dma_wait();
-      __syncthreads();
-      if (k + (t & 1) + 1 < nstep) issue(k + (t & 1) + 1, nxt);
-      if (t > 0) fold(t - 1);
-      float cs0 = 0.f, cs1 = 0.f;
-      if (wave_active && t * C::PT < M) {
-        ssa_f16v a0, a1;
-        stage_scores<DT, D, false, false>(cur + (lane & 31) * C::KROW + (lane >> 5) * C::KPL, qf,
-                                          a0, a1, nullptr, nullptr, lane);
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          cs0 += fast_exp2(__builtin_fmaf(a0[r], sl2, -lrow[r]));
-          cs1 += fast_exp2(__builtin_fmaf(a1[r], sl2, -lrow[r]));
-        }
-        cs0 = xor32_sum(cs0);
-        cs1 = xor32_sum(cs1);
-      }
-      if (g == 0) {
-        stage_sum[t & 1][wave][c] = cs0;
-        stage_sum[t & 1][wave][32 + c] = cs1;
-      }
-    };
-    for (int t = 0; t < ntile; t += 2, k += 2) {
-      p2(t, stage0, stage1);
-      p2(t + 1, stage1, stage0);
-    }
-    if (sw + 1 < nsw) {
-      if constexpr (QPRE) {
-#pragma unroll
-        for (int i = 0; i < C::NKS; ++i) qf[i] = qn[i];
+    // ---------------- pass 2: importance column sums, key-stationary
+    const int nq = (min(rows - sw * ROWS, ROWS) + 31) / 32;  // query tiles of this sweep
+    const int npair = nkt * nq;
+    const int pa = (int)((int64_t)npair * wave / SEL_WAVES), pb = (int)((int64_t)npair * (wave + 1) / SEL_WAVES);
+    F kf[C::NS][C::NKS];
+    float cs = 0.f;
+    int kt_cur = -1;
+    auto flush = [&](int p_end) __attribute__((always_inline)) {  // column sums of key tile kt_cur
+      const float tot = xor32_sum(cs);
+      const bool first = kt_cur * nq < pa, last = (kt_cur + 1) * nq > p_end;
+      const int key = kt_cur * KT + c;
+      if (!first && !last) {  // the whole tile in this range
+        if (g == 0 && key < M) sig[key] += tot;
       } else {
-        const int nrow = row_of(sw + 1);
-        load_q<DT, D>(qf, q + ((int64_t)(nrow < rows ? perm[r0 + nrow] : 0) * H + h) * D, nrow < rows, lane);
+        const int slot = first ? 0 : 1;  // a range within one tile uses slot 0
+        if (g == 0) bpart[wave][slot][c] = tot;
+        if (lane == 0) bkt[wave][slot] = kt_cur;
       }
+      cs = 0.f;
+    };
+#pragma unroll 1
+    for (int p = pa; p < pb; ++p) {
+      const int kt = p / nq, u = p % nq;
+      if (kt != kt_cur) {
+        if (kt_cur >= 0) flush(pb);
+        kt_cur = kt;
+        const T* krow = pstage + (int64_t)(kt / 2) * C::STAGE + ((kt % 2) * KT + (lane & 31)) * C::KROW +
+                        (lane >> 5) * C::KPL;
+#pragma unroll
+        for (int s2 = 0; s2 < C::NS; ++s2)
+#pragma unroll
+          for (int ks = 0; ks < C::NKS; ++ks) kf[s2][ks] = load_frag<DT>(krow + s2 * C::KPLANE + ks * C::KS);
+      }
+      const T* qrow = qtile(u) + (lane & 31) * QROW + (lane >> 5) * C::KPL;
+      ssa_f16v acc = zero16();
+#pragma unroll
+      for (int ks = 0; ks < C::NKS; ++ks) {
+        const F qq = load_frag<DT>(qrow + ks * C::KS);
+#pragma unroll
+        for (int s2 = 0; s2 < C::NS; ++s2) acc = Tr<DT>::mma(qq, kf[s2][ks], acc);
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        cs += fast_exp2(__builtin_fmaf(acc[r], sl2, -lse_lds[u * 32 + res_row(r, g)]));
+    }
+    if (kt_cur >= 0) flush(pb);
+    __syncthreads();
+    if (tid < KT) {  // range ends, in wave order
+      for (int w = 0; w < SEL_WAVES; ++w)
+        for (int sl = 0; sl < 2; ++sl) {
+          const int kt = bkt[w][sl];
+          if (kt >= 0 && kt * KT + tid < M) sig[kt * KT + tid] += bpart[w][sl][tid];
+        }
+    }
+    __syncthreads();  // sigma complete for this sweep; the stage buffers are free again
+  }
+  if (sigma_out) {  // the top-k kernel takes it from here
+    float* dst = sigma_out + ((int64_t)h * M + b) * Mp;
+    for (int j = tid; j < M; j += 64 * SEL_WAVES) dst[j] = sig[j];
+  } else {
+    topk_radix<SEL_WAVES>(sig, M, topk, sel + ((int64_t)h * M + b) * topk, hist, bcast, wcnt, tid);
+  }
+}
+
+// Top-k of one importance row per wave (rows of at most TOPK_SPLIT_MAX_M entries, held in
+// registers): the keff-th largest fp32 bit pattern T is found bit by bit from the top with
+// ballot counts, then the entries above T and the first ties at T are placed in id order.
+__global__ __launch_bounds__(256) void k_topk(const float* __restrict__ sigma, int M, int Mp,
+                                              int nrows, int topk, int32_t* __restrict__ sel) {
+  constexpr int MAXV = TOPK_SPLIT_MAX_M / 64;
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= nrows) return;  // uniform per wave
+  const float* src = sigma + (int64_t)row * Mp;
+  int32_t* out = sel + (int64_t)row * topk;
+  const int nv = (M + 63) / 64;
+  uint32_t u[MAXV];
+#pragma unroll
+  for (int i = 0; i < MAXV; ++i) u[i] = (i < nv && lane + 64 * i < M) ? __float_as_uint(src[lane + 64 * i]) : 0u;
+  auto ok = [&](int i) { return i < nv && lane + 64 * i < M; };
+  const int keff = min(topk, M);
+  const bool all = keff == M;
+  uint32_t T = 0;
+  if (!all) {
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t cand = T | (1u << bit);
+      int cnt = 0;
+#pragma unroll
+      for (int i = 0; i < MAXV; ++i)
+        if (i < nv) cnt += __builtin_popcountll(__builtin_amdgcn_ballot_w64(ok(i) && u[i] >= cand));
+      if (cnt >= keff) T = cand;
     }
   }
-  __syncthreads();
-  fold(ntile - 1);
-  __syncthreads();
-  topk_radix<SEL_WAVES>(sig, M, topk, sel + ((int64_t)h * M + b) * topk, hist, bcast, wcnt, tid);
+  int ngt = 0;
+  if (!all) {
+#pragma unroll
+    for (int i = 0; i < MAXV; ++i)
+      if (i < nv) ngt += __builtin_popcountll(__builtin_amdgcn_ballot_w64(ok(i) && u[i] > T));
+  }
+  const int need = keff - ngt;  // ties at T to take, lowest ids first
+  int run_gt = 0, run_eq = 0;
+#pragma unroll
+  for (int i = 0; i < MAXV; ++i) {
+    if (i >= nv) break;
+    const bool gt = ok(i) && (all || u[i] > T);
+    const bool eq = ok(i) && !all && u[i] == T;
+    const uint64_t bg = __builtin_amdgcn_ballot_w64(gt), be = __builtin_amdgcn_ballot_w64(eq);
+    const int lg = run_gt + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bg >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bg, 0u));
+    const int le = run_eq + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(be >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)be, 0u));
+    if (gt || (eq && le < need)) out[lg + min(le, need)] = lane + 64 * i;
+    run_gt += __builtin_popcountll(bg);
+    run_eq += __builtin_popcountll(be);
+  }
+  for (int t = keff + lane; t < topk; t += 64) out[t] = -1;
 }
 
 // ------------------------------------------------------------------ selected + window + combine
@@ -930,7 +1002,12 @@ hipError_t run_select(const ssa_plan_s* p, int H, int topk, float sl2, const voi
   const size_t shm = (size_t)Mp * sizeof(float);
   hipLaunchKernelGGL((k_select<DT, D>), dim3((unsigned)(p->M * H)), dim3(64 * SEL_WAVES), shm, s,
                      (const T*)q, (const T*)w.pooled, p->perm, p->blk_off, p->lpt, (int)p->M, Mp, H,
-                     p->n, sl2, topk, (T*)w.oc, sel, w.lse, w.obr);
+                     p->n, sl2, topk, (T*)w.oc, sel, w.lse, w.obr, w.sigma);
+  if (w.sigma) {
+    const int nrows = (int)(p->M * H);
+    hipLaunchKernelGGL(k_topk, dim3((unsigned)((nrows + 3) / 4)), dim3(256), 0, s, w.sigma, (int)p->M,
+                       Mp, nrows, topk, sel);
+  }
   return hipGetLastError();
 }
 

@@ -59,6 +59,12 @@ static inline bool buffer_addressable(int64_t bytes) { return bytes <= (int64_t)
 // Pooled blocks per head as stored: a whole, even number of 64-block stages, so that every
 // pass of the selection starts on the same stage buffer.
 static inline int64_t pooled_rows(int64_t M) { return ((M > 0 ? M : 1) + 127) / 128 * 128; }
+// The top-k runs as its own kernel (one wave per (head, query block) row) when the importance
+// rows are short and their buffer small; else at the end of the selection kernel.
+constexpr int TOPK_SPLIT_MAX_M = 1024;
+static inline bool split_topk(int64_t M, int64_t H) {
+  return M <= TOPK_SPLIT_MAX_M && H * M * pooled_rows(M) * 4 <= ((int64_t)256 << 20);
+}
 static inline int krow_of(ssa_dtype dt, int d) { return d + (dt == SSA_F32 ? 4 : 8); }
 static inline int vrow_of(ssa_dtype dt, int d) { return d + (dt == SSA_F32 ? 8 : 16); }
 static inline int vtrow_of(ssa_dtype dt) { return dt == SSA_F32 ? POOL_TILE + 1 : POOL_TILE + 4; }
@@ -72,6 +78,7 @@ struct FwdWs {
   void* pooled_v;    // [H][Mp][vrow] dtype: pooled values, row-major
   void* oc;          // [N][H][d] compressed-branch output (dtype)
   int32_t* sel;      // [H][M][topk]
+  float* sigma;      // [H][M][Mp] importance scores when the top-k runs as its own kernel, else null
   // saved for the backward (save_for_bwd only; else null)
   float* lse;        // [3][H][N] per-branch log2-sum-exp2 of the scaled scores
   float* obr;        // [3][N][H][d] the three branch outputs in fp32 (compressed, selected, window)
