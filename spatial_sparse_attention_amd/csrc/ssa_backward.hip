@@ -63,35 +63,44 @@ size_t carve(Carver& c, const ssa_plan_s* p, int H, int d, int topk, BwdWs* w) {
 }
 
 // ------------------------------------------------------------------ prep
-// One thread per (sorted row r, head h): dgates and D for the three branches.
+// dgates and D for the three branches.  A group of GS lanes per (sorted row r, head h): lane
+// j of the group reads the j-th 16-byte chunk of dO's head row (and the matching fp32 chunks
+// of the three saved branch outputs), so a group reads contiguous rows; the dot products are
+// finished with shuffles inside the group.
 template <int DT, int D>
 __global__ __launch_bounds__(256) void k_bwd_prep(
     const typename Tr<DT>::T* __restrict__ dout, const typename Tr<DT>::T* __restrict__ gates,
     const float* __restrict__ obr, const int32_t* __restrict__ perm, int64_t N, int H,
     float* __restrict__ dgates, float* __restrict__ Dsave) {
   using T = typename Tr<DT>::T;
-  constexpr int EPC = 16 / sizeof(T);
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (idx >= N * H) return;
-  const int64_t r = idx / H;
-  const int h = (int)(idx % H);
-  const int64_t t = perm[r];
-  const T* dO = dout + (t * H + h) * D;
+  constexpr int EPC = 16 / sizeof(T), CPR = D / EPC;
+  constexpr int GS = CPR <= 16 ? 16 : (CPR <= 32 ? 32 : 64);  // lanes per head row
+  static_assert(CPR <= GS, "one lane group per head row");
+  const int64_t idx = ((int64_t)blockIdx.x * 256 + threadIdx.x) / GS;
+  const int j = threadIdx.x & (GS - 1);
+  const bool live = idx < N * H;
+  const int64_t r = live ? idx / H : 0;
+  const int h = live ? (int)(idx % H) : 0;
+  const int64_t t = live ? perm[r] : 0;
   float acc[3] = {0.f, 0.f, 0.f};
-  for (int c0 = 0; c0 < D; c0 += EPC) {
-    const uint4 a = *reinterpret_cast<const uint4*>(dO + c0);
+  if (live && j < CPR) {
+    const uint4 a = *reinterpret_cast<const uint4*>(dout + (t * H + h) * D + j * EPC);
     const T* ae = reinterpret_cast<const T*>(&a);
 #pragma unroll
     for (int x = 0; x < 3; ++x) {
-      const float* o = obr + (((int64_t)x * N + r) * H + h) * D + c0;
+      const float* o = obr + (((int64_t)x * N + r) * H + h) * D + j * EPC;
 #pragma unroll
       for (int e = 0; e < EPC; ++e) acc[x] += Tr<DT>::up(ae[e]) * o[e];
     }
   }
 #pragma unroll
-  for (int x = 0; x < 3; ++x) {
-    dgates[(t * H + h) * 3 + x] = acc[x];
-    Dsave[((int64_t)x * H + h) * N + r] = Tr<DT>::up(gates[(t * H + h) * 3 + x]) * acc[x];
+  for (int x = 0; x < 3; ++x)
+#pragma unroll
+    for (int off = GS / 2; off > 0; off >>= 1) acc[x] += __shfl_xor(acc[x], off, GS);
+  if (live && j < 3) {
+    const float v = j == 0 ? acc[0] : (j == 1 ? acc[1] : acc[2]);
+    dgates[(t * H + h) * 3 + j] = v;
+    Dsave[((int64_t)j * H + h) * N + r] = Tr<DT>::up(gates[(t * H + h) * 3 + j]) * v;
   }
 }
 
@@ -541,7 +550,8 @@ hipError_t run_backward(const ssa_plan_s* p, int H, int topk, float scale, const
   const int64_t N = p->n;
   const float sl2 = scale * 1.4426950408889634f;
   const int nchunk = (p->max_rows + BROWS - 1) / BROWS;
-  hipLaunchKernelGGL((k_bwd_prep<DT, D>), dim3((unsigned)((N * H + 255) / 256)), dim3(256), 0, s,
+  constexpr int PREP_GS = 16 / sizeof(T) * 16 >= D ? 16 : (16 / sizeof(T) * 32 >= D ? 32 : 64);
+  hipLaunchKernelGGL((k_bwd_prep<DT, D>), dim3((unsigned)((N * H * PREP_GS + 255) / 256)), dim3(256), 0, s,
                      (const T*)dout, (const T*)gates, fw.obr, p->perm, N, H, dgates, w.D);
   const bool buf = buffer_addressable(N * H * D * (int64_t)sizeof(T));
   if (buf)
