@@ -14,7 +14,8 @@
 // key-side sum runs in a fixed order); dk/dv of the selected and window branches
 // (key-major, S layout so the queries are the MFMA contraction index); the compressed
 // key side over query chunks; the pooling backward, which folds the chunk partials in
-// order and adds them into dK, dV.  No atomics: results are bitwise reproducible.
+// order into one dK, dV term per (block, head), added by the dk/dv kernel as it writes.  No
+// atomics: results are bitwise reproducible.
 #include <hip/hip_runtime.h>
 #include "ssa_internal.h"
 #include "ssa_mfma.h"
@@ -32,6 +33,7 @@ struct BwdWs {
   int32_t *va, *vb, *rank, *hist, *part;
   int32_t* inv_off;            // [H*M + 1]
   float *part_k, *part_v;      // [qch][H][Mp][d] compressed key-side partials
+  float* ukv;                  // [2][H][Mp][d] per-block dK, dV terms of the compressed branch
   int qch;
 };
 
@@ -58,6 +60,7 @@ size_t carve(Carver& c, const ssa_plan_s* p, int H, int d, int topk, BwdWs* w) {
   t.inv_off = c.take<int32_t>((int64_t)H * M + 1);
   t.part_k = c.take<float>((int64_t)t.qch * H * Mp * d);
   t.part_v = c.take<float>((int64_t)t.qch * H * Mp * d);
+  t.ukv = c.take<float>((int64_t)2 * H * Mp * d);
   if (w) *w = t;
   return c.off;
 }
@@ -365,7 +368,7 @@ __global__ __launch_bounds__(64 * BW) void k_bwd_dkdv(
     const int32_t* __restrict__ cell_off, const int32_t* __restrict__ cell_blk,
     const int32_t* __restrict__ lpt, const int32_t* __restrict__ inv_off,
     const int32_t* __restrict__ inv_q, int M, int H, int nchunk, int64_t N, float scale, float sl2,
-    float* __restrict__ dk, float* __restrict__ dv) {
+    const float* __restrict__ ukv, int Mp, float* __restrict__ dk, float* __restrict__ dv) {
   using C = Cfg<DT, D>;
   using T = typename Tr<DT>::T;
   constexpr int NTH = 64 * BW;
@@ -416,7 +419,16 @@ __global__ __launch_bounds__(64 * BW) void k_bwd_dkdv(
       }
     }
   }
-  // write: lane holds column 32j + c of keys res_row(r, g)
+  // write, with the block's compressed-branch terms: lane holds column 32j + c of keys
+  // res_row(r, g)
+  const float* uk = ukv + ((int64_t)h * Mp + b) * D;
+  const float* uv = ukv + (((int64_t)H + h) * Mp + b) * D;
+  float ukc[C::NDV], uvc[C::NDV];
+#pragma unroll
+  for (int j = 0; j < C::NDV; ++j) {
+    ukc[j] = uk[32 * j + c];
+    uvc[j] = uv[32 * j + c];
+  }
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     const int kr = kbase + res_row(r, g);
@@ -424,8 +436,8 @@ __global__ __launch_bounds__(64 * BW) void k_bwd_dkdv(
       const int64_t t = perm[r0 + kr];
 #pragma unroll
       for (int j = 0; j < C::NDV; ++j) {
-        dk[(t * H + h) * D + 32 * j + c] = scale * S.dk[j][r];
-        dv[(t * H + h) * D + 32 * j + c] = S.dv[j][r];
+        dk[(t * H + h) * D + 32 * j + c] = scale * S.dk[j][r] + ukc[j];
+        dv[(t * H + h) * D + 32 * j + c] = S.dv[j][r] + uvc[j];
       }
     }
   }
@@ -500,15 +512,14 @@ __global__ __launch_bounds__(64 * BW) void k_bwd_cmp(
 }
 
 // ------------------------------------------------------------------ pooling backward
-// grid (M, H): sum the chunk partials in order, map through W^T and the mean, add into dK,
-// dV of every token of the block.
+// grid (M, H): sum the chunk partials in order and map them through W^T and the mean: the
+// compressed branch's dK, dV term shared by every token of the block.
 template <int DT, int D>
 __global__ __launch_bounds__(256) void k_bwd_pool(
     const typename Tr<DT>::T* __restrict__ wk, const typename Tr<DT>::T* __restrict__ wv,
     const float* __restrict__ part_k, const float* __restrict__ part_v,
-    const int32_t* __restrict__ perm, const int32_t* __restrict__ blk_off, int Mp, int H, int qch,
-    float* __restrict__ dk, float* __restrict__ dv) {
-  __shared__ float gk[D], gv[D], uk[D], uv[D];
+    const int32_t* __restrict__ blk_off, int Mp, int H, int qch, float* __restrict__ ukv) {
+  __shared__ float gk[D], gv[D];
   const int b = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
   for (int j = tid; j < 2 * D; j += 256) {
     const float* src = j < D ? part_k : part_v;
@@ -518,8 +529,7 @@ __global__ __launch_bounds__(256) void k_bwd_pool(
     (j < D ? gk : gv)[c] = s;
   }
   __syncthreads();
-  const int r0 = blk_off[b], r1 = blk_off[b + 1];
-  const float inv = 1.f / (float)(r1 - r0);
+  const float inv = 1.f / (float)(blk_off[b + 1] - blk_off[b]);
   for (int j = tid; j < 2 * D; j += 256) {
     const bool isk = j < D;
     const int i = isk ? j : j - D;
@@ -527,14 +537,7 @@ __global__ __launch_bounds__(256) void k_bwd_pool(
     const float* gsrc = isk ? gk : gv;
     float s = 0.f;
     for (int c = 0; c < D; ++c) s += Tr<DT>::up(W[(int64_t)i * D + c]) * gsrc[c];
-    (isk ? uk : uv)[i] = s * inv;
-  }
-  __syncthreads();
-  for (int e = tid; e < (r1 - r0) * D; e += 256) {
-    const int64_t t = perm[r0 + e / D];
-    const int i = e % D;
-    dk[(t * H + h) * D + i] += uk[i];
-    dv[(t * H + h) * D + i] += uv[i];
+    ukv[(((int64_t)(isk ? 0 : 1) * H + h) * Mp + b) * D + i] = s * inv;
   }
 }
 
@@ -575,16 +578,6 @@ hipError_t run_backward(const ssa_plan_s* p, int H, int topk, float scale, const
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_inv_off, dim3((unsigned)((H * M + 1 + 255) / 256)), dim3(256), 0, s, ka, E,
                      H * M, w.inv_off);
-  if (buf)
-    hipLaunchKernelGGL((k_bwd_dkdv<DT, D, true>), dim3(xcd_grid(M, (int64_t)H * nchunk)), dim3(64 * BW), 0, s,
-                     (const T*)q, (const T*)k, (const T*)v, (const T*)gates, (const T*)dout, fw.lse,
-                     w.D, p->perm, p->blk_off, p->blk_cell, p->cell_off, p->cell_blk, p->lpt,
-                     w.inv_off, va, M, H, nchunk, N, scale, sl2, dk, dv);
-  else
-    hipLaunchKernelGGL((k_bwd_dkdv<DT, D, false>), dim3(xcd_grid(M, (int64_t)H * nchunk)), dim3(64 * BW), 0, s,
-                     (const T*)q, (const T*)k, (const T*)v, (const T*)gates, (const T*)dout, fw.lse,
-                     w.D, p->perm, p->blk_off, p->blk_cell, p->cell_off, p->cell_blk, p->lpt,
-                     w.inv_off, va, M, H, nchunk, N, scale, sl2, dk, dv);
   const int groups = (Mp / KT + BW - 1) / BW;
   if (buf)
     hipLaunchKernelGGL((k_bwd_cmp<DT, D, true>), dim3((unsigned)(groups * H * w.qch)), dim3(64 * BW), 0, s,
@@ -597,7 +590,17 @@ hipError_t run_backward(const ssa_plan_s* p, int H, int topk, float scale, const
                      (const T*)fw.pooled_v, fw.lse, w.D,
                      p->perm, Mp, H, w.qch, N, scale, sl2, w.part_k, w.part_v);
   hipLaunchKernelGGL((k_bwd_pool<DT, D>), dim3(M, H), dim3(256), 0, s, (const T*)wk, (const T*)wv,
-                     w.part_k, w.part_v, p->perm, p->blk_off, Mp, H, w.qch, dk, dv);
+                     w.part_k, w.part_v, p->blk_off, Mp, H, w.qch, w.ukv);
+  if (buf)
+    hipLaunchKernelGGL((k_bwd_dkdv<DT, D, true>), dim3(xcd_grid(M, (int64_t)H * nchunk)), dim3(64 * BW), 0, s,
+                     (const T*)q, (const T*)k, (const T*)v, (const T*)gates, (const T*)dout, fw.lse,
+                     w.D, p->perm, p->blk_off, p->blk_cell, p->cell_off, p->cell_blk, p->lpt,
+                     w.inv_off, va, M, H, nchunk, N, scale, sl2, w.ukv, Mp, dk, dv);
+  else
+    hipLaunchKernelGGL((k_bwd_dkdv<DT, D, false>), dim3(xcd_grid(M, (int64_t)H * nchunk)), dim3(64 * BW), 0, s,
+                     (const T*)q, (const T*)k, (const T*)v, (const T*)gates, (const T*)dout, fw.lse,
+                     w.D, p->perm, p->blk_off, p->blk_cell, p->cell_off, p->cell_blk, p->lpt,
+                     w.inv_off, va, M, H, nchunk, N, scale, sl2, w.ukv, Mp, dk, dv);
   return hipGetLastError();
 }
 
