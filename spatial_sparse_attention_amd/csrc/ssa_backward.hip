@@ -297,10 +297,16 @@ __global__ void k_inv_off(const uint32_t* __restrict__ key, int64_t E, int nkeys
 }
 
 // ------------------------------------------------------------------ key side (S layout)
-// A wave owns 32 keys: their K and V rows are B operands held in registers.  For each tile
-// of 32 queries (Q rows in the stage's first area, dO rows in the second):
-//   S = Q K^T, P = exp2(S sl2 - lse_q), dP = dO V^T, dS = P o (g_q dP - D_q),
-//   dv += (g_q P)^T dO,  dk += dS^T Q.
+// A wave owns 32 keys: their K and V rows are B operands held in registers.  The queries
+// that attend to the key block (the blocks of its window cell, then the query blocks whose
+// selection holds it) form one stream of 32-row tiles: a stage holds the tile's Q rows (at
+// 0, row stride KROW) and dO rows (at VOFF, row stride VROW); the stream runs through three
+// stage buffers like the forward's key stream (copy of tile t + 2 issued at step t), with
+// each query's sorted row, token and (lse, g, D) of its branch staged per segment in LDS.
+// Per tile: S = Q K^T, P = exp2(S sl2 - lse), dP = dO V^T, dS = P o (g dP - D),
+// dv += (g P)^T dO, dk += dS^T Q.
+constexpr int QSEG = 1024;  // query rows staged per segment
+
 template <int DT, int D>
 struct KvState {
   using C = Cfg<DT, D>;
@@ -371,12 +377,19 @@ __global__ __launch_bounds__(64 * BW) void k_bwd_dkdv(
     const float* __restrict__ ukv, int Mp, float* __restrict__ dk, float* __restrict__ dv) {
   using C = Cfg<DT, D>;
   using T = typename Tr<DT>::T;
+  using F = typename Tr<DT>::frag;
+  using TC = TileCopy<DT, D, BW>;
   constexpr int NTH = 64 * BW;
-  __shared__ __attribute__((aligned(1024))) T stage[C::KTILE + C::VTILE];
-  __shared__ float4 info[KT];
+  __shared__ __attribute__((aligned(1024))) T buf0[TC::ELEMS];
+  __shared__ __attribute__((aligned(1024))) T buf1[TC::ELEMS];
+  __shared__ __attribute__((aligned(1024))) T buf2[TC::ELEMS];
   __shared__ int32_t pre[NTH + 1];
   __shared__ int32_t lst_off[NTH];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 5, c = lane & 31;
+  __shared__ int32_t ent_x[NTH];
+  __shared__ int32_t qtok[QSEG];
+  __shared__ float4 qinf[QSEG];
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, c = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   int unit, member;
   xcd_split(blockIdx.x, nchunk * H, unit, member);
   if (unit >= M) return;
@@ -386,6 +399,7 @@ __global__ __launch_bounds__(64 * BW) void k_bwd_dkdv(
   if (chunk * BROWS >= rows) return;
   const int kbase = chunk * BROWS + wave * 32;
   const bool kvalid = kbase + c < rows;
+  const bool wave_active = kbase < rows;
   const int64_t ktok = perm[r0 + (kvalid ? kbase + c : 0)];
   KvState<DT, D> S;
   load_q<DT, D>(S.kf, kin + (ktok * H + h) * D, kvalid, lane);
@@ -393,29 +407,114 @@ __global__ __launch_bounds__(64 * BW) void k_bwd_dkdv(
 #pragma unroll
   for (int j = 0; j < C::NDV; ++j) S.dk[j] = S.dv[j] = zero16();
   const int cell = blk_cell[b];
-  const int dt16 = DT == DT_F32 ? 0 : (DT == DT_F16 ? 1 : 2);
-  Gather<DT, D, BW> ga;
-  ga.init(wave, lane);
-#pragma unroll 1
-  for (int x = 2; x >= 1; --x) {
-    // window: the query blocks of this block's cell; selected: the query blocks whose
-    // selection holds this block
-    const int32_t* blist = x == 2 ? cell_blk + cell_off[cell] : inv_q + inv_off[h * M + b];
-    const int nlist = x == 2 ? cell_off[cell + 1] - cell_off[cell]
-                             : inv_off[h * M + b + 1] - inv_off[h * M + b];
-    const float* lse = lse3 + ((int64_t)x * H + h) * N;
-    const float* Dx = D3 + ((int64_t)x * H + h) * N;
-    for (int l0 = 0; l0 < nlist; l0 += NTH) {
-      const int L = min(NTH, nlist - l0);
-      const int total = list_prefix<NTH>(blist + l0, L, blk_off, pre, lst_off);
-      for (int k0 = 0; k0 < total; k0 += KT) {
+  const int c0 = cell_off[cell], nwin = cell_off[cell + 1] - c0;
+  const int i0 = inv_off[h * M + b], ninv = inv_off[h * M + b + 1] - i0;
+  const int nent = nwin + ninv;  // window query blocks, then the selecting ones
+  TC tc;
+  tc.init(wave, lane);
+
+  for (int e0 = 0; e0 < nent; e0 += NTH) {
+    const int L = min(NTH, nent - e0);
+    __syncthreads();  // the previous chunk's tables and stages are no longer read
+    int sz = 0;
+    if (tid < L) {
+      const int e = e0 + tid;
+      const int qb = e < nwin ? cell_blk[c0 + e] : inv_q[i0 + e - nwin];
+      lst_off[tid] = blk_off[qb];
+      sz = blk_off[qb + 1] - blk_off[qb];
+      ent_x[tid] = e < nwin ? 2 : 1;
+    }
+    pre[tid + 1] = sz;
+    if (tid == 0) pre[0] = 0;
+    __syncthreads();
+    if (L > 1) {
+      for (int off = 1; off < NTH; off <<= 1) {
+        const int t = (tid + 1 > off) ? pre[tid + 1 - off] : 0;
         __syncthreads();
-        ga.lookup(k0, total, L, pre, lst_off, perm);
-        ga.template issue<BUF>(stage, q, dout, H, h, wave);
-        fill_info(info, k0, total, L, pre, lst_off, lse, Dx, gates, dt16, perm, H, h, x);
-        dma_wait();
+        pre[tid + 1] += t;
         __syncthreads();
-        S.tile(stage, info, sl2, lane);
+      }
+    }
+    const int total = pre[L];
+    for (int s0 = 0; s0 < total; s0 += QSEG) {
+      const int n = min(QSEG, total - s0);
+      __syncthreads();  // the previous segment's tiles have been read
+      for (int j = tid; j < n; j += NTH) {
+        const int pos = s0 + j;
+        int lo = 0, hi = L - 1;  // last entry starting at or before the position
+        while (lo < hi) {
+          const int mid = (lo + hi + 1) >> 1;
+          if (pre[mid] <= pos) lo = mid; else hi = mid - 1;
+        }
+        const int r = lst_off[lo] + (pos - pre[lo]);
+        const int x = ent_x[lo];
+        const int64_t t = perm[r];
+        qtok[j] = (int32_t)t;
+        qinf[j] = make_float4(lse3[((int64_t)x * H + h) * N + r], Tr<DT>::up(gates[(t * H + h) * 3 + x]),
+                              D3[((int64_t)x * H + h) * N + r], 0.f);
+      }
+      __syncthreads();
+      const int ntile = (n + KT - 1) / KT;
+      auto step = [&](int t, T* cur, T* nx2) __attribute__((always_inline)) {
+        if (t + 1 < ntile) vm_wait<TC::NI>();  // tile t landed; tile t + 1 may be in flight
+        else vm_wait<0>();
+        __syncthreads();
+        ssa_f16v ds = zero16(), pg = zero16();
+        if (wave_active) {
+          ssa_f16v sv = zero16(), dp = zero16();
+          const T* qrow = cur + (lane & 31) * C::KROW + g * C::KPL;
+          const T* orow = cur + TC::VOFF + (lane & 31) * C::VROW + g * C::KPL;
+#pragma unroll
+          for (int ks = 0; ks < C::NKS; ++ks) {
+            sv = Tr<DT>::mma(load_frag<DT>(qrow + ks * C::KS), S.kf[ks], sv);
+            dp = Tr<DT>::mma(load_frag<DT>(orow + ks * C::KS), S.vf[ks], dp);
+          }
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int j = t * KT + res_row(r, g);
+            const float4 in = j < n ? qinf[j] : make_float4(INFINITY, 0.f, 0.f, 0.f);
+            const float pr = fast_exp2(__builtin_fmaf(sv[r], sl2, -in.x));
+            ds[r] = pr * (in.y * dp[r] - in.z);
+            pg[r] = in.y * pr;
+          }
+        }
+        // transposed fragments of the tile, read before tile t + 2's copy is issued (the
+        // transpose reads carry no alias information)
+        F qt[C::PK][C::NDV], ot[C::PK][C::NDV];
+        if (wave_active) {
+#pragma unroll
+          for (int ks = 0; ks < C::PK; ++ks)
+#pragma unroll
+            for (int jd = 0; jd < C::NDV; ++jd) {
+              qt[ks][jd] = tr_frag<DT, C::KROW>(cur, ks, jd, lane);
+              ot[ks][jd] = tr_frag<DT, C::VROW>(cur + TC::VOFF, ks, jd, lane);
+            }
+        }
+        if (t + 2 < ntile) tc.template issue<BUF>(nx2, q, dout, H, h, wave);
+        if (t + 3 < ntile) tc.fetch(qtok, (t + 3) * KT, n);
+        if (wave_active) {
+#pragma unroll
+          for (int ks = 0; ks < C::PK; ++ks) {
+            const F pf = p_frag<DT>(pg, ks), sf = p_frag<DT>(ds, ks);
+#pragma unroll
+            for (int jd = 0; jd < C::NDV; ++jd) {
+              S.dv[jd] = Tr<DT>::mma(pf, ot[ks][jd], S.dv[jd]);
+              S.dk[jd] = Tr<DT>::mma(sf, qt[ks][jd], S.dk[jd]);
+            }
+          }
+        }
+      };
+      tc.fetch(qtok, 0, n);
+      tc.template issue<BUF>(buf0, q, dout, H, h, wave);
+      if (ntile > 1) {
+        tc.fetch(qtok, KT, n);
+        tc.template issue<BUF>(buf1, q, dout, H, h, wave);
+      }
+      if (ntile > 2) tc.fetch(qtok, 2 * KT, n);
+      for (int t = 0; t < ntile; t += 3) {
+        step(t, buf0, buf2);
+        if (t + 1 < ntile) step(t + 1, buf1, buf0);
+        if (t + 2 < ntile) step(t + 2, buf2, buf1);
       }
     }
   }

@@ -372,4 +372,71 @@ struct Gather {
   }
 };
 
+// Copies of one gathered 32-key tile from the caller's K and V into LDS, 16 bytes per lane
+// and instruction: the K rows ([32][KROW]) at the start of the stage, the V rows ([32][VROW])
+// at VOFF.  K and V copies never share an instruction, so each instruction reads through one
+// (wave-uniform) buffer descriptor, and every wave issues the same NI instructions per tile,
+// so a wave can wait for all but its newest tile's copies with one count.  Lanes on a row's
+// padding chunk, past a part's chunks or past the tile copy a valid chunk into a spot nobody
+// reads (the row padding, the gap before VOFF, or the buffer's tail).
+template <int DT, int D, int NW>
+struct TileCopy {
+  using C = Cfg<DT, D>;
+  using T = typename Tr<DT>::T;
+  static constexpr int KRC = C::KCH / KT, VRC = C::VCH / KT;  // chunks per padded row
+  static constexpr int KI = (C::KCH + 63) / 64, VI = (C::VCH + 63) / 64;  // instructions
+  static constexpr int NI = (KI + VI + NW - 1) / NW;
+  static constexpr int ELEMS = NI * NW * 64 * C::EPC;  // stage buffer, tail included
+  static constexpr int VOFF = KI * 64 * C::EPC;         // V rows' offset in the stage
+  int32_t row[NI];   // tile row (key) of each copy
+  int32_t goff[NI];  // element offset inside the token's head row
+  int32_t tok[NI];
+  __device__ inline void init(int wave, int lane) {
+#pragma unroll
+    for (int m = 0; m < NI; ++m) {
+      const int i = wave + m * NW;
+      const bool isk = i < KI;
+      const int p = (isk ? i : i - KI) * 64 + lane;
+      const int rr = isk ? p / KRC : p / VRC, ch = isk ? p % KRC : p % VRC;
+      const bool ok = (isk ? p < C::KCH : (i < KI + VI && p < C::VCH)) && ch < C::CPR;
+      row[m] = ok ? rr : 0;
+      goff[m] = ok ? ch * C::EPC : 0;
+    }
+  }
+  // tokens of the tile starting at key k0 of a staged segment of n keys (rows past n: key 0)
+  __device__ inline void fetch(const int32_t* keytok, int k0, int n) {
+#pragma unroll
+    for (int m = 0; m < NI; ++m) {
+      const int j = k0 + row[m];
+      tok[m] = keytok[j < n ? j : 0];
+    }
+  }
+  template <bool BUF>
+  __device__ inline void issue(T* stage, const T* kin, const T* vin, int H, int h, int wave) const {
+    if constexpr (BUF) {
+      const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(kin + h * D), 0, -1, 0x00020000);
+      const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(vin + h * D), 0, -1, 0x00020000);
+#pragma unroll
+      for (int m = 0; m < NI; ++m) {
+        const uint32_t off = ((uint32_t)tok[m] * (uint32_t)(H * D) + (uint32_t)goff[m]) * (uint32_t)sizeof(T);
+        lds_void_t* dst = (lds_void_t*)(stage + (wave + m * NW) * 64 * C::EPC);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(wave + m * NW < KI ? rk : rv, dst, 16, off, 0, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int m = 0; m < NI; ++m) {
+        const T* src = (wave + m * NW < KI ? kin : vin) + ((int64_t)tok[m] * H + h) * D + goff[m];
+        dma16(src, stage + (wave + m * NW) * 64 * C::EPC);
+      }
+    }
+  }
+};
+
+// Waits until at most N of this wave's vector memory operations are outstanding.
+template <int N>
+__device__ inline void vm_wait() {
+  static_assert(N >= 0 && N < 16, "vmcnt immediate");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+}
+
 }  // namespace ssa_dev
