@@ -364,6 +364,105 @@ __device__ inline void fill_info(float4* info, int k0, int total, int L, const i
   info[j] = v;
 }
 
+// The query stream of a key-side kernel: `total` positions, position -> (sorted row r,
+// branch x) by row_of.  Per segment of up to QSEG positions the tokens and (lse, g, D) of
+// the branch go to LDS, then the segment's 32-row tiles (Q rows at 0, dO rows at VOFF) run
+// through three stage buffers with copies two tiles ahead; per tile
+//   S = Q K^T, P = exp2(S sl2 - lse), dP = dO V^T, dS = P o (g dP - D),
+//   dv += (g P)^T dO, dk += dS^T Q
+// (dS and g P with the queries as the contraction index, read back from registers).
+template <int DT, int D, bool BUF, typename RowOf>
+__device__ inline void kv_stream(KvState<DT, D>& S, TileCopy<DT, D, BW>& tc, typename Tr<DT>::T* buf0,
+                                 typename Tr<DT>::T* buf1, typename Tr<DT>::T* buf2, int32_t* qtok,
+                                 float4* qinf, int total, const typename Tr<DT>::T* __restrict__ q,
+                                 const typename Tr<DT>::T* __restrict__ dout,
+                                 const typename Tr<DT>::T* __restrict__ gates,
+                                 const float* __restrict__ lse3, const float* __restrict__ D3,
+                                 const int32_t* __restrict__ perm, int H, int h, int64_t N, float sl2,
+                                 bool wave_active, int wave, int lane, RowOf row_of) {
+  using C = Cfg<DT, D>;
+  using T = typename Tr<DT>::T;
+  using F = typename Tr<DT>::frag;
+  using TC = TileCopy<DT, D, BW>;
+  constexpr int NTH = 64 * BW;
+  const int tid = threadIdx.x, g = lane >> 5;
+  for (int s0 = 0; s0 < total; s0 += QSEG) {
+    const int n = min(QSEG, total - s0);
+    __syncthreads();  // the previous segment's tiles have been read
+    for (int j = tid; j < n; j += NTH) {
+      int r, x;
+      row_of(s0 + j, r, x);
+      const int64_t t = perm[r];
+      qtok[j] = (int32_t)t;
+      qinf[j] = make_float4(lse3[((int64_t)x * H + h) * N + r], Tr<DT>::up(gates[(t * H + h) * 3 + x]),
+                            D3[((int64_t)x * H + h) * N + r], 0.f);
+    }
+    __syncthreads();
+      const int ntile = (n + KT - 1) / KT;
+      auto step = [&](int t, T* cur, T* nx2) __attribute__((always_inline)) {
+        if (t + 1 < ntile) vm_wait<TC::NI>();  // tile t landed; tile t + 1 may be in flight
+        else vm_wait<0>();
+        __syncthreads();
+        ssa_f16v ds = zero16(), pg = zero16();
+        if (wave_active) {
+          ssa_f16v sv = zero16(), dp = zero16();
+          const T* qrow = cur + (lane & 31) * C::KROW + g * C::KPL;
+          const T* orow = cur + TC::VOFF + (lane & 31) * C::VROW + g * C::KPL;
+#pragma unroll
+          for (int ks = 0; ks < C::NKS; ++ks) {
+            sv = Tr<DT>::mma(load_frag<DT>(qrow + ks * C::KS), S.kf[ks], sv);
+            dp = Tr<DT>::mma(load_frag<DT>(orow + ks * C::KS), S.vf[ks], dp);
+          }
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int j = t * KT + res_row(r, g);
+            const float4 in = j < n ? qinf[j] : make_float4(INFINITY, 0.f, 0.f, 0.f);
+            const float pr = fast_exp2(__builtin_fmaf(sv[r], sl2, -in.x));
+            ds[r] = pr * (in.y * dp[r] - in.z);
+            pg[r] = in.y * pr;
+          }
+        }
+        // transposed fragments of the tile, read before tile t + 2's copy is issued (the
+        // transpose reads carry no alias information)
+        F qt[C::PK][C::NDV], ot[C::PK][C::NDV];
+        if (wave_active) {
+#pragma unroll
+          for (int ks = 0; ks < C::PK; ++ks)
+#pragma unroll
+            for (int jd = 0; jd < C::NDV; ++jd) {
+              qt[ks][jd] = tr_frag<DT, C::KROW>(cur, ks, jd, lane);
+              ot[ks][jd] = tr_frag<DT, C::VROW>(cur + TC::VOFF, ks, jd, lane);
+            }
+        }
+        if (t + 2 < ntile) tc.template issue<BUF>(nx2, q, dout, H, h, wave);
+        if (t + 3 < ntile) tc.fetch(qtok, (t + 3) * KT, n);
+        if (wave_active) {
+#pragma unroll
+          for (int ks = 0; ks < C::PK; ++ks) {
+            const F pf = p_frag<DT>(pg, ks), sf = p_frag<DT>(ds, ks);
+#pragma unroll
+            for (int jd = 0; jd < C::NDV; ++jd) {
+              S.dv[jd] = Tr<DT>::mma(pf, ot[ks][jd], S.dv[jd]);
+              S.dk[jd] = Tr<DT>::mma(sf, qt[ks][jd], S.dk[jd]);
+            }
+          }
+        }
+      };
+      tc.fetch(qtok, 0, n);
+      tc.template issue<BUF>(buf0, q, dout, H, h, wave);
+      if (ntile > 1) {
+        tc.fetch(qtok, KT, n);
+        tc.template issue<BUF>(buf1, q, dout, H, h, wave);
+      }
+      if (ntile > 2) tc.fetch(qtok, 2 * KT, n);
+      for (int t = 0; t < ntile; t += 3) {
+        step(t, buf0, buf2);
+        if (t + 1 < ntile) step(t + 1, buf1, buf0);
+        if (t + 2 < ntile) step(t + 2, buf2, buf1);
+      }
+    }
+}
+
 template <int DT, int D, bool BUF>
 __global__ __launch_bounds__(64 * BW) void k_bwd_dkdv(
     const typename Tr<DT>::T* __restrict__ q, const typename Tr<DT>::T* __restrict__ kin,
@@ -436,87 +535,17 @@ __global__ __launch_bounds__(64 * BW) void k_bwd_dkdv(
       }
     }
     const int total = pre[L];
-    for (int s0 = 0; s0 < total; s0 += QSEG) {
-      const int n = min(QSEG, total - s0);
-      __syncthreads();  // the previous segment's tiles have been read
-      for (int j = tid; j < n; j += NTH) {
-        const int pos = s0 + j;
-        int lo = 0, hi = L - 1;  // last entry starting at or before the position
-        while (lo < hi) {
-          const int mid = (lo + hi + 1) >> 1;
-          if (pre[mid] <= pos) lo = mid; else hi = mid - 1;
-        }
-        const int r = lst_off[lo] + (pos - pre[lo]);
-        const int x = ent_x[lo];
-        const int64_t t = perm[r];
-        qtok[j] = (int32_t)t;
-        qinf[j] = make_float4(lse3[((int64_t)x * H + h) * N + r], Tr<DT>::up(gates[(t * H + h) * 3 + x]),
-                              D3[((int64_t)x * H + h) * N + r], 0.f);
-      }
-      __syncthreads();
-      const int ntile = (n + KT - 1) / KT;
-      auto step = [&](int t, T* cur, T* nx2) __attribute__((always_inline)) {
-        if (t + 1 < ntile) vm_wait<TC::NI>();  // tile t landed; tile t + 1 may be in flight
-        else vm_wait<0>();
-        __syncthreads();
-        ssa_f16v ds = zero16(), pg = zero16();
-        if (wave_active) {
-          ssa_f16v sv = zero16(), dp = zero16();
-          const T* qrow = cur + (lane & 31) * C::KROW + g * C::KPL;
-          const T* orow = cur + TC::VOFF + (lane & 31) * C::VROW + g * C::KPL;
-#pragma unroll
-          for (int ks = 0; ks < C::NKS; ++ks) {
-            sv = Tr<DT>::mma(load_frag<DT>(qrow + ks * C::KS), S.kf[ks], sv);
-            dp = Tr<DT>::mma(load_frag<DT>(orow + ks * C::KS), S.vf[ks], dp);
-          }
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int j = t * KT + res_row(r, g);
-            const float4 in = j < n ? qinf[j] : make_float4(INFINITY, 0.f, 0.f, 0.f);
-            const float pr = fast_exp2(__builtin_fmaf(sv[r], sl2, -in.x));
-            ds[r] = pr * (in.y * dp[r] - in.z);
-            pg[r] = in.y * pr;
-          }
-        }
-        // transposed fragments of the tile, read before tile t + 2's copy is issued (the
-        // transpose reads carry no alias information)
-        F qt[C::PK][C::NDV], ot[C::PK][C::NDV];
-        if (wave_active) {
-#pragma unroll
-          for (int ks = 0; ks < C::PK; ++ks)
-#pragma unroll
-            for (int jd = 0; jd < C::NDV; ++jd) {
-              qt[ks][jd] = tr_frag<DT, C::KROW>(cur, ks, jd, lane);
-              ot[ks][jd] = tr_frag<DT, C::VROW>(cur + TC::VOFF, ks, jd, lane);
-            }
-        }
-        if (t + 2 < ntile) tc.template issue<BUF>(nx2, q, dout, H, h, wave);
-        if (t + 3 < ntile) tc.fetch(qtok, (t + 3) * KT, n);
-        if (wave_active) {
-#pragma unroll
-          for (int ks = 0; ks < C::PK; ++ks) {
-            const F pf = p_frag<DT>(pg, ks), sf = p_frag<DT>(ds, ks);
-#pragma unroll
-            for (int jd = 0; jd < C::NDV; ++jd) {
-              S.dv[jd] = Tr<DT>::mma(pf, ot[ks][jd], S.dv[jd]);
-              S.dk[jd] = Tr<DT>::mma(sf, qt[ks][jd], S.dk[jd]);
-            }
-          }
-        }
-      };
-      tc.fetch(qtok, 0, n);
-      tc.template issue<BUF>(buf0, q, dout, H, h, wave);
-      if (ntile > 1) {
-        tc.fetch(qtok, KT, n);
-        tc.template issue<BUF>(buf1, q, dout, H, h, wave);
-      }
-      if (ntile > 2) tc.fetch(qtok, 2 * KT, n);
-      for (int t = 0; t < ntile; t += 3) {
-        step(t, buf0, buf2);
-        if (t + 1 < ntile) step(t + 1, buf1, buf0);
-        if (t + 2 < ntile) step(t + 2, buf2, buf1);
-      }
-    }
+    kv_stream<DT, D, BUF>(S, tc, buf0, buf1, buf2, qtok, qinf, total, q, dout, gates, lse3, D3, perm,
+                          H, h, N, sl2, wave_active, wave, lane,
+                          [&](int pos, int& r, int& x) __attribute__((always_inline)) {
+                            int lo = 0, hi = L - 1;  // last entry starting at or before pos
+                            while (lo < hi) {
+                              const int mid = (lo + hi + 1) >> 1;
+                              if (pre[mid] <= pos) lo = mid; else hi = mid - 1;
+                            }
+                            r = lst_off[lo] + (pos - pre[lo]);
+                            x = ent_x[lo];
+                          });
   }
   // write, with the block's compressed-branch terms: lane holds column 32j + c of keys
   // res_row(r, g)
@@ -543,24 +572,27 @@ __global__ __launch_bounds__(64 * BW) void k_bwd_dkdv(
 }
 
 // ------------------------------------------------------------------ compressed key side
-// Wave w of a workgroup owns pooled key tile blockIdx-group*BW + w; the workgroup walks the
-// sorted query rows of its chunk.  Partials per chunk: part[qc][h][key][d].
+// Wave w of a workgroup owns pooled key tile blockIdx-group*BW + w; the workgroup streams the
+// sorted query rows of its chunk (every query attends to every pooled key).  Partials per
+// chunk: part[qc][h][key][d].
 template <int DT, int D, bool BUF>
 __global__ __launch_bounds__(64 * BW) void k_bwd_cmp(
     const typename Tr<DT>::T* __restrict__ q, const typename Tr<DT>::T* __restrict__ gates,
     const typename Tr<DT>::T* __restrict__ dout, const typename Tr<DT>::T* __restrict__ pooled,
     const typename Tr<DT>::T* __restrict__ pooled_v, const float* __restrict__ lse3,
-    const float* __restrict__ D3, const int32_t* __restrict__ perm, int Mp, int H, int qch, int64_t N, float scale, float sl2, float* __restrict__ part_k,
-    float* __restrict__ part_v) {
+    const float* __restrict__ D3, const int32_t* __restrict__ perm, int Mp, int H, int qch, int64_t N,
+    float scale, float sl2, float* __restrict__ part_k, float* __restrict__ part_v) {
   using C = Cfg<DT, D>;
   using T = typename Tr<DT>::T;
-  __shared__ __attribute__((aligned(1024))) T stage[C::KTILE + C::VTILE];
-  __shared__ float4 info[KT];
-  __shared__ int32_t pre[2];
-  __shared__ int32_t lst_off[1];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 5, c = lane & 31;
+  using TC = TileCopy<DT, D, BW>;
+  __shared__ __attribute__((aligned(1024))) T buf0[TC::ELEMS];
+  __shared__ __attribute__((aligned(1024))) T buf1[TC::ELEMS];
+  __shared__ __attribute__((aligned(1024))) T buf2[TC::ELEMS];
+  __shared__ int32_t qtok[QSEG];
+  __shared__ float4 qinf[QSEG];
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, c = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int ntile = Mp / KT;
-  const int groups = (ntile + BW - 1) / BW;
   const int qc = blockIdx.x % qch;
   const int h = (blockIdx.x / qch) % H;
   const int kt = (blockIdx.x / (qch * H)) * BW + wave;
@@ -575,28 +607,15 @@ __global__ __launch_bounds__(64 * BW) void k_bwd_cmp(
   for (int j = 0; j < C::NDV; ++j) S.dk[j] = S.dv[j] = zero16();
   const int64_t qlen = (N + qch - 1) / qch;
   const int64_t q0 = qc * qlen, q1 = min(N, q0 + qlen);
-  if (tid == 0) {
-    pre[0] = 0;
-    pre[1] = (int)max((int64_t)0, q1 - q0);
-    lst_off[0] = (int)q0;
-  }
-  __syncthreads();
-  const int total = pre[1];
-  const int dt16 = DT == DT_F32 ? 0 : (DT == DT_F16 ? 1 : 2);
-  const float* lse = lse3 + (int64_t)h * N;
-  const float* Dx = D3 + (int64_t)h * N;
-  Gather<DT, D, BW> ga;
-  ga.init(wave, lane);
-  for (int k0 = 0; k0 < total; k0 += KT) {
-    __syncthreads();
-    ga.lookup(k0, total, 1, pre, lst_off, perm);
-    ga.template issue<BUF>(stage, q, dout, H, h, wave);
-    fill_info(info, k0, total, 1, pre, lst_off, lse, Dx, gates, dt16, perm, H, h, 0);
-    dma_wait();
-    __syncthreads();
-    if (ktv) S.tile(stage, info, sl2, lane);
-  }
-  (void)groups;
+  const int total = (int)max((int64_t)0, q1 - q0);
+  TC tc;
+  tc.init(wave, lane);
+  kv_stream<DT, D, BUF>(S, tc, buf0, buf1, buf2, qtok, qinf, total, q, dout, gates, lse3, D3, perm, H,
+                        h, N, sl2, ktv, wave, lane,
+                        [&](int pos, int& r, int& x) __attribute__((always_inline)) {
+                          r = (int)q0 + pos;
+                          x = 0;
+                        });
   if (ktv) {
     float* pk = part_k + (((int64_t)qc * H + h) * Mp + kt * KT) * D;
     float* pv = part_v + (((int64_t)qc * H + h) * Mp + kt * KT) * D;
