@@ -17,6 +17,7 @@
 // order into one dK, dV term per (block, head), added by the dk/dv kernel as it writes.  No
 // atomics: results are bitwise reproducible.
 #include <hip/hip_runtime.h>
+#include <algorithm>
 #include "ssa_internal.h"
 #include "ssa_mfma.h"
 #include "ssa_tiles.h"
@@ -24,8 +25,10 @@
 namespace {
 
 using namespace ssa_dev;
-constexpr int BW = 4;           // waves per workgroup
-constexpr int BROWS = 32 * BW;  // query rows (dq) or keys (dk/dv) per workgroup
+constexpr int BW = 4;           // waves per workgroup (dq, compressed key side)
+constexpr int BROWS = 32 * BW;  // query rows per dq workgroup
+constexpr int KW = 4;           // waves per dk/dv workgroup
+constexpr int KROWS = 32 * KW;  // keys per dk/dv workgroup
 
 struct BwdWs {
   float* D;                    // [3][H][N]
@@ -35,7 +38,23 @@ struct BwdWs {
   float *part_k, *part_v;      // [qch][H][Mp][d] compressed key-side partials
   float* ukv;                  // [2][H][Mp][d] per-block dK, dV terms of the compressed branch
   int qch;
+  // key-side schedule: (head, block) units in descending stream length, their work items
+  uint32_t *ska, *skb;         // [H*M] sort keys
+  int32_t *sva, *svb;          // [H*M] unit ids
+  int4* sinfo;                 // [H*M] per sorted unit: {unit, pieces, partial row offset, -}
+  int32_t* ioff;               // [H*M + 1] first item of each sorted unit
+  int4* items;                 // [item_cap] {unit, key chunk, piece, partial row offset or -1}
+  int32_t* xbase;              // [9] first item of each XCD's list, then the total
+  float* kpart;                // [KV_BUDGET rows][2][d] partial dK, dV of split units
+  int64_t item_cap;
 };
+
+// A key-side unit (head, key block) whose query stream has more than KV_EP query blocks
+// (window blocks, then the selecting query blocks) is split into pieces of KV_EP blocks,
+// while the partial sums of the pieces fit a fixed budget of key rows; the pieces' partial
+// dK, dV are summed in piece order by k_kv_reduce.
+constexpr int KV_EP = 8;
+inline int64_t kv_budget_rows(int d) { return (int64_t)(64 << 20) / (8 * d); }
 
 int cmp_chunks(int64_t Mp, int H) {
   const int64_t groups = (Mp / KT + BW - 1) / BW * H;
@@ -61,6 +80,19 @@ size_t carve(Carver& c, const ssa_plan_s* p, int H, int d, int topk, BwdWs* w) {
   t.part_k = c.take<float>((int64_t)t.qch * H * Mp * d);
   t.part_v = c.take<float>((int64_t)t.qch * H * Mp * d);
   t.ukv = c.take<float>((int64_t)2 * H * Mp * d);
+  const int64_t U = (int64_t)H * M;
+  const int64_t nch = ((p->max_rows > 0 ? p->max_rows : 1) + KROWS - 1) / KROWS;
+  t.ska = c.take<uint32_t>(U);
+  t.skb = c.take<uint32_t>(U);
+  t.sva = c.take<int32_t>(U);
+  t.svb = c.take<int32_t>(U);
+  t.sinfo = c.take<int4>(U);
+  t.ioff = c.take<int32_t>(U + 1);
+  // unsplit units give at most nch items each; split pieces at most one item per partial row
+  t.item_cap = U * nch + kv_budget_rows(d);
+  t.items = c.take<int4>(t.item_cap);
+  t.xbase = c.take<int32_t>(NXCD + 1);
+  t.kpart = c.take<float>(kv_budget_rows(d) * 2 * d);
   if (w) *w = t;
   return c.off;
 }
@@ -146,38 +178,89 @@ __device__ inline int set_row(int j, int L, const int32_t* pre, const int32_t* l
 }
 
 // ------------------------------------------------------------------ dq (query-major)
-// Per branch: tiles of keys; S^T = K Q^T, P^T from the saved lse, dP^T = V dO^T,
-// dS^T = P^T o (g dP^T - D), dq^T += K^T dS^T.  The stage holds the K tile ([32][KROW])
-// then the V tile ([32][VROW]).
+// A wave owns 32 query rows: their Q and dO rows are B operands held in registers.  Per
+// branch the keys form a stream of 32-key tiles -- the pooled keys, the selected blocks' keys,
+// the window cell's keys -- copied through NB stage buffers (K rows at 0, V rows at VOFF),
+// the copy of tile t + NB - 1 issued while tile t is in use.  Per tile, keys as rows:
+//   S^T = K Q^T, P^T = exp2(S^T sl2 - lse), dP^T = V dO^T, dS^T = P^T o (g dP^T - D),
+//   dq^T += K^T dS^T.
+constexpr int DSEG = 2048;  // gathered keys staged per segment
+
 template <int DT, int D>
 struct DqState {
   using C = Cfg<DT, D>;
   using F = typename Tr<DT>::frag;
   F qf[C::NKS], dof[C::NKS];
   ssa_f16v dq[C::NDV];
-  __device__ inline void tile(const typename Tr<DT>::T* st, int nvalid, float sl2, float lse,
-                              float gx, float Dx, int lane) {
-    const int g = lane >> 5;
-    ssa_f16v s = st_tile<DT, D>(st, qf, zero16(), lane);
-    // dP^T = V dO^T: the V tile rows are the A operand
-    ssa_f16v dp = zero16();
-    const typename Tr<DT>::T* vrow = st + C::KTILE + (lane & 31) * C::VROW + g * C::KPL;
-#pragma unroll
-    for (int ks = 0; ks < C::NKS; ++ks) dp = Tr<DT>::mma(load_frag<DT>(vrow + ks * C::KS), dof[ks], dp);
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float p = res_row(r, g) < nvalid ? fast_exp2(__builtin_fmaf(s[r], sl2, -lse)) : 0.f;
-      s[r] = p * (gx * dp[r] - Dx);
-    }
-#pragma unroll
-    for (int ks = 0; ks < C::PK; ++ks) {
-      const F sf = p_frag<DT>(s, ks);
-#pragma unroll
-      for (int j = 0; j < C::NDV; ++j)
-        dq[j] = Tr<DT>::mma(tr_frag<DT, C::KROW>(st, ks, j, lane), sf, dq[j]);
-    }
-  }
 };
+
+// One branch's tile stream of n keys; fetch(t) readies tile t's copy addresses, issue(buf)
+// starts that copy.
+template <int DT, int D, int NB, typename Fetch, typename Issue>
+__device__ inline void dq_stream(DqState<DT, D>& S, int n, float lse, float gx, float Dx, float sl2,
+                                 bool wave_active, typename Tr<DT>::T* const* bufs, int lane, Fetch fetch,
+                                 Issue issue) {
+  using C = Cfg<DT, D>;
+  using T = typename Tr<DT>::T;
+  using F = typename Tr<DT>::frag;
+  using TC = TileCopy<DT, D, BW>;
+  const int g = lane >> 5;
+  __syncthreads();  // the stage buffers' previous tiles have been read
+  tile_pipeline<NB, TC::NI>(
+      (n + KT - 1) / KT, bufs, fetch, issue,
+      [&](int t, const T* cur, auto&& next) __attribute__((always_inline)) {
+        ssa_f16v ds = zero16();
+        constexpr bool PRE = C::KPL != 1;
+        F kt[PRE ? C::PK : 1][C::NDV];
+        if (wave_active) {
+          ssa_f16v sv = zero16(), dp = zero16();
+          const T* krow = cur + (lane & 31) * C::KROW + g * C::KPL;
+          const T* vrow = cur + TC::VOFF + (lane & 31) * C::VROW + g * C::KPL;
+          F ka[C::NKS], va[C::NKS];  // all fragment reads before the first MFMA
+#pragma unroll
+          for (int ks = 0; ks < C::NKS; ++ks) {
+            ka[ks] = load_frag<DT>(krow + ks * C::KS);
+            va[ks] = load_frag<DT>(vrow + ks * C::KS);
+          }
+#pragma unroll
+          for (int ks = 0; ks < C::NKS; ++ks) {
+            sv = Tr<DT>::mma(ka[ks], S.qf[ks], sv);
+            dp = Tr<DT>::mma(va[ks], S.dof[ks], dp);
+          }
+          if constexpr (C::KPL != 1) {
+            __builtin_amdgcn_sched_group_barrier(0x100, 2 * C::NKS, 0);  // DS reads
+            __builtin_amdgcn_sched_group_barrier(0x008, 2 * C::NKS, 0);  // then MFMAs
+          }
+#pragma unroll
+          for (int r = 0; r < 16; ++r) ds[r] = fast_exp2(__builtin_fmaf(sv[r], sl2, -lse)) * (gx * dp[r] - Dx);
+          if ((t + 1) * KT > n) {  // keys past n (finite rows) get no weight
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+              if (t * KT + res_row(r, g) >= n) ds[r] = 0.f;
+          }
+          // 16-bit types: the K^T fragments are read before the next copy is issued (the
+          // transpose reads carry no alias information); fp32 reads them in place (too many
+          // registers) and issues the copy after its MFMAs
+          if constexpr (PRE) {
+#pragma unroll
+            for (int ks = 0; ks < C::PK; ++ks)
+#pragma unroll
+              for (int j = 0; j < C::NDV; ++j) kt[ks][j] = tr_frag<DT, C::KROW>(cur, ks, j, lane);
+          }
+        }
+        if constexpr (PRE) next();
+        if (wave_active) {
+#pragma unroll
+          for (int ks = 0; ks < C::PK; ++ks) {
+            const F sf = p_frag<DT>(ds, ks);
+#pragma unroll
+            for (int j = 0; j < C::NDV; ++j)
+              S.dq[j] = Tr<DT>::mma(PRE ? kt[ks][j] : tr_frag<DT, C::KROW>(cur, ks, j, lane), sf, S.dq[j]);
+          }
+        }
+        if constexpr (!PRE) next();
+      });
+}
 
 template <int DT, int D, bool BUF>
 __global__ __launch_bounds__(64 * BW) void k_bwd_dq(
@@ -192,12 +275,17 @@ __global__ __launch_bounds__(64 * BW) void k_bwd_dq(
     int nchunk, int64_t N, int topk, float scale, float sl2, float* __restrict__ dq) {
   using C = Cfg<DT, D>;
   using T = typename Tr<DT>::T;
+  using TC = TileCopy<DT, D, BW>;
   constexpr int NTH = 64 * BW;
-  __shared__ __attribute__((aligned(1024))) T stage[C::KTILE + C::VTILE];
+  // two workgroups per CU where the registers allow it
+  constexpr int NB = stage_depth<DT, D, BW>(LDS_BYTES / 2 - 2048, DSEG * 4 + (2 * NTH + 257) * 4);
+  SSA_STAGE_BUFFERS(T, TC::ELEMS, NB);
   __shared__ int32_t pre[NTH + 1];
   __shared__ int32_t lst_off[NTH];
   __shared__ int32_t sel_lds[256];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, g = lane >> 5, c = lane & 31;
+  __shared__ int32_t keytok[DSEG];
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, c = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   int unit, member;
   xcd_split(blockIdx.x, nchunk * H, unit, member);
   if (unit >= M) return;
@@ -205,14 +293,16 @@ __global__ __launch_bounds__(64 * BW) void k_bwd_dq(
   const int b = lpt[unit];
   const int r0 = blk_off[b], rows = blk_off[b + 1] - r0;
   if (chunk * BROWS >= rows) return;
-  int nsel = 0;
   const int32_t* srow = sel + ((int64_t)h * M + b) * topk;
-  for (int t = 0; t < topk; ++t) nsel += srow[t] >= 0;
-  for (int t = tid; t < nsel; t += NTH) sel_lds[t] = srow[t];
+  const int sb = tid < topk ? srow[tid] : -1;  // selected ids ascend, -1 padded at the end
+  if (sb >= 0) sel_lds[tid] = sb;
+  const int nsel = __syncthreads_count(sb >= 0);
   const int cell = blk_cell[b];
   const int cb0 = cell_off[cell], cb1 = cell_off[cell + 1];
 
-  const int my_row = chunk * BROWS + wave * 32 + c;
+  const int wbase = chunk * BROWS + wave * 32;
+  const bool wave_active = wbase < rows;
+  const int my_row = wbase + c;
   const bool valid = my_row < rows;
   const int64_t row = r0 + (valid ? my_row : 0);
   const int64_t tok = perm[row];
@@ -228,24 +318,23 @@ __global__ __launch_bounds__(64 * BW) void k_bwd_dq(
     lse[x] = lse3[((int64_t)x * H + h) * N + row];
     Dx[x] = valid ? D3[((int64_t)x * H + h) * N + row] : 0.f;
   }
+  TC tc;
+  tc.init(wave, lane);
 
-  // compressed branch, 32 pooled keys per tile: K = first (hi) pooled key plane of the
-  // 64-key stage, V = the row-major pooled values
-  const T* pst = pooled + (int64_t)h * (Mp / C::PT) * C::STAGE;
-  const T* pvh = pooled_v + (int64_t)h * Mp * C::VROW;
-  for (int t = 0; t * KT < M; ++t) {
-    __syncthreads();
-    const T* ksrc = pst + (int64_t)(t / 2) * C::STAGE + (t % 2) * KT * C::KROW;
-    const T* vsrc = pvh + (int64_t)t * KT * C::VROW;
-    dma_contiguous<BW>(stage, ksrc, C::KCH, wave, lane);
-    dma_contiguous<BW>(stage + C::KTILE, vsrc, C::VCH, wave, lane);
-    dma_wait();
-    __syncthreads();
-    S.tile(stage, min(KT, M - t * KT), sl2, lse[0], gx[0], Dx[0], lane);
+  // compressed branch: pooled key row r is row r % 64 of the first (hi) key plane of stage
+  // r / 64; pooled values are row-major.  Rows past M are zero.
+  {
+    const T* kb = pooled + (int64_t)h * (Mp / C::PT) * C::STAGE;
+    const T* vb = pooled_v + (int64_t)h * Mp * C::VROW;
+    dq_stream<DT, D, NB>(S, M, lse[0], gx[0], Dx[0], sl2, wave_active, bufs, lane,
+                     [&](int t) __attribute__((always_inline)) { tc.set_rows(t * KT); },
+                     [&](T* dst) __attribute__((always_inline)) {
+                       tc.template issue_rows<BUF>(
+                           dst, kb, vb, [](int r) { return (r / C::PT) * C::STAGE + (r % C::PT) * C::KROW; },
+                           [](int r) { return r * C::VROW; }, wave);
+                     });
   }
-  // selected and window branches: gathered key tiles
-  Gather<DT, D, BW> ga;
-  ga.init(wave, lane);
+  // selected and window branches: the list's blocks in order, staged DSEG keys at a time
 #pragma unroll 1
   for (int x = 1; x <= 2; ++x) {
     const int32_t* blist = x == 1 ? sel_lds : cell_blk + cb0;
@@ -253,13 +342,17 @@ __global__ __launch_bounds__(64 * BW) void k_bwd_dq(
     for (int l0 = 0; l0 < nlist; l0 += NTH) {
       const int L = min(NTH, nlist - l0);
       const int total = list_prefix<NTH>(blist + l0, L, blk_off, pre, lst_off);
-      for (int k0 = 0; k0 < total; k0 += KT) {
+      for (int ks0 = 0; ks0 < total; ks0 += DSEG) {
+        const int n = min(DSEG, total - ks0);
+        __syncthreads();  // the previous segment's tiles have been fetched
+        fill_tokens<DSEG / NTH, NTH>(keytok, n, [&](int j) { return set_row(ks0 + j, L, pre, lst_off); }, perm);
         __syncthreads();
-        ga.lookup(k0, total, L, pre, lst_off, perm);
-        ga.template issue<BUF>(stage, kin, vin, H, h, wave);
-        dma_wait();
-        __syncthreads();
-        S.tile(stage, min(KT, total - k0), sl2, lse[x], gx[x], Dx[x], lane);
+        dq_stream<DT, D, NB>(S, n, x == 1 ? lse[1] : lse[2], x == 1 ? gx[1] : gx[2], x == 1 ? Dx[1] : Dx[2],
+                             sl2, wave_active, bufs, lane,
+                         [&](int t) __attribute__((always_inline)) { tc.fetch(keytok, t * KT, n); },
+                         [&](T* dst) __attribute__((always_inline)) {
+                           tc.template issue<BUF>(dst, kin, vin, H, h, wave);
+                         });
       }
     }
   }
@@ -296,16 +389,172 @@ __global__ void k_inv_off(const uint32_t* __restrict__ key, int64_t E, int nkeys
   off[k] = (int32_t)lo;
 }
 
+// ------------------------------------------------------------------ key-side schedule
+// Units u = h*M + b in head-major order, each head's units by descending stream length in
+// query blocks (stable), are split into pieces and cut into work items (piece, key chunk).
+// Sorted unit s goes to XCD s % 8; each XCD's items form one list, taken round-robin by the
+// workgroups on that XCD, so the key chunks of a piece (which read the same query rows) run
+// side by side on one L2, and the workgroups sweep the heads in order (one head's query rows
+// at a time in the last-level cache).
+__global__ void k_kv_keys(const int32_t* __restrict__ inv_off, const int32_t* __restrict__ blk_cell,
+                          const int32_t* __restrict__ cell_off, int M, int U, uint32_t* __restrict__ key,
+                          int32_t* __restrict__ val) {
+  const int u = blockIdx.x * blockDim.x + threadIdx.x;
+  if (u >= U) return;
+  const int cell = blk_cell[u % M];
+  const int nent = cell_off[cell + 1] - cell_off[cell] + inv_off[u + 1] - inv_off[u];
+  key[u] = (uint32_t)(u / M) * (uint32_t)(2 * M + 1) + (uint32_t)(2 * M - nent);  // nent <= 2M
+  val[u] = u;
+}
+
+// Exclusive scan of one value per thread over a 1024-thread workgroup; returns the total.
+template <typename V>
+__device__ inline V wg_exclusive_scan(V x, V* sh) {
+  const int tid = threadIdx.x;
+  sh[tid] = x;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {
+    const V y = tid >= off ? sh[tid - off] : (V)0;
+    __syncthreads();
+    sh[tid] += y;
+    __syncthreads();
+  }
+  const V incl = sh[tid], total = sh[1023];
+  __syncthreads();
+  sh[tid] = incl - x;
+  return total;
+}
+
+// One workgroup: per sorted unit, its pieces (split while the running partial demand, in
+// key rows, stays within the budget), its item count and first item (its XCD's list base
+// plus its place in that list); xbase[x] = first item of XCD x's list, xbase[8] = total.
+__global__ __launch_bounds__(1024) void k_kv_schedule(
+    const int32_t* __restrict__ order, int U, int M, const int32_t* __restrict__ inv_off,
+    const int32_t* __restrict__ blk_cell, const int32_t* __restrict__ cell_off,
+    const int32_t* __restrict__ blk_off, int64_t budget, int4* __restrict__ sinfo,
+    int32_t* __restrict__ ioff, int32_t* __restrict__ xbase) {
+  __shared__ int64_t sh64[1024];
+  __shared__ int32_t sh32[1024];
+  __shared__ int32_t xtot[NXCD + 1];
+  const int tid = threadIdx.x;
+  const int per = (U + 1023) / 1024;
+  const int s0 = min(U, tid * per), s1 = min(U, s0 + per);
+  auto unit_info = [&](int si, int& u, int& want, int& rows) {
+    u = order[si];
+    const int b = u % M, cell = blk_cell[b];
+    const int nent = cell_off[cell + 1] - cell_off[cell] + inv_off[u + 1] - inv_off[u];
+    want = (nent + KV_EP - 1) / KV_EP;
+    rows = blk_off[b + 1] - blk_off[b];
+  };
+  int64_t dsum = 0;
+  for (int si = s0; si < s1; ++si) {
+    int u, want, rows;
+    unit_info(si, u, want, rows);
+    if (want > 1) dsum += (int64_t)want * rows;
+  }
+  wg_exclusive_scan<int64_t>(dsum, sh64);
+  int64_t dpre = sh64[tid];
+  int isum[NXCD];
+#pragma unroll
+  for (int x = 0; x < NXCD; ++x) isum[x] = 0;
+  for (int si = s0; si < s1; ++si) {
+    int u, want, rows;
+    unit_info(si, u, want, rows);
+    const int64_t dem = want > 1 ? (int64_t)want * rows : 0;
+    const bool split = want > 1 && dpre + dem <= budget;
+    const int pieces = split ? want : 1;
+    sinfo[si] = make_int4(u, pieces, split ? (int)dpre : -1, 0);
+    dpre += dem;
+    const int n = (rows + KROWS - 1) / KROWS * pieces;
+#pragma unroll
+    for (int x = 0; x < NXCD; ++x) isum[x] += (si % NXCD == x) ? n : 0;
+  }
+  int ipre[NXCD];
+#pragma unroll
+  for (int x = 0; x < NXCD; ++x) {
+    const int tot = wg_exclusive_scan<int32_t>(isum[x], sh32);
+    ipre[x] = sh32[tid];
+    if (tid == 0) xtot[x] = tot;
+    __syncthreads();
+  }
+  if (tid == 0) {
+    int acc = 0;
+    for (int x = 0; x < NXCD; ++x) {
+      xbase[x] = acc;
+      const int t = xtot[x];
+      xtot[x] = acc;
+      acc += t;
+    }
+    xbase[NXCD] = acc;
+  }
+  __syncthreads();
+  for (int si = s0; si < s1; ++si) {
+    int u, want, rows;
+    unit_info(si, u, want, rows);
+    const int n = (rows + KROWS - 1) / KROWS * sinfo[si].y;
+#pragma unroll
+    for (int x = 0; x < NXCD; ++x) {
+      if (si % NXCD == x) {
+        ioff[si] = xtot[x] + ipre[x];
+        ipre[x] += n;
+      }
+    }
+  }
+}
+
+// Items of each sorted unit: piece-major, key chunks inner (a piece's chunks read the same
+// query stream).
+__global__ void k_kv_items(const int4* __restrict__ sinfo, const int32_t* __restrict__ ioff,
+                           const int32_t* __restrict__ blk_off, int U, int M, int4* __restrict__ items) {
+  const int si = blockIdx.x * blockDim.x + threadIdx.x;
+  if (si >= U) return;
+  const int4 in = sinfo[si];
+  const int b = in.x % M, rows = blk_off[b + 1] - blk_off[b];
+  const int nch = (rows + KROWS - 1) / KROWS;
+  int i = ioff[si];
+  for (int pc = 0; pc < in.y; ++pc)
+    for (int ch = 0; ch < nch; ++ch)
+      items[i++] = make_int4(in.x, ch, pc, in.z < 0 ? -1 : in.z + pc * rows);
+}
+
+// Split units: dK, dV = the pieces' partials summed in piece order, plus the block's
+// compressed-branch terms.
+template <int D>
+__global__ __launch_bounds__(256) void k_kv_reduce(const int4* __restrict__ sinfo, const float* __restrict__ kpart,
+                                                   const float* __restrict__ ukv, const int32_t* __restrict__ blk_off,
+                                                   const int32_t* __restrict__ perm, int M, int Mp, int H,
+                                                   float* __restrict__ dk, float* __restrict__ dv) {
+  const int4 in = sinfo[blockIdx.x];
+  if (in.y <= 1) return;
+  const int h = in.x / M, b = in.x % M;
+  const int r0 = blk_off[b], rows = blk_off[b + 1] - r0;
+  const float* uk = ukv + ((int64_t)h * Mp + b) * D;
+  const float* uv = ukv + (((int64_t)H + h) * Mp + b) * D;
+  for (int idx = threadIdx.x; idx < rows * D; idx += 256) {
+    const int kr = idx / D, c = idx % D;
+    float sk = 0.f, sv = 0.f;
+    for (int pc = 0; pc < in.y; ++pc) {
+      const float* src = kpart + ((int64_t)in.z + (int64_t)pc * rows + kr) * 2 * D;
+      sk += src[c];
+      sv += src[D + c];
+    }
+    const int64_t t = perm[r0 + kr];
+    dk[(t * H + h) * D + c] = sk + uk[c];
+    dv[(t * H + h) * D + c] = sv + uv[c];
+  }
+}
+
 // ------------------------------------------------------------------ key side (S layout)
 // A wave owns 32 keys: their K and V rows are B operands held in registers.  The queries
 // that attend to the key block (the blocks of its window cell, then the query blocks whose
 // selection holds it) form one stream of 32-row tiles: a stage holds the tile's Q rows (at
-// 0, row stride KROW) and dO rows (at VOFF, row stride VROW); the stream runs through three
-// stage buffers like the forward's key stream (copy of tile t + 2 issued at step t), with
-// each query's sorted row, token and (lse, g, D) of its branch staged per segment in LDS.
+// 0, row stride KROW) and dO rows (at VOFF, row stride VROW); the stream runs through NB
+// stage buffers like the forward's key stream (copy of tile t + NB - 1 issued at step t),
+// with each query's sorted row, token and (lse, g, D) of its branch staged per segment in LDS.
 // Per tile: S = Q K^T, P = exp2(S sl2 - lse), dP = dO V^T, dS = P o (g dP - D),
 // dv += (g P)^T dO, dk += dS^T Q.
-constexpr int QSEG = 1024;  // query rows staged per segment
+constexpr int QSEG = 1024;  // query rows staged per segment (a multiple of the workgroup size)
+constexpr int QPAD = QSEG + KT;  // per-row table length: a segment and its last tile's padding
 
 template <int DT, int D>
 struct KvState {
@@ -367,14 +616,13 @@ __device__ inline void fill_info(float4* info, int k0, int total, int L, const i
 // The query stream of a key-side kernel: `total` positions, position -> (sorted row r,
 // branch x) by row_of.  Per segment of up to QSEG positions the tokens and (lse, g, D) of
 // the branch go to LDS, then the segment's 32-row tiles (Q rows at 0, dO rows at VOFF) run
-// through three stage buffers with copies two tiles ahead; per tile
+// through NB stage buffers (copies NB - 1 tiles ahead); per tile
 //   S = Q K^T, P = exp2(S sl2 - lse), dP = dO V^T, dS = P o (g dP - D),
 //   dv += (g P)^T dO, dk += dS^T Q
 // (dS and g P with the queries as the contraction index, read back from registers).
-template <int DT, int D, bool BUF, typename RowOf>
-__device__ inline void kv_stream(KvState<DT, D>& S, TileCopy<DT, D, BW>& tc, typename Tr<DT>::T* buf0,
-                                 typename Tr<DT>::T* buf1, typename Tr<DT>::T* buf2, int32_t* qtok,
-                                 float4* qinf, int total, const typename Tr<DT>::T* __restrict__ q,
+template <int DT, int D, bool BUF, int NB, int NW, typename RowOf>
+__device__ inline void kv_stream(KvState<DT, D>& S, TileCopy<DT, D, NW>& tc, typename Tr<DT>::T* const* bufs,
+                                 int32_t* qtok, float* qinf, int total, const typename Tr<DT>::T* __restrict__ q,
                                  const typename Tr<DT>::T* __restrict__ dout,
                                  const typename Tr<DT>::T* __restrict__ gates,
                                  const float* __restrict__ lse3, const float* __restrict__ D3,
@@ -383,189 +631,269 @@ __device__ inline void kv_stream(KvState<DT, D>& S, TileCopy<DT, D, BW>& tc, typ
   using C = Cfg<DT, D>;
   using T = typename Tr<DT>::T;
   using F = typename Tr<DT>::frag;
-  using TC = TileCopy<DT, D, BW>;
-  constexpr int NTH = 64 * BW;
+  using TC = TileCopy<DT, D, NW>;
+  constexpr int NTH = 64 * NW;
   const int tid = threadIdx.x, g = lane >> 5;
   for (int s0 = 0; s0 < total; s0 += QSEG) {
     const int n = min(QSEG, total - s0);
     __syncthreads();  // the previous segment's tiles have been read
-    for (int j = tid; j < n; j += NTH) {
-      int r, x;
-      row_of(s0 + j, r, x);
-      const int64_t t = perm[r];
-      qtok[j] = (int32_t)t;
-      qinf[j] = make_float4(lse3[((int64_t)x * H + h) * N + r], Tr<DT>::up(gates[(t * H + h) * 3 + x]),
-                            D3[((int64_t)x * H + h) * N + r], 0.f);
+    // a thread's QSEG / NTH positions: rows first, then every load in flight at once
+    constexpr int PER = QSEG / NTH;
+    int rr[PER], xx[PER];
+    int64_t tk[PER];
+    float ls[PER], dd[PER], gg[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      rr[i] = 0;
+      xx[i] = 0;
+      if (tid + i * NTH < n) row_of(s0 + tid + i * NTH, rr[i], xx[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const bool ok = tid + i * NTH < n;
+      const int64_t o = ((int64_t)xx[i] * H + h) * N + rr[i];
+      tk[i] = ok ? perm[rr[i]] : 0;
+      ls[i] = ok ? lse3[o] : 0.f;
+      dd[i] = ok ? D3[o] : 0.f;
+    }
+#pragma unroll
+    for (int i = 0; i < PER; ++i)
+      gg[i] = tid + i * NTH < n ? Tr<DT>::up(gates[(tk[i] * H + h) * 3 + xx[i]]) : 0.f;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      if (tid + i * NTH < n) {
+        qtok[tid + i * NTH] = (int32_t)tk[i];
+        qinf[tid + i * NTH] = ls[i];
+        qinf[QPAD + tid + i * NTH] = gg[i];
+        qinf[2 * QPAD + tid + i * NTH] = dd[i];
+      }
+    }
+    if (tid < (KT - n % KT) % KT) {  // the last tile's rows past n: probability 0
+      qinf[n + tid] = INFINITY;
+      qinf[QPAD + n + tid] = 0.f;
+      qinf[2 * QPAD + n + tid] = 0.f;
     }
     __syncthreads();
-      const int ntile = (n + KT - 1) / KT;
-      auto step = [&](int t, T* cur, T* nx2) __attribute__((always_inline)) {
-        if (t + 1 < ntile) vm_wait<TC::NI>();  // tile t landed; tile t + 1 may be in flight
-        else vm_wait<0>();
-        __syncthreads();
-        ssa_f16v ds = zero16(), pg = zero16();
-        if (wave_active) {
-          ssa_f16v sv = zero16(), dp = zero16();
-          const T* qrow = cur + (lane & 31) * C::KROW + g * C::KPL;
-          const T* orow = cur + TC::VOFF + (lane & 31) * C::VROW + g * C::KPL;
+    // S = Q K^T and dP = dO V^T of a tile (waves without keys compute on zero key rows;
+    // their results are not written)
+    auto sdp = [&](const T* cur, ssa_f16v& sv, ssa_f16v& dp) __attribute__((always_inline)) {
+      sv = zero16();
+      dp = zero16();
+      const T* qrow = cur + (lane & 31) * C::KROW + g * C::KPL;
+      const T* orow = cur + TC::VOFF + (lane & 31) * C::VROW + g * C::KPL;
+      // every fragment read is issued before the first MFMA (one LDS round trip, not one
+      // per K step)
+      F qa[C::NKS], oa[C::NKS];
 #pragma unroll
-          for (int ks = 0; ks < C::NKS; ++ks) {
-            sv = Tr<DT>::mma(load_frag<DT>(qrow + ks * C::KS), S.kf[ks], sv);
-            dp = Tr<DT>::mma(load_frag<DT>(orow + ks * C::KS), S.vf[ks], dp);
-          }
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int j = t * KT + res_row(r, g);
-            const float4 in = j < n ? qinf[j] : make_float4(INFINITY, 0.f, 0.f, 0.f);
-            const float pr = fast_exp2(__builtin_fmaf(sv[r], sl2, -in.x));
-            ds[r] = pr * (in.y * dp[r] - in.z);
-            pg[r] = in.y * pr;
-          }
-        }
-        // transposed fragments of the tile, read before tile t + 2's copy is issued (the
-        // transpose reads carry no alias information)
-        F qt[C::PK][C::NDV], ot[C::PK][C::NDV];
-        if (wave_active) {
-#pragma unroll
-          for (int ks = 0; ks < C::PK; ++ks)
-#pragma unroll
-            for (int jd = 0; jd < C::NDV; ++jd) {
-              qt[ks][jd] = tr_frag<DT, C::KROW>(cur, ks, jd, lane);
-              ot[ks][jd] = tr_frag<DT, C::VROW>(cur + TC::VOFF, ks, jd, lane);
-            }
-        }
-        if (t + 2 < ntile) tc.template issue<BUF>(nx2, q, dout, H, h, wave);
-        if (t + 3 < ntile) tc.fetch(qtok, (t + 3) * KT, n);
-        if (wave_active) {
-#pragma unroll
-          for (int ks = 0; ks < C::PK; ++ks) {
-            const F pf = p_frag<DT>(pg, ks), sf = p_frag<DT>(ds, ks);
-#pragma unroll
-            for (int jd = 0; jd < C::NDV; ++jd) {
-              S.dv[jd] = Tr<DT>::mma(pf, ot[ks][jd], S.dv[jd]);
-              S.dk[jd] = Tr<DT>::mma(sf, qt[ks][jd], S.dk[jd]);
-            }
-          }
-        }
-      };
-      tc.fetch(qtok, 0, n);
-      tc.template issue<BUF>(buf0, q, dout, H, h, wave);
-      if (ntile > 1) {
-        tc.fetch(qtok, KT, n);
-        tc.template issue<BUF>(buf1, q, dout, H, h, wave);
+      for (int ks = 0; ks < C::NKS; ++ks) {
+        qa[ks] = load_frag<DT>(qrow + ks * C::KS);
+        oa[ks] = load_frag<DT>(orow + ks * C::KS);
       }
-      if (ntile > 2) tc.fetch(qtok, 2 * KT, n);
-      for (int t = 0; t < ntile; t += 3) {
-        step(t, buf0, buf2);
-        if (t + 1 < ntile) step(t + 1, buf1, buf0);
-        if (t + 2 < ntile) step(t + 2, buf2, buf1);
+#pragma unroll
+      for (int ks = 0; ks < C::NKS; ++ks) {
+        sv = Tr<DT>::mma(qa[ks], S.kf[ks], sv);
+        dp = Tr<DT>::mma(oa[ks], S.vf[ks], dp);
       }
+      if constexpr (C::KPL != 1) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * C::NKS, 0);  // DS reads
+        __builtin_amdgcn_sched_group_barrier(0x008, 2 * C::NKS, 0);  // then MFMAs
+      }
+    };
+    // the rest of a tile: dS, g P, then dK, dV
+    auto finish = [&](int t, const T* cur, const ssa_f16v& sv, const ssa_f16v& dp, auto&& next)
+                      __attribute__((always_inline)) {
+      ssa_f16v ds, pg;
+      // (lse, g, D) of the tile's rows t KT + res_row(r, g): rows 8 (r / 4) + 4 g + r % 4
+      const float* base = qinf + t * KT + 4 * g;
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const float4 l4 = *reinterpret_cast<const float4*>(base + 8 * r4);
+        const float4 g4 = *reinterpret_cast<const float4*>(base + QPAD + 8 * r4);
+        const float4 d4 = *reinterpret_cast<const float4*>(base + 2 * QPAD + 8 * r4);
+        const float la[4] = {l4.x, l4.y, l4.z, l4.w}, ga[4] = {g4.x, g4.y, g4.z, g4.w},
+                    da[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * r4 + e;
+          const float pr = fast_exp2(__builtin_fmaf(sv[r], sl2, -la[e]));
+          ds[r] = pr * (ga[e] * dp[r] - da[e]);
+          pg[r] = ga[e] * pr;
+        }
+      }
+      // 16-bit types: the transposed fragments of the tile are read before the next copy is
+      // issued (the transpose reads carry no alias information); fp32 reads them in place
+      // (registers) and issues the copy after its MFMAs
+      constexpr bool PRE = C::KPL != 1;
+      F qt[PRE ? C::PK : 1][C::NDV], ot[PRE ? C::PK : 1][C::NDV];
+      if constexpr (PRE) {
+#pragma unroll
+        for (int ks = 0; ks < C::PK; ++ks)
+#pragma unroll
+          for (int jd = 0; jd < C::NDV; ++jd) {
+            qt[ks][jd] = tr_frag<DT, C::KROW>(cur, ks, jd, lane);
+            ot[ks][jd] = tr_frag<DT, C::VROW>(cur + TC::VOFF, ks, jd, lane);
+          }
+        next();
+      }
+#pragma unroll
+      for (int ks = 0; ks < C::PK; ++ks) {
+        const F pf = p_frag<DT>(pg, ks), sf = p_frag<DT>(ds, ks);
+#pragma unroll
+        for (int jd = 0; jd < C::NDV; ++jd) {
+          S.dv[jd] = Tr<DT>::mma(pf, PRE ? ot[ks][jd] : tr_frag<DT, C::VROW>(cur + TC::VOFF, ks, jd, lane),
+                                 S.dv[jd]);
+          S.dk[jd] = Tr<DT>::mma(sf, PRE ? qt[ks][jd] : tr_frag<DT, C::KROW>(cur, ks, jd, lane), S.dk[jd]);
+        }
+      }
+      if constexpr (!PRE) next();
+    };
+    auto fetch = [&](int t) __attribute__((always_inline)) { tc.fetch(qtok, t * KT, n); };
+    auto issue = [&](T* dst) __attribute__((always_inline)) { tc.template issue<BUF>(dst, q, dout, H, h, wave); };
+    if constexpr (sizeof(T) == 2 && D <= 96) {  // (registers for the second slot)
+      // S and dP of tile t + 1 run on the matrix cores while tile t is finished (two slots)
+      ssa_f16v sv[2], dp[2];
+      tile_pipeline_ahead<NB, TC::NI>(
+          (n + KT - 1) / KT, bufs, fetch, issue,
+          [&](int, const T* cur, auto sc) __attribute__((always_inline)) {
+            sdp(cur, sv[decltype(sc)::value], dp[decltype(sc)::value]);
+          },
+          [&](int t, const T* cur, auto sc, auto&& next) __attribute__((always_inline)) {
+            finish(t, cur, sv[decltype(sc)::value], dp[decltype(sc)::value], next);
+          });
+    } else {
+      tile_pipeline<NB, TC::NI>((n + KT - 1) / KT, bufs, fetch, issue,
+                                [&](int t, const T* cur, auto&& next) __attribute__((always_inline)) {
+                                  ssa_f16v sv, dp;
+                                  sdp(cur, sv, dp);
+                                  finish(t, cur, sv, dp, next);
+                                });
     }
+  }
 }
 
+// Resident workgroups (a multiple of 8) take their XCD's list of items round-robin.
+// An item is 128 keys of a unit's block and one piece of its query stream; an unsplit unit
+// writes dK, dV (with the block's compressed-branch terms), a piece of a split unit writes
+// its partial sums to kpart.
 template <int DT, int D, bool BUF>
-__global__ __launch_bounds__(64 * BW) void k_bwd_dkdv(
+__global__ __launch_bounds__(64 * KW) void k_bwd_dkdv(
     const typename Tr<DT>::T* __restrict__ q, const typename Tr<DT>::T* __restrict__ kin,
     const typename Tr<DT>::T* __restrict__ vin, const typename Tr<DT>::T* __restrict__ gates,
     const typename Tr<DT>::T* __restrict__ dout, const float* __restrict__ lse3,
     const float* __restrict__ D3, const int32_t* __restrict__ perm,
     const int32_t* __restrict__ blk_off, const int32_t* __restrict__ blk_cell,
     const int32_t* __restrict__ cell_off, const int32_t* __restrict__ cell_blk,
-    const int32_t* __restrict__ lpt, const int32_t* __restrict__ inv_off,
-    const int32_t* __restrict__ inv_q, int M, int H, int nchunk, int64_t N, float scale, float sl2,
-    const float* __restrict__ ukv, int Mp, float* __restrict__ dk, float* __restrict__ dv) {
+    const int4* __restrict__ items, const int32_t* __restrict__ xbase, const int32_t* __restrict__ inv_off,
+    const int32_t* __restrict__ inv_q, int M, int H, int64_t N, float scale, float sl2,
+    const float* __restrict__ ukv, int Mp, float* __restrict__ kpart, float* __restrict__ dk,
+    float* __restrict__ dv) {
   using C = Cfg<DT, D>;
   using T = typename Tr<DT>::T;
-  using F = typename Tr<DT>::frag;
-  using TC = TileCopy<DT, D, BW>;
-  constexpr int NTH = 64 * BW;
-  __shared__ __attribute__((aligned(1024))) T buf0[TC::ELEMS];
-  __shared__ __attribute__((aligned(1024))) T buf1[TC::ELEMS];
-  __shared__ __attribute__((aligned(1024))) T buf2[TC::ELEMS];
+  using TC = TileCopy<DT, D, KW>;
+  constexpr int NTH = 64 * KW;
+  constexpr int NB = stage_depth<DT, D, KW>(LDS_BYTES - 4096, QSEG * 20 + (3 * NTH + 1) * 4);
+  SSA_STAGE_BUFFERS(T, TC::ELEMS, NB);
   __shared__ int32_t pre[NTH + 1];
   __shared__ int32_t lst_off[NTH];
   __shared__ int32_t ent_x[NTH];
   __shared__ int32_t qtok[QSEG];
-  __shared__ float4 qinf[QSEG];
+  __shared__ __attribute__((aligned(16))) float qinf[3 * QPAD];
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, c = lane & 31;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  int unit, member;
-  xcd_split(blockIdx.x, nchunk * H, unit, member);
-  if (unit >= M) return;
-  const int h = member % H, chunk = member / H;
-  const int b = lpt[unit];
-  const int r0 = blk_off[b], rows = blk_off[b + 1] - r0;
-  if (chunk * BROWS >= rows) return;
-  const int kbase = chunk * BROWS + wave * 32;
-  const bool kvalid = kbase + c < rows;
-  const bool wave_active = kbase < rows;
-  const int64_t ktok = perm[r0 + (kvalid ? kbase + c : 0)];
-  KvState<DT, D> S;
-  load_q<DT, D>(S.kf, kin + (ktok * H + h) * D, kvalid, lane);
-  load_q<DT, D>(S.vf, vin + (ktok * H + h) * D, kvalid, lane);
-#pragma unroll
-  for (int j = 0; j < C::NDV; ++j) S.dk[j] = S.dv[j] = zero16();
-  const int cell = blk_cell[b];
-  const int c0 = cell_off[cell], nwin = cell_off[cell + 1] - c0;
-  const int i0 = inv_off[h * M + b], ninv = inv_off[h * M + b + 1] - i0;
-  const int nent = nwin + ninv;  // window query blocks, then the selecting ones
+  const int x = blockIdx.x % NXCD, nx = gridDim.x / NXCD;
+  const int ib = xbase[x], ie = xbase[x + 1];
   TC tc;
   tc.init(wave, lane);
+#pragma unroll 1
+  for (int it = ib + (int)blockIdx.x / NXCD; it < ie; it += nx) {
+    const int4 item = items[it];
+    const int h = item.x / M, b = item.x % M, chunk = item.y, piece = item.z, prow = item.w;
+    const int r0 = blk_off[b], rows = blk_off[b + 1] - r0;
+    const int kbase = chunk * KROWS + wave * 32;
+    const bool kvalid = kbase + c < rows;
+    const bool wave_active = kbase < rows;
+    const int64_t ktok = perm[r0 + (kvalid ? kbase + c : 0)];
+    KvState<DT, D> S;
+    load_q<DT, D>(S.kf, kin + (ktok * H + h) * D, kvalid, lane);
+    load_q<DT, D>(S.vf, vin + (ktok * H + h) * D, kvalid, lane);
+#pragma unroll
+    for (int j = 0; j < C::NDV; ++j) S.dk[j] = S.dv[j] = zero16();
+    const int cell = blk_cell[b];
+    const int c0 = cell_off[cell], nwin = cell_off[cell + 1] - c0;
+    const int i0 = inv_off[item.x], ninv = inv_off[item.x + 1] - i0;
+    const int nent = nwin + ninv;  // window query blocks, then the selecting ones
+    const int e_lo = prow < 0 ? 0 : piece * KV_EP;
+    const int e_hi = prow < 0 ? nent : min(nent, e_lo + KV_EP);
 
-  for (int e0 = 0; e0 < nent; e0 += NTH) {
-    const int L = min(NTH, nent - e0);
-    __syncthreads();  // the previous chunk's tables and stages are no longer read
-    int sz = 0;
-    if (tid < L) {
-      const int e = e0 + tid;
-      const int qb = e < nwin ? cell_blk[c0 + e] : inv_q[i0 + e - nwin];
-      lst_off[tid] = blk_off[qb];
-      sz = blk_off[qb + 1] - blk_off[qb];
-      ent_x[tid] = e < nwin ? 2 : 1;
-    }
-    pre[tid + 1] = sz;
-    if (tid == 0) pre[0] = 0;
-    __syncthreads();
-    if (L > 1) {
-      for (int off = 1; off < NTH; off <<= 1) {
-        const int t = (tid + 1 > off) ? pre[tid + 1 - off] : 0;
-        __syncthreads();
-        pre[tid + 1] += t;
-        __syncthreads();
+    for (int e0 = e_lo; e0 < e_hi; e0 += NTH) {
+      const int L = min(NTH, e_hi - e0);
+      __syncthreads();  // the previous tables and stages are no longer read
+      int sz = 0;
+      if (tid < L) {
+        const int e = e0 + tid;
+        const int qb = e < nwin ? cell_blk[c0 + e] : inv_q[i0 + e - nwin];
+        lst_off[tid] = blk_off[qb];
+        sz = blk_off[qb + 1] - blk_off[qb];
+        ent_x[tid] = e < nwin ? 2 : 1;
       }
+      pre[tid + 1] = sz;
+      if (tid == 0) pre[0] = 0;
+      __syncthreads();
+      if (L > 1) {
+        for (int off = 1; off < NTH; off <<= 1) {
+          const int t = (tid + 1 > off) ? pre[tid + 1 - off] : 0;
+          __syncthreads();
+          pre[tid + 1] += t;
+          __syncthreads();
+        }
+      }
+      const int total = pre[L];
+      kv_stream<DT, D, BUF, NB, KW>(S, tc, bufs, qtok, qinf, total, q, dout, gates, lse3, D3, perm,
+                                H, h, N, sl2, wave_active, wave, lane,
+                            [&](int pos, int& r, int& x) __attribute__((always_inline)) {
+                              int lo = 0, hi = L - 1;  // last entry starting at or before pos
+                              while (lo < hi) {
+                                const int mid = (lo + hi + 1) >> 1;
+                                if (pre[mid] <= pos) lo = mid; else hi = mid - 1;
+                              }
+                              r = lst_off[lo] + (pos - pre[lo]);
+                              x = ent_x[lo];
+                            });
     }
-    const int total = pre[L];
-    kv_stream<DT, D, BUF>(S, tc, buf0, buf1, buf2, qtok, qinf, total, q, dout, gates, lse3, D3, perm,
-                          H, h, N, sl2, wave_active, wave, lane,
-                          [&](int pos, int& r, int& x) __attribute__((always_inline)) {
-                            int lo = 0, hi = L - 1;  // last entry starting at or before pos
-                            while (lo < hi) {
-                              const int mid = (lo + hi + 1) >> 1;
-                              if (pre[mid] <= pos) lo = mid; else hi = mid - 1;
-                            }
-                            r = lst_off[lo] + (pos - pre[lo]);
-                            x = ent_x[lo];
-                          });
-  }
-  // write, with the block's compressed-branch terms: lane holds column 32j + c of keys
-  // res_row(r, g)
-  const float* uk = ukv + ((int64_t)h * Mp + b) * D;
-  const float* uv = ukv + (((int64_t)H + h) * Mp + b) * D;
-  float ukc[C::NDV], uvc[C::NDV];
-#pragma unroll
-  for (int j = 0; j < C::NDV; ++j) {
-    ukc[j] = uk[32 * j + c];
-    uvc[j] = uv[32 * j + c];
-  }
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int kr = kbase + res_row(r, g);
-    if (kr < rows) {
-      const int64_t t = perm[r0 + kr];
+    // write: lane holds column 32j + c of keys res_row(r, g)
+    if (prow < 0) {
+      const float* uk = ukv + ((int64_t)h * Mp + b) * D;
+      const float* uv = ukv + (((int64_t)H + h) * Mp + b) * D;
+      float ukc[C::NDV], uvc[C::NDV];
 #pragma unroll
       for (int j = 0; j < C::NDV; ++j) {
-        dk[(t * H + h) * D + 32 * j + c] = scale * S.dk[j][r] + ukc[j];
-        dv[(t * H + h) * D + 32 * j + c] = S.dv[j][r] + uvc[j];
+        ukc[j] = uk[32 * j + c];
+        uvc[j] = uv[32 * j + c];
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int kr = kbase + res_row(r, g);
+        if (kr < rows) {
+          const int64_t t = perm[r0 + kr];
+#pragma unroll
+          for (int j = 0; j < C::NDV; ++j) {
+            dk[(t * H + h) * D + 32 * j + c] = scale * S.dk[j][r] + ukc[j];
+            dv[(t * H + h) * D + 32 * j + c] = S.dv[j][r] + uvc[j];
+          }
+        }
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int kr = kbase + res_row(r, g);
+        if (kr < rows) {
+          float* dst = kpart + ((int64_t)prow + kr) * 2 * D;
+#pragma unroll
+          for (int j = 0; j < C::NDV; ++j) {
+            dst[32 * j + c] = scale * S.dk[j][r];
+            dst[D + 32 * j + c] = S.dv[j][r];
+          }
+        }
       }
     }
   }
@@ -585,11 +913,10 @@ __global__ __launch_bounds__(64 * BW) void k_bwd_cmp(
   using C = Cfg<DT, D>;
   using T = typename Tr<DT>::T;
   using TC = TileCopy<DT, D, BW>;
-  __shared__ __attribute__((aligned(1024))) T buf0[TC::ELEMS];
-  __shared__ __attribute__((aligned(1024))) T buf1[TC::ELEMS];
-  __shared__ __attribute__((aligned(1024))) T buf2[TC::ELEMS];
+  constexpr int NB = stage_depth<DT, D, BW>(LDS_BYTES - 4096, QSEG * 20);
+  SSA_STAGE_BUFFERS(T, TC::ELEMS, NB);
   __shared__ int32_t qtok[QSEG];
-  __shared__ float4 qinf[QSEG];
+  __shared__ __attribute__((aligned(16))) float qinf[3 * QPAD];
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, c = lane & 31;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int ntile = Mp / KT;
@@ -610,8 +937,8 @@ __global__ __launch_bounds__(64 * BW) void k_bwd_cmp(
   const int total = (int)max((int64_t)0, q1 - q0);
   TC tc;
   tc.init(wave, lane);
-  kv_stream<DT, D, BUF>(S, tc, buf0, buf1, buf2, qtok, qinf, total, q, dout, gates, lse3, D3, perm, H,
-                        h, N, sl2, ktv, wave, lane,
+  kv_stream<DT, D, BUF, NB, BW>(S, tc, bufs, qtok, qinf, total, q, dout, gates, lse3, D3, perm, H,
+                            h, N, sl2, ktv, wave, lane,
                         [&](int pos, int& r, int& x) __attribute__((always_inline)) {
                           r = (int)q0 + pos;
                           x = 0;
@@ -709,16 +1036,42 @@ hipError_t run_backward(const ssa_plan_s* p, int H, int topk, float scale, const
                      p->perm, Mp, H, w.qch, N, scale, sl2, w.part_k, w.part_v);
   hipLaunchKernelGGL((k_bwd_pool<DT, D>), dim3(M, H), dim3(256), 0, s, (const T*)wk, (const T*)wv,
                      w.part_k, w.part_v, p->blk_off, Mp, H, w.qch, w.ukv);
+  // key-side schedule
+  const int U = H * M;
+  hipLaunchKernelGGL(k_kv_keys, dim3((U + 255) / 256), dim3(256), 0, s, w.inv_off, p->blk_cell, p->cell_off, M,
+                     U, w.ska, w.sva);
+  uint32_t *sa = w.ska, *sb2 = w.skb;
+  int32_t *oa = w.sva, *ob = w.svb;
+  e = ssa_sort::radix_sort(sa, oa, sb2, ob, U, ssa_sort::bits_for((uint64_t)H * (2 * M + 1)), w.rank, w.hist,
+                           w.part, s);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_kv_schedule, dim3(1), dim3(1024), 0, s, oa, U, M, w.inv_off, p->blk_cell, p->cell_off,
+                     p->blk_off, kv_budget_rows(D), w.sinfo, w.ioff, w.xbase);
+  hipLaunchKernelGGL(k_kv_items, dim3((U + 255) / 256), dim3(256), 0, s, w.sinfo, w.ioff, p->blk_off, U, M,
+                     w.items);
+  int dev = 0, cus = 0, per_cu = 0;
+  if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
+  if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
   if (buf)
-    hipLaunchKernelGGL((k_bwd_dkdv<DT, D, true>), dim3(xcd_grid(M, (int64_t)H * nchunk)), dim3(64 * BW), 0, s,
-                     (const T*)q, (const T*)k, (const T*)v, (const T*)gates, (const T*)dout, fw.lse,
-                     w.D, p->perm, p->blk_off, p->blk_cell, p->cell_off, p->cell_blk, p->lpt,
-                     w.inv_off, va, M, H, nchunk, N, scale, sl2, w.ukv, Mp, dk, dv);
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_bwd_dkdv<DT, D, true>, 64 * KW, 0);
   else
-    hipLaunchKernelGGL((k_bwd_dkdv<DT, D, false>), dim3(xcd_grid(M, (int64_t)H * nchunk)), dim3(64 * BW), 0, s,
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_bwd_dkdv<DT, D, false>, 64 * KW, 0);
+  if (e != hipSuccess) return e;
+  const int64_t items_max = (int64_t)U * ((p->max_rows + KROWS - 1) / KROWS);  // an unsplit schedule
+  const int64_t resident = std::max<int64_t>(NXCD, (int64_t)cus * std::max(per_cu, 1) / NXCD * NXCD);
+  const unsigned grid = (unsigned)std::min<int64_t>(resident, (items_max + kv_budget_rows(D) + NXCD - 1) / NXCD * NXCD);
+  if (buf)
+    hipLaunchKernelGGL((k_bwd_dkdv<DT, D, true>), dim3(grid), dim3(64 * KW), 0, s,
                      (const T*)q, (const T*)k, (const T*)v, (const T*)gates, (const T*)dout, fw.lse,
-                     w.D, p->perm, p->blk_off, p->blk_cell, p->cell_off, p->cell_blk, p->lpt,
-                     w.inv_off, va, M, H, nchunk, N, scale, sl2, w.ukv, Mp, dk, dv);
+                     w.D, p->perm, p->blk_off, p->blk_cell, p->cell_off, p->cell_blk, w.items, w.xbase,
+                     w.inv_off, va, M, H, N, scale, sl2, w.ukv, Mp, w.kpart, dk, dv);
+  else
+    hipLaunchKernelGGL((k_bwd_dkdv<DT, D, false>), dim3(grid), dim3(64 * KW), 0, s,
+                     (const T*)q, (const T*)k, (const T*)v, (const T*)gates, (const T*)dout, fw.lse,
+                     w.D, p->perm, p->blk_off, p->blk_cell, p->cell_off, p->cell_blk, w.items, w.xbase,
+                     w.inv_off, va, M, H, N, scale, sl2, w.ukv, Mp, w.kpart, dk, dv);
+  hipLaunchKernelGGL((k_kv_reduce<D>), dim3(U), dim3(256), 0, s, w.sinfo, w.kpart, w.ukv, p->blk_off, p->perm,
+                     M, Mp, H, dk, dv);
   return hipGetLastError();
 }
 

@@ -580,18 +580,37 @@ __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ sigma, i
 // A key set is a list of blocks (the selected blocks, or the blocks of the query's window
 // cell), concatenated in sorted token order and cut into 32-key tiles.  The set is staged in
 // segments of up to KSEG keys: first the token of every key of the segment goes to LDS
-// (keytok), then the segment's tiles stream through three stage buffers, the copy of tile
-// t + 2 being issued while tile t is in use.  Keys past the end of a segment reuse its first
+// (keytok), then the segment's tiles stream through NB stage buffers, the copy of tile
+// t + NB - 1 being issued while tile t is in use.  Keys past the end of a segment reuse its first
 // key (finite values; their scores are masked).
 constexpr int KSEG = 2048;
-template <int DT, int D, bool BUF>
+
+// S^T = K Q^T of a 32-key tile (K rows at the stage start), every fragment read issued
+// before the first MFMA.
+template <int DT, int D>
+__device__ inline ssa_f16v s_chain(const typename Tr<DT>::T* cur, const typename Tr<DT>::frag* qf, int lane) {
+  using C = Cfg<DT, D>;
+  const typename Tr<DT>::T* krow = cur + (lane & 31) * C::KROW + (lane >> 5) * C::KPL;
+  typename Tr<DT>::frag ka[C::NKS];
+#pragma unroll
+  for (int ks = 0; ks < C::NKS; ++ks) ka[ks] = load_frag<DT>(krow + ks * C::KS);
+  ssa_f16v acc = zero16();
+#pragma unroll
+  for (int ks = 0; ks < C::NKS; ++ks) acc = Tr<DT>::mma(ka[ks], qf[ks], acc);
+  if constexpr (C::KPL != 1) {
+    __builtin_amdgcn_sched_group_barrier(0x100, C::NKS, 0);  // DS reads
+    __builtin_amdgcn_sched_group_barrier(0x008, C::NKS, 0);  // then MFMAs
+  }
+  return acc;
+}
+
+template <int DT, int D, bool BUF, int NB>
 __device__ inline void gathered_branch(
     Online<D / 32>& st, const TileCopy<DT, D, ATT_WAVES>& tc0, const int32_t* blist, int nlist,
     const typename Tr<DT>::frag* qf, const typename Tr<DT>::T* __restrict__ kin,
     const typename Tr<DT>::T* __restrict__ vin, const int32_t* __restrict__ perm,
     const int32_t* __restrict__ blk_off, int H, int h, float sl2, bool wave_active,
-    typename Tr<DT>::T* buf0, typename Tr<DT>::T* buf1, typename Tr<DT>::T* buf2, int32_t* pre,
-    int32_t* lst_off, int32_t* keytok) {
+    typename Tr<DT>::T* const* bufs, int32_t* pre, int32_t* lst_off, int32_t* keytok) {
   using C = Cfg<DT, D>;
   using T = typename Tr<DT>::T;
   using F = typename Tr<DT>::frag;
@@ -625,60 +644,45 @@ __device__ inline void gathered_branch(
     for (int ks0 = 0; ks0 < total; ks0 += KSEG) {
       const int n = min(KSEG, total - ks0);
       __syncthreads();  // the previous segment's tiles have been read
-      for (int j = tid; j < n; j += NTH) {
+      fill_tokens<KSEG / NTH, NTH>(keytok, n, [&](int j) {
         const int key = ks0 + j;
         int lo = 0, hi = L - 1;  // last list entry starting at or before the key
         while (lo < hi) {
           const int mid = (lo + hi + 1) >> 1;
           if (pre[mid] <= key) lo = mid; else hi = mid - 1;
         }
-        keytok[j] = perm[lst_off[lo] + (key - pre[lo])];
-      }
+        return lst_off[lo] + (key - pre[lo]);
+      }, perm);
       __syncthreads();
-      const int ntile = (n + KT - 1) / KT;
-      auto step = [&](int t, T* cur, T* nx2) {
-        if (t + 1 < ntile) vm_wait<TC::NI>();  // tile t landed; tile t + 1 may be in flight
-        else vm_wait<0>();
-        __syncthreads();
-        ssa_f16v acc = zero16();
-        if (wave_active) {
-          const T* krow = cur + (lane & 31) * C::KROW + (lane >> 5) * C::KPL;
+      tile_pipeline<NB, TC::NI>(
+          (n + KT - 1) / KT, bufs,
+          [&](int t) __attribute__((always_inline)) { tc.fetch(keytok, t * KT, n); },
+          [&](T* dst) __attribute__((always_inline)) { tc.template issue<BUF>(dst, kin, vin, H, h, wave); },
+          [&](int t, const T* cur, auto&& next) __attribute__((always_inline)) {
+            ssa_f16v acc = zero16();
+            if (wave_active) {
+              acc = s_chain<DT, D>(cur, qf, lane);
+              if ((t + 1) * KT > n) {
 #pragma unroll
-          for (int ks = 0; ks < C::NKS; ++ks) acc = Tr<DT>::mma(load_frag<DT>(krow + ks * C::KS), qf[ks], acc);
-          if (t == ntile - 1) {
+                for (int r = 0; r < 16; ++r)
+                  if (t * KT + res_row(r, g) >= n) acc[r] = -INFINITY;
+              }
+              st.update(acc, sl2);
+            }
+            // the value fragments are read before the next copy is issued: the transpose
+            // reads carry no alias information, so reading after it would wait for that copy
+            VFrags<DT, D> vf;
+            if (wave_active) vf.read(cur + TC::VOFF, lane);
+            next();
+            if (wave_active) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r)
-              if (t * KT + res_row(r, g) >= n) acc[r] = -INFINITY;
-          }
-          st.update(acc, sl2);
-        }
-        // the value fragments are read before tile t + 2's copy is issued: the transpose
-        // reads carry no alias information, so reading after it would wait for that copy
-        VFrags<DT, D> vf;
-        if (wave_active) vf.read(cur + TC::VOFF, lane);
-        if (t + 2 < ntile) tc.template issue<BUF>(nx2, kin, vin, H, h, wave);
-        if (t + 3 < ntile) tc.fetch(keytok, (t + 3) * KT, n);
-        if (wave_active) {
+              for (int ks = 0; ks < C::PK; ++ks) {
+                const F pf = p_frag<DT>(acc, ks);
 #pragma unroll
-          for (int ks = 0; ks < C::PK; ++ks) {
-            const F pf = p_frag<DT>(acc, ks);
-#pragma unroll
-            for (int j = 0; j < C::NDV; ++j) st.o[j] = Tr<DT>::mma(vf.f[ks][j], pf, st.o[j]);
-          }
-        }
-      };
-      tc.fetch(keytok, 0, n);
-      tc.template issue<BUF>(buf0, kin, vin, H, h, wave);
-      if (ntile > 1) {
-        tc.fetch(keytok, KT, n);
-        tc.template issue<BUF>(buf1, kin, vin, H, h, wave);
-      }
-      if (ntile > 2) tc.fetch(keytok, 2 * KT, n);
-      for (int t = 0; t < ntile; t += 3) {
-        step(t, buf0, buf2);
-        if (t + 1 < ntile) step(t + 1, buf1, buf0);
-        if (t + 2 < ntile) step(t + 2, buf2, buf1);
-      }
+                for (int j = 0; j < C::NDV; ++j) st.o[j] = Tr<DT>::mma(vf.f[ks][j], pf, st.o[j]);
+              }
+            }
+          });
     }
   }
 }
@@ -703,7 +707,7 @@ __device__ inline int wave_incl_scan(int x, int lane) {
 // output kept in registers) and the window branch starts.  Otherwise each set is streamed on
 // its own (gathered_branch).
 template <int DT, int D, bool BUF>
-__global__ __launch_bounds__(64 * ATT_WAVES) __attribute__((amdgpu_waves_per_eu(2))) void k_attend(
+__global__ __launch_bounds__(64 * ATT_WAVES) __attribute__((amdgpu_waves_per_eu(D <= 96 ? 2 : 1))) void k_attend(
     const typename Tr<DT>::T* __restrict__ q, const typename Tr<DT>::T* __restrict__ kin,
     const typename Tr<DT>::T* __restrict__ vin, const typename Tr<DT>::T* __restrict__ gates,
     const int32_t* __restrict__ perm, const int32_t* __restrict__ blk_off,
@@ -718,9 +722,10 @@ __global__ __launch_bounds__(64 * ATT_WAVES) __attribute__((amdgpu_waves_per_eu(
   using TC = TileCopy<DT, D, ATT_WAVES>;
   constexpr int NTH = 64 * ATT_WAVES;
   static_assert(NTH >= 256, "one thread per top-k slot");
-  __shared__ __attribute__((aligned(1024))) T buf0[TC::ELEMS];
-  __shared__ __attribute__((aligned(1024))) T buf1[TC::ELEMS];
-  __shared__ __attribute__((aligned(1024))) T buf2[TC::ELEMS];
+  // two workgroups per CU
+  constexpr int NB = stage_depth<DT, D, ATT_WAVES>(LDS_BYTES / 2 - 2048,
+                                                   KSEG * 4 + (2 * NTH + 257) * 4 + 4 * 129 * 4);
+  SSA_STAGE_BUFFERS(T, TC::ELEMS, NB);
   __shared__ int32_t pre[NTH + 1];
   __shared__ int32_t lst_off[NTH];
   __shared__ int32_t sel_lds[256];
@@ -812,7 +817,7 @@ __global__ __launch_bounds__(64 * ATT_WAVES) __attribute__((amdgpu_waves_per_eu(
     const int S = e_pre[0][nsel], W = e_pre[1][nwin];
     const int P1 = (S + KT - 1) / KT * KT;  // the window keys start on a tile
     const int tot = P1 + W;
-    for (int j = tid; j < tot; j += NTH) {
+    fill_tokens<KSEG / NTH, NTH>(keytok, tot, [&](int j) {
       const int part = j < P1 ? 0 : 1;
       const int key = part ? j - P1 : (j < S ? j : 0);  // padding keys reuse key 0
       const int ne = part ? nwin : nsel;
@@ -821,65 +826,51 @@ __global__ __launch_bounds__(64 * ATT_WAVES) __attribute__((amdgpu_waves_per_eu(
         const int mid = (lo + hi + 1) >> 1;
         if (e_pre[part][mid] <= key) lo = mid; else hi = mid - 1;
       }
-      keytok[j] = perm[e_off[part][lo] + (key - e_pre[part][lo])];
-    }
+      return e_off[part][lo] + (key - e_pre[part][lo]);
+    }, perm);
     __syncthreads();
-    const int ntile = (tot + KT - 1) / KT, tb = P1 / KT;
+    const int tb = P1 / KT;
     st.init();
-    auto step = [&](int t, T* cur, T* nx2) __attribute__((always_inline)) {
-      if (t + 1 < ntile) vm_wait<TC::NI>();  // tile t landed; tile t + 1 may be in flight
-      else vm_wait<0>();
-      __syncthreads();
-      if (t == tb) {  // first window tile: close the selected branch
-        close_selected();
-        st.init();
-      }
-      const int lim = t < tb ? S : tot;  // keys at or past lim are masked
-      ssa_f16v acc = zero16();
-      if (wave_active) {
-        const T* krow = cur + (lane & 31) * C::KROW + (lane >> 5) * C::KPL;
+    tile_pipeline<NB, TC::NI>(
+        (tot + KT - 1) / KT, bufs,
+        [&](int t) __attribute__((always_inline)) { tc.fetch(keytok, t * KT, tot); },
+        [&](T* dst) __attribute__((always_inline)) { tc.template issue<BUF>(dst, kin, vin, H, h, wave); },
+        [&](int t, const T* cur, auto&& next) __attribute__((always_inline)) {
+          if (t == tb) {  // first window tile: close the selected branch
+            close_selected();
+            st.init();
+          }
+          const int lim = t < tb ? S : tot;  // keys at or past lim are masked
+          ssa_f16v acc = zero16();
+          if (wave_active) {
+            acc = s_chain<DT, D>(cur, qf, lane);
+            if ((t + 1) * KT > lim) {
 #pragma unroll
-        for (int ks = 0; ks < C::NKS; ++ks) acc = Tr<DT>::mma(load_frag<DT>(krow + ks * C::KS), qf[ks], acc);
-        if ((t + 1) * KT > lim) {
+              for (int r = 0; r < 16; ++r)
+                if (t * KT + res_row(r, g) >= lim) acc[r] = -INFINITY;
+            }
+            st.update(acc, sl2);
+          }
+          // the value fragments are read before the next copy is issued: the transpose reads
+          // carry no alias information, so reading after it would wait for that copy
+          VFrags<DT, D> vf;
+          if (wave_active) vf.read(cur + TC::VOFF, lane);
+          next();
+          if (wave_active) {
 #pragma unroll
-          for (int r = 0; r < 16; ++r)
-            if (t * KT + res_row(r, g) >= lim) acc[r] = -INFINITY;
-        }
-        st.update(acc, sl2);
-      }
-      // the value fragments are read before tile t + 2's copy is issued: the transpose
-      // reads carry no alias information, so reading after it would wait for that copy
-      VFrags<DT, D> vf;
-      if (wave_active) vf.read(cur + TC::VOFF, lane);
-      if (t + 2 < ntile) tc.template issue<BUF>(nx2, kin, vin, H, h, wave);
-      if (t + 3 < ntile) tc.fetch(keytok, (t + 3) * KT, tot);
-      if (wave_active) {
+            for (int ks = 0; ks < C::PK; ++ks) {
+              const F pf = p_frag<DT>(acc, ks);
 #pragma unroll
-        for (int ks = 0; ks < C::PK; ++ks) {
-          const F pf = p_frag<DT>(acc, ks);
-#pragma unroll
-          for (int j = 0; j < C::NDV; ++j) st.o[j] = Tr<DT>::mma(vf.f[ks][j], pf, st.o[j]);
-        }
-      }
-    };
-    tc.fetch(keytok, 0, tot);
-    tc.template issue<BUF>(buf0, kin, vin, H, h, wave);
-    if (ntile > 1) {
-      tc.fetch(keytok, KT, tot);
-      tc.template issue<BUF>(buf1, kin, vin, H, h, wave);
-    }
-    if (ntile > 2) tc.fetch(keytok, 2 * KT, tot);
-    for (int t = 0; t < ntile; t += 3) {
-      step(t, buf0, buf2);
-      if (t + 1 < ntile) step(t + 1, buf1, buf0);
-      if (t + 2 < ntile) step(t + 2, buf2, buf1);
-    }
+              for (int j = 0; j < C::NDV; ++j) st.o[j] = Tr<DT>::mma(vf.f[ks][j], pf, st.o[j]);
+            }
+          }
+        });
   } else {
-    gathered_branch<DT, D, BUF>(st, tc, sel_lds, nsel, qf, kin, vin, perm, blk_off, H, h, sl2,
-                                wave_active, buf0, buf1, buf2, pre, lst_off, keytok);
+    gathered_branch<DT, D, BUF, NB>(st, tc, sel_lds, nsel, qf, kin, vin, perm, blk_off, H, h, sl2,
+                                    wave_active, bufs, pre, lst_off, keytok);
     close_selected();
-    gathered_branch<DT, D, BUF>(st, tc, cell_blk + c0, nwin, qf, kin, vin, perm, blk_off, H, h, sl2,
-                                wave_active, buf0, buf1, buf2, pre, lst_off, keytok);
+    gathered_branch<DT, D, BUF, NB>(st, tc, cell_blk + c0, nwin, qf, kin, vin, perm, blk_off, H, h, sl2,
+                                    wave_active, bufs, pre, lst_off, keytok);
   }
   if (wave_active && valid) {
     const float ltot = xor32_sum(st.l);

@@ -1,6 +1,7 @@
 // Tile geometry and MFMA building blocks shared by the forward and backward kernels.
 #pragma once
 #include <hip/hip_runtime.h>
+#include <type_traits>
 #include "ssa_mfma.h"
 
 namespace ssa_dev {
@@ -430,13 +431,171 @@ struct TileCopy {
       }
     }
   }
+  // The same copies from two row-addressed sources: row r of the K part at kb + ko(r) and of
+  // the V part at vb + vo(r) (element offsets), for the rows r0 + tile row (set_rows).
+  __device__ inline void set_rows(int r0) {
+#pragma unroll
+    for (int m = 0; m < NI; ++m) tok[m] = r0 + row[m];
+  }
+  template <bool BUF, typename KO, typename VO>
+  __device__ inline void issue_rows(T* stage, const T* kb, const T* vb, KO ko, VO vo, int wave) const {
+    if constexpr (BUF) {
+      const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(kb), 0, -1, 0x00020000);
+      const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(vb), 0, -1, 0x00020000);
+#pragma unroll
+      for (int m = 0; m < NI; ++m) {
+        const bool isk = wave + m * NW < KI;
+        const uint32_t off = ((uint32_t)(isk ? ko(tok[m]) : vo(tok[m])) + (uint32_t)goff[m]) * (uint32_t)sizeof(T);
+        lds_void_t* dst = (lds_void_t*)(stage + (wave + m * NW) * 64 * C::EPC);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(isk ? rk : rv, dst, 16, off, 0, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int m = 0; m < NI; ++m) {
+        const bool isk = wave + m * NW < KI;
+        const T* src = isk ? kb + ko(tok[m]) + goff[m] : vb + vo(tok[m]) + goff[m];
+        dma16(src, stage + (wave + m * NW) * 64 * C::EPC);
+      }
+    }
+  }
 };
 
-// Waits until at most N of this wave's vector memory operations are outstanding.
+// keytok[j] = perm[row(j)] for j < n <= PER * NT (NT threads): a thread's PER rows first,
+// then all of its loads in flight at once.
+template <int PER, int NT, typename Row>
+__device__ inline void fill_tokens(int32_t* keytok, int n, Row row, const int32_t* __restrict__ perm) {
+  const int tid = threadIdx.x;
+  constexpr int nt = NT;
+  int r[PER], v[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) r[i] = tid + i * nt < n ? row(tid + i * nt) : -1;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) v[i] = r[i] >= 0 ? perm[r[i]] : 0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i)
+    if (r[i] >= 0) keytok[tid + i * nt] = v[i];
+}
+
+// Waits until at most N of this wave's vector memory operations are outstanding (vmcnt is
+// six bits: 3:0 and 15:14 of the immediate).
 template <int N>
 __device__ inline void vm_wait() {
-  static_assert(N >= 0 && N < 16, "vmcnt immediate");
-  __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+  static_assert(N >= 0 && N < 64, "vmcnt immediate");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
 }
+
+// Waits until at most k tiles' copies (NI instructions each) are outstanding, k <= 4.
+template <int NI>
+__device__ inline void vm_wait_tiles(int k) {
+  switch (k) {
+    case 0: vm_wait<0>(); break;
+    case 1: vm_wait<NI>(); break;
+    case 2: vm_wait<2 * NI>(); break;
+    case 3: vm_wait<3 * NI>(); break;
+    default: vm_wait<4 * NI>(); break;
+  }
+}
+
+// Stage buffers that fit an LDS budget next to `other` bytes of tables: 3 to 6.
+template <int DT, int D, int NW>
+constexpr int stage_depth(int budget, int other) {
+  const int n = (budget - other) / (TileCopy<DT, D, NW>::ELEMS * (int)sizeof(typename Tr<DT>::T));
+  return n < 3 ? 3 : (n > 6 ? 6 : n);
+}
+
+// A stream of ntile tiles through NB stage buffers (separate LDS arrays, so the compiler
+// knows a copy into one does not touch reads of another): the copies of tiles 0 .. NB-2 are
+// issued up front, and step t, once tile t has landed and every wave has passed the
+// barrier, runs body(t, stage, next) where next() issues tile t + NB - 1 into the buffer
+// tile t - 1 used and readies tile t + NB's addresses.  fetch(t) readies tile t's copy
+// addresses, issue(buffer) starts the copy (NI instructions per wave).
+template <int NB, int NI, typename T, typename Fetch, typename Issue, typename Body>
+__device__ inline void tile_pipeline(int ntile, T* const* bufs, Fetch&& fetch, Issue&& issue, Body&& body) {
+  static_assert(NB >= 3 && NB <= 6, "stage depth");
+  if (ntile <= 0) return;
+#pragma unroll
+  for (int u = 0; u < NB - 1; ++u) {
+    if (u < ntile) {
+      fetch(u);
+      issue(bufs[u]);
+    }
+  }
+  if (NB - 1 < ntile) fetch(NB - 1);
+  for (int t0 = 0; t0 < ntile; t0 += NB) {
+#pragma unroll
+    for (int u = 0; u < NB; ++u) {
+      const int t = t0 + u;
+      if (t < ntile) {
+        vm_wait_tiles<NI>(min(NB - 2, ntile - 1 - t));
+        __syncthreads();
+        body(t, bufs[u], [&]() __attribute__((always_inline)) {
+          if (t + NB - 1 < ntile) issue(bufs[(u + NB - 1) % NB]);
+          if (t + NB < ntile) fetch(t + NB);
+        });
+      }
+    }
+  }
+}
+
+// Calls f(std::integral_constant<int, I>) for I = B .. E-1.
+template <int B, int E, typename F>
+__device__ inline void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
+// The same stream with a one-tile lookahead inside each wave: step t first runs
+// ahead(t + 1, stage of t + 1, slot (t + 1) % 2) -- the MFMAs whose results step t + 1 needs
+// -- and then body(t, stage of t, slot t % 2, next), so the matrix cores work on tile t + 1
+// while the vector units finish tile t.  Tile t + 1 must have landed at step t, so NB - 3
+// tiles stay in flight beyond it.  The caller keeps two state slots.
+template <int NB, int NI, typename T, typename Fetch, typename Issue, typename Ahead, typename Body>
+__device__ inline void tile_pipeline_ahead(int ntile, T* const* bufs, Fetch&& fetch, Issue&& issue, Ahead&& ahead,
+                                           Body&& body) {
+  static_assert(NB >= 3 && NB <= 6, "stage depth");
+  constexpr int UN = NB % 2 == 0 ? NB : 2 * NB;  // unrolled steps: buffer and slot both static
+  if (ntile <= 0) return;
+#pragma unroll
+  for (int u = 0; u < NB - 1; ++u) {
+    if (u < ntile) {
+      fetch(u);
+      issue(bufs[u]);
+    }
+  }
+  if (NB - 1 < ntile) fetch(NB - 1);
+  vm_wait_tiles<NI>(min(NB - 2, ntile - 1));
+  __syncthreads();
+  ahead(0, bufs[0], std::integral_constant<int, 0>{});
+  for (int t0 = 0; t0 < ntile; t0 += UN) {
+    static_for<0, UN>([&](auto uc) __attribute__((always_inline)) {
+      constexpr int u = decltype(uc)::value;
+      const int t = t0 + u;
+      if (t < ntile) {
+        if (t + 1 < ntile) {
+          vm_wait_tiles<NI>(min(NB - 3, ntile - 2 - t));  // tile t + 1 landed
+          __syncthreads();
+          ahead(t + 1, bufs[(u + 1) % NB], std::integral_constant<int, (u + 1) % 2>{});
+        }
+        body(t, bufs[u % NB], std::integral_constant<int, u % 2>{}, [&]() __attribute__((always_inline)) {
+          if (t + NB - 1 < ntile) issue(bufs[(u + NB - 1) % NB]);
+          if (t + NB < ntile) fetch(t + NB);
+        });
+      }
+    });
+  }
+}
+
+// Declares the stage buffers buf0 .. buf5 of a kernel (those past NB are 16-byte stubs) and
+// the pointer table `bufs`.
+#define SSA_STAGE_BUFFERS(T, ELEMS, NB)                                                          \
+  __shared__ __attribute__((aligned(1024))) T buf0[ELEMS];                                     \
+  __shared__ __attribute__((aligned(1024))) T buf1[ELEMS];                                     \
+  __shared__ __attribute__((aligned(1024))) T buf2[ELEMS];                                     \
+  __shared__ __attribute__((aligned((NB) > 3 ? 1024 : 16))) T buf3[(NB) > 3 ? (ELEMS) : 16 / sizeof(T)]; \
+  __shared__ __attribute__((aligned((NB) > 4 ? 1024 : 16))) T buf4[(NB) > 4 ? (ELEMS) : 16 / sizeof(T)]; \
+  __shared__ __attribute__((aligned((NB) > 5 ? 1024 : 16))) T buf5[(NB) > 5 ? (ELEMS) : 16 / sizeof(T)]; \
+  T* const bufs[6] = {buf0, buf1, buf2, buf3, buf4, buf5}
 
 }  // namespace ssa_dev
