@@ -30,6 +30,25 @@ PEAK_F32_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
 
 
+def select_traffic():
+    """HBM bytes per k_select dispatch at this workload from the committed rocprofv3 summary
+    (FETCH_SIZE + WRITE_SIZE, calibrated), or None when the kernel sources it was measured on
+    have changed since (digest mismatch) or the summary is missing."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "ssa_forward_shells80k_hbm_traffic.md")
+    try:
+        line = next(l for l in open(path) if l.startswith("traffic-record: "))
+        rec = json.loads(line[len("traffic-record: "):])
+        h = hashlib.sha256()
+        for f in rec["digest_files"]:
+            h.update(open(os.path.join(ROOT, "spatial_sparse_attention_amd", "csrc", f), "rb").read())
+        if h.hexdigest()[:16] != rec["source_digest"]:
+            return None
+        return float(rec["fetch_bytes"] + rec["write_bytes"])
+    except (OSError, StopIteration, ValueError, KeyError):
+        return None
+
+
 def attended_pairs(plan_arrays, sel, window_is_block):
     """Per-head sum over queries of (M + |selected keys| + |window keys|)."""
     blk_off = plan_arrays["blk_off"].astype(np.int64)
@@ -206,7 +225,8 @@ def main():
         "algorithmic_bytes": alg_bytes,
         "roofline": {"kernel": "k_select (compressed branch + top-k)", "bound": "mfma",
                      "achieved": sel_tflops, "peak": peak, "unit": "TFLOP/s",
-                     "frac": sel_tflops / peak, "traffic": None,
+                     "frac": sel_tflops / peak,
+                     "traffic": select_traffic() if wl.name == WORKLOAD else None,
                      "work_per_launch_flops": cmp_flops},
     }
     if not args.no_bwd:
