@@ -562,55 +562,76 @@ struct KvState {
   using F = typename Tr<DT>::frag;
   F kf[C::NKS], vf[C::NKS];
   ssa_f16v dk[C::NDV], dv[C::NDV];
-  // info[j] = {lse, g, D, 0} of tile query j
-  __device__ inline void tile(const typename Tr<DT>::T* st, const float4* info, float sl2, int lane) {
-    const int g = lane >> 5;
-    ssa_f16v s = zero16(), dp = zero16();
-    const typename Tr<DT>::T* qrow = st + (lane & 31) * C::KROW + g * C::KPL;
-    const typename Tr<DT>::T* orow = st + C::KTILE + (lane & 31) * C::VROW + g * C::KPL;
-#pragma unroll
-    for (int ks = 0; ks < C::NKS; ++ks) {
-      s = Tr<DT>::mma(load_frag<DT>(qrow + ks * C::KS), kf[ks], s);
-      dp = Tr<DT>::mma(load_frag<DT>(orow + ks * C::KS), vf[ks], dp);
-    }
-    ssa_f16v pg;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float4 in = info[res_row(r, g)];
-      const float p = fast_exp2(__builtin_fmaf(s[r], sl2, -in.x));
-      pg[r] = in.y * p;
-      s[r] = p * (in.y * dp[r] - in.z);
-    }
-#pragma unroll
-    for (int ks = 0; ks < C::PK; ++ks) {
-      const F pf = p_frag<DT>(pg, ks), sf = p_frag<DT>(s, ks);
-#pragma unroll
-      for (int j = 0; j < C::NDV; ++j) {
-        dv[j] = Tr<DT>::mma(pf, tr_frag<DT, C::VROW>(st + C::KTILE, ks, j, lane), dv[j]);
-        dk[j] = Tr<DT>::mma(sf, tr_frag<DT, C::KROW>(st, ks, j, lane), dk[j]);
-      }
-    }
-  }
 };
 
-// per-query info of a tile of set positions k0 .. k0+31 (threads 0..31)
-__device__ inline void fill_info(float4* info, int k0, int total, int L, const int32_t* pre,
-                                 const int32_t* lst_off, const float* __restrict__ lse,
-                                 const float* __restrict__ Dx, const void* gates, int dt16,
-                                 const int32_t* __restrict__ perm, int H, int h, int x) {
-  const int j = threadIdx.x;
-  if (j >= KT) return;
-  float4 v = make_float4(INFINITY, 0.f, 0.f, 0.f);
-  if (k0 + j < total) {
-    const int r = set_row(k0 + j, L, pre, lst_off);
-    const int64_t gi = ((int64_t)perm[r] * H + h) * 3 + x;
-    float gv;
-    if (dt16 == 0) gv = reinterpret_cast<const float*>(gates)[gi];
-    else if (dt16 == 1) gv = (float)reinterpret_cast<const _Float16*>(gates)[gi];
-    else gv = (float)reinterpret_cast<const __bf16*>(gates)[gi];
-    v = make_float4(lse[r], gv, Dx[r], 0.f);
+// Token and (lse, g, D) tables of one segment: positions s0 .. s0 + n - 1 of a query stream
+// (position -> sorted row r, branch x by row_of), three padded arrays of QPAD floats; the
+// last tile's rows past n get probability 0.  A thread's QSEG / NTH positions: rows first,
+// then every load in flight at once.
+template <int DT, int NTH, typename RowOf>
+__device__ inline void fill_qtables(int32_t* qtok, float* qinf, int s0, int n, RowOf& row_of,
+                                    const typename Tr<DT>::T* __restrict__ gates, const float* __restrict__ lse3,
+                                    const float* __restrict__ D3, const int32_t* __restrict__ perm, int H,
+                                    int h, int64_t N) {
+  const int tid = threadIdx.x;
+  constexpr int PER = QSEG / NTH;
+  int rr[PER], xx[PER];
+  int64_t tk[PER];
+  float ls[PER], dd[PER], gg[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    rr[i] = 0;
+    xx[i] = 0;
+    if (tid + i * NTH < n) row_of(s0 + tid + i * NTH, rr[i], xx[i]);
   }
-  info[j] = v;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const bool ok = tid + i * NTH < n;
+    const int64_t o = ((int64_t)xx[i] * H + h) * N + rr[i];
+    tk[i] = ok ? perm[rr[i]] : 0;
+    ls[i] = ok ? lse3[o] : 0.f;
+    dd[i] = ok ? D3[o] : 0.f;
+  }
+#pragma unroll
+  for (int i = 0; i < PER; ++i)
+    gg[i] = tid + i * NTH < n ? Tr<DT>::up(gates[(tk[i] * H + h) * 3 + xx[i]]) : 0.f;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    if (tid + i * NTH < n) {
+      qtok[tid + i * NTH] = (int32_t)tk[i];
+      qinf[tid + i * NTH] = ls[i];
+      qinf[QPAD + tid + i * NTH] = gg[i];
+      qinf[2 * QPAD + tid + i * NTH] = dd[i];
+    }
+  }
+  if (tid < (KT - n % KT) % KT) {
+    qinf[n + tid] = INFINITY;
+    qinf[QPAD + n + tid] = 0.f;
+    qinf[2 * QPAD + n + tid] = 0.f;
+  }
+}
+
+// dS and g P of a 32-query tile (queries as rows res_row(r, g) of tile t of the segment)
+// from its scores S and dP, with (lse, g, D) from the segment's tables.
+__device__ inline void tile_ds_pg(const ssa_f16v& sv, const ssa_f16v& dp, const float* qinf, int t, int g,
+                                  float sl2, ssa_f16v& ds, ssa_f16v& pg) {
+  // rows t KT + res_row(r, g) = t KT + 8 (r / 4) + 4 g + r % 4
+  const float* base = qinf + t * KT + 4 * g;
+#pragma unroll
+  for (int r4 = 0; r4 < 4; ++r4) {
+    const float4 l4 = *reinterpret_cast<const float4*>(base + 8 * r4);
+    const float4 g4 = *reinterpret_cast<const float4*>(base + QPAD + 8 * r4);
+    const float4 d4 = *reinterpret_cast<const float4*>(base + 2 * QPAD + 8 * r4);
+    const float la[4] = {l4.x, l4.y, l4.z, l4.w}, ga[4] = {g4.x, g4.y, g4.z, g4.w},
+                da[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = 4 * r4 + e;
+      const float pr = fast_exp2(__builtin_fmaf(sv[r], sl2, -la[e]));
+      ds[r] = pr * (ga[e] * dp[r] - da[e]);
+      pg[r] = ga[e] * pr;
+    }
+  }
 }
 
 // The query stream of a key-side kernel: `total` positions, position -> (sorted row r,
@@ -637,42 +658,7 @@ __device__ inline void kv_stream(KvState<DT, D>& S, TileCopy<DT, D, NW>& tc, typ
   for (int s0 = 0; s0 < total; s0 += QSEG) {
     const int n = min(QSEG, total - s0);
     __syncthreads();  // the previous segment's tiles have been read
-    // a thread's QSEG / NTH positions: rows first, then every load in flight at once
-    constexpr int PER = QSEG / NTH;
-    int rr[PER], xx[PER];
-    int64_t tk[PER];
-    float ls[PER], dd[PER], gg[PER];
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      rr[i] = 0;
-      xx[i] = 0;
-      if (tid + i * NTH < n) row_of(s0 + tid + i * NTH, rr[i], xx[i]);
-    }
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const bool ok = tid + i * NTH < n;
-      const int64_t o = ((int64_t)xx[i] * H + h) * N + rr[i];
-      tk[i] = ok ? perm[rr[i]] : 0;
-      ls[i] = ok ? lse3[o] : 0.f;
-      dd[i] = ok ? D3[o] : 0.f;
-    }
-#pragma unroll
-    for (int i = 0; i < PER; ++i)
-      gg[i] = tid + i * NTH < n ? Tr<DT>::up(gates[(tk[i] * H + h) * 3 + xx[i]]) : 0.f;
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      if (tid + i * NTH < n) {
-        qtok[tid + i * NTH] = (int32_t)tk[i];
-        qinf[tid + i * NTH] = ls[i];
-        qinf[QPAD + tid + i * NTH] = gg[i];
-        qinf[2 * QPAD + tid + i * NTH] = dd[i];
-      }
-    }
-    if (tid < (KT - n % KT) % KT) {  // the last tile's rows past n: probability 0
-      qinf[n + tid] = INFINITY;
-      qinf[QPAD + n + tid] = 0.f;
-      qinf[2 * QPAD + n + tid] = 0.f;
-    }
+    fill_qtables<DT, NTH>(qtok, qinf, s0, n, row_of, gates, lse3, D3, perm, H, h, N);
     __syncthreads();
     // S = Q K^T and dP = dO V^T of a tile (waves without keys compute on zero key rows;
     // their results are not written)
@@ -703,23 +689,7 @@ __device__ inline void kv_stream(KvState<DT, D>& S, TileCopy<DT, D, NW>& tc, typ
     auto finish = [&](int t, const T* cur, const ssa_f16v& sv, const ssa_f16v& dp, auto&& next)
                       __attribute__((always_inline)) {
       ssa_f16v ds, pg;
-      // (lse, g, D) of the tile's rows t KT + res_row(r, g): rows 8 (r / 4) + 4 g + r % 4
-      const float* base = qinf + t * KT + 4 * g;
-#pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const float4 l4 = *reinterpret_cast<const float4*>(base + 8 * r4);
-        const float4 g4 = *reinterpret_cast<const float4*>(base + QPAD + 8 * r4);
-        const float4 d4 = *reinterpret_cast<const float4*>(base + 2 * QPAD + 8 * r4);
-        const float la[4] = {l4.x, l4.y, l4.z, l4.w}, ga[4] = {g4.x, g4.y, g4.z, g4.w},
-                    da[4] = {d4.x, d4.y, d4.z, d4.w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * r4 + e;
-          const float pr = fast_exp2(__builtin_fmaf(sv[r], sl2, -la[e]));
-          ds[r] = pr * (ga[e] * dp[r] - da[e]);
-          pg[r] = ga[e] * pr;
-        }
-      }
+      tile_ds_pg(sv, dp, qinf, t, g, sl2, ds, pg);
       // 16-bit types: the transposed fragments of the tile are read before the next copy is
       // issued (the transpose reads carry no alias information); fp32 reads them in place
       // (registers) and issues the copy after its MFMAs
@@ -771,6 +741,122 @@ __device__ inline void kv_stream(KvState<DT, D>& S, TileCopy<DT, D, NW>& tc, typ
   }
 }
 
+// Narrow key blocks (at most 32 keys): every wave holds the same 32 keys, and wave w takes
+// the query tiles w, w + NW, w + 2 NW, ... of each segment, each wave copying its own tiles
+// through its own two buffers (the copy of its next tile issued while it finishes the
+// current one), with no workgroup barrier inside a segment.  The waves' dK, dV are partial
+// sums over their tiles, added in wave order by the caller.
+template <int DT, int D, bool BUF, int NW, typename RowOf>
+__device__ inline void kv_stream_narrow(KvState<DT, D>& S, typename Tr<DT>::T* b0, typename Tr<DT>::T* b1,
+                                        typename Tr<DT>::T* b2, typename Tr<DT>::T* b3, typename Tr<DT>::T* b4,
+                                        typename Tr<DT>::T* b5, typename Tr<DT>::T* b6, typename Tr<DT>::T* b7,
+                                        int32_t* qtok,
+                                        float* qinf, int total, const typename Tr<DT>::T* __restrict__ q,
+                                        const typename Tr<DT>::T* __restrict__ dout,
+                                        const typename Tr<DT>::T* __restrict__ gates,
+                                        const float* __restrict__ lse3, const float* __restrict__ D3,
+                                        const int32_t* __restrict__ perm, int H, int h, int64_t N, float sl2,
+                                        int wave, int lane, RowOf row_of) {
+  using C = Cfg<DT, D>;
+  using T = typename Tr<DT>::T;
+  using F = typename Tr<DT>::frag;
+  using T1 = TileCopy<DT, D, 1>;  // one wave copies a whole tile (the same layout)
+  constexpr int NTH = 64 * NW;
+  static_assert(T1::ELEMS <= TileCopy<DT, D, NW>::ELEMS, "a wave's tile fits a stage buffer");
+  const int g = lane >> 5;
+  // copy of the tile of segment rows k0 .. k0 + 31 into `stage`: instruction m covers 16-byte
+  // positions 64 m .. 64 m + 63 of the K part (m < KI) or of the V part; row and chunk of a
+  // lane are computed per instruction, the token read just before its copy
+  auto copy_tile = [&](T* stage, int k0, int n) __attribute__((always_inline)) {
+    int tk[T1::KI + T1::VI];
+#pragma unroll
+    for (int m = 0; m < T1::KI + T1::VI; ++m) {
+      const bool isk = m < T1::KI;
+      const int p = (isk ? m : m - T1::KI) * 64 + lane;
+      const int rr = isk ? p / T1::KRC : p / T1::VRC;
+      const int j = k0 + (rr < KT ? rr : 0);
+      tk[m] = qtok[j < n ? j : 0];
+    }
+#pragma unroll
+    for (int m = 0; m < T1::KI + T1::VI; ++m) {
+      const bool isk = m < T1::KI;
+      const int p = (isk ? m : m - T1::KI) * 64 + lane;
+      const int ch = isk ? p % T1::KRC : p % T1::VRC;
+      const int goff = ch < C::CPR ? ch * C::EPC : 0;  // padding lanes copy a valid chunk
+      lds_void_t* dst = (lds_void_t*)(stage + m * 64 * C::EPC);
+      if constexpr (BUF) {
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<T*>((isk ? q : dout) + h * D), 0, -1, 0x00020000);
+        const uint32_t off = ((uint32_t)tk[m] * (uint32_t)(H * D) + (uint32_t)goff) * (uint32_t)sizeof(T);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 16, off, 0, 0, 0);
+      } else {
+        dma16((isk ? q : dout) + ((int64_t)tk[m] * H + h) * D + goff, stage + m * 64 * C::EPC);
+      }
+    }
+  };
+  for (int s0 = 0; s0 < total; s0 += QSEG) {
+    const int n = min(QSEG, total - s0);
+    __syncthreads();  // every wave is done with the previous segment
+    fill_qtables<DT, NTH>(qtok, qinf, s0, n, row_of, gates, lse3, D3, perm, H, h, N);
+    __syncthreads();
+    const int ntile = (n + KT - 1) / KT;
+    // one tile of this wave: stage `cur`, the next tile of the wave goes to `oth`
+    auto step = [&](int t, T* cur, T* oth) __attribute__((always_inline)) {
+      vm_wait<0>();  // tile t landed (the wave's only copy in flight)
+      const T* qrow = cur + (lane & 31) * C::KROW + g * C::KPL;
+      const T* orow = cur + T1::VOFF + (lane & 31) * C::VROW + g * C::KPL;
+      ssa_f16v sv = zero16(), dp = zero16();
+      {
+        F qa[C::NKS], oa[C::NKS];  // all fragment reads before the first MFMA
+#pragma unroll
+        for (int ks = 0; ks < C::NKS; ++ks) {
+          qa[ks] = load_frag<DT>(qrow + ks * C::KS);
+          oa[ks] = load_frag<DT>(orow + ks * C::KS);
+        }
+#pragma unroll
+        for (int ks = 0; ks < C::NKS; ++ks) {
+          sv = Tr<DT>::mma(qa[ks], S.kf[ks], sv);
+          dp = Tr<DT>::mma(oa[ks], S.vf[ks], dp);
+        }
+      }
+      ssa_f16v ds, pg;
+      tile_ds_pg(sv, dp, qinf, t, g, sl2, ds, pg);
+      F qt[C::PK][C::NDV], ot[C::PK][C::NDV];  // read before the next copy is issued
+#pragma unroll
+      for (int ks = 0; ks < C::PK; ++ks)
+#pragma unroll
+        for (int jd = 0; jd < C::NDV; ++jd) {
+          qt[ks][jd] = tr_frag<DT, C::KROW>(cur, ks, jd, lane);
+          ot[ks][jd] = tr_frag<DT, C::VROW>(cur + T1::VOFF, ks, jd, lane);
+        }
+      if (t + NW < ntile) copy_tile(oth, (t + NW) * KT, n);
+#pragma unroll
+      for (int ks = 0; ks < C::PK; ++ks) {
+        const F pf = p_frag<DT>(pg, ks), sf = p_frag<DT>(ds, ks);
+#pragma unroll
+        for (int jd = 0; jd < C::NDV; ++jd) {
+          S.dv[jd] = Tr<DT>::mma(pf, ot[ks][jd], S.dv[jd]);
+          S.dk[jd] = Tr<DT>::mma(sf, qt[ks][jd], S.dk[jd]);
+        }
+      }
+    };
+    auto run = [&](T* ba, T* bb) __attribute__((always_inline)) {
+      if (wave >= ntile) return;
+      copy_tile(ba, wave * KT, n);
+      for (int t = wave; t < ntile; t += 2 * NW) {
+        step(t, ba, bb);
+        if (t + NW < ntile) step(t + NW, bb, ba);
+      }
+    };
+    // static buffer pairs per wave (the compiler keeps each copy apart from the other reads)
+    static_assert(NW == 4, "four waves, eight buffers");
+    if (wave == 0) run(b0, b1);
+    else if (wave == 1) run(b2, b3);
+    else if (wave == 2) run(b4, b5);
+    else run(b6, b7);
+  }
+}
+
 // Resident workgroups (a multiple of 8) take their XCD's list of items round-robin.
 // An item is 128 keys of a unit's block and one piece of its query stream; an unsplit unit
 // writes dK, dV (with the block's compressed-branch terms), a piece of a split unit writes
@@ -791,8 +877,16 @@ __global__ __launch_bounds__(64 * KW) void k_bwd_dkdv(
   using T = typename Tr<DT>::T;
   using TC = TileCopy<DT, D, KW>;
   constexpr int NTH = 64 * KW;
-  constexpr int NB = stage_depth<DT, D, KW>(LDS_BYTES - 4096, QSEG * 20 + (3 * NTH + 1) * 4);
+  // 16-bit, d <= 96: two more buffers, so that narrow key blocks get two per wave
+  constexpr bool NARROW = sizeof(T) == 2 && D <= 96;
+  constexpr int NB = stage_depth<DT, D, KW>(LDS_BYTES - 4096 - (NARROW ? 2 * TC::ELEMS * (int)sizeof(T) : 0),
+                                            QSEG * 20 + (3 * NTH + 1) * 4);
+  static_assert(!NARROW || (NB == 6 && KW == 4), "eight stage buffers for the narrow blocks");
+  static_assert(32 * D * 4 <= TC::ELEMS * (int)sizeof(T), "a wave's partial dK or dV fits a buffer");
   SSA_STAGE_BUFFERS(T, TC::ELEMS, NB);
+  __shared__ __attribute__((aligned(NARROW ? 1024 : 16))) T buf6[NARROW ? TC::ELEMS : 16 / sizeof(T)];
+  __shared__ __attribute__((aligned(NARROW ? 1024 : 16))) T buf7[NARROW ? TC::ELEMS : 16 / sizeof(T)];
+
   __shared__ int32_t pre[NTH + 1];
   __shared__ int32_t lst_off[NTH];
   __shared__ int32_t ent_x[NTH];
@@ -809,7 +903,10 @@ __global__ __launch_bounds__(64 * KW) void k_bwd_dkdv(
     const int4 item = items[it];
     const int h = item.x / M, b = item.x % M, chunk = item.y, piece = item.z, prow = item.w;
     const int r0 = blk_off[b], rows = blk_off[b + 1] - r0;
-    const int kbase = chunk * KROWS + wave * 32;
+    // a narrow block (at most 32 keys): every wave holds its keys and takes a share of the
+    // query tiles
+    const bool narrow = NARROW && rows <= 32;
+    const int kbase = narrow ? 0 : chunk * KROWS + wave * 32;
     const bool kvalid = kbase + c < rows;
     const bool wave_active = kbase < rows;
     const int64_t ktok = perm[r0 + (kvalid ? kbase + c : 0)];
@@ -848,17 +945,57 @@ __global__ __launch_bounds__(64 * KW) void k_bwd_dkdv(
         }
       }
       const int total = pre[L];
-      kv_stream<DT, D, BUF, NB, KW>(S, tc, bufs, qtok, qinf, total, q, dout, gates, lse3, D3, perm,
-                                H, h, N, sl2, wave_active, wave, lane,
-                            [&](int pos, int& r, int& x) __attribute__((always_inline)) {
-                              int lo = 0, hi = L - 1;  // last entry starting at or before pos
-                              while (lo < hi) {
-                                const int mid = (lo + hi + 1) >> 1;
-                                if (pre[mid] <= pos) lo = mid; else hi = mid - 1;
-                              }
-                              r = lst_off[lo] + (pos - pre[lo]);
-                              x = ent_x[lo];
-                            });
+      auto row_of = [&](int pos, int& r, int& x) __attribute__((always_inline)) {
+        int lo = 0, hi = L - 1;  // last entry starting at or before pos
+        while (lo < hi) {
+          const int mid = (lo + hi + 1) >> 1;
+          if (pre[mid] <= pos) lo = mid; else hi = mid - 1;
+        }
+        r = lst_off[lo] + (pos - pre[lo]);
+        x = ent_x[lo];
+      };
+      if constexpr (NARROW) {
+        if (narrow) {
+          kv_stream_narrow<DT, D, BUF, KW>(S, buf0, buf1, buf2, buf3, buf4, buf5, buf6, buf7, qtok, qinf, total, q,
+                                           dout, gates, lse3, D3, perm, H, h, N, sl2, wave, lane, row_of);
+          continue;
+        }
+      }
+      kv_stream<DT, D, BUF, NB, KW>(S, tc, bufs, qtok, qinf, total, q, dout, gates, lse3, D3, perm, H, h, N,
+                                    sl2, wave_active, wave, lane, row_of);
+    }
+    if constexpr (NARROW) {
+      if (narrow) {  // the waves' partial sums, added in wave order
+        __syncthreads();  // every wave's stream is done: the buffers are free
+        float* pk = reinterpret_cast<float*>(wave == 0 ? buf0 : wave == 1 ? buf1 : wave == 2 ? buf2 : buf3);
+        float* pv = reinterpret_cast<float*>(wave == 0 ? buf4 : wave == 1 ? buf5 : wave == 2 ? buf6 : buf7);
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+#pragma unroll
+          for (int j = 0; j < C::NDV; ++j) {
+            pk[res_row(r, g) * D + 32 * j + c] = S.dk[j][r];
+            pv[res_row(r, g) * D + 32 * j + c] = S.dv[j][r];
+          }
+        __syncthreads();
+        const float* uk = ukv + ((int64_t)h * Mp + b) * D;
+        const float* uv = ukv + (((int64_t)H + h) * Mp + b) * D;
+        for (int idx = tid; idx < rows * D; idx += NTH) {
+          auto at = [&](const T* bf) __attribute__((always_inline)) { return reinterpret_cast<const float*>(bf)[idx]; };
+          const float sk = ((at(buf0) + at(buf1)) + at(buf2)) + at(buf3);
+          const float sv = ((at(buf4) + at(buf5)) + at(buf6)) + at(buf7);
+          const int kr = idx / D, col = idx % D;
+          if (prow < 0) {
+            const int64_t t = perm[r0 + kr];
+            dk[(t * H + h) * D + col] = scale * sk + uk[col];
+            dv[(t * H + h) * D + col] = sv + uv[col];
+          } else {
+            float* dst = kpart + ((int64_t)prow + kr) * 2 * D;
+            dst[col] = scale * sk;
+            dst[D + col] = sv;
+          }
+        }
+        continue;
+      }
     }
     // write: lane holds column 32j + c of keys res_row(r, g)
     if (prow < 0) {
