@@ -43,9 +43,13 @@ struct BwdWs {
   int32_t *sva, *svb;          // [H*M] unit ids
   int4* sinfo;                 // [H*M] per sorted unit: {unit, pieces, partial row offset, -}
   int32_t* ioff;               // [H*M + 1] first item of each sorted unit
-  int4* items;                 // [item_cap] {unit, key chunk, piece, partial row offset or -1}
-  int32_t* xbase;              // [9] first item of each XCD's list, then the total
-  float* kpart;                // [KV_BUDGET rows][2][d] partial dK, dV of split units
+  int4* items;                 // [item_cap] {unit, key chunk, piece, partial row offset or -1},
+                               // or {-(group + 1), group piece, 0, 0}
+  int4* grp_meta;              // [H*M] per key group: {head, members, first member, keys}
+  int4* grp_mem;               // [H*M] per member: {block, first key slot, partial row, rows}
+  int32_t* ngrp;               // [1] key groups
+  int32_t* xbase;              // [3 kinds][9]: list starts per XCD, then the kind's end
+  float* kpart;                // [budget rows][2][d] partial dK, dV of split and tiny units
   int64_t item_cap;
 };
 
@@ -53,8 +57,16 @@ struct BwdWs {
 // (window blocks, then the selecting query blocks) is split into pieces of KV_EP blocks,
 // while the partial sums of the pieces fit a fixed budget of key rows; the pieces' partial
 // dK, dV are summed in piece order by k_kv_reduce.
+//
+// A tiny unit (at most KG_TINY keys, selected by some query block) instead keeps only its
+// window part as an item (piece 0) and joins a key group: up to KG_KEYS keys of at most
+// KG_MEM tiny units of one head, which streams the union of its members' selecting query
+// blocks once, each row masked to the members that its block selected.  The union is cut
+// into KG_QB-block ranges of query blocks (group pieces 1, 2, ...).
 constexpr int KV_EP = 8;
-inline int64_t kv_budget_rows(int d) { return (int64_t)(64 << 20) / (8 * d); }
+constexpr int KG_TINY = 32, KG_KEYS = 128, KG_MEM = 32, KG_QB = 16;
+__host__ __device__ inline int kg_pieces(int M) { return (M + KG_QB - 1) / KG_QB; }
+inline int64_t kv_budget_rows(int d) { return (int64_t)(128 << 20) / (8 * d); }
 
 int cmp_chunks(int64_t Mp, int H) {
   const int64_t groups = (Mp / KT + BW - 1) / BW * H;
@@ -88,10 +100,14 @@ size_t carve(Carver& c, const ssa_plan_s* p, int H, int d, int topk, BwdWs* w) {
   t.svb = c.take<int32_t>(U);
   t.sinfo = c.take<int4>(U);
   t.ioff = c.take<int32_t>(U + 1);
-  // unsplit units give at most nch items each; split pieces at most one item per partial row
-  t.item_cap = U * nch + kv_budget_rows(d);
+  // unsplit units give at most nch items each, split pieces at most one per partial row,
+  // key groups (at most one per unit) kg_pieces each
+  t.item_cap = U * nch + kv_budget_rows(d) + U * kg_pieces((int)M);
   t.items = c.take<int4>(t.item_cap);
-  t.xbase = c.take<int32_t>(NXCD + 1);
+  t.grp_meta = c.take<int4>(U);
+  t.grp_mem = c.take<int4>(U);
+  t.ngrp = c.take<int32_t>(1);
+  t.xbase = c.take<int32_t>(3 * (NXCD + 1));
   t.kpart = c.take<float>(kv_budget_rows(d) * 2 * d);
   if (w) *w = t;
   return c.off;
@@ -425,96 +441,221 @@ __device__ inline V wg_exclusive_scan(V x, V* sh) {
   return total;
 }
 
-// One workgroup: per sorted unit, its pieces (split while the running partial demand, in
-// key rows, stays within the budget), its item count and first item (its XCD's list base
-// plus its place in that list); xbase[x] = first item of XCD x's list, xbase[8] = total.
+// Item kinds, each run by its own key-side kernel: key-group pieces, units of more than 32
+// keys (or all units where the narrow form is not built), narrow units (at most 32 keys).
+constexpr int KV_GRP = 0, KV_UNIT = 1, KV_NARROW = 2, KV_KINDS = 3;
+
+// One workgroup.  Per sorted unit: tiny (a key group member), split into pieces, or whole,
+// taken in sorted order while the running partial demand (key rows) stays within the
+// budget; sinfo = {unit, pieces, partial row offset or -1, flags: 1 tiny, 2 narrow}.  Then,
+// one thread per head, the head's tiny units in sorted order are packed into key groups.
+// Items of kind k form 8 lists (one per XCD): list x of kind k holds items xbase[9k + x] ..
+// xbase[9k + x + 1] - 1 (xbase[9k + 8] = end of kind k).  Group pieces and narrow items go
+// to list i mod 8 by their index i; a wide unit's items stay together on XCD (sorted unit
+// mod 8), ioff = its first item.  A narrow unit's ioff is its first narrow item index.
 __global__ __launch_bounds__(1024) void k_kv_schedule(
-    const int32_t* __restrict__ order, int U, int M, const int32_t* __restrict__ inv_off,
+    const int32_t* __restrict__ order, int U, int M, int H, int narrow_ok, const int32_t* __restrict__ inv_off,
     const int32_t* __restrict__ blk_cell, const int32_t* __restrict__ cell_off,
     const int32_t* __restrict__ blk_off, int64_t budget, int4* __restrict__ sinfo,
-    int32_t* __restrict__ ioff, int32_t* __restrict__ xbase) {
+    int32_t* __restrict__ ioff, int32_t* __restrict__ xbase, int4* __restrict__ grp_meta,
+    int4* __restrict__ grp_mem, int32_t* __restrict__ ngrp, int4* __restrict__ items) {
   __shared__ int64_t sh64[1024];
   __shared__ int32_t sh32[1024];
-  __shared__ int32_t xtot[NXCD + 1];
+  __shared__ int32_t ubase[NXCD], ucount[NXCD];
+  __shared__ int32_t s_ng, s_n2;
   const int tid = threadIdx.x;
   const int per = (U + 1023) / 1024;
   const int s0 = min(U, tid * per), s1 = min(U, s0 + per);
-  auto unit_info = [&](int si, int& u, int& want, int& rows) {
+  const int GP = kg_pieces(M);
+  auto unit_info = [&](int si, int& u, int& want, int& rows, bool& cand) {
     u = order[si];
     const int b = u % M, cell = blk_cell[b];
-    const int nent = cell_off[cell + 1] - cell_off[cell] + inv_off[u + 1] - inv_off[u];
+    const int ninv = inv_off[u + 1] - inv_off[u];
+    const int nent = cell_off[cell + 1] - cell_off[cell] + ninv;
     want = (nent + KV_EP - 1) / KV_EP;
     rows = blk_off[b + 1] - blk_off[b];
+    cand = rows <= KG_TINY && ninv > 0;
+  };
+  auto demand = [&](int want, int rows, bool cand) -> int64_t {
+    return cand ? (int64_t)(1 + GP) * rows : (want > 1 ? (int64_t)want * rows : 0);
   };
   int64_t dsum = 0;
   for (int si = s0; si < s1; ++si) {
     int u, want, rows;
-    unit_info(si, u, want, rows);
-    if (want > 1) dsum += (int64_t)want * rows;
+    bool cand;
+    unit_info(si, u, want, rows, cand);
+    dsum += demand(want, rows, cand);
   }
   wg_exclusive_scan<int64_t>(dsum, sh64);
   int64_t dpre = sh64[tid];
   int isum[NXCD];
 #pragma unroll
   for (int x = 0; x < NXCD; ++x) isum[x] = 0;
+  int nsum = 0;  // narrow items
   for (int si = s0; si < s1; ++si) {
     int u, want, rows;
-    unit_info(si, u, want, rows);
-    const int64_t dem = want > 1 ? (int64_t)want * rows : 0;
-    const bool split = want > 1 && dpre + dem <= budget;
-    const int pieces = split ? want : 1;
-    sinfo[si] = make_int4(u, pieces, split ? (int)dpre : -1, 0);
+    bool cand;
+    unit_info(si, u, want, rows, cand);
+    const int64_t dem = demand(want, rows, cand);
+    const bool fits = dem > 0 && dpre + dem <= budget;
+    const bool tiny = cand && fits, split = !cand && fits;
+    const bool narrow = narrow_ok && rows <= 32;
+    const int pieces = tiny ? 1 + GP : (split ? want : 1);
+    sinfo[si] = make_int4(u, pieces, fits ? (int)dpre : -1, (tiny ? 1 : 0) | (narrow ? 2 : 0));
     dpre += dem;
-    const int n = (rows + KROWS - 1) / KROWS * pieces;
+    const int n = tiny ? 1 : (rows + KROWS - 1) / KROWS * pieces;
+    if (narrow) {
+      nsum += n;
+    } else {
 #pragma unroll
-    for (int x = 0; x < NXCD; ++x) isum[x] += (si % NXCD == x) ? n : 0;
+      for (int x = 0; x < NXCD; ++x) isum[x] += (si % NXCD == x) ? n : 0;
+    }
   }
+  __syncthreads();  // sinfo is complete (global writes of this workgroup)
+  // key groups: wave w packs the tiny units of heads w, w + 16, ... (sorted units h M ..
+  // h M + M - 1 of head h) in order, a group never spanning two heads; the 64 units of a
+  // chunk are read by the wave's lanes at once, then taken in order from the tiny ones'
+  // ballot.  Pass 0 counts groups and members per wave, pass 1 writes them.
+  const int wv = tid >> 6, ln = tid & 63;
+  __shared__ int32_t wng[16], wnm[16], wgb[16], wmb[16];
+  for (int pass = 0; pass < 2; ++pass) {
+    int g = 0, m = 0;
+    const int gb0 = pass ? wgb[wv] : 0, mb0 = pass ? wmb[wv] : 0;
+    for (int h = wv; h < H; h += 16) {
+      int keys = 0, mem = 0;
+      for (int c0 = h * M; c0 < (h + 1) * M; c0 += 64) {
+        const int si = c0 + ln;
+        int4 in = make_int4(0, 0, -1, 0);
+        int rows = 0;
+        if (si < (h + 1) * M) {
+          in = sinfo[si];
+          if (in.w & 1) rows = blk_off[in.x % M + 1] - blk_off[in.x % M];
+        }
+        uint64_t bal = __builtin_amdgcn_ballot_w64((in.w & 1) != 0);
+        while (bal) {
+          const int l = __builtin_ctzll(bal);
+          bal &= bal - 1;
+          const int r = __builtin_amdgcn_readlane(rows, l);
+          const int ub = __builtin_amdgcn_readlane(in.x, l) % M;
+          const int po = __builtin_amdgcn_readlane(in.z, l);
+          if (mem > 0 && (keys + r > KG_KEYS || mem == KG_MEM)) {  // close the open group
+            if (pass && ln == 0) grp_meta[gb0 + g] = make_int4(h, mem, mb0 + m - mem, keys);
+            ++g;
+            keys = mem = 0;
+          }
+          if (pass && ln == 0) grp_mem[mb0 + m] = make_int4(ub, keys, po, r);
+          keys += r;
+          ++mem;
+          ++m;
+        }
+      }
+      if (mem > 0) {
+        if (pass && ln == 0) grp_meta[gb0 + g] = make_int4(h, mem, mb0 + m - mem, keys);
+        ++g;
+      }
+    }
+    if (pass == 0) {
+      if (ln == 0) {
+        wng[wv] = g;
+        wnm[wv] = m;
+      }
+      __syncthreads();
+      if (tid == 0) {
+        int ga = 0, ma = 0;
+        for (int i = 0; i < 16; ++i) {
+          wgb[i] = ga;
+          wmb[i] = ma;
+          ga += wng[i];
+          ma += wnm[i];
+        }
+        s_ng = ga;
+      }
+      __syncthreads();
+    }
+  }
+  __syncthreads();
+  const int gtot = s_ng;
+  const int n2tot = wg_exclusive_scan<int32_t>(nsum, sh32);
+  int n2pre = sh32[tid];
+  if (tid == 0) {
+    *ngrp = gtot;
+    s_n2 = n2tot;
+  }
+  __syncthreads();
+  const int NGP = s_ng * GP, N2 = s_n2;
   int ipre[NXCD];
 #pragma unroll
   for (int x = 0; x < NXCD; ++x) {
     const int tot = wg_exclusive_scan<int32_t>(isum[x], sh32);
     ipre[x] = sh32[tid];
-    if (tid == 0) xtot[x] = tot;
+    if (tid == 0) ucount[x] = tot;
     __syncthreads();
   }
   if (tid == 0) {
     int acc = 0;
-    for (int x = 0; x < NXCD; ++x) {
-      xbase[x] = acc;
-      const int t = xtot[x];
-      xtot[x] = acc;
-      acc += t;
+    for (int x = 0; x < NXCD; ++x) {  // kind 0: group pieces
+      xbase[KV_GRP * 9 + x] = acc;
+      acc += (NGP + NXCD - 1 - x) / NXCD;
     }
-    xbase[NXCD] = acc;
+    for (int x = 0; x < NXCD; ++x) {  // kind 1: wide units
+      xbase[KV_UNIT * 9 + x] = acc;
+      ubase[x] = acc;
+      acc += ucount[x];
+    }
+    xbase[KV_GRP * 9 + 8] = xbase[KV_UNIT * 9];
+    for (int x = 0; x < NXCD; ++x) {  // kind 2: narrow units
+      xbase[KV_NARROW * 9 + x] = acc;
+      acc += (N2 + NXCD - 1 - x) / NXCD;
+    }
+    xbase[KV_UNIT * 9 + 8] = xbase[KV_NARROW * 9];
+    xbase[KV_NARROW * 9 + 8] = acc;
   }
   __syncthreads();
   for (int si = s0; si < s1; ++si) {
-    int u, want, rows;
-    unit_info(si, u, want, rows);
-    const int n = (rows + KROWS - 1) / KROWS * sinfo[si].y;
+    const int4 in = sinfo[si];
+    const int b = in.x % M, rows = blk_off[b + 1] - blk_off[b];
+    const int n = (in.w & 1) ? 1 : (rows + KROWS - 1) / KROWS * in.y;
+    if (in.w & 2) {
+      ioff[si] = n2pre;
+      n2pre += n;
+    } else {
 #pragma unroll
-    for (int x = 0; x < NXCD; ++x) {
-      if (si % NXCD == x) {
-        ioff[si] = xtot[x] + ipre[x];
-        ipre[x] += n;
+      for (int x = 0; x < NXCD; ++x) {
+        if (si % NXCD == x) {
+          ioff[si] = ubase[x] + ipre[x];
+          ipre[x] += n;
+        }
       }
     }
   }
+  // group items: piece-major within a group (group g piece p = item i = g GP + p)
+  for (int i = tid; i < NGP; i += 1024)
+    items[xbase[KV_GRP * 9 + i % NXCD] + i / NXCD] = make_int4(-(i / GP) - 1, i % GP, 0, 0);
 }
 
 // Items of each sorted unit: piece-major, key chunks inner (a piece's chunks read the same
-// query stream).
+// query stream); a tiny unit has one item, its window part.
 __global__ void k_kv_items(const int4* __restrict__ sinfo, const int32_t* __restrict__ ioff,
-                           const int32_t* __restrict__ blk_off, int U, int M, int4* __restrict__ items) {
+                           const int32_t* __restrict__ xbase, const int32_t* __restrict__ blk_off, int U, int M,
+                           int4* __restrict__ items) {
   const int si = blockIdx.x * blockDim.x + threadIdx.x;
   if (si >= U) return;
   const int4 in = sinfo[si];
   const int b = in.x % M, rows = blk_off[b + 1] - blk_off[b];
-  const int nch = (rows + KROWS - 1) / KROWS;
   int i = ioff[si];
+  // narrow item i goes to narrow list i mod 8; a wide unit's items are consecutive
+  auto put = [&](int4 v) {
+    if (in.w & 2) items[xbase[KV_NARROW * 9 + i % NXCD] + i / NXCD] = v;
+    else items[i] = v;
+    ++i;
+  };
+  if (in.w & 1) {  // tiny: the window part only (piece 0); the key group supplies the rest
+    put(make_int4(in.x, 0, -1, in.z));
+    return;
+  }
+  const int nch = (rows + KROWS - 1) / KROWS;
   for (int pc = 0; pc < in.y; ++pc)
-    for (int ch = 0; ch < nch; ++ch)
-      items[i++] = make_int4(in.x, ch, pc, in.z < 0 ? -1 : in.z + pc * rows);
+    for (int ch = 0; ch < nch; ++ch) put(make_int4(in.x, ch, pc, in.z < 0 ? -1 : in.z + pc * rows));
 }
 
 // Split units: dK, dV = the pieces' partials summed in piece order, plus the block's
@@ -532,11 +673,20 @@ __global__ __launch_bounds__(256) void k_kv_reduce(const int4* __restrict__ sinf
   const float* uv = ukv + (((int64_t)H + h) * Mp + b) * D;
   for (int idx = threadIdx.x; idx < rows * D; idx += 256) {
     const int kr = idx / D, c = idx % D;
-    float sk = 0.f, sv = 0.f;
-    for (int pc = 0; pc < in.y; ++pc) {
-      const float* src = kpart + ((int64_t)in.z + (int64_t)pc * rows + kr) * 2 * D;
-      sk += src[c];
-      sv += src[D + c];
+    float sk = 0.f, sv = 0.f;  // in piece order; eight pieces' loads in flight at once
+    for (int p0 = 0; p0 < in.y; p0 += 8) {
+      float ak[8], av[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float* src = kpart + ((int64_t)in.z + (int64_t)(p0 + i) * rows + kr) * 2 * D;
+        ak[i] = p0 + i < in.y ? src[c] : 0.f;
+        av[i] = p0 + i < in.y ? src[D + c] : 0.f;
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        sk += ak[i];
+        sv += av[i];
+      }
     }
     const int64_t t = perm[r0 + kr];
     dk[(t * H + h) * D + c] = sk + uk[c];
@@ -566,9 +716,10 @@ struct KvState {
 
 // Token and (lse, g, D) tables of one segment: positions s0 .. s0 + n - 1 of a query stream
 // (position -> sorted row r, branch x by row_of), three padded arrays of QPAD floats; the
-// last tile's rows past n get probability 0.  A thread's QSEG / NTH positions: rows first,
+// last tile's rows past n get probability 0.  MASK: row_of also gives the row's key mask
+// (bit m: the row attends to the keys of key-group member m), a fourth array.  A thread's QSEG / NTH positions: rows first,
 // then every load in flight at once.
-template <int DT, int NTH, typename RowOf>
+template <int DT, int NTH, bool MASK = false, typename RowOf>
 __device__ inline void fill_qtables(int32_t* qtok, float* qinf, int s0, int n, RowOf& row_of,
                                     const typename Tr<DT>::T* __restrict__ gates, const float* __restrict__ lse3,
                                     const float* __restrict__ D3, const int32_t* __restrict__ perm, int H,
@@ -576,13 +727,18 @@ __device__ inline void fill_qtables(int32_t* qtok, float* qinf, int s0, int n, R
   const int tid = threadIdx.x;
   constexpr int PER = QSEG / NTH;
   int rr[PER], xx[PER];
+  uint32_t mk[PER];
   int64_t tk[PER];
   float ls[PER], dd[PER], gg[PER];
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     rr[i] = 0;
     xx[i] = 0;
-    if (tid + i * NTH < n) row_of(s0 + tid + i * NTH, rr[i], xx[i]);
+    mk[i] = 0;
+    if (tid + i * NTH < n) {
+      if constexpr (MASK) row_of(s0 + tid + i * NTH, rr[i], xx[i], mk[i]);
+      else row_of(s0 + tid + i * NTH, rr[i], xx[i]);
+    }
   }
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
@@ -602,19 +758,23 @@ __device__ inline void fill_qtables(int32_t* qtok, float* qinf, int s0, int n, R
       qinf[tid + i * NTH] = ls[i];
       qinf[QPAD + tid + i * NTH] = gg[i];
       qinf[2 * QPAD + tid + i * NTH] = dd[i];
+      if constexpr (MASK) reinterpret_cast<uint32_t*>(qinf)[3 * QPAD + tid + i * NTH] = mk[i];
     }
   }
   if (tid < (KT - n % KT) % KT) {
     qinf[n + tid] = INFINITY;
     qinf[QPAD + n + tid] = 0.f;
     qinf[2 * QPAD + n + tid] = 0.f;
+    if constexpr (MASK) reinterpret_cast<uint32_t*>(qinf)[3 * QPAD + n + tid] = 0u;
   }
 }
 
 // dS and g P of a 32-query tile (queries as rows res_row(r, g) of tile t of the segment)
 // from its scores S and dP, with (lse, g, D) from the segment's tables.
+// MASK: a row whose key mask lacks bit mlane (the lane's key's group member) gets no weight.
+template <bool MASK = false>
 __device__ inline void tile_ds_pg(const ssa_f16v& sv, const ssa_f16v& dp, const float* qinf, int t, int g,
-                                  float sl2, ssa_f16v& ds, ssa_f16v& pg) {
+                                  float sl2, ssa_f16v& ds, ssa_f16v& pg, int mlane = 0) {
   // rows t KT + res_row(r, g) = t KT + 8 (r / 4) + 4 g + r % 4
   const float* base = qinf + t * KT + 4 * g;
 #pragma unroll
@@ -622,12 +782,19 @@ __device__ inline void tile_ds_pg(const ssa_f16v& sv, const ssa_f16v& dp, const 
     const float4 l4 = *reinterpret_cast<const float4*>(base + 8 * r4);
     const float4 g4 = *reinterpret_cast<const float4*>(base + QPAD + 8 * r4);
     const float4 d4 = *reinterpret_cast<const float4*>(base + 2 * QPAD + 8 * r4);
-    const float la[4] = {l4.x, l4.y, l4.z, l4.w}, ga[4] = {g4.x, g4.y, g4.z, g4.w},
-                da[4] = {d4.x, d4.y, d4.z, d4.w};
+    const float la[4] = {l4.x, l4.y, l4.z, l4.w}, da[4] = {d4.x, d4.y, d4.z, d4.w};
+    float ga[4] = {g4.x, g4.y, g4.z, g4.w};
+    if constexpr (MASK) {
+      const uint4 m4 = *reinterpret_cast<const uint4*>(base + 3 * QPAD + 8 * r4);
+      const uint32_t ma[4] = {m4.x, m4.y, m4.z, m4.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ga[e] = (ma[e] >> mlane) & 1u ? ga[e] : 0.f;  // g = 0: dS = gP = 0
+    }
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int r = 4 * r4 + e;
-      const float pr = fast_exp2(__builtin_fmaf(sv[r], sl2, -la[e]));
+      float pr = fast_exp2(__builtin_fmaf(sv[r], sl2, -la[e]));
+      if constexpr (MASK) pr = ga[e] != 0.f ? pr : 0.f;
       ds[r] = pr * (ga[e] * dp[r] - da[e]);
       pg[r] = ga[e] * pr;
     }
@@ -641,14 +808,14 @@ __device__ inline void tile_ds_pg(const ssa_f16v& sv, const ssa_f16v& dp, const 
 //   S = Q K^T, P = exp2(S sl2 - lse), dP = dO V^T, dS = P o (g dP - D),
 //   dv += (g P)^T dO, dk += dS^T Q
 // (dS and g P with the queries as the contraction index, read back from registers).
-template <int DT, int D, bool BUF, int NB, int NW, typename RowOf>
+template <int DT, int D, bool BUF, int NB, int NW, bool MASK = false, typename RowOf>
 __device__ inline void kv_stream(KvState<DT, D>& S, TileCopy<DT, D, NW>& tc, typename Tr<DT>::T* const* bufs,
                                  int32_t* qtok, float* qinf, int total, const typename Tr<DT>::T* __restrict__ q,
                                  const typename Tr<DT>::T* __restrict__ dout,
                                  const typename Tr<DT>::T* __restrict__ gates,
                                  const float* __restrict__ lse3, const float* __restrict__ D3,
                                  const int32_t* __restrict__ perm, int H, int h, int64_t N, float sl2,
-                                 bool wave_active, int wave, int lane, RowOf row_of) {
+                                 bool wave_active, int wave, int lane, RowOf row_of, int mlane = 0) {
   using C = Cfg<DT, D>;
   using T = typename Tr<DT>::T;
   using F = typename Tr<DT>::frag;
@@ -658,7 +825,7 @@ __device__ inline void kv_stream(KvState<DT, D>& S, TileCopy<DT, D, NW>& tc, typ
   for (int s0 = 0; s0 < total; s0 += QSEG) {
     const int n = min(QSEG, total - s0);
     __syncthreads();  // the previous segment's tiles have been read
-    fill_qtables<DT, NTH>(qtok, qinf, s0, n, row_of, gates, lse3, D3, perm, H, h, N);
+    fill_qtables<DT, NTH, MASK>(qtok, qinf, s0, n, row_of, gates, lse3, D3, perm, H, h, N);
     __syncthreads();
     // S = Q K^T and dP = dO V^T of a tile (waves without keys compute on zero key rows;
     // their results are not written)
@@ -689,7 +856,7 @@ __device__ inline void kv_stream(KvState<DT, D>& S, TileCopy<DT, D, NW>& tc, typ
     auto finish = [&](int t, const T* cur, const ssa_f16v& sv, const ssa_f16v& dp, auto&& next)
                       __attribute__((always_inline)) {
       ssa_f16v ds, pg;
-      tile_ds_pg(sv, dp, qinf, t, g, sl2, ds, pg);
+      tile_ds_pg<MASK>(sv, dp, qinf, t, g, sl2, ds, pg, mlane);
       // 16-bit types: the transposed fragments of the tile are read before the next copy is
       // issued (the transpose reads carry no alias information); fp32 reads them in place
       // (registers) and issues the copy after its MFMAs
@@ -857,11 +1024,12 @@ __device__ inline void kv_stream_narrow(KvState<DT, D>& S, typename Tr<DT>::T* b
   }
 }
 
-// Resident workgroups (a multiple of 8) take their XCD's list of items round-robin.
-// An item is 128 keys of a unit's block and one piece of its query stream; an unsplit unit
-// writes dK, dV (with the block's compressed-branch terms), a piece of a split unit writes
-// its partial sums to kpart.
-template <int DT, int D, bool BUF>
+// Resident workgroups (a multiple of 8) take their XCD's list of items of one kind
+// round-robin.  KV_UNIT: an item is 128 keys of a unit's block and one piece of its query
+// stream.  KV_NARROW: a unit of at most 32 keys, one piece (kv_stream_narrow).  KV_GRP: a
+// key-group piece.  An unsplit unit writes dK, dV (with the block's compressed-branch
+// terms); pieces write their partial sums to kpart.
+template <int DT, int D, bool BUF, int MODE>
 __global__ __launch_bounds__(64 * KW) void k_bwd_dkdv(
     const typename Tr<DT>::T* __restrict__ q, const typename Tr<DT>::T* __restrict__ kin,
     const typename Tr<DT>::T* __restrict__ vin, const typename Tr<DT>::T* __restrict__ gates,
@@ -870,71 +1038,98 @@ __global__ __launch_bounds__(64 * KW) void k_bwd_dkdv(
     const int32_t* __restrict__ blk_off, const int32_t* __restrict__ blk_cell,
     const int32_t* __restrict__ cell_off, const int32_t* __restrict__ cell_blk,
     const int4* __restrict__ items, const int32_t* __restrict__ xbase, const int32_t* __restrict__ inv_off,
-    const int32_t* __restrict__ inv_q, int M, int H, int64_t N, float scale, float sl2,
-    const float* __restrict__ ukv, int Mp, float* __restrict__ kpart, float* __restrict__ dk,
-    float* __restrict__ dv) {
+    const int32_t* __restrict__ inv_q, const int32_t* __restrict__ sel, int topk,
+    const int4* __restrict__ grp_meta, const int4* __restrict__ grp_mem, int M, int H, int64_t N,
+    float scale, float sl2, const float* __restrict__ ukv, int Mp, float* __restrict__ kpart,
+    float* __restrict__ dk, float* __restrict__ dv) {
   using C = Cfg<DT, D>;
   using T = typename Tr<DT>::T;
   using TC = TileCopy<DT, D, KW>;
   constexpr int NTH = 64 * KW;
-  // 16-bit, d <= 96: two more buffers, so that narrow key blocks get two per wave
-  constexpr bool NARROW = sizeof(T) == 2 && D <= 96;
-  constexpr int NB = stage_depth<DT, D, KW>(LDS_BYTES - 4096 - (NARROW ? 2 * TC::ELEMS * (int)sizeof(T) : 0),
-                                            QSEG * 20 + (3 * NTH + 1) * 4);
-  static_assert(!NARROW || (NB == 6 && KW == 4), "eight stage buffers for the narrow blocks");
-  static_assert(32 * D * 4 <= TC::ELEMS * (int)sizeof(T), "a wave's partial dK or dV fits a buffer");
+  constexpr bool NARROW = MODE == KV_NARROW;  // eight stage buffers, two per wave
+  constexpr bool MASK = MODE == KV_GRP;
+  constexpr int QPLANES = MASK ? 4 : 3;
+  constexpr int NB = NARROW ? 6
+                            : stage_depth<DT, D, KW>(LDS_BYTES - 4096, QSEG * 4 + QPLANES * QPAD * 4 + (3 * NTH + 1) * 4);
+  static_assert(!NARROW || KW == 4, "four waves with two buffers each");
+  static_assert(!NARROW || 32 * D * 4 <= TC::ELEMS * (int)sizeof(T), "a wave's partial dK or dV fits a buffer");
   SSA_STAGE_BUFFERS(T, TC::ELEMS, NB);
   __shared__ __attribute__((aligned(NARROW ? 1024 : 16))) T buf6[NARROW ? TC::ELEMS : 16 / sizeof(T)];
   __shared__ __attribute__((aligned(NARROW ? 1024 : 16))) T buf7[NARROW ? TC::ELEMS : 16 / sizeof(T)];
-
   __shared__ int32_t pre[NTH + 1];
   __shared__ int32_t lst_off[NTH];
-  __shared__ int32_t ent_x[NTH];
+  __shared__ int32_t ent_x[NTH];  // an entry's branch, or a key-group entry's member mask
   __shared__ int32_t qtok[QSEG];
-  __shared__ __attribute__((aligned(16))) float qinf[3 * QPAD];
+  __shared__ __attribute__((aligned(16))) float qinf[QPLANES * QPAD];  // lse, g, D (, mask)
+  __shared__ int32_t gmb[MASK ? KG_MEM : 1], gko[MASK ? KG_MEM + 1 : 1], gpr[MASK ? KG_MEM : 1],
+      grw[MASK ? KG_MEM : 1], wsum[KW];
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, c = lane & 31;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int x = blockIdx.x % NXCD, nx = gridDim.x / NXCD;
-  const int ib = xbase[x], ie = xbase[x + 1];
+  const int ib = xbase[MODE * 9 + x], ie = xbase[MODE * 9 + x + 1];
   TC tc;
   tc.init(wave, lane);
 #pragma unroll 1
   for (int it = ib + (int)blockIdx.x / NXCD; it < ie; it += nx) {
     const int4 item = items[it];
-    const int h = item.x / M, b = item.x % M, chunk = item.y, piece = item.z, prow = item.w;
-    const int r0 = blk_off[b], rows = blk_off[b + 1] - r0;
-    // a narrow block (at most 32 keys): every wave holds its keys and takes a share of the
-    // query tiles
-    const bool narrow = NARROW && rows <= 32;
-    const int kbase = narrow ? 0 : chunk * KROWS + wave * 32;
-    const bool kvalid = kbase + c < rows;
-    const bool wave_active = kbase < rows;
-    const int64_t ktok = perm[r0 + (kvalid ? kbase + c : 0)];
-    KvState<DT, D> S;
-    load_q<DT, D>(S.kf, kin + (ktok * H + h) * D, kvalid, lane);
-    load_q<DT, D>(S.vf, vin + (ktok * H + h) * D, kvalid, lane);
-#pragma unroll
-    for (int j = 0; j < C::NDV; ++j) S.dk[j] = S.dv[j] = zero16();
-    const int cell = blk_cell[b];
-    const int c0 = cell_off[cell], nwin = cell_off[cell + 1] - c0;
-    const int i0 = inv_off[item.x], ninv = inv_off[item.x + 1] - i0;
-    const int nent = nwin + ninv;  // window query blocks, then the selecting ones
-    const int e_lo = prow < 0 ? 0 : piece * KV_EP;
-    const int e_hi = prow < 0 ? nent : min(nent, e_lo + KV_EP);
-
-    for (int e0 = e_lo; e0 < e_hi; e0 += NTH) {
-      const int L = min(NTH, e_hi - e0);
-      __syncthreads();  // the previous tables and stages are no longer read
-      int sz = 0;
-      if (tid < L) {
-        const int e = e0 + tid;
-        const int qb = e < nwin ? cell_blk[c0 + e] : inv_q[i0 + e - nwin];
-        lst_off[tid] = blk_off[qb];
-        sz = blk_off[qb + 1] - blk_off[qb];
-        ent_x[tid] = e < nwin ? 2 : 1;
+    if constexpr (MODE == KV_GRP) {
+      // ---- key group piece: members' keys in slots 0 .. keys - 1 (member m from slot
+      // gko[m]); the query blocks gp KG_QB .. gp KG_QB + KG_QB - 1 whose selection holds a
+      // member, each row masked to those members
+      const int4 gm = grp_meta[-item.x - 1];  // {head, members, first member, keys}
+      const int gh = gm.x, nmem = gm.y, keys = gm.w, gp = item.y;
+      __syncthreads();  // the previous item's tables are no longer read
+      if (tid < nmem) {
+        const int4 mm = grp_mem[gm.z + tid];  // {block, first slot, partial row, rows}
+        gmb[tid] = mm.x;
+        gko[tid] = mm.y;
+        gpr[tid] = mm.z;
+        grw[tid] = mm.w;
       }
-      pre[tid + 1] = sz;
+      if (tid == 0) gko[nmem] = keys;
+      __syncthreads();
+      auto member_of = [&](int slot) __attribute__((always_inline)) {
+        int m = 0;  // last member starting at or before the slot
+        for (int i = 1; i < nmem; ++i) m = gko[i] <= slot ? i : m;
+        return m;
+      };
+      const int slot = wave * 32 + c;
+      const bool kvalid = slot < keys;
+      const int mlane = kvalid ? member_of(slot) : 0;
+      const int64_t ktok = kvalid ? perm[blk_off[gmb[mlane]] + slot - gko[mlane]] : 0;
+      KvState<DT, D> S;
+      load_q<DT, D>(S.kf, kin + (ktok * H + gh) * D, kvalid, lane);
+      load_q<DT, D>(S.vf, vin + (ktok * H + gh) * D, kvalid, lane);
+#pragma unroll
+      for (int j = 0; j < C::NDV; ++j) S.dk[j] = S.dv[j] = zero16();
+      static_assert(KG_QB <= NTH, "one entry per thread");
+      const int qb = gp * KG_QB + tid;
+      uint32_t msk = 0;
+      if (tid < KG_QB && qb < M) {
+        const int32_t* srow = sel + ((int64_t)gh * M + qb) * topk;
+        for (int t = 0; t < topk; ++t) {
+          const int sb = srow[t];
+          if (sb < 0) break;  // ids ascend, -1 padded at the end
+          for (int i = 0; i < nmem; ++i) msk |= gmb[i] == sb ? 1u << i : 0u;
+        }
+      }
+      // compaction in block order: wave ballots, then the waves' counts
+      const uint64_t bal = __builtin_amdgcn_ballot_w64(msk != 0);
+      if (lane == 0) wsum[wave] = __builtin_popcountll(bal);
+      pre[tid + 1] = 0;
       if (tid == 0) pre[0] = 0;
+      __syncthreads();
+      int pos = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0));
+      int L = 0;
+      for (int w2 = 0; w2 < KW; ++w2) {
+        pos += w2 < wave ? wsum[w2] : 0;
+        L += wsum[w2];
+      }
+      if (msk != 0) {
+        lst_off[pos] = blk_off[qb];
+        ent_x[pos] = (int)msk;
+        pre[pos + 1] = blk_off[qb + 1] - blk_off[qb];
+      }
       __syncthreads();
       if (L > 1) {
         for (int off = 1; off < NTH; off <<= 1) {
@@ -945,27 +1140,99 @@ __global__ __launch_bounds__(64 * KW) void k_bwd_dkdv(
         }
       }
       const int total = pre[L];
-      auto row_of = [&](int pos, int& r, int& x) __attribute__((always_inline)) {
-        int lo = 0, hi = L - 1;  // last entry starting at or before pos
-        while (lo < hi) {
-          const int mid = (lo + hi + 1) >> 1;
-          if (pre[mid] <= pos) lo = mid; else hi = mid - 1;
-        }
-        r = lst_off[lo] + (pos - pre[lo]);
-        x = ent_x[lo];
-      };
-      if constexpr (NARROW) {
-        if (narrow) {
-          kv_stream_narrow<DT, D, BUF, KW>(S, buf0, buf1, buf2, buf3, buf4, buf5, buf6, buf7, qtok, qinf, total, q,
-                                           dout, gates, lse3, D3, perm, H, h, N, sl2, wave, lane, row_of);
-          continue;
+      kv_stream<DT, D, BUF, NB, KW, true>(
+          S, tc, bufs, qtok, qinf, total, q, dout, gates, lse3, D3, perm, H, gh, N, sl2, true, wave, lane,
+          [&](int pos2, int& r, int& xb, uint32_t& mk) __attribute__((always_inline)) {
+            int lo = 0, hi = L - 1;  // last entry starting at or before pos2
+            while (lo < hi) {
+              const int mid = (lo + hi + 1) >> 1;
+              if (pre[mid] <= pos2) lo = mid; else hi = mid - 1;
+            }
+            r = lst_off[lo] + (pos2 - pre[lo]);
+            xb = 1;
+            mk = (uint32_t)ent_x[lo];
+          },
+          mlane);
+      // partial sums: group piece gp is piece 1 + gp of each member; lane holds column
+      // 32j + c of key slots wave 32 + res_row(r, g)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int sl = wave * 32 + res_row(r, g);
+        if (sl < keys) {
+          const int m = member_of(sl);
+          float* dst = kpart + ((int64_t)gpr[m] + (int64_t)(1 + gp) * grw[m] + (sl - gko[m])) * 2 * D;
+#pragma unroll
+          for (int j = 0; j < C::NDV; ++j) {
+            dst[32 * j + c] = scale * S.dk[j][r];
+            dst[D + 32 * j + c] = S.dv[j][r];
+          }
         }
       }
-      kv_stream<DT, D, BUF, NB, KW>(S, tc, bufs, qtok, qinf, total, q, dout, gates, lse3, D3, perm, H, h, N,
-                                    sl2, wave_active, wave, lane, row_of);
-    }
-    if constexpr (NARROW) {
-      if (narrow) {  // the waves' partial sums, added in wave order
+    } else {
+      const int h = item.x / M, b = item.x % M, chunk = item.y, piece = item.z, prow = item.w;
+      const int r0 = blk_off[b], rows = blk_off[b + 1] - r0;
+      // narrow (at most 32 keys): every wave holds the block's keys and takes a share of the
+      // query tiles
+      const int kbase = NARROW ? 0 : chunk * KROWS + wave * 32;
+      const bool kvalid = kbase + c < rows;
+      const bool wave_active = kbase < rows;
+      const int64_t ktok = perm[r0 + (kvalid ? kbase + c : 0)];
+      KvState<DT, D> S;
+      load_q<DT, D>(S.kf, kin + (ktok * H + h) * D, kvalid, lane);
+      load_q<DT, D>(S.vf, vin + (ktok * H + h) * D, kvalid, lane);
+#pragma unroll
+      for (int j = 0; j < C::NDV; ++j) S.dk[j] = S.dv[j] = zero16();
+      const int cell = blk_cell[b];
+      const int c0 = cell_off[cell], nwin = cell_off[cell + 1] - c0;
+      const int i0 = inv_off[item.x], ninv = inv_off[item.x + 1] - i0;
+      const int nent = nwin + ninv;  // window query blocks, then the selecting ones
+      // piece -1: a tiny unit's window part (its selecting query blocks are in a key group)
+      const int e_lo = prow < 0 || piece < 0 ? 0 : piece * KV_EP;
+      const int e_hi = prow < 0 ? nent : (piece < 0 ? nwin : min(nent, e_lo + KV_EP));
+
+      for (int e0 = e_lo; e0 < e_hi; e0 += NTH) {
+        const int L = min(NTH, e_hi - e0);
+        __syncthreads();  // the previous tables and stages are no longer read
+        int sz = 0;
+        if (tid < L) {
+          const int e = e0 + tid;
+          const int qb = e < nwin ? cell_blk[c0 + e] : inv_q[i0 + e - nwin];
+          lst_off[tid] = blk_off[qb];
+          sz = blk_off[qb + 1] - blk_off[qb];
+          ent_x[tid] = e < nwin ? 2 : 1;
+        }
+        pre[tid + 1] = sz;
+        if (tid == 0) pre[0] = 0;
+        __syncthreads();
+        if (L > 1) {
+          for (int off = 1; off < NTH; off <<= 1) {
+            const int t = (tid + 1 > off) ? pre[tid + 1 - off] : 0;
+            __syncthreads();
+            pre[tid + 1] += t;
+            __syncthreads();
+          }
+        }
+        const int total = pre[L];
+        auto row_of = [&](int pos, int& r, int& xb) __attribute__((always_inline)) {
+          int lo = 0, hi = L - 1;  // last entry starting at or before pos
+          while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (pre[mid] <= pos) lo = mid; else hi = mid - 1;
+          }
+          r = lst_off[lo] + (pos - pre[lo]);
+          xb = ent_x[lo];
+        };
+        if constexpr (NARROW)
+          kv_stream_narrow<DT, D, BUF, KW>(S, buf0, buf1, buf2, buf3, buf4, buf5, buf6, buf7, qtok, qinf, total, q,
+                                           dout, gates, lse3, D3, perm, H, h, N, sl2, wave, lane, row_of);
+        else
+          kv_stream<DT, D, BUF, NB, KW>(S, tc, bufs, qtok, qinf, total, q, dout, gates, lse3, D3, perm, H, h, N,
+                                        sl2, wave_active, wave, lane, row_of);
+      }
+      const float* uk = ukv + ((int64_t)h * Mp + b) * D;
+      const float* uv = ukv + (((int64_t)H + h) * Mp + b) * D;
+      if constexpr (NARROW) {
+        // the waves' partial sums, added in wave order
         __syncthreads();  // every wave's stream is done: the buffers are free
         float* pk = reinterpret_cast<float*>(wave == 0 ? buf0 : wave == 1 ? buf1 : wave == 2 ? buf2 : buf3);
         float* pv = reinterpret_cast<float*>(wave == 0 ? buf4 : wave == 1 ? buf5 : wave == 2 ? buf6 : buf7);
@@ -977,8 +1244,6 @@ __global__ __launch_bounds__(64 * KW) void k_bwd_dkdv(
             pv[res_row(r, g) * D + 32 * j + c] = S.dv[j][r];
           }
         __syncthreads();
-        const float* uk = ukv + ((int64_t)h * Mp + b) * D;
-        const float* uv = ukv + (((int64_t)H + h) * Mp + b) * D;
         for (int idx = tid; idx < rows * D; idx += NTH) {
           auto at = [&](const T* bf) __attribute__((always_inline)) { return reinterpret_cast<const float*>(bf)[idx]; };
           const float sk = ((at(buf0) + at(buf1)) + at(buf2)) + at(buf3);
@@ -994,41 +1259,38 @@ __global__ __launch_bounds__(64 * KW) void k_bwd_dkdv(
             dst[D + col] = sv;
           }
         }
-        continue;
-      }
-    }
-    // write: lane holds column 32j + c of keys res_row(r, g)
-    if (prow < 0) {
-      const float* uk = ukv + ((int64_t)h * Mp + b) * D;
-      const float* uv = ukv + (((int64_t)H + h) * Mp + b) * D;
-      float ukc[C::NDV], uvc[C::NDV];
+        __syncthreads();  // the buffers are read before the next item's copies
+      } else if (prow < 0) {
+        // lane holds column 32j + c of keys res_row(r, g)
+        float ukc[C::NDV], uvc[C::NDV];
 #pragma unroll
-      for (int j = 0; j < C::NDV; ++j) {
-        ukc[j] = uk[32 * j + c];
-        uvc[j] = uv[32 * j + c];
-      }
+        for (int j = 0; j < C::NDV; ++j) {
+          ukc[j] = uk[32 * j + c];
+          uvc[j] = uv[32 * j + c];
+        }
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int kr = kbase + res_row(r, g);
-        if (kr < rows) {
-          const int64_t t = perm[r0 + kr];
+        for (int r = 0; r < 16; ++r) {
+          const int kr = kbase + res_row(r, g);
+          if (kr < rows) {
+            const int64_t t = perm[r0 + kr];
 #pragma unroll
-          for (int j = 0; j < C::NDV; ++j) {
-            dk[(t * H + h) * D + 32 * j + c] = scale * S.dk[j][r] + ukc[j];
-            dv[(t * H + h) * D + 32 * j + c] = S.dv[j][r] + uvc[j];
+            for (int j = 0; j < C::NDV; ++j) {
+              dk[(t * H + h) * D + 32 * j + c] = scale * S.dk[j][r] + ukc[j];
+              dv[(t * H + h) * D + 32 * j + c] = S.dv[j][r] + uvc[j];
+            }
           }
         }
-      }
-    } else {
+      } else {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int kr = kbase + res_row(r, g);
-        if (kr < rows) {
-          float* dst = kpart + ((int64_t)prow + kr) * 2 * D;
+        for (int r = 0; r < 16; ++r) {
+          const int kr = kbase + res_row(r, g);
+          if (kr < rows) {
+            float* dst = kpart + ((int64_t)prow + kr) * 2 * D;
 #pragma unroll
-          for (int j = 0; j < C::NDV; ++j) {
-            dst[32 * j + c] = scale * S.dk[j][r];
-            dst[D + 32 * j + c] = S.dv[j][r];
+            for (int j = 0; j < C::NDV; ++j) {
+              dst[32 * j + c] = scale * S.dk[j][r];
+              dst[D + 32 * j + c] = S.dv[j][r];
+            }
           }
         }
       }
@@ -1182,31 +1444,39 @@ hipError_t run_backward(const ssa_plan_s* p, int H, int topk, float scale, const
   e = ssa_sort::radix_sort(sa, oa, sb2, ob, U, ssa_sort::bits_for((uint64_t)H * (2 * M + 1)), w.rank, w.hist,
                            w.part, s);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_kv_schedule, dim3(1), dim3(1024), 0, s, oa, U, M, w.inv_off, p->blk_cell, p->cell_off,
-                     p->blk_off, kv_budget_rows(D), w.sinfo, w.ioff, w.xbase);
-  hipLaunchKernelGGL(k_kv_items, dim3((U + 255) / 256), dim3(256), 0, s, w.sinfo, w.ioff, p->blk_off, U, M,
-                     w.items);
-  int dev = 0, cus = 0, per_cu = 0;
+  // narrow units (at most 32 keys) where the eight-buffer form fits: 16-bit, d <= 96
+  constexpr bool narrow_ok = sizeof(T) == 2 && D <= 96;
+  hipLaunchKernelGGL(k_kv_schedule, dim3(1), dim3(1024), 0, s, oa, U, M, H, narrow_ok ? 1 : 0, w.inv_off,
+                     p->blk_cell, p->cell_off, p->blk_off, kv_budget_rows(D), w.sinfo, w.ioff, w.xbase, w.grp_meta,
+                     w.grp_mem, w.ngrp, w.items);
+  hipLaunchKernelGGL(k_kv_items, dim3((U + 255) / 256), dim3(256), 0, s, w.sinfo, w.ioff, w.xbase, p->blk_off, U,
+                     M, w.items);
+  int dev = 0, cus = 0;
   if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
   if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
-  if (buf)
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_bwd_dkdv<DT, D, true>, 64 * KW, 0);
-  else
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_bwd_dkdv<DT, D, false>, 64 * KW, 0);
-  if (e != hipSuccess) return e;
-  const int64_t items_max = (int64_t)U * ((p->max_rows + KROWS - 1) / KROWS);  // an unsplit schedule
-  const int64_t resident = std::max<int64_t>(NXCD, (int64_t)cus * std::max(per_cu, 1) / NXCD * NXCD);
-  const unsigned grid = (unsigned)std::min<int64_t>(resident, (items_max + kv_budget_rows(D) + NXCD - 1) / NXCD * NXCD);
-  if (buf)
-    hipLaunchKernelGGL((k_bwd_dkdv<DT, D, true>), dim3(grid), dim3(64 * KW), 0, s,
-                     (const T*)q, (const T*)k, (const T*)v, (const T*)gates, (const T*)dout, fw.lse,
-                     w.D, p->perm, p->blk_off, p->blk_cell, p->cell_off, p->cell_blk, w.items, w.xbase,
-                     w.inv_off, va, M, H, N, scale, sl2, w.ukv, Mp, w.kpart, dk, dv);
-  else
-    hipLaunchKernelGGL((k_bwd_dkdv<DT, D, false>), dim3(grid), dim3(64 * KW), 0, s,
-                     (const T*)q, (const T*)k, (const T*)v, (const T*)gates, (const T*)dout, fw.lse,
-                     w.D, p->perm, p->blk_off, p->blk_cell, p->cell_off, p->cell_blk, w.items, w.xbase,
-                     w.inv_off, va, M, H, N, scale, sl2, w.ukv, Mp, w.kpart, dk, dv);
+  // one resident grid (a multiple of 8) per item kind; each kind's lists are read from xbase
+  auto launch_kind = [&](auto kernel) -> hipError_t {
+    int per_cu = 0;
+    hipError_t e2 = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 64 * KW, 0);
+    if (e2 != hipSuccess) return e2;
+    const unsigned grid = (unsigned)std::max<int64_t>(NXCD, (int64_t)cus * std::max(per_cu, 1) / NXCD * NXCD);
+    hipLaunchKernelGGL(kernel, dim3(grid), dim3(64 * KW), 0, s, (const T*)q, (const T*)k, (const T*)v,
+                       (const T*)gates, (const T*)dout, fw.lse, w.D, p->perm, p->blk_off, p->blk_cell, p->cell_off,
+                       p->cell_blk, w.items, w.xbase, w.inv_off, va, sel, topk, w.grp_meta, w.grp_mem, M, H, N, scale,
+                       sl2, w.ukv, Mp, w.kpart, dk, dv);
+    return hipSuccess;
+  };
+  if (buf) {
+    if ((e = launch_kind(k_bwd_dkdv<DT, D, true, KV_GRP>)) != hipSuccess) return e;
+    if ((e = launch_kind(k_bwd_dkdv<DT, D, true, KV_UNIT>)) != hipSuccess) return e;
+    if constexpr (narrow_ok)
+      if ((e = launch_kind(k_bwd_dkdv<DT, D, true, KV_NARROW>)) != hipSuccess) return e;
+  } else {
+    if ((e = launch_kind(k_bwd_dkdv<DT, D, false, KV_GRP>)) != hipSuccess) return e;
+    if ((e = launch_kind(k_bwd_dkdv<DT, D, false, KV_UNIT>)) != hipSuccess) return e;
+    if constexpr (narrow_ok)
+      if ((e = launch_kind(k_bwd_dkdv<DT, D, false, KV_NARROW>)) != hipSuccess) return e;
+  }
   hipLaunchKernelGGL((k_kv_reduce<D>), dim3(U), dim3(256), 0, s, w.sinfo, w.kpart, w.ukv, p->blk_off, p->perm,
                      M, Mp, H, dk, dv);
   return hipGetLastError();
