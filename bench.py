@@ -10,7 +10,7 @@ A step is one pass of the whole path over resident inputs: the block partition
 + selection, selected/window branches + gated combine).  HIP events on the launch
 stream time every stage of every step.  The CPU baseline is the float64 oracle
 timed on a bounded sample of the same workload on the host.
-Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu] [--no-bwd] [--copy-probe]
+Usage: python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu] [--no-bwd] [--no-full] [--copy-probe]
 """
 import argparse
 import json
@@ -64,6 +64,21 @@ def attended_pairs(plan_arrays, sel, window_is_block):
     return per_head, sizes
 
 
+def workload_record(sizes, sel):
+    """Per-run workload facts: blocks, occupancy histogram (block rows in powers of two),
+    sum of squared block sizes (window pairs) and the mean size of a selected block."""
+    edges = [1, 2, 4, 8, 16, 32, 64, 128, 256, 512, 1 << 30]
+    hist = np.histogram(sizes, bins=edges)[0].tolist()
+    chosen = sel[sel >= 0]
+    return {"blocks": int(len(sizes)),
+            "occupancy_hist": {f"{edges[i]}-{edges[i + 1] - 1}": int(hist[i]) for i in range(len(hist) - 1)
+                               if edges[i] <= sizes.max()},
+            "occupancy_min_median_mean_max": [int(sizes.min()), float(np.median(sizes)),
+                                              float(sizes.mean()), int(sizes.max())],
+            "sum_nb2": int((sizes.astype(np.int64) ** 2).sum()),
+            "mean_selected_block_rows": float(sizes[chosen].mean()) if chosen.size else 0.0}
+
+
 def cpu_baseline(inp, heads_sample):
     """The float64 oracle, as it stands, on `heads_sample` heads of the workload."""
     import oracle
@@ -84,6 +99,37 @@ def cpu_baseline(inp, heads_sample):
             "kind": "oracle",
             "sample": f"partition + pooling of all {H} heads, then all {part.M} blocks of "
                       f"{heads_sample} of {H} heads ({dt:.1f} s); tokens/s scaled by the head fraction"}
+
+
+def full_attention_timing(ssa, coords, dev, wl, torch, stream, sparse_fwd_ms, reps=2):
+    """Dense attention over every occupied voxel on the same kernels: a window cell covering
+    the whole grid makes the window branch full attention (every query attends to all N
+    keys); the selected and window branches' stage is timed (HIP events) and credited
+    4 d N^2 H FLOPs.  The ratio to the sparse forward is the speed-up the method gives here."""
+    q = dev["q"]
+    N, H, d = q.shape
+    plan = ssa.Plan(coords, wl.grid, wl.block, wl.grid)  # one window cell = the whole grid
+    out = torch.empty_like(q)
+    sel = torch.empty((H, plan.num_blocks, wl.topk), dtype=torch.int32, device="cuda")
+    ws = torch.empty(ssa.forward_workspace_size(plan, q.dtype, H, d, wl.topk), dtype=torch.uint8, device="cuda")
+    run = lambda st: ssa.forward(plan, q, dev["k"], dev["v"], dev["wk"], dev["wv"], dev["gates"], wl.topk, 0.0,
+                                 out=out, sel_out=sel, ws=ws, stages=st)
+    run(ssa.STAGE_POOL)
+    run(ssa.STAGE_SELECT)
+    run(ssa.STAGE_ATTEND)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        run(ssa.STAGE_ATTEND)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    flops = 4.0 * d * float(N) * float(N) * H
+    return {"ms": ms, "tflops": flops / (ms * 1e-3) / 1e12, "reps": reps,
+            "sparse_speedup": ms / sparse_fwd_ms,
+            "what": "window cell = whole grid (dense attention over all voxels) on the same kernels; "
+                    "selected/window stage only"}
 
 
 def backward_timing(ssa, plan, dev, wl, torch, stream, reps=5):
@@ -123,6 +169,7 @@ def main():
     ap.add_argument("--cpu-heads", type=int, default=22,
                     help="heads of the workload the CPU oracle runs (all 22: about 15 s)")
     ap.add_argument("--no-bwd", action="store_true", help="skip the backward timing")
+    ap.add_argument("--no-full", action="store_true", help="skip the dense full-attention baseline")
     ap.add_argument("--workload", default=WORKLOAD)
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device copy 3 times (HBM counter calibration)")
@@ -184,11 +231,13 @@ def main():
     stage_ms = {nm: float(np.mean([evs[s][i].elapsed_time(evs[s][i + 1]) for s in range(args.steps)]))
                 for i, nm in enumerate(names)}
     ms_step = wall * 1e3 / args.steps
+    step_ev = [evs[s][0].elapsed_time(evs[s][4]) for s in range(args.steps)]
     fwd_ms = stage_ms["pool"] + stage_ms["select"] + stage_ms["attend"]
 
     # credited work: 4 d FLOPs per attended (query, key, head) pair over the three branches
     arrays = {k: v.cpu().numpy() for k, v in plan.arrays().items()}
-    per_head, sizes = attended_pairs(arrays, sel.cpu().numpy(), plan.num_cells == plan.num_blocks)
+    sel_np = sel.cpu().numpy()
+    per_head, sizes = attended_pairs(arrays, sel_np, plan.num_cells == plan.num_blocks)
     flops = 4.0 * d * float(per_head.sum())
     M = plan.num_blocks
     cmp_flops = 4.0 * d * H * N * M               # the compressed branch alone
@@ -221,6 +270,8 @@ def main():
                          "tflops": flops / (fwd_ms * 1e-3) / 1e12,
                          "mfma_peak_frac": flops / (fwd_ms * 1e-3) / 1e12 / peak},
         "stage_ms": stage_ms,
+        "step_ms_events": {"median": float(np.median(step_ev)), "min": float(np.min(step_ev))},
+        "recorded": workload_record(sizes, sel_np),
         "credited_flops": flops,
         "algorithmic_bytes": alg_bytes,
         "roofline": {"kernel": "k_select (compressed branch + top-k)", "bound": "mfma",
@@ -231,6 +282,8 @@ def main():
     }
     if not args.no_bwd:
         res["backward"] = backward_timing(ssa, plan, dev, wl, torch, stream)
+    if not args.no_full:
+        res["full_attention"] = full_attention_timing(ssa, coords, dev, wl, torch, stream, fwd_ms)
     if not args.no_cpu:
         res["cpu_baseline"] = cpu_baseline(inp, min(args.cpu_heads, H))
     print(json.dumps(res))
