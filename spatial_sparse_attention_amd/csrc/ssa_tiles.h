@@ -208,39 +208,6 @@ struct Online {
   }
 };
 
-// S^T tile (keys x queries) from a K tile in LDS ([32][KROW]).
-template <int DT, int D>
-__device__ inline ssa_f16v st_tile(const typename Tr<DT>::T* kt, const typename Tr<DT>::frag* qf,
-                                   ssa_f16v acc, int lane) {
-  using C = Cfg<DT, D>;
-  const typename Tr<DT>::T* row = kt + (lane & 31) * C::KROW + (lane >> 5) * C::KPL;
-#pragma unroll
-  for (int ks = 0; ks < C::NKS; ++ks) acc = Tr<DT>::mma(load_frag<DT>(row + ks * C::KS), qf[ks], acc);
-  return acc;
-}
-
-// S tile (queries x keys) from a K tile in LDS.
-template <int DT, int D>
-__device__ inline ssa_f16v s_tile(const typename Tr<DT>::T* kt, const typename Tr<DT>::frag* qf,
-                                  ssa_f16v acc, int lane) {
-  using C = Cfg<DT, D>;
-  const typename Tr<DT>::T* row = kt + (lane & 31) * C::KROW + (lane >> 5) * C::KPL;
-#pragma unroll
-  for (int ks = 0; ks < C::NKS; ++ks) acc = Tr<DT>::mma(qf[ks], load_frag<DT>(row + ks * C::KS), acc);
-  return acc;
-}
-
-template <int DT, int D>
-__device__ inline void pv_tile(Online<D / 32>& st, const ssa_f16v& p, const VFrags<DT, D>& vf) {
-  using C = Cfg<DT, D>;
-#pragma unroll
-  for (int ks = 0; ks < C::PK; ++ks) {
-    const typename Tr<DT>::frag pf = p_frag<DT>(p, ks);
-#pragma unroll
-    for (int j = 0; j < C::NDV; ++j) st.o[j] = Tr<DT>::mma(vf.f[ks][j], pf, st.o[j]);
-  }
-}
-
 template <int DT, int D>
 __device__ inline void load_q(typename Tr<DT>::frag* qf, const typename Tr<DT>::T* qrow, bool valid,
                               int lane) {
@@ -289,90 +256,6 @@ __device__ inline void xcd_split(int id, int per, int& unit, int& member) {
 }
 
 // ------------------------------------------------------------------ gathered token tiles
-// A key (or query) set is a list of blocks, concatenated in sorted token order and cut into
-// 32-row tiles.  A stage holds the tile's first-operand rows ([32][KROW]) followed by its
-// second-operand rows ([32][VROW]), copied straight from two caller tensors [N,H,d] through
-// the token permutation.  Rows past the end of the set reuse the set's first row (finite
-// values; callers mask them).
-template <int DT, int D, int NW>
-struct Gather {
-  using C = Cfg<DT, D>;
-  static constexpr int KRC = C::KCH / KT, VRC = C::VCH / KT;  // chunks per padded row
-  static constexpr int NPOS = C::KCH + C::VCH;
-  static constexpr int NINSTR = (NPOS + 63) / 64;
-  static constexpr int NI = (NINSTR + NW - 1) / NW;  // copies per lane per tile
-  int32_t row[NI];    // tile row of each copy (-1: none)
-  int32_t goff[NI];   // element offset inside the token's head row, with bit 30 set for V
-  int32_t tok[NI];
-  __device__ inline void init(int wave, int lane) {
-#pragma unroll
-    for (int m = 0; m < NI; ++m) {
-      const int i = wave + m * NW, p = i * 64 + lane;
-      const bool isk = p < C::KCH;
-      const int q = isk ? p : p - C::KCH;
-      const int rr = isk ? q / KRC : q / VRC, ch = isk ? q % KRC : q % VRC;
-      const bool ok = i < NINSTR && p < NPOS && ch < C::CPR;
-      row[m] = ok ? rr : -1;
-      goff[m] = ch * C::EPC + (isk ? 0 : (1 << 30));
-    }
-  }
-  // tokens of this lane's copies for the tile starting at key k0 of a staged key segment
-  // (keytok: token of each of the segment's n keys, in LDS); rows past n take key 0
-  __device__ inline void fetch(const int32_t* keytok, int k0, int n) {
-#pragma unroll
-    for (int m = 0; m < NI; ++m) {
-      const int j = k0 + (row[m] < 0 ? 0 : row[m]);
-      tok[m] = keytok[j < n ? j : 0];
-    }
-  }
-  // tokens of this lane's copies for the tile starting at key k0
-  __device__ inline void lookup(int k0, int total, int L, const int32_t* pre, const int32_t* lst_off,
-                                const int32_t* __restrict__ perm) {
-#pragma unroll
-    for (int m = 0; m < NI; ++m) {
-      int j = k0 + (row[m] < 0 ? 0 : row[m]);
-      if (j >= total) j = 0;
-      int lo = 0, hi = L - 1;  // last list entry starting at or before key j (none to search
-      while (lo < hi) {        // when the list is one block)
-        const int mid = (lo + hi + 1) >> 1;
-        if (pre[mid] <= j) lo = mid; else hi = mid - 1;
-      }
-      tok[m] = perm[lst_off[lo] + (j - pre[lo])];
-    }
-  }
-  // BUF: buffer loads to LDS with 32-bit offsets from each tensor's head-h row (tensors
-  // below 4 GiB); else global loads to LDS.  The buffer form keeps the compiler's LDS read
-  // counting exact (with the global form it waits for every LDS read at once).
-  template <bool BUF>
-  __device__ inline void issue(typename Tr<DT>::T* stage, const typename Tr<DT>::T* kin,
-                               const typename Tr<DT>::T* vin, int H, int h, int wave) const {
-    using T = typename Tr<DT>::T;
-    if constexpr (BUF) {
-      const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(kin + h * D), 0, -1, 0x00020000);
-      const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(const_cast<T*>(vin + h * D), 0, -1, 0x00020000);
-#pragma unroll
-      for (int m = 0; m < NI; ++m) {
-        if (row[m] >= 0) {
-          const bool isv = goff[m] & (1 << 30);
-          const uint32_t off = ((uint32_t)tok[m] * (uint32_t)(H * D) + (uint32_t)(goff[m] & ((1 << 30) - 1))) * (uint32_t)sizeof(T);
-          lds_void_t* dst = (lds_void_t*)(stage + (wave + m * NW) * 64 * C::EPC);
-          if (isv) __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, dst, 16, off, 0, 0, 0);
-          else __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, dst, 16, off, 0, 0, 0);
-        }
-      }
-    } else {
-#pragma unroll
-      for (int m = 0; m < NI; ++m) {
-        if (row[m] >= 0) {
-          const bool isv = goff[m] & (1 << 30);
-          const T* src = (isv ? vin : kin) + ((int64_t)tok[m] * H + h) * D + (goff[m] & ((1 << 30) - 1));
-          dma16(src, stage + (wave + m * NW) * 64 * C::EPC);
-        }
-      }
-    }
-  }
-};
-
 // Copies of one gathered 32-key tile from the caller's K and V into LDS, 16 bytes per lane
 // and instruction: the K rows ([32][KROW]) at the start of the stage, the V rows ([32][VROW])
 // at VOFF.  K and V copies never share an instruction, so each instruction reads through one
