@@ -148,6 +148,7 @@ ssa_status ssa_forward_stages(ssa_plan plan, ssa_dtype dtype, int32_t heads, int
  * ssa_forward call with save_for_bwd != 0 on the same plan and inputs (read only).
  * ws: device workspace of at least ssa_backward_workspace_size(...) bytes.  Every
  * sum runs in a fixed order (no atomics), so results are bitwise reproducible.
+ * The plan must be within the forward's block limit (else SSA_ERR_UNSUPPORTED).
  * Asynchronous on `stream`.
  */
 size_t ssa_backward_workspace_size(ssa_plan plan, ssa_dtype dtype, int32_t heads, int32_t dim,

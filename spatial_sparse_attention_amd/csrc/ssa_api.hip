@@ -112,6 +112,7 @@ extern "C" ssa_status ssa_backward(ssa_plan p, ssa_dtype dt, int32_t H, int32_t 
   if (p->n == 0) return SSA_OK;
   if (!q || !k || !v || !wk || !wv || !gates || !sel || !dout || !dq || !dk || !dv || !dgates)
     return SSA_ERR_INVALID_ARG;
+  if (p->M > select_block_limit(dt, d)) return SSA_ERR_UNSUPPORTED;  // the forward's limit
   if (!fwd_ws || fwd_ws_bytes < ssa_forward_workspace_size(p, dt, H, d, topk, 1)) return SSA_ERR_WORKSPACE;
   if (!ws || ws_bytes < ssa_backward_workspace_size(p, dt, H, d, topk)) return SSA_ERR_WORKSPACE;
   Carver c(const_cast<void*>(fwd_ws));

@@ -62,10 +62,17 @@ struct BwdWs {
 // window part as an item (piece 0) and joins a key group: up to KG_KEYS keys of at most
 // KG_MEM tiny units of one head, which streams the union of its members' selecting query
 // blocks once, each row masked to the members that its block selected.  The union is cut
-// into KG_QB-block ranges of query blocks (group pieces 1, 2, ...).
+// into at most KG_GP ranges of at least KG_QB query blocks (group pieces 1, 2, ...).
 constexpr int KV_EP = 8;
-constexpr int KG_TINY = 32, KG_KEYS = 128, KG_MEM = 32, KG_QB = 16;
-__host__ __device__ inline int kg_pieces(int M) { return (M + KG_QB - 1) / KG_QB; }
+constexpr int KG_TINY = 32, KG_KEYS = 128, KG_MEM = 32, KG_QB = 16, KG_GP = 32;
+__host__ __device__ inline int kg_pieces(int M) {
+  const int p = (M + KG_QB - 1) / KG_QB;
+  return p < KG_GP ? p : KG_GP;
+}
+__host__ __device__ inline int kg_qbp(int M) {  // query blocks per group piece
+  const int gp = kg_pieces(M);
+  return (M + gp - 1) / gp;
+}
 inline int64_t kv_budget_rows(int d) { return (int64_t)(128 << 20) / (8 * d); }
 
 int cmp_chunks(int64_t Mp, int H) {
@@ -100,9 +107,9 @@ size_t carve(Carver& c, const ssa_plan_s* p, int H, int d, int topk, BwdWs* w) {
   t.svb = c.take<int32_t>(U);
   t.sinfo = c.take<int4>(U);
   t.ioff = c.take<int32_t>(U + 1);
-  // unsplit units give at most nch items each, split pieces at most one per partial row,
-  // key groups (at most one per unit) kg_pieces each
-  t.item_cap = U * nch + kv_budget_rows(d) + U * kg_pieces((int)M);
+  // unsplit units give at most nch items each; split pieces and key-group pieces at most
+  // one per partial row each (a piece's partial sums take at least one row)
+  t.item_cap = U * nch + 2 * kv_budget_rows(d);
   t.items = c.take<int4>(t.item_cap);
   t.grp_meta = c.take<int4>(U);
   t.grp_mem = c.take<int4>(U);
@@ -1074,8 +1081,8 @@ __global__ __launch_bounds__(64 * KW) void k_bwd_dkdv(
     const int4 item = items[it];
     if constexpr (MODE == KV_GRP) {
       // ---- key group piece: members' keys in slots 0 .. keys - 1 (member m from slot
-      // gko[m]); the query blocks gp KG_QB .. gp KG_QB + KG_QB - 1 whose selection holds a
-      // member, each row masked to those members
+      // gko[m]); the query blocks of piece gp whose selection holds a member, each row masked
+      // to those members
       const int4 gm = grp_meta[-item.x - 1];  // {head, members, first member, keys}
       const int gh = gm.x, nmem = gm.y, keys = gm.w, gp = item.y;
       __syncthreads();  // the previous item's tables are no longer read
@@ -1102,10 +1109,10 @@ __global__ __launch_bounds__(64 * KW) void k_bwd_dkdv(
       load_q<DT, D>(S.vf, vin + (ktok * H + gh) * D, kvalid, lane);
 #pragma unroll
       for (int j = 0; j < C::NDV; ++j) S.dk[j] = S.dv[j] = zero16();
-      static_assert(KG_QB <= NTH, "one entry per thread");
-      const int qb = gp * KG_QB + tid;
+      const int qbp = kg_qbp(M);  // at most NTH (M is within the forward's limit)
+      const int qb = gp * qbp + tid;
       uint32_t msk = 0;
-      if (tid < KG_QB && qb < M) {
+      if (tid < qbp && qb < M) {
         const int32_t* srow = sel + ((int64_t)gh * M + qb) * topk;
         for (int t = 0; t < topk; ++t) {
           const int sb = srow[t];
