@@ -38,6 +38,7 @@ size_t fwd_carve(Carver& c, const ssa_plan_s* p, ssa_dtype dt, int H, int d, int
     t.lse = c.take<float>((size_t)3 * H * n1);
     t.obr = c.take<float>((size_t)3 * H * n1 * d);
   }
+  t.lsec = save ? t.lse : c.take<float>((size_t)H * n1);
   if (w) *w = t;
   return c.off;
 }

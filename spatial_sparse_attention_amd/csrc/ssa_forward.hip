@@ -14,11 +14,12 @@
 // LDS transpose reads of the row-major value tile.
 //
 // The compressed branch runs twice over the pooled keys:
-//   pass 1 computes S^T = Ktil Q^T (a lane holds one query, 16 keys), keeps an
-//          online softmax, accumulates O^T, and yields o_c and the exact
-//          log-sum-exp;
-//   pass 2 computes S = Q Ktil^T (a lane holds one key, 16 queries), so the
-//          importance column sums over the block's queries are register sums.
+//   pass 1 (k_compress, over fixed chunks of the token order) computes
+//          S^T = Ktil Q^T (a lane holds one query, 16 keys), keeps an online
+//          softmax, accumulates O^T, and yields o_c and the exact log-sum-exp;
+//   pass 2 (k_select, per query block) computes S = Q Ktil^T (a lane holds one
+//          key, 16 queries), so the importance column sums over the block's
+//          queries are register sums.
 // The pooled keys are fp32; they enter the MFMA as two (f16) or three (bf16) dtype
 // planes whose sum reproduces the fp32 value, so the scores that decide the top-k
 // carry fp32-level error.
@@ -32,7 +33,8 @@
 namespace {
 
 using namespace ssa_dev;
-constexpr int SEL_WAVES = 8;      // compressed/select: waves per workgroup (256 rows per sweep)
+constexpr int CMP_WAVES = 8;      // compressed pass 1: waves per workgroup, 32 query rows each
+constexpr int SEL_WAVES = 8;      // importance pass: waves per workgroup (256 rows per sweep)
 constexpr int ATT_WAVES = 4;      // selected/window: waves per workgroup, 32 query rows each
 constexpr int ATT_ROWS = 32 * ATT_WAVES;
 
@@ -315,37 +317,209 @@ __device__ void topk_radix(const float* sig, int M, int topk, int32_t* __restric
   for (int t = keff + tid; t < topk; t += NTH) out[t] = -1;
 }
 
-// One workgroup per (query block, head), longest blocks first; the workgroup sweeps the block
-// 32 * SEL_WAVES rows at a time.
-//  Pass 1 (query-stationary): each wave owns a tile of 32 query rows and streams every pooled
-//  stage through two LDS buffers (online softmax: compressed output and lse); stage t + 1's
-//  copy is issued at step t.
-//  Pass 2 (key-stationary): the sweep's queries and lse go to LDS (the stage buffers); the
-//  (32-key tile, 32-query tile) pairs, key-tile major, are split into equal contiguous ranges,
-//  one per wave, so a wave keeps a key tile's fragments in registers while it walks query
-//  tiles, and column-sums the probabilities.  A key tile whose pairs lie in one wave's range
-//  goes straight into sigma; the ends of ranges are folded in wave order, so every sum is in
-//  a fixed order.
+// Compressed branch, pass 1 (query-stationary).  Every query attends to all pooled blocks of
+// its head, so this pass needs no block structure: the block-sorted token order is cut into
+// chunks of 32 * CMP_WAVES rows (units (head, chunk), head-major), and every wave but the
+// last of a head owns a full tile of 32 query rows.  The grid is resident: the units of XCD x
+// are the contiguous range [x per, (x + 1) per), so an XCD's L2 holds the pooled stages of the
+// few heads it works on, and its wpx workgroups take them in turn.  A workgroup's units form
+// one stream of pooled stages (ntv per unit) through a ring of NB LDS buffers, copies issued
+// NB - 1 steps ahead across unit bounds; the queries of the next unit are loaded during the
+// last step of the current one.  Each wave keeps an online softmax and writes its rows' o_c
+// and exact lse.
+template <int DT, int D>
+constexpr int cmp_depth() {
+  constexpr int bytes = (Cfg<DT, D>::STAGE * (int)sizeof(typename Tr<DT>::T) + 1023) / 1024 * 1024;
+  return LDS_BYTES / bytes >= 4 ? 4 : LDS_BYTES / bytes;
+}
+
+template <int DT, int D>
+__global__ __launch_bounds__(64 * CMP_WAVES) void k_compress(
+    const typename Tr<DT>::T* __restrict__ q, const typename Tr<DT>::T* __restrict__ pooled,
+    const int32_t* __restrict__ perm, int M, int Mp, int H, int64_t N, int nch, int per, int wpx,
+    float sl2, typename Tr<DT>::T* __restrict__ oc, float* __restrict__ lsec,
+    float* __restrict__ oc_save) {
+  using C = Cfg<DT, D>;
+  using T = typename Tr<DT>::T;
+  using F = typename Tr<DT>::frag;
+  constexpr int NS = C::NS;
+  constexpr int ROWS = 32 * CMP_WAVES;
+  constexpr int NB = cmp_depth<DT, D>();
+  static_assert(NB >= 2, "two pooled stages fit LDS");
+  constexpr int NCH1 = C::STAGE * sizeof(T) / 16;                // 16-byte chunks of a stage
+  constexpr int NI = ((NCH1 + 63) / 64 + CMP_WAVES - 1) / CMP_WAVES;  // copy instructions per wave
+  SSA_STAGE_BUFFERS(T, C::STAGE, NB);
+
+  const int x = blockIdx.x % 8, j = blockIdx.x / 8;
+  const int U = H * nch;
+  const int cx = max(0, min(U, (x + 1) * per) - x * per);  // units of this XCD
+  const int nmine = j < cx ? (cx - j + wpx - 1) / wpx : 0;
+  const int ntv = (M + C::PT - 1) / C::PT;  // stages holding real blocks
+  const int nsteps = nmine * ntv;
+  if (nsteps == 0) return;  // the whole workgroup
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, c = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int ntile = Mp / C::PT;
+  auto unit_of = [&](int m) __attribute__((always_inline)) { return x * per + j + m * wpx; };
+  auto tile_row = [&](int m) __attribute__((always_inline)) {  // first row of this wave's tile
+    return (int64_t)(unit_of(m) % nch) * ROWS + wave * 32;
+  };
+  auto perm_of = [&](int m) __attribute__((always_inline)) {  // token of this lane's row, or -1
+    const int64_t r = tile_row(m) + c;
+    return r < N ? perm[r] : -1;
+  };
+  auto load_unit_q = [&](F* dst, int m, int tok) __attribute__((always_inline)) {
+    load_q<DT, D>(dst, q + ((int64_t)(tok >= 0 ? tok : 0) * H + unit_of(m) / nch) * D, tok >= 0, lane);
+  };
+
+  // the next unit's queries are prefetched where the registers allow it
+  constexpr bool QPRE = D <= 96;
+  F qf[C::NKS], qn[QPRE ? C::NKS : 1];
+  int tok_next = 0;
+  if constexpr (QPRE) load_unit_q(qn, 0, perm_of(0));
+  Online<C::NDV> st;
+  const T* src = nullptr;
+  auto fetch = [&](int s) __attribute__((always_inline)) {
+    src = pooled + ((int64_t)(unit_of(s / ntv) / nch) * ntile + s % ntv) * C::STAGE;
+  };
+  auto issue = [&](T* dst) __attribute__((always_inline)) { dma_stage<CMP_WAVES, NI>(dst, src, NCH1, wave, lane); };
+  // unit mu's compressed output and lse (the online state still holds it)
+  auto flush = [&](int mu) __attribute__((always_inline)) {
+    const int64_t row0 = tile_row(mu);
+    if (row0 < N) {
+      const float ltot = xor32_sum(st.l);
+      const int64_t my_row = row0 + c;
+      if (my_row < N) {
+        const int h = unit_of(mu) / nch;
+        const float inv = 1.f / ltot;
+        T* orow = oc + (my_row * H + h) * D;
+        float* srow = oc_save ? oc_save + (my_row * H + h) * D : nullptr;
+        if (g == 0) lsec[(int64_t)h * N + my_row] = st.m + fast_log2(ltot);
+#pragma unroll
+        for (int jj = 0; jj < C::NDV; ++jj)
+#pragma unroll
+          for (int rq = 0; rq < 4; ++rq) {
+            const int col = 32 * jj + 8 * rq + 4 * g;
+            const float v0 = st.o[jj][4 * rq] * inv, v1 = st.o[jj][4 * rq + 1] * inv;
+            const float v2 = st.o[jj][4 * rq + 2] * inv, v3 = st.o[jj][4 * rq + 3] * inv;
+            store4(orow + col, v0, v1, v2, v3);
+            if (srow) store4(srow + col, v0, v1, v2, v3);
+          }
+      }
+    }
+  };
+  // The stream of steps: stage s lands in buffer s % NB; its copy is issued NB - 1 steps
+  // ahead.  Vector memory operations complete in issue order, so before step s a wave waits
+  // until only what it issued after stage s's copy is outstanding: the later stages' copies
+  // and, from the steps in between that began a unit, that unit's predecessor's output
+  // stores (E of them at least).  The stores thus never hold up a step; the copies issued
+  // after them land NB - 1 steps later, when the stores are long done.  A step stores the
+  // previous unit's outputs at a unit's first step, runs the scores' MFMAs, then issues its
+  // copy (which overlaps the MFMAs), the softmax and P.V.
+  constexpr int E = C::NDV * 4;  // output stores of a flush
+  auto flushed_at = [&](int s2) __attribute__((always_inline)) {
+    if (s2 < 0) return false;
+    const int m2 = s2 / ntv;
+    return s2 == m2 * ntv && m2 > 0 && tile_row(m2 - 1) < N;
+  };
+#pragma unroll
+  for (int u = 0; u < NB - 1; ++u)
+    if (u < nsteps) {
+      fetch(u);
+      issue(bufs[u]);
+    }
+  if (NB - 1 < nsteps) fetch(NB - 1);
+  for (int s0 = 0; s0 < nsteps; s0 += NB) {
+    static_for<0, NB>([&](auto uc) __attribute__((always_inline)) {
+      constexpr int u = decltype(uc)::value;
+      const int s = s0 + u;
+      if (s >= nsteps) return;
+      int nf = 0;
+#pragma unroll
+      for (int j = 1; j <= NB - 2; ++j) nf += flushed_at(s - j) ? 1 : 0;
+      vm_wait_kn<NI, E, (NB > 2 ? NB - 2 : 0)>(min(NB - 2, nsteps - 1 - s), nf);
+      lds_barrier();
+      T* cur = bufs[u];
+      auto next = [&]() __attribute__((always_inline)) {
+        if (s + NB - 1 < nsteps) issue(bufs[(u + NB - 1) % NB]);
+        if (s + NB < nsteps) fetch(s + NB);
+      };
+      const int m = s / ntv, t = s - m * ntv;
+      // next unit's queries: its tokens at step 0, its rows two steps before the end, so that
+      // the copies in flight need not drain to use them
+      if (t == 0) {
+        if constexpr (QPRE) {
+#pragma unroll
+          for (int ks = 0; ks < C::NKS; ++ks) qf[ks] = qn[ks];
+        } else {
+          load_unit_q(qf, m, perm_of(m));
+        }
+        if (m > 0) flush(m - 1);
+        st.init();
+        if constexpr (QPRE)
+          if (m + 1 < nmine) tok_next = perm_of(m + 1);
+      }
+      if constexpr (QPRE)
+        if (t == max(ntv - 2, 0) && m + 1 < nmine) load_unit_q(qn, m + 1, tok_next);
+      if (tile_row(m) < N) {
+        ssa_f16v a0, a1;
+        // value fragments read ahead for 16-bit types (fp32 ones would take 2*D registers)
+        constexpr bool VPRE = sizeof(T) == 2;
+        const T* vtt = cur + NS * C::KPLANE;
+        F vt[2][C::PK][C::NDV];
+        stage_scores<DT, D, true, VPRE>(cur + (lane & 31) * C::KROW + (lane >> 5) * C::KPL, qf, a0, a1,
+                                        vtt, vt, lane);
+        next();
+        if ((t + 1) * C::PT > M) {  // padding blocks
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            if (t * C::PT + res_row(r, g) >= M) a0[r] = -INFINITY;
+            if (t * C::PT + 32 + res_row(r, g) >= M) a1[r] = -INFINITY;
+          }
+        }
+        st.update2(a0, a1, sl2);
+#pragma unroll
+        for (int ks = 0; ks < C::PK; ++ks) {
+          const F p0 = p_frag<DT>(a0, ks), p1f = p_frag<DT>(a1, ks);
+#pragma unroll
+          for (int jj = 0; jj < C::NDV; ++jj) {
+            if constexpr (VPRE) {
+              st.o[jj] = Tr<DT>::mma(vt[0][ks][jj], p0, st.o[jj]);
+              st.o[jj] = Tr<DT>::mma(vt[1][ks][jj], p1f, st.o[jj]);
+            } else {
+              st.o[jj] = Tr<DT>::mma(vtt_frag<DT, D>(vtt, 0, ks, jj, lane), p0, st.o[jj]);
+              st.o[jj] = Tr<DT>::mma(vtt_frag<DT, D>(vtt, 32, ks, jj, lane), p1f, st.o[jj]);
+            }
+          }
+        }
+      } else {
+        next();
+      }
+    });
+  }
+  flush(nmine - 1);
+}
+
+// Compressed branch, pass 2 (key-stationary) and the top-k: one workgroup per (query block,
+// head), longest blocks first, sweeping the block 32 * SEL_WAVES rows at a time.  The sweep's
+// queries and their pass-1 lse go to LDS; the (32-key tile, 32-query tile) pairs, key-tile
+// major, are split into equal contiguous ranges, one per wave, so a wave keeps a key tile's
+// fragments in registers while it walks query tiles, and column-sums the probabilities.  A key
+// tile whose pairs lie in one wave's range goes straight into sigma; the ends of ranges are
+// folded in wave order, so every sum is in a fixed order.
 template <int DT, int D>
 __global__ __launch_bounds__(64 * SEL_WAVES) void k_select(
     const typename Tr<DT>::T* __restrict__ q, const typename Tr<DT>::T* __restrict__ pooled,
     const int32_t* __restrict__ perm, const int32_t* __restrict__ blk_off,
     const int32_t* __restrict__ lpt, int M, int Mp, int H, int64_t N, float sl2, int topk,
-    typename Tr<DT>::T* __restrict__ oc, int32_t* __restrict__ sel, float* __restrict__ lse_save,
-    float* __restrict__ oc_save, float* __restrict__ sigma_out) {
+    const float* __restrict__ lsec, int32_t* __restrict__ sel, float* __restrict__ sigma_out) {
   using C = Cfg<DT, D>;
   using T = typename Tr<DT>::T;
   using F = typename Tr<DT>::frag;
-  constexpr int NS = C::NS;
   constexpr int ROWS = 32 * SEL_WAVES;
-  // queries of a sweep in LDS for pass 2, half in each stage buffer: row stride QROW
+  // the sweep's queries, one 32-row tile per wave: row stride QROW
   constexpr int QROW = sizeof(T) == 2 ? D + 8 : D;
-  static_assert(ROWS / 2 * QROW <= C::STAGE, "half the sweep's queries fit a stage buffer");
-  __shared__ __attribute__((aligned(1024))) T stage0[C::STAGE];
-  __shared__ __attribute__((aligned(1024))) T stage1[C::STAGE];
-  auto qtile = [&](int u) __attribute__((always_inline)) {  // query tile u (32 rows) in LDS
-    return (u < SEL_WAVES / 2 ? stage0 : stage1) + (u % (SEL_WAVES / 2)) * 32 * QROW;
-  };
+  __shared__ __attribute__((aligned(1024))) T qlds[SEL_WAVES * 32 * QROW];
   __shared__ float lse_lds[ROWS];
   __shared__ float bpart[SEL_WAVES][2][32];  // column sums of a range's first / last key tile
   __shared__ int32_t bkt[SEL_WAVES][2];
@@ -363,104 +537,23 @@ __global__ __launch_bounds__(64 * SEL_WAVES) void k_select(
   const int nkt = (M + KT - 1) / KT;  // 32-key tiles holding real blocks
   const int nsw = (rows + ROWS - 1) / ROWS;
   const T* pstage = pooled + (int64_t)h * ntile * C::STAGE;
-  constexpr int NCH1 = C::STAGE * sizeof(T) / 16;
-  auto issue = [&](int t, T* dst) __attribute__((always_inline)) {
-    dma_contiguous<SEL_WAVES>(dst, pstage + (int64_t)t * C::STAGE, NCH1, wave, lane);
-  };
-  issue(0, stage0);
   for (int j = tid; j < Mp; j += 64 * SEL_WAVES) sig[j] = 0.f;
 
-  auto row_of = [&](int sw) __attribute__((always_inline)) { return sw * ROWS + wave * 32 + c; };
-  F qf[C::NKS];
-  {
-    const int my_row = row_of(0);
-    load_q<DT, D>(qf, q + ((int64_t)(my_row < rows ? perm[r0 + my_row] : 0) * H + h) * D, my_row < rows, lane);
-  }
-
   for (int sw = 0; sw < nsw; ++sw) {
-    const int my_row = row_of(sw);
-    const bool wave_active = sw * ROWS + wave * 32 < rows;
-    const bool valid = my_row < rows;
-    if (sw > 0) {  // the previous sweep's pass 2 is done with the stage buffers
-      issue(0, stage0);
+    {  // this wave's queries to LDS (natural row order, zero past the block), lse beside them
+      const int my_row = sw * ROWS + wave * 32 + c;
+      const bool valid = my_row < rows;
+      F qf[C::NKS];
       load_q<DT, D>(qf, q + ((int64_t)(valid ? perm[r0 + my_row] : 0) * H + h) * D, valid, lane);
-    }
-
-    // ---------------- pass 1: online softmax over all pooled keys -> o_c, lse
-    Online<C::NDV> st;
-    st.init();
-    auto p1 = [&](int t, T* cur, T* nxt) __attribute__((always_inline)) {
-      dma_wait();
-      __syncthreads();
-      if (t + 1 < ntile) issue(t + 1, nxt);
-      if (wave_active && t * C::PT < M) {
-        ssa_f16v a0, a1;
-        // value fragments read ahead for 16-bit types (fp32 ones would take 2*D registers)
-        constexpr bool VPRE = sizeof(T) == 2;
-        const T* vtt = cur + NS * C::KPLANE;
-        F vt[2][C::PK][C::NDV];
-        stage_scores<DT, D, true, VPRE>(cur + (lane & 31) * C::KROW + (lane >> 5) * C::KPL, qf, a0,
-                                        a1, vtt, vt, lane);
-        if ((t + 1) * C::PT > M) {  // padding blocks
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            if (t * C::PT + res_row(r, g) >= M) a0[r] = -INFINITY;
-            if (t * C::PT + 32 + res_row(r, g) >= M) a1[r] = -INFINITY;
-          }
-        }
-        st.update2(a0, a1, sl2);
-#pragma unroll
-        for (int ks = 0; ks < C::PK; ++ks) {
-          const F p0 = p_frag<DT>(a0, ks), p1f = p_frag<DT>(a1, ks);
-#pragma unroll
-          for (int j = 0; j < C::NDV; ++j) {
-            if constexpr (VPRE) {
-              st.o[j] = Tr<DT>::mma(vt[0][ks][j], p0, st.o[j]);
-              st.o[j] = Tr<DT>::mma(vt[1][ks][j], p1f, st.o[j]);
-            } else {
-              st.o[j] = Tr<DT>::mma(vtt_frag<DT, D>(vtt, 0, ks, j, lane), p0, st.o[j]);
-              st.o[j] = Tr<DT>::mma(vtt_frag<DT, D>(vtt, 32, ks, j, lane), p1f, st.o[j]);
-            }
-          }
-        }
-      }
-    };
-    for (int t = 0; t < ntile; t += 2) {  // ntile is even
-      p1(t, stage0, stage1);
-      p1(t + 1, stage1, stage0);
-    }
-    {  // this sweep's compressed output and lse
-      const float ltot = xor32_sum(st.l);
-      const float lse = st.m + fast_log2(ltot);
-      if (wave_active && valid) {
-        const float inv = 1.f / ltot;
-        T* orow = oc + ((int64_t)(r0 + my_row) * H + h) * D;
-        float* srow = oc_save ? oc_save + ((int64_t)(r0 + my_row) * H + h) * D : nullptr;
-        if (lse_save && g == 0) lse_save[(int64_t)h * N + r0 + my_row] = lse;
-#pragma unroll
-        for (int j = 0; j < C::NDV; ++j)
-#pragma unroll
-          for (int rq = 0; rq < 4; ++rq) {
-            const int col = 32 * j + 8 * rq + 4 * g;
-            const float v0 = st.o[j][4 * rq] * inv, v1 = st.o[j][4 * rq + 1] * inv;
-            const float v2 = st.o[j][4 * rq + 2] * inv, v3 = st.o[j][4 * rq + 3] * inv;
-            store4(orow + col, v0, v1, v2, v3);
-            if (srow) store4(srow + col, v0, v1, v2, v3);
-          }
-      }
-      // rows past the block get +inf, so their probabilities in pass 2 are exactly zero
-      if (g == 0) lse_lds[wave * 32 + c] = valid ? lse : INFINITY;
-    }
-    __syncthreads();  // every wave is done with the stage buffers
-    {  // this wave's queries to LDS, in the layout the fragments were read in
-      T* qrow = qtile(wave) + c * QROW + g * C::KPL;
+      T* qrow = qlds + (wave * 32 + c) * QROW + g * C::KPL;
 #pragma unroll
       for (int ks = 0; ks < C::NKS; ++ks) *reinterpret_cast<F*>(qrow + ks * C::KS) = qf[ks];
+      // rows past the block get +inf, so their probabilities are exactly zero
+      if (g == 0) lse_lds[wave * 32 + c] = valid ? lsec[(int64_t)h * N + r0 + my_row] : INFINITY;
     }
     if (tid < SEL_WAVES * 2) bkt[tid / 2][tid % 2] = -1;
     __syncthreads();
 
-    // ---------------- pass 2: importance column sums, key-stationary
     const int nq = (min(rows - sw * ROWS, ROWS) + 31) / 32;  // query tiles of this sweep
     const int npair = nkt * nq;
     const int pa = (int)((int64_t)npair * wave / SEL_WAVES), pb = (int)((int64_t)npair * (wave + 1) / SEL_WAVES);
@@ -493,7 +586,7 @@ __global__ __launch_bounds__(64 * SEL_WAVES) void k_select(
 #pragma unroll
           for (int ks = 0; ks < C::NKS; ++ks) kf[s2][ks] = load_frag<DT>(krow + s2 * C::KPLANE + ks * C::KS);
       }
-      const T* qrow = qtile(u) + (lane & 31) * QROW + (lane >> 5) * C::KPL;
+      const T* qrow = qlds + (u * 32 + (lane & 31)) * QROW + (lane >> 5) * C::KPL;
       ssa_f16v acc = zero16();
 #pragma unroll
       for (int ks = 0; ks < C::NKS; ++ks) {
@@ -514,7 +607,7 @@ __global__ __launch_bounds__(64 * SEL_WAVES) void k_select(
           if (kt >= 0 && kt * KT + tid < M) sig[kt * KT + tid] += bpart[w][sl][tid];
         }
     }
-    __syncthreads();  // sigma complete for this sweep; the stage buffers are free again
+    __syncthreads();  // sigma complete for this sweep; the query tiles are free again
   }
   if (sigma_out) {  // the top-k kernel takes it from here
     float* dst = sigma_out + ((int64_t)h * M + b) * Mp;
@@ -924,9 +1017,22 @@ hipError_t run_select(const ssa_plan_s* p, int H, int topk, float sl2, const voi
   using T = typename Tr<DT>::T;
   const int Mp = (int)pooled_rows(p->M);
   const size_t shm = (size_t)Mp * sizeof(float);
+  const int nch = (int)((p->n + 32 * CMP_WAVES - 1) / (32 * CMP_WAVES));
+  const int per = (int)(((int64_t)H * nch + 7) / 8);
+  int dev = 0, cus = 0, per_cu = 0;
+  hipError_t e;
+  if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
+  if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
+  if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_compress<DT, D>, 64 * CMP_WAVES, 0)) !=
+      hipSuccess)
+    return e;
+  const int wpx = std::max(1, std::min(per, cus * std::max(per_cu, 1) / 8));  // workgroups per XCD
+  hipLaunchKernelGGL((k_compress<DT, D>), dim3((unsigned)(8 * wpx)), dim3(64 * CMP_WAVES), 0, s,
+                     (const T*)q, (const T*)w.pooled, p->perm, (int)p->M, Mp, H, p->n, nch, per, wpx, sl2,
+                     (T*)w.oc, w.lsec, w.obr);
   hipLaunchKernelGGL((k_select<DT, D>), dim3((unsigned)(p->M * H)), dim3(64 * SEL_WAVES), shm, s,
                      (const T*)q, (const T*)w.pooled, p->perm, p->blk_off, p->lpt, (int)p->M, Mp, H,
-                     p->n, sl2, topk, (T*)w.oc, sel, w.lse, w.obr, w.sigma);
+                     p->n, sl2, topk, w.lsec, sel, w.sigma);
   if (w.sigma) {
     const int nrows = (int)(p->M * H);
     hipLaunchKernelGGL(k_topk, dim3((unsigned)((nrows + 3) / 4)), dim3(256), 0, s, w.sigma, (int)p->M,

@@ -79,6 +79,7 @@ struct FwdWs {
   void* oc;          // [N][H][d] compressed-branch output (dtype)
   int32_t* sel;      // [H][M][topk]
   float* sigma;      // [H][M][Mp] importance scores when the top-k runs as its own kernel, else null
+  float* lsec;       // [H][N] log2-sum-exp2 of the compressed branch's scaled scores (= lse plane 0)
   // saved for the backward (save_for_bwd only; else null)
   float* lse;        // [3][H][N] per-branch log2-sum-exp2 of the scaled scores
   float* obr;        // [3][N][H][d] the three branch outputs in fp32 (compressed, selected, window)

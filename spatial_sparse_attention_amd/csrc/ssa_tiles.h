@@ -367,6 +367,14 @@ __device__ inline void vm_wait() {
   __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
 }
 
+// Workgroup barrier of the copy pipelines: this wave's LDS accesses complete, then s_barrier,
+// in one asm statement whose memory clobber keeps the compiler from moving any memory access
+// across it.  __syncthreads() would not do here: its workgroup release fence makes the
+// compiler wait for every copy into LDS still in flight (vmcnt(0)), which drains the pipeline
+// at each step.  The caller has already waited (vm_wait) for the copies that the next step
+// reads, and the steps share data through LDS only.
+__device__ inline void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 // Waits until at most k tiles' copies (NI instructions each) are outstanding, k <= 4.
 template <int NI>
 __device__ inline void vm_wait_tiles(int k) {
@@ -394,7 +402,7 @@ constexpr int stage_depth(int budget, int other) {
 // addresses, issue(buffer) starts the copy (NI instructions per wave).
 template <int NB, int NI, typename T, typename Fetch, typename Issue, typename Body>
 __device__ inline void tile_pipeline(int ntile, T* const* bufs, Fetch&& fetch, Issue&& issue, Body&& body) {
-  static_assert(NB >= 3 && NB <= 6, "stage depth");
+  static_assert(NB >= 2 && NB <= 6, "stage depth");
   if (ntile <= 0) return;
 #pragma unroll
   for (int u = 0; u < NB - 1; ++u) {
@@ -410,7 +418,7 @@ __device__ inline void tile_pipeline(int ntile, T* const* bufs, Fetch&& fetch, I
       const int t = t0 + u;
       if (t < ntile) {
         vm_wait_tiles<NI>(min(NB - 2, ntile - 1 - t));
-        __syncthreads();
+        lds_barrier();
         body(t, bufs[u], [&]() __attribute__((always_inline)) {
           if (t + NB - 1 < ntile) issue(bufs[(u + NB - 1) % NB]);
           if (t + NB < ntile) fetch(t + NB);
@@ -427,6 +435,18 @@ __device__ inline void static_for(F&& f) {
     f(std::integral_constant<int, B>{});
     static_for<B + 1, E>(f);
   }
+}
+
+// Waits until at most kt * NI + nf * E of this wave's vector memory operations are
+// outstanding, for kt, nf in [0, K].
+template <int NI, int E, int K>
+__device__ inline void vm_wait_kn(int kt, int nf) {
+  static_for<0, K + 1>([&](auto a) __attribute__((always_inline)) {
+    static_for<0, K + 1>([&](auto b) __attribute__((always_inline)) {
+      constexpr int A = decltype(a)::value, B = decltype(b)::value;
+      if (kt == A && nf == B) vm_wait<A * NI + B * E>();
+    });
+  });
 }
 
 // The same stream with a one-tile lookahead inside each wave: step t first runs
@@ -449,7 +469,7 @@ __device__ inline void tile_pipeline_ahead(int ntile, T* const* bufs, Fetch&& fe
   }
   if (NB - 1 < ntile) fetch(NB - 1);
   vm_wait_tiles<NI>(min(NB - 2, ntile - 1));
-  __syncthreads();
+  lds_barrier();
   ahead(0, bufs[0], std::integral_constant<int, 0>{});
   for (int t0 = 0; t0 < ntile; t0 += UN) {
     static_for<0, UN>([&](auto uc) __attribute__((always_inline)) {
@@ -458,7 +478,7 @@ __device__ inline void tile_pipeline_ahead(int ntile, T* const* bufs, Fetch&& fe
       if (t < ntile) {
         if (t + 1 < ntile) {
           vm_wait_tiles<NI>(min(NB - 3, ntile - 2 - t));  // tile t + 1 landed
-          __syncthreads();
+          lds_barrier();
           ahead(t + 1, bufs[(u + 1) % NB], std::integral_constant<int, (u + 1) % 2>{});
         }
         body(t, bufs[u % NB], std::integral_constant<int, u % 2>{}, [&]() __attribute__((always_inline)) {
@@ -470,12 +490,28 @@ __device__ inline void tile_pipeline_ahead(int ntile, T* const* bufs, Fetch&& fe
   }
 }
 
+// Copy of nchunks 16-byte chunks (a whole pooled stage) from global g to LDS, spread over NW
+// waves in exactly NI instructions per wave, so that a wave can wait for a given number of
+// stages by counting instructions: a wave with fewer real instructions repeats the last one
+// (the same bytes to the same place).  Lane l of instruction i writes LDS base + 1024 i + 16 l.
+template <int NW, int NI>
+__device__ inline void dma_stage(void* lds, const void* g, int nchunks, int wave, int lane) {
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(g), 0, nchunks * 16, 0x00020000);
+  const int last = (nchunks - 1) >> 6;
+#pragma unroll
+  for (int m = 0; m < NI; ++m) {
+    const int i = min(wave + m * NW, last);
+    const int p = i * 64 + lane;
+    if (p < nchunks) __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)((char*)lds + i * 1024), 16, p * 16, 0, 0, 0);
+  }
+}
+
 // Declares the stage buffers buf0 .. buf5 of a kernel (those past NB are 16-byte stubs) and
 // the pointer table `bufs`.
 #define SSA_STAGE_BUFFERS(T, ELEMS, NB)                                                          \
   __shared__ __attribute__((aligned(1024))) T buf0[ELEMS];                                     \
   __shared__ __attribute__((aligned(1024))) T buf1[ELEMS];                                     \
-  __shared__ __attribute__((aligned(1024))) T buf2[ELEMS];                                     \
+  __shared__ __attribute__((aligned((NB) > 2 ? 1024 : 16))) T buf2[(NB) > 2 ? (ELEMS) : 16 / sizeof(T)]; \
   __shared__ __attribute__((aligned((NB) > 3 ? 1024 : 16))) T buf3[(NB) > 3 ? (ELEMS) : 16 / sizeof(T)]; \
   __shared__ __attribute__((aligned((NB) > 4 ? 1024 : 16))) T buf4[(NB) > 4 ? (ELEMS) : 16 / sizeof(T)]; \
   __shared__ __attribute__((aligned((NB) > 5 ? 1024 : 16))) T buf5[(NB) > 5 ? (ELEMS) : 16 / sizeof(T)]; \
