@@ -375,8 +375,22 @@ __global__ __launch_bounds__(64 * CMP_WAVES) void k_compress(
   // the next unit's queries are prefetched where the registers allow it
   constexpr bool QPRE = D <= 96;
   F qf[C::NKS], qn[QPRE ? C::NKS : 1];
-  int tok_next = 0;
-  if constexpr (QPRE) load_unit_q(qn, 0, perm_of(0));
+  bool qn_ok = false;
+  // prefetch: the loads always run (row 0 for a missing row) and the mask applies at the copy,
+  // so that nothing writes the registers while their loads are in flight
+  auto prefetch_q = [&](int m, int tok) __attribute__((always_inline)) {
+    qn_ok = tok >= 0;
+    const T* qrow = q + ((int64_t)(tok >= 0 ? tok : 0) * H + unit_of(m) / nch) * D + (lane >> 5) * C::KPL;
+#pragma unroll
+    for (int ks = 0; ks < C::NKS; ++ks) qn[ks] = load_frag<DT>(qrow + ks * C::KS);
+  };
+  if constexpr (QPRE) prefetch_q(0, perm_of(0));
+  // the next unit's tokens come by a copy into LDS (lanes 0-7 of a wave, 16 bytes each), so
+  // that no register load has to be waited for inside the stream; rows past N read padding
+  // inside the token array's 256-byte slot and are not used
+  __shared__ int32_t ptok[CMP_WAVES][32];
+  const __amdgpu_buffer_rsrc_t rperm =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<int32_t*>(perm), 0, (int)((N + 3) / 4 * 16), 0x00020000);
   Online<C::NDV> st;
   const T* src = nullptr;
   auto fetch = [&](int s) __attribute__((always_inline)) {
@@ -450,17 +464,27 @@ __global__ __launch_bounds__(64 * CMP_WAVES) void k_compress(
       if (t == 0) {
         if constexpr (QPRE) {
 #pragma unroll
-          for (int ks = 0; ks < C::NKS; ++ks) qf[ks] = qn[ks];
+          for (int ks = 0; ks < C::NKS; ++ks) qf[ks] = qn_ok ? qn[ks] : zero_frag<DT>();
         } else {
           load_unit_q(qf, m, perm_of(m));
         }
+        if constexpr (QPRE)
+          if (m + 1 < nmine && lane < 8)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rperm, (lds_void_t*)&ptok[wave][0], 16,
+                                                     (uint32_t)((tile_row(m + 1) + 4 * lane) * 4), 0, 0, 0);
         if (m > 0) flush(m - 1);
         st.init();
-        if constexpr (QPRE)
-          if (m + 1 < nmine) tok_next = perm_of(m + 1);
       }
-      if constexpr (QPRE)
-        if (t == max(ntv - 2, 0) && m + 1 < nmine) load_unit_q(qn, m + 1, tok_next);
+      // the next unit's rows, once the token copy is covered by the stage waits (NB - 1 steps
+      // on; a unit shorter than that waits for it)
+      if constexpr (QPRE) {
+        const int tq = min(NB - 1, ntv - 1);
+        if (t == tq && m + 1 < nmine) {
+          if (tq < NB - 1) vm_wait<0>();
+          const int64_t r = tile_row(m + 1) + c;
+          prefetch_q(m + 1, r < N ? ptok[wave][c] : -1);
+        }
+      }
       if (tile_row(m) < N) {
         ssa_f16v a0, a1;
         // value fragments read ahead for 16-bit types (fp32 ones would take 2*D registers)
