@@ -30,8 +30,8 @@ PEAK_F32_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
 
 
-def select_traffic():
-    """HBM bytes per k_select dispatch at this workload from the committed rocprofv3 summary
+def attend_traffic():
+    """HBM bytes per k_attend dispatch at this workload from the committed rocprofv3 summary
     (FETCH_SIZE + WRITE_SIZE, calibrated), or None when the kernel sources it was measured on
     have changed since (digest mismatch) or the summary is missing."""
     import hashlib
@@ -245,6 +245,10 @@ def main():
     alg_bytes = N * H * es * (4 * d + 3) + 12 * N + 2 * d * d * es
     peak = PEAK_F32_TFLOPS if wl.dtype == "f32" else PEAK_F16_TFLOPS
     sel_tflops = cmp_flops / (stage_ms["select"] * 1e-3) / 1e12
+    # the dominant kernel: k_attend, the attend stage's only launch (selected + window branches
+    # and the combine), credited 4 d FLOPs per attended selected or window pair
+    att_flops = flops - cmp_flops
+    att_tflops = att_flops / (stage_ms["attend"] * 1e-3) / 1e12
     res = {
         "metric": "SSA fwd tokens/s and TFLOP/s (% MFMA peak) at 80k voxels, 22h×96d fp16",
         "value": N / (ms_step * 1e-3),
@@ -274,11 +278,14 @@ def main():
         "recorded": workload_record(sizes, sel_np),
         "credited_flops": flops,
         "algorithmic_bytes": alg_bytes,
-        "roofline": {"kernel": "k_select (compressed branch + top-k)", "bound": "mfma",
-                     "achieved": sel_tflops, "peak": peak, "unit": "TFLOP/s",
-                     "frac": sel_tflops / peak,
-                     "traffic": select_traffic() if wl.name == WORKLOAD else None,
-                     "work_per_launch_flops": cmp_flops},
+        "roofline": {"kernel": "k_attend (selected + window branches, gated combine)", "bound": "mfma",
+                     "achieved": att_tflops, "peak": peak, "unit": "TFLOP/s",
+                     "frac": att_tflops / peak,
+                     "traffic": attend_traffic() if wl.name == WORKLOAD else None,
+                     "work_per_launch_flops": att_flops},
+        "compressed_branch": {"kernels": "k_compress + k_select + k_topk", "ms": stage_ms["select"],
+                              "tflops": sel_tflops, "mfma_peak_frac": sel_tflops / peak,
+                              "work_flops": cmp_flops},
     }
     if not args.no_bwd:
         res["backward"] = backward_timing(ssa, plan, dev, wl, torch, stream)
