@@ -145,6 +145,26 @@ def test_forward_full_sampled(name):
     assert (np.diff(sel[:, :, :kk], axis=2) > 0).all()
 
 
+@pytest.mark.parametrize("dtype,dim", [("f32", 32), ("f16", 128), ("bf16", 96)])
+def test_forward_sampled_resident_streams(dtype, dim):
+    """The torus geometry (20,000 voxels) at 16 heads: 1,264 (head, 256-row chunk) units, so
+    each resident compressed-branch workgroup streams several units back to back (output
+    stores and next-unit query prefetch inside the stream); covers the fp32 path, the
+    d = 128 path without query prefetch (three stage buffers) and bf16 at d = 96."""
+    wl, base = _workload("torus20k")
+    inp = W.random_inputs(base["coords"], 16, dim, dtype, seed=21, grid=wl.grid)
+    inp.update(block=wl.block, window=wl.window, topk=wl.topk)
+    out, sel, plan = gpu_forward(inp)
+    M = plan.num_blocks
+    a = _plan_arrays(plan)
+    sizes = np.diff(a["blk_off"])
+    rng = np.random.default_rng(5)
+    blocks = list(np.argsort(-sizes, kind="stable")[:2]) + list(rng.choice(M, 6, replace=False))
+    items = sorted({(int(rng.integers(0, 16)), int(b)) for b in blocks})
+    check_items(inp, out, sel, items)
+    assert np.isfinite(out).all()
+
+
 def test_forward_deterministic():
     wl, inp = _workload("torus20k")
     o1, s1, plan = gpu_forward(inp)
