@@ -219,6 +219,42 @@ __global__ void k_block_stats(const int32_t* __restrict__ blk_off, int M, int n,
   ids[b] = b;
 }
 
+// Longest-first block order for up to LPT_RANK_MAX blocks in one workgroup: block i goes to
+// position #{j : size_j > size_i} + #{j < i : size_j == size_i} (sizes in LDS, every thread
+// reading the same entry at a time), which is the stable order by descending size; also the
+// largest block size.  Replaces a three-pass radix sort of a few hundred keys.
+constexpr int LPT_RANK_MAX = 8192;
+__global__ __launch_bounds__(1024) void k_lpt_rank(const int32_t* __restrict__ blk_off, int M,
+                                                   int32_t* __restrict__ lpt, int32_t* __restrict__ max_rows) {
+  __shared__ int32_t sz[LPT_RANK_MAX];
+  __shared__ int32_t wmax[16];
+  const int tid = threadIdx.x;
+  int mx = 0;
+  for (int i = tid; i < M; i += 1024) {
+    const int v = blk_off[i + 1] - blk_off[i];
+    sz[i] = v;
+    mx = max(mx, v);
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) mx = max(mx, __shfl_xor(mx, off));
+  if ((tid & 63) == 0) wmax[tid >> 6] = mx;
+  __syncthreads();
+  for (int i = tid; i < M; i += 1024) {
+    const int si = sz[i];
+    int r = 0;
+    for (int j = 0; j < M; ++j) {
+      const int sj = sz[j];
+      r += (sj > si || (sj == si && j < i)) ? 1 : 0;
+    }
+    lpt[r] = i;
+  }
+  if (tid == 0) {
+    int m = 0;
+    for (int w = 0; w < 16; ++w) m = max(m, wmax[w]);
+    *max_rows = m;
+  }
+}
+
 __global__ void k_cell_keys(const int32_t* __restrict__ blk_key, int M, int3 dims, int ratio,
                             bool single, int3 cdims, uint32_t* __restrict__ ckey,
                             int32_t* __restrict__ ids) {
@@ -406,13 +442,17 @@ extern "C" ssa_status ssa_plan_create(const int32_t* coords, int64_t n, const in
   p->M = M;
 
   // longest-first block order (stable: ties keep ascending block id)
-  hipLaunchKernelGGL(k_block_stats, dim3((M + 255) / 256), dim3(256), 0, stream, w.blk_off, M, ni,
-                     w.key_a, w.val_a, w.counters + 1);
-  ka = w.key_a; kb = w.key_b; va = w.val_a; vb = w.val_b;
-  if (radix_sort(ka, va, kb, vb, M, bits_for((uint64_t)n), w.rank, w.hist, w.scan_part, stream) != hipSuccess)
-    return fail(SSA_ERR_HIP);
-  if (hipMemcpyAsync(w.lpt, va, M * sizeof(int32_t), hipMemcpyDeviceToDevice, stream) != hipSuccess)
-    return fail(SSA_ERR_HIP);
+  if (M <= LPT_RANK_MAX) {
+    hipLaunchKernelGGL(k_lpt_rank, dim3(1), dim3(1024), 0, stream, w.blk_off, M, w.lpt, w.counters + 1);
+  } else {
+    hipLaunchKernelGGL(k_block_stats, dim3((M + 255) / 256), dim3(256), 0, stream, w.blk_off, M, ni,
+                       w.key_a, w.val_a, w.counters + 1);
+    ka = w.key_a; kb = w.key_b; va = w.val_a; vb = w.val_b;
+    if (radix_sort(ka, va, kb, vb, M, bits_for((uint64_t)n), w.rank, w.hist, w.scan_part, stream) != hipSuccess)
+      return fail(SSA_ERR_HIP);
+    if (hipMemcpyAsync(w.lpt, va, M * sizeof(int32_t), hipMemcpyDeviceToDevice, stream) != hipSuccess)
+      return fail(SSA_ERR_HIP);
+  }
 
   // window cells as groups of blocks
   if (p->window_is_block) {
