@@ -524,91 +524,128 @@ __global__ __launch_bounds__(64 * CMP_WAVES) void k_compress(
   flush(nmine - 1);
 }
 
-// Compressed branch, pass 2 (key-stationary) and the top-k: one workgroup per (query block,
-// head), longest blocks first, sweeping the block 32 * SEL_WAVES rows at a time.  The sweep's
-// queries and their pass-1 lse go to LDS; the (32-key tile, 32-query tile) pairs, key-tile
-// major, are split into equal contiguous ranges, one per wave, so a wave keeps a key tile's
-// fragments in registers while it walks query tiles, and column-sums the probabilities.  A key
-// tile whose pairs lie in one wave's range goes straight into sigma; the ends of ranges are
-// folded in wave order, so every sum is in a fixed order.
-template <int DT, int D>
+// Compressed branch, pass 2 (key-stationary) and the top-k.  One workgroup per (group of G
+// consecutive query blocks in longest-first order, head): with small blocks several blocks
+// share each pooled key tile the workgroup loads (G = 1 for blocks of a few hundred rows).
+// The group's 32-row query tiles (a tile never mixes blocks) are taken SEL_WAVES at a time
+// (a sweep): their queries and pass-1 lse go to LDS; the (32-key tile, query tile) pairs,
+// key-tile major, are split into equal contiguous ranges, one per wave, so a wave keeps a key
+// tile's fragments in registers while it walks query tiles, and column-sums the
+// probabilities into the importance row of the tile's block (one row per member in LDS).  A
+// (key tile, block) segment that lies in one wave's range goes straight into the row; the
+// pieces of segments cut by range ends are added in wave order, so every sum is in a fixed
+// order.
+constexpr int SEL_GMAX = 8;  // blocks per workgroup at most
+template <int DT, int D, bool GRP>
 __global__ __launch_bounds__(64 * SEL_WAVES) void k_select(
     const typename Tr<DT>::T* __restrict__ q, const typename Tr<DT>::T* __restrict__ pooled,
     const int32_t* __restrict__ perm, const int32_t* __restrict__ blk_off,
-    const int32_t* __restrict__ lpt, int M, int Mp, int H, int64_t N, float sl2, int topk,
+    const int32_t* __restrict__ lpt, int M, int Mp, int H, int64_t N, float sl2, int topk, int G,
     const float* __restrict__ lsec, int32_t* __restrict__ sel, float* __restrict__ sigma_out) {
   using C = Cfg<DT, D>;
   using T = typename Tr<DT>::T;
   using F = typename Tr<DT>::frag;
-  constexpr int ROWS = 32 * SEL_WAVES;
   // the sweep's queries, one 32-row tile per wave: row stride QROW
   constexpr int QROW = sizeof(T) == 2 ? D + 8 : D;
   __shared__ __attribute__((aligned(1024))) T qlds[SEL_WAVES * 32 * QROW];
-  __shared__ float lse_lds[ROWS];
-  __shared__ float bpart[SEL_WAVES][2][32];  // column sums of a range's first / last key tile
-  __shared__ int32_t bkt[SEL_WAVES][2];
+  __shared__ float lse_lds[SEL_WAVES * 32];
+  __shared__ float bpart[SEL_WAVES][2][32];  // column sums of a range's first / last segment
+  __shared__ int32_t bkt[SEL_WAVES][2];      // their key tile * SEL_GMAX + member, -1 none
+  __shared__ int32_t mb[SEL_GMAX], mr0[SEL_GMAX], mrows[SEL_GMAX], mtp[SEL_GMAX + 1];
   __shared__ uint32_t hist[256];
   __shared__ uint32_t bcast[2];
   __shared__ uint32_t wcnt[2][SEL_WAVES];
-  extern __shared__ float sig[];  // [Mp]
+  extern __shared__ float sig[];  // [G][Mp]
 
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, c = lane & 31;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int h = blockIdx.x % H;  // consecutive workgroups: the heads of one block
-  const int b = lpt[blockIdx.x / H];
-  const int r0 = blk_off[b], rows = blk_off[b + 1] - r0;
+  const int h = blockIdx.x % H;  // consecutive workgroups: the heads of one group
+  const int gi = blockIdx.x / H;
+  const int G0 = gi * G, Gk = min(G, M - G0);  // members
+  if (tid == 0) {
+    int tp = 0;
+    for (int k = 0; k < Gk; ++k) {
+      const int bb = lpt[G0 + k];
+      mb[k] = bb;
+      mr0[k] = blk_off[bb];
+      mrows[k] = blk_off[bb + 1] - mr0[k];
+      mtp[k] = tp;
+      tp += (mrows[k] + 31) / 32;
+    }
+    mtp[Gk] = tp;
+  }
   const int ntile = Mp / C::PT;
   const int nkt = (M + KT - 1) / KT;  // 32-key tiles holding real blocks
-  const int nsw = (rows + ROWS - 1) / ROWS;
   const T* pstage = pooled + (int64_t)h * ntile * C::STAGE;
-  for (int j = tid; j < Mp; j += 64 * SEL_WAVES) sig[j] = 0.f;
+  for (int j = tid; j < Gk * Mp; j += 64 * SEL_WAVES) sig[j] = 0.f;
+  __syncthreads();
+  const int T_all = mtp[Gk];
+  auto member_of = [&](int ti) __attribute__((always_inline)) {  // block of group tile ti
+    int k = 0;
+    if constexpr (GRP)
+      while (k + 1 < Gk && mtp[k + 1] <= ti) ++k;
+    return k;
+  };
 
-  for (int sw = 0; sw < nsw; ++sw) {
-    {  // this wave's queries to LDS (natural row order, zero past the block), lse beside them
-      const int my_row = sw * ROWS + wave * 32 + c;
-      const bool valid = my_row < rows;
+  for (int ts = 0; ts < T_all; ts += SEL_WAVES) {
+    const int nq = min(SEL_WAVES, T_all - ts);  // query tiles of this sweep
+    {  // this wave's query tile to LDS (zero past its block), lse beside it
+      const int ti = ts + wave;
+      int tok = -1;
+      float lse = INFINITY;  // rows past a block get +inf: their probabilities are exactly zero
+      if (ti < T_all) {
+        const int k = member_of(ti);
+        const int row = (ti - mtp[k]) * 32 + c;
+        if (row < mrows[k]) {
+          tok = perm[mr0[k] + row];
+          lse = lsec[(int64_t)h * N + mr0[k] + row];
+        }
+      }
       F qf[C::NKS];
-      load_q<DT, D>(qf, q + ((int64_t)(valid ? perm[r0 + my_row] : 0) * H + h) * D, valid, lane);
+      load_q<DT, D>(qf, q + ((int64_t)(tok >= 0 ? tok : 0) * H + h) * D, tok >= 0, lane);
       T* qrow = qlds + (wave * 32 + c) * QROW + g * C::KPL;
 #pragma unroll
       for (int ks = 0; ks < C::NKS; ++ks) *reinterpret_cast<F*>(qrow + ks * C::KS) = qf[ks];
-      // rows past the block get +inf, so their probabilities are exactly zero
-      if (g == 0) lse_lds[wave * 32 + c] = valid ? lsec[(int64_t)h * N + r0 + my_row] : INFINITY;
+      if (g == 0) lse_lds[wave * 32 + c] = lse;
     }
     if (tid < SEL_WAVES * 2) bkt[tid / 2][tid % 2] = -1;
     __syncthreads();
 
-    const int nq = (min(rows - sw * ROWS, ROWS) + 31) / 32;  // query tiles of this sweep
     const int npair = nkt * nq;
     const int pa = (int)((int64_t)npair * wave / SEL_WAVES), pb = (int)((int64_t)npair * (wave + 1) / SEL_WAVES);
     F kf[C::NS][C::NKS];
     float cs = 0.f;
-    int kt_cur = -1;
-    auto flush = [&](int p_end) __attribute__((always_inline)) {  // column sums of key tile kt_cur
+    int kt_cur = -1, k_cur = -1;
+    auto flush = [&]() __attribute__((always_inline)) {  // column sums of segment (kt_cur, k_cur)
       const float tot = xor32_sum(cs);
-      const bool first = kt_cur * nq < pa, last = (kt_cur + 1) * nq > p_end;
+      const int ulo = GRP ? max(mtp[k_cur] - ts, 0) : 0, uhi = GRP ? min(mtp[k_cur + 1] - ts, nq) : nq;
+      const bool first = kt_cur * nq + ulo < pa, last = kt_cur * nq + uhi > pb;
       const int key = kt_cur * KT + c;
-      if (!first && !last) {  // the whole tile in this range
-        if (g == 0 && key < M) sig[key] += tot;
+      if (!first && !last) {  // the whole segment in this range
+        if (g == 0 && key < M) sig[k_cur * Mp + key] += tot;
       } else {
-        const int slot = first ? 0 : 1;  // a range within one tile uses slot 0
+        const int slot = first ? 0 : 1;  // a range within one segment uses slot 0
         if (g == 0) bpart[wave][slot][c] = tot;
-        if (lane == 0) bkt[wave][slot] = kt_cur;
+        if (lane == 0) bkt[wave][slot] = kt_cur * SEL_GMAX + k_cur;
       }
       cs = 0.f;
     };
 #pragma unroll 1
     for (int p = pa; p < pb; ++p) {
       const int kt = p / nq, u = p % nq;
-      if (kt != kt_cur) {
-        if (kt_cur >= 0) flush(pb);
+      const int k = member_of(ts + u);
+      if (kt != kt_cur || k != k_cur) {
+        if (kt_cur >= 0) flush();
+        if (kt != kt_cur) {
+          const T* krow = pstage + (int64_t)(kt / 2) * C::STAGE + ((kt % 2) * KT + (lane & 31)) * C::KROW +
+                          (lane >> 5) * C::KPL;
+#pragma unroll
+          for (int s2 = 0; s2 < C::NS; ++s2)
+#pragma unroll
+            for (int ks = 0; ks < C::NKS; ++ks) kf[s2][ks] = load_frag<DT>(krow + s2 * C::KPLANE + ks * C::KS);
+        }
         kt_cur = kt;
-        const T* krow = pstage + (int64_t)(kt / 2) * C::STAGE + ((kt % 2) * KT + (lane & 31)) * C::KROW +
-                        (lane >> 5) * C::KPL;
-#pragma unroll
-        for (int s2 = 0; s2 < C::NS; ++s2)
-#pragma unroll
-          for (int ks = 0; ks < C::NKS; ++ks) kf[s2][ks] = load_frag<DT>(krow + s2 * C::KPLANE + ks * C::KS);
+        k_cur = k;
       }
       const T* qrow = qlds + (u * 32 + (lane & 31)) * QROW + (lane >> 5) * C::KPL;
       ssa_f16v acc = zero16();
@@ -622,22 +659,29 @@ __global__ __launch_bounds__(64 * SEL_WAVES) void k_select(
       for (int r = 0; r < 16; ++r)
         cs += fast_exp2(__builtin_fmaf(acc[r], sl2, -lse_lds[u * 32 + res_row(r, g)]));
     }
-    if (kt_cur >= 0) flush(pb);
+    if (kt_cur >= 0) flush();
     __syncthreads();
-    if (tid < KT) {  // range ends, in wave order
+    if (tid < KT) {  // cut segments, in wave order
       for (int w = 0; w < SEL_WAVES; ++w)
         for (int sl = 0; sl < 2; ++sl) {
-          const int kt = bkt[w][sl];
-          if (kt >= 0 && kt * KT + tid < M) sig[kt * KT + tid] += bpart[w][sl][tid];
+          const int tag = bkt[w][sl];
+          if (tag >= 0) {
+            const int kt = tag / SEL_GMAX, k = tag % SEL_GMAX;
+            if (kt * KT + tid < M) sig[k * Mp + kt * KT + tid] += bpart[w][sl][tid];
+          }
         }
     }
-    __syncthreads();  // sigma complete for this sweep; the query tiles are free again
+    __syncthreads();  // the rows are complete for this sweep; the query tiles are free again
   }
-  if (sigma_out) {  // the top-k kernel takes it from here
-    float* dst = sigma_out + ((int64_t)h * M + b) * Mp;
-    for (int j = tid; j < M; j += 64 * SEL_WAVES) dst[j] = sig[j];
-  } else {
-    topk_radix<SEL_WAVES>(sig, M, topk, sel + ((int64_t)h * M + b) * topk, hist, bcast, wcnt, tid);
+  for (int k = 0; k < Gk; ++k) {
+    const int bb = mb[k];
+    if (sigma_out) {  // the top-k kernel takes it from here
+      float* dst = sigma_out + ((int64_t)h * M + bb) * Mp;
+      for (int j = tid; j < M; j += 64 * SEL_WAVES) dst[j] = sig[k * Mp + j];
+    } else {
+      topk_radix<SEL_WAVES>(sig + k * Mp, M, topk, sel + ((int64_t)h * M + bb) * topk, hist, bcast, wcnt, tid);
+      __syncthreads();
+    }
   }
 }
 
@@ -1036,6 +1080,9 @@ hipError_t run_pool(const ssa_plan_s* p, int H, const void* k, const void* v, co
 }
 
 template <int DT, int D>
+int64_t select_static_lds();
+
+template <int DT, int D>
 hipError_t run_select(const ssa_plan_s* p, int H, int topk, float sl2, const void* q,
                       const FwdWs& w, int32_t* sel, hipStream_t s) {
   using T = typename Tr<DT>::T;
@@ -1054,9 +1101,25 @@ hipError_t run_select(const ssa_plan_s* p, int H, int topk, float sl2, const voi
   hipLaunchKernelGGL((k_compress<DT, D>), dim3((unsigned)(8 * wpx)), dim3(64 * CMP_WAVES), 0, s,
                      (const T*)q, (const T*)w.pooled, p->perm, (int)p->M, Mp, H, p->n, nch, per, wpx, sl2,
                      (T*)w.oc, w.lsec, w.obr);
-  hipLaunchKernelGGL((k_select<DT, D>), dim3((unsigned)(p->M * H)), dim3(64 * SEL_WAVES), shm, s,
-                     (const T*)q, (const T*)w.pooled, p->perm, p->blk_off, p->lpt, (int)p->M, Mp, H,
-                     p->n, sl2, topk, w.lsec, sel, w.sigma);
+  // blocks per importance workgroup: one for blocks of 64 rows and more on average, else
+  // enough for about 256 rows, as far as their importance rows fit the LDS
+  int G = 1;
+  const int64_t avg = p->n / p->M;
+  if (avg < 64) {
+    const int64_t room = (int64_t)LDS_BYTES - select_static_lds<DT, D>();
+    const int64_t fit = room / ((int64_t)Mp * (int64_t)sizeof(float));
+    const int64_t want = 256 / ((avg + 31) / 32 * 32);
+    G = (int)std::max<int64_t>(1, std::min<int64_t>({(int64_t)SEL_GMAX, fit, want}));
+  }
+  const int ngrp = (int)((p->M + G - 1) / G);
+  if (G > 1)
+    hipLaunchKernelGGL((k_select<DT, D, true>), dim3((unsigned)(ngrp * H)), dim3(64 * SEL_WAVES), shm * G, s,
+                       (const T*)q, (const T*)w.pooled, p->perm, p->blk_off, p->lpt, (int)p->M, Mp, H,
+                       p->n, sl2, topk, G, w.lsec, sel, w.sigma);
+  else
+    hipLaunchKernelGGL((k_select<DT, D, false>), dim3((unsigned)(ngrp * H)), dim3(64 * SEL_WAVES), shm, s,
+                       (const T*)q, (const T*)w.pooled, p->perm, p->blk_off, p->lpt, (int)p->M, Mp, H,
+                       p->n, sl2, topk, 1, w.lsec, sel, w.sigma);
   if (w.sigma) {
     const int nrows = (int)(p->M * H);
     hipLaunchKernelGGL(k_topk, dim3((unsigned)((nrows + 3) / 4)), dim3(256), 0, s, w.sigma, (int)p->M,
@@ -1100,12 +1163,24 @@ hipError_t pool_d(int d, const ssa_plan_s* p, int H, const void* k, const void* 
 
 // Most pooled blocks the selection kernel takes: its importance vector [pooled_rows(M)]
 // fp32 lives in LDS beside the kernel's static arrays, within the 160 KB of a workgroup.
+// Static LDS of the importance kernel (its importance rows come on top).
+template <int DT, int D>
+int64_t select_static_lds() {
+  static int64_t bytes = -1;
+  if (bytes < 0) {
+    hipFuncAttributes a;
+    if (hipFuncGetAttributes(&a, reinterpret_cast<const void*>(&k_select<DT, D, false>)) != hipSuccess) return LDS_BYTES;
+    bytes = (int64_t)a.sharedSizeBytes;
+  }
+  return bytes;
+}
+
 template <int DT, int D>
 int64_t select_limit() {
   static int64_t lim = -1;
   if (lim < 0) {
     hipFuncAttributes a;
-    if (hipFuncGetAttributes(&a, reinterpret_cast<const void*>(&k_select<DT, D>)) != hipSuccess) return 0;
+    if (hipFuncGetAttributes(&a, reinterpret_cast<const void*>(&k_select<DT, D, false>)) != hipSuccess) return 0;
     const int64_t room = (int64_t)LDS_BYTES - (int64_t)a.sharedSizeBytes;
     lim = room <= 0 ? 0 : room / (int64_t)sizeof(float) / 128 * 128;  // pooled_rows(M) fits
   }
