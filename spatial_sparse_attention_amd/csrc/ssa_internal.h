@@ -42,7 +42,6 @@ struct PlanWs {
 };
 size_t plan_carve(Carver& c, int64_t n, PlanWs* w);
 
-static inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 static inline int nsplit_of(ssa_dtype dt) { return dt == SSA_F32 ? 1 : (dt == SSA_F16 ? 2 : 3); }
 static inline size_t esize_of(ssa_dtype dt) { return dt == SSA_F32 ? 4 : 2; }
 

@@ -225,23 +225,6 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 __device__ inline void dma16(const void* g, void* lds_instr_base) {
   __builtin_amdgcn_global_load_lds(g, (lds_void_t*)lds_instr_base, 16, 0, 0);
 }
-// Waits for this wave's outstanding copies (vmcnt(0)); a barrier after it publishes them to
-// the workgroup.  Written as the builtin so that the compiler's own wait bookkeeping sees it.
-__device__ inline void dma_wait() { __builtin_amdgcn_s_waitcnt(0x0F70); }
-
-// Copy of nchunks 16-byte chunks from global g to LDS, spread over NW waves; lane l of a
-// wave's instruction writes LDS base + 16 l.  Uses buffer loads to LDS (g is wave-uniform
-// and the span is below 4 GiB): unlike the global form, the compiler keeps counting its
-// LDS reads separately from these copies, so it does not wait for every read at once.
-template <int NW>
-__device__ inline void dma_contiguous(void* lds, const void* g, int nchunks, int wave, int lane) {
-  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(g), 0, nchunks * 16, 0x00020000);
-  for (int i = wave; i * 64 < nchunks; i += NW) {
-    const int p = i * 64 + lane;
-    if (p < nchunks) __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)((char*)lds + i * 1024), 16, p * 16, 0, 0, 0);
-  }
-}
-
 // ------------------------------------------------------------------ XCD-aware work order
 // gfx950 dispatches workgroup i of a grid to XCD i % 8, and each XCD has its own L2.  Work
 // comes in units of `per` workgroups that read the same rows (the heads and chunks of one
