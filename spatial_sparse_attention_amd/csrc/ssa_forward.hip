@@ -925,6 +925,18 @@ __global__ __launch_bounds__(64 * ATT_WAVES) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
     for (int x = 0; x < 3; ++x) gt[x] = Tr<DT>::up(gates[(tok_q * H + h) * 3 + x]);
   }
+  // 16-bit types: this lane's part of the compressed branch's output row, read now so that
+  // the combine at the end need not wait for it (rows past the block read row 0, unused)
+  typedef unsigned ocv_t __attribute__((ext_vector_type(2)));
+  constexpr bool OCPRE = sizeof(T) == 2 && (BUF || D <= 64);  // register budget
+  ocv_t ocv[OCPRE ? C::NDV * 4 : 1];
+  if constexpr (OCPRE) {
+    const T* orow0 = oc + ((int64_t)(r0 + (valid ? my_row : 0)) * H + h) * D + 4 * g;
+#pragma unroll
+    for (int j = 0; j < C::NDV; ++j)
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq) ocv[j * 4 + rq] = *reinterpret_cast<const ocv_t*>(orow0 + 32 * j + 8 * rq);
+  }
   if (sb >= 0) sel_lds[tid] = sb;
   const int nsel = __syncthreads_count(sb >= 0);
   const int nwin = c1 - c0;
@@ -1055,7 +1067,14 @@ __global__ __launch_bounds__(64 * ATT_WAVES) __attribute__((amdgpu_waves_per_eu(
       for (int rq = 0; rq < 4; ++rq) {
         const int col = 32 * j + 8 * rq + 4 * g;
         float v[4];
-        load4(orow + col, v);
+        if constexpr (OCPRE) {
+          struct V4 { T e[4]; };
+          const V4 x = __builtin_bit_cast(V4, ocv[j * 4 + rq]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = (float)x.e[e];
+        } else {
+          load4(orow + col, v);
+        }
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[e] = res[j][4 * rq + e] + f * st.o[j][4 * rq + e] + gt[0] * v[e];
         store4(dst + col, v[0], v[1], v[2], v[3]);
