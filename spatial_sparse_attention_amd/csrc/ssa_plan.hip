@@ -225,10 +225,14 @@ __global__ void k_block_stats(const int32_t* __restrict__ blk_off, int M, int n,
 // largest block size.  Replaces a three-pass radix sort of up to a few thousand keys (the
 // work grows as M^2: about 20 us at M = 2048, where the radix sort takes about 30).
 constexpr int LPT_RANK_MAX = 2048;
-__global__ __launch_bounds__(1024) void k_lpt_rank(const int32_t* __restrict__ blk_off, int M,
+// M is read from device memory (launched before the host learns it); with more than
+// LPT_RANK_MAX blocks the kernel does nothing and the host sorts instead.
+__global__ __launch_bounds__(1024) void k_lpt_rank(const int32_t* __restrict__ blk_off, const int32_t* __restrict__ Mdev,
                                                    int32_t* __restrict__ lpt, int32_t* __restrict__ max_rows) {
   __shared__ int32_t sz[LPT_RANK_MAX];
   __shared__ int32_t wmax[16];
+  const int M = *Mdev;
+  if (M > LPT_RANK_MAX) return;  // the whole workgroup
   const int tid = threadIdx.x;
   int mx = 0;
   for (int i = tid; i < M; i += 1024) {
@@ -273,13 +277,17 @@ __global__ void k_cell_keys(const int32_t* __restrict__ blk_key, int M, int3 dim
   ids[b] = b;
 }
 
-__global__ void k_identity_cells(int M, int32_t* blk_cell, int32_t* cell_off, int32_t* cell_blk) {
-  int b = blockIdx.x * blockDim.x + threadIdx.x;
-  if (b > M) return;
-  cell_off[b] = b;
-  if (b < M) {
-    blk_cell[b] = b;
-    cell_blk[b] = b;
+// Window cells equal to blocks; the block count M is read from device memory (the plan
+// launches this before the host learns M), grid-stride.
+__global__ void k_identity_cells(const int32_t* __restrict__ Mdev, int32_t* blk_cell, int32_t* cell_off,
+                                 int32_t* cell_blk) {
+  const int M = *Mdev;
+  for (int b = blockIdx.x * blockDim.x + threadIdx.x; b <= M; b += gridDim.x * blockDim.x) {
+    cell_off[b] = b;
+    if (b < M) {
+      blk_cell[b] = b;
+      cell_blk[b] = b;
+    }
   }
 }
 
@@ -435,17 +443,28 @@ extern "C" ssa_status ssa_plan_create(const int32_t* coords, int64_t n, const in
   if (segments(ka, va, ni, w.tile_cnt, w.counters + 0, w.blk_off, w.blk_key, w.tok2blk, w.scan_part, stream) !=
       hipSuccess)
     return fail(SSA_ERR_HIP);
+  // Before the host learns M: the longest-first order by ranking (up to LPT_RANK_MAX blocks)
+  // and, when cells are blocks, the identity cells, so that the usual plan needs one host
+  // synchronisation.
+  hipLaunchKernelGGL(k_lpt_rank, dim3(1), dim3(1024), 0, stream, w.blk_off, w.counters + 0, w.lpt, w.counters + 1);
+  if (p->window_is_block)
+    hipLaunchKernelGGL(k_identity_cells, dim3((unsigned)std::min<int64_t>((n + 256) / 256, 1024)), dim3(256), 0,
+                       stream, w.counters + 0, w.blk_cell, w.cell_off, w.cell_blk);
   if (hipMemcpyAsync(host_cnt, w.counters, sizeof(host_cnt), hipMemcpyDeviceToHost, stream) != hipSuccess ||
       hipStreamSynchronize(stream) != hipSuccess)
     return fail(SSA_ERR_HIP);
   if (host_cnt[7]) return fail(SSA_ERR_COORD_RANGE);
   const int M = host_cnt[0];
   p->M = M;
+  if (p->window_is_block && M <= LPT_RANK_MAX) {  // everything is in place
+    p->max_rows = host_cnt[1];
+    p->ncells = M;
+    *out = p;
+    return SSA_OK;
+  }
 
   // longest-first block order (stable: ties keep ascending block id)
-  if (M <= LPT_RANK_MAX) {
-    hipLaunchKernelGGL(k_lpt_rank, dim3(1), dim3(1024), 0, stream, w.blk_off, M, w.lpt, w.counters + 1);
-  } else {
+  if (M > LPT_RANK_MAX) {
     hipLaunchKernelGGL(k_block_stats, dim3((M + 255) / 256), dim3(256), 0, stream, w.blk_off, M, ni,
                        w.key_a, w.val_a, w.counters + 1);
     ka = w.key_a; kb = w.key_b; va = w.val_a; vb = w.val_b;
@@ -455,11 +474,8 @@ extern "C" ssa_status ssa_plan_create(const int32_t* coords, int64_t n, const in
       return fail(SSA_ERR_HIP);
   }
 
-  // window cells as groups of blocks
-  if (p->window_is_block) {
-    hipLaunchKernelGGL(k_identity_cells, dim3((M + 256) / 256), dim3(256), 0, stream, M, w.blk_cell,
-                       w.cell_off, w.cell_blk);
-  } else {
+  // window cells as groups of blocks (identity cells were written above)
+  if (!p->window_is_block) {
     const int ratio = single ? 1 : window / block;
     int3 cd = make_int3(1, 1, 1);
     if (!single)
