@@ -61,7 +61,9 @@ typedef enum { SSA_F32 = 0, SSA_F16 = 1, SSA_BF16 = 2 } ssa_dtype;
 
 typedef struct ssa_plan_s* ssa_plan;
 
-/* Views of a plan's device arrays (owned by the plan's workspace), for tests. */
+/* Views of a plan's device arrays (owned by the plan's workspace), for tests.  They
+ * come back in one struct, filled by ssa_plan_get_info, rather than as a list of
+ * out-parameters, so that views can be added without changing the call. */
 typedef struct {
   int64_t n;               /* tokens */
   int64_t num_blocks;      /* M: occupied blocks */
@@ -79,8 +81,8 @@ typedef struct {
 } ssa_plan_info_t;
 
 /*
- * Block partition of a coordinate set (the pages' "partitions input tokens by 3D
- * coordinates").  Computed on the device: block keys, a stable LSD radix sort of
+ * Block partition of a coordinate set (the partition step of nav.superapi.store,
+ * "Technical principles of Direct3D-S2": tokens grouped by 3D coordinates).  Computed on the device: block keys, a stable LSD radix sort of
  * the keys (token index order inside a block), segment offsets, the window-cell
  * grouping of blocks and a longest-first block order.
  *
@@ -140,8 +142,10 @@ ssa_status ssa_forward_stages(ssa_plan plan, ssa_dtype dtype, int32_t heads, int
                               int save_for_bwd, hipStream_t stream, uint32_t stages);
 
 /*
- * SSA backward (the gradients that a training step at the 80k-voxel shape needs):
- * given dout = dL/dout [N,H,d] (dtype) and the selection sel [H,M,topk] that the
+ * SSA backward: the gradient of the forward defined above (the pages report SSA's
+ * backward pass alongside its forward: pixal-3d.com "Direct3D-S2", sections "What
+ * is Direct3D-S2?" and "Technical snapshot", where training at 1024^3 resolution
+ * relies on it).  Given dout = dL/dout [N,H,d] (dtype) and the selection sel [H,M,topk] that the
  * forward used (held fixed: no gradient flows through the importance scores or the
  * top-k, and none into W_k, W_v), writes fp32 dq, dk, dv [N,H,d] and dgates
  * [N,H,3] (order: compressed, selected, window).  fwd_ws is the workspace of an
@@ -149,6 +153,9 @@ ssa_status ssa_forward_stages(ssa_plan plan, ssa_dtype dtype, int32_t heads, int
  * ws: device workspace of at least ssa_backward_workspace_size(...) bytes.  Every
  * sum runs in a fixed order (no atomics), so results are bitwise reproducible.
  * The plan must be within the forward's block limit (else SSA_ERR_UNSUPPORTED).
+ * scale must be the value the forward used (0 = 1/sqrt(d)): the saved log-sum-exp
+ * values hold it, and a backward on a workspace whose saving forward (one of the
+ * plan's 16 most recent) ran with another scale returns SSA_ERR_INVALID_ARG.
  * Asynchronous on `stream`.
  */
 size_t ssa_backward_workspace_size(ssa_plan plan, ssa_dtype dtype, int32_t heads, int32_t dim,

@@ -67,10 +67,11 @@ class Partition:
 def partition(coords: np.ndarray, edge: int, grid) -> Partition:
     """Partition tokens into edge^3 blocks by their 3D coordinates.
 
-    Follows the pages' "partitions input tokens by 3D coordinates" (nav.superapi.store,
-    "Technical principles of Direct3D-S2"): beta = floor(c / edge) per axis, block key
-    kappa = (beta_x * n_y + beta_y) * n_z + beta_z with n_a = ceil(G_a / edge); blocks
-    are the distinct keys in ascending order; tokens within a block keep index order.
+    Follows the partition step of nav.superapi.store, Direct3D-S2, "Technical principles
+    of Direct3D-S2" (tokens grouped into blocks by their 3D coordinates): beta =
+    floor(c / edge) per axis, block key kappa = (beta_x * n_y + beta_y) * n_z + beta_z
+    with n_a = ceil(G_a / edge); blocks are the distinct keys in ascending order;
+    tokens within a block keep index order.
     """
     c = np.asarray(coords, dtype=np.int64)
     g = np.broadcast_to(np.asarray(grid, dtype=np.int64), (3,))
@@ -124,8 +125,9 @@ def compressed_block(qb: np.ndarray, ktil_h: np.ndarray, vtil_h: np.ndarray, sca
 
     Each query attends to every compressed block token (global context; pixal-3d.com
     "What is Direct3D-S2?").  The block importance vector is the column sum of the
-    probabilities over the query block ("based on the attention scores of the
-    compression module", nav.superapi.store).  Returns (o_c [n,d], sigma [M]).
+    probabilities over the query block: the selection is driven by the compression
+    branch's attention scores (nav.superapi.store, "Technical principles of
+    Direct3D-S2").  Returns (o_c [n,d], sigma [M]).
     """
     s = scale * (np.asarray(qb, dtype=np.float64) @ ktil_h.T)
     p = _softmax_rows(s)
@@ -148,8 +150,8 @@ def _attend(qb, kj, vj, scale):
 
 
 def selected_block(qb, k_h, v_h, part: Partition, sel_row: np.ndarray, scale: float):
-    """Fine branch: one softmax over all tokens of the selected blocks (nav.superapi.store,
-    "selects important blocks for fine-grained feature extraction")."""
+    """Fine branch: one softmax over all tokens of the selected blocks, which are attended
+    at full resolution (nav.superapi.store, "Technical principles of Direct3D-S2")."""
     blocks = [int(b) for b in sel_row if b >= 0]
     j = np.concatenate([part.tokens(b) for b in blocks]) if blocks else np.zeros(0, np.int64)
     return _attend(np.asarray(qb, np.float64), k_h[j], v_h[j], scale)
@@ -162,8 +164,8 @@ def window_partition(coords, w: int, grid) -> Partition:
 
 
 def window_attention(q, k, v, wpart: Partition, scale: float) -> np.ndarray:
-    """Local window branch: every token attends to all tokens of its own window cell
-    ("injects local features based on local window operations", nav.superapi.store)."""
+    """Local window branch: every token attends to all tokens of its own window cell, the
+    local-feature module (nav.superapi.store, "Technical principles of Direct3D-S2")."""
     q = np.asarray(q, np.float64)
     k = np.asarray(k, np.float64)
     v = np.asarray(v, np.float64)
@@ -177,8 +179,8 @@ def window_attention(q, k, v, wpart: Partition, scale: float) -> np.ndarray:
 
 
 def combine(gates, oc, os_, ow):
-    """Gated aggregation of the three branch outputs (nav.superapi.store: "aggregates the
-    outputs of the three modules based on predicted gating scores")."""
+    """Gated aggregation of the three branch outputs: predicted gates weight the three
+    modules' outputs (nav.superapi.store, "Technical principles of Direct3D-S2")."""
     g = np.asarray(gates, np.float64)
     return g[..., 0:1] * oc + g[..., 1:2] * os_ + g[..., 2:3] * ow
 

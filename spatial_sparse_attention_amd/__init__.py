@@ -7,6 +7,7 @@ importing the binding without it raises immediately.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 
@@ -91,6 +92,24 @@ def _stream(stream):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
+def _alloc_on(stream):
+    """Context for the binding's own allocations: torch's caching allocator ties a block to
+    the stream current at allocation, so tensors that the library's kernels use on
+    `stream` are allocated with `stream` current (their memory is then reused only in that
+    stream's order)."""
+    return contextlib.nullcontext() if stream is None else torch.cuda.stream(stream)
+
+
+def _uses(stream, *tensors):
+    """Tell the caching allocator that `stream` uses caller-held tensors allocated on another
+    stream (so their memory is not reused while its kernels may still read or write them)."""
+    if stream is None or stream == torch.cuda.current_stream():
+        return
+    for t in tensors:
+        if t is not None and t.is_cuda:
+            t.record_stream(stream)
+
+
 class Plan:
     """Block partition of int32 coordinates [N,3] on the GPU (ssa_plan_create)."""
 
@@ -106,7 +125,9 @@ class Plan:
         size = lib.ssa_plan_workspace_size(self.n, self.grid, self.block, self.window)
         if size == 0:
             raise SSAError(1, "ssa_plan_workspace_size")
-        self.ws = torch.empty(size, dtype=torch.uint8, device=coords.device)
+        with _alloc_on(stream):
+            self.ws = torch.empty(size, dtype=torch.uint8, device=coords.device)
+        _uses(stream, coords)
         self.coords = coords
         h = _vp()
         st = lib.ssa_plan_create(_ptr(coords), self.n, self.grid, self.block, self.window,
@@ -169,15 +190,18 @@ def forward(plan: Plan, q, k, v, wk, wv, gates, topk: int, scale: float = 0.0, o
     kept and passed to backward()."""
     N, H, d = _check_qkv(plan, q, k, v, wk, wv, gates)
     dt = _DTYPES[q.dtype]
-    if out is None:
-        out = torch.empty_like(q)
-    if sel_out is None and want_sel:
-        sel_out = torch.empty((H, max(plan.num_blocks, 1), topk), dtype=torch.int32, device=q.device)
     size = lib.ssa_forward_workspace_size(plan.handle, dt, H, d, topk, int(save_for_bwd))
     if size == 0:
         raise SSAError(2, "ssa_forward_workspace_size")
-    if ws is None or ws.numel() < size:
-        ws = torch.empty(size, dtype=torch.uint8, device=q.device)
+    _uses(stream, q, k, v, wk, wv, gates, out, sel_out, ws, plan.ws)
+    with _alloc_on(stream):
+        if out is None:
+            out = torch.empty_like(q)
+        if sel_out is None and want_sel:
+            sel_out = torch.empty((H, max(plan.num_blocks, 1), topk), dtype=torch.int32,
+                                  device=q.device)
+        if ws is None or ws.numel() < size:
+            ws = torch.empty(size, dtype=torch.uint8, device=q.device)
     st = lib.ssa_forward_stages(plan.handle, dt, H, d, _ptr(q), _ptr(k), _ptr(v), _ptr(wk),
                                 _ptr(wv), _ptr(gates), int(topk), float(scale), _ptr(out),
                                 _ptr(sel_out), _ptr(ws), ws.numel(), int(save_for_bwd),
@@ -202,13 +226,16 @@ def backward(plan: Plan, q, k, v, wk, wv, gates, topk: int, sel, dout, fwd_ws, s
         raise ValueError("sel must be a contiguous int32 tensor [H, M, topk]")
     dt = _DTYPES[q.dtype]
     f32 = dict(dtype=torch.float32, device=q.device)
-    dq, dk, dv = torch.empty(q.shape, **f32), torch.empty(q.shape, **f32), torch.empty(q.shape, **f32)
-    dg = torch.empty((N, H, 3), **f32)
     size = lib.ssa_backward_workspace_size(plan.handle, dt, H, d, topk)
     if size == 0:
         raise SSAError(2, "ssa_backward_workspace_size")
-    if ws is None or ws.numel() < size:
-        ws = torch.empty(size, dtype=torch.uint8, device=q.device)
+    _uses(stream, q, k, v, wk, wv, gates, sel, dout, fwd_ws, ws, plan.ws)
+    with _alloc_on(stream):
+        dq, dk, dv = (torch.empty(q.shape, **f32), torch.empty(q.shape, **f32),
+                      torch.empty(q.shape, **f32))
+        dg = torch.empty((N, H, 3), **f32)
+        if ws is None or ws.numel() < size:
+            ws = torch.empty(size, dtype=torch.uint8, device=q.device)
     st = lib.ssa_backward(plan.handle, dt, H, d, _ptr(q), _ptr(k), _ptr(v), _ptr(wk), _ptr(wv),
                           _ptr(gates), int(topk), float(scale), _ptr(sel), _ptr(dout), _ptr(dq),
                           _ptr(dk), _ptr(dv), _ptr(dg), _ptr(fwd_ws), fwd_ws.numel(), _ptr(ws),

@@ -19,6 +19,24 @@ ssa_status check_common(ssa_plan p, ssa_dtype dt, int32_t H, int32_t d, int32_t 
   if (p->n * (int64_t)H >= ((int64_t)1 << 31)) return SSA_ERR_UNSUPPORTED;
   return SSA_OK;
 }
+// The saved log-sum-exp values of a forward hold its scale: remember it per workspace so
+// that a backward with another scale is refused instead of returning wrong gradients.
+void record_forward(ssa_plan_s* p, const void* ws, float scale) {
+  std::lock_guard<std::mutex> lk(p->rec_mu);
+  for (auto& r : p->rec)
+    if (r.ws == ws) { r.scale = scale; return; }
+  p->rec[p->rec_next] = {ws, scale};
+  p->rec_next = (p->rec_next + 1) % ssa_plan_s::NREC;
+}
+
+// True unless this plan's record of a saving forward on fwd_ws holds a different scale
+// (a workspace the record no longer holds, after NREC later ones, is not checked).
+bool recorded_scale_matches(ssa_plan_s* p, const void* fwd_ws, float scale) {
+  std::lock_guard<std::mutex> lk(p->rec_mu);
+  for (const auto& r : p->rec)
+    if (r.ws == fwd_ws) return r.scale == scale;
+  return true;
+}
 }  // namespace
 
 size_t fwd_carve(Carver& c, const ssa_plan_s* p, ssa_dtype dt, int H, int d, int topk, int save,
@@ -66,17 +84,17 @@ extern "C" ssa_status ssa_forward_stages(ssa_plan p, ssa_dtype dt, int32_t H, in
   if (!ws) return SSA_ERR_WORKSPACE;
   const int save = save_for_bwd ? 1 : 0;
   if (ws_bytes < ssa_forward_workspace_size(p, dt, H, d, topk, save)) return SSA_ERR_WORKSPACE;
+  if (p->M > select_block_limit(dt, d)) return SSA_ERR_UNSUPPORTED;  // before any launch
   Carver c(ws);
   c.off = (256 - (reinterpret_cast<uintptr_t>(ws) & 255)) & 255;
   FwdWs w;
   fwd_carve(c, p, dt, H, d, topk, save, &w);
   int32_t* sel = sel_out ? sel_out : w.sel;
+  if (save && (stages & SSA_STAGE_SELECT)) record_forward(p, ws, scale);
   if (stages & SSA_STAGE_POOL)
     if (launch_pool(dt, p, H, d, k, v, wk, wv, w, stream) != hipSuccess) return SSA_ERR_HIP;
-  if (stages & SSA_STAGE_SELECT) {
-    if (p->M > select_block_limit(dt, d)) return SSA_ERR_UNSUPPORTED;
+  if (stages & SSA_STAGE_SELECT)
     if (launch_select(dt, p, H, d, topk, scale, q, w, sel, stream) != hipSuccess) return SSA_ERR_HIP;
-  }
   if (stages & SSA_STAGE_ATTEND)
     if (launch_attend(dt, p, H, d, topk, scale, q, k, v, gates, w, sel, out, stream) != hipSuccess)
       return SSA_ERR_HIP;
@@ -116,6 +134,7 @@ extern "C" ssa_status ssa_backward(ssa_plan p, ssa_dtype dt, int32_t H, int32_t 
   if (p->M > select_block_limit(dt, d)) return SSA_ERR_UNSUPPORTED;  // the forward's limit
   if (!fwd_ws || fwd_ws_bytes < ssa_forward_workspace_size(p, dt, H, d, topk, 1)) return SSA_ERR_WORKSPACE;
   if (!ws || ws_bytes < ssa_backward_workspace_size(p, dt, H, d, topk)) return SSA_ERR_WORKSPACE;
+  if (!recorded_scale_matches(p, fwd_ws, scale)) return SSA_ERR_INVALID_ARG;
   Carver c(const_cast<void*>(fwd_ws));
   c.off = (256 - (reinterpret_cast<uintptr_t>(fwd_ws) & 255)) & 255;
   FwdWs fw;

@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <stddef.h>
+#include <mutex>
 #include "ssa.h"
 
 #define SSA_PLAN_MAGIC 0x53534150u  // "SSAP"
@@ -18,6 +19,14 @@ struct ssa_plan_s {
   int32_t max_rows;
   bool window_is_block;     // w == B: cells alias blocks
   int32_t *perm, *blk_off, *blk_key, *tok2blk, *blk_cell, *cell_off, *cell_blk, *lpt;
+  // Softmax scale of the most recent forwards that saved state for the backward, by
+  // workspace address: the saved log-sum-exp values hold that scale, so a backward on
+  // the same workspace must use it.  Guarded by rec_mu (a plan may serve several threads).
+  struct FwdRecord { const void* ws; float scale; };
+  static constexpr int NREC = 16;
+  FwdRecord rec[NREC] = {};
+  int rec_next = 0;
+  std::mutex rec_mu;
 };
 
 // Bump allocator over a caller workspace.  With base == nullptr it only measures.

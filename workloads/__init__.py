@@ -144,9 +144,11 @@ def make_geometry(wl: Workload) -> np.ndarray:
 
 
 def random_inputs(coords: np.ndarray, heads: int, dim: int, dtype: str, seed: int,
-                  grid: int, backward: bool = False) -> dict:
-    """Q, K, V ~ N(0,1) [N,H,d]; W ~ N(0, 1/d) [d,d] (used as both W_k and W_v);
-    gates ~ U(0,1) [N,H,3] (order: compressed, selected, window); dO ~ N(0,1)."""
+                  grid: int, backward: bool = False, distinct_w: bool = True) -> dict:
+    """Q, K, V ~ N(0,1) [N,H,d]; W_k ~ N(0, 1/d) [d,d]; gates ~ U(0,1) [N,H,3] (order:
+    compressed, selected, window); dO ~ N(0,1).  W_v is a second draw from the W stream
+    (distinct_w) or the same matrix as W_k (one projection W, as the workload tables
+    state it)."""
     st = _streams(seed)
     n = len(coords)
     out = {
@@ -159,16 +161,20 @@ def random_inputs(coords: np.ndarray, heads: int, dim: int, dtype: str, seed: in
     }
     w = round_to_dtype(st["w"].standard_normal((dim, dim)) / math.sqrt(dim), dtype)
     out["wk"] = w
-    out["wv"] = w.copy()
+    out["wv"] = (round_to_dtype(st["w"].standard_normal((dim, dim)) / math.sqrt(dim), dtype)
+                 if distinct_w else w.copy())
     out["gates"] = round_to_dtype(st["gates"].random((n, heads, 3)), dtype)
     if backward:
         out["do"] = round_to_dtype(st["do"].standard_normal((n, heads, dim)), dtype)
     return out
 
 
-def make_inputs(name_or_wl) -> tuple[Workload, dict]:
+def make_inputs(name_or_wl, distinct_w: bool = False) -> tuple[Workload, dict]:
+    """A named workload's inputs.  By default one projection W serves as W_k and W_v (the
+    workload tables name a single W); distinct_w draws W_v separately."""
     wl = WORKLOADS[name_or_wl] if isinstance(name_or_wl, str) else name_or_wl
     coords = make_geometry(wl)
-    inp = random_inputs(coords, wl.heads, wl.dim, wl.dtype, wl.seed, wl.grid, wl.backward)
+    inp = random_inputs(coords, wl.heads, wl.dim, wl.dtype, wl.seed, wl.grid, wl.backward,
+                        distinct_w=distinct_w)
     inp.update(block=wl.block, window=wl.window, topk=wl.topk)
     return wl, inp
