@@ -54,7 +54,8 @@ typedef enum {
   SSA_ERR_WORKSPACE = 3,     /* workspace missing or smaller than the *_workspace_size query */
   SSA_ERR_COORD_RANGE = 4,   /* a coordinate outside [0, grid) (detected on the device) */
   SSA_ERR_HIP = 5,           /* a HIP runtime call or kernel launch failed */
-  SSA_ERR_BAD_PLAN = 6       /* null or destroyed plan handle */
+  SSA_ERR_BAD_PLAN = 6,      /* null or destroyed plan handle */
+  SSA_ERR_TOO_LARGE = 7      /* ssa_forward_noalloc: the problem needs more than its scratch area */
 } ssa_status;
 
 typedef enum { SSA_F32 = 0, SSA_F16 = 1, SSA_BF16 = 2 } ssa_dtype;
@@ -140,6 +141,25 @@ ssa_status ssa_forward_stages(ssa_plan plan, ssa_dtype dtype, int32_t heads, int
                               const void* wv, const void* gates, int32_t topk, float scale,
                               void* out, int32_t* sel_out, void* ws, size_t ws_bytes,
                               int save_for_bwd, hipStream_t stream, uint32_t stages);
+
+/*
+ * For callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation): ssa_forward without a workspace
+ * argument.  The workspace is a fixed array of SSA_NOALLOC_SCRATCH_BYTES (64 MiB) in
+ * the library's device code, one copy per GPU, held from the library's first use on
+ * that GPU until the process ends; the call itself allocates nothing.  A problem whose
+ * forward workspace (ssa_forward_workspace_size with save_for_bwd = 0, less its 256
+ * bytes of alignment slack) exceeds it returns SSA_ERR_TOO_LARGE before any launch.
+ * Arguments and results as ssa_forward with ws = NULL and save_for_bwd = 0.  Every call
+ * on one GPU uses that GPU's one array: calls that overlap on a GPU (concurrent streams
+ * or threads) race and give undefined results; calls ordered on one stream are safe.
+ * Nothing in the array needs to start zeroed.
+ */
+#define SSA_NOALLOC_SCRATCH_BYTES (64u << 20)
+ssa_status ssa_forward_noalloc(ssa_plan plan, ssa_dtype dtype, int32_t heads, int32_t dim,
+                               const void* q, const void* k, const void* v, const void* wk,
+                               const void* wv, const void* gates, int32_t topk, float scale,
+                               void* out, int32_t* sel_out, hipStream_t stream);
 
 /*
  * SSA backward: the gradient of the forward defined above (the pages report SSA's

@@ -13,14 +13,16 @@ import os
 
 import torch
 
-__all__ = ["Plan", "forward", "forward_workspace_size", "backward", "backward_workspace_size",
+__all__ = ["Plan", "forward", "forward_workspace_size", "forward_noalloc", "backward",
+           "backward_workspace_size", "NOALLOC_SCRATCH_BYTES",
            "SSAError", "lib", "LIB_PATH", "STAGE_POOL", "STAGE_SELECT", "STAGE_ATTEND", "STAGE_ALL"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libssa.so")
 STAGE_POOL, STAGE_SELECT, STAGE_ATTEND, STAGE_ALL = 1, 2, 4, 7
 _DTYPES = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
 _STATUS = {0: "SSA_OK", 1: "SSA_ERR_INVALID_ARG", 2: "SSA_ERR_UNSUPPORTED", 3: "SSA_ERR_WORKSPACE",
-           4: "SSA_ERR_COORD_RANGE", 5: "SSA_ERR_HIP", 6: "SSA_ERR_BAD_PLAN"}
+           4: "SSA_ERR_COORD_RANGE", 5: "SSA_ERR_HIP", 6: "SSA_ERR_BAD_PLAN", 7: "SSA_ERR_TOO_LARGE"}
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 _vp = ctypes.c_void_p
 _i32 = ctypes.c_int32
@@ -57,6 +59,9 @@ def _load():
     L.ssa_forward.restype = ctypes.c_int
     L.ssa_forward_stages.argtypes = fwd + [ctypes.c_uint32]
     L.ssa_forward_stages.restype = ctypes.c_int
+    L.ssa_forward_noalloc.argtypes = [_vp, ctypes.c_int, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp,
+                                      _i32, ctypes.c_float, _vp, _vp, _vp]
+    L.ssa_forward_noalloc.restype = ctypes.c_int
     L.ssa_backward_workspace_size.argtypes = [_vp, ctypes.c_int, _i32, _i32, _i32]
     L.ssa_backward_workspace_size.restype = _sz
     L.ssa_backward.argtypes = [_vp, ctypes.c_int, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _i32,
@@ -207,6 +212,24 @@ def forward(plan: Plan, q, k, v, wk, wv, gates, topk: int, scale: float = 0.0, o
                                 _ptr(sel_out), _ptr(ws), ws.numel(), int(save_for_bwd),
                                 _stream(stream), int(stages))
     _check(st, "ssa_forward")
+    return out, sel_out
+
+
+def forward_noalloc(plan: Plan, q, k, v, wk, wv, gates, topk: int, out, sel_out=None,
+                    scale: float = 0.0, stream=None):
+    """SSA forward through ssa_forward_noalloc: no workspace; `out` [N,H,d] (and `sel_out`
+    [H,M,topk] int32, optional) are the caller's.  Allocates nothing."""
+    N, H, d = _check_qkv(plan, q, k, v, wk, wv, gates)
+    if out.shape != q.shape or out.dtype != q.dtype or not out.is_contiguous():
+        raise ValueError("out must match q")
+    if sel_out is not None and (sel_out.dtype != torch.int32 or not sel_out.is_contiguous()
+                                or sel_out.numel() < H * max(plan.num_blocks, 1) * topk):
+        raise ValueError("sel_out must be a contiguous int32 tensor [H, M, topk]")
+    _uses(stream, q, k, v, wk, wv, gates, out, sel_out, plan.ws)
+    st = lib.ssa_forward_noalloc(plan.handle, _DTYPES[q.dtype], H, d, _ptr(q), _ptr(k), _ptr(v),
+                                 _ptr(wk), _ptr(wv), _ptr(gates), int(topk), float(scale),
+                                 _ptr(out), _ptr(sel_out), _stream(stream))
+    _check(st, "ssa_forward_noalloc")
     return out, sel_out
 
 

@@ -83,12 +83,13 @@ extern "C" ssa_status ssa_forward_stages(ssa_plan p, ssa_dtype dt, int32_t H, in
   if (!q || !k || !v || !wk || !wv || !gates || !out) return SSA_ERR_INVALID_ARG;
   if (!ws) return SSA_ERR_WORKSPACE;
   const int save = save_for_bwd ? 1 : 0;
-  if (ws_bytes < ssa_forward_workspace_size(p, dt, H, d, topk, save)) return SSA_ERR_WORKSPACE;
   if (p->M > select_block_limit(dt, d)) return SSA_ERR_UNSUPPORTED;  // before any launch
+  // the size query adds 256 bytes of alignment slack; what counts is the carve from the
+  // workspace's actual alignment
   Carver c(ws);
   c.off = (256 - (reinterpret_cast<uintptr_t>(ws) & 255)) & 255;
   FwdWs w;
-  fwd_carve(c, p, dt, H, d, topk, save, &w);
+  if (ws_bytes < fwd_carve(c, p, dt, H, d, topk, save, &w)) return SSA_ERR_WORKSPACE;
   int32_t* sel = sel_out ? sel_out : w.sel;
   if (save && (stages & SSA_STAGE_SELECT)) record_forward(p, ws, scale);
   if (stages & SSA_STAGE_POOL)
@@ -108,6 +109,50 @@ extern "C" ssa_status ssa_forward(ssa_plan p, ssa_dtype dt, int32_t H, int32_t d
                                   hipStream_t stream) {
   return ssa_forward_stages(p, dt, H, d, q, k, v, wk, wv, gates, topk, scale, out, sel_out, ws,
                             ws_bytes, save_for_bwd, stream, SSA_STAGE_ALL);
+}
+
+// ------------------------------------------------------------------ no-allocation forward
+// The forward's workspace in a fixed device array instead of a caller's buffer.  Host code
+// never uses the array's name as an address: the name is a host-side stand-in, and the
+// device address of each GPU's copy comes from hipGetSymbolAddress, fetched once per device
+// with that device current.
+static __device__ __align__(256) char scratch[SSA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int MAX_DEVICES = 64;
+std::mutex scratch_mu;
+void* scratch_ptr[MAX_DEVICES] = {};
+
+// The current device's copy of the scratch array, or nullptr on a HIP error.
+void* scratch_address() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) return nullptr;
+  std::lock_guard<std::mutex> lk(scratch_mu);
+  if (!scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+    scratch_ptr[dev] = ptr;
+  }
+  return scratch_ptr[dev];
+}
+}  // namespace
+
+extern "C" ssa_status ssa_forward_noalloc(ssa_plan p, ssa_dtype dt, int32_t H, int32_t d,
+                                          const void* q, const void* k, const void* v,
+                                          const void* wk, const void* wv, const void* gates,
+                                          int32_t topk, float scale, void* out, int32_t* sel_out,
+                                          hipStream_t stream) {
+  ssa_status st = check_common(p, dt, H, d, topk);
+  if (st != SSA_OK) return st;
+  if (p->n == 0) return ssa_forward_stages(p, dt, H, d, q, k, v, wk, wv, gates, topk, scale, out,
+                                           sel_out, nullptr, 0, 0, stream, SSA_STAGE_ALL);
+  Carver c(nullptr);  // the array is 256-byte aligned: the carve starts at offset 0
+  if (fwd_carve(c, p, dt, H, d, topk, 0, nullptr) > (size_t)SSA_NOALLOC_SCRATCH_BYTES)
+    return SSA_ERR_TOO_LARGE;
+  void* ws = scratch_address();
+  if (!ws) return SSA_ERR_HIP;
+  return ssa_forward_stages(p, dt, H, d, q, k, v, wk, wv, gates, topk, scale, out, sel_out, ws,
+                            (size_t)SSA_NOALLOC_SCRATCH_BYTES, 0, stream, SSA_STAGE_ALL);
 }
 
 extern "C" size_t ssa_backward_workspace_size(ssa_plan p, ssa_dtype dt, int32_t H, int32_t d,
@@ -154,6 +199,8 @@ extern "C" const char* ssa_status_string(ssa_status s) {
     case SSA_ERR_COORD_RANGE: return "coordinate outside the grid";
     case SSA_ERR_HIP: return "HIP runtime error";
     case SSA_ERR_BAD_PLAN: return "invalid plan handle";
+    case SSA_ERR_TOO_LARGE:
+      return "the forward's workspace exceeds the fixed scratch area of ssa_forward_noalloc";
   }
   return "unknown status";
 }

@@ -36,7 +36,7 @@ def test_header_symbols_exported(ssa):
 
 
 def test_status_strings(ssa):
-    for code in range(7):
+    for code in range(8):
         assert ssa.lib.ssa_status_string(code)
     assert ssa.lib.ssa_status_string(99) == b"unknown status"
 
