@@ -105,3 +105,12 @@ class HeadPool:
             self.pool.join()
             self.pool = None
         self.close()
+
+
+def forward_blocks_task(inp_h, h, payload, shared):
+    """The oracle forward of the blocks `payload` of head h (pooled keys shared as "ktil",
+    "vtil" [H, M, d]).  Returns the number of blocks done."""
+    import oracle
+    ktv = (np.asarray(shared["ktil"][h:h + 1]), np.asarray(shared["vtil"][h:h + 1]))
+    oracle.forward_items(inp_h, [(0, int(b)) for b in payload], ktv=ktv)
+    return len(payload)

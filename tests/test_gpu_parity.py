@@ -256,3 +256,36 @@ def test_forward_within_block_permutation():
     o2, s2, _ = gpu_forward(inp2)
     np.testing.assert_array_equal(s1, s2)
     np.testing.assert_allclose(o2, o1[pi], atol=2e-3)
+
+
+# ------------------------------------------------------------------ dense attention (one window cell)
+@pytest.mark.timeout(900)
+def test_dense_torus_geometry_all():
+    """Dense attention over every voxel (one window cell covering the 256^3 grid) at the torus
+    geometry's 20,000 voxels, 2 heads x 64 in bf16: every output element and selection row."""
+    wl, base = _workload("torus20k")
+    inp = W.random_inputs(base["coords"], 2, 64, "bf16", seed=31, grid=wl.grid)
+    inp.update(block=wl.block, window=wl.grid, topk=wl.topk)
+    plan = _check_full(inp)
+    assert plan.num_cells == 1
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", ["shells80k", "shells110k"])
+def test_dense_full_shape_sampled(name):
+    """Dense attention over every voxel in the configuration the benchmark times as its dense
+    baseline (the workload's own 22 x 96 fp16 inputs, one window cell covering the grid):
+    sampled (head, block) items, largest and smallest blocks included, plus properties of
+    every output."""
+    wl, inp0 = _workload(name)
+    inp = dict(inp0)
+    inp["window"] = wl.grid
+    out, sel, plan = gpu_forward(inp)
+    assert plan.num_cells == 1
+    a = _plan_arrays(plan)
+    sizes = np.diff(a["blk_off"])
+    rng = np.random.default_rng(11)
+    blocks = [int(np.argmax(sizes)), int(np.argmin(sizes))] + [int(b) for b in rng.choice(plan.num_blocks, 2, replace=False)]
+    items = sorted({(int(h), b) for b in blocks for h in (0, wl.heads - 1)})
+    check_items(inp, out, sel, items)
+    assert np.isfinite(out).all()
