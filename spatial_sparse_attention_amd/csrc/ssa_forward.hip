@@ -747,21 +747,21 @@ __global__ __launch_bounds__(256) void k_topk(const float* __restrict__ sigma, i
 constexpr int KSEG = 2048;
 
 // S^T = K Q^T of a 32-key tile (K rows at the stage start), every fragment read issued
-// before the first MFMA.
+// before the first MFMA (16-bit types: in one asm statement, see lds_frags_b128).
 template <int DT, int D>
 __device__ inline ssa_f16v s_chain(const typename Tr<DT>::T* cur, const typename Tr<DT>::frag* qf, int lane) {
   using C = Cfg<DT, D>;
   const typename Tr<DT>::T* krow = cur + (lane & 31) * C::KROW + (lane >> 5) * C::KPL;
   typename Tr<DT>::frag ka[C::NKS];
+  if constexpr (C::KPL != 1) {
+    lds_frags_b128<C::NKS, C::KS * (int)sizeof(typename Tr<DT>::T)>(krow, ka);  // one asm statement
+  } else {
 #pragma unroll
-  for (int ks = 0; ks < C::NKS; ++ks) ka[ks] = load_frag<DT>(krow + ks * C::KS);
+    for (int ks = 0; ks < C::NKS; ++ks) ka[ks] = load_frag<DT>(krow + ks * C::KS);
+  }
   ssa_f16v acc = zero16();
 #pragma unroll
   for (int ks = 0; ks < C::NKS; ++ks) acc = Tr<DT>::mma(ka[ks], qf[ks], acc);
-  if constexpr (C::KPL != 1) {
-    __builtin_amdgcn_sched_group_barrier(0x100, C::NKS, 0);  // DS reads
-    __builtin_amdgcn_sched_group_barrier(0x008, C::NKS, 0);  // then MFMAs
-  }
   return acc;
 }
 

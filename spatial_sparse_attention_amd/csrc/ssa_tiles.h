@@ -32,6 +32,173 @@ struct Cfg {
   static constexpr int STAGE = NS * KPLANE + D * VTROW;
 };
 
+
+// ------------------------------------------------------------------ stage-buffer reads in asm
+// Reads of a stage buffer while copies into other stage buffers are in flight.  Written as
+// plain loads, the compiler makes the wave wait for every copy into LDS still in flight
+// (vmcnt(0)) before them, wherever it loses track of which copy wrote which buffer (at the
+// joins of the stream's control flow), and so drains the copy pipeline at every tile.  The
+// stream's own wait and barrier already guarantee that this buffer's copy has landed, so
+// these reads are issued from asm, all at once, and waited for (lgkmcnt) inside the same
+// statement; the outputs are early-clobber so that no output shares the address register.
+__device__ inline uint32_t lds_u32(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+template <int S, typename V>
+__device__ inline void lds_rd_b128_x2(uint32_t a, V (&o)[2]) {
+  asm volatile("ds_read_b128 %0, %2 offset:%3\n\t"
+               "ds_read_b128 %1, %2 offset:%4\n\t"
+               "s_waitcnt lgkmcnt(0)"
+               : "=&v"(o[0]), "=&v"(o[1])
+               : "v"(a), "i"(0 * S), "i"(1 * S));
+}
+template <int S, typename V>
+__device__ inline void lds_rd_b128_x4(uint32_t a, V (&o)[4]) {
+  asm volatile("ds_read_b128 %0, %4 offset:%5\n\t"
+               "ds_read_b128 %1, %4 offset:%6\n\t"
+               "ds_read_b128 %2, %4 offset:%7\n\t"
+               "ds_read_b128 %3, %4 offset:%8\n\t"
+               "s_waitcnt lgkmcnt(0)"
+               : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3])
+               : "v"(a), "i"(0 * S), "i"(1 * S), "i"(2 * S), "i"(3 * S));
+}
+template <int S, typename V>
+__device__ inline void lds_rd_b128_x6(uint32_t a, V (&o)[6]) {
+  asm volatile("ds_read_b128 %0, %6 offset:%7\n\t"
+               "ds_read_b128 %1, %6 offset:%8\n\t"
+               "ds_read_b128 %2, %6 offset:%9\n\t"
+               "ds_read_b128 %3, %6 offset:%10\n\t"
+               "ds_read_b128 %4, %6 offset:%11\n\t"
+               "ds_read_b128 %5, %6 offset:%12\n\t"
+               "s_waitcnt lgkmcnt(0)"
+               : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3]), "=&v"(o[4]), "=&v"(o[5])
+               : "v"(a), "i"(0 * S), "i"(1 * S), "i"(2 * S), "i"(3 * S), "i"(4 * S), "i"(5 * S));
+}
+template <int S, typename V>
+__device__ inline void lds_rd_b128_x8(uint32_t a, V (&o)[8]) {
+  asm volatile("ds_read_b128 %0, %8 offset:%9\n\t"
+               "ds_read_b128 %1, %8 offset:%10\n\t"
+               "ds_read_b128 %2, %8 offset:%11\n\t"
+               "ds_read_b128 %3, %8 offset:%12\n\t"
+               "ds_read_b128 %4, %8 offset:%13\n\t"
+               "ds_read_b128 %5, %8 offset:%14\n\t"
+               "ds_read_b128 %6, %8 offset:%15\n\t"
+               "ds_read_b128 %7, %8 offset:%16\n\t"
+               "s_waitcnt lgkmcnt(0)"
+               : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3]), "=&v"(o[4]), "=&v"(o[5]), "=&v"(o[6]), "=&v"(o[7])
+               : "v"(a), "i"(0 * S), "i"(1 * S), "i"(2 * S), "i"(3 * S), "i"(4 * S), "i"(5 * S), "i"(6 * S), "i"(7 * S));
+}
+template <int ROW>
+__device__ inline void lds_rd_tr_ndv1(uint32_t a, ssa_s4 (&o)[4]) {
+  asm volatile("ds_read_b64_tr_b16 %0, %4 offset:%5\n\t"
+               "ds_read_b64_tr_b16 %1, %4 offset:%6\n\t"
+               "ds_read_b64_tr_b16 %2, %4 offset:%7\n\t"
+               "ds_read_b64_tr_b16 %3, %4 offset:%8\n\t"
+               "s_waitcnt lgkmcnt(0)"
+               : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3])
+               : "v"(a), "i"(((16 * 0 + 8 * 0) * ROW + 32 * 0) * 2),
+                 "i"(((16 * 0 + 8 * 1) * ROW + 32 * 0) * 2),
+                 "i"(((16 * 1 + 8 * 0) * ROW + 32 * 0) * 2),
+                 "i"(((16 * 1 + 8 * 1) * ROW + 32 * 0) * 2));
+}
+template <int ROW>
+__device__ inline void lds_rd_tr_ndv2(uint32_t a, ssa_s4 (&o)[8]) {
+  asm volatile("ds_read_b64_tr_b16 %0, %8 offset:%9\n\t"
+               "ds_read_b64_tr_b16 %1, %8 offset:%10\n\t"
+               "ds_read_b64_tr_b16 %2, %8 offset:%11\n\t"
+               "ds_read_b64_tr_b16 %3, %8 offset:%12\n\t"
+               "ds_read_b64_tr_b16 %4, %8 offset:%13\n\t"
+               "ds_read_b64_tr_b16 %5, %8 offset:%14\n\t"
+               "ds_read_b64_tr_b16 %6, %8 offset:%15\n\t"
+               "ds_read_b64_tr_b16 %7, %8 offset:%16\n\t"
+               "s_waitcnt lgkmcnt(0)"
+               : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3]), "=&v"(o[4]), "=&v"(o[5]), "=&v"(o[6]), "=&v"(o[7])
+               : "v"(a), "i"(((16 * 0 + 8 * 0) * ROW + 32 * 0) * 2),
+                 "i"(((16 * 0 + 8 * 1) * ROW + 32 * 0) * 2),
+                 "i"(((16 * 0 + 8 * 0) * ROW + 32 * 1) * 2),
+                 "i"(((16 * 0 + 8 * 1) * ROW + 32 * 1) * 2),
+                 "i"(((16 * 1 + 8 * 0) * ROW + 32 * 0) * 2),
+                 "i"(((16 * 1 + 8 * 1) * ROW + 32 * 0) * 2),
+                 "i"(((16 * 1 + 8 * 0) * ROW + 32 * 1) * 2),
+                 "i"(((16 * 1 + 8 * 1) * ROW + 32 * 1) * 2));
+}
+template <int ROW>
+__device__ inline void lds_rd_tr_ndv3(uint32_t a, ssa_s4 (&o)[12]) {
+  asm volatile("ds_read_b64_tr_b16 %0, %12 offset:%13\n\t"
+               "ds_read_b64_tr_b16 %1, %12 offset:%14\n\t"
+               "ds_read_b64_tr_b16 %2, %12 offset:%15\n\t"
+               "ds_read_b64_tr_b16 %3, %12 offset:%16\n\t"
+               "ds_read_b64_tr_b16 %4, %12 offset:%17\n\t"
+               "ds_read_b64_tr_b16 %5, %12 offset:%18\n\t"
+               "ds_read_b64_tr_b16 %6, %12 offset:%19\n\t"
+               "ds_read_b64_tr_b16 %7, %12 offset:%20\n\t"
+               "ds_read_b64_tr_b16 %8, %12 offset:%21\n\t"
+               "ds_read_b64_tr_b16 %9, %12 offset:%22\n\t"
+               "ds_read_b64_tr_b16 %10, %12 offset:%23\n\t"
+               "ds_read_b64_tr_b16 %11, %12 offset:%24\n\t"
+               "s_waitcnt lgkmcnt(0)"
+               : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3]), "=&v"(o[4]), "=&v"(o[5]), "=&v"(o[6]), "=&v"(o[7]), "=&v"(o[8]), "=&v"(o[9]), "=&v"(o[10]), "=&v"(o[11])
+               : "v"(a), "i"(((16 * 0 + 8 * 0) * ROW + 32 * 0) * 2),
+                 "i"(((16 * 0 + 8 * 1) * ROW + 32 * 0) * 2),
+                 "i"(((16 * 0 + 8 * 0) * ROW + 32 * 1) * 2),
+                 "i"(((16 * 0 + 8 * 1) * ROW + 32 * 1) * 2),
+                 "i"(((16 * 0 + 8 * 0) * ROW + 32 * 2) * 2),
+                 "i"(((16 * 0 + 8 * 1) * ROW + 32 * 2) * 2),
+                 "i"(((16 * 1 + 8 * 0) * ROW + 32 * 0) * 2),
+                 "i"(((16 * 1 + 8 * 1) * ROW + 32 * 0) * 2),
+                 "i"(((16 * 1 + 8 * 0) * ROW + 32 * 1) * 2),
+                 "i"(((16 * 1 + 8 * 1) * ROW + 32 * 1) * 2),
+                 "i"(((16 * 1 + 8 * 0) * ROW + 32 * 2) * 2),
+                 "i"(((16 * 1 + 8 * 1) * ROW + 32 * 2) * 2));
+}
+template <int ROW>
+__device__ inline void lds_rd_tr_ndv4(uint32_t a, ssa_s4 (&o)[16]) {
+  asm volatile("ds_read_b64_tr_b16 %0, %16 offset:%17\n\t"
+               "ds_read_b64_tr_b16 %1, %16 offset:%18\n\t"
+               "ds_read_b64_tr_b16 %2, %16 offset:%19\n\t"
+               "ds_read_b64_tr_b16 %3, %16 offset:%20\n\t"
+               "ds_read_b64_tr_b16 %4, %16 offset:%21\n\t"
+               "ds_read_b64_tr_b16 %5, %16 offset:%22\n\t"
+               "ds_read_b64_tr_b16 %6, %16 offset:%23\n\t"
+               "ds_read_b64_tr_b16 %7, %16 offset:%24\n\t"
+               "ds_read_b64_tr_b16 %8, %16 offset:%25\n\t"
+               "ds_read_b64_tr_b16 %9, %16 offset:%26\n\t"
+               "ds_read_b64_tr_b16 %10, %16 offset:%27\n\t"
+               "ds_read_b64_tr_b16 %11, %16 offset:%28\n\t"
+               "ds_read_b64_tr_b16 %12, %16 offset:%29\n\t"
+               "ds_read_b64_tr_b16 %13, %16 offset:%30\n\t"
+               "ds_read_b64_tr_b16 %14, %16 offset:%31\n\t"
+               "ds_read_b64_tr_b16 %15, %16 offset:%32\n\t"
+               "s_waitcnt lgkmcnt(0)"
+               : "=&v"(o[0]), "=&v"(o[1]), "=&v"(o[2]), "=&v"(o[3]), "=&v"(o[4]), "=&v"(o[5]), "=&v"(o[6]), "=&v"(o[7]), "=&v"(o[8]), "=&v"(o[9]), "=&v"(o[10]), "=&v"(o[11]), "=&v"(o[12]), "=&v"(o[13]), "=&v"(o[14]), "=&v"(o[15])
+               : "v"(a), "i"(((16 * 0 + 8 * 0) * ROW + 32 * 0) * 2),
+                 "i"(((16 * 0 + 8 * 1) * ROW + 32 * 0) * 2),
+                 "i"(((16 * 0 + 8 * 0) * ROW + 32 * 1) * 2),
+                 "i"(((16 * 0 + 8 * 1) * ROW + 32 * 1) * 2),
+                 "i"(((16 * 0 + 8 * 0) * ROW + 32 * 2) * 2),
+                 "i"(((16 * 0 + 8 * 1) * ROW + 32 * 2) * 2),
+                 "i"(((16 * 0 + 8 * 0) * ROW + 32 * 3) * 2),
+                 "i"(((16 * 0 + 8 * 1) * ROW + 32 * 3) * 2),
+                 "i"(((16 * 1 + 8 * 0) * ROW + 32 * 0) * 2),
+                 "i"(((16 * 1 + 8 * 1) * ROW + 32 * 0) * 2),
+                 "i"(((16 * 1 + 8 * 0) * ROW + 32 * 1) * 2),
+                 "i"(((16 * 1 + 8 * 1) * ROW + 32 * 1) * 2),
+                 "i"(((16 * 1 + 8 * 0) * ROW + 32 * 2) * 2),
+                 "i"(((16 * 1 + 8 * 1) * ROW + 32 * 2) * 2),
+                 "i"(((16 * 1 + 8 * 0) * ROW + 32 * 3) * 2),
+                 "i"(((16 * 1 + 8 * 1) * ROW + 32 * 3) * 2));
+}
+// N 16-byte fragments at byte offsets i * S from p (one asm statement).
+template <int N, int S, typename V>
+__device__ inline void lds_frags_b128(const void* p, V (&o)[N]) {
+  const uint32_t a = lds_u32(p);
+  if constexpr (N == 2) lds_rd_b128_x2<S>(a, o);
+  else if constexpr (N == 4) lds_rd_b128_x4<S>(a, o);
+  else if constexpr (N == 6) lds_rd_b128_x6<S>(a, o);
+  else if constexpr (N == 8) lds_rd_b128_x8<S>(a, o);
+  else static_assert(N == 2, "fragment count");
+}
+
 // ------------------------------------------------------------------ MFMA building blocks
 // Reduction with the other half of the wave (lanes l and l^32 hold the same query row):
 // v_permlane32_swap returns the pair {x[l], x[l^32]} in its two results.
@@ -104,10 +271,33 @@ template <int DT, int D>
 struct VFrags {
   typename Tr<DT>::frag f[Cfg<DT, D>::PK][Cfg<DT, D>::NDV];
   __device__ inline void read(const typename Tr<DT>::T* vt, int lane) {
+    using C = Cfg<DT, D>;
+    if constexpr (C::KPL != 1 && C::PK == 2) {  // 16-bit: the tr_frag reads in one asm statement
+      const int i = lane & 15, G = lane >> 4;
+      const typename Tr<DT>::T* p = vt + (4 * (G >> 1) + (i >> 2)) * C::VROW + 16 * (G & 1) + 4 * (i & 3);
+      ssa_s4 o[4 * C::NDV];
+      const uint32_t a = lds_u32(p);
+      if constexpr (C::NDV == 1) lds_rd_tr_ndv1<C::VROW>(a, o);
+      else if constexpr (C::NDV == 2) lds_rd_tr_ndv2<C::VROW>(a, o);
+      else if constexpr (C::NDV == 3) lds_rd_tr_ndv3<C::VROW>(a, o);
+      else lds_rd_tr_ndv4<C::VROW>(a, o);
+      typedef unsigned u2 __attribute__((ext_vector_type(2)));
+      typedef unsigned u4 __attribute__((ext_vector_type(4)));
 #pragma unroll
-    for (int ks = 0; ks < Cfg<DT, D>::PK; ++ks)
+      for (int ks = 0; ks < C::PK; ++ks)
 #pragma unroll
-      for (int j = 0; j < Cfg<DT, D>::NDV; ++j) f[ks][j] = vt_frag<DT, D>(vt, ks, j, lane);
+        for (int j = 0; j < C::NDV; ++j) {
+          const u2 x = __builtin_bit_cast(u2, o[(ks * C::NDV + j) * 2]);
+          const u2 y = __builtin_bit_cast(u2, o[(ks * C::NDV + j) * 2 + 1]);
+          const u4 u = {x.x, x.y, y.x, y.y};
+          f[ks][j] = __builtin_bit_cast(typename Tr<DT>::frag, u);
+        }
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < C::PK; ++ks)
+#pragma unroll
+        for (int j = 0; j < C::NDV; ++j) f[ks][j] = vt_frag<DT, D>(vt, ks, j, lane);
+    }
   }
 };
 
