@@ -79,7 +79,8 @@ class HeadPool:
         for nm, arr in arrays.items():
             np.save(os.path.join(self.dir, nm + ".npy"), np.ascontiguousarray(arr))
             names.append(nm)
-        meta = {k: inp[k] for k in ("grid", "block", "window", "topk", "dtype") if k in inp}
+        meta = {k: inp[k] for k in ("grid", "block", "window", "topk", "dtype", "window_shift", "sfc_tokens")
+                if k in inp}
         if "scale" in inp:
             meta["scale"] = inp["scale"]
         ctx = mp.get_context("spawn")

@@ -26,7 +26,8 @@ The pages give no equations.  The readings taken where they are silent:
     block id, reported in ascending id order and padded with -1;
   * the selected branch is one softmax over the union of the selected blocks'
     tokens; the window branch is one softmax over all tokens in the query's
-    window cell (non-overlapping w^3 cells anchored at the origin);
+    window cell (non-overlapping w^3 cells anchored at the origin, optionally
+    shifted, or fixed-size runs along the Morton order of the voxels);
   * gates are used as given, layout [N,H,3] in the order (compressed, selected,
     window).
 Everything is float64; inputs are the dtype-rounded values, upcast exactly.
@@ -157,10 +158,49 @@ def selected_block(qb, k_h, v_h, part: Partition, sel_row: np.ndarray, scale: fl
     return _attend(np.asarray(qb, np.float64), k_h[j], v_h[j], scale)
 
 
-def window_partition(coords, w: int, grid) -> Partition:
-    """Window cells: non-overlapping w^3 cells anchored at the origin (same construction
-    as the block partition, with edge w)."""
-    return partition(coords, w, grid)
+def window_partition(coords, w: int, grid, shift=(0, 0, 0)) -> Partition:
+    """Window cells: non-overlapping w^3 cells, the cell of a voxel being floor((c + shift)/w)
+    per axis (shift 0: anchored at the origin; shift w/2: the shifted windows of alternate
+    layers).  The same construction as the block partition, on the shifted coordinates in
+    the grid extended by the shift."""
+    s = np.asarray(shift, dtype=np.int64).reshape(3)
+    g = np.broadcast_to(np.asarray(grid, dtype=np.int64), (3,))
+    return partition(np.asarray(coords, np.int64) + s[None, :], w, g + s)
+
+
+def morton_codes(coords, bits: int) -> np.ndarray:
+    """Morton (Z-order) code of each voxel: the bits of x, y and z interleaved from the most
+    significant down, x first in each triple."""
+    c = np.asarray(coords, dtype=np.int64)
+    code = np.zeros(len(c), dtype=np.int64)
+    for b in range(bits - 1, -1, -1):
+        for axis in range(3):
+            code = code * 2 + ((c[:, axis] >> b) & 1)
+    return code
+
+
+def sfc_windows(coords, tokens: int, grid) -> Partition:
+    """Fixed-size windows along a space-filling curve (the Hi3D pipeline page, "Stage 4"):
+    tokens ordered by the Morton code of their voxel (equal codes keep token order), cut into
+    consecutive runs of `tokens` tokens, the last one shorter."""
+    g = np.broadcast_to(np.asarray(grid, dtype=np.int64), (3,))
+    bits = int(max(int(g.max()) - 1, 0)).bit_length()
+    order = np.argsort(morton_codes(coords, bits), kind="stable")
+    n = len(order)
+    ncell = -(-n // tokens)
+    blk_off = np.minimum(np.arange(ncell + 1, dtype=np.int64) * tokens, n)
+    tok2blk = np.empty(n, dtype=np.int64)
+    tok2blk[order] = np.arange(n) // tokens
+    return Partition(order.astype(np.int64), blk_off, np.arange(ncell, dtype=np.int64), tok2blk,
+                     tokens, (ncell,))
+
+
+def window_cells(inp: dict) -> Partition:
+    """The window partition an input dict asks for: "sfc_tokens" > 0 selects Morton-order
+    windows, else cubic cells of edge "window" shifted by "window_shift" (default none)."""
+    if inp.get("sfc_tokens"):
+        return sfc_windows(inp["coords"], int(inp["sfc_tokens"]), inp["grid"])
+    return window_partition(inp["coords"], inp["window"], inp["grid"], inp.get("window_shift", (0, 0, 0)))
 
 
 def window_attention(q, k, v, wpart: Partition, scale: float) -> np.ndarray:
@@ -205,7 +245,7 @@ def forward_items(inp: dict, items, sel_override=None, scale=None, ktv=None):
     N, H, d = q.shape
     sc = _scale(scale, d)
     part = partition(inp["coords"], inp["block"], inp["grid"])
-    wpart = window_partition(inp["coords"], inp["window"], inp["grid"])
+    wpart = window_cells(inp)
     if ktv is None:
         ktil, vtil = pool(k, v, inp["wk"], inp["wv"], part)
     else:
@@ -293,7 +333,7 @@ def backward(inp: dict, sel: np.ndarray, dout: np.ndarray, scale=None):
     N, H, d = q.shape
     sc = _scale(scale, d)
     part = partition(inp["coords"], inp["block"], inp["grid"])
-    wpart = window_partition(inp["coords"], inp["window"], inp["grid"])
+    wpart = window_cells(inp)
     ktil, vtil = pool(k, v, wk, wv, part)
     dq = np.zeros((N, H, d))
     dk = np.zeros((N, H, d))

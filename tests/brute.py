@@ -16,7 +16,38 @@ def _masked_softmax(s, mask):
     return np.exp(s - logsumexp(s, axis=1, keepdims=True))
 
 
-def brute_forward(coords, q, k, v, wk, wv, gates, B, w, topk, scale=None, sel_force=None):
+def _spread3(x):
+    """Bits of x (< 1024) moved to every third position (bit i -> bit 3i)."""
+    x = np.asarray(x, np.int64) & 0x3FF
+    x = (x | (x << 16)) & 0x030000FF
+    x = (x | (x << 8)) & 0x0300F00F
+    x = (x | (x << 4)) & 0x030C30C3
+    x = (x | (x << 2)) & 0x09249249
+    return x
+
+
+def spread_morton(coords):
+    """Morton codes by bit spreading (x in the top bit of each triple)."""
+    c = np.asarray(coords, np.int64)
+    return (_spread3(c[:, 0]) << 2) | (_spread3(c[:, 1]) << 1) | _spread3(c[:, 2])
+
+
+def brute_window_mask(c, w, shift=(0, 0, 0), sfc_tokens=0):
+    """N x N mask: j is in i's window.  Cubic cells by comparing floor((c + shift) / w);
+    Morton-order windows by comparing rank // tokens (rank from bit-spread codes)."""
+    if sfc_tokens:
+        code = spread_morton(c)
+        rank = np.empty(len(c), np.int64)
+        rank[np.lexsort((np.arange(len(c)), code))] = np.arange(len(c))
+        wid = rank // sfc_tokens
+        return wid[:, None] == wid[None, :]
+    s = np.asarray(shift, np.int64)
+    cs = np.asarray(c, np.int64) + s
+    return np.all((cs[:, None, :] // w) == (cs[None, :, :] // w), axis=2)
+
+
+def brute_forward(coords, q, k, v, wk, wv, gates, B, w, topk, scale=None, sel_force=None,
+                  shift=(0, 0, 0), sfc_tokens=0):
     c = np.asarray(coords, np.int64)
     q = np.asarray(q, np.float64)
     k = np.asarray(k, np.float64)
@@ -33,7 +64,7 @@ def brute_forward(coords, q, k, v, wk, wv, gates, B, w, topk, scale=None, sel_fo
     member = np.zeros((M, N), bool)
     member[bid, np.arange(N)] = True
     pool_mat = member / member.sum(axis=1, keepdims=True)
-    win = np.all((c[:, None, :] // w) == (c[None, :, :] // w), axis=2)
+    win = brute_window_mask(c, w, shift, sfc_tokens)
     out = np.zeros((N, H, d))
     oc = np.zeros((N, H, d))
     os_ = np.zeros((N, H, d))
