@@ -246,6 +246,40 @@ def full_attention_timing(r, sparse_fwd_ms, reps=2):
                     "kernels; selected/window stage only"}
 
 
+def window_variant_timing(r, label, window=None, reps=10, **plan_kw):
+    """The forward (all stages) with a window partition of its own (cells that are not unions
+    of blocks: a separate window pass over a token-level sort), HIP events around `reps`
+    calls; credited 4 d FLOPs per attended pair, the window pairs counted per cell."""
+    torch, ssa, wl = r.torch, r.ssa, r.wl
+    N, H, d = r.N, r.H, r.d
+    plan = ssa.Plan(r.coords, wl.grid, wl.block, window or wl.window, **plan_kw)
+    out = torch.empty_like(r.dev["q"])
+    sel = torch.empty((H, plan.num_blocks, wl.topk), dtype=torch.int32, device="cuda")
+    ws = torch.empty(ssa.forward_workspace_size(plan, r.tdt, H, d, wl.topk), dtype=torch.uint8, device="cuda")
+    run = lambda: r.fwd(plan, ssa.STAGE_ALL, out=out, sel=sel, ws=ws)
+    run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(r.stream)
+    for _ in range(reps):
+        run()
+    e1.record(r.stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    a = {k: v.cpu().numpy().astype(np.int64) for k, v in plan.arrays().items()}
+    sizes = np.diff(a["blk_off"])
+    M = len(sizes)
+    sel_np = sel.cpu().numpy()
+    sel_keys = np.where(sel_np >= 0, sizes[np.clip(sel_np, 0, M - 1)], 0).sum(axis=2)
+    wsz = np.diff(a["wcell_off"]).astype(np.float64)
+    pairs = H * (N * M + (wsz ** 2).sum()) + float((sizes[None, :] * sel_keys).sum())
+    flops = 4.0 * d * pairs
+    tf = flops / (ms * 1e-3) / 1e12
+    return {"what": label, "forward_ms": ms, "reps": reps, "window_cells": int(plan.num_wcells),
+            "largest_window": int(wsz.max()), "credited_flops": flops, "tflops": tf,
+            "mfma_peak_frac": tf / r.peak}
+
+
 def backward_timing(r, reps=5):
     """Forward with saved state, then the backward (fixed selection, the workload's dO), timed
     apart from the step: HIP events around `reps` backward calls.  Credited 10 d FLOPs per
@@ -370,6 +404,14 @@ def main():
     if not args.no_full and wl.name in DENSE:
         progress("dense baseline")
         res["full_attention"] = {wl.name: full_attention_timing(r, fwd_ms)}
+    if not args.no_full and wl.name == WORKLOAD:
+        progress("window partitions")
+        res["window_variants"] = {
+            "shifted8": window_variant_timing(r, "8^3 cells shifted by (4,4,4) (alternate-layer shifted windows)",
+                                              shift=(4, 4, 4)),
+            "sfc512": window_variant_timing(r, "windows of 512 tokens along the Morton order", sfc_tokens=512),
+            "cube4": window_variant_timing(r, "4^3 cells (smaller than the 8^3 blocks)", window=4),
+        }
     inp0 = r.inp
     del r
     torch.cuda.empty_cache()

@@ -79,7 +79,40 @@ typedef struct {
   const int32_t* cell_off; /* [C+1] offsets into cell_blk */
   const int32_t* cell_blk; /* [M]   block ids grouped by cell, ascending within a cell */
   const int32_t* lpt;      /* [M]   block ids by descending occupancy (ties: lower id) */
+  /* window partition (see ssa_window_t) */
+  int32_t window_kind;     /* SSA_WINDOW_CUBE or SSA_WINDOW_SFC */
+  int32_t window_shift[3]; /* CUBE: cell origin shift */
+  int32_t window_tokens;   /* SFC: tokens per window */
+  int32_t cells_are_block_unions; /* 1: cells are blk_cell/cell_off/cell_blk above; 0: the w* views */
+  int64_t num_wcells;      /* C': cells of the token-level window partition (0 if unions of blocks) */
+  int32_t max_wcell_rows;  /* tokens of its largest cell */
+  const int32_t* wperm;    /* [N]    token index at window-sorted position r */
+  const int32_t* wcell_off;/* [C'+1] first window-sorted position of each cell */
+  const int32_t* wlpt;     /* [C']   cell ids by descending size (ties: lower id) */
 } ssa_plan_info_t;
+
+/*
+ * The window branch's cells (pixal-3d.com "Direct3D-S2", "What is Direct3D-S2?": local
+ * windows; Hi3D pipeline page, "Stage 4": fixed-size windows along a space-filling curve).
+ *   SSA_WINDOW_CUBE: a token attends to every token of its cubic cell floor((c + shift) / edge)
+ *                    (per axis; edge >= 1, 0 <= shift < edge).  Shifting alternate layers by
+ *                    edge / 2 gives shifted windows.
+ *   SSA_WINDOW_SFC:  tokens sorted by the Morton code of their voxel (bits interleaved x, y, z,
+ *                    x most significant; equal codes in token order) are cut into consecutive
+ *                    windows of `tokens` tokens (the last one shorter); a token attends to its
+ *                    window.  Grid extents up to 1024.
+ * Cells that are unions of blocks (CUBE with no shift and edge a multiple of the block edge, or
+ * one cell covering the grid) run inside the selected branch's kernel; any other partition gets
+ * a token-level sort of its own and a separate window pass, and is forward-only (the backward
+ * and save_for_bwd return SSA_ERR_UNSUPPORTED).
+ */
+typedef enum { SSA_WINDOW_CUBE = 0, SSA_WINDOW_SFC = 1 } ssa_window_kind;
+typedef struct {
+  int32_t kind;      /* ssa_window_kind */
+  int32_t edge;      /* CUBE: cell edge */
+  int32_t shift[3];  /* CUBE: cell origin shift per axis */
+  int32_t tokens;    /* SFC: tokens per window */
+} ssa_window_t;
 
 /*
  * Block partition of a coordinate set (the partition step of nav.superapi.store,
@@ -87,9 +120,8 @@ typedef struct {
  * the keys (token index order inside a block), segment offsets, the window-cell
  * grouping of blocks and a longest-first block order.
  *
- * grid (host, [3]): grid extent per axis, each >= 1.  block B >= 1.  window w >= 1;
- * the window cells must be unions of blocks: w % B == 0, or w >= every grid extent
- * (one cell), else SSA_ERR_UNSUPPORTED.  n = 0 is allowed (an empty plan).
+ * grid (host, [3]): grid extent per axis, each >= 1.  block B >= 1.  window w >= 1: cubic
+ * window cells of edge w (see ssa_window_t).  n = 0 is allowed (an empty plan).
  * ws: caller-owned device workspace of at least ssa_plan_workspace_size(...) bytes;
  * it holds the plan's arrays and must outlive the plan.  The call synchronises
  * `stream` once (to read M back).  Coordinates outside [0, grid) give
@@ -99,6 +131,14 @@ size_t ssa_plan_workspace_size(int64_t n, const int32_t grid[3], int32_t block, 
 ssa_status ssa_plan_create(const int32_t* coords, int64_t n, const int32_t grid[3], int32_t block,
                            int32_t window, void* ws, size_t ws_bytes, hipStream_t stream,
                            ssa_plan* out);
+/* The same with any window partition (ssa_window_t, host).  ssa_plan_create(..., window, ...)
+ * is ssa_plan_create_ex with {SSA_WINDOW_CUBE, window, {0, 0, 0}, 0}.  Window cells that are
+ * not unions of blocks synchronise the stream once or twice more. */
+size_t ssa_plan_workspace_size_ex(int64_t n, const int32_t grid[3], int32_t block,
+                                  const ssa_window_t* win);
+ssa_status ssa_plan_create_ex(const int32_t* coords, int64_t n, const int32_t grid[3], int32_t block,
+                              const ssa_window_t* win, void* ws, size_t ws_bytes, hipStream_t stream,
+                              ssa_plan* out);
 ssa_status ssa_plan_get_info(ssa_plan plan, ssa_plan_info_t* info /* host */);
 /* Frees the host-side handle only (the workspace stays the caller's). */
 void ssa_plan_destroy(ssa_plan plan);
@@ -160,6 +200,25 @@ ssa_status ssa_forward_noalloc(ssa_plan plan, ssa_dtype dtype, int32_t heads, in
                                const void* q, const void* k, const void* v, const void* wk,
                                const void* wv, const void* gates, int32_t topk, float scale,
                                void* out, int32_t* sel_out, hipStream_t stream);
+
+/*
+ * Several samples in one call (a varlen batch; SSA never mixes tokens of different
+ * samples: each sample has its own plan, blocks, selection and windows).  Sample i owns
+ * tokens [tok_off[i], tok_off[i+1]) of the concatenated q, k, v, gates and out tensors
+ * ([N_total,H,d] / [N_total,H,3]); plans[i] (host array) is its plan, with
+ * plans[i]->n == tok_off[i+1] - tok_off[i]; tok_off (host, [nsamples+1]) starts at 0.
+ * W_k, W_v, dtype, heads, dim, topk and scale are shared.  The samples run one after
+ * another on `stream` through one workspace of ssa_forward_batch_workspace_size bytes
+ * (the largest sample's forward workspace).  Every argument check runs before the first
+ * launch.  The selection is not returned.
+ */
+size_t ssa_forward_batch_workspace_size(const ssa_plan* plans, int32_t nsamples, ssa_dtype dtype,
+                                        int32_t heads, int32_t dim, int32_t topk);
+ssa_status ssa_forward_batch(const ssa_plan* plans, int32_t nsamples, const int64_t* tok_off,
+                             ssa_dtype dtype, int32_t heads, int32_t dim, const void* q, const void* k,
+                             const void* v, const void* wk, const void* wv, const void* gates,
+                             int32_t topk, float scale, void* out, void* ws, size_t ws_bytes,
+                             hipStream_t stream);
 
 /*
  * SSA backward: the gradient of the forward defined above (the pages report SSA's

@@ -13,7 +13,7 @@ import os
 
 import torch
 
-__all__ = ["Plan", "forward", "forward_workspace_size", "forward_noalloc", "backward",
+__all__ = ["Plan", "Window", "forward", "forward_batch", "forward_workspace_size", "forward_noalloc", "backward",
            "backward_workspace_size", "NOALLOC_SCRATCH_BYTES",
            "SSAError", "lib", "LIB_PATH", "STAGE_POOL", "STAGE_SELECT", "STAGE_ATTEND", "STAGE_ALL"]
 
@@ -34,7 +34,14 @@ class PlanInfo(ctypes.Structure):
     _fields_ = [("n", _i64), ("num_blocks", _i64), ("num_cells", _i64), ("block", _i32),
                 ("window", _i32), ("max_block_rows", _i32), ("perm", _vp), ("blk_off", _vp),
                 ("blk_key", _vp), ("tok2blk", _vp), ("blk_cell", _vp), ("cell_off", _vp),
-                ("cell_blk", _vp), ("lpt", _vp)]
+                ("cell_blk", _vp), ("lpt", _vp), ("window_kind", _i32), ("window_shift", _i32 * 3),
+                ("window_tokens", _i32), ("cells_are_block_unions", _i32), ("num_wcells", _i64),
+                ("max_wcell_rows", _i32), ("wperm", _vp), ("wcell_off", _vp), ("wlpt", _vp)]
+
+
+class Window(ctypes.Structure):
+    """ssa_window_t: kind 0 = cubic cells floor((c + shift) / edge), 1 = Morton-order runs."""
+    _fields_ = [("kind", _i32), ("edge", _i32), ("shift", _i32 * 3), ("tokens", _i32)]
 
 
 def _load():
@@ -47,6 +54,11 @@ def _load():
     L.ssa_plan_workspace_size.restype = _sz
     L.ssa_plan_create.argtypes = [_vp, _i64, grid_t, _i32, _i32, _vp, _sz, _vp, ctypes.POINTER(_vp)]
     L.ssa_plan_create.restype = ctypes.c_int
+    L.ssa_plan_workspace_size_ex.argtypes = [_i64, grid_t, _i32, ctypes.POINTER(Window)]
+    L.ssa_plan_workspace_size_ex.restype = _sz
+    L.ssa_plan_create_ex.argtypes = [_vp, _i64, grid_t, _i32, ctypes.POINTER(Window), _vp, _sz, _vp,
+                                     ctypes.POINTER(_vp)]
+    L.ssa_plan_create_ex.restype = ctypes.c_int
     L.ssa_plan_get_info.argtypes = [_vp, ctypes.POINTER(PlanInfo)]
     L.ssa_plan_get_info.restype = ctypes.c_int
     L.ssa_plan_destroy.argtypes = [_vp]
@@ -62,6 +74,11 @@ def _load():
     L.ssa_forward_noalloc.argtypes = [_vp, ctypes.c_int, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp,
                                       _i32, ctypes.c_float, _vp, _vp, _vp]
     L.ssa_forward_noalloc.restype = ctypes.c_int
+    L.ssa_forward_batch_workspace_size.argtypes = [_vp, _i32, ctypes.c_int, _i32, _i32, _i32]
+    L.ssa_forward_batch_workspace_size.restype = _sz
+    L.ssa_forward_batch.argtypes = [_vp, _i32, _vp, ctypes.c_int, _i32, _i32, _vp, _vp, _vp, _vp, _vp,
+                                    _vp, _i32, ctypes.c_float, _vp, _vp, _sz, _vp]
+    L.ssa_forward_batch.restype = ctypes.c_int
     L.ssa_backward_workspace_size.argtypes = [_vp, ctypes.c_int, _i32, _i32, _i32]
     L.ssa_backward_workspace_size.restype = _sz
     L.ssa_backward.argtypes = [_vp, ctypes.c_int, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _i32,
@@ -116,9 +133,12 @@ def _uses(stream, *tensors):
 
 
 class Plan:
-    """Block partition of int32 coordinates [N,3] on the GPU (ssa_plan_create)."""
+    """Block partition of int32 coordinates [N,3] on the GPU (ssa_plan_create_ex).  The window
+    branch uses cubic cells of edge `window` shifted by `shift`, or, with sfc_tokens > 0,
+    runs of sfc_tokens tokens along the Morton order of the voxels."""
 
-    def __init__(self, coords: torch.Tensor, grid, block: int, window: int, stream=None):
+    def __init__(self, coords: torch.Tensor, grid, block: int, window: int, stream=None,
+                 shift=(0, 0, 0), sfc_tokens: int = 0):
         if coords.dtype != torch.int32 or coords.dim() != 2 or coords.shape[1] != 3:
             raise ValueError("coords must be an int32 tensor of shape [N,3]")
         if not coords.is_contiguous():
@@ -127,7 +147,9 @@ class Plan:
         self.grid = (_i32 * 3)(*grid)
         self.n = int(coords.shape[0])
         self.block, self.window = int(block), int(window)
-        size = lib.ssa_plan_workspace_size(self.n, self.grid, self.block, self.window)
+        self.win = Window(1 if sfc_tokens else 0, int(window), (_i32 * 3)(*[int(x) for x in shift]),
+                          int(sfc_tokens))
+        size = lib.ssa_plan_workspace_size_ex(self.n, self.grid, self.block, ctypes.byref(self.win))
         if size == 0:
             raise SSAError(1, "ssa_plan_workspace_size")
         with _alloc_on(stream):
@@ -135,8 +157,8 @@ class Plan:
         _uses(stream, coords)
         self.coords = coords
         h = _vp()
-        st = lib.ssa_plan_create(_ptr(coords), self.n, self.grid, self.block, self.window,
-                                 _ptr(self.ws), size, _stream(stream), ctypes.byref(h))
+        st = lib.ssa_plan_create_ex(_ptr(coords), self.n, self.grid, self.block, ctypes.byref(self.win),
+                                    _ptr(self.ws), size, _stream(stream), ctypes.byref(h))
         _check(st, "ssa_plan_create")
         self.handle = h
         info = PlanInfo()
@@ -145,6 +167,8 @@ class Plan:
         self.num_blocks = int(info.num_blocks)
         self.num_cells = int(info.num_cells)
         self.max_block_rows = int(info.max_block_rows)
+        self.cells_are_block_unions = bool(info.cells_are_block_unions)
+        self.num_wcells = int(info.num_wcells)
 
     def _view(self, ptr, count):
         off = int(ptr) - self.ws.data_ptr()
@@ -156,10 +180,17 @@ class Plan:
         if n == 0:
             return {}
         i = self.info
-        return {"perm": self._view(i.perm, n), "blk_off": self._view(i.blk_off, M + 1),
-                "blk_key": self._view(i.blk_key, M), "tok2blk": self._view(i.tok2blk, n),
-                "blk_cell": self._view(i.blk_cell, M), "cell_off": self._view(i.cell_off, C + 1),
-                "cell_blk": self._view(i.cell_blk, M), "lpt": self._view(i.lpt, M)}
+        a = {"perm": self._view(i.perm, n), "blk_off": self._view(i.blk_off, M + 1),
+             "blk_key": self._view(i.blk_key, M), "tok2blk": self._view(i.tok2blk, n),
+             "lpt": self._view(i.lpt, M)}
+        if self.cells_are_block_unions:
+            a.update(blk_cell=self._view(i.blk_cell, M), cell_off=self._view(i.cell_off, C + 1),
+                     cell_blk=self._view(i.cell_blk, M))
+        else:
+            Cw = self.num_wcells
+            a.update(wperm=self._view(i.wperm, n), wcell_off=self._view(i.wcell_off, Cw + 1),
+                     wlpt=self._view(i.wlpt, Cw))
+        return a
 
     def __del__(self):
         h = getattr(self, "handle", None)
@@ -231,6 +262,37 @@ def forward_noalloc(plan: Plan, q, k, v, wk, wv, gates, topk: int, out, sel_out=
                                  _ptr(out), _ptr(sel_out), _stream(stream))
     _check(st, "ssa_forward_noalloc")
     return out, sel_out
+
+
+def forward_batch(plans, tok_off, q, k, v, wk, wv, gates, topk: int, scale: float = 0.0, out=None,
+                  ws=None, stream=None):
+    """SSA forward of several samples (ssa_forward_batch): sample i owns tokens
+    [tok_off[i], tok_off[i+1]) of the concatenated q, k, v, gates [N_total,H,d|3] and has its
+    own plan plans[i].  Returns out [N_total,H,d]."""
+    N, H, d = q.shape
+    for t in (q, k, v, wk, wv, gates):
+        if t.dtype != q.dtype or not t.is_contiguous() or t.device != q.device:
+            raise ValueError("all tensors must be contiguous, on one device, with one dtype")
+    if k.shape != q.shape or v.shape != q.shape or gates.shape != (N, H, 3) or wk.shape != (d, d) \
+            or wv.shape != (d, d) or int(tok_off[-1]) != N or len(tok_off) != len(plans) + 1:
+        raise ValueError("shape mismatch")
+    dt = _DTYPES[q.dtype]
+    handles = (_vp * len(plans))(*[p.handle.value for p in plans])
+    offs = (_i64 * len(tok_off))(*[int(x) for x in tok_off])
+    size = lib.ssa_forward_batch_workspace_size(handles, len(plans), dt, H, d, topk)
+    if size == 0:
+        raise SSAError(2, "ssa_forward_batch_workspace_size")
+    _uses(stream, q, k, v, wk, wv, gates, out, ws, *[p.ws for p in plans])
+    with _alloc_on(stream):
+        if out is None:
+            out = torch.empty_like(q)
+        if ws is None or ws.numel() < size:
+            ws = torch.empty(size, dtype=torch.uint8, device=q.device)
+    st = lib.ssa_forward_batch(handles, len(plans), offs, dt, H, d, _ptr(q), _ptr(k), _ptr(v), _ptr(wk),
+                               _ptr(wv), _ptr(gates), int(topk), float(scale), _ptr(out), _ptr(ws),
+                               ws.numel(), _stream(stream))
+    _check(st, "ssa_forward_batch")
+    return out
 
 
 def backward_workspace_size(plan: Plan, dtype, heads: int, dim: int, topk: int) -> int:

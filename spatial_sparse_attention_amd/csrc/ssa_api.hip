@@ -57,6 +57,7 @@ size_t fwd_carve(Carver& c, const ssa_plan_s* p, ssa_dtype dt, int H, int d, int
     t.obr = c.take<float>((size_t)3 * H * n1 * d);
   }
   t.lsec = save ? t.lse : c.take<float>((size_t)H * n1);
+  t.ow = p->wkind != 0 ? c.take<char>((size_t)n1 * H * d * es) : nullptr;
   if (w) *w = t;
   return c.off;
 }
@@ -84,6 +85,7 @@ extern "C" ssa_status ssa_forward_stages(ssa_plan p, ssa_dtype dt, int32_t H, in
   if (!ws) return SSA_ERR_WORKSPACE;
   const int save = save_for_bwd ? 1 : 0;
   if (p->M > select_block_limit(dt, d)) return SSA_ERR_UNSUPPORTED;  // before any launch
+  if (save && p->wkind != 0) return SSA_ERR_UNSUPPORTED;  // the backward needs cells of blocks
   // the size query adds 256 bytes of alignment slack; what counts is the carve from the
   // workspace's actual alignment
   Carver c(ws);
@@ -155,9 +157,51 @@ extern "C" ssa_status ssa_forward_noalloc(ssa_plan p, ssa_dtype dt, int32_t H, i
                             (size_t)SSA_NOALLOC_SCRATCH_BYTES, 0, stream, SSA_STAGE_ALL);
 }
 
+// ------------------------------------------------------------------ several samples
+extern "C" size_t ssa_forward_batch_workspace_size(const ssa_plan* plans, int32_t nsamples, ssa_dtype dt,
+                                                   int32_t H, int32_t d, int32_t topk) {
+  if (!plans || nsamples < 1) return 0;
+  size_t mx = 0;
+  for (int i = 0; i < nsamples; ++i) {
+    const size_t sz = ssa_forward_workspace_size(plans[i], dt, H, d, topk, 0);
+    if (sz == 0) return 0;
+    mx = sz > mx ? sz : mx;
+  }
+  return mx;
+}
+
+extern "C" ssa_status ssa_forward_batch(const ssa_plan* plans, int32_t nsamples, const int64_t* tok_off,
+                                        ssa_dtype dt, int32_t H, int32_t d, const void* q, const void* k,
+                                        const void* v, const void* wk, const void* wv, const void* gates,
+                                        int32_t topk, float scale, void* out, void* ws, size_t ws_bytes,
+                                        hipStream_t stream) {
+  if (!plans || !tok_off || nsamples < 1) return SSA_ERR_INVALID_ARG;
+  if (tok_off[0] != 0) return SSA_ERR_INVALID_ARG;
+  for (int i = 0; i < nsamples; ++i) {  // every check before any launch
+    const ssa_status st = check_common(plans[i], dt, H, d, topk);
+    if (st != SSA_OK) return st;
+    if (tok_off[i + 1] - tok_off[i] != plans[i]->n) return SSA_ERR_INVALID_ARG;
+    if (plans[i]->M > select_block_limit(dt, d)) return SSA_ERR_UNSUPPORTED;
+  }
+  if (ws_bytes < ssa_forward_batch_workspace_size(plans, nsamples, dt, H, d, topk)) return SSA_ERR_WORKSPACE;
+  const size_t es = esize_of(dt);
+  auto at = [&](const void* base, int64_t tok, int64_t per) -> const void* {
+    return base ? static_cast<const char*>(base) + (size_t)tok * per * es : nullptr;
+  };
+  for (int i = 0; i < nsamples; ++i) {
+    const int64_t t0 = tok_off[i];
+    const ssa_status st = ssa_forward_stages(
+        plans[i], dt, H, d, at(q, t0, (int64_t)H * d), at(k, t0, (int64_t)H * d), at(v, t0, (int64_t)H * d), wk, wv,
+        at(gates, t0, (int64_t)H * 3), topk, scale, const_cast<void*>(at(out, t0, (int64_t)H * d)), nullptr, ws,
+        ws_bytes, 0, stream, SSA_STAGE_ALL);
+    if (st != SSA_OK) return st;
+  }
+  return SSA_OK;
+}
+
 extern "C" size_t ssa_backward_workspace_size(ssa_plan p, ssa_dtype dt, int32_t H, int32_t d,
                                               int32_t topk) {
-  if (check_common(p, dt, H, d, topk) != SSA_OK) return 0;
+  if (check_common(p, dt, H, d, topk) != SSA_OK || p->wkind != 0) return 0;
   Carver c(nullptr);
   return bwd_carve(c, p, H, d, topk, nullptr) + 256;
 }
@@ -177,6 +221,7 @@ extern "C" ssa_status ssa_backward(ssa_plan p, ssa_dtype dt, int32_t H, int32_t 
   if (!q || !k || !v || !wk || !wv || !gates || !sel || !dout || !dq || !dk || !dv || !dgates)
     return SSA_ERR_INVALID_ARG;
   if (p->M > select_block_limit(dt, d)) return SSA_ERR_UNSUPPORTED;  // the forward's limit
+  if (p->wkind != 0) return SSA_ERR_UNSUPPORTED;  // window cells must be unions of blocks
   if (!fwd_ws || fwd_ws_bytes < ssa_forward_workspace_size(p, dt, H, d, topk, 1)) return SSA_ERR_WORKSPACE;
   if (!ws || ws_bytes < ssa_backward_workspace_size(p, dt, H, d, topk)) return SSA_ERR_WORKSPACE;
   if (!recorded_scale_matches(p, fwd_ws, scale)) return SSA_ERR_INVALID_ARG;

@@ -37,6 +37,10 @@ constexpr int CMP_WAVES = 8;      // compressed pass 1: waves per workgroup, 32 
 constexpr int SEL_WAVES = 8;      // importance pass: waves per workgroup (256 rows per sweep)
 constexpr int ATT_WAVES = 4;      // selected/window: waves per workgroup, 32 query rows each
 constexpr int ATT_ROWS = 32 * ATT_WAVES;
+// k_attend modes: both branches of the block partition (window cells are unions of blocks);
+// the window branch alone over a token-level window partition (its output to a buffer);
+// the selected branch alone, combined with that buffer.
+enum { ATT_BOTH = 0, ATT_WINDOW = 1, ATT_SELECTED = 2 };
 
 // ------------------------------------------------------------------ pooling
 // One workgroup per (block, group of hg heads), blocks longest first: ktil[h,b] =
@@ -876,7 +880,8 @@ __global__ __launch_bounds__(64 * ATT_WAVES) __attribute__((amdgpu_waves_per_eu(
     const int32_t* __restrict__ cell_blk, const int32_t* __restrict__ lpt,
     const int32_t* __restrict__ sel, const typename Tr<DT>::T* __restrict__ oc, int M, int H,
     int nchunk, int64_t N, int topk, float sl2, int window_is_block, typename Tr<DT>::T* __restrict__ out,
-    float* __restrict__ lse_save, float* __restrict__ os_save, float* __restrict__ ow_save) {
+    float* __restrict__ lse_save, float* __restrict__ os_save, float* __restrict__ ow_save, int mode,
+    const typename Tr<DT>::T* __restrict__ ow_in) {
   using C = Cfg<DT, D>;
   using T = typename Tr<DT>::T;
   using F = typename Tr<DT>::frag;
@@ -905,8 +910,7 @@ __global__ __launch_bounds__(64 * ATT_WAVES) __attribute__((amdgpu_waves_per_eu(
   if (chunk * ATT_ROWS >= rows) return;  // uniform across the workgroup
 
   // ---- metadata, loads issued side by side: selection row, window cell, queries, gates
-  const int32_t* srow = sel + ((int64_t)h * M + b) * topk;
-  const int sb = tid < topk ? srow[tid] : -1;  // selected ids ascend, -1 padded at the end
+  const int sb = mode != ATT_WINDOW && tid < topk ? sel[((int64_t)h * M + b) * topk + tid] : -1;  // ascending, -1 padded
   int c0 = b, c1 = b + 1;                       // window cell as a range of cell_blk
   if (!window_is_block) {
     const int cell = blk_cell[b];
@@ -921,7 +925,7 @@ __global__ __launch_bounds__(64 * ATT_WAVES) __attribute__((amdgpu_waves_per_eu(
   F qf[C::NKS];
   load_q<DT, D>(qf, q + (tok_q * H + h) * D, valid, lane);
   float gt[3] = {0.f, 0.f, 0.f};
-  if (valid) {
+  if (valid && mode != ATT_WINDOW) {
 #pragma unroll
     for (int x = 0; x < 3; ++x) gt[x] = Tr<DT>::up(gates[(tok_q * H + h) * 3 + x]);
   }
@@ -930,7 +934,7 @@ __global__ __launch_bounds__(64 * ATT_WAVES) __attribute__((amdgpu_waves_per_eu(
   typedef unsigned ocv_t __attribute__((ext_vector_type(2)));
   constexpr bool OCPRE = sizeof(T) == 2 && (BUF || D <= 64);  // register budget
   ocv_t ocv[OCPRE ? C::NDV * 4 : 1];
-  if constexpr (OCPRE) {
+  if constexpr (OCPRE) if (mode != ATT_WINDOW) {
     const T* orow0 = oc + ((int64_t)(r0 + (valid ? my_row : 0)) * H + h) * D + 4 * g;
 #pragma unroll
     for (int j = 0; j < C::NDV; ++j)
@@ -939,7 +943,7 @@ __global__ __launch_bounds__(64 * ATT_WAVES) __attribute__((amdgpu_waves_per_eu(
   }
   if (sb >= 0) sel_lds[tid] = sb;
   const int nsel = __syncthreads_count(sb >= 0);
-  const int nwin = c1 - c0;
+  const int nwin = mode == ATT_SELECTED ? 0 : c1 - c0;
   TC tc;
   tc.init(wave, lane);
   Online<C::NDV> st;
@@ -1009,7 +1013,7 @@ __global__ __launch_bounds__(64 * ATT_WAVES) __attribute__((amdgpu_waves_per_eu(
         [&](int t) __attribute__((always_inline)) { tc.fetch(keytok, t * KT, tot); },
         [&](T* dst) __attribute__((always_inline)) { tc.template issue<BUF>(dst, kin, vin, H, h, wave); },
         [&](int t, const T* cur, auto&& next) __attribute__((always_inline)) {
-          if (t == tb) {  // first window tile: close the selected branch
+          if (t == tb && tb > 0) {  // first window tile: close the selected branch
             close_selected();
             st.init();
           }
@@ -1038,15 +1042,31 @@ __global__ __launch_bounds__(64 * ATT_WAVES) __attribute__((amdgpu_waves_per_eu(
             }
           }
         });
+    if (mode == ATT_SELECTED) close_selected();
   } else {
-    gathered_branch<DT, D, BUF, NB>(st, tc, sel_lds, nsel, qf, kin, vin, perm, blk_off, H, h, sl2,
-                                    wave_active, bufs, pre, lst_off, keytok);
-    close_selected();
-    gathered_branch<DT, D, BUF, NB>(st, tc, cell_blk + c0, nwin, qf, kin, vin, perm, blk_off, H, h, sl2,
-                                    wave_active, bufs, pre, lst_off, keytok);
+    if (mode != ATT_WINDOW) {
+      gathered_branch<DT, D, BUF, NB>(st, tc, sel_lds, nsel, qf, kin, vin, perm, blk_off, H, h, sl2,
+                                      wave_active, bufs, pre, lst_off, keytok);
+      close_selected();
+    }
+    if (mode != ATT_SELECTED) {
+      const int32_t* wlist = window_is_block ? lpt + unit : cell_blk + c0;  // lpt[unit] == b
+      gathered_branch<DT, D, BUF, NB>(st, tc, wlist, nwin, qf, kin, vin, perm, blk_off, H, h, sl2,
+                                      wave_active, bufs, pre, lst_off, keytok);
+    }
   }
-  if (wave_active && valid) {
-    const float ltot = xor32_sum(st.l);
+  if (wave_active && valid && mode == ATT_WINDOW) {  // the window branch's output, caller order
+    const float inv = 1.f / xor32_sum(st.l);
+    T* dst = out + (tok_q * H + h) * D;
+#pragma unroll
+    for (int j = 0; j < C::NDV; ++j)
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq)
+        store4(dst + 32 * j + 8 * rq + 4 * g, st.o[j][4 * rq] * inv, st.o[j][4 * rq + 1] * inv,
+               st.o[j][4 * rq + 2] * inv, st.o[j][4 * rq + 3] * inv);
+  }
+  if (wave_active && valid && mode != ATT_WINDOW) {
+    const float ltot = mode == ATT_SELECTED ? 1.f : xor32_sum(st.l);
     const float f = gt[2] / ltot;
     const T* orow = oc + ((int64_t)(r0 + my_row) * H + h) * D;
     T* dst = out + (tok_q * H + h) * D;
@@ -1075,8 +1095,15 @@ __global__ __launch_bounds__(64 * ATT_WAVES) __attribute__((amdgpu_waves_per_eu(
         } else {
           load4(orow + col, v);
         }
+        if (mode == ATT_SELECTED) {  // the window branch came from its own pass
+          float w4[4];
+          load4(ow_in + (tok_q * H + h) * D + col, w4);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = res[j][4 * rq + e] + f * st.o[j][4 * rq + e] + gt[0] * v[e];
+          for (int e = 0; e < 4; ++e) v[e] = res[j][4 * rq + e] + gt[2] * w4[e] + gt[0] * v[e];
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = res[j][4 * rq + e] + f * st.o[j][4 * rq + e] + gt[0] * v[e];
+        }
         store4(dst + col, v[0], v[1], v[2], v[3]);
       }
   }
@@ -1152,19 +1179,27 @@ hipError_t run_attend(const ssa_plan_s* p, int H, int topk, float sl2, const voi
                       const void* k, const void* v, const void* gates, const FwdWs& w,
                       const int32_t* sel, void* out, hipStream_t s) {
   using T = typename Tr<DT>::T;
-  const int nchunk = (p->max_rows + ATT_ROWS - 1) / ATT_ROWS;
-  if (buffer_addressable(p->n * H * D * (int64_t)sizeof(T)))
-    hipLaunchKernelGGL((k_attend<DT, D, true>), dim3(xcd_grid(p->M, (int64_t)H * nchunk)), dim3(64 * ATT_WAVES), 0,
-                     s, (const T*)q, (const T*)k, (const T*)v, (const T*)gates, p->perm, p->blk_off,
-                     p->blk_cell, p->cell_off, p->cell_blk, p->lpt, sel, (const T*)w.oc, (int)p->M,
-                     H, nchunk, p->n, topk, sl2, (int)p->window_is_block, (T*)out, w.lse,
-                     w.obr ? w.obr + p->n * H * D : nullptr, w.obr ? w.obr + 2 * p->n * H * D : nullptr);
-  else
-    hipLaunchKernelGGL((k_attend<DT, D, false>), dim3(xcd_grid(p->M, (int64_t)H * nchunk)), dim3(64 * ATT_WAVES), 0,
-                     s, (const T*)q, (const T*)k, (const T*)v, (const T*)gates, p->perm, p->blk_off,
-                     p->blk_cell, p->cell_off, p->cell_blk, p->lpt, sel, (const T*)w.oc, (int)p->M,
-                     H, nchunk, p->n, topk, sl2, (int)p->window_is_block, (T*)out, w.lse,
-                     w.obr ? w.obr + p->n * H * D : nullptr, w.obr ? w.obr + 2 * p->n * H * D : nullptr);
+  const bool buf = buffer_addressable(p->n * H * D * (int64_t)sizeof(T));
+  auto launch = [&](int mode, int64_t units, const int32_t* perm, const int32_t* off, const int32_t* lpt,
+                    int max_rows, int wib, T* dst) {
+    const int nchunk = (max_rows + ATT_ROWS - 1) / ATT_ROWS;
+    float* lse = mode == ATT_BOTH ? w.lse : nullptr;
+    float* os = mode == ATT_BOTH && w.obr ? w.obr + p->n * H * D : nullptr;
+    float* ows = mode == ATT_BOTH && w.obr ? w.obr + 2 * p->n * H * D : nullptr;
+    auto kern = buf ? k_attend<DT, D, true> : k_attend<DT, D, false>;
+    hipLaunchKernelGGL(kern, dim3(xcd_grid(units, (int64_t)H * nchunk)), dim3(64 * ATT_WAVES), 0, s,
+                       (const T*)q, (const T*)k, (const T*)v, (const T*)gates, perm, off, p->blk_cell,
+                       p->cell_off, p->cell_blk, lpt, sel, (const T*)w.oc, (int)units, H, nchunk, p->n,
+                       topk, sl2, wib, dst, lse, os, ows, mode, (const T*)w.ow);
+  };
+  if (p->wkind == 0) {
+    launch(ATT_BOTH, p->M, p->perm, p->blk_off, p->lpt, p->max_rows, (int)p->window_is_block, (T*)out);
+  } else {
+    // window cells that are not unions of blocks: the window branch over its own partition
+    // (each cell's tokens attend to each other), then the selected branch and the combine
+    launch(ATT_WINDOW, p->wC, p->wperm, p->wcell_off, p->wlpt, p->wmax_rows, 1, (T*)w.ow);
+    launch(ATT_SELECTED, p->M, p->perm, p->blk_off, p->lpt, p->max_rows, 1, (T*)out);
+  }
   return hipGetLastError();
 }
 

@@ -19,6 +19,15 @@ struct ssa_plan_s {
   int32_t max_rows;
   bool window_is_block;     // w == B: cells alias blocks
   int32_t *perm, *blk_off, *blk_key, *tok2blk, *blk_cell, *cell_off, *cell_blk, *lpt;
+  // Window cells that are not unions of blocks get a token-level partition of their own:
+  // wkind 0 = cells are unions of blocks (blk_cell, cell_off, cell_blk above); 1 = cubic
+  // cells floor((c + wshift) / window); 2 = runs of sfc_tokens tokens along the Morton order.
+  int32_t wkind = 0;
+  int32_t wshift[3] = {0, 0, 0};
+  int32_t sfc_tokens = 0;
+  int64_t wC = 0;           // cells of the token-level partition
+  int32_t wmax_rows = 0;    // tokens of its largest cell
+  int32_t *wperm = nullptr, *wcell_off = nullptr, *wlpt = nullptr;
   // Softmax scale of the most recent forwards that saved state for the backward, by
   // workspace address: the saved log-sum-exp values hold that scale, so a backward on
   // the same workspace must use it.  Guarded by rec_mu (a plan may serve several threads).
@@ -48,6 +57,7 @@ struct PlanWs {
   uint32_t *key_a, *key_b;
   int32_t *val_a, *val_b, *rank, *hist, *tile_cnt, *counters, *scan_part;
   int32_t* cell_key;
+  int32_t *wperm, *wcell_off, *wlpt;  // token-level window partition (when cells are not unions of blocks)
 };
 size_t plan_carve(Carver& c, int64_t n, PlanWs* w);
 
@@ -88,6 +98,8 @@ struct FwdWs {
   int32_t* sel;      // [H][M][topk]
   float* sigma;      // [H][M][Mp] importance scores when the top-k runs as its own kernel, else null
   float* lsec;       // [H][N] log2-sum-exp2 of the compressed branch's scaled scores (= lse plane 0)
+  void* ow;          // [N][H][d] dtype, caller order: the window branch's output when window cells
+                     // have a token-level partition of their own (else null)
   // saved for the backward (save_for_bwd only; else null)
   float* lse;        // [3][H][N] per-branch log2-sum-exp2 of the scaled scores
   float* obr;        // [3][N][H][d] the three branch outputs in fp32 (compressed, selected, window)

@@ -291,6 +291,35 @@ __global__ void k_identity_cells(const int32_t* __restrict__ Mdev, int32_t* blk_
   }
 }
 
+// Keys of the token-level window partition: kind 1 = cubic cells floor((c + shift) / w)
+// (x-major cell key over cdims), kind 2 = Morton code of the voxel (bit b of x, y, z at
+// bits 3b+2, 3b+1, 3b: x most significant in each triple).  Coordinates were range-checked
+// by k_block_keys.
+__global__ void k_window_keys(const int32_t* __restrict__ coords, int64_t n, int kind, int w, int3 shift,
+                              int3 cdims, int sfc_bits, uint32_t* __restrict__ keys, int32_t* __restrict__ vals) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const uint32_t x = (uint32_t)coords[3 * i], y = (uint32_t)coords[3 * i + 1], z = (uint32_t)coords[3 * i + 2];
+  uint32_t key = 0;
+  if (kind == 1) {
+    const uint32_t cx = (x + shift.x) / w, cy = (y + shift.y) / w, cz = (z + shift.z) / w;
+    key = (cx * (uint32_t)cdims.y + cy) * (uint32_t)cdims.z + cz;
+  } else {
+    for (int b = sfc_bits - 1; b >= 0; --b)
+      key = (key << 3) | (((x >> b) & 1u) << 2) | (((y >> b) & 1u) << 1) | ((z >> b) & 1u);
+  }
+  keys[i] = key;
+  vals[i] = (int32_t)i;
+}
+
+// Cells of a space-filling-curve window partition: runs of `per` consecutive tokens of the
+// Morton order, the last one shorter; *count = number of cells.
+__global__ void k_sfc_cells(int32_t* __restrict__ cell_off, int n, int per, int ncell, int32_t* __restrict__ count) {
+  const int j = blockIdx.x * blockDim.x + threadIdx.x;
+  if (j <= ncell) cell_off[j] = (int32_t)min((int64_t)j * per, (int64_t)n);
+  if (j == 0) *count = ncell;
+}
+
 }  // namespace
 
 namespace ssa_sort {
@@ -345,9 +374,72 @@ hipError_t segments(const uint32_t* keys, const int32_t* vals, int n, int32_t* t
 namespace {
 using namespace ssa_sort;
 
-bool window_supported(const int32_t grid[3], int B, int w, bool* single) {
-  *single = w >= grid[0] && w >= grid[1] && w >= grid[2];
-  return *single || (w % B == 0);
+// Window cells that are unions of blocks: one cell covering the grid, or an edge that is a
+// multiple of the block edge with no shift.
+bool window_is_union(const int32_t grid[3], int B, const ssa_window_t& win, bool* single) {
+  *single = false;
+  if (win.kind != SSA_WINDOW_CUBE) return false;
+  const int w = win.edge;
+  const bool noshift = win.shift[0] == 0 && win.shift[1] == 0 && win.shift[2] == 0;
+  *single = noshift && w >= grid[0] && w >= grid[1] && w >= grid[2];
+  return *single || (noshift && w % B == 0);
+}
+
+// The token-level window partition: keys, a stable radix sort, cells (key runs, or runs of
+// sfc_tokens tokens) and their longest-first order.  Synchronises the stream once or twice.
+ssa_status build_window_partition(ssa_plan_s* p, const int32_t* coords, PlanWs& w, hipStream_t stream) {
+  const int ni = (int)p->n;
+  int3 cd = make_int3(1, 1, 1);
+  int nbits = 0;
+  uint64_t maxkey = 1;
+  if (p->wkind == 1) {
+    cd = make_int3((p->grid[0] + p->wshift[0] + p->window - 1) / p->window,
+                   (p->grid[1] + p->wshift[1] + p->window - 1) / p->window,
+                   (p->grid[2] + p->wshift[2] + p->window - 1) / p->window);
+    maxkey = (uint64_t)cd.x * cd.y * cd.z;
+  } else {
+    const int g = std::max(p->grid[0], std::max(p->grid[1], p->grid[2]));
+    nbits = bits_for((uint64_t)(g - 1));
+    maxkey = (uint64_t)1 << (3 * nbits);
+  }
+  hipLaunchKernelGGL(k_window_keys, dim3((ni + 255) / 256), dim3(256), 0, stream, coords, p->n, p->wkind,
+                     p->window, make_int3(p->wshift[0], p->wshift[1], p->wshift[2]), cd, nbits, w.key_a, w.val_a);
+  uint32_t *ka = w.key_a, *kb = w.key_b;
+  int32_t *va = w.val_a, *vb = w.val_b;
+  if (radix_sort(ka, va, kb, vb, ni, bits_for(maxkey - 1), w.rank, w.hist, w.scan_part, stream) != hipSuccess)
+    return SSA_ERR_HIP;
+  if (hipMemcpyAsync(w.wperm, va, p->n * sizeof(int32_t), hipMemcpyDeviceToDevice, stream) != hipSuccess)
+    return SSA_ERR_HIP;
+  if (p->wkind == 1) {
+    if (segments(ka, va, ni, w.tile_cnt, w.counters + 3, w.wcell_off, nullptr, nullptr, w.scan_part, stream) !=
+        hipSuccess)
+      return SSA_ERR_HIP;
+  } else {
+    const int nc = (int)((p->n + p->sfc_tokens - 1) / p->sfc_tokens);
+    hipLaunchKernelGGL(k_sfc_cells, dim3((nc + 256) / 256), dim3(256), 0, stream, w.wcell_off, ni, p->sfc_tokens,
+                       nc, w.counters + 3);
+  }
+  hipLaunchKernelGGL(k_lpt_rank, dim3(1), dim3(1024), 0, stream, w.wcell_off, w.counters + 3, w.wlpt,
+                     w.counters + 4);
+  int32_t host_cnt[8];
+  if (hipMemcpyAsync(host_cnt, w.counters, sizeof(host_cnt), hipMemcpyDeviceToHost, stream) != hipSuccess ||
+      hipStreamSynchronize(stream) != hipSuccess)
+    return SSA_ERR_HIP;
+  const int C = host_cnt[3];
+  if (C > LPT_RANK_MAX) {  // longest-first cell order by a radix sort of (n - size)
+    hipLaunchKernelGGL(k_block_stats, dim3((C + 255) / 256), dim3(256), 0, stream, w.wcell_off, C, ni, w.key_a,
+                       w.val_a, w.counters + 4);
+    ka = w.key_a; kb = w.key_b; va = w.val_a; vb = w.val_b;
+    if (radix_sort(ka, va, kb, vb, C, bits_for((uint64_t)p->n), w.rank, w.hist, w.scan_part, stream) != hipSuccess)
+      return SSA_ERR_HIP;
+    if (hipMemcpyAsync(w.wlpt, va, C * sizeof(int32_t), hipMemcpyDeviceToDevice, stream) != hipSuccess ||
+        hipMemcpyAsync(host_cnt, w.counters, sizeof(host_cnt), hipMemcpyDeviceToHost, stream) != hipSuccess ||
+        hipStreamSynchronize(stream) != hipSuccess)
+      return SSA_ERR_HIP;
+  }
+  p->wC = C;
+  p->wmax_rows = host_cnt[4];
+  return SSA_OK;
 }
 
 }  // namespace
@@ -374,6 +466,9 @@ size_t plan_carve(Carver& c, int64_t n, PlanWs* w) {
   t.counters = c.take<int32_t>(8);
   t.scan_part = c.take<int32_t>(tiles * 256 / 4096 + 2);
   t.cell_key = c.take<int32_t>(n1);
+  t.wperm = c.take<int32_t>(n1);
+  t.wcell_off = c.take<int32_t>(n1 + 1);
+  t.wlpt = c.take<int32_t>(n1);
   if (w) *w = t;
   return c.off;
 }
@@ -386,14 +481,41 @@ extern "C" size_t ssa_plan_workspace_size(int64_t n, const int32_t grid[3], int3
   return plan_carve(c, n, nullptr) + 256;
 }
 
+extern "C" size_t ssa_plan_workspace_size_ex(int64_t n, const int32_t grid[3], int32_t block,
+                                             const ssa_window_t* win) {
+  (void)win;
+  return ssa_plan_workspace_size(n, grid, block, 1);
+}
+
 extern "C" ssa_status ssa_plan_create(const int32_t* coords, int64_t n, const int32_t grid[3],
                                       int32_t block, int32_t window, void* ws, size_t ws_bytes,
                                       hipStream_t stream, ssa_plan* out) {
-  if (!out || !grid) return SSA_ERR_INVALID_ARG;
+  ssa_window_t win = {SSA_WINDOW_CUBE, window, {0, 0, 0}, 0};
+  return ssa_plan_create_ex(coords, n, grid, block, &win, ws, ws_bytes, stream, out);
+}
+
+extern "C" ssa_status ssa_plan_create_ex(const int32_t* coords, int64_t n, const int32_t grid[3],
+                                         int32_t block, const ssa_window_t* winp, void* ws, size_t ws_bytes,
+                                         hipStream_t stream, ssa_plan* out) {
+  if (!out || !grid || !winp) return SSA_ERR_INVALID_ARG;
   *out = nullptr;
-  if (n < 0 || block < 1 || window < 1) return SSA_ERR_INVALID_ARG;
+  const ssa_window_t win = *winp;
+  if (n < 0 || block < 1) return SSA_ERR_INVALID_ARG;
   if (grid[0] < 1 || grid[1] < 1 || grid[2] < 1) return SSA_ERR_INVALID_ARG;
   if (n > 0 && !coords) return SSA_ERR_INVALID_ARG;
+  if (win.kind == SSA_WINDOW_CUBE) {
+    if (win.edge < 1) return SSA_ERR_INVALID_ARG;
+    for (int a = 0; a < 3; ++a)
+      if (win.shift[a] < 0 || win.shift[a] >= win.edge) return SSA_ERR_INVALID_ARG;
+    uint64_t ncell = 1;
+    for (int a = 0; a < 3; ++a) ncell *= (uint64_t)((grid[a] + win.shift[a] + win.edge - 1) / win.edge);
+    if (ncell > (1ull << 31)) return SSA_ERR_UNSUPPORTED;
+  } else if (win.kind == SSA_WINDOW_SFC) {
+    if (win.tokens < 1) return SSA_ERR_INVALID_ARG;
+    if (grid[0] > 1024 || grid[1] > 1024 || grid[2] > 1024) return SSA_ERR_UNSUPPORTED;  // 30-bit codes
+  } else {
+    return SSA_ERR_INVALID_ARG;
+  }
   if (n >= (int64_t)1 << 31) return SSA_ERR_UNSUPPORTED;
   int32_t dims[3];
   uint64_t nblocks = 1;
@@ -403,9 +525,10 @@ extern "C" ssa_status ssa_plan_create(const int32_t* coords, int64_t n, const in
   }
   if (nblocks > (1ull << 31)) return SSA_ERR_UNSUPPORTED;
   bool single = false;
-  if (!window_supported(grid, block, window, &single)) return SSA_ERR_UNSUPPORTED;
+  const bool uni = window_is_union(grid, block, win, &single);
+  const int32_t window = win.kind == SSA_WINDOW_CUBE ? win.edge : 0;
   if (!ws) return SSA_ERR_WORKSPACE;
-  if (ws_bytes < ssa_plan_workspace_size(n, grid, block, window)) return SSA_ERR_WORKSPACE;
+  if (ws_bytes < ssa_plan_workspace_size(n, grid, block, 1)) return SSA_ERR_WORKSPACE;
 
   Carver c(ws);
   c.off = (256 - (reinterpret_cast<uintptr_t>(ws) & 255)) & 255;
@@ -419,7 +542,11 @@ extern "C" ssa_status ssa_plan_create(const int32_t* coords, int64_t n, const in
   memcpy(p->dims, dims, sizeof(p->dims));
   p->block = block;
   p->window = window;
-  p->window_is_block = (window == block) || (single && nblocks == 1);
+  p->window_is_block = uni && ((window == block) || (single && nblocks == 1));
+  p->wkind = uni ? 0 : (win.kind == SSA_WINDOW_CUBE ? 1 : 2);
+  for (int a = 0; a < 3; ++a) p->wshift[a] = win.kind == SSA_WINDOW_CUBE ? win.shift[a] : 0;
+  p->sfc_tokens = win.kind == SSA_WINDOW_SFC ? win.tokens : 0;
+  p->wperm = w.wperm; p->wcell_off = w.wcell_off; p->wlpt = w.wlpt;
   p->perm = w.perm; p->blk_off = w.blk_off; p->blk_key = w.blk_key; p->tok2blk = w.tok2blk;
   p->blk_cell = w.blk_cell; p->cell_off = w.cell_off; p->cell_blk = w.cell_blk; p->lpt = w.lpt;
   p->M = 0; p->ncells = 0; p->max_rows = 0;
@@ -475,7 +602,7 @@ extern "C" ssa_status ssa_plan_create(const int32_t* coords, int64_t n, const in
   }
 
   // window cells as groups of blocks (identity cells were written above)
-  if (!p->window_is_block) {
+  if (!p->window_is_block && p->wkind == 0) {
     const int ratio = single ? 1 : window / block;
     int3 cd = make_int3(1, 1, 1);
     if (!single)
@@ -497,7 +624,11 @@ extern "C" ssa_status ssa_plan_create(const int32_t* coords, int64_t n, const in
       hipStreamSynchronize(stream) != hipSuccess)
     return fail(SSA_ERR_HIP);
   p->max_rows = host_cnt[1];
-  p->ncells = p->window_is_block ? M : host_cnt[2];
+  p->ncells = p->wkind != 0 ? 0 : (p->window_is_block ? M : host_cnt[2]);
+  if (p->wkind != 0) {
+    const ssa_status st = build_window_partition(p, coords, w, stream);
+    if (st != SSA_OK) return fail(st);
+  }
   *out = p;
   return SSA_OK;
 }
@@ -519,6 +650,15 @@ extern "C" ssa_status ssa_plan_get_info(ssa_plan p, ssa_plan_info_t* info) {
   info->cell_off = p->cell_off;
   info->cell_blk = p->cell_blk;
   info->lpt = p->lpt;
+  info->window_kind = p->wkind == 2 ? SSA_WINDOW_SFC : SSA_WINDOW_CUBE;
+  for (int a = 0; a < 3; ++a) info->window_shift[a] = p->wshift[a];
+  info->window_tokens = p->sfc_tokens;
+  info->cells_are_block_unions = p->wkind == 0;
+  info->num_wcells = p->wkind != 0 ? p->wC : 0;
+  info->max_wcell_rows = p->wkind != 0 ? p->wmax_rows : 0;
+  info->wperm = p->wkind != 0 ? p->wperm : nullptr;
+  info->wcell_off = p->wkind != 0 ? p->wcell_off : nullptr;
+  info->wlpt = p->wkind != 0 ? p->wlpt : nullptr;
   return SSA_OK;
 }
 

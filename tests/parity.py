@@ -29,11 +29,18 @@ def gpu_forward(inp, dt=None, plan=None, stream=None):
     import spatial_sparse_attention_amd as ssa
     dev = to_dev(inp, dt)
     if plan is None:
-        plan = ssa.Plan(dev["coords"], inp["grid"], inp["block"], inp["window"])
+        plan = make_plan(inp, dev["coords"])
     out, sel = ssa.forward(plan, dev["q"], dev["k"], dev["v"], dev["wk"], dev["wv"], dev["gates"],
                            inp["topk"], inp.get("scale", 0.0) or 0.0, stream=stream)
     torch.cuda.synchronize()
     return out.double().cpu().numpy(), sel.cpu().numpy().astype(np.int64), plan
+
+
+def make_plan(inp, coords_dev):
+    """The GPU plan of an input dict, its window partition included."""
+    import spatial_sparse_attention_amd as ssa
+    return ssa.Plan(coords_dev, inp["grid"], inp["block"], inp["window"],
+                    shift=inp.get("window_shift", (0, 0, 0)), sfc_tokens=inp.get("sfc_tokens", 0))
 
 
 def check_selection(sigma, k, row):

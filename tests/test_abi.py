@@ -60,9 +60,17 @@ def test_plan_argument_errors(ssa):
     assert L.ssa_plan_create(FAKE, 10, _grid(), 2, 0, ws, size, None, ctypes.byref(h)) == 1
     assert L.ssa_plan_create(FAKE, 10, _grid((8, 0, 8)), 2, 2, ws, size, None, ctypes.byref(h)) == 1
     assert L.ssa_plan_create(None, 10, _grid(), 2, 2, ws, size, None, ctypes.byref(h)) == 1
-    # window cells that are not unions of blocks
-    assert L.ssa_plan_create(FAKE, 10, _grid(), 2, 3, ws, size, None, ctypes.byref(h)) == 2
-    assert L.ssa_plan_create(FAKE, 10, _grid(), 4, 2, ws, size, None, ctypes.byref(h)) == 2
+    # window descriptions (ssa_plan_create_ex): checked before any launch
+    W = ssa.Window
+    ex = lambda win, g=_grid(): L.ssa_plan_create_ex(FAKE, 10, g, 2, ctypes.byref(win), ws, size, None,
+                                                    ctypes.byref(h))
+    assert ex(W(7, 2, (ctypes.c_int32 * 3)(0, 0, 0), 0)) == 1          # unknown kind
+    assert ex(W(0, 0, (ctypes.c_int32 * 3)(0, 0, 0), 0)) == 1          # zero edge
+    assert ex(W(0, 4, (ctypes.c_int32 * 3)(0, -1, 0), 0)) == 1         # negative shift
+    assert ex(W(0, 4, (ctypes.c_int32 * 3)(0, 4, 0), 0)) == 1          # shift >= edge
+    assert ex(W(1, 0, (ctypes.c_int32 * 3)(0, 0, 0), 0)) == 1          # SFC without a window size
+    assert ex(W(1, 0, (ctypes.c_int32 * 3)(0, 0, 0), 8), _grid((2048, 8, 8))) == 2  # Morton codes > 30 bits
+    assert L.ssa_plan_create_ex(FAKE, 10, _grid(), 2, None, ws, size, None, ctypes.byref(h)) == 1
     # workspace missing / too small
     assert L.ssa_plan_create(FAKE, 10, _grid(), 2, 2, None, size, None, ctypes.byref(h)) == 3
     assert L.ssa_plan_create(FAKE, 10, _grid(), 2, 2, ws, size - 1, None, ctypes.byref(h)) == 3
@@ -113,6 +121,19 @@ def test_empty_plan_and_forward_checks(ssa):
     assert L.ssa_backward(*bargs(k=0)) == 1
     assert L.ssa_backward(*bargs(sc=-2.0)) == 1
     assert L.ssa_backward(*((None,) + bargs()[1:])) == 6
+    # several samples: argument checks before any launch
+    plans = (ctypes.c_void_p * 1)(h.value)
+    offs = (ctypes.c_int64 * 2)(0, 0)
+    assert L.ssa_forward_batch_workspace_size(plans, 1, 1, 2, 64, 4) > 0
+    assert L.ssa_forward_batch(None, 1, offs, 1, 2, 64, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4,
+                               ctypes.c_float(0), FAKE, fws, wsz, None) == 1
+    bad = (ctypes.c_int64 * 2)(0, 5)                       # the plan holds 0 tokens
+    assert L.ssa_forward_batch(plans, 1, bad, 1, 2, 64, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4,
+                               ctypes.c_float(0), FAKE, fws, wsz, None) == 1
+    assert L.ssa_forward_batch(plans, 1, offs, 1, 2, 48, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4,
+                               ctypes.c_float(0), FAKE, fws, wsz, None) == 2
+    assert L.ssa_forward_batch(plans, 1, offs, 1, 2, 64, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 4,
+                               ctypes.c_float(0), FAKE, fws, wsz, None) == 0
     L.ssa_plan_destroy(h)
     L.ssa_plan_destroy(None)
 

@@ -289,3 +289,111 @@ def test_dense_full_shape_sampled(name):
     items = sorted({(int(h), b) for b in blocks for h in (0, wl.heads - 1)})
     check_items(inp, out, sel, items)
     assert np.isfinite(out).all()
+
+
+
+# ------------------------------------------------------------------ window partitions of their own
+def _check_window_plan(inp, plan):
+    wp = oracle.window_cells(inp)
+    a = _plan_arrays(plan)
+    assert not plan.cells_are_block_unions and plan.num_wcells == wp.M
+    np.testing.assert_array_equal(a["wperm"], wp.perm)
+    np.testing.assert_array_equal(a["wcell_off"], wp.blk_off)
+    sizes = np.diff(wp.blk_off)
+    np.testing.assert_array_equal(a["wlpt"], np.lexsort((np.arange(wp.M), -sizes)))
+
+
+WINDOWS = [  # (N, G, H, d, B, k, dtype, window options)
+    (1500, 20, 2, 64, 4, 4, "f16", dict(window=2)),                          # w < B
+    (1500, 20, 2, 96, 4, 4, "f16", dict(window=6)),                          # w not a multiple of B
+    (1200, 16, 2, 64, 4, 3, "bf16", dict(window=8, window_shift=(4, 4, 4))),  # shifted windows
+    (1200, 16, 1, 32, 4, 3, "f32", dict(window=3, window_shift=(1, 0, 2))),
+    (1500, 20, 2, 64, 4, 4, "f16", dict(window=4, sfc_tokens=64)),            # Morton-order windows
+    (900, 12, 2, 96, 2, 5, "bf16", dict(window=4, sfc_tokens=37)),
+    (700, 12, 1, 64, 2, 4, "f16", dict(window=4, sfc_tokens=5000)),           # one window: dense
+    (3000, 40, 1, 64, 2, 4, "f16", dict(window=3, window_shift=(2, 1, 0))),   # > 1024 blocks
+]
+
+
+@pytest.mark.parametrize("case", WINDOWS, ids=[f"{c[6]}_d{c[3]}_B{c[4]}_{'_'.join(f'{k}{v}' for k, v in c[7].items())}"
+                                               .replace(' ', '').replace(',', '-') for c in WINDOWS])
+def test_forward_window_partitions(case):
+    N, G, H, d, B, k, dt, win = case
+    rng = np.random.default_rng(N + d + B)
+    c = tiny_case(rng, N, G, H, d)
+    inp = W.random_inputs(c["coords"], H, d, dt, seed=N + 3 * d, grid=G)
+    inp.update(block=B, topk=k, **win)
+    import torch
+    import spatial_sparse_attention_amd as ssa
+    from parity import make_plan
+    plan = make_plan(inp, torch.from_numpy(inp["coords"]).cuda())
+    _check_window_plan(inp, plan)
+    _check_small(inp)
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("win", [dict(window=8, window_shift=(4, 4, 4)), dict(sfc_tokens=512)],
+                         ids=["shifted8", "sfc512"])
+def test_forward_window_partitions_full(win):
+    """The 80k-voxel workload (22 x 96 fp16) with shifted 8^3 windows and with 512-token windows
+    along the Morton order: every output element and selection row."""
+    wl, inp0 = _workload("shells80k", True)
+    inp = dict(inp0)
+    inp.update(win)
+    plan = _check_full(inp)
+    assert not plan.cells_are_block_unions
+
+
+def test_general_windows_refuse_backward():
+    import torch
+    import spatial_sparse_attention_amd as ssa
+    rng = np.random.default_rng(4)
+    c = tiny_case(rng, 600, 12, 2, 64)
+    inp = W.random_inputs(c["coords"], 2, 64, "f16", seed=4, grid=12)
+    inp.update(block=4, window=2, topk=3)
+    dev = to_dev(inp)
+    plan = ssa.Plan(dev["coords"], 12, 4, 2)
+    assert ssa.backward_workspace_size(plan, torch.float16, 2, 64, 3) == 0
+    with pytest.raises(ssa.SSAError) as e:
+        ssa.forward(plan, dev["q"], dev["k"], dev["v"], dev["wk"], dev["wv"], dev["gates"], 3,
+                    save_for_bwd=True)
+    assert e.value.status == 2
+
+
+def test_forward_batch_varlen():
+    """Three samples of different sizes in one ssa_forward_batch call: each equals its own
+    ssa_forward call bit for bit and the oracle on that sample alone."""
+    import torch
+    import spatial_sparse_attention_amd as ssa
+    H, d, dt, k = 2, 64, "f16", 4
+    samples = []
+    for i, (N, G) in enumerate(((1500, 20), (300, 10), (2600, 36))):
+        rng = np.random.default_rng(40 + i)
+        c = tiny_case(rng, N, G, H, d)
+        inp = W.random_inputs(c["coords"], H, d, dt, seed=50 + i, grid=G)
+        inp.update(block=2 if G == 36 else 4, window=4, topk=k)
+        samples.append(inp)
+    wk = samples[0]["wk"]
+    wv = samples[0]["wv"]
+    for s in samples:       # the projection is shared by the batch
+        s["wk"], s["wv"] = wk, wv
+    cat = {x: np.concatenate([s[x] for s in samples]) for x in ("q", "k", "v", "gates")}
+    dev = {x: torch.from_numpy(cat[x]).cuda().half() for x in cat}
+    wkd, wvd = torch.from_numpy(wk).cuda().half(), torch.from_numpy(wv).cuda().half()
+    plans = [ssa.Plan(torch.from_numpy(s["coords"]).cuda(), s["grid"], s["block"], s["window"]) for s in samples]
+    off = np.cumsum([0] + [len(s["coords"]) for s in samples])
+    out = ssa.forward_batch(plans, off, dev["q"], dev["k"], dev["v"], wkd, wvd, dev["gates"], k)
+    torch.cuda.synchronize()
+    out = out.double().cpu().numpy()
+    for i, s in enumerate(samples):
+        o1, s1, _ = gpu_forward(s, plan=plans[i])
+        np.testing.assert_array_equal(out[off[i]:off[i + 1]], o1)
+        ref = oracle.forward(s)
+        near = {}
+        for h in range(H):
+            for b in range(ref["part"].M):
+                if check_selection(ref["sigma"][h, b], k, s1[h, b]) == "near":
+                    near[(h, b)] = s1[h, b]
+        if near:
+            ref = oracle.forward(s, sel_override=near)
+        compare(out[off[i]:off[i + 1]], ref["out"], dt, f"sample {i}")
