@@ -381,6 +381,60 @@ def backward(inp: dict, sel: np.ndarray, dout: np.ndarray, scale=None):
     return dq, dk, dv, dg
 
 
+# --------------------------------------------------------------------------- inputs of SSA
+# The step before the path: the transformer block produces each token's queries, keys,
+# values and gates from its features (the Sparc3D/Hi3D pipeline page, "Stage 3": RMS
+# normalisation of the self-attention queries and keys, rotary position embeddings; the
+# nav.superapi.store page, "Technical principles of Direct3D-S2": predicted gating scores).
+def rms_norm(x, gamma, eps):
+    """x / sqrt(mean(x^2) + eps) * gamma over the last axis."""
+    x = np.asarray(x, np.float64)
+    return x / np.sqrt((x * x).mean(axis=-1, keepdims=True) + eps) * np.asarray(gamma, np.float64)
+
+
+def rope_3d(x, coords, base):
+    """Rotary position embedding from a voxel's three coordinates: the head dimension d is cut
+    into three parts of 2P = 2 floor(d / 6) dimensions (x, y, z axes; the last d - 6P stay as
+    they are); pair i of axis a, dimensions (2Pa + 2i, 2Pa + 2i + 1), is rotated by the angle
+    c_a * base^(-i / P).  x: [N, H, d]; coords: [N, 3]."""
+    x = np.asarray(x, np.float64)
+    c = np.asarray(coords, np.float64)
+    d = x.shape[-1]
+    P = d // 6
+    out = x.copy()
+    for a in range(3):
+        for i in range(P):
+            ang = c[:, a] * base ** (-i / P)                      # [N]
+            cs, sn = np.cos(ang)[:, None], np.sin(ang)[:, None]
+            j = 2 * P * a + 2 * i
+            u, v = x[:, :, j], x[:, :, j + 1]
+            out[:, :, j] = u * cs - v * sn
+            out[:, :, j + 1] = u * sn + v * cs
+    return out
+
+
+def qkv_gates(x, w_qkv, w_gate, b_gate, gamma_q, gamma_k, coords, heads, dim, base=10000.0, eps=1e-6):
+    """Queries, keys, values and gates of every token from its features x [N, C]:
+    y = x W_qkv^T (W_qkv [3 H d, C], output features in the order q | k | v, each head-major);
+    q = rope(rmsnorm(y_q, gamma_q)), k = rope(rmsnorm(y_k, gamma_k)), v = y_v; gates =
+    sigmoid(x W_gate^T + b_gate) with W_gate [3 H, C], feature h * 3 + branch.  Returns
+    float64 q, k, v [N, H, d] and gates [N, H, 3]."""
+    x = np.asarray(x, np.float64)
+    N = x.shape[0]
+    H, d = heads, dim
+    y = x @ np.asarray(w_qkv, np.float64).T
+    yq = y[:, :H * d].reshape(N, H, d)
+    yk = y[:, H * d:2 * H * d].reshape(N, H, d)
+    yv = y[:, 2 * H * d:].reshape(N, H, d)
+    q = rope_3d(rms_norm(yq, gamma_q, eps), coords, base)
+    k = rope_3d(rms_norm(yk, gamma_k, eps), coords, base)
+    z = x @ np.asarray(w_gate, np.float64).T
+    if b_gate is not None:
+        z = z + np.asarray(b_gate, np.float64)
+    gates = (1.0 / (1.0 + np.exp(-z))).reshape(N, H, 3)
+    return q, k, yv, gates
+
+
 # --------------------------------------------------------------------------- textbook
 def sdpa_dense(q, k, v, scale):
     """Textbook dense softmax attention per head via torch's float64 CPU SDPA (a library
