@@ -280,6 +280,36 @@ def window_variant_timing(r, label, window=None, reps=10, **plan_kw):
             "mfma_peak_frac": tf / r.peak}
 
 
+def producer_timing(r, channels=2112, reps=5):
+    """The step before SSA at the workload's shape (width 2,112 = 22 x 96 on the Hi3D page's
+    Stage 3): q, k, v and gates from token features (ssa_qkv_gates: projections on MFMA, RMS
+    norm and 3D rotary embedding of q and k, sigmoid gates).  Credited 2 N C (3 H d + 3 H)
+    FLOPs."""
+    torch, ssa, wl = r.torch, r.ssa, r.wl
+    N, H, d = r.N, r.H, r.d
+    import workloads as W
+    pin = W.producer_inputs(N, channels, H, d, wl.dtype, seed=11)
+    dev = {k: torch.from_numpy(np.ascontiguousarray(v)).cuda().to(r.tdt) for k, v in pin.items()}
+    out = (torch.empty_like(r.dev["q"]), torch.empty_like(r.dev["q"]), torch.empty_like(r.dev["q"]),
+           torch.empty_like(r.dev["gates"]))
+    run = lambda: ssa.qkv_gates(dev["x"], dev["w_qkv"], dev["w_gate"], dev["b_gate"], dev["gamma_q"],
+                                dev["gamma_k"], r.coords, H, d, out=out)
+    run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(r.stream)
+    for _ in range(reps):
+        run()
+    e1.record(r.stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    flops = 2.0 * N * channels * (3 * H * d + 3 * H)
+    tf = flops / (ms * 1e-3) / 1e12
+    return {"what": f"k_qkv_gates: x [{N},{channels}] -> q, k, v [{N},{H},{d}], gates [{N},{H},3]",
+            "ms": ms, "reps": reps, "credited_flops": flops, "tflops": tf, "mfma_peak": r.peak,
+            "mfma_peak_frac": tf / r.peak}
+
+
 def backward_timing(r, reps=5):
     """Forward with saved state, then the backward (fixed selection, the workload's dO), timed
     apart from the step: HIP events around `reps` backward calls.  Credited 10 d FLOPs per
@@ -412,6 +442,9 @@ def main():
             "sfc512": window_variant_timing(r, "windows of 512 tokens along the Morton order", sfc_tokens=512),
             "cube4": window_variant_timing(r, "4^3 cells (smaller than the 8^3 blocks)", window=4),
         }
+    if not args.no_full and wl.name == WORKLOAD and wl.dtype != "f32":
+        progress("producer")
+        res["producer"] = producer_timing(r)
     inp0 = r.inp
     del r
     torch.cuda.empty_cache()

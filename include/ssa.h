@@ -246,6 +246,29 @@ ssa_status ssa_backward(ssa_plan plan, ssa_dtype dtype, int32_t heads, int32_t d
                         float* dgates, const void* fwd_ws, size_t fwd_ws_bytes, void* ws,
                         size_t ws_bytes, hipStream_t stream);
 
+/*
+ * The step before SSA: each token's queries, keys, values and gates from its features
+ * (Hi3D pipeline page, "Stage 3": RMS normalisation of the self-attention queries and keys,
+ * rotary position embeddings; nav.superapi.store "Direct3D-S2", "Technical principles of
+ * Direct3D-S2": predicted gating scores), in one kernel:
+ *   y = x W_qkv^T, W_qkv [3*H*d, C] (linear-layer layout; output features q | k | v, each
+ *       head-major), x [N, C];
+ *   q = rope(rmsnorm(y_q) * gamma_q), k = rope(rmsnorm(y_k) * gamma_k), v = y_v   [N,H,d];
+ *       rmsnorm over each head's d features with eps (0 means 1e-6); rope rotates features
+ *       (2Pa + 2i, 2Pa + 2i + 1), P = floor(d / 6), of axis a by coords[n][a] * base^(-i / P)
+ *       (rope_base 0 means 10000); features past 6P are not rotated;
+ *   gates = sigmoid(x W_gate^T + b_gate), W_gate [3*H, C], b_gate [3*H] or NULL;
+ *       layout [N, H, 3] (feature h * 3 + branch: compressed, selected, window).
+ * dtype F16 or BF16 (F32 returns SSA_ERR_UNSUPPORTED); d in {32, 64, 96, 128}; C a multiple
+ * of 8.  gamma_q, gamma_k [d]; coords int32 [N,3].  All device pointers; fp32 accumulation;
+ * outputs in the dtype.  Asynchronous on `stream`; allocates nothing.
+ */
+ssa_status ssa_qkv_gates(ssa_dtype dtype, int64_t n, int32_t channels, int32_t heads, int32_t dim,
+                         const void* x, const void* w_qkv, const void* w_gate, const void* b_gate,
+                         const void* gamma_q, const void* gamma_k, const int32_t* coords,
+                         float rope_base, float eps, void* q, void* k, void* v, void* gates,
+                         hipStream_t stream);
+
 const char* ssa_status_string(ssa_status status);
 
 #ifdef __cplusplus

@@ -13,7 +13,7 @@ import os
 
 import torch
 
-__all__ = ["Plan", "Window", "forward", "forward_batch", "forward_workspace_size", "forward_noalloc", "backward",
+__all__ = ["Plan", "Window", "qkv_gates", "forward", "forward_batch", "forward_workspace_size", "forward_noalloc", "backward",
            "backward_workspace_size", "NOALLOC_SCRATCH_BYTES",
            "SSAError", "lib", "LIB_PATH", "STAGE_POOL", "STAGE_SELECT", "STAGE_ATTEND", "STAGE_ALL"]
 
@@ -84,6 +84,9 @@ def _load():
     L.ssa_backward.argtypes = [_vp, ctypes.c_int, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _i32,
                                ctypes.c_float, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp, _sz, _vp]
     L.ssa_backward.restype = ctypes.c_int
+    L.ssa_qkv_gates.argtypes = [ctypes.c_int, _i64, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                ctypes.c_float, ctypes.c_float, _vp, _vp, _vp, _vp, _vp]
+    L.ssa_qkv_gates.restype = ctypes.c_int
     L.ssa_status_string.argtypes = [ctypes.c_int]
     L.ssa_status_string.restype = ctypes.c_char_p
     return L
@@ -293,6 +296,34 @@ def forward_batch(plans, tok_off, q, k, v, wk, wv, gates, topk: int, scale: floa
                                ws.numel(), _stream(stream))
     _check(st, "ssa_forward_batch")
     return out
+
+
+def qkv_gates(x, w_qkv, w_gate, b_gate, gamma_q, gamma_k, coords, heads: int, dim: int,
+              rope_base: float = 0.0, eps: float = 0.0, out=None, stream=None):
+    """ssa_qkv_gates: q, k, v [N,H,d] and gates [N,H,3] from token features x [N,C] (one dtype,
+    f16 or bf16; W in linear-layer layout [out, C]; b_gate may be None).  Returns (q, k, v, gates)."""
+    N, C = x.shape
+    H, d = heads, dim
+    for t in (x, w_qkv, w_gate, gamma_q, gamma_k) + ((b_gate,) if b_gate is not None else ()):
+        if t.dtype != x.dtype or not t.is_contiguous() or t.device != x.device:
+            raise ValueError("all tensors must be contiguous, on one device, with one dtype")
+    if w_qkv.shape != (3 * H * d, C) or w_gate.shape != (3 * H, C) or gamma_q.shape != (d,) \
+            or gamma_k.shape != (d,) or coords.shape != (N, 3) or coords.dtype != torch.int32 \
+            or (b_gate is not None and b_gate.shape != (3 * H,)):
+        raise ValueError("shape mismatch")
+    _uses(stream, x, w_qkv, w_gate, b_gate, gamma_q, gamma_k, coords)
+    with _alloc_on(stream):
+        if out is None:
+            out = (torch.empty((N, H, d), dtype=x.dtype, device=x.device),
+                   torch.empty((N, H, d), dtype=x.dtype, device=x.device),
+                   torch.empty((N, H, d), dtype=x.dtype, device=x.device),
+                   torch.empty((N, H, 3), dtype=x.dtype, device=x.device))
+    q, k, v, g = out
+    st = lib.ssa_qkv_gates(_DTYPES[x.dtype], N, C, H, d, _ptr(x), _ptr(w_qkv), _ptr(w_gate), _ptr(b_gate),
+                           _ptr(gamma_q), _ptr(gamma_k), _ptr(coords), float(rope_base), float(eps),
+                           _ptr(q), _ptr(k), _ptr(v), _ptr(g), _stream(stream))
+    _check(st, "ssa_qkv_gates")
+    return q, k, v, g
 
 
 def backward_workspace_size(plan: Plan, dtype, heads: int, dim: int, topk: int) -> int:

@@ -138,6 +138,25 @@ def test_empty_plan_and_forward_checks(ssa):
     L.ssa_plan_destroy(None)
 
 
+def test_qkv_gates_argument_errors(ssa):
+    L = ssa.lib
+    f = ctypes.c_float
+    args = lambda dt=1, n=10, C=64, d=96: (dt, n, C, 2, d, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, f(0), f(0),
+                                           FAKE, FAKE, FAKE, FAKE, None)
+    assert L.ssa_qkv_gates(*args(n=0)) == 0           # nothing to do
+    assert L.ssa_qkv_gates(*args(dt=0)) == 2          # f32
+    assert L.ssa_qkv_gates(*args(dt=5)) == 1
+    assert L.ssa_qkv_gates(*args(d=48)) == 2
+    assert L.ssa_qkv_gates(*args(C=60)) == 2          # rows not 16-byte aligned
+    assert L.ssa_qkv_gates(*args(C=0)) == 1
+    bad = list(args())
+    bad[5] = None
+    assert L.ssa_qkv_gates(*bad) == 1                 # no features
+    bad = list(args())
+    bad[12] = f(-1.0)
+    assert L.ssa_qkv_gates(*bad) == 1                 # negative rotary base
+
+
 def test_workspace_sizes_monotone(ssa):
     L = ssa.lib
     a = L.ssa_plan_workspace_size(1000, _grid(), 2, 2)

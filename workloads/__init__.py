@@ -23,7 +23,7 @@ import math
 import numpy as np
 
 __all__ = ["Workload", "WORKLOADS", "make_inputs", "make_geometry", "round_to_dtype",
-           "random_inputs"]
+           "random_inputs", "producer_inputs"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -178,3 +178,21 @@ def make_inputs(name_or_wl, distinct_w: bool = False) -> tuple[Workload, dict]:
                         distinct_w=distinct_w)
     inp.update(block=wl.block, window=wl.window, topk=wl.topk)
     return wl, inp
+
+
+def producer_inputs(n: int, channels: int, heads: int, dim: int, dtype: str, seed: int,
+                    bias: bool = True) -> dict:
+    """Token features and weights of the step that produces SSA's inputs: x ~ N(0,1) [N,C];
+    W_qkv ~ N(0, 1/C) [3 H d, C] and W_gate ~ N(0, 1/C) [3 H, C] (linear-layer layout);
+    b_gate ~ N(0, 1/4) [3 H] (or None); gamma_q, gamma_k ~ 1 + N(0, 0.1^2) [d]."""
+    ss = np.random.SeedSequence([seed, 7])
+    r = [np.random.default_rng(x) for x in ss.spawn(6)]
+    sd = 1.0 / math.sqrt(channels)
+    return {
+        "x": round_to_dtype(r[0].standard_normal((n, channels)), dtype),
+        "w_qkv": round_to_dtype(r[1].standard_normal((3 * heads * dim, channels)) * sd, dtype),
+        "w_gate": round_to_dtype(r[2].standard_normal((3 * heads, channels)) * sd, dtype),
+        "b_gate": round_to_dtype(r[3].standard_normal(3 * heads) * 0.5, dtype) if bias else None,
+        "gamma_q": round_to_dtype(1.0 + 0.1 * r[4].standard_normal(dim), dtype),
+        "gamma_k": round_to_dtype(1.0 + 0.1 * r[5].standard_normal(dim), dtype),
+    }
