@@ -871,7 +871,7 @@ __device__ inline int wave_incl_scan(int x, int lane) {
 // buffers without a break; at the boundary tile the selected branch is closed (its gated
 // output kept in registers) and the window branch starts.  Otherwise each set is streamed on
 // its own (gathered_branch).
-template <int DT, int D, bool BUF>
+template <int DT, int D, bool BUF, int MODE>
 __global__ __launch_bounds__(64 * ATT_WAVES) __attribute__((amdgpu_waves_per_eu(D <= 96 ? 2 : 1))) void k_attend(
     const typename Tr<DT>::T* __restrict__ q, const typename Tr<DT>::T* __restrict__ kin,
     const typename Tr<DT>::T* __restrict__ vin, const typename Tr<DT>::T* __restrict__ gates,
@@ -880,8 +880,9 @@ __global__ __launch_bounds__(64 * ATT_WAVES) __attribute__((amdgpu_waves_per_eu(
     const int32_t* __restrict__ cell_blk, const int32_t* __restrict__ lpt,
     const int32_t* __restrict__ sel, const typename Tr<DT>::T* __restrict__ oc, int M, int H,
     int nchunk, int64_t N, int topk, float sl2, int window_is_block, typename Tr<DT>::T* __restrict__ out,
-    float* __restrict__ lse_save, float* __restrict__ os_save, float* __restrict__ ow_save, int mode,
+    float* __restrict__ lse_save, float* __restrict__ os_save, float* __restrict__ ow_save,
     const typename Tr<DT>::T* __restrict__ ow_in) {
+  constexpr int mode = MODE;
   using C = Cfg<DT, D>;
   using T = typename Tr<DT>::T;
   using F = typename Tr<DT>::frag;
@@ -934,7 +935,7 @@ __global__ __launch_bounds__(64 * ATT_WAVES) __attribute__((amdgpu_waves_per_eu(
   typedef unsigned ocv_t __attribute__((ext_vector_type(2)));
   constexpr bool OCPRE = sizeof(T) == 2 && (BUF || D <= 64);  // register budget
   ocv_t ocv[OCPRE ? C::NDV * 4 : 1];
-  if constexpr (OCPRE) if (mode != ATT_WINDOW) {
+  if constexpr (OCPRE && MODE != ATT_WINDOW) {
     const T* orow0 = oc + ((int64_t)(r0 + (valid ? my_row : 0)) * H + h) * D + 4 * g;
 #pragma unroll
     for (int j = 0; j < C::NDV; ++j)
@@ -1186,11 +1187,13 @@ hipError_t run_attend(const ssa_plan_s* p, int H, int topk, float sl2, const voi
     float* lse = mode == ATT_BOTH ? w.lse : nullptr;
     float* os = mode == ATT_BOTH && w.obr ? w.obr + p->n * H * D : nullptr;
     float* ows = mode == ATT_BOTH && w.obr ? w.obr + 2 * p->n * H * D : nullptr;
-    auto kern = buf ? k_attend<DT, D, true> : k_attend<DT, D, false>;
+    auto kern = mode == ATT_BOTH ? (buf ? k_attend<DT, D, true, ATT_BOTH> : k_attend<DT, D, false, ATT_BOTH>)
+              : mode == ATT_WINDOW ? (buf ? k_attend<DT, D, true, ATT_WINDOW> : k_attend<DT, D, false, ATT_WINDOW>)
+                                   : (buf ? k_attend<DT, D, true, ATT_SELECTED> : k_attend<DT, D, false, ATT_SELECTED>);
     hipLaunchKernelGGL(kern, dim3(xcd_grid(units, (int64_t)H * nchunk)), dim3(64 * ATT_WAVES), 0, s,
                        (const T*)q, (const T*)k, (const T*)v, (const T*)gates, perm, off, p->blk_cell,
                        p->cell_off, p->cell_blk, lpt, sel, (const T*)w.oc, (int)units, H, nchunk, p->n,
-                       topk, sl2, wib, dst, lse, os, ows, mode, (const T*)w.ow);
+                       topk, sl2, wib, dst, lse, os, ows, (const T*)w.ow);
   };
   if (p->wkind == 0) {
     launch(ATT_BOTH, p->M, p->perm, p->blk_off, p->lpt, p->max_rows, (int)p->window_is_block, (T*)out);
