@@ -58,6 +58,9 @@ def _head_inputs(h):
     inp["coords"] = np.asarray(a["coords"])
     inp["wk"] = np.asarray(a["wk"])
     inp["wv"] = np.asarray(a["wv"])
+    for nm in ("wk_conv", "wv_conv"):
+        if nm in a:
+            inp[nm] = np.asarray(a[nm])
     return inp
 
 
@@ -75,6 +78,9 @@ class HeadPool:
         names = []
         arrays = {k: inp[k] for k in _TOKEN_ARRAYS if k in inp}
         arrays.update(coords=inp["coords"], wk=inp["wk"], wv=inp["wv"])
+        for nm in ("wk_conv", "wv_conv"):
+            if inp.get(nm) is not None:
+                arrays[nm] = inp[nm]
         arrays.update(shared or {})
         for nm, arr in arrays.items():
             np.save(os.path.join(self.dir, nm + ".npy"), np.ascontiguousarray(arr))

@@ -115,6 +115,47 @@ def pool(k: np.ndarray, v: np.ndarray, wk: np.ndarray, wv: np.ndarray, part: Par
     return ktil, vtil
 
 
+def block_offsets(coords, edge: int) -> np.ndarray:
+    """Position of each voxel inside its block: (c mod B) per axis, as the x-major index
+    (o_x * B + o_y) * B + o_z in [0, B^3)."""
+    o = np.asarray(coords, dtype=np.int64) % edge
+    return (o[:, 0] * edge + o[:, 1]) * edge + o[:, 2]
+
+
+def pool_conv(k, v, wck, wcv, part: Partition, coords):
+    """Compressed keys/values by a sparse 3D convolution then pooling (nav.superapi.store,
+    "Technical principles of Direct3D-S2": block-level information through sparse 3D
+    convolution and pooling).  Reading: a convolution with kernel size and stride B over the
+    occupied voxels, so every block is one output site and every voxel's weight depends on its
+    position inside the block, followed by the mean over the block's occupied voxels:
+    ktil[h, b] = (1/n_b) sum_{i in b} k[i, h] @ Wc_k[o(i)]^T with Wc [B^3, d_out, d_in] (each
+    position a linear-layer matrix).  Returns (ktil, vtil), each [H, M, d]."""
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    wck = np.asarray(wck, dtype=np.float64)
+    wcv = np.asarray(wcv, dtype=np.float64)
+    H, d = k.shape[1], k.shape[2]
+    off = block_offsets(coords, part.edge)
+    ktil = np.zeros((H, part.M, d))
+    vtil = np.zeros((H, part.M, d))
+    for b in range(part.M):
+        t = part.tokens(b)
+        for i in t:
+            ktil[:, b] += k[i] @ wck[off[i]].T
+            vtil[:, b] += v[i] @ wcv[off[i]].T
+        ktil[:, b] /= len(t)
+        vtil[:, b] /= len(t)
+    return ktil, vtil
+
+
+def compress(inp: dict, k, v, part: Partition):
+    """The compression module an input dict asks for: the sparse-convolution compressor when
+    it carries "wk_conv", "wv_conv" [B^3, d, d], else mean-pool + linear map (wk, wv)."""
+    if inp.get("wk_conv") is not None:
+        return pool_conv(k, v, inp["wk_conv"], inp["wv_conv"], part, inp["coords"])
+    return pool(k, v, inp["wk"], inp["wv"], part)
+
+
 def _softmax_rows(s: np.ndarray) -> np.ndarray:
     s = s - s.max(axis=1, keepdims=True)
     e = np.exp(s)
@@ -247,7 +288,7 @@ def forward_items(inp: dict, items, sel_override=None, scale=None, ktv=None):
     part = partition(inp["coords"], inp["block"], inp["grid"])
     wpart = window_cells(inp)
     if ktv is None:
-        ktil, vtil = pool(k, v, inp["wk"], inp["wv"], part)
+        ktil, vtil = compress(inp, k, v, part)
     else:
         ktil, vtil = ktv
     g = np.asarray(inp["gates"], np.float64)
@@ -334,7 +375,12 @@ def backward(inp: dict, sel: np.ndarray, dout: np.ndarray, scale=None):
     sc = _scale(scale, d)
     part = partition(inp["coords"], inp["block"], inp["grid"])
     wpart = window_cells(inp)
-    ktil, vtil = pool(k, v, wk, wv, part)
+    ktil, vtil = compress(inp, k, v, part)
+    conv = inp.get("wk_conv") is not None
+    if conv:
+        off = block_offsets(inp["coords"], inp["block"])
+        wck = np.asarray(inp["wk_conv"], np.float64)
+        wcv = np.asarray(inp["wv_conv"], np.float64)
     dq = np.zeros((N, H, d))
     dk = np.zeros((N, H, d))
     dv = np.zeros((N, H, d))
@@ -376,8 +422,13 @@ def backward(inp: dict, sel: np.ndarray, dout: np.ndarray, scale=None):
     for b in range(part.M):
         t = part.tokens(b)
         n = len(t)
-        dk[t] += (dktil[:, b] @ wk.T)[None] / n
-        dv[t] += (dvtil[:, b] @ wv.T)[None] / n
+        if conv:  # each voxel's own position weight
+            for i in t:
+                dk[i] += dktil[:, b] @ wck[off[i]] / n
+                dv[i] += dvtil[:, b] @ wcv[off[i]] / n
+        else:
+            dk[t] += (dktil[:, b] @ wk.T)[None] / n
+            dv[t] += (dvtil[:, b] @ wv.T)[None] / n
     return dq, dk, dv, dg
 
 

@@ -199,7 +199,7 @@ def check_forward_all(inp, out_gpu, sel_gpu, heads=None, workers=None):
     in a process pool (one task per (head, run of blocks)).  Returns (counts, max_abs, rel)."""
     from oracle.parallel import HeadPool, workers_available
     part = oracle.partition(inp["coords"], inp["block"], inp["grid"])
-    ktil, vtil = oracle.pool(inp["k"], inp["v"], inp["wk"], inp["wv"], part)
+    ktil, vtil = oracle.compress(inp, inp["k"], inp["v"], part)
     N, H, d = inp["q"].shape
     heads = list(range(H)) if heads is None else list(heads)
     nw = workers or workers_available()
