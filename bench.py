@@ -280,6 +280,33 @@ def window_variant_timing(r, label, window=None, reps=10, **plan_kw):
             "mfma_peak_frac": tf / r.peak}
 
 
+def conv_timing(r, reps=10):
+    """The forward with the sparse-convolution compressor (B^3 position weights per K and V):
+    HIP events around `reps` calls of all stages; credited as the mean-pool forward (the
+    attention pairs do not change) plus 4 N H d^2 FLOPs of position-weight products."""
+    torch, ssa, wl = r.torch, r.ssa, r.wl
+    N, H, d = r.N, r.H, r.d
+    import workloads as W
+    wkc, wvc = W.conv_weights(wl.block, d, wl.dtype, seed=7)
+    wkc, wvc = torch.from_numpy(wkc).cuda().to(r.tdt), torch.from_numpy(wvc).cuda().to(r.tdt)
+    dv = r.dev
+    run = lambda: ssa.forward(r.plan, dv["q"], dv["k"], dv["v"], wkc, wvc, dv["gates"], wl.topk, 0.0, out=r.out,
+                              sel_out=r.sel, ws=r.ws)
+    run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(r.stream)
+    for _ in range(reps):
+        run()
+    e1.record(r.stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    flops = r.work()[0] + 4.0 * N * H * d * d
+    tf = flops / (ms * 1e-3) / 1e12
+    return {"what": f"forward with the sparse-convolution compressor ({wl.block}^3 position weights)",
+            "forward_ms": ms, "reps": reps, "credited_flops": flops, "tflops": tf, "mfma_peak_frac": tf / r.peak}
+
+
 def producer_timing(r, channels=2112, reps=5):
     """The step before SSA at the workload's shape (width 2,112 = 22 x 96 on the Hi3D page's
     Stage 3): q, k, v and gates from token features (ssa_qkv_gates: projections on MFMA, RMS
@@ -445,6 +472,8 @@ def main():
     if not args.no_full and wl.name == WORKLOAD and wl.dtype != "f32":
         progress("producer")
         res["producer"] = producer_timing(r)
+        progress("convolution compressor")
+        res["conv_compressor"] = conv_timing(r)
     inp0 = r.inp
     del r
     torch.cuda.empty_cache()

@@ -183,6 +183,32 @@ ssa_status ssa_forward_stages(ssa_plan plan, ssa_dtype dtype, int32_t heads, int
                               int save_for_bwd, hipStream_t stream, uint32_t stages);
 
 /*
+ * SSA forward and backward with the sparse-convolution compressor (nav.superapi.store
+ * "Direct3D-S2", "Technical principles of Direct3D-S2": block-level information by sparse 3D
+ * convolution and pooling).  A convolution with kernel size and stride B over the occupied
+ * voxels -- every block one output site, every voxel weighted by its position inside the
+ * block -- then the mean over the block's occupied voxels:
+ *   ktil[h,b] = (1/n_b) sum_{i in b} k[i,h] Wc_k[o(i)]^T,   vtil likewise with Wc_v,
+ * o(i) = ((c_x mod B) * B + (c_y mod B)) * B + (c_z mod B).  wk_conv, wv_conv: [B^3][d][d],
+ * each position's matrix in linear-layer layout [d_out][d_in].  Every other argument and
+ * result as ssa_forward / ssa_backward (the workspace sizes are the same queries); with
+ * uniform position weights Wc[o] = W^T the results equal those of ssa_forward.  The backward
+ * must be ssa_backward_conv on a workspace saved by ssa_forward_conv (and ssa_backward on one
+ * saved by ssa_forward), else SSA_ERR_INVALID_ARG for the plan's 16 most recent forwards.
+ */
+ssa_status ssa_forward_conv(ssa_plan plan, ssa_dtype dtype, int32_t heads, int32_t dim,
+                            const void* q, const void* k, const void* v, const void* wk_conv,
+                            const void* wv_conv, const void* gates, int32_t topk, float scale,
+                            void* out, int32_t* sel_out, void* ws, size_t ws_bytes,
+                            int save_for_bwd, hipStream_t stream);
+ssa_status ssa_backward_conv(ssa_plan plan, ssa_dtype dtype, int32_t heads, int32_t dim,
+                             const void* q, const void* k, const void* v, const void* wk_conv,
+                             const void* wv_conv, const void* gates, int32_t topk, float scale,
+                             const int32_t* sel, const void* dout, float* dq, float* dk, float* dv,
+                             float* dgates, const void* fwd_ws, size_t fwd_ws_bytes, void* ws,
+                             size_t ws_bytes, hipStream_t stream);
+
+/*
  * For callers that cannot allocate device memory (code under HIP graph capture, tight
  * serving loops, harnesses that forbid allocation): ssa_forward without a workspace
  * argument.  The workspace is a fixed array of SSA_NOALLOC_SCRATCH_BYTES (64 MiB) in

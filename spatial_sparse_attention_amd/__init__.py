@@ -71,6 +71,8 @@ def _load():
     L.ssa_forward.restype = ctypes.c_int
     L.ssa_forward_stages.argtypes = fwd + [ctypes.c_uint32]
     L.ssa_forward_stages.restype = ctypes.c_int
+    L.ssa_forward_conv.argtypes = fwd
+    L.ssa_forward_conv.restype = ctypes.c_int
     L.ssa_forward_noalloc.argtypes = [_vp, ctypes.c_int, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp,
                                       _i32, ctypes.c_float, _vp, _vp, _vp]
     L.ssa_forward_noalloc.restype = ctypes.c_int
@@ -84,6 +86,8 @@ def _load():
     L.ssa_backward.argtypes = [_vp, ctypes.c_int, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _i32,
                                ctypes.c_float, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp, _sz, _vp]
     L.ssa_backward.restype = ctypes.c_int
+    L.ssa_backward_conv.argtypes = L.ssa_backward.argtypes
+    L.ssa_backward_conv.restype = ctypes.c_int
     L.ssa_qkv_gates.argtypes = [ctypes.c_int, _i64, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                 ctypes.c_float, ctypes.c_float, _vp, _vp, _vp, _vp, _vp]
     L.ssa_qkv_gates.restype = ctypes.c_int
@@ -215,8 +219,10 @@ def _check_qkv(plan, q, k, v, wk, wv, gates):
         if t.dtype != q.dtype or not t.is_contiguous() or t.device != q.device:
             raise ValueError("all tensors must be contiguous, on one device, with one dtype")
     N, H, d = q.shape
+    # W [d,d] (mean pool + linear map), or [B^3,d,d] position weights (sparse convolution)
+    wshape = (d, d) if wk.dim() == 2 else (plan.block ** 3, d, d)
     if N != plan.n or k.shape != q.shape or v.shape != q.shape or gates.shape != (N, H, 3) \
-            or wk.shape != (d, d) or wv.shape != (d, d):
+            or wk.shape != wshape or wv.shape != wshape:
         raise ValueError("shape mismatch")
     return N, H, d
 
@@ -224,7 +230,8 @@ def _check_qkv(plan, q, k, v, wk, wv, gates):
 def forward(plan: Plan, q, k, v, wk, wv, gates, topk: int, scale: float = 0.0, out=None,
             sel_out=None, ws=None, stream=None, stages: int = STAGE_ALL, want_sel: bool = True,
             save_for_bwd: bool = False):
-    """SSA forward (ssa_forward_stages).  q,k,v [N,H,d], gates [N,H,3], wk,wv [d,d], one dtype.
+    """SSA forward (ssa_forward_stages).  q,k,v [N,H,d], gates [N,H,3], wk,wv [d,d], one dtype;
+    wk, wv of shape [B^3,d,d] select the sparse-convolution compressor (ssa_forward_conv).
     Returns (out [N,H,d], sel [H,M,topk] int32 or None).  With save_for_bwd, `ws` must be
     kept and passed to backward()."""
     N, H, d = _check_qkv(plan, q, k, v, wk, wv, gates)
@@ -241,10 +248,14 @@ def forward(plan: Plan, q, k, v, wk, wv, gates, topk: int, scale: float = 0.0, o
                                   device=q.device)
         if ws is None or ws.numel() < size:
             ws = torch.empty(size, dtype=torch.uint8, device=q.device)
-    st = lib.ssa_forward_stages(plan.handle, dt, H, d, _ptr(q), _ptr(k), _ptr(v), _ptr(wk),
-                                _ptr(wv), _ptr(gates), int(topk), float(scale), _ptr(out),
-                                _ptr(sel_out), _ptr(ws), ws.numel(), int(save_for_bwd),
-                                _stream(stream), int(stages))
+    args = (plan.handle, dt, H, d, _ptr(q), _ptr(k), _ptr(v), _ptr(wk), _ptr(wv), _ptr(gates), int(topk),
+            float(scale), _ptr(out), _ptr(sel_out), _ptr(ws), ws.numel(), int(save_for_bwd), _stream(stream))
+    if wk.dim() == 3:       # the sparse-convolution compressor (all stages)
+        if stages != STAGE_ALL:
+            raise ValueError("the sparse-convolution forward runs all stages")
+        st = lib.ssa_forward_conv(*args)
+    else:
+        st = lib.ssa_forward_stages(*args, int(stages))
     _check(st, "ssa_forward")
     return out, sel_out
 
@@ -352,7 +363,8 @@ def backward(plan: Plan, q, k, v, wk, wv, gates, topk: int, sel, dout, fwd_ws, s
         dg = torch.empty((N, H, 3), **f32)
         if ws is None or ws.numel() < size:
             ws = torch.empty(size, dtype=torch.uint8, device=q.device)
-    st = lib.ssa_backward(plan.handle, dt, H, d, _ptr(q), _ptr(k), _ptr(v), _ptr(wk), _ptr(wv),
+    fn = lib.ssa_backward_conv if wk.dim() == 3 else lib.ssa_backward
+    st = fn(plan.handle, dt, H, d, _ptr(q), _ptr(k), _ptr(v), _ptr(wk), _ptr(wv),
                           _ptr(gates), int(topk), float(scale), _ptr(sel), _ptr(dout), _ptr(dq),
                           _ptr(dk), _ptr(dv), _ptr(dg), _ptr(fwd_ws), fwd_ws.numel(), _ptr(ws),
                           ws.numel(), _stream(stream))

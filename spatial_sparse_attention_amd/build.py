@@ -8,7 +8,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libssa.so")
-SOURCES = ["ssa_plan.hip", "ssa_forward.hip", "ssa_backward.hip", "ssa_api.hip", "ssa_producer.hip"]
+SOURCES = ["ssa_plan.hip", "ssa_forward.hip", "ssa_backward.hip", "ssa_api.hip", "ssa_producer.hip", "ssa_conv.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

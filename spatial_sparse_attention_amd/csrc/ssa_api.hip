@@ -21,20 +21,20 @@ ssa_status check_common(ssa_plan p, ssa_dtype dt, int32_t H, int32_t d, int32_t 
 }
 // The saved log-sum-exp values of a forward hold its scale: remember it per workspace so
 // that a backward with another scale is refused instead of returning wrong gradients.
-void record_forward(ssa_plan_s* p, const void* ws, float scale) {
+void record_forward(ssa_plan_s* p, const void* ws, float scale, int conv) {
   std::lock_guard<std::mutex> lk(p->rec_mu);
   for (auto& r : p->rec)
-    if (r.ws == ws) { r.scale = scale; return; }
-  p->rec[p->rec_next] = {ws, scale};
+    if (r.ws == ws) { r.scale = scale; r.conv = conv; return; }
+  p->rec[p->rec_next] = {ws, scale, conv};
   p->rec_next = (p->rec_next + 1) % ssa_plan_s::NREC;
 }
 
-// True unless this plan's record of a saving forward on fwd_ws holds a different scale
-// (a workspace the record no longer holds, after NREC later ones, is not checked).
-bool recorded_scale_matches(ssa_plan_s* p, const void* fwd_ws, float scale) {
+// True unless this plan's record of a saving forward on fwd_ws holds a different scale or
+// compressor (a workspace the record no longer holds, after NREC later ones, is not checked).
+bool recorded_forward_matches(ssa_plan_s* p, const void* fwd_ws, float scale, int conv) {
   std::lock_guard<std::mutex> lk(p->rec_mu);
   for (const auto& r : p->rec)
-    if (r.ws == fwd_ws) return r.scale == scale;
+    if (r.ws == fwd_ws) return r.scale == scale && r.conv == conv;
   return true;
 }
 }  // namespace
@@ -69,12 +69,10 @@ extern "C" size_t ssa_forward_workspace_size(ssa_plan p, ssa_dtype dt, int32_t H
   return fwd_carve(c, p, dt, H, d, topk, save_for_bwd ? 1 : 0, nullptr) + 256;
 }
 
-extern "C" ssa_status ssa_forward_stages(ssa_plan p, ssa_dtype dt, int32_t H, int32_t d,
-                                         const void* q, const void* k, const void* v,
-                                         const void* wk, const void* wv, const void* gates,
-                                         int32_t topk, float scale, void* out, int32_t* sel_out,
-                                         void* ws, size_t ws_bytes, int save_for_bwd,
-                                         hipStream_t stream, uint32_t stages) {
+static ssa_status forward_impl(ssa_plan p, ssa_dtype dt, int32_t H, int32_t d, const void* q, const void* k,
+                               const void* v, const void* wk, const void* wv, const void* gates, int32_t topk,
+                               float scale, void* out, int32_t* sel_out, void* ws, size_t ws_bytes,
+                               int save_for_bwd, hipStream_t stream, uint32_t stages, int conv) {
   ssa_status st = check_common(p, dt, H, d, topk);
   if (st != SSA_OK) return st;
   if (stages == 0 || (stages & ~7u)) return SSA_ERR_INVALID_ARG;
@@ -93,15 +91,37 @@ extern "C" ssa_status ssa_forward_stages(ssa_plan p, ssa_dtype dt, int32_t H, in
   FwdWs w;
   if (ws_bytes < fwd_carve(c, p, dt, H, d, topk, save, &w)) return SSA_ERR_WORKSPACE;
   int32_t* sel = sel_out ? sel_out : w.sel;
-  if (save && (stages & SSA_STAGE_SELECT)) record_forward(p, ws, scale);
-  if (stages & SSA_STAGE_POOL)
-    if (launch_pool(dt, p, H, d, k, v, wk, wv, w, stream) != hipSuccess) return SSA_ERR_HIP;
+  if (save && (stages & SSA_STAGE_SELECT)) record_forward(p, ws, scale, conv);
+  if (stages & SSA_STAGE_POOL) {
+    const hipError_t e = conv ? launch_pool_conv(dt, p, H, d, k, v, wk, wv, w, stream)
+                              : launch_pool(dt, p, H, d, k, v, wk, wv, w, stream);
+    if (e != hipSuccess) return SSA_ERR_HIP;
+  }
   if (stages & SSA_STAGE_SELECT)
     if (launch_select(dt, p, H, d, topk, scale, q, w, sel, stream) != hipSuccess) return SSA_ERR_HIP;
   if (stages & SSA_STAGE_ATTEND)
     if (launch_attend(dt, p, H, d, topk, scale, q, k, v, gates, w, sel, out, stream) != hipSuccess)
       return SSA_ERR_HIP;
   return SSA_OK;
+}
+
+extern "C" ssa_status ssa_forward_stages(ssa_plan p, ssa_dtype dt, int32_t H, int32_t d,
+                                         const void* q, const void* k, const void* v,
+                                         const void* wk, const void* wv, const void* gates,
+                                         int32_t topk, float scale, void* out, int32_t* sel_out,
+                                         void* ws, size_t ws_bytes, int save_for_bwd,
+                                         hipStream_t stream, uint32_t stages) {
+  return forward_impl(p, dt, H, d, q, k, v, wk, wv, gates, topk, scale, out, sel_out, ws, ws_bytes, save_for_bwd,
+                      stream, stages, 0);
+}
+
+extern "C" ssa_status ssa_forward_conv(ssa_plan p, ssa_dtype dt, int32_t H, int32_t d, const void* q,
+                                       const void* k, const void* v, const void* wk_conv, const void* wv_conv,
+                                       const void* gates, int32_t topk, float scale, void* out,
+                                       int32_t* sel_out, void* ws, size_t ws_bytes, int save_for_bwd,
+                                       hipStream_t stream) {
+  return forward_impl(p, dt, H, d, q, k, v, wk_conv, wv_conv, gates, topk, scale, out, sel_out, ws, ws_bytes,
+                      save_for_bwd, stream, SSA_STAGE_ALL, 1);
 }
 
 extern "C" ssa_status ssa_forward(ssa_plan p, ssa_dtype dt, int32_t H, int32_t d, const void* q,
@@ -206,13 +226,11 @@ extern "C" size_t ssa_backward_workspace_size(ssa_plan p, ssa_dtype dt, int32_t 
   return bwd_carve(c, p, H, d, topk, nullptr) + 256;
 }
 
-extern "C" ssa_status ssa_backward(ssa_plan p, ssa_dtype dt, int32_t H, int32_t d, const void* q,
-                                   const void* k, const void* v, const void* wk, const void* wv,
-                                   const void* gates, int32_t topk, float scale,
-                                   const int32_t* sel, const void* dout, float* dq, float* dk,
-                                   float* dv, float* dgates, const void* fwd_ws,
-                                   size_t fwd_ws_bytes, void* ws, size_t ws_bytes,
-                                   hipStream_t stream) {
+static ssa_status backward_impl(ssa_plan p, ssa_dtype dt, int32_t H, int32_t d, const void* q, const void* k,
+                                const void* v, const void* wk, const void* wv, const void* gates, int32_t topk,
+                                float scale, const int32_t* sel, const void* dout, float* dq, float* dk,
+                                float* dv, float* dgates, const void* fwd_ws, size_t fwd_ws_bytes, void* ws,
+                                size_t ws_bytes, hipStream_t stream, int conv) {
   ssa_status st = check_common(p, dt, H, d, topk);
   if (st != SSA_OK) return st;
   if (!(scale >= 0.f) || isinf(scale)) return SSA_ERR_INVALID_ARG;
@@ -224,15 +242,36 @@ extern "C" ssa_status ssa_backward(ssa_plan p, ssa_dtype dt, int32_t H, int32_t 
   if (p->wkind != 0) return SSA_ERR_UNSUPPORTED;  // window cells must be unions of blocks
   if (!fwd_ws || fwd_ws_bytes < ssa_forward_workspace_size(p, dt, H, d, topk, 1)) return SSA_ERR_WORKSPACE;
   if (!ws || ws_bytes < ssa_backward_workspace_size(p, dt, H, d, topk)) return SSA_ERR_WORKSPACE;
-  if (!recorded_scale_matches(p, fwd_ws, scale)) return SSA_ERR_INVALID_ARG;
+  if (!recorded_forward_matches(p, fwd_ws, scale, conv)) return SSA_ERR_INVALID_ARG;
   Carver c(const_cast<void*>(fwd_ws));
   c.off = (256 - (reinterpret_cast<uintptr_t>(fwd_ws) & 255)) & 255;
   FwdWs fw;
   fwd_carve(c, p, dt, H, d, topk, 1, &fw);
   if (launch_backward(dt, p, H, d, topk, scale, q, k, v, wk, wv, gates, sel, dout, dq, dk, dv,
-                      dgates, fw, ws, stream) != hipSuccess)
+                      dgates, fw, ws, stream, conv) != hipSuccess)
     return SSA_ERR_HIP;
   return SSA_OK;
+}
+
+extern "C" ssa_status ssa_backward(ssa_plan p, ssa_dtype dt, int32_t H, int32_t d, const void* q,
+                                   const void* k, const void* v, const void* wk, const void* wv,
+                                   const void* gates, int32_t topk, float scale,
+                                   const int32_t* sel, const void* dout, float* dq, float* dk,
+                                   float* dv, float* dgates, const void* fwd_ws,
+                                   size_t fwd_ws_bytes, void* ws, size_t ws_bytes,
+                                   hipStream_t stream) {
+  return backward_impl(p, dt, H, d, q, k, v, wk, wv, gates, topk, scale, sel, dout, dq, dk, dv, dgates, fwd_ws,
+                       fwd_ws_bytes, ws, ws_bytes, stream, 0);
+}
+
+extern "C" ssa_status ssa_backward_conv(ssa_plan p, ssa_dtype dt, int32_t H, int32_t d, const void* q,
+                                        const void* k, const void* v, const void* wk_conv, const void* wv_conv,
+                                        const void* gates, int32_t topk, float scale, const int32_t* sel,
+                                        const void* dout, float* dq, float* dk, float* dv, float* dgates,
+                                        const void* fwd_ws, size_t fwd_ws_bytes, void* ws, size_t ws_bytes,
+                                        hipStream_t stream) {
+  return backward_impl(p, dt, H, d, q, k, v, wk_conv, wv_conv, gates, topk, scale, sel, dout, dq, dk, dv, dgates,
+                       fwd_ws, fwd_ws_bytes, ws, ws_bytes, stream, 1);
 }
 
 extern "C" const char* ssa_status_string(ssa_status s) {

@@ -1368,8 +1368,8 @@ __global__ __launch_bounds__(64 * BW) void k_bwd_cmp(
 template <int DT, int D>
 __global__ __launch_bounds__(256) void k_bwd_pool(
     const typename Tr<DT>::T* __restrict__ wk, const typename Tr<DT>::T* __restrict__ wv,
-    const float* __restrict__ part_k, const float* __restrict__ part_v,
-    const int32_t* __restrict__ blk_off, int Mp, int H, int qch, float* __restrict__ ukv) {
+    float* __restrict__ part_k, float* __restrict__ part_v,
+    const int32_t* __restrict__ blk_off, int Mp, int H, int qch, float* __restrict__ ukv, int conv) {
   __shared__ float gk[D], gv[D];
   const int b = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
   for (int j = tid; j < 2 * D; j += 256) {
@@ -1381,6 +1381,15 @@ __global__ __launch_bounds__(256) void k_bwd_pool(
   }
   __syncthreads();
   const float inv = 1.f / (float)(blk_off[b + 1] - blk_off[b]);
+  if (conv) {  // no term shared by the block: each token's own position weight maps it later
+    for (int j = tid; j < 2 * D; j += 256) {
+      const bool isk = j < D;
+      const int i = isk ? j : j - D;
+      ukv[(((int64_t)(isk ? 0 : 1) * H + h) * Mp + b) * D + i] = 0.f;
+      (isk ? part_k : part_v)[((int64_t)h * Mp + b) * D + i] = (isk ? gk : gv)[i] * inv;  // chunk 0's slot
+    }
+    return;
+  }
   for (int j = tid; j < 2 * D; j += 256) {
     const bool isk = j < D;
     const int i = isk ? j : j - D;
@@ -1397,7 +1406,7 @@ hipError_t run_backward(const ssa_plan_s* p, int H, int topk, float scale, const
                         const void* k, const void* v, const void* wk, const void* wv,
                         const void* gates, const int32_t* sel, const void* dout, float* dq,
                         float* dk, float* dv, float* dgates, const FwdWs& fw, const BwdWs& w,
-                        hipStream_t s) {
+                        hipStream_t s, int conv) {
   using T = typename Tr<DT>::T;
   const int M = (int)p->M;
   const int Mp = (int)pooled_rows(M);
@@ -1441,7 +1450,7 @@ hipError_t run_backward(const ssa_plan_s* p, int H, int topk, float scale, const
                      (const T*)fw.pooled_v, fw.lse, w.D,
                      p->perm, Mp, H, w.qch, N, scale, sl2, w.part_k, w.part_v);
   hipLaunchKernelGGL((k_bwd_pool<DT, D>), dim3(M, H), dim3(256), 0, s, (const T*)wk, (const T*)wv,
-                     w.part_k, w.part_v, p->blk_off, Mp, H, w.qch, w.ukv);
+                     w.part_k, w.part_v, p->blk_off, Mp, H, w.qch, w.ukv, conv);
   // key-side schedule
   const int U = H * M;
   hipLaunchKernelGGL(k_kv_keys, dim3((U + 255) / 256), dim3(256), 0, s, w.inv_off, p->blk_cell, p->cell_off, M,
@@ -1486,6 +1495,10 @@ hipError_t run_backward(const ssa_plan_s* p, int H, int topk, float scale, const
   }
   hipLaunchKernelGGL((k_kv_reduce<D>), dim3(U), dim3(256), 0, s, w.sinfo, w.kpart, w.ukv, p->blk_off, p->perm,
                      M, Mp, H, dk, dv);
+  if (conv) {  // the compressed branch's term through each token's own position weight
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    return launch_conv_term((ssa_dtype)DT, p, H, D, wk, wv, w.part_k, w.part_v, dk, dv, s);
+  }
   return hipGetLastError();
 }
 
@@ -1494,12 +1507,12 @@ hipError_t backward_d(int d, const ssa_plan_s* p, int H, int topk, float scale, 
                       const void* k, const void* v, const void* wk, const void* wv,
                       const void* gates, const int32_t* sel, const void* dout, float* dq,
                       float* dk, float* dv, float* dgates, const FwdWs& fw, const BwdWs& w,
-                      hipStream_t s) {
+                      hipStream_t s, int conv) {
   switch (d) {
-    case 32: return run_backward<DT, 32>(p, H, topk, scale, q, k, v, wk, wv, gates, sel, dout, dq, dk, dv, dgates, fw, w, s);
-    case 64: return run_backward<DT, 64>(p, H, topk, scale, q, k, v, wk, wv, gates, sel, dout, dq, dk, dv, dgates, fw, w, s);
-    case 96: return run_backward<DT, 96>(p, H, topk, scale, q, k, v, wk, wv, gates, sel, dout, dq, dk, dv, dgates, fw, w, s);
-    case 128: return run_backward<DT, 128>(p, H, topk, scale, q, k, v, wk, wv, gates, sel, dout, dq, dk, dv, dgates, fw, w, s);
+    case 32: return run_backward<DT, 32>(p, H, topk, scale, q, k, v, wk, wv, gates, sel, dout, dq, dk, dv, dgates, fw, w, s, conv);
+    case 64: return run_backward<DT, 64>(p, H, topk, scale, q, k, v, wk, wv, gates, sel, dout, dq, dk, dv, dgates, fw, w, s, conv);
+    case 96: return run_backward<DT, 96>(p, H, topk, scale, q, k, v, wk, wv, gates, sel, dout, dq, dk, dv, dgates, fw, w, s, conv);
+    case 128: return run_backward<DT, 128>(p, H, topk, scale, q, k, v, wk, wv, gates, sel, dout, dq, dk, dv, dgates, fw, w, s, conv);
   }
   return hipErrorInvalidValue;
 }
@@ -1514,15 +1527,15 @@ hipError_t launch_backward(ssa_dtype dt, const ssa_plan_s* p, int H, int d, int 
                            const void* q, const void* k, const void* v, const void* wk,
                            const void* wv, const void* gates, const int32_t* sel, const void* dout,
                            float* dq, float* dk, float* dv, float* dgates, const FwdWs& fw,
-                           void* ws, hipStream_t s) {
+                           void* ws, hipStream_t s, int conv) {
   Carver c(ws);
   c.off = (256 - (reinterpret_cast<uintptr_t>(ws) & 255)) & 255;
   BwdWs w;
   carve(c, p, H, d, topk, &w);
   switch (dt) {
-    case SSA_F32: return backward_d<DT_F32>(d, p, H, topk, scale, q, k, v, wk, wv, gates, sel, dout, dq, dk, dv, dgates, fw, w, s);
-    case SSA_F16: return backward_d<DT_F16>(d, p, H, topk, scale, q, k, v, wk, wv, gates, sel, dout, dq, dk, dv, dgates, fw, w, s);
-    case SSA_BF16: return backward_d<DT_BF16>(d, p, H, topk, scale, q, k, v, wk, wv, gates, sel, dout, dq, dk, dv, dgates, fw, w, s);
+    case SSA_F32: return backward_d<DT_F32>(d, p, H, topk, scale, q, k, v, wk, wv, gates, sel, dout, dq, dk, dv, dgates, fw, w, s, conv);
+    case SSA_F16: return backward_d<DT_F16>(d, p, H, topk, scale, q, k, v, wk, wv, gates, sel, dout, dq, dk, dv, dgates, fw, w, s, conv);
+    case SSA_BF16: return backward_d<DT_BF16>(d, p, H, topk, scale, q, k, v, wk, wv, gates, sel, dout, dq, dk, dv, dgates, fw, w, s, conv);
   }
   return hipErrorInvalidValue;
 }

@@ -28,10 +28,11 @@ struct ssa_plan_s {
   int64_t wC = 0;           // cells of the token-level partition
   int32_t wmax_rows = 0;    // tokens of its largest cell
   int32_t *wperm = nullptr, *wcell_off = nullptr, *wlpt = nullptr;
+  int32_t* pos = nullptr;   // [N] position of each token inside its block, x-major, in [0, B^3)
   // Softmax scale of the most recent forwards that saved state for the backward, by
   // workspace address: the saved log-sum-exp values hold that scale, so a backward on
   // the same workspace must use it.  Guarded by rec_mu (a plan may serve several threads).
-  struct FwdRecord { const void* ws; float scale; };
+  struct FwdRecord { const void* ws; float scale; int conv; };
   static constexpr int NREC = 16;
   FwdRecord rec[NREC] = {};
   int rec_next = 0;
@@ -58,6 +59,7 @@ struct PlanWs {
   int32_t *val_a, *val_b, *rank, *hist, *tile_cnt, *counters, *scan_part;
   int32_t* cell_key;
   int32_t *wperm, *wcell_off, *wlpt;  // token-level window partition (when cells are not unions of blocks)
+  int32_t* pos;                       // position of each token inside its block
 };
 size_t plan_carve(Carver& c, int64_t n, PlanWs* w);
 
@@ -136,7 +138,12 @@ hipError_t launch_backward(ssa_dtype dt, const ssa_plan_s* p, int H, int d, int 
                            const void* q, const void* k, const void* v, const void* wk,
                            const void* wv, const void* gates, const int32_t* sel, const void* dout,
                            float* dq, float* dk, float* dv, float* dgates, const FwdWs& fw,
-                           void* ws, hipStream_t s);
+                           void* ws, hipStream_t s, int conv);
+// The sparse-convolution compressor (wk, wv are [B^3][d][d] position weights).
+hipError_t launch_pool_conv(ssa_dtype dt, const ssa_plan_s* p, int H, int d, const void* k, const void* v,
+                            const void* wck, const void* wcv, const FwdWs& w, hipStream_t s);
+hipError_t launch_conv_term(ssa_dtype dt, const ssa_plan_s* p, int H, int d, const void* wck, const void* wcv,
+                            const float* gk, const float* gv, float* dk, float* dv, hipStream_t s);
 size_t bwd_carve(Carver& c, const ssa_plan_s* p, int H, int d, int topk, void* w);
 hipError_t launch_attend(ssa_dtype dt, const ssa_plan_s* p, int H, int d, int topk, float scale,
                          const void* q, const void* k, const void* v, const void* gates,

@@ -19,7 +19,7 @@ constexpr int STILE = 1024;  // segment-scan tile: 4 elements per thread
 
 __global__ void k_block_keys(const int32_t* __restrict__ coords, int64_t n, int3 grid, int B,
                              int3 dims, uint32_t* __restrict__ keys, int32_t* __restrict__ vals,
-                             int32_t* __restrict__ err) {
+                             int32_t* __restrict__ err, int32_t* __restrict__ pos) {
   int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= n) return;
   int x = coords[3 * i], y = coords[3 * i + 1], z = coords[3 * i + 2];
@@ -31,6 +31,8 @@ __global__ void k_block_keys(const int32_t* __restrict__ coords, int64_t n, int3
   uint32_t bx = x / B, by = y / B, bz = z / B;
   keys[i] = (bx * (uint32_t)dims.y + by) * (uint32_t)dims.z + bz;
   vals[i] = (int32_t)i;
+  // position inside the block, x-major (the sparse-convolution compressor's weight index)
+  pos[i] = (int32_t)(((x - bx * B) * (uint32_t)B + (y - by * B)) * (uint32_t)B + (z - bz * B));
 }
 
 // Per tile: stable rank of every key among equal digits, and the tile's digit histogram
@@ -469,6 +471,7 @@ size_t plan_carve(Carver& c, int64_t n, PlanWs* w) {
   t.wperm = c.take<int32_t>(n1);
   t.wcell_off = c.take<int32_t>(n1 + 1);
   t.wlpt = c.take<int32_t>(n1);
+  t.pos = c.take<int32_t>(n1);
   if (w) *w = t;
   return c.off;
 }
@@ -547,6 +550,7 @@ extern "C" ssa_status ssa_plan_create_ex(const int32_t* coords, int64_t n, const
   for (int a = 0; a < 3; ++a) p->wshift[a] = win.kind == SSA_WINDOW_CUBE ? win.shift[a] : 0;
   p->sfc_tokens = win.kind == SSA_WINDOW_SFC ? win.tokens : 0;
   p->wperm = w.wperm; p->wcell_off = w.wcell_off; p->wlpt = w.wlpt;
+  p->pos = w.pos;
   p->perm = w.perm; p->blk_off = w.blk_off; p->blk_key = w.blk_key; p->tok2blk = w.tok2blk;
   p->blk_cell = w.blk_cell; p->cell_off = w.cell_off; p->cell_blk = w.cell_blk; p->lpt = w.lpt;
   p->M = 0; p->ncells = 0; p->max_rows = 0;
@@ -560,7 +564,7 @@ extern "C" ssa_status ssa_plan_create_ex(const int32_t* coords, int64_t n, const
   if (hipMemsetAsync(w.counters, 0, 8 * sizeof(int32_t), stream) != hipSuccess) return fail(SSA_ERR_HIP);
   hipLaunchKernelGGL(k_block_keys, dim3((ni + 255) / 256), dim3(256), 0, stream, coords, n,
                      make_int3(grid[0], grid[1], grid[2]), block, make_int3(dims[0], dims[1], dims[2]),
-                     w.key_a, w.val_a, w.counters + 7);
+                     w.key_a, w.val_a, w.counters + 7, w.pos);
   uint32_t *ka = w.key_a, *kb = w.key_b;
   int32_t *va = w.val_a, *vb = w.val_b;
   if (radix_sort(ka, va, kb, vb, ni, bits_for(nblocks - 1), w.rank, w.hist, w.scan_part, stream) != hipSuccess)

@@ -131,11 +131,16 @@ GRAD_TOL = {"f32": {"abs": 1e-4, "rel_l2": 1e-5}, "f16": {"abs": 2e-2, "rel_l2":
 
 
 def compare_grad(got, ref, dt, what=""):
+    """Gradients (fp32 outputs) against the oracle.  For bf16 inputs the max-abs bound grows with
+    the gradient's magnitude past 8: the GPU's probabilities and pooled values enter the
+    products in bf16 (unit roundoff 2^-9), so a gradient of size G carries errors of order
+    G * 2^-9 -- at |G| = 8 that is bf16's own half-ulp, above 2e-2 (the rel-L2 bound stays)."""
     tol = GRAD_TOL[dt]
     assert np.isfinite(got).all(), f"{what}: non-finite"
     err = np.abs(got - ref).max()
     rel = np.linalg.norm(got - ref) / max(np.linalg.norm(ref), 1e-30)
-    assert err <= tol["abs"], f"{what}: max-abs {err:.3g} > {tol['abs']} (rel-L2 {rel:.3g})"
+    bound = tol["abs"] * (max(1.0, float(np.abs(ref).max()) / 8.0) if dt == "bf16" else 1.0)
+    assert err <= bound, f"{what}: max-abs {err:.3g} > {bound:.3g} (rel-L2 {rel:.3g}, max |ref| {np.abs(ref).max():.3g})"
     assert rel <= tol["rel_l2"], f"{what}: rel-L2 {rel:.3g} > {tol['rel_l2']}"
     return float(err), float(rel)
 

@@ -23,7 +23,7 @@ import math
 import numpy as np
 
 __all__ = ["Workload", "WORKLOADS", "make_inputs", "make_geometry", "round_to_dtype",
-           "random_inputs", "producer_inputs"]
+           "random_inputs", "producer_inputs", "conv_weights"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -196,3 +196,13 @@ def producer_inputs(n: int, channels: int, heads: int, dim: int, dtype: str, see
         "gamma_q": round_to_dtype(1.0 + 0.1 * r[4].standard_normal(dim), dtype),
         "gamma_k": round_to_dtype(1.0 + 0.1 * r[5].standard_normal(dim), dtype),
     }
+
+
+def conv_weights(block: int, dim: int, dtype: str, seed: int) -> tuple:
+    """Position weights of the sparse-convolution compressor: W_k, W_v ~ N(0, 1/d), each
+    [B^3, d, d] (every position inside a block a linear-layer matrix [d_out, d_in])."""
+    ss = np.random.SeedSequence([seed, 11])
+    rk, rv = [np.random.default_rng(x) for x in ss.spawn(2)]
+    shape = (block ** 3, dim, dim)
+    return (round_to_dtype(rk.standard_normal(shape) / math.sqrt(dim), dtype),
+            round_to_dtype(rv.standard_normal(shape) / math.sqrt(dim), dtype))
