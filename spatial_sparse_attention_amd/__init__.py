@@ -13,7 +13,7 @@ import os
 
 import torch
 
-__all__ = ["Plan", "Window", "qkv_gates", "forward", "forward_batch", "forward_workspace_size", "forward_noalloc", "backward",
+__all__ = ["Plan", "Window", "qkv_gates", "forward", "forward_batch", "forward_batch_workspace_size", "forward_workspace_size", "forward_noalloc", "backward",
            "backward_workspace_size", "NOALLOC_SCRATCH_BYTES",
            "SSAError", "lib", "LIB_PATH", "STAGE_POOL", "STAGE_SELECT", "STAGE_ATTEND", "STAGE_ALL"]
 
@@ -142,10 +142,11 @@ def _uses(stream, *tensors):
 class Plan:
     """Block partition of int32 coordinates [N,3] on the GPU (ssa_plan_create_ex).  The window
     branch uses cubic cells of edge `window` shifted by `shift`, or, with sfc_tokens > 0,
-    runs of sfc_tokens tokens along the Morton order of the voxels."""
+    runs of sfc_tokens tokens along the Morton order of the voxels.  `ws`: an optional uint8
+    device buffer for the plan's arrays (allocated here when absent or too small)."""
 
     def __init__(self, coords: torch.Tensor, grid, block: int, window: int, stream=None,
-                 shift=(0, 0, 0), sfc_tokens: int = 0):
+                 shift=(0, 0, 0), sfc_tokens: int = 0, ws=None):
         if coords.dtype != torch.int32 or coords.dim() != 2 or coords.shape[1] != 3:
             raise ValueError("coords must be an int32 tensor of shape [N,3]")
         if not coords.is_contiguous():
@@ -159,13 +160,15 @@ class Plan:
         size = lib.ssa_plan_workspace_size_ex(self.n, self.grid, self.block, ctypes.byref(self.win))
         if size == 0:
             raise SSAError(1, "ssa_plan_workspace_size")
-        with _alloc_on(stream):
-            self.ws = torch.empty(size, dtype=torch.uint8, device=coords.device)
-        _uses(stream, coords)
+        if ws is None or ws.numel() < size:
+            with _alloc_on(stream):
+                ws = torch.empty(size, dtype=torch.uint8, device=coords.device)
+        self.ws = ws
+        _uses(stream, coords, ws)
         self.coords = coords
         h = _vp()
         st = lib.ssa_plan_create_ex(_ptr(coords), self.n, self.grid, self.block, ctypes.byref(self.win),
-                                    _ptr(self.ws), size, _stream(stream), ctypes.byref(h))
+                                    _ptr(self.ws), self.ws.numel(), _stream(stream), ctypes.byref(h))
         _check(st, "ssa_plan_create")
         self.handle = h
         info = PlanInfo()
@@ -276,6 +279,11 @@ def forward_noalloc(plan: Plan, q, k, v, wk, wv, gates, topk: int, out, sel_out=
                                  _ptr(out), _ptr(sel_out), _stream(stream))
     _check(st, "ssa_forward_noalloc")
     return out, sel_out
+
+
+def forward_batch_workspace_size(plans, dtype, heads: int, dim: int, topk: int) -> int:
+    handles = (_vp * len(plans))(*[p.handle.value for p in plans])
+    return int(lib.ssa_forward_batch_workspace_size(handles, len(plans), _DTYPES[dtype], heads, dim, topk))
 
 
 def forward_batch(plans, tok_off, q, k, v, wk, wv, gates, topk: int, scale: float = 0.0, out=None,

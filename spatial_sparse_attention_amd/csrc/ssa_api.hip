@@ -64,6 +64,7 @@ size_t fwd_carve(Carver& c, const ssa_plan_s* p, ssa_dtype dt, int H, int d, int
 
 extern "C" size_t ssa_forward_workspace_size(ssa_plan p, ssa_dtype dt, int32_t H, int32_t d,
                                              int32_t topk, int save_for_bwd) {
+  if (!abi_enum_in(&dt, 0, 2)) return 0;
   if (check_common(p, dt, H, d, topk) != SSA_OK) return 0;
   Carver c(nullptr);
   return fwd_carve(c, p, dt, H, d, topk, save_for_bwd ? 1 : 0, nullptr) + 256;
@@ -93,15 +94,20 @@ static ssa_status forward_impl(ssa_plan p, ssa_dtype dt, int32_t H, int32_t d, c
   int32_t* sel = sel_out ? sel_out : w.sel;
   if (save && (stages & SSA_STAGE_SELECT)) record_forward(p, ws, scale, conv);
   if (stages & SSA_STAGE_POOL) {
+    RoctxRange r(conv ? "ssa_forward/pool_conv" : "ssa_forward/pool");
     const hipError_t e = conv ? launch_pool_conv(dt, p, H, d, k, v, wk, wv, w, stream)
                               : launch_pool(dt, p, H, d, k, v, wk, wv, w, stream);
     if (e != hipSuccess) return SSA_ERR_HIP;
   }
-  if (stages & SSA_STAGE_SELECT)
+  if (stages & SSA_STAGE_SELECT) {
+    RoctxRange r("ssa_forward/select");
     if (launch_select(dt, p, H, d, topk, scale, q, w, sel, stream) != hipSuccess) return SSA_ERR_HIP;
-  if (stages & SSA_STAGE_ATTEND)
+  }
+  if (stages & SSA_STAGE_ATTEND) {
+    RoctxRange r("ssa_forward/attend");
     if (launch_attend(dt, p, H, d, topk, scale, q, k, v, gates, w, sel, out, stream) != hipSuccess)
       return SSA_ERR_HIP;
+  }
   return SSA_OK;
 }
 
@@ -111,6 +117,7 @@ extern "C" ssa_status ssa_forward_stages(ssa_plan p, ssa_dtype dt, int32_t H, in
                                          int32_t topk, float scale, void* out, int32_t* sel_out,
                                          void* ws, size_t ws_bytes, int save_for_bwd,
                                          hipStream_t stream, uint32_t stages) {
+  if (!abi_enum_in(&dt, 0, 2)) return SSA_ERR_INVALID_ARG;
   return forward_impl(p, dt, H, d, q, k, v, wk, wv, gates, topk, scale, out, sel_out, ws, ws_bytes, save_for_bwd,
                       stream, stages, 0);
 }
@@ -120,6 +127,7 @@ extern "C" ssa_status ssa_forward_conv(ssa_plan p, ssa_dtype dt, int32_t H, int3
                                        const void* gates, int32_t topk, float scale, void* out,
                                        int32_t* sel_out, void* ws, size_t ws_bytes, int save_for_bwd,
                                        hipStream_t stream) {
+  if (!abi_enum_in(&dt, 0, 2)) return SSA_ERR_INVALID_ARG;
   return forward_impl(p, dt, H, d, q, k, v, wk_conv, wv_conv, gates, topk, scale, out, sel_out, ws, ws_bytes,
                       save_for_bwd, stream, SSA_STAGE_ALL, 1);
 }
@@ -129,6 +137,7 @@ extern "C" ssa_status ssa_forward(ssa_plan p, ssa_dtype dt, int32_t H, int32_t d
                                   const void* gates, int32_t topk, float scale, void* out,
                                   int32_t* sel_out, void* ws, size_t ws_bytes, int save_for_bwd,
                                   hipStream_t stream) {
+  if (!abi_enum_in(&dt, 0, 2)) return SSA_ERR_INVALID_ARG;
   return ssa_forward_stages(p, dt, H, d, q, k, v, wk, wv, gates, topk, scale, out, sel_out, ws,
                             ws_bytes, save_for_bwd, stream, SSA_STAGE_ALL);
 }
@@ -164,6 +173,7 @@ extern "C" ssa_status ssa_forward_noalloc(ssa_plan p, ssa_dtype dt, int32_t H, i
                                           const void* wk, const void* wv, const void* gates,
                                           int32_t topk, float scale, void* out, int32_t* sel_out,
                                           hipStream_t stream) {
+  if (!abi_enum_in(&dt, 0, 2)) return SSA_ERR_INVALID_ARG;
   ssa_status st = check_common(p, dt, H, d, topk);
   if (st != SSA_OK) return st;
   if (p->n == 0) return ssa_forward_stages(p, dt, H, d, q, k, v, wk, wv, gates, topk, scale, out,
@@ -180,6 +190,7 @@ extern "C" ssa_status ssa_forward_noalloc(ssa_plan p, ssa_dtype dt, int32_t H, i
 // ------------------------------------------------------------------ several samples
 extern "C" size_t ssa_forward_batch_workspace_size(const ssa_plan* plans, int32_t nsamples, ssa_dtype dt,
                                                    int32_t H, int32_t d, int32_t topk) {
+  if (!abi_enum_in(&dt, 0, 2)) return 0;
   if (!plans || nsamples < 1) return 0;
   size_t mx = 0;
   for (int i = 0; i < nsamples; ++i) {
@@ -195,6 +206,7 @@ extern "C" ssa_status ssa_forward_batch(const ssa_plan* plans, int32_t nsamples,
                                         const void* v, const void* wk, const void* wv, const void* gates,
                                         int32_t topk, float scale, void* out, void* ws, size_t ws_bytes,
                                         hipStream_t stream) {
+  if (!abi_enum_in(&dt, 0, 2)) return SSA_ERR_INVALID_ARG;
   if (!plans || !tok_off || nsamples < 1) return SSA_ERR_INVALID_ARG;
   if (tok_off[0] != 0) return SSA_ERR_INVALID_ARG;
   for (int i = 0; i < nsamples; ++i) {  // every check before any launch
@@ -221,6 +233,7 @@ extern "C" ssa_status ssa_forward_batch(const ssa_plan* plans, int32_t nsamples,
 
 extern "C" size_t ssa_backward_workspace_size(ssa_plan p, ssa_dtype dt, int32_t H, int32_t d,
                                               int32_t topk) {
+  if (!abi_enum_in(&dt, 0, 2)) return 0;
   if (check_common(p, dt, H, d, topk) != SSA_OK || p->wkind != 0) return 0;
   Carver c(nullptr);
   return bwd_carve(c, p, H, d, topk, nullptr) + 256;
@@ -247,6 +260,7 @@ static ssa_status backward_impl(ssa_plan p, ssa_dtype dt, int32_t H, int32_t d, 
   c.off = (256 - (reinterpret_cast<uintptr_t>(fwd_ws) & 255)) & 255;
   FwdWs fw;
   fwd_carve(c, p, dt, H, d, topk, 1, &fw);
+  RoctxRange r(conv ? "ssa_backward_conv" : "ssa_backward");
   if (launch_backward(dt, p, H, d, topk, scale, q, k, v, wk, wv, gates, sel, dout, dq, dk, dv,
                       dgates, fw, ws, stream, conv) != hipSuccess)
     return SSA_ERR_HIP;
@@ -260,6 +274,7 @@ extern "C" ssa_status ssa_backward(ssa_plan p, ssa_dtype dt, int32_t H, int32_t 
                                    float* dv, float* dgates, const void* fwd_ws,
                                    size_t fwd_ws_bytes, void* ws, size_t ws_bytes,
                                    hipStream_t stream) {
+  if (!abi_enum_in(&dt, 0, 2)) return SSA_ERR_INVALID_ARG;
   return backward_impl(p, dt, H, d, q, k, v, wk, wv, gates, topk, scale, sel, dout, dq, dk, dv, dgates, fwd_ws,
                        fwd_ws_bytes, ws, ws_bytes, stream, 0);
 }
@@ -270,11 +285,13 @@ extern "C" ssa_status ssa_backward_conv(ssa_plan p, ssa_dtype dt, int32_t H, int
                                         const void* dout, float* dq, float* dk, float* dv, float* dgates,
                                         const void* fwd_ws, size_t fwd_ws_bytes, void* ws, size_t ws_bytes,
                                         hipStream_t stream) {
+  if (!abi_enum_in(&dt, 0, 2)) return SSA_ERR_INVALID_ARG;
   return backward_impl(p, dt, H, d, q, k, v, wk_conv, wv_conv, gates, topk, scale, sel, dout, dq, dk, dv, dgates,
                        fwd_ws, fwd_ws_bytes, ws, ws_bytes, stream, 1);
 }
 
 extern "C" const char* ssa_status_string(ssa_status s) {
+  if (!abi_enum_in(&s, SSA_OK, SSA_ERR_TOO_LARGE)) return "unknown status";
   switch (s) {
     case SSA_OK: return "ok";
     case SSA_ERR_INVALID_ARG: return "invalid argument";

@@ -3,12 +3,34 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <stddef.h>
+#include <cstring>
 #include <mutex>
+#include <rocprofiler-sdk-roctx/roctx.h>
 #include "ssa.h"
 
 #define SSA_PLAN_MAGIC 0x53534150u  // "SSAP"
 
 // Host-side plan handle.  Device arrays live in the caller's plan workspace.
+// A roctx range around one host call's launches (rocprofv3 --marker-trace shows them per
+// phase; without a profiler attached a push or pop is a call into an empty table).
+struct RoctxRange {
+  explicit RoctxRange(const char* name) { roctxRangePushA(name); }
+  ~RoctxRange() { roctxRangePop(); }
+  RoctxRange(const RoctxRange&) = delete;
+  RoctxRange& operator=(const RoctxRange&) = delete;
+};
+
+// Enum arguments of the C ABI may carry any int (C allows that); C++ forbids reading an
+// enum object whose value lies outside its enumerators' range, so entry points test the raw
+// bits before the first read of such an argument.
+template <class E>
+inline bool abi_enum_in(const E* e, int lo, int hi) {
+  static_assert(sizeof(E) == sizeof(int), "C enums are int-sized on this ABI");
+  int v;
+  std::memcpy(&v, e, sizeof v);
+  return v >= lo && v <= hi;
+}
+
 struct ssa_plan_s {
   uint32_t magic;
   int64_t n;

@@ -479,7 +479,7 @@ size_t plan_carve(Carver& c, int64_t n, PlanWs* w) {
 extern "C" size_t ssa_plan_workspace_size(int64_t n, const int32_t grid[3], int32_t block,
                                           int32_t window) {
   (void)grid; (void)block; (void)window;
-  if (n < 0) return 0;
+  if (n < 0 || n >= (int64_t)1 << 31) return 0;  // ssa_plan_create refuses n >= 2^31
   Carver c(nullptr);
   return plan_carve(c, n, nullptr) + 256;
 }
@@ -532,6 +532,7 @@ extern "C" ssa_status ssa_plan_create_ex(const int32_t* coords, int64_t n, const
   const int32_t window = win.kind == SSA_WINDOW_CUBE ? win.edge : 0;
   if (!ws) return SSA_ERR_WORKSPACE;
   if (ws_bytes < ssa_plan_workspace_size(n, grid, block, 1)) return SSA_ERR_WORKSPACE;
+  RoctxRange range("ssa_plan_create");
 
   Carver c(ws);
   c.off = (256 - (reinterpret_cast<uintptr_t>(ws) & 255)) & 255;

@@ -208,15 +208,18 @@ extern "C" ssa_status ssa_qkv_gates(ssa_dtype dt, int64_t n, int32_t C, int32_t 
                                     const void* gamma_q, const void* gamma_k, const int32_t* coords,
                                     float rope_base, float eps, void* q, void* k, void* v, void* gates,
                                     hipStream_t stream) {
-  if ((int)dt < 0 || (int)dt > 2) return SSA_ERR_INVALID_ARG;
+  if (!abi_enum_in(&dt, 0, 2)) return SSA_ERR_INVALID_ARG;
   if (n < 0 || C < 1 || H < 1 || d < 1) return SSA_ERR_INVALID_ARG;
   if (!(rope_base >= 0.f) || isinf(rope_base) || !(eps >= 0.f) || isinf(eps)) return SSA_ERR_INVALID_ARG;
   if (dt == SSA_F32) return SSA_ERR_UNSUPPORTED;
   if (!(d == 32 || d == 64 || d == 96 || d == 128) || C % 8 != 0) return SSA_ERR_UNSUPPORTED;
-  if (n * (int64_t)H * d >= ((int64_t)1 << 31) || n * (int64_t)C >= ((int64_t)1 << 40)) return SSA_ERR_UNSUPPORTED;
+  // element offsets of q, k, v stay below 2^31 and those of x below 2^40 (divisions: no overflow)
+  if (n > (((int64_t)1 << 31) - 1) / ((int64_t)H * d) || n > (((int64_t)1 << 40) - 1) / C)
+    return SSA_ERR_UNSUPPORTED;
   if (n == 0) return SSA_OK;
   if (!x || !w_qkv || !w_gate || !gamma_q || !gamma_k || !coords || !q || !k || !v || !gates)
     return SSA_ERR_INVALID_ARG;
+  RoctxRange r("ssa_qkv_gates");
   const float base = rope_base == 0.f ? 10000.f : rope_base;
   const float e = eps == 0.f ? 1e-6f : eps;
   const hipError_t err = dt == SSA_F16
