@@ -243,82 +243,56 @@ __device__ inline void load4(const T* p, float* v) {
   }
 }
 
-// Top keff = min(topk, M) entries of sig[0..M) (ties to the lower id), written in ascending
-// id order to out[0..keff), out[keff..topk) = -1.  sig >= 0, so the fp32 bit patterns order
-// like the values: a radix select over four 8-bit digits finds the keff-th largest pattern
-// T and how many entries equal to T to take; a scan in id order then places every entry
-// above T and the first such ties.  All NW waves take part.
-template <int NW>
-__device__ void topk_radix(const float* sig, int M, int topk, int32_t* __restrict__ out,
-                           uint32_t* hist, uint32_t* bc, uint32_t (*wc)[NW], int tid) {
-  constexpr int NTH = 64 * NW;
-  const int lane = tid & 63, wave = tid >> 6;
+// Top keff = min(topk, M) entries of sig[0..M) (in LDS, zero from M up to the next multiple of
+// four; ties to the lower id) by one wave, written in ascending id order to out[0..keff),
+// out[keff..topk) = -1.  sig >= 0, so the fp32 bit patterns order like the values: the
+// keff-th largest pattern T is found bit by bit from the top, each step counting the entries
+// at or above the candidate (four 16-byte LDS reads in flight per lane, then across the wave;
+// the zeros never count), and a scan in id order places every entry above T and the first
+// entries equal to T.  The rows of a workgroup's blocks are taken one per wave.
+__device__ void topk_wave(const float* sig, int M, int topk, int32_t* __restrict__ out, int lane) {
   const int keff = min(topk, M);
-  uint32_t prefix = 0, need = (uint32_t)keff;
   const bool all = keff == M;
+  const uint32_t* u32 = reinterpret_cast<const uint32_t*>(sig);
+  const uint4* u4 = reinterpret_cast<const uint4*>(sig);  // rows start 16-byte aligned
+  const int NQ = (M + 3) / 4;
+  auto count_ge = [&](uint32_t cand) {  // entries with pattern >= cand (cand >= 1), wave total
+    int cnt = 0;
+    for (int q = lane; q < NQ; q += 256) {
+      uint4 v[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) v[t] = q + 64 * t < NQ ? u4[q + 64 * t] : make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        cnt += (v[t].x >= cand ? 1 : 0) + (v[t].y >= cand ? 1 : 0) + (v[t].z >= cand ? 1 : 0) + (v[t].w >= cand ? 1 : 0);
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) cnt += __shfl_xor(cnt, off);
+    return cnt;
+  };
+  uint32_t T = 0;
+  int need = keff;
   if (!all) {
-    for (int shift = 24; shift >= 0; shift -= 8) {
-      const uint32_t hmask = shift == 24 ? 0u : (0xFFFFFFFFu << (shift + 8));
-      for (int e = tid; e < 256; e += NTH) hist[e] = 0;
-      __syncthreads();
-      for (int j = tid; j < M; j += NTH) {
-        const uint32_t u = __float_as_uint(sig[j]);
-        if ((u & hmask) == prefix) atomicAdd(&hist[(u >> shift) & 255], 1u);
-      }
-      __syncthreads();
-      if (wave == 0) {
-        uint32_t hb[4], sum = 0;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) sum += (hb[i] = hist[4 * lane + i]);
-        uint32_t incl = sum;  // inclusive suffix sum over lanes >= lane
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-          const uint32_t o = __shfl_down(incl, off);
-          if (lane + off < 64) incl += o;
-        }
-        uint32_t acc = incl - sum;  // candidates whose digit lies in higher lanes' bins
-#pragma unroll
-        for (int i = 3; i >= 0; --i) {
-          if (acc < need && acc + hb[i] >= need) {
-            bc[0] = prefix | ((uint32_t)(4 * lane + i) << shift);
-            bc[1] = need - acc;
-          }
-          acc += hb[i];
-        }
-      }
-      __syncthreads();
-      prefix = bc[0];
-      need = bc[1];
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t cand = T | (1u << bit);
+      if (count_ge(cand) >= keff) T = cand;
     }
+    need = keff - count_ge(T + 1u);  // ties at T to take, lowest ids first
   }
-  uint32_t run_gt = 0, run_eq = 0;
-  for (int base = 0; base < M; base += NTH) {
-    const int j = base + tid;
-    const uint32_t u = j < M ? __float_as_uint(sig[j]) : 0u;
-    const bool gt = j < M && (all || u > prefix);
-    const bool eq = j < M && !all && u == prefix;
+  int run_gt = 0, run_eq = 0;
+  for (int base = 0; base < M; base += 64) {
+    const int j = base + lane;
+    const uint32_t u = j < M ? u32[j] : 0u;
+    const bool gt = j < M && (all || u > T);
+    const bool eq = j < M && !all && u == T;
     const uint64_t bg = __builtin_amdgcn_ballot_w64(gt), be = __builtin_amdgcn_ballot_w64(eq);
-    if (lane == 0) {
-      wc[0][wave] = (uint32_t)__builtin_popcountll(bg);
-      wc[1][wave] = (uint32_t)__builtin_popcountll(be);
-    }
-    __syncthreads();
-    uint32_t lg = run_gt, le = run_eq;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      if (w < wave) {
-        lg += wc[0][w];
-        le += wc[1][w];
-      }
-      run_gt += wc[0][w];
-      run_eq += wc[1][w];
-    }
-    lg += __builtin_amdgcn_mbcnt_hi((uint32_t)(bg >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bg, 0u));
-    le += __builtin_amdgcn_mbcnt_hi((uint32_t)(be >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)be, 0u));
+    const int lg = run_gt + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bg >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bg, 0u));
+    const int le = run_eq + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(be >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)be, 0u));
     if (gt || (eq && le < need)) out[lg + min(le, need)] = j;
-    __syncthreads();
+    run_gt += __builtin_popcountll(bg);
+    run_eq += __builtin_popcountll(be);
   }
-  for (int t = keff + tid; t < topk; t += NTH) out[t] = -1;
+  for (int t = keff + lane; t < topk; t += 64) out[t] = -1;
 }
 
 // Compressed branch, pass 1 (query-stationary).  Every query attends to all pooled blocks of
@@ -556,15 +530,19 @@ __global__ __launch_bounds__(64 * SEL_WAVES) void k_select(
   __shared__ float bpart[SEL_WAVES][2][32];  // column sums of a range's first / last segment
   __shared__ int32_t bkt[SEL_WAVES][2];      // their key tile * SEL_GMAX + member, -1 none
   __shared__ int32_t mb[SEL_GMAX], mr0[SEL_GMAX], mrows[SEL_GMAX], mtp[SEL_GMAX + 1];
-  __shared__ uint32_t hist[256];
-  __shared__ uint32_t bcast[2];
-  __shared__ uint32_t wcnt[2][SEL_WAVES];
-  extern __shared__ float sig[];  // [G][Mp]
+  extern __shared__ __attribute__((aligned(16))) float sig[];  // [G][Mp]
 
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 5, c = lane & 31;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int h = blockIdx.x % H;  // consecutive workgroups: the heads of one group
-  const int gi = blockIdx.x / H;
+  // items (head, group) head-major, in one contiguous range per XCD (workgroup i runs on XCD
+  // i % 8): the workgroups on an XCD at any time mostly share a head, whose pooled keys every
+  // one of them streams, so those stay in that XCD's L2
+  const int ngrp = (M + G - 1) / G;
+  const int per = (ngrp * H + NXCD - 1) / NXCD;
+  const int item = (int)(blockIdx.x % NXCD) * per + (int)(blockIdx.x / NXCD);
+  if (item >= ngrp * H) return;  // the whole workgroup
+  const int h = item / ngrp;
+  const int gi = item % ngrp;
   const int G0 = gi * G, Gk = min(G, M - G0);  // members
   if (tid == 0) {
     int tp = 0;
@@ -677,15 +655,14 @@ __global__ __launch_bounds__(64 * SEL_WAVES) void k_select(
     }
     __syncthreads();  // the rows are complete for this sweep; the query tiles are free again
   }
-  for (int k = 0; k < Gk; ++k) {
-    const int bb = mb[k];
-    if (sigma_out) {  // the top-k kernel takes it from here
-      float* dst = sigma_out + ((int64_t)h * M + bb) * Mp;
+  if (sigma_out) {  // the top-k kernel takes it from here
+    for (int k = 0; k < Gk; ++k) {
+      float* dst = sigma_out + ((int64_t)h * M + mb[k]) * Mp;
       for (int j = tid; j < M; j += 64 * SEL_WAVES) dst[j] = sig[k * Mp + j];
-    } else {
-      topk_radix<SEL_WAVES>(sig + k * Mp, M, topk, sel + ((int64_t)h * M + bb) * topk, hist, bcast, wcnt, tid);
-      __syncthreads();
     }
+  } else {
+    for (int k = wave; k < Gk; k += SEL_WAVES)
+      topk_wave(sig + k * Mp, M, topk, sel + ((int64_t)h * M + mb[k]) * topk, lane);
   }
 }
 
@@ -1159,12 +1136,13 @@ hipError_t run_select(const ssa_plan_s* p, int H, int topk, float sl2, const voi
     G = (int)std::max<int64_t>(1, std::min<int64_t>({(int64_t)SEL_GMAX, fit, want}));
   }
   const int ngrp = (int)((p->M + G - 1) / G);
+  const unsigned sel_grid = (unsigned)((ngrp * H + NXCD - 1) / NXCD * NXCD);
   if (G > 1)
-    hipLaunchKernelGGL((k_select<DT, D, true>), dim3((unsigned)(ngrp * H)), dim3(64 * SEL_WAVES), shm * G, s,
+    hipLaunchKernelGGL((k_select<DT, D, true>), dim3(sel_grid), dim3(64 * SEL_WAVES), shm * G, s,
                        (const T*)q, (const T*)w.pooled, p->perm, p->blk_off, p->lpt, (int)p->M, Mp, H,
                        p->n, sl2, topk, G, w.lsec, sel, w.sigma);
   else
-    hipLaunchKernelGGL((k_select<DT, D, false>), dim3((unsigned)(ngrp * H)), dim3(64 * SEL_WAVES), shm, s,
+    hipLaunchKernelGGL((k_select<DT, D, false>), dim3(sel_grid), dim3(64 * SEL_WAVES), shm, s,
                        (const T*)q, (const T*)w.pooled, p->perm, p->blk_off, p->lpt, (int)p->M, Mp, H,
                        p->n, sl2, topk, 1, w.lsec, sel, w.sigma);
   if (w.sigma) {

@@ -10,7 +10,6 @@
 
 #define SSA_PLAN_MAGIC 0x53534150u  // "SSAP"
 
-// Host-side plan handle.  Device arrays live in the caller's plan workspace.
 // A roctx range around one host call's launches (rocprofv3 --marker-trace shows them per
 // phase; without a profiler attached a push or pop is a call into an empty table).
 struct RoctxRange {
@@ -31,6 +30,7 @@ inline bool abi_enum_in(const E* e, int lo, int hi) {
   return v >= lo && v <= hi;
 }
 
+// Host-side plan handle.  Device arrays live in the caller's plan workspace.
 struct ssa_plan_s {
   uint32_t magic;
   int64_t n;

@@ -221,44 +221,38 @@ __global__ void k_block_stats(const int32_t* __restrict__ blk_off, int M, int n,
   ids[b] = b;
 }
 
-// Longest-first block order for up to LPT_RANK_MAX blocks in one workgroup: block i goes to
-// position #{j : size_j > size_i} + #{j < i : size_j == size_i} (sizes in LDS, every thread
-// reading the same entry at a time), which is the stable order by descending size; also the
-// largest block size.  Replaces a three-pass radix sort of up to a few thousand keys (the
-// work grows as M^2: about 20 us at M = 2048, where the radix sort takes about 30).
-constexpr int LPT_RANK_MAX = 2048;
-// M is read from device memory (launched before the host learns it); with more than
-// LPT_RANK_MAX blocks the kernel does nothing and the host sorts instead.
-__global__ __launch_bounds__(1024) void k_lpt_rank(const int32_t* __restrict__ blk_off, const int32_t* __restrict__ Mdev,
-                                                   int32_t* __restrict__ lpt, int32_t* __restrict__ max_rows) {
-  __shared__ int32_t sz[LPT_RANK_MAX];
-  __shared__ int32_t wmax[16];
+// Longest-first block order for up to LPT_RANK_MAX blocks: block i goes to position
+// #{j : size_j > size_i} + #{j < i : size_j == size_i}, which is the stable order by descending
+// size, i.e. the number of keys (size_j, -j) above (size_i, -i) taken as one 64-bit integer;
+// also the largest block size.  Every workgroup holds all keys in LDS (padded with -1, which
+// never counts) and ranks LPT_NT blocks, two keys per LDS access.  M^2 comparisons spread over
+// M / LPT_NT workgroups: about 10 us at M = 2048, where a radix sort of the keys takes about 30.
+constexpr int LPT_RANK_MAX = 2048, LPT_NT = 256;
+// M is read from device memory (launched before the host learns it, LPT_RANK_MAX / LPT_NT
+// workgroups); with more than LPT_RANK_MAX blocks the kernel does nothing and the host sorts
+// instead.
+__global__ __launch_bounds__(LPT_NT) void k_lpt_rank(const int32_t* __restrict__ blk_off, const int32_t* __restrict__ Mdev,
+                                                     int32_t* __restrict__ lpt, int32_t* __restrict__ max_rows) {
+  __shared__ longlong2 key2[LPT_RANK_MAX / 2];
+  long long* key = reinterpret_cast<long long*>(key2);
   const int M = *Mdev;
-  if (M > LPT_RANK_MAX) return;  // the whole workgroup
+  if (M > LPT_RANK_MAX || (int)blockIdx.x * LPT_NT >= M) return;  // the whole workgroup
   const int tid = threadIdx.x;
-  int mx = 0;
-  for (int i = tid; i < M; i += 1024) {
-    const int v = blk_off[i + 1] - blk_off[i];
-    sz[i] = v;
-    mx = max(mx, v);
-  }
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) mx = max(mx, __shfl_xor(mx, off));
-  if ((tid & 63) == 0) wmax[tid >> 6] = mx;
+  const int M2 = (M + 1) / 2;
+  for (int j = tid; j < 2 * M2; j += LPT_NT)
+    key[j] = j < M ? ((long long)(blk_off[j + 1] - blk_off[j]) << 32) | (long long)(0x7FFFFFFF - j) : -1ll;
   __syncthreads();
-  for (int i = tid; i < M; i += 1024) {
-    const int si = sz[i];
+  const int i = blockIdx.x * LPT_NT + tid;
+  if (i < M) {
+    const long long ki = key[i];
     int r = 0;
-    for (int j = 0; j < M; ++j) {
-      const int sj = sz[j];
-      r += (sj > si || (sj == si && j < i)) ? 1 : 0;
+    for (int j2 = 0; j2 < M2; ++j2) {
+      const longlong2 v = key2[j2];
+      r += v.x > ki ? 1 : 0;
+      r += v.y > ki ? 1 : 0;
     }
     lpt[r] = i;
-  }
-  if (tid == 0) {
-    int m = 0;
-    for (int w = 0; w < 16; ++w) m = max(m, wmax[w]);
-    *max_rows = m;
+    if (r == 0) *max_rows = (int32_t)(ki >> 32);  // the longest block
   }
 }
 
@@ -421,8 +415,8 @@ ssa_status build_window_partition(ssa_plan_s* p, const int32_t* coords, PlanWs& 
     hipLaunchKernelGGL(k_sfc_cells, dim3((nc + 256) / 256), dim3(256), 0, stream, w.wcell_off, ni, p->sfc_tokens,
                        nc, w.counters + 3);
   }
-  hipLaunchKernelGGL(k_lpt_rank, dim3(1), dim3(1024), 0, stream, w.wcell_off, w.counters + 3, w.wlpt,
-                     w.counters + 4);
+  hipLaunchKernelGGL(k_lpt_rank, dim3(LPT_RANK_MAX / LPT_NT), dim3(LPT_NT), 0, stream, w.wcell_off, w.counters + 3,
+                     w.wlpt, w.counters + 4);
   int32_t host_cnt[8];
   if (hipMemcpyAsync(host_cnt, w.counters, sizeof(host_cnt), hipMemcpyDeviceToHost, stream) != hipSuccess ||
       hipStreamSynchronize(stream) != hipSuccess)
@@ -578,7 +572,8 @@ extern "C" ssa_status ssa_plan_create_ex(const int32_t* coords, int64_t n, const
   // Before the host learns M: the longest-first order by ranking (up to LPT_RANK_MAX blocks)
   // and, when cells are blocks, the identity cells, so that the usual plan needs one host
   // synchronisation.
-  hipLaunchKernelGGL(k_lpt_rank, dim3(1), dim3(1024), 0, stream, w.blk_off, w.counters + 0, w.lpt, w.counters + 1);
+  hipLaunchKernelGGL(k_lpt_rank, dim3(LPT_RANK_MAX / LPT_NT), dim3(LPT_NT), 0, stream, w.blk_off, w.counters + 0,
+                     w.lpt, w.counters + 1);
   if (p->window_is_block)
     hipLaunchKernelGGL(k_identity_cells, dim3((unsigned)std::min<int64_t>((n + 256) / 256, 1024)), dim3(256), 0,
                        stream, w.counters + 0, w.blk_cell, w.cell_off, w.cell_blk);
