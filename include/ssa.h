@@ -157,11 +157,16 @@ void ssa_plan_destroy(ssa_plan plan);
  * selection are computed from a split of the fp32 pooled keys into two (f16) or
  * three (bf16) dtype terms, so they carry fp32-level accuracy).  The selection
  * keeps each work item's importance vector in on-chip memory, which bounds the
- * number of occupied blocks M: at most 6144, and at most 5760 (f32) or 4480
- * (bf16) for d = 128; a larger plan returns SSA_ERR_UNSUPPORTED.
+ * number of occupied blocks M (ssa_forward_max_blocks; from 7296 for f32 at d = 128
+ * to 34944 for 16-bit types at d = 32); a larger plan returns SSA_ERR_UNSUPPORTED.
  */
 size_t ssa_forward_workspace_size(ssa_plan plan, ssa_dtype dtype, int32_t heads, int32_t dim,
                                   int32_t topk, int save_for_bwd);
+/* The largest number of occupied blocks M the forward (and backward) accepts for this dtype
+ * and head dimension on the current device (the importance vectors' share of the selection
+ * kernel's on-chip memory); 0 for an invalid dtype or dim or when the device cannot be
+ * queried. */
+int64_t ssa_forward_max_blocks(ssa_dtype dtype, int32_t dim);
 ssa_status ssa_forward(ssa_plan plan, ssa_dtype dtype, int32_t heads, int32_t dim,
                        const void* q, const void* k, const void* v, const void* wk,
                        const void* wv, const void* gates, int32_t topk, float scale,

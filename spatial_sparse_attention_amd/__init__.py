@@ -13,7 +13,7 @@ import os
 
 import torch
 
-__all__ = ["Plan", "Window", "qkv_gates", "forward", "forward_batch", "forward_batch_workspace_size", "forward_workspace_size", "forward_noalloc", "backward",
+__all__ = ["Plan", "Window", "qkv_gates", "forward", "forward_batch", "forward_batch_workspace_size", "forward_max_blocks", "forward_workspace_size", "forward_noalloc", "backward",
            "backward_workspace_size", "NOALLOC_SCRATCH_BYTES",
            "SSAError", "lib", "LIB_PATH", "STAGE_POOL", "STAGE_SELECT", "STAGE_ATTEND", "STAGE_ALL"]
 
@@ -63,6 +63,8 @@ def _load():
     L.ssa_plan_get_info.restype = ctypes.c_int
     L.ssa_plan_destroy.argtypes = [_vp]
     L.ssa_plan_destroy.restype = None
+    L.ssa_forward_max_blocks.argtypes = [ctypes.c_int, _i32]
+    L.ssa_forward_max_blocks.restype = _i64
     L.ssa_forward_workspace_size.argtypes = [_vp, ctypes.c_int, _i32, _i32, _i32, ctypes.c_int]
     L.ssa_forward_workspace_size.restype = _sz
     fwd = [_vp, ctypes.c_int, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _i32, ctypes.c_float,
@@ -207,6 +209,11 @@ class Plan:
         if h is not None and h.value:
             lib.ssa_plan_destroy(h)
             self.handle = None
+
+
+def forward_max_blocks(dtype, dim: int) -> int:
+    """Largest number of occupied blocks the forward accepts for dtype and dim (0: unknown)."""
+    return int(lib.ssa_forward_max_blocks(_DTYPES[dtype], dim))
 
 
 def forward_workspace_size(plan: Plan, dtype, heads: int, dim: int, topk: int,

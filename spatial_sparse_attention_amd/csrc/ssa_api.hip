@@ -5,7 +5,6 @@
 
 namespace {
 constexpr int KT = 32;
-constexpr int64_t MAX_BLOCKS = 6144;  // importance vector of one work item lives in LDS (24 KB)
 constexpr int MAX_TOPK = 256;
 
 bool dim_ok(int d) { return d == 32 || d == 64 || d == 96 || d == 128; }
@@ -15,7 +14,6 @@ ssa_status check_common(ssa_plan p, ssa_dtype dt, int32_t H, int32_t d, int32_t 
   if ((int)dt < 0 || (int)dt > 2) return SSA_ERR_INVALID_ARG;
   if (H < 1 || d < 1 || topk < 1) return SSA_ERR_INVALID_ARG;
   if (!dim_ok(d) || topk > MAX_TOPK) return SSA_ERR_UNSUPPORTED;
-  if (p->M > MAX_BLOCKS) return SSA_ERR_UNSUPPORTED;
   if (p->n * (int64_t)H >= ((int64_t)1 << 31)) return SSA_ERR_UNSUPPORTED;
   return SSA_OK;
 }
@@ -60,6 +58,11 @@ size_t fwd_carve(Carver& c, const ssa_plan_s* p, ssa_dtype dt, int H, int d, int
   t.ow = p->wkind != 0 ? c.take<char>((size_t)n1 * H * d * es) : nullptr;
   if (w) *w = t;
   return c.off;
+}
+
+extern "C" int64_t ssa_forward_max_blocks(ssa_dtype dt, int32_t d) {
+  if (!abi_enum_in(&dt, 0, 2) || !dim_ok(d)) return 0;
+  return select_block_limit(dt, d);
 }
 
 extern "C" size_t ssa_forward_workspace_size(ssa_plan p, ssa_dtype dt, int32_t H, int32_t d,

@@ -190,6 +190,14 @@ static void empty_plan_entry_points() {
                     FAKE, 1, 0, nullptr) == SSA_ERR_BAD_PLAN);
 }
 
+static void max_blocks() {
+  CHECK(ssa_forward_max_blocks((ssa_dtype)5, 64) == 0);
+  CHECK(ssa_forward_max_blocks((ssa_dtype)-1, 64) == 0);
+  CHECK(ssa_forward_max_blocks(SSA_F16, 48) == 0);
+  for (int dt = 0; dt < 3; ++dt)
+    for (int d : {32, 64, 96, 128}) CHECK(ssa_forward_max_blocks((ssa_dtype)dt, d) >= 0);
+}
+
 static void producer_argument_errors() {
   auto call = [](int dt, int64_t n, int C, int H, int d, const void* x, float base) {
     return ssa_qkv_gates((ssa_dtype)dt, n, C, H, d, x, FAKE, FAKE, nullptr, FAKE, FAKE,
@@ -215,6 +223,7 @@ int main() {
   plan_argument_errors();
   empty_plan_entry_points();
   producer_argument_errors();
+  max_blocks();
   if (failures) {
     std::fprintf(stderr, "%d checks failed\n", failures);
     return 1;

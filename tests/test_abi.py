@@ -157,6 +157,14 @@ def test_qkv_gates_argument_errors(ssa):
     assert L.ssa_qkv_gates(*bad) == 1                 # negative rotary base
 
 
+def test_max_blocks_argument_errors(ssa):
+    L = ssa.lib
+    assert L.ssa_forward_max_blocks(5, 64) == 0
+    assert L.ssa_forward_max_blocks(-1, 64) == 0
+    assert L.ssa_forward_max_blocks(1, 48) == 0
+    assert L.ssa_forward_max_blocks(1, 96) >= 0      # 0 without a device
+
+
 def test_workspace_sizes_monotone(ssa):
     L = ssa.lib
     a = L.ssa_plan_workspace_size(1000, _grid(), 2, 2)

@@ -25,6 +25,7 @@ CASES = [  # (N, G, H, d, B, w, k, dtype)
     (700, 9, 1, 32, 1, 1, 6, "f32"),
     (400, 8, 2, 96, 8, 8, 3, "f16"),
     (3000, 40, 2, 64, 2, 2, 4, "f16"),      # ~2,500 blocks
+    (7000, 40, 1, 32, 1, 1, 8, "f32"),      # 7,000 single-token blocks
 ]
 
 

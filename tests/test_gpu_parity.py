@@ -98,6 +98,7 @@ SMALL = [  # (N, G, H, d, B, w, k, dtype)
     (3000, 40, 2, 64, 2, 2, 4, "f16"),       # ~2,500 blocks: in-kernel radix top-k (M > 1024)
     (3000, 40, 1, 96, 2, 4, 6, "bf16"),      # the same path with three key planes
     (2600, 36, 2, 32, 2, 2, 3, "f32"),       # and in fp32
+    (7000, 40, 1, 32, 1, 1, 8, "f16"),       # 7,000 single-token blocks: beyond 6,144 blocks
 ]
 
 
@@ -140,7 +141,31 @@ def _check_small(inp):
 def test_forward_small(case):
     M = _check_small(_small_inputs(case))
     if case[0] >= 2600:
-        assert M > 1024          # the radix-select path of the selection kernel
+        assert M > 1024          # the top-k inside the selection kernel
+    if case[0] == 7000:
+        assert M > 6144
+
+
+def test_forward_refuses_beyond_max_blocks():
+    """A plan with more occupied blocks than the selection's on-chip memory holds for the
+    dtype and d is refused before any launch (f32 at d = 128 has the lowest bound)."""
+    import torch
+    import spatial_sparse_attention_amd as ssa
+    lim = ssa.forward_max_blocks(torch.float32, 128)
+    assert 6000 < lim < 20000
+    assert ssa.forward_max_blocks(torch.float16, 96) > lim
+    N = lim + 500
+    rng = np.random.default_rng(5)
+    flat = rng.choice(64 ** 3, N, replace=False)
+    coords = torch.from_numpy(np.stack(np.unravel_index(flat, (64, 64, 64)), -1).astype(np.int32)).cuda()
+    plan = ssa.Plan(coords, 64, 1, 1)
+    assert plan.num_blocks == N
+    x = torch.zeros((N, 1, 128), dtype=torch.float32, device="cuda")
+    w = torch.zeros((128, 128), dtype=torch.float32, device="cuda")
+    g = torch.zeros((N, 1, 3), dtype=torch.float32, device="cuda")
+    with pytest.raises(ssa.SSAError) as e:
+        ssa.forward(plan, x, x, x, w, w, g, 4)
+    assert e.value.status == 2
 
 
 @pytest.mark.parametrize("case,scale", [((1500, 20, 2, 64, 4, 4, 4, "f16"), 0.05),
