@@ -1,6 +1,7 @@
 // Host side of the C ABI: argument validation, workspace carving and stage launches.
 #include <hip/hip_runtime.h>
 #include <math.h>
+#include <algorithm>
 #include "ssa_internal.h"
 
 namespace {
@@ -47,6 +48,8 @@ size_t fwd_carve(Carver& c, const ssa_plan_s* p, ssa_dtype dt, int H, int d, int
   t.pooled_v = c.take<char>((size_t)H * Mp * vrow_of(dt, d) * es);
   t.oc = c.take<char>((size_t)H * n1 * d * es);
   t.sel = c.take<int32_t>((size_t)H * (p->M > 0 ? p->M : 1) * topk);
+  t.sdesc = c.take<int2>((size_t)H * (p->M > 0 ? p->M : 1) * topk);
+  t.utab = c.take<int4>((size_t)std::max<int64_t>(std::max<int64_t>(p->M, p->wC), 1));
   t.sigma = split_topk(p->M, H) ? c.take<float>((size_t)H * (p->M > 0 ? p->M : 1) * Mp) : nullptr;
   t.lse = nullptr;
   t.obr = nullptr;

@@ -858,7 +858,8 @@ __global__ __launch_bounds__(64 * ATT_WAVES) __attribute__((amdgpu_waves_per_eu(
     const int32_t* __restrict__ sel, const typename Tr<DT>::T* __restrict__ oc, int M, int H,
     int nchunk, int64_t N, int topk, float sl2, int window_is_block, typename Tr<DT>::T* __restrict__ out,
     float* __restrict__ lse_save, float* __restrict__ os_save, float* __restrict__ ow_save,
-    const typename Tr<DT>::T* __restrict__ ow_in) {
+    const typename Tr<DT>::T* __restrict__ ow_in, const int4* __restrict__ utab,
+    const int2* __restrict__ sdesc) {
   constexpr int mode = MODE;
   using C = Cfg<DT, D>;
   using T = typename Tr<DT>::T;
@@ -883,12 +884,16 @@ __global__ __launch_bounds__(64 * ATT_WAVES) __attribute__((amdgpu_waves_per_eu(
   xcd_split(blockIdx.x, nchunk * H, unit, member);
   if (unit >= M) return;
   const int h = member % H, chunk = member / H;
-  const int b = lpt[unit];
-  const int r0 = blk_off[b], rows = blk_off[b + 1] - r0;
+  const int4 ut = utab[unit];  // (block, first row, rows)
+  const int b = ut.x;
+  const int r0 = ut.y, rows = ut.z;
   if (chunk * ATT_ROWS >= rows) return;  // uniform across the workgroup
 
-  // ---- metadata, loads issued side by side: selection row, window cell, queries, gates
-  const int sb = mode != ATT_WINDOW && tid < topk ? sel[((int64_t)h * M + b) * topk + tid] : -1;  // ascending, -1 padded
+  // ---- metadata, loads issued side by side: selection row and its blocks' extents, window
+  // cell, queries, gates
+  const int64_t srow = ((int64_t)h * M + b) * topk + tid;
+  const int sb = mode != ATT_WINDOW && tid < topk ? sel[srow] : -1;  // ascending, -1 padded
+  const int2 sd = mode != ATT_WINDOW && tid < 64 && tid < topk ? sdesc[srow] : make_int2(0, 0);
   int c0 = b, c1 = b + 1;                       // window cell as a range of cell_blk
   if (!window_is_block) {
     const int cell = blk_cell[b];
@@ -953,9 +958,17 @@ __global__ __launch_bounds__(64 * ATT_WAVES) __attribute__((amdgpu_waves_per_eu(
       const int ne = wave == 0 ? nsel : nwin;
       int off = 0, sz = 0;
       if (lane < ne) {
-        const int blk = wave == 0 ? sel_lds[lane] : (window_is_block ? b : cell_blk[c0 + lane]);
-        off = blk_off[blk];
-        sz = blk_off[blk + 1] - off;
+        if (wave == 0) {  // selected block `lane` is this thread's entry
+          off = sd.x;
+          sz = sd.y;
+        } else if (window_is_block) {
+          off = r0;
+          sz = rows;
+        } else {
+          const int blk = cell_blk[c0 + lane];
+          off = blk_off[blk];
+          sz = blk_off[blk + 1] - off;
+        }
       }
       const int incl = wave_incl_scan(sz, lane);
       if (lane < ne) {
@@ -1153,6 +1166,24 @@ hipError_t run_select(const ssa_plan_s* p, int H, int topk, float sl2, const voi
   return hipGetLastError();
 }
 
+// Per launch of k_attend: its units' (block, first row, rows) and, with a selection, each
+// selected block's first sorted row and size, so that a work item reads them in one step.
+__global__ __launch_bounds__(256) void k_att_prep(const int32_t* __restrict__ lpt, const int32_t* __restrict__ off,
+                                                  int units, int4* __restrict__ utab,
+                                                  const int32_t* __restrict__ sel,
+                                                  const int32_t* __restrict__ blk_off, int64_t nsel,
+                                                  int2* __restrict__ sdesc) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < units) {
+    const int b = lpt[i], r0 = off[b];
+    utab[i] = make_int4(b, r0, off[b + 1] - r0, 0);
+  }
+  if (i < nsel) {
+    const int s = sel[i];
+    sdesc[i] = s >= 0 ? make_int2(blk_off[s], blk_off[s + 1] - blk_off[s]) : make_int2(0, 0);
+  }
+}
+
 template <int DT, int D>
 hipError_t run_attend(const ssa_plan_s* p, int H, int topk, float sl2, const void* q,
                       const void* k, const void* v, const void* gates, const FwdWs& w,
@@ -1165,13 +1196,17 @@ hipError_t run_attend(const ssa_plan_s* p, int H, int topk, float sl2, const voi
     float* lse = mode == ATT_BOTH ? w.lse : nullptr;
     float* os = mode == ATT_BOTH && w.obr ? w.obr + p->n * H * D : nullptr;
     float* ows = mode == ATT_BOTH && w.obr ? w.obr + 2 * p->n * H * D : nullptr;
+    const int64_t nsel = mode == ATT_WINDOW ? 0 : (int64_t)H * p->M * topk;
+    const int64_t nprep = std::max<int64_t>(units, nsel);
+    hipLaunchKernelGGL(k_att_prep, dim3((unsigned)((nprep + 255) / 256)), dim3(256), 0, s, lpt, off, (int)units,
+                       w.utab, sel, p->blk_off, nsel, w.sdesc);
     auto kern = mode == ATT_BOTH ? (buf ? k_attend<DT, D, true, ATT_BOTH> : k_attend<DT, D, false, ATT_BOTH>)
               : mode == ATT_WINDOW ? (buf ? k_attend<DT, D, true, ATT_WINDOW> : k_attend<DT, D, false, ATT_WINDOW>)
                                    : (buf ? k_attend<DT, D, true, ATT_SELECTED> : k_attend<DT, D, false, ATT_SELECTED>);
     hipLaunchKernelGGL(kern, dim3(xcd_grid(units, (int64_t)H * nchunk)), dim3(64 * ATT_WAVES), 0, s,
                        (const T*)q, (const T*)k, (const T*)v, (const T*)gates, perm, off, p->blk_cell,
                        p->cell_off, p->cell_blk, lpt, sel, (const T*)w.oc, (int)units, H, nchunk, p->n,
-                       topk, sl2, wib, dst, lse, os, ows, (const T*)w.ow);
+                       topk, sl2, wib, dst, lse, os, ows, (const T*)w.ow, w.utab, w.sdesc);
   };
   if (p->wkind == 0) {
     launch(ATT_BOTH, p->M, p->perm, p->blk_off, p->lpt, p->max_rows, (int)p->window_is_block, (T*)out);

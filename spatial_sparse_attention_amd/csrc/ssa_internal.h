@@ -120,6 +120,8 @@ struct FwdWs {
   void* pooled_v;    // [H][Mp][vrow] dtype: pooled values, row-major
   void* oc;          // [N][H][d] compressed-branch output (dtype)
   int32_t* sel;      // [H][M][topk]
+  int2* sdesc;       // [H][M][topk] first sorted row and size of each selected block ((0, 0) for -1)
+  int4* utab;        // [max(M, window cells)] per longest-first unit: (block, first row, rows, 0)
   float* sigma;      // [H][M][Mp] importance scores when the top-k runs as its own kernel, else null
   float* lsec;       // [H][N] log2-sum-exp2 of the compressed branch's scaled scores (= lse plane 0)
   void* ow;          // [N][H][d] dtype, caller order: the window branch's output when window cells
