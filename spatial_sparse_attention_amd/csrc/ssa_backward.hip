@@ -73,7 +73,7 @@ __host__ __device__ inline int kg_qbp(int M) {  // query blocks per group piece
   const int gp = kg_pieces(M);
   return (M + gp - 1) / gp;
 }
-inline int64_t kv_budget_rows(int d) { return (int64_t)(128 << 20) / (8 * d); }
+inline int64_t kv_budget_rows(int d) { return (int64_t)(256 << 20) / (8 * d); }
 
 int cmp_chunks(int64_t Mp, int H) {
   const int64_t groups = (Mp / KT + BW - 1) / BW * H;
@@ -453,8 +453,8 @@ __device__ inline V wg_exclusive_scan(V x, V* sh) {
 constexpr int KV_GRP = 0, KV_UNIT = 1, KV_NARROW = 2, KV_KINDS = 3;
 
 // One workgroup.  Per sorted unit: tiny (a key group member), split into pieces, or whole,
-// taken in sorted order while the running partial demand (key rows) stays within the
-// budget; sinfo = {unit, pieces, partial row offset or -1, flags: 1 tiny, 2 narrow}.  Then,
+// taken in sorted order while the running partial demand (key rows) stays within its head's
+// share of the budget; sinfo = {unit, pieces, partial row offset or -1, flags: 1 tiny, 2 narrow}.  Then,
 // one thread per head, the head's tiny units in sorted order are packed into key groups.
 // Items of kind k form 8 lists (one per XCD): list x of kind k holds items xbase[9k + x] ..
 // xbase[9k + x + 1] - 1 (xbase[9k + 8] = end of kind k).  Group pieces and narrow items go
@@ -495,6 +495,23 @@ __global__ __launch_bounds__(1024) void k_kv_schedule(
   }
   wg_exclusive_scan<int64_t>(dsum, sh64);
   int64_t dpre = sh64[tid];
+  // the budget is shared out by head (units are head-major, M per head; with more than 1024
+  // heads it is one pool): each head's units, most entries first, take from its share, so
+  // the long streams of every head are split or grouped, not only those of the first heads
+  __shared__ int64_t hbase[1024];
+  const bool per_head = H <= 1024;
+  const int64_t share = per_head ? budget / H : budget;
+  if (per_head) {
+    int64_t run = dpre;
+    for (int si = s0; si < s1; ++si) {
+      if (si % M == 0) hbase[si / M] = run;
+      int u, want, rows;
+      bool cand;
+      unit_info(si, u, want, rows, cand);
+      run += demand(want, rows, cand);
+    }
+  }
+  __syncthreads();
   int isum[NXCD];
 #pragma unroll
   for (int x = 0; x < NXCD; ++x) isum[x] = 0;
@@ -504,11 +521,13 @@ __global__ __launch_bounds__(1024) void k_kv_schedule(
     bool cand;
     unit_info(si, u, want, rows, cand);
     const int64_t dem = demand(want, rows, cand);
-    const bool fits = dem > 0 && dpre + dem <= budget;
+    const int64_t local = per_head ? dpre - hbase[si / M] : dpre;  // demand before it in its share
+    const bool fits = dem > 0 && local + dem <= share;
     const bool tiny = cand && fits, split = !cand && fits;
     const bool narrow = narrow_ok && rows <= 32;
     const int pieces = tiny ? 1 + GP : (split ? want : 1);
-    sinfo[si] = make_int4(u, pieces, fits ? (int)dpre : -1, (tiny ? 1 : 0) | (narrow ? 2 : 0));
+    const int64_t prow = per_head ? (int64_t)(si / M) * share + local : dpre;  // partial rows
+    sinfo[si] = make_int4(u, pieces, fits ? (int)prow : -1, (tiny ? 1 : 0) | (narrow ? 2 : 0));
     dpre += dem;
     const int n = tiny ? 1 : (rows + KROWS - 1) / KROWS * pieces;
     if (narrow) {
