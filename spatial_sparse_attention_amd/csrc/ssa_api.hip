@@ -55,7 +55,7 @@ size_t fwd_carve(Carver& c, const ssa_plan_s* p, ssa_dtype dt, int H, int d, int
   t.obr = nullptr;
   if (save) {
     t.lse = c.take<float>((size_t)3 * H * n1);
-    t.obr = c.take<float>((size_t)3 * H * n1 * d);
+    t.obr = save_f16(dt) ? (void*)c.take<uint16_t>((size_t)2 * H * n1 * d) : (void*)c.take<float>((size_t)3 * H * n1 * d);
   }
   t.lsec = save ? t.lse : c.take<float>((size_t)H * n1);
   t.ow = p->wkind != 0 ? c.take<char>((size_t)n1 * H * d * es) : nullptr;

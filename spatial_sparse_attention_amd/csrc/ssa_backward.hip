@@ -122,13 +122,14 @@ size_t carve(Carver& c, const ssa_plan_s* p, int H, int d, int topk, BwdWs* w) {
 
 // ------------------------------------------------------------------ prep
 // dgates and D for the three branches.  A group of GS lanes per (sorted row r, head h): lane
-// j of the group reads the j-th 16-byte chunk of dO's head row (and the matching fp32 chunks
-// of the three saved branch outputs), so a group reads contiguous rows; the dot products are
-// finished with shuffles inside the group.
+// j of the group reads the j-th 16-byte chunk of dO's head row (and the matching chunks of
+// the three saved branch outputs o0, o1, o2, sorted rows), so a group reads contiguous rows;
+// the dot products are finished with shuffles inside the group.
 template <int DT, int D>
 __global__ __launch_bounds__(256) void k_bwd_prep(
     const typename Tr<DT>::T* __restrict__ dout, const typename Tr<DT>::T* __restrict__ gates,
-    const float* __restrict__ obr, const int32_t* __restrict__ perm, int64_t N, int H,
+    const typename SaveT<DT>::type* __restrict__ o0, const typename SaveT<DT>::type* __restrict__ o1,
+    const typename SaveT<DT>::type* __restrict__ o2, const int32_t* __restrict__ perm, int64_t N, int H,
     float* __restrict__ dgates, float* __restrict__ Dsave) {
   using T = typename Tr<DT>::T;
   constexpr int EPC = 16 / sizeof(T), CPR = D / EPC;
@@ -146,9 +147,9 @@ __global__ __launch_bounds__(256) void k_bwd_prep(
     const T* ae = reinterpret_cast<const T*>(&a);
 #pragma unroll
     for (int x = 0; x < 3; ++x) {
-      const float* o = obr + (((int64_t)x * N + r) * H + h) * D + j * EPC;
+      const typename SaveT<DT>::type* o = (x == 0 ? o0 : (x == 1 ? o1 : o2)) + (r * H + h) * D + j * EPC;
 #pragma unroll
-      for (int e = 0; e < EPC; ++e) acc[x] += Tr<DT>::up(ae[e]) * o[e];
+      for (int e = 0; e < EPC; ++e) acc[x] += Tr<DT>::up(ae[e]) * (float)o[e];
     }
   }
 #pragma unroll
@@ -1433,8 +1434,13 @@ hipError_t run_backward(const ssa_plan_s* p, int H, int topk, float scale, const
   const float sl2 = scale * 1.4426950408889634f;
   const int nchunk = (p->max_rows + BROWS - 1) / BROWS;
   constexpr int PREP_GS = 16 / sizeof(T) * 16 >= D ? 16 : (16 / sizeof(T) * 32 >= D ? 32 : 64);
+  using ST = typename SaveT<DT>::type;
+  const int64_t plane = N * H * D;  // f16: the compressed branch's plane is oc
+  const ST* o0 = DT == DT_F16 ? (const ST*)fw.oc : (const ST*)fw.obr;
+  const ST* o1 = (const ST*)fw.obr + (DT == DT_F16 ? 0 : plane);
+  const ST* o2 = (const ST*)fw.obr + (DT == DT_F16 ? 1 : 2) * plane;
   hipLaunchKernelGGL((k_bwd_prep<DT, D>), dim3((unsigned)((N * H * PREP_GS + 255) / 256)), dim3(256), 0, s,
-                     (const T*)dout, (const T*)gates, fw.obr, p->perm, N, H, dgates, w.D);
+                     (const T*)dout, (const T*)gates, o0, o1, o2, p->perm, N, H, dgates, w.D);
   const bool buf = buffer_addressable(N * H * D * (int64_t)sizeof(T));
   if (buf)
     hipLaunchKernelGGL((k_bwd_dq<DT, D, true>), dim3(xcd_grid(M, (int64_t)H * nchunk)), dim3(64 * BW), 0, s,

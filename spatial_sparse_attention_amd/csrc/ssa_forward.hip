@@ -857,8 +857,9 @@ __global__ __launch_bounds__(64 * ATT_WAVES) __attribute__((amdgpu_waves_per_eu(
     const int32_t* __restrict__ cell_blk, const int32_t* __restrict__ lpt,
     const int32_t* __restrict__ sel, const typename Tr<DT>::T* __restrict__ oc, int M, int H,
     int nchunk, int64_t N, int topk, float sl2, int window_is_block, typename Tr<DT>::T* __restrict__ out,
-    float* __restrict__ lse_save, float* __restrict__ os_save, float* __restrict__ ow_save,
-    const typename Tr<DT>::T* __restrict__ ow_in, const int4* __restrict__ utab,
+    float* __restrict__ lse_save, typename SaveT<DT>::type* __restrict__ os_save,
+    typename SaveT<DT>::type* __restrict__ ow_save, const typename Tr<DT>::T* __restrict__ ow_in,
+    const int4* __restrict__ utab,
     const int2* __restrict__ sdesc) {
   constexpr int mode = MODE;
   using C = Cfg<DT, D>;
@@ -938,7 +939,7 @@ __global__ __launch_bounds__(64 * ATT_WAVES) __attribute__((amdgpu_waves_per_eu(
     if (lse_save && wave_active && valid) {
       const int64_t row = r0 + my_row;
       if (g == 0) lse_save[(int64_t)(H + h) * N + row] = st.m + fast_log2(ls);
-      float* srow2 = os_save + (row * H + h) * D;
+      typename SaveT<DT>::type* srow2 = os_save + (row * H + h) * D;
       const float inv = 1.f / ls;
 #pragma unroll
       for (int j = 0; j < C::NDV; ++j)
@@ -1063,7 +1064,7 @@ __global__ __launch_bounds__(64 * ATT_WAVES) __attribute__((amdgpu_waves_per_eu(
     T* dst = out + (tok_q * H + h) * D;
     if (lse_save) {
       if (g == 0) lse_save[(int64_t)(2 * H + h) * N + r0 + my_row] = st.m + fast_log2(ltot);
-      float* wrow = ow_save + ((int64_t)(r0 + my_row) * H + h) * D;
+      typename SaveT<DT>::type* wrow = ow_save + ((int64_t)(r0 + my_row) * H + h) * D;
       const float inv = 1.f / ltot;
 #pragma unroll
       for (int j = 0; j < C::NDV; ++j)
@@ -1137,7 +1138,7 @@ hipError_t run_select(const ssa_plan_s* p, int H, int topk, float sl2, const voi
   const int wpx = std::max(1, std::min(per, cus * std::max(per_cu, 1) / 8));  // workgroups per XCD
   hipLaunchKernelGGL((k_compress<DT, D>), dim3((unsigned)(8 * wpx)), dim3(64 * CMP_WAVES), 0, s,
                      (const T*)q, (const T*)w.pooled, p->perm, (int)p->M, Mp, H, p->n, nch, per, wpx, sl2,
-                     (T*)w.oc, w.lsec, w.obr);
+                     (T*)w.oc, w.lsec, DT == DT_F16 ? nullptr : (float*)w.obr);  // f16: oc is the saved plane
   // blocks per importance workgroup: one for blocks of 64 rows and more on average, else
   // enough for about 256 rows, as far as their importance rows fit the LDS
   int G = 1;
@@ -1194,8 +1195,10 @@ hipError_t run_attend(const ssa_plan_s* p, int H, int topk, float sl2, const voi
                     int max_rows, int wib, T* dst) {
     const int nchunk = (max_rows + ATT_ROWS - 1) / ATT_ROWS;
     float* lse = mode == ATT_BOTH ? w.lse : nullptr;
-    float* os = mode == ATT_BOTH && w.obr ? w.obr + p->n * H * D : nullptr;
-    float* ows = mode == ATT_BOTH && w.obr ? w.obr + 2 * p->n * H * D : nullptr;
+    using ST = typename SaveT<DT>::type;
+    const int64_t plane = p->n * H * D;  // f16 keeps no compressed plane (oc is it)
+    ST* os = mode == ATT_BOTH && w.obr ? (ST*)w.obr + (DT == DT_F16 ? 0 : plane) : nullptr;
+    ST* ows = mode == ATT_BOTH && w.obr ? (ST*)w.obr + (DT == DT_F16 ? 1 : 2) * plane : nullptr;
     const int64_t nsel = mode == ATT_WINDOW ? 0 : (int64_t)H * p->M * topk;
     const int64_t nprep = std::max<int64_t>(units, nsel);
     hipLaunchKernelGGL(k_att_prep, dim3((unsigned)((nprep + 255) / 256)), dim3(256), 0, s, lpt, off, (int)units,

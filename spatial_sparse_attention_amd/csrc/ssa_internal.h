@@ -128,8 +128,13 @@ struct FwdWs {
                      // have a token-level partition of their own (else null)
   // saved for the backward (save_for_bwd only; else null)
   float* lse;        // [3][H][N] per-branch log2-sum-exp2 of the scaled scores
-  float* obr;        // [3][N][H][d] the three branch outputs in fp32 (compressed, selected, window)
+  void* obr;         // the branch outputs, sorted rows: fp32 [3][N][H][d] (compressed, selected,
+                     // window); f16 inputs: f16 [2][N][H][d] (selected, window; the compressed
+                     // output is oc itself)
 };
+// Saved branch outputs: f16 inputs keep them in f16 (the backward's dgates and D read them
+// once; f16 rounding is below the gradients' own), other types in fp32.
+static inline bool save_f16(ssa_dtype dt) { return dt == SSA_F16; }
 size_t fwd_carve(Carver& c, const ssa_plan_s* p, ssa_dtype dt, int H, int d, int topk, int save,
                  FwdWs* w);
 

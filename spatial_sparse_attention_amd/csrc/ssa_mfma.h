@@ -14,6 +14,10 @@ typedef float ssa_f16v __attribute__((ext_vector_type(16)));
 typedef float ssa_f4v __attribute__((ext_vector_type(4)));
 
 enum { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2 };
+template <int DT> struct Tr;
+// element type of the saved branch outputs: f16 for f16 inputs, else fp32
+template <int DT> struct SaveT { using type = float; };
+template <> struct SaveT<DT_F16> { using type = _Float16; };
 
 template <int DT> struct Tr;
 
