@@ -58,6 +58,34 @@ def attend_traffic():
         return None
 
 
+HBM_PEAK_GBS = 8000.0
+
+
+def attend_roofline(flops, alg_bytes, ms, peak_tflops, traffic):
+    """Roofline of k_attend, the attend stage's one launch.  Its work: flops (4 d per attended
+    selected or window pair).  Its algorithmic bytes are the method's: Q, K, V and gates read
+    and O written -- all of which this kernel moves (every key is in some window cell); the
+    compressed branch's output, an intermediate of the split into kernels that it also reads,
+    is not counted.  The binding roof is the one its arithmetic intensity falls under: HBM
+    below the ridge (peak FLOP/s over HBM bandwidth), MFMA above it; both fractions are given."""
+    ai = flops / alg_bytes
+    ridge = peak_tflops * 1e12 / (HBM_PEAK_GBS * 1e9)
+    tflops = flops / (ms * 1e-3) / 1e12
+    gbs = alg_bytes / (ms * 1e-3) / 1e9
+    hbm = ai < ridge
+    return {"kernel": "k_attend (selected + window branches, gated combine)",
+            "bound": "hbm" if hbm else "mfma",
+            "achieved": gbs if hbm else tflops, "peak": HBM_PEAK_GBS if hbm else peak_tflops,
+            "unit": "GB/s" if hbm else "TFLOP/s",
+            "frac": gbs / HBM_PEAK_GBS if hbm else tflops / peak_tflops,
+            "traffic": traffic,
+            "arithmetic_intensity": ai, "ridge": ridge,
+            "bytes_per_launch": alg_bytes, "flops_per_launch": flops,
+            "mfma_tflops": tflops, "mfma_frac": tflops / peak_tflops,
+            "hbm_gbs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS,
+            "launch_us_hip_events": ms * 1e3}
+
+
 def attended_pairs(plan_arrays, sel):
     """Per-head sum over queries of (M + |selected keys| + |window keys|)."""
     blk_off = plan_arrays["blk_off"].astype(np.int64)
@@ -448,12 +476,8 @@ def main():
         "recorded": workload_record(sizes, sel_np),
         "credited_flops": flops,
         "algorithmic_bytes": alg_bytes,
-        "roofline": {"kernel": "k_attend (selected + window branches, gated combine)", "bound": "mfma",
-                     "achieved": att_tflops, "peak": peak, "unit": "TFLOP/s",
-                     "frac": att_tflops / peak,
-                     "traffic": attend_traffic() if wl.name == WORKLOAD else None,
-                     "work_per_launch_flops": att_flops,
-                     "launch_us_hip_events": stage_ms["attend"] * 1e3},
+        "roofline": attend_roofline(att_flops, alg_bytes, stage_ms["attend"], peak,
+                                    attend_traffic() if wl.name == WORKLOAD else None),
         "compressed_branch": {"kernels": "k_compress + k_select (+ k_topk when M <= 1024)",
                               "ms": stage_ms["select"], "tflops": sel_tflops,
                               "mfma_peak_frac": sel_tflops / peak, "work_flops": cmp_flops},
