@@ -245,17 +245,81 @@ __device__ inline void load4(const T* p, float* v) {
 
 // Top keff = min(topk, M) entries of sig[0..M) (in LDS, zero from M up to the next multiple of
 // four; ties to the lower id) by one wave, written in ascending id order to out[0..keff),
-// out[keff..topk) = -1.  sig >= 0, so the fp32 bit patterns order like the values: the
-// keff-th largest pattern T is found bit by bit from the top, each step counting the entries
-// at or above the candidate (four 16-byte LDS reads in flight per lane, then across the wave;
-// the zeros never count), and a scan in id order places every entry above T and the first
-// entries equal to T.  The rows of a workgroup's blocks are taken one per wave.
-__device__ void topk_wave(const float* sig, int M, int topk, int32_t* __restrict__ out, int lane) {
+// out[keff..topk) = -1.  sig >= 0, so the fp32 bit patterns order like the values.
+// Usual case (keff <= 64): the keff-th largest of the 64 lane maxima is a lower bound lb of the
+// keff-th largest entry (keff lanes hold an entry at or above it), so every entry that can be
+// chosen is at least lb; those entries are compacted in id order into the wave's candidate
+// buffer cbuf (64 patterns, then 64 ids) and, when there are at most 64, the exact threshold
+// and the placement are found among them, one candidate per lane: two passes over the row in
+// all.  Otherwise (more candidates, keff > 64, lb = 0) the keff-th largest pattern T is found
+// bit by bit from the top over the whole row, each step counting the entries at or above the
+// candidate (four 16-byte LDS reads in flight per lane, then across the wave; the zeros never
+// count), and a scan in id order places every entry above T and the first entries equal to T.
+// The rows of a workgroup's blocks are taken one per wave.
+__device__ void topk_wave(const float* sig, int M, int topk, int32_t* __restrict__ out, int lane,
+                          uint32_t* cbuf) {
   const int keff = min(topk, M);
   const bool all = keff == M;
   const uint32_t* u32 = reinterpret_cast<const uint32_t*>(sig);
   const uint4* u4 = reinterpret_cast<const uint4*>(sig);  // rows start 16-byte aligned
   const int NQ = (M + 3) / 4;
+  auto wave_rank = [&](uint64_t m) {  // set bits of m below this lane
+    return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+  };
+  if (!all && keff <= 64) {
+    uint32_t lmax = 0;
+    for (int q = lane; q < NQ; q += 256) {
+      uint4 v[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) v[t] = q + 64 * t < NQ ? u4[q + 64 * t] : make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) lmax = max(lmax, max(max(v[t].x, v[t].y), max(v[t].z, v[t].w)));
+    }
+    uint32_t lb = 0;
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t cand = lb | (1u << bit);
+      if (__builtin_popcountll(__builtin_amdgcn_ballot_w64(lmax >= cand)) >= keff) lb = cand;
+    }
+    if (lb > 0) {
+      int nc = 0;
+      for (int base = 0; base < M; base += 256) {
+        uint32_t v[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) v[t] = base + 64 * t + lane < M ? u32[base + 64 * t + lane] : 0u;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const bool in = v[t] >= lb;  // the zeros past M never reach lb >= 1
+          const uint64_t bm = __builtin_amdgcn_ballot_w64(in);
+          const int pos = nc + wave_rank(bm);
+          if (in && pos < 64) {
+            cbuf[pos] = v[t];
+            cbuf[64 + pos] = (uint32_t)(base + 64 * t + lane);
+          }
+          nc += __builtin_popcountll(bm);
+        }
+      }
+      if (nc <= 64) {
+        // LDS operations of a wave complete in order: the candidates are in place once the
+        // writes above have been issued and the compiler keeps the reads behind them
+        __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        const uint32_t cu = lane < nc ? cbuf[lane] : 0u;  // ids ascend with the lane
+        const int cj = lane < nc ? (int)cbuf[64 + lane] : 0;
+        // the search over the candidates alone finds the row's threshold: every entry at or
+        // above a trial value that does not exceed it is a candidate
+        uint32_t T = 0;
+        for (int bit = 31; bit >= 0; --bit) {
+          const uint32_t cand = T | (1u << bit);
+          if (__builtin_popcountll(__builtin_amdgcn_ballot_w64(cu >= cand)) >= keff) T = cand;
+        }
+        const uint64_t bg = __builtin_amdgcn_ballot_w64(cu > T), be = __builtin_amdgcn_ballot_w64(lane < nc && cu == T);
+        const int need = keff - __builtin_popcountll(bg);
+        const int lg = wave_rank(bg), le = wave_rank(be);
+        if (cu > T || (lane < nc && cu == T && le < need)) out[lg + min(le, need)] = cj;
+        for (int t = keff + lane; t < topk; t += 64) out[t] = -1;
+        return;
+      }
+    }
+  }
   auto count_ge = [&](uint32_t cand) {  // entries with pattern >= cand (cand >= 1), wave total
     int cnt = 0;
     for (int q = lane; q < NQ; q += 256) {
@@ -286,8 +350,7 @@ __device__ void topk_wave(const float* sig, int M, int topk, int32_t* __restrict
     const bool gt = j < M && (all || u > T);
     const bool eq = j < M && !all && u == T;
     const uint64_t bg = __builtin_amdgcn_ballot_w64(gt), be = __builtin_amdgcn_ballot_w64(eq);
-    const int lg = run_gt + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bg >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bg, 0u));
-    const int le = run_eq + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(be >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)be, 0u));
+    const int lg = run_gt + wave_rank(bg), le = run_eq + wave_rank(be);
     if (gt || (eq && le < need)) out[lg + min(le, need)] = j;
     run_gt += __builtin_popcountll(bg);
     run_eq += __builtin_popcountll(be);
@@ -544,17 +607,27 @@ __global__ __launch_bounds__(64 * SEL_WAVES) void k_select(
   const int h = item / ngrp;
   const int gi = item % ngrp;
   const int G0 = gi * G, Gk = min(G, M - G0);  // members
-  if (tid == 0) {
-    int tp = 0;
-    for (int k = 0; k < Gk; ++k) {
-      const int bb = lpt[G0 + k];
-      mb[k] = bb;
-      mr0[k] = blk_off[bb];
-      mrows[k] = blk_off[bb + 1] - mr0[k];
-      mtp[k] = tp;
-      tp += (mrows[k] + 31) / 32;
+  if (tid < 64) {  // member k in lane k (loads side by side), first tiles by a scan over the lanes
+    int bb = 0, r0m = 0, rows = 0;
+    if (tid < Gk) {
+      bb = lpt[G0 + tid];
+      r0m = blk_off[bb];
+      rows = blk_off[bb + 1] - r0m;
     }
-    mtp[Gk] = tp;
+    const int nt = (rows + 31) / 32;
+    int incl = nt;
+#pragma unroll
+    for (int off = 1; off < SEL_GMAX; off <<= 1) {
+      const int o = __shfl_up(incl, off);
+      if (tid >= off) incl += o;
+    }
+    if (tid < Gk) {
+      mb[tid] = bb;
+      mr0[tid] = r0m;
+      mrows[tid] = rows;
+      mtp[tid] = incl - nt;
+    }
+    if (tid == Gk - 1) mtp[Gk] = incl;
   }
   const int ntile = Mp / C::PT;
   const int nkt = (M + KT - 1) / KT;  // 32-key tiles holding real blocks
@@ -662,7 +735,8 @@ __global__ __launch_bounds__(64 * SEL_WAVES) void k_select(
     }
   } else {
     for (int k = wave; k < Gk; k += SEL_WAVES)
-      topk_wave(sig + k * Mp, M, topk, sel + ((int64_t)h * M + mb[k]) * topk, lane);
+      topk_wave(sig + k * Mp, M, topk, sel + ((int64_t)h * M + mb[k]) * topk, lane,
+                reinterpret_cast<uint32_t*>(qlds) + wave * 128);  // the query tiles are free now
   }
 }
 
