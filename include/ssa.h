@@ -281,7 +281,7 @@ ssa_status ssa_backward(ssa_plan plan, ssa_dtype dtype, int32_t heads, int32_t d
  * The step before SSA: each token's queries, keys, values and gates from its features
  * (Hi3D pipeline page, "Stage 3": RMS normalisation of the self-attention queries and keys,
  * rotary position embeddings; nav.superapi.store "Direct3D-S2", "Technical principles of
- * Direct3D-S2": predicted gating scores), in one kernel:
+ * Direct3D-S2": the model predicts the per-branch gates), in one kernel:
  *   y = x W_qkv^T, W_qkv [3*H*d, C] (linear-layer layout; output features q | k | v, each
  *       head-major), x [N, C];
  *   q = rope(rmsnorm(y_q) * gamma_q), k = rope(rmsnorm(y_k) * gamma_k), v = y_v   [N,H,d];

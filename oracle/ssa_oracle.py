@@ -11,7 +11,7 @@ compression module reduces each block to one token by pooling and attends to
 those block tokens (global context); the attention scores of the compression
 module pick the important blocks, whose tokens are attended at full
 resolution (selection); a local window module attends to nearby tokens; and the
-three outputs are aggregated with predicted gating scores.
+three outputs are summed with per-branch weights (gates) that the model predicts.
 
 The pages give no equations.  The readings taken where they are silent:
   * blocks are axis-aligned B^3 cubes anchored at the origin, ids ordered by the
@@ -436,7 +436,7 @@ def backward(inp: dict, sel: np.ndarray, dout: np.ndarray, scale=None):
 # The step before the path: the transformer block produces each token's queries, keys,
 # values and gates from its features (the Sparc3D/Hi3D pipeline page, "Stage 3": RMS
 # normalisation of the self-attention queries and keys, rotary position embeddings; the
-# nav.superapi.store page, "Technical principles of Direct3D-S2": predicted gating scores).
+# nav.superapi.store page, "Technical principles of Direct3D-S2": the model predicts the per-branch gates).
 def rms_norm(x, gamma, eps):
     """x / sqrt(mean(x^2) + eps) * gamma over the last axis."""
     x = np.asarray(x, np.float64)

@@ -4,8 +4,8 @@
 //
 // The Sparc3D/Hi3D pipeline page ("Stage 3") names RMS normalisation of the self-attention
 // queries and keys and rotary position embeddings; the nav.superapi.store Direct3D-S2 page
-// ("Technical principles of Direct3D-S2") aggregates SSA's branches with predicted gating
-// scores.  Definitions (ssa.h, ssa_qkv_gates): y = x W^T with W in linear-layer layout
+// ("Technical principles of Direct3D-S2") sums SSA's branches with per-branch gates that the
+// model predicts.  Definitions (ssa.h, ssa_qkv_gates): y = x W^T with W in linear-layer layout
 // [out_features, C]; q = rope(rmsnorm(y_q) * gamma_q), k likewise, v = y_v, gates =
 // sigmoid(x W_g^T + b_g); rope rotates pair i of axis a (dimensions 2Pa + 2i, 2Pa + 2i + 1,
 // P = floor(d / 6)) by c_a * base^(-i / P).

@@ -1,6 +1,6 @@
 """Pins of the oracle's producer of SSA's inputs: RMS norm of queries and keys, the 3D rotary
 embedding, the projections and the sigmoid gates (the Hi3D pipeline page, "Stage 3";
-nav.superapi.store, "Technical principles of Direct3D-S2": predicted gating scores)."""
+nav.superapi.store, "Technical principles of Direct3D-S2": the model predicts the per-branch gates)."""
 import json
 import os
 
